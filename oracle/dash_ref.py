@@ -1,0 +1,344 @@
+"""DashAttention forward, decode and backward in plain float64 (test infrastructure only).
+
+One query row at a time, gathering only the tokens the row attends, so that
+the arithmetic of a row does not depend on blocks it does not select.  This
+is slow by design; it is the reference the HIP library is checked against.
+
+Method, as the pages state it:
+
+* Stage 0 (page "DashAttention and the year sparse attention became a
+  field", section "What alpha-entmax changes"): each block of keys gets a
+  summary; the learned summariser starts at zero, i.e. from mean pooling.
+  Here the summary is the mean of the block's keys.
+* Stage 1 (page "DashAttention: Making Sparse Attention Fully
+  Differentiable...", sections "Core Mechanism" and its pipeline figure):
+  coarse score q . summary for each block, then alpha-entmax gives sparse
+  block weights p.
+* Stage 2 (same sections): for the selected blocks, fine logits q . k plus
+  log p of the key's block, one softmax, weighted sum of V.
+* Gradients flow from Stage 2 through log p into the entmax and on to the
+  summaries (same sections; "What alpha-entmax changes").
+
+Readings taken where the pages are silent (each is restated in the design doc):
+
+* R1 entmax parameterisation u = (alpha-1) z, p = [u - tau]_+^(1/(alpha-1)).
+* R2 one joint softmax over all attended tokens with log p added to the logits.
+* R4 causal: the candidates of query i are the blocks strictly before its
+  own block; its own block is always attended under the causal mask with
+  log-prior 0.  Queries of block 0 attend only their own block.
+* R5 the summary is the exact mean of the block's keys, rounded once
+  (round-to-nearest-even) to the storage dtype of K.
+* R7 decode: the new token is the last cached token; the decode output is
+  row N-1 of a causal prefill over the cache.
+* R9 separate fine scale (logits) and coarse scale (block scores).
+* Backward treats the rounding of the summary to its storage dtype as the
+  identity (straight-through).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from .entmax import entmax, entmax_jvp
+
+
+@dataclass(frozen=True)
+class Params:
+    block: int = 64
+    alpha: float = 1.5
+    causal: bool = True
+    fine_scale: float | None = None  # default 1/sqrt(D)
+    coarse_scale: float | None = None  # default 1/sqrt(D)
+    storage: str = "bf16"  # dtype the summaries are stored in: bf16 | fp32 | fp64
+
+    def scales(self, D: int) -> tuple[float, float]:
+        sf = self.fine_scale if self.fine_scale is not None else 1.0 / np.sqrt(D)
+        sc = self.coarse_scale if self.coarse_scale is not None else 1.0 / np.sqrt(D)
+        return float(sf), float(sc)
+
+
+# ----------------------------------------------------------------------------- rounding
+
+
+def round_bf16(x):
+    """Round float64 values to the nearest bfloat16 value, ties to even, in one step.
+
+    bfloat16 keeps 8 significant bits.  With x = m * 2**e and 0.5 <= |m| < 1
+    (``frexp``), the rounded value is rint(m * 2**8) * 2**(e - 8), where
+    ``rint`` rounds half to even.  Rounding straight from float64 avoids the
+    double rounding of a float64 -> float32 -> bfloat16 chain.  Values here
+    are far from the bfloat16 overflow and subnormal ranges.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+
+
+def round_storage(x, storage: str):
+    if storage == "bf16":
+        return round_bf16(x)
+    if storage == "fp32":
+        return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    if storage == "fp64":
+        return np.asarray(x, dtype=np.float64)
+    raise ValueError(f"unknown storage {storage!r}")
+
+
+# ----------------------------------------------------------------------------- Stage 0
+
+
+def pool_blocks(k_head, block: int, storage: str):
+    """Stage 0: mean of each block's keys, rounded once to the storage dtype.
+
+    ``k_head`` is [T, D] (T a multiple of ``block``); returns [T/block, D].
+    The sum of 64 bfloat16 (or float32) values of ordinary magnitude is exact
+    in float64, so the mean is exact before the single rounding (R5).
+    """
+    k_head = np.asarray(k_head, dtype=np.float64)
+    T, D = k_head.shape
+    if T % block:
+        raise ValueError("T must be a multiple of the block size")
+    mean = k_head.reshape(T // block, block, D).sum(axis=1) / block
+    return round_storage(mean, storage)
+
+
+# ----------------------------------------------------------------------------- Stage 1
+
+
+def candidate_blocks(i: int, nb: int, block: int, causal: bool):
+    """Blocks query ``i`` scores in Stage 1: all blocks, or those before its own (R4)."""
+    return np.arange(i // block) if causal else np.arange(nb)
+
+
+def select_row(q_i, kbar, i: int, prm: Params, D: int):
+    """Stage 1 for one query row: coarse scores, alpha-entmax, support.
+
+    Returns a dict with the candidate block ids, z, p (over the candidates),
+    tau (u-units for alpha > 1, z-units for alpha = 1; NaN with no
+    candidates) and the boolean support.
+    """
+    _, sc = prm.scales(D)
+    nb = kbar.shape[0]
+    cand = candidate_blocks(i, nb, prm.block, prm.causal)
+    if cand.size == 0:
+        return dict(cand=cand, z=np.zeros(0), p=np.zeros(0), tau=np.nan,
+                    support=np.zeros(0, dtype=bool))
+    # Row-wise dot products, reduced along the contiguous feature axis, so
+    # each score depends only on its own summary.
+    z = sc * (kbar[cand] * q_i[None, :]).sum(axis=1)
+    p, tau, support = entmax(z, prm.alpha)
+    return dict(cand=cand, z=z, p=p, tau=tau, support=support)
+
+
+# ----------------------------------------------------------------------------- Stage 2
+
+
+def attend_row(q_i, k_head, v_head, i: int, sel, prm: Params, D: int):
+    """Stage 2 for one query row.
+
+    Attended tokens: every token of every selected candidate block (prior
+    log p_b) and, when causal, the tokens j <= i of the row's own block
+    (prior 0).  One softmax over logits fine_scale * q . k_j + prior_j, then
+    the weighted sum of V.  Returns (o, lse, ctx) where ctx holds what the
+    backward needs.
+    """
+    sf, _ = prm.scales(D)
+    blk = prm.block
+    chosen = sel["cand"][sel["support"]]
+    logp = np.log(sel["p"][sel["support"]])
+    idx_parts = [np.arange(b * blk, (b + 1) * blk) for b in chosen]
+    prior_parts = [np.full(blk, lp) for lp in logp]
+    if prm.causal:
+        start = (i // blk) * blk
+        idx_parts.append(np.arange(start, i + 1))
+        prior_parts.append(np.zeros(i + 1 - start))
+    idx = np.concatenate(idx_parts) if idx_parts else np.zeros(0, dtype=np.int64)
+    prior = np.concatenate(prior_parts) if prior_parts else np.zeros(0)
+    if idx.size == 0:
+        # Non-causal row whose support is empty cannot happen (entmax always
+        # selects at least one block); keep the shape honest anyway.
+        return np.zeros(D), -np.inf, dict(idx=idx, a=np.zeros(0), prior=prior,
+                                          chosen=chosen, logp=logp)
+    ks = k_head[idx]
+    logits = sf * (ks @ q_i) + prior
+    mx = logits.max()
+    w = np.exp(logits - mx)
+    den = w.sum()
+    a = w / den
+    o = a @ v_head[idx]
+    lse = mx + np.log(den)
+    return o, lse, dict(idx=idx, a=a, prior=prior, chosen=chosen, logp=logp)
+
+
+# ----------------------------------------------------------------------------- forward
+
+
+def _as64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def forward_rows(q, k, v, prm: Params, rows, kbar=None):
+    """Forward for selected rows only.
+
+    ``q, k, v``: [B, H, T, D]; ``rows``: iterable of (b, h, i).  Returns a
+    list of dicts (o, lse, tau, nsel, mask over all nb blocks, p over all nb
+    blocks).  ``kbar`` may be passed to avoid re-pooling ([B, H, nb, D]).
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    D = q.shape[-1]
+    nb = k.shape[2] // prm.block
+    cache = {}
+    out = []
+    for (b, h, i) in rows:
+        if kbar is not None:
+            kb = _as64(kbar[b, h])
+        else:
+            if (b, h) not in cache:
+                cache[(b, h)] = pool_blocks(k[b, h], prm.block, prm.storage)
+            kb = cache[(b, h)]
+        sel = select_row(q[b, h, i], kb, i, prm, D)
+        o, lse, _ = attend_row(q[b, h, i], k[b, h], v[b, h], i, sel, prm, D)
+        mask = np.zeros(nb, dtype=bool)
+        mask[sel["cand"][sel["support"]]] = True
+        pfull = np.zeros(nb)
+        pfull[sel["cand"]] = sel["p"]
+        out.append(dict(o=o, lse=lse, tau=sel["tau"], nsel=int(sel["support"].sum()),
+                        mask=mask, p=pfull, z=sel["z"], cand=sel["cand"]))
+    return out
+
+
+def forward(q, k, v, prm: Params):
+    """Full forward over every row: summaries, selection and attention.
+
+    Returns a dict of arrays: kbar [B,H,nb,D], tau [B,H,T], nsel [B,H,T],
+    mask [B,H,T,nb] (bool), p [B,H,T,nb], o [B,H,T,D], lse [B,H,T].
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, H, T, D = q.shape
+    nb = T // prm.block
+    kbar = np.zeros((B, H, nb, D))
+    tau = np.full((B, H, T), np.nan)
+    nsel = np.zeros((B, H, T), dtype=np.int64)
+    mask = np.zeros((B, H, T, nb), dtype=bool)
+    p = np.zeros((B, H, T, nb))
+    o = np.zeros((B, H, T, D))
+    lse = np.zeros((B, H, T))
+    for b in range(B):
+        for h in range(H):
+            kb = pool_blocks(k[b, h], prm.block, prm.storage)
+            kbar[b, h] = kb
+            for i in range(T):
+                sel = select_row(q[b, h, i], kb, i, prm, D)
+                oi, li, _ = attend_row(q[b, h, i], k[b, h], v[b, h], i, sel, prm, D)
+                tau[b, h, i] = sel["tau"]
+                nsel[b, h, i] = int(sel["support"].sum())
+                mask[b, h, i, sel["cand"][sel["support"]]] = True
+                p[b, h, i, sel["cand"]] = sel["p"]
+                o[b, h, i] = oi
+                lse[b, h, i] = li
+    return dict(kbar=kbar, tau=tau, nsel=nsel, mask=mask, p=p, o=o, lse=lse)
+
+
+# ----------------------------------------------------------------------------- backward
+
+
+def backward(q, k, v, dout, prm: Params):
+    """Gradients of the scalar <dout, O> with respect to q, k, v and the summaries.
+
+    Per row (notation of the forward): a = softmax weights over the attended
+    tokens, D_i = dout_i . o_i,
+
+        dl_j   = a_j (dout_i . v_j - D_i)           (gradient of the logit)
+        dv_j  += a_j dout_i
+        dq_i  += fine_scale * sum_j dl_j k_j
+        dk_j  += fine_scale * dl_j q_i
+        G_b    = sum_{j in block b} dl_j              (gradient of log p_b)
+
+    then through log p (dp_b = G_b / p_b) and alpha-entmax
+    (:func:`oracle.entmax.entmax_jvp`) to dz, and through
+    z_b = coarse_scale * q_i . kbar_b:
+
+        dq_i    += coarse_scale * sum_b dz_b kbar_b
+        dkbar_b += coarse_scale * dz_b q_i
+
+    Finally mean pooling sends dkbar_b / block to every key of block b.
+    Returns dict(dq, dk, dv, dkbar) (dk includes the pooling path).
+    """
+    q, k, v, dout = _as64(q), _as64(k), _as64(v), _as64(dout)
+    B, H, T, D = q.shape
+    blk = prm.block
+    nb = T // blk
+    sf, sc = prm.scales(D)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dkbar = np.zeros((B, H, nb, D))
+    for b in range(B):
+        for h in range(H):
+            kb = pool_blocks(k[b, h], blk, prm.storage)
+            kh, vh = k[b, h], v[b, h]
+            for i in range(T):
+                qi = q[b, h, i]
+                sel = select_row(qi, kb, i, prm, D)
+                oi, _, ctx = attend_row(qi, kh, vh, i, sel, prm, D)
+                idx, a = ctx["idx"], ctx["a"]
+                if idx.size == 0:
+                    continue
+                gi = dout[b, h, i]
+                Di = gi @ oi
+                dl = a * (vh[idx] @ gi - Di)
+                dv[b, h, idx] += np.outer(a, gi)
+                dq[b, h, i] += sf * (dl @ kh[idx])
+                dk[b, h, idx] += sf * np.outer(dl, qi)
+                chosen = ctx["chosen"]
+                if chosen.size == 0:
+                    continue
+                # G over the selected candidate blocks (the causal own block
+                # carries prior 0 and no gradient into Stage 1).
+                G = dl[: chosen.size * blk].reshape(chosen.size, blk).sum(axis=1)
+                pc = sel["p"]
+                sup = sel["support"]
+                g = np.zeros_like(pc)
+                g[sup] = G / pc[sup]
+                dz = entmax_jvp(pc, g, prm.alpha)
+                cand = sel["cand"]
+                dq[b, h, i] += sc * (dz @ kb[cand])
+                dkbar[b, h, cand] += sc * np.outer(dz, qi)
+            dk[b, h] += np.repeat(dkbar[b, h], blk, axis=0) / blk
+    return dict(dq=dq, dk=dk, dv=dv, dkbar=dkbar)
+
+
+# ----------------------------------------------------------------------------- decode
+
+
+def decode(q, kc, vc, prm: Params, kbar=None):
+    """Decode: one new query per (sequence, head) against a KV cache.
+
+    ``q``: [S, H, D]; ``kc, vc``: [S, H, N, D] with the new token already
+    appended at position N-1 (R7).  The output equals row N-1 of a causal
+    prefill over the cache: candidates are blocks 0..N/block-2, the last
+    block is attended causally (all of it) with prior 0.  ``kbar`` may be
+    given ([S, H, N/block, D]); by default it is pooled here.
+    Returns dict(o [S,H,D], lse [S,H], nsel [S,H], mask [S,H,nb], tau [S,H]).
+    """
+    if not prm.causal:
+        raise ValueError("decode is defined as the last row of a causal prefill")
+    q, kc, vc = _as64(q), _as64(kc), _as64(vc)
+    S, H, N, D = kc.shape
+    nb = N // prm.block
+    o = np.zeros((S, H, D))
+    lse = np.zeros((S, H))
+    nsel = np.zeros((S, H), dtype=np.int64)
+    mask = np.zeros((S, H, nb), dtype=bool)
+    tau = np.zeros((S, H))
+    for s in range(S):
+        for h in range(H):
+            kb = _as64(kbar[s, h]) if kbar is not None else pool_blocks(kc[s, h], prm.block, prm.storage)
+            sel = select_row(q[s, h], kb, N - 1, prm, D)
+            oi, li, _ = attend_row(q[s, h], kc[s, h], vc[s, h], N - 1, sel, prm, D)
+            o[s, h], lse[s, h], tau[s, h] = oi, li, sel["tau"]
+            nsel[s, h] = int(sel["support"].sum())
+            mask[s, h, sel["cand"][sel["support"]]] = True
+    return dict(o=o, lse=lse, nsel=nsel, mask=mask, tau=tau)
