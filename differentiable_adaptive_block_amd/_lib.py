@@ -1,0 +1,143 @@
+"""ctypes binding of libdash.so (argument marshalling only).
+
+Every entry point mirrors a declaration of include/dash.h.  Nothing here
+computes any part of the method; when the library is missing the import of
+this module fails loudly.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdash.so")
+
+DASH_OK, DASH_EINVAL, DASH_EUNSUPPORTED, DASH_EWORKSPACE, DASH_EHIP = range(5)
+DASH_F32, DASH_BF16 = 0, 1
+STATUS_NAMES = {0: "DASH_OK", 1: "DASH_EINVAL", 2: "DASH_EUNSUPPORTED", 3: "DASH_EWORKSPACE", 4: "DASH_EHIP"}
+
+EXPORTS = [
+    "dash_query_tile",
+    "dash_sel_sizes",
+    "dash_fwd_workspace_bytes",
+    "dash_bwd_workspace_bytes",
+    "dash_pool",
+    "dash_fwd",
+    "dash_bwd",
+    "dash_decode_workspace_bytes",
+    "dash_decode",
+    "dash_last_error",
+]
+
+
+class DashParams(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("block", ctypes.c_int32), ("alpha", ctypes.c_float), ("causal", ctypes.c_int32),
+        ("fine_scale", ctypes.c_float), ("coarse_scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+    ]
+
+
+class DashSel(ctypes.Structure):
+    _fields_ = [
+        ("tau", ctypes.c_void_p), ("lognorm", ctypes.c_void_p), ("nsel", ctypes.c_void_p),
+        ("mask", ctypes.c_void_p), ("tile_cnt", ctypes.c_void_p), ("tile_blk", ctypes.c_void_p),
+        ("tile_bits", ctypes.c_void_p),
+    ]
+
+
+class DashDecodeParams(ctypes.Structure):
+    _fields_ = [
+        ("S", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("block", ctypes.c_int32), ("alpha", ctypes.c_float), ("fine_scale", ctypes.c_float),
+        ("coarse_scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+    ]
+
+
+class DashError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libdash.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m differentiable_adaptive_block_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    vp = ctypes.c_void_p
+    L.dash_query_tile.restype = ctypes.c_int32
+    L.dash_query_tile.argtypes = []
+    L.dash_sel_sizes.restype = ctypes.c_int
+    L.dash_sel_sizes.argtypes = [P(DashParams), P(ctypes.c_size_t)]
+    L.dash_fwd_workspace_bytes.restype = ctypes.c_size_t
+    L.dash_fwd_workspace_bytes.argtypes = [P(DashParams)]
+    L.dash_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.dash_bwd_workspace_bytes.argtypes = [P(DashParams)]
+    L.dash_pool.restype = ctypes.c_int
+    L.dash_pool.argtypes = [P(DashParams), vp, vp, vp]
+    L.dash_fwd.restype = ctypes.c_int
+    L.dash_fwd.argtypes = [P(DashParams), vp, vp, vp, vp, vp, vp, P(DashSel), vp, ctypes.c_size_t, vp]
+    L.dash_bwd.restype = ctypes.c_int
+    L.dash_bwd.argtypes = [P(DashParams), vp, vp, vp, vp, vp, vp, vp, P(DashSel), vp, vp, vp, vp, vp,
+                           ctypes.c_size_t, vp]
+    L.dash_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.dash_decode_workspace_bytes.argtypes = [P(DashDecodeParams)]
+    L.dash_decode.restype = ctypes.c_int
+    L.dash_decode.argtypes = [P(DashDecodeParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.dash_last_error.restype = ctypes.c_char_p
+    L.dash_last_error.argtypes = []
+    _lib = L
+    return L
+
+
+def check(status: int) -> None:
+    if status != DASH_OK:
+        raise DashError(status, load().dash_last_error().decode())
+
+
+def query_tile() -> int:
+    return int(load().dash_query_tile())
+
+
+def sel_sizes(p: DashParams):
+    out = (ctypes.c_size_t * 7)()
+    check(load().dash_sel_sizes(ctypes.byref(p), out))
+    return list(out)
+
+
+def fwd_workspace_bytes(p: DashParams) -> int:
+    return int(load().dash_fwd_workspace_bytes(ctypes.byref(p)))
+
+
+def bwd_workspace_bytes(p: DashParams) -> int:
+    return int(load().dash_bwd_workspace_bytes(ctypes.byref(p)))
+
+
+def decode_workspace_bytes(p: DashDecodeParams) -> int:
+    return int(load().dash_decode_workspace_bytes(ctypes.byref(p)))
+
+
+def pool(p: DashParams, k, kbar, stream) -> None:
+    check(load().dash_pool(ctypes.byref(p), k, kbar, stream))
+
+
+def fwd(p: DashParams, q, k, v, o, lse, kbar, sel: DashSel, ws, ws_bytes, stream) -> None:
+    check(load().dash_fwd(ctypes.byref(p), q, k, v, o, lse, kbar, ctypes.byref(sel), ws, ws_bytes, stream))
+
+
+def bwd(p: DashParams, q, k, v, o, lse, dout, kbar, sel: DashSel, dq, dk, dv, dkbar, ws, ws_bytes, stream) -> None:
+    check(load().dash_bwd(ctypes.byref(p), q, k, v, o, lse, dout, kbar, ctypes.byref(sel), dq, dk, dv, dkbar, ws,
+                          ws_bytes, stream))
+
+
+def decode(p: DashDecodeParams, q, kc, vc, kbar, o, lse, nsel, tau, ws, ws_bytes, stream) -> None:
+    check(load().dash_decode(ctypes.byref(p), q, kc, vc, kbar, o, lse, nsel, tau, ws, ws_bytes, stream))

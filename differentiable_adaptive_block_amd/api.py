@@ -1,0 +1,194 @@
+"""PyTorch-facing entry points of the DashAttention hot path.
+
+PyTorch provides device memory and the current HIP stream; every step of the
+method runs in libdash.so (see include/dash.h).  Tensors must live on a ROCm
+device; there is no CPU fallback.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+
+BLOCK = 64
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _lib.DASH_BF16
+    if t.dtype == torch.float32:
+        return _lib.DASH_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require(t: torch.Tensor, name: str, shape=None, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def make_params(q: torch.Tensor, alpha: float, causal: bool, fine_scale=None, coarse_scale=None):
+    B, H, T, D = q.shape
+    p = _lib.DashParams()
+    p.B, p.H, p.T, p.D, p.block = B, H, T, D, BLOCK
+    p.alpha = float(alpha)
+    p.causal = int(bool(causal))
+    p.fine_scale = float(fine_scale if fine_scale is not None else 1.0 / math.sqrt(D))
+    p.coarse_scale = float(coarse_scale if coarse_scale is not None else 1.0 / math.sqrt(D))
+    p.dtype = _dtype_code(q)
+    return p
+
+
+@dataclass
+class Selection:
+    """Stage-1 outputs (device tensors), see dash_sel in include/dash.h."""
+    tau: torch.Tensor
+    lognorm: torch.Tensor
+    nsel: torch.Tensor | None
+    mask: torch.Tensor | None
+    tile_cnt: torch.Tensor
+    tile_blk: torch.Tensor
+    tile_bits: torch.Tensor
+
+    def as_c(self) -> _lib.DashSel:
+        s = _lib.DashSel()
+        s.tau, s.lognorm = _ptr(self.tau), _ptr(self.lognorm)
+        s.nsel, s.mask = _ptr(self.nsel), _ptr(self.mask)
+        s.tile_cnt, s.tile_blk, s.tile_bits = _ptr(self.tile_cnt), _ptr(self.tile_blk), _ptr(self.tile_bits)
+        return s
+
+
+def alloc_selection(p: _lib.DashParams, device, want_mask: bool = True) -> Selection:
+    n = _lib.sel_sizes(p)
+    B, H, T = p.B, p.H, p.T
+    nb = T // BLOCK
+    nbw = (nb + 31) // 32
+    ntile = n[4] // (B * H)
+    e = lambda m, dt: torch.empty(m, dtype=dt, device=device)  # noqa: E731
+    return Selection(
+        tau=e(n[0], torch.float32).view(B, H, T),
+        lognorm=e(n[1], torch.float32).view(B, H, T),
+        nsel=e(n[2], torch.int32).view(B, H, T) if want_mask else None,
+        # the library writes 32-bit words; torch has no uint32 arithmetic, so int32 storage
+        mask=e(n[3], torch.int32).view(B, H, T, nbw) if want_mask else None,
+        tile_cnt=e(n[4], torch.int32).view(B, H, ntile),
+        tile_blk=e(n[5], torch.int32).view(B, H, ntile, nb),
+        tile_bits=e(n[6], torch.int32).view(B, H, ntile, nbw),
+    )
+
+
+def pool(k: torch.Tensor) -> torch.Tensor:
+    """Stage 0: block summaries kbar [B,H,T/64,D] of k [B,H,T,D]."""
+    _require(k, "k")
+    p = make_params(k, 1.5, True)
+    kbar = torch.empty((p.B, p.H, p.T // BLOCK, p.D), dtype=k.dtype, device=k.device)
+    _lib.pool(p, _ptr(k), _ptr(kbar), _stream(k.device))
+    return kbar
+
+
+def forward(q, k, v, alpha=1.5, causal=True, fine_scale=None, coarse_scale=None, want_mask=True):
+    """Stages 0-2.  Returns dict(o, lse, kbar, sel, params)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(t, name, q.shape, q.dtype)
+    p = make_params(q, alpha, causal, fine_scale, coarse_scale)
+    dev = q.device
+    o = torch.empty_like(q)
+    lse = torch.empty((p.B, p.H, p.T), dtype=torch.float32, device=dev)
+    kbar = torch.empty((p.B, p.H, p.T // BLOCK, p.D), dtype=q.dtype, device=dev)
+    sel = alloc_selection(p, dev, want_mask)
+    wsb = _lib.fwd_workspace_bytes(p)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    csel = sel.as_c()
+    _lib.fwd(p, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(kbar), csel, _ptr(ws), wsb, _stream(dev))
+    return dict(o=o, lse=lse, kbar=kbar, sel=sel, params=p)
+
+
+def backward(q, k, v, o, lse, dout, kbar, sel: Selection, p: _lib.DashParams):
+    """Gradients of <dout, O>: dict(dq, dk, dv, dkbar)."""
+    _require(dout, "dout", q.shape, q.dtype)
+    dev = q.device
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dkbar = torch.empty((p.B, p.H, p.T // BLOCK, p.D), dtype=torch.float32, device=dev)
+    wsb = _lib.bwd_workspace_bytes(p)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    _lib.bwd(p, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(kbar), sel.as_c(), _ptr(dq),
+             _ptr(dk), _ptr(dv), _ptr(dkbar), _ptr(ws), wsb, _stream(dev))
+    return dict(dq=dq, dk=dk, dv=dv, dkbar=dkbar)
+
+
+def make_decode_params(q, kc, alpha, fine_scale=None, coarse_scale=None):
+    S, H, N, D = kc.shape
+    p = _lib.DashDecodeParams()
+    p.S, p.H, p.N, p.D, p.block = S, H, N, D, BLOCK
+    p.alpha = float(alpha)
+    p.fine_scale = float(fine_scale if fine_scale is not None else 1.0 / math.sqrt(D))
+    p.coarse_scale = float(coarse_scale if coarse_scale is not None else 1.0 / math.sqrt(D))
+    p.dtype = _dtype_code(q)
+    return p
+
+
+class DecodeBuffers:
+    """Outputs and workspace of one decode step, allocated once and reused."""
+
+    def __init__(self, p: _lib.DashDecodeParams, dtype, device):
+        self.o = torch.empty((p.S, p.H, p.D), dtype=dtype, device=device)
+        self.lse = torch.empty((p.S, p.H), dtype=torch.float32, device=device)
+        self.nsel = torch.empty((p.S, p.H), dtype=torch.int32, device=device)
+        self.tau = torch.empty((p.S, p.H), dtype=torch.float32, device=device)
+        self.ws_bytes = _lib.decode_workspace_bytes(p)
+        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=device)
+
+
+def decode(q, kc, vc, kbar, alpha=1.5, fine_scale=None, coarse_scale=None, bufs: DecodeBuffers | None = None):
+    """One decode step: q [S,H,D] against caches kc, vc [S,H,N,D] and summaries kbar."""
+    S, H, N, D = kc.shape
+    _require(q, "q", (S, H, D), kc.dtype)
+    _require(vc, "vc", kc.shape, kc.dtype)
+    _require(kbar, "kbar", (S, H, N // BLOCK, D), kc.dtype)
+    p = make_decode_params(q, kc, alpha, fine_scale, coarse_scale)
+    if bufs is None:
+        bufs = DecodeBuffers(p, q.dtype, q.device)
+    _lib.decode(p, _ptr(q), _ptr(kc), _ptr(vc), _ptr(kbar), _ptr(bufs.o), _ptr(bufs.lse), _ptr(bufs.nsel),
+                _ptr(bufs.tau), _ptr(bufs.ws), bufs.ws_bytes, _stream(q.device))
+    return dict(o=bufs.o, lse=bufs.lse, nsel=bufs.nsel, tau=bufs.tau)
+
+
+class DashAttentionFn(torch.autograd.Function):
+    """DashAttention as an autograd function (forward: Stages 0-2; backward through all of them)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, alpha, causal, fine_scale, coarse_scale):
+        r = forward(q, k, v, alpha, causal, fine_scale, coarse_scale, want_mask=False)
+        ctx.save_for_backward(q, k, v, r["o"], r["lse"], r["kbar"])
+        ctx.sel = r["sel"]
+        ctx.p = r["params"]
+        return r["o"]
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, o, lse, kbar = ctx.saved_tensors
+        g = backward(q, k, v, o, lse, dout.contiguous(), kbar, ctx.sel, ctx.p)
+        return g["dq"], g["dk"], g["dv"], None, None, None, None
+
+
+def dash_attention(q, k, v, alpha=1.5, causal=True, fine_scale=None, coarse_scale=None):
+    return DashAttentionFn.apply(q, k, v, alpha, causal, fine_scale, coarse_scale)

@@ -1,0 +1,296 @@
+// C ABI of the DashAttention hot path: host-side validation and launches.
+// The declarations, argument meaning, layouts and error behaviour are in
+// include/dash.h.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "dash.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+dash_status fail(dash_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+dash_status fail(dash_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+dash_status hip_fail(hipError_t e, const char* where) {
+  return fail(DASH_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool ok_ptr(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool ok_opt(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool finite_pos(float x) { return std::isfinite(x) && x > 0.f; }
+
+CoarseArith make_ca(float alpha, float coarse_scale) {
+  CoarseArith ca;
+  ca.coarse_scale = coarse_scale;
+  ca.softmax = alpha == 1.0f;
+  ca.am1 = alpha - 1.0f;
+  ca.m = ca.softmax ? 1.0f : 1.0f / (alpha - 1.0f);
+  return ca;
+}
+
+dash_status check_common(int D, int block, float alpha, float fs, float cs, int dtype) {
+  if (!(alpha >= 1.0f && alpha <= 2.0f)) return fail(DASH_EINVAL, "alpha must lie in [1, 2] (got %g)", alpha);
+  if (!finite_pos(fs) || !finite_pos(cs)) return fail(DASH_EINVAL, "scales must be finite and positive");
+  if (dtype != DASH_F32 && dtype != DASH_BF16) return fail(DASH_EINVAL, "unknown dtype %d", dtype);
+  if (block != DASH_BLOCK) return fail(DASH_EUNSUPPORTED, "block must be 64 (got %d)", block);
+  if (D != 64 && D != 128) return fail(DASH_EUNSUPPORTED, "head dim must be 64 or 128 (got %d)", D);
+  return DASH_OK;
+}
+
+dash_status check_params(const dash_params* p) {
+  if (!p) return fail(DASH_EINVAL, "null params");
+  if (p->B < 1 || p->H < 1) return fail(DASH_EINVAL, "B and H must be >= 1");
+  if (p->T < DASH_BLOCK || p->T % DASH_BLOCK) return fail(DASH_EINVAL, "T must be a positive multiple of 64 (got %d)", p->T);
+  if (p->causal != 0 && p->causal != 1) return fail(DASH_EINVAL, "causal must be 0 or 1");
+  dash_status s = check_common(p->D, p->block, p->alpha, p->fine_scale, p->coarse_scale, p->dtype);
+  if (s != DASH_OK) return s;
+  if (p->T / DASH_BLOCK > DASH_MAX_NB) return fail(DASH_EUNSUPPORTED, "T above %d is not built", DASH_MAX_NB * DASH_BLOCK);
+  return DASH_OK;
+}
+
+int ntile_of(int T) { return (T + DASH_QTILE - 1) / DASH_QTILE; }
+int nbw_of(int nb) { return (nb + 31) / 32; }
+
+dash_status check_sel(const dash_sel* sel, bool need_bits) {
+  if (!sel) return fail(DASH_EINVAL, "null selection struct");
+  if (!ok_ptr(sel->tau) || !ok_ptr(sel->lognorm) || !ok_ptr(sel->tile_cnt) || !ok_ptr(sel->tile_blk) ||
+      !ok_ptr(sel->tile_bits))
+    return fail(DASH_EINVAL, "selection buffers tau/lognorm/tile_cnt/tile_blk/tile_bits must be non-null and 16-byte aligned");
+  if (!ok_opt(sel->nsel) || !ok_opt(sel->mask)) return fail(DASH_EINVAL, "nsel/mask must be 16-byte aligned");
+  (void)need_bits;
+  return DASH_OK;
+}
+
+size_t bwd_ws_layout(const dash_params* p, size_t off[4]) {
+  const size_t BH = (size_t)p->B * p->H, T = p->T, D = p->D, nb = T / DASH_BLOCK, nt = ntile_of(p->T);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o += (bytes + 255) & ~size_t(255); return r; };
+  off[0] = take(BH * T * sizeof(float));               // delta
+  off[1] = take(BH * T * D * sizeof(float));           // dq accumulator
+  off[2] = take(BH * nt * nb * DASH_QTILE * sizeof(float));  // G
+  off[3] = take(BH * nt * nb * DASH_QTILE * sizeof(float));  // prior
+  return o;
+}
+
+size_t decode_ws_layout(const dash_decode_params* p, size_t off[6], int* nsplit, int* chunk) {
+  const size_t SH = (size_t)p->S * p->H, nb = p->N / DASH_BLOCK, D = p->D;
+  const int ch = 8;  // blocks per split-KV work item
+  const int ns = (int)((nb + ch - 1) / ch);
+  if (nsplit) *nsplit = ns;
+  if (chunk) *chunk = ch;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o += (bytes + 255) & ~size_t(255); return r; };
+  off[0] = take(SH * nb * sizeof(float));          // u scores
+  off[1] = take(SH * 2 * sizeof(float));           // tau, lognorm
+  off[2] = take(SH * sizeof(int));                 // list length
+  off[3] = take(SH * nb * sizeof(int));            // list
+  off[4] = take(SH * nb * sizeof(float));          // log2 priors
+  off[5] = take(SH * ns * (D + 2) * sizeof(float));  // partials
+  return o;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t dash_query_tile(void) { return DASH_QTILE; }
+
+const char* dash_last_error(void) { return g_err.c_str(); }
+
+dash_status dash_sel_sizes(const dash_params* p, size_t out[7]) {
+  dash_status s = check_params(p);
+  if (s != DASH_OK) return s;
+  if (!out) return fail(DASH_EINVAL, "null output array");
+  const size_t BH = (size_t)p->B * p->H, T = p->T, nb = T / DASH_BLOCK, nbw = nbw_of((int)nb), nt = ntile_of(p->T);
+  out[0] = BH * T;
+  out[1] = BH * T;
+  out[2] = BH * T;
+  out[3] = BH * T * nbw;
+  out[4] = BH * nt;
+  out[5] = BH * nt * nb;
+  out[6] = BH * nt * nbw;
+  return DASH_OK;
+}
+
+size_t dash_fwd_workspace_bytes(const dash_params* p) {
+  (void)p;
+  return 0;
+}
+
+size_t dash_bwd_workspace_bytes(const dash_params* p) {
+  if (check_params(p) != DASH_OK) return 0;
+  size_t off[4];
+  return bwd_ws_layout(p, off);
+}
+
+size_t dash_decode_workspace_bytes(const dash_decode_params* p) {
+  if (!p || p->S < 1 || p->H < 1 || p->N < DASH_BLOCK || p->N % DASH_BLOCK) return 0;
+  size_t off[6];
+  return decode_ws_layout(p, off, nullptr, nullptr);
+}
+
+dash_status dash_pool(const dash_params* p, const void* k, void* kbar, void* stream) {
+  dash_status s = check_params(p);
+  if (s != DASH_OK) return s;
+  if (!ok_ptr(k) || !ok_ptr(kbar)) return fail(DASH_EINVAL, "k and kbar must be non-null and 16-byte aligned");
+  hipError_t e = launch_pool(k, kbar, p->B * p->H, p->T, p->D, p->dtype, (hipStream_t)stream);
+  return e == hipSuccess ? DASH_OK : hip_fail(e, "pool");
+}
+
+dash_status dash_fwd(const dash_params* p, const void* q, const void* k, const void* v, void* o, float* lse,
+                     void* kbar, const dash_sel* sel, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  dash_status s = check_params(p);
+  if (s != DASH_OK) return s;
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(lse) || !ok_ptr(kbar))
+    return fail(DASH_EINVAL, "q, k, v, o, lse and kbar must be non-null and 16-byte aligned");
+  if ((s = check_sel(sel, true)) != DASH_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  const int BH = p->B * p->H;
+  const int nb = p->T / DASH_BLOCK;
+  const CoarseArith ca = make_ca(p->alpha, p->coarse_scale);
+  hipError_t e;
+  if ((e = launch_pool(k, kbar, BH, p->T, p->D, p->dtype, st)) != hipSuccess) return hip_fail(e, "pool");
+  if ((e = launch_fill_u32(sel->tile_bits, (size_t)BH * ntile_of(p->T) * nbw_of(nb), 0u, st)) != hipSuccess)
+    return hip_fail(e, "clear tile bits");
+  SelectArgs sa;
+  sa.q = q;
+  sa.kbar = kbar;
+  sa.T = p->T;
+  sa.D = p->D;
+  sa.causal = p->causal;
+  sa.ca = ca;
+  sa.tau = sel->tau;
+  sa.lognorm = sel->lognorm;
+  sa.nsel = sel->nsel;
+  sa.mask = sel->mask;
+  sa.tile_bits = sel->tile_bits;
+  if ((e = launch_select(sa, BH, p->dtype, st)) != hipSuccess) return hip_fail(e, "select");
+  if ((e = launch_tile_lists(sel->tile_bits, sel->tile_cnt, sel->tile_blk, BH, p->T, p->causal, st)) != hipSuccess)
+    return hip_fail(e, "tile lists");
+  FwdArgs fa;
+  fa.q = q;
+  fa.k = k;
+  fa.v = v;
+  fa.kbar = kbar;
+  fa.o = o;
+  fa.lse = lse;
+  fa.tau = sel->tau;
+  fa.lognorm = sel->lognorm;
+  fa.tile_cnt = sel->tile_cnt;
+  fa.tile_blk = sel->tile_blk;
+  fa.BH = BH;
+  fa.T = p->T;
+  fa.D = p->D;
+  fa.causal = p->causal;
+  fa.fine_scale = p->fine_scale;
+  fa.ca = ca;
+  if ((e = launch_fwd(fa, p->dtype, st)) != hipSuccess) return hip_fail(e, "stage 2 forward");
+  return DASH_OK;
+}
+
+dash_status dash_bwd(const dash_params* p, const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dout, const void* kbar, const dash_sel* sel, void* dq, void* dk,
+                     void* dv, float* dkbar, void* workspace, size_t workspace_bytes, void* stream) {
+  dash_status s = check_params(p);
+  if (s != DASH_OK) return s;
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(lse) || !ok_ptr(dout) || !ok_ptr(kbar) ||
+      !ok_ptr(dq) || !ok_ptr(dk) || !ok_ptr(dv) || !ok_ptr(dkbar))
+    return fail(DASH_EINVAL, "tensor pointers must be non-null and 16-byte aligned");
+  if ((s = check_sel(sel, true)) != DASH_OK) return s;
+  size_t off[4];
+  const size_t need = bwd_ws_layout(p, off);
+  if (workspace_bytes < need) return fail(DASH_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (!ok_ptr(workspace)) return fail(DASH_EINVAL, "workspace must be non-null and 16-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  BwdArgs ba;
+  ba.q = q;
+  ba.k = k;
+  ba.v = v;
+  ba.o = o;
+  ba.lse = lse;
+  ba.dout = dout;
+  ba.kbar = kbar;
+  ba.tau = sel->tau;
+  ba.lognorm = sel->lognorm;
+  ba.tile_cnt = sel->tile_cnt;
+  ba.tile_blk = sel->tile_blk;
+  ba.tile_bits = sel->tile_bits;
+  ba.dq = dq;
+  ba.dk = dk;
+  ba.dv = dv;
+  ba.dkbar = dkbar;
+  ba.delta = reinterpret_cast<float*>(ws + off[0]);
+  ba.dq_acc = reinterpret_cast<float*>(ws + off[1]);
+  ba.gbuf = reinterpret_cast<float*>(ws + off[2]);
+  ba.pbuf = reinterpret_cast<float*>(ws + off[3]);
+  ba.BH = p->B * p->H;
+  ba.T = p->T;
+  ba.D = p->D;
+  ba.causal = p->causal;
+  ba.fine_scale = p->fine_scale;
+  ba.ca = make_ca(p->alpha, p->coarse_scale);
+  hipError_t e = launch_bwd(ba, p->dtype, (hipStream_t)stream);
+  return e == hipSuccess ? DASH_OK : hip_fail(e, "backward");
+}
+
+dash_status dash_decode(const dash_decode_params* p, const void* q, const void* kc, const void* vc,
+                        const void* kbar, void* o, float* lse, int32_t* nsel, float* tau, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (!p) return fail(DASH_EINVAL, "null params");
+  if (p->S < 1 || p->H < 1) return fail(DASH_EINVAL, "S and H must be >= 1");
+  if (p->N < DASH_BLOCK || p->N % DASH_BLOCK) return fail(DASH_EINVAL, "N must be a positive multiple of 64 (got %d)", p->N);
+  dash_status s = check_common(p->D, p->block, p->alpha, p->fine_scale, p->coarse_scale, p->dtype);
+  if (s != DASH_OK) return s;
+  if (p->N / DASH_BLOCK > 4096) return fail(DASH_EUNSUPPORTED, "cache above 262144 tokens is not built");
+  if (!ok_ptr(q) || !ok_ptr(kc) || !ok_ptr(vc) || !ok_ptr(kbar) || !ok_ptr(o))
+    return fail(DASH_EINVAL, "q, kc, vc, kbar and o must be non-null and 16-byte aligned");
+  if (!ok_opt(lse) || !ok_opt(nsel) || !ok_opt(tau)) return fail(DASH_EINVAL, "lse/nsel/tau must be 16-byte aligned");
+  size_t off[6];
+  int nsplit = 0, chunk = 0;
+  const size_t need = decode_ws_layout(p, off, &nsplit, &chunk);
+  if (workspace_bytes < need) return fail(DASH_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (!ok_ptr(workspace)) return fail(DASH_EINVAL, "workspace must be non-null and 16-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  DecodeArgs da;
+  da.q = q;
+  da.kc = kc;
+  da.vc = vc;
+  da.kbar = kbar;
+  da.o = o;
+  da.lse = lse;
+  da.nsel = nsel;
+  da.tau_out = tau;
+  da.zrow = reinterpret_cast<float*>(ws + off[0]);
+  da.rowstat = reinterpret_cast<float*>(ws + off[1]);
+  da.sel_cnt = reinterpret_cast<int*>(ws + off[2]);
+  da.sel_blk = reinterpret_cast<int*>(ws + off[3]);
+  da.sel_lp = reinterpret_cast<float*>(ws + off[4]);
+  da.part = reinterpret_cast<float*>(ws + off[5]);
+  da.SH = p->S * p->H;
+  da.N = p->N;
+  da.D = p->D;
+  da.nsplit = nsplit;
+  da.chunk = chunk;
+  da.fine_scale = p->fine_scale;
+  da.ca = make_ca(p->alpha, p->coarse_scale);
+  hipError_t e = launch_decode(da, p->dtype, (hipStream_t)stream);
+  return e == hipSuccess ? DASH_OK : hip_fail(e, "decode");
+}
+
+}  // extern "C"

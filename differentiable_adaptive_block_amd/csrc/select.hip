@@ -1,0 +1,284 @@
+// Stage 0 (block pooling) and Stage 1 (block scores + alpha-entmax + tile lists).
+//
+// Stage 0: the pages' summariser starts from mean pooling ("What
+// alpha-entmax changes", montana-research page).  Stage 1: coarse scores
+// q . kbar and alpha-entmax over them ("Core Mechanism", alanhou.org page).
+#include "kernels.h"
+#include "entmax.h"
+
+// ---------------------------------------------------------------------------- Stage 0
+
+// kbar[bh][b][d] = mean of k[bh][64 b + r][d] over r, summed in fp64 (exact for
+// bf16 keys and for fp32 keys of ordinary magnitude), divided by 64 (exact)
+// and rounded once to the storage type.  grid (nb, BH), 64 threads.
+template <typename T>
+__global__ __launch_bounds__(64) void pool_kernel(const T* __restrict__ k, T* __restrict__ kbar, int T_, int D) {
+  const int b = blockIdx.x;
+  const size_t bh = blockIdx.y;
+  const int nb = T_ / DASH_BLOCK;
+  const T* src = k + (bh * T_ + (size_t)b * DASH_BLOCK) * D;
+  T* dst = kbar + (bh * nb + b) * D;
+  for (int c = threadIdx.x; c < D; c += 64) {
+    double acc = 0.0;
+    for (int r = 0; r < DASH_BLOCK; ++r) acc += to_d<T>(src[(size_t)r * D + c]);
+    double mean = acc * (1.0 / DASH_BLOCK);
+    if constexpr (sizeof(T) == 2) dst[c] = d2bf(mean);
+    else dst[c] = __double2float_rn(mean);
+  }
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+// ---------------------------------------------------------------------------- Stage 1 outputs
+
+// Writes tau / lognorm / nsel / mask for one row (lane 0 writes the scalars)
+// and returns nothing; `uni` receives the row's selected bits (OR).
+template <int NPL>
+__device__ __forceinline__ void write_row_selection(const SelectArgs& a, size_t row_g, const float (&u)[NPL],
+                                                    int nc, const EntmaxOut& e, const CoarseArith& ca,
+                                                    uint32_t* uni_lds, uint32_t* tile_bits_g) {
+  const int l = lane_id();
+  const int nbw = (a.T / DASH_BLOCK + 31) / 32;
+  if (l == 0) {
+    a.tau[row_g] = e.tau;
+    a.lognorm[row_g] = e.lognorm;
+    if (a.nsel) a.nsel[row_g] = e.nsel;
+  }
+#pragma unroll
+  for (int k = 0; k < NPL; ++k) {
+    const int idx = l + 64 * k;
+    unsigned long long bal = __ballot(idx < nc && ca.selected(u[k], e.tau));
+    const uint32_t lo = (uint32_t)bal, hi = (uint32_t)(bal >> 32);
+    if (l == 0) {
+      if (2 * k < nbw) {
+        if (a.mask) a.mask[row_g * nbw + 2 * k] = lo;
+        if (lo) {
+          if (uni_lds) atomicOr(&uni_lds[2 * k], lo);
+          else atomicOr(&tile_bits_g[2 * k], lo);
+        }
+      }
+      if (2 * k + 1 < nbw) {
+        if (a.mask) a.mask[row_g * nbw + 2 * k + 1] = hi;
+        if (hi) {
+          if (uni_lds) atomicOr(&uni_lds[2 * k + 1], hi);
+          else atomicOr(&tile_bits_g[2 * k + 1], hi);
+        }
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void write_empty_row(const SelectArgs& a, size_t row_g) {
+  const int l = lane_id();
+  const int nbw = (a.T / DASH_BLOCK + 31) / 32;
+  if (l == 0) {
+    a.tau[row_g] = __uint_as_float(0x7fc00000u);
+    a.lognorm[row_g] = 0.f;
+    if (a.nsel) a.nsel[row_g] = 0;
+  }
+  if (a.mask)
+    for (int w = l; w < nbw; w += 64) a.mask[row_g * nbw + w] = 0u;
+}
+
+// ---------------------------------------------------------------------------- Stage 1, bf16 MFMA
+
+// One workgroup (4 waves) per 32 query rows.  The block scores of the 32
+// rows (all inside one 64-block, so they share their causal candidates) are
+// computed 32 blocks at a time on the 32x32x16 bf16 MFMA as
+//     Z^T[block][query] = kbar[block] . q[query]
+// (operand A = summary rows, B = the queries, fp32 accumulation) and kept in
+// LDS as u = (alpha-1) * coarse_scale * acc; then each wave solves tau for 8
+// rows.  coarse_u_chunk() is the one definition of this arithmetic; the
+// Stage-2 and backward kernels call it too, so they see the same bits.
+template <int D, int NPL>
+__global__ __launch_bounds__(256) void select_mfma_kernel(SelectArgs a) {
+  extern __shared__ float zs[];  // [32][nb + 1] followed by nbw union words
+  const int nb = a.T / DASH_BLOCK;
+  const int nbp = nb + 1;
+  const int nbw = (nb + 31) / 32;
+  uint32_t* uni = reinterpret_cast<uint32_t*>(zs + 32 * nbp);
+  const size_t bh = blockIdx.y;
+  const int row0 = blockIdx.x * 32;
+  const int w = threadIdx.x >> 6, l = lane_id(), j = l & 31, h = l >> 5;
+  const int nc = a.causal ? row0 / DASH_BLOCK : nb;
+  const CoarseArith ca = a.ca;
+  for (int x = threadIdx.x; x < nbw; x += 256) uni[x] = 0u;
+
+  const bf16_t* qh = reinterpret_cast<const bf16_t*>(a.q) + bh * a.T * D;
+  const bf16_t* kb = reinterpret_cast<const bf16_t*>(a.kbar) + bh * nb * D;
+  if (nc > 0) {
+    bf16x8 qb[D / 16];
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) qb[s] = load8(qh + (size_t)(row0 + j) * D + 16 * s + 8 * h);
+    for (int c = w; c * 32 < nc; c += 4) {
+      const int brow = c * 32 + j;
+      f32x16 acc = coarse_acc_chunk<D>(kb, brow < nc ? brow : 0, qb);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int b = c * 32 + acc_row32(r, l);
+        if (b < nc) zs[j * nbp + b] = ca.u_of(acc[r]);
+      }
+    }
+  }
+  __syncthreads();
+  for (int rr = 0; rr < 8; ++rr) {
+    const int row = 8 * w + rr;
+    const size_t row_g = bh * a.T + row0 + row;
+    if (nc == 0) {
+      write_empty_row(a, row_g);
+      continue;
+    }
+    float u[NPL];
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) {
+      const int idx = l + 64 * k;
+      u[k] = idx < nc ? zs[row * nbp + idx] : -INFINITY;
+    }
+    const EntmaxOut e = entmax_solve<NPL>(u, ca);
+    write_row_selection<NPL>(a, row_g, u, nc, e, ca, uni, nullptr);
+  }
+  __syncthreads();
+  const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
+  uint32_t* tb = a.tile_bits + (bh * ntile + row0 / DASH_QTILE) * nbw;
+  for (int x = threadIdx.x; x < nbw; x += 256)
+    if (uni[x]) atomicOr(&tb[x], uni[x]);
+}
+
+// ---------------------------------------------------------------------------- Stage 1, generic
+
+// One wave per query row; scores by a sequential fp32 dot product
+// (dot_row), the same function the generic Stage-2 kernel uses.
+template <typename T, int NPL>
+__global__ __launch_bounds__(64) void select_generic_kernel(SelectArgs a) {
+  __shared__ float qs[128];
+  const int D = a.D;
+  const int nb = a.T / DASH_BLOCK;
+  const int nbw = (nb + 31) / 32;
+  const size_t bh = blockIdx.y;
+  const int i = blockIdx.x;
+  const int l = lane_id();
+  const T* q = reinterpret_cast<const T*>(a.q) + (bh * a.T + i) * D;
+  const T* kb = reinterpret_cast<const T*>(a.kbar) + bh * nb * D;
+  for (int d = l; d < D; d += 64) qs[d] = to_f<T>(q[d]);
+  __syncthreads();
+  const int nc = a.causal ? i / DASH_BLOCK : nb;
+  const size_t row_g = bh * a.T + i;
+  if (nc == 0) {
+    write_empty_row(a, row_g);
+    return;
+  }
+  const CoarseArith ca = a.ca;
+  float u[NPL];
+#pragma unroll
+  for (int k = 0; k < NPL; ++k) {
+    const int b = l + 64 * k;
+    u[k] = b < nc ? ca.u_of(dot_row<T>(qs, kb + (size_t)b * D, D)) : -INFINITY;
+  }
+  const EntmaxOut e = entmax_solve<NPL>(u, ca);
+  const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
+  uint32_t* tb = a.tile_bits + (bh * ntile + i / DASH_QTILE) * nbw;
+  write_row_selection<NPL>(a, row_g, u, nc, e, ca, nullptr, tb);
+}
+
+// ---------------------------------------------------------------------------- tile lists
+
+// Per query tile: add the tile's own blocks (causal), write the bit set back
+// and compact it into an ascending block list.  grid (ntile, BH), 64 threads;
+// nbw <= 32.
+__global__ __launch_bounds__(64) void tile_list_kernel(uint32_t* tile_bits, int* tile_cnt, int* tile_blk, int T_,
+                                                       int causal) {
+  const int nb = T_ / DASH_BLOCK;
+  const int nbw = (nb + 31) / 32;
+  const int ntile = (T_ + DASH_QTILE - 1) / DASH_QTILE;
+  const size_t t = (size_t)blockIdx.y * ntile + blockIdx.x;
+  const int l = lane_id();
+  uint32_t word = l < nbw ? tile_bits[t * nbw + l] : 0u;
+  if (causal) {
+    const int r0 = blockIdx.x * DASH_QTILE;
+    const int r1 = min(T_, r0 + DASH_QTILE) - 1;
+    for (int b = r0 / DASH_BLOCK; b <= r1 / DASH_BLOCK; ++b)
+      if ((b >> 5) == l) word |= 1u << (b & 31);
+  }
+  if (l < nbw) tile_bits[t * nbw + l] = word;
+  const int c = __popc(word);
+  int incl = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(incl, o, 64);
+    if (l >= o) incl += y;
+  }
+  int pos = incl - c;
+  int* dst = tile_blk + t * nb;
+  while (word) {
+    const int bit = __ffs(word) - 1;
+    word &= word - 1;
+    dst[pos++] = l * 32 + bit;
+  }
+  if (l == 63) tile_cnt[t] = incl;
+}
+
+// ---------------------------------------------------------------------------- launchers
+
+hipError_t launch_pool(const void* k, void* kbar, int BH, int T_, int D, int dtype, hipStream_t st) {
+  dim3 grid(T_ / DASH_BLOCK, BH);
+  if (dtype == 1)
+    pool_kernel<bf16_t><<<grid, 64, 0, st>>>((const bf16_t*)k, (bf16_t*)kbar, T_, D);
+  else
+    pool_kernel<float><<<grid, 64, 0, st>>>((const float*)k, (float*)kbar, T_, D);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  int blocks = (int)((n + 255) / 256);
+  if (blocks > 4096) blocks = 4096;
+  fill_u32_kernel<<<blocks, 256, 0, st>>>(p, n, v);
+  return hipGetLastError();
+}
+
+template <int D, int NPL>
+static hipError_t launch_select_mfma_t(const SelectArgs& a, int BH, hipStream_t st) {
+  const int nb = a.T / DASH_BLOCK;
+  const size_t lds = (size_t)32 * (nb + 1) * sizeof(float) + ((nb + 31) / 32) * sizeof(uint32_t);
+  auto kfn = select_mfma_kernel<D, NPL>;
+  hipError_t e = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  kfn<<<dim3(a.T / 32, BH), 256, lds, st>>>(a);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_select_mfma_d(const SelectArgs& a, int BH, hipStream_t st) {
+  const int nb = a.T / DASH_BLOCK;
+  if (nb <= 64) return launch_select_mfma_t<D, 1>(a, BH, st);
+  if (nb <= 128) return launch_select_mfma_t<D, 2>(a, BH, st);
+  if (nb <= 256) return launch_select_mfma_t<D, 4>(a, BH, st);
+  if (nb <= 512) return launch_select_mfma_t<D, 8>(a, BH, st);
+  return launch_select_mfma_t<D, 16>(a, BH, st);
+}
+
+template <typename T>
+static hipError_t launch_select_generic_t(const SelectArgs& a, int BH, hipStream_t st) {
+  const int nb = a.T / DASH_BLOCK;
+  dim3 grid(a.T, BH);
+  if (nb <= 64) select_generic_kernel<T, 1><<<grid, 64, 0, st>>>(a);
+  else if (nb <= 128) select_generic_kernel<T, 2><<<grid, 64, 0, st>>>(a);
+  else if (nb <= 256) select_generic_kernel<T, 4><<<grid, 64, 0, st>>>(a);
+  else if (nb <= 512) select_generic_kernel<T, 8><<<grid, 64, 0, st>>>(a);
+  else select_generic_kernel<T, 16><<<grid, 64, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const SelectArgs& a, int BH, int dtype, hipStream_t st) {
+  if (dtype == 1) return a.D == 128 ? launch_select_mfma_d<128>(a, BH, st) : launch_select_mfma_d<64>(a, BH, st);
+  return launch_select_generic_t<float>(a, BH, st);
+}
+
+hipError_t launch_tile_lists(uint32_t* tile_bits, int* tile_cnt, int* tile_blk, int BH, int T_, int causal,
+                             hipStream_t st) {
+  const int ntile = (T_ + DASH_QTILE - 1) / DASH_QTILE;
+  tile_list_kernel<<<dim3(ntile, BH), 64, 0, st>>>(tile_bits, tile_cnt, tile_blk, T_, causal);
+  return hipGetLastError();
+}

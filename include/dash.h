@@ -1,0 +1,169 @@
+/*
+ * dash.h -- C ABI of the DashAttention hot path for AMD Instinct MI355X (gfx950).
+ *
+ * The method (DashAttention pages: "DashAttention: Making Sparse Attention Fully
+ * Differentiable with Adaptive Block Selection", sections "Core Mechanism" and
+ * "Key Concepts"; "DashAttention and the year sparse attention became a field",
+ * section "What alpha-entmax changes"):
+ *
+ *   Stage 0  kbar_b = mean of the 64 keys of block b (the zero-initialised
+ *            summariser starts from mean pooling);
+ *   Stage 1  z_ib = coarse_scale * q_i . kbar_b for the candidate blocks of
+ *            query i, p_i = alpha-entmax(z_i): u = (alpha-1) z,
+ *            p_b = [u_b - tau_i]_+^(1/(alpha-1)), sum_b p_b = 1 (alpha = 1:
+ *            softmax); blocks with p_ib = 0 are dropped;
+ *   Stage 2  one softmax over the tokens j of the selected blocks of
+ *            l_ij = fine_scale * q_i . k_j + log p_{i,blk(j)}, O_i = sum a_ij v_j.
+ *
+ * Conventions taken where the pages are silent:
+ *   - causal: the candidates of query i are the blocks strictly before its own
+ *     block; its own block is always attended with the causal mask (j <= i)
+ *     and log-prior 0; non-causal: every block is a candidate;
+ *   - kbar is the exact mean rounded once (to nearest even) to the tensor dtype;
+ *   - decode: the new token is the last cached token (position N-1), so decode
+ *     equals the last row of a causal prefill over the cache.
+ *
+ * Memory: every pointer is a DEVICE pointer owned by the caller.  The library
+ * never allocates, frees or synchronises; all work is enqueued on `stream`
+ * (a hipStream_t passed as void*, NULL = the default stream).  Tensors are
+ * dense and contiguous, layout [B, H, T, D] (row-major, D fastest) for
+ * q/k/v/o/dout/dq/dk/dv, [B, H, T/64, D] for kbar/dkbar.  Element type is
+ * dash_params.dtype (bf16 or fp32); lse, tau, lognorm and dkbar are fp32.
+ * Pointers must be 16-byte aligned.
+ *
+ * Errors: arguments are validated on the host before anything is launched, so
+ * a call that returns an error has enqueued no work.  DASH_EHIP reports a
+ * launch failure.  dash_last_error() returns a thread-local message for the
+ * last failing call on the calling thread.
+ *
+ * Determinism: forward, decode and backward results do not depend on
+ * scheduling (no floating-point atomics).
+ */
+#ifndef DASH_H
+#define DASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DASH_OK = 0,
+  DASH_EINVAL = 1,        /* null/misaligned pointer, bad shape, alpha or scale */
+  DASH_EUNSUPPORTED = 2,  /* valid but not built: D not in {64,128}, block != 64, T too long */
+  DASH_EWORKSPACE = 3,    /* workspace smaller than the *_workspace_bytes() result */
+  DASH_EHIP = 4           /* a HIP launch failed; see dash_last_error() */
+} dash_status;
+
+typedef enum { DASH_F32 = 0, DASH_BF16 = 1 } dash_dtype;
+
+/* Prefill / training shapes and hyper-parameters. */
+typedef struct {
+  int32_t B, H, T, D;   /* batch, heads, sequence length (multiple of 64, <= 65536), head dim (64|128) */
+  int32_t block;        /* keys per block; must be 64 */
+  float alpha;          /* entmax alpha in [1, 2] */
+  int32_t causal;       /* 0 or 1 */
+  float fine_scale;     /* scale of q.k in Stage 2 (usually 1/sqrt(D)); finite, > 0 */
+  float coarse_scale;   /* scale of q.kbar in Stage 1; finite, > 0 */
+  int32_t dtype;        /* dash_dtype of q, k, v, o, kbar, dout, dq, dk, dv */
+} dash_params;
+
+/*
+ * Stage-1 selection, written by dash_fwd and read by dash_bwd.  All buffers are
+ * caller-owned device memory; sizes (in elements) come from dash_sel_sizes().
+ * nb = T/64, nbw = ceil(nb/32), ntile = ceil(T/dash_query_tile()).
+ *   tau      [B,H,T]        f32  entmax threshold (u-units for alpha>1, z-units
+ *                                (log-sum-exp) for alpha=1; NaN when the row has
+ *                                no candidate block)
+ *   lognorm  [B,H,T]        f32  log of sum_b [u_b - tau]_+^(1/(alpha-1)) (about 0)
+ *   nsel     [B,H,T]        i32  number of selected candidate blocks (may be NULL)
+ *   mask     [B,H,T,nbw]    u32  bit b set iff block b is a selected candidate (may be NULL)
+ *   tile_cnt [B,H,ntile]    i32  length of each query tile's block list
+ *   tile_blk [B,H,ntile,nb] i32  ascending blocks the tile must visit: the union of its
+ *                                rows' selected blocks plus, when causal, the tile's own
+ *                                blocks
+ *   tile_bits[B,H,ntile,nbw]u32  the same set as a bit mask
+ */
+typedef struct {
+  float* tau;
+  float* lognorm;
+  int32_t* nsel;
+  uint32_t* mask;
+  int32_t* tile_cnt;
+  int32_t* tile_blk;
+  uint32_t* tile_bits;
+} dash_sel;
+
+/* Query rows per Stage-2 tile (the granularity of tile_cnt / tile_blk). */
+int32_t dash_query_tile(void);
+
+/* Element counts of the seven dash_sel buffers, in struct order. */
+dash_status dash_sel_sizes(const dash_params* p, size_t out_elems[7]);
+
+/* Bytes of device workspace dash_fwd / dash_bwd need (may be 0). */
+size_t dash_fwd_workspace_bytes(const dash_params* p);
+size_t dash_bwd_workspace_bytes(const dash_params* p);
+
+/*
+ * Stage 0 alone: kbar[B,H,T/64,D] = mean of each 64-key block of k[B,H,T,D],
+ * accumulated in fp64 and rounded once to dtype.  (Stage 0 of the pages,
+ * "What alpha-entmax changes"; used to build the summaries of a decode cache.)
+ */
+dash_status dash_pool(const dash_params* p, const void* k, void* kbar, void* stream);
+
+/*
+ * Forward (Stages 0, 1, 2).  Inputs q, k, v.  Outputs: o [B,H,T,D] (dtype),
+ * lse [B,H,T] (f32, log-sum-exp of the Stage-2 logits, for the backward),
+ * kbar [B,H,T/64,D] (dtype) and the selection `sel`.
+ */
+dash_status dash_fwd(const dash_params* p, const void* q, const void* k, const void* v,
+                     void* o, float* lse, void* kbar, const dash_sel* sel,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of the scalar <dout, O>: gradients through Stage 2, log p, the
+ * alpha-entmax Jacobian (s = p^(2-alpha), dz = s*(g - <s,g>/sum s), g = dL/dp),
+ * the block scores and mean pooling.  Inputs are the forward's q, k, v, o, lse,
+ * kbar and sel plus dout.  Outputs dq, dk, dv (dtype; dk includes the pooling
+ * path dkbar/64) and dkbar [B,H,T/64,D] (f32, gradient w.r.t. the summaries).
+ * The rounding of kbar to dtype is treated as the identity.
+ */
+dash_status dash_bwd(const dash_params* p, const void* q, const void* k, const void* v,
+                     const void* o, const float* lse, const void* dout, const void* kbar,
+                     const dash_sel* sel, void* dq, void* dk, void* dv, float* dkbar,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Decode shapes: S sequences x H heads, one new query each, cache length N. */
+typedef struct {
+  int32_t S, H, N, D;   /* N multiple of 64, >= 64; D in {64,128} */
+  int32_t block;        /* must be 64 */
+  float alpha;
+  float fine_scale;
+  float coarse_scale;
+  int32_t dtype;
+} dash_decode_params;
+
+size_t dash_decode_workspace_bytes(const dash_decode_params* p);
+
+/*
+ * Decode (the pages' decoding path; speed claim at 96K context in "The
+ * numbers").  q [S,H,D]; caches kc, vc [S,H,N,D] with the new token at N-1;
+ * kbar [S,H,N/64,D] the summaries of the cache (dash_pool).  Candidates are
+ * blocks 0..N/64-2; block N/64-1 is attended whole with prior 0.
+ * Outputs o [S,H,D] (dtype), lse [S,H] (f32, may be NULL), nsel [S,H] (i32,
+ * may be NULL), tau [S,H] (f32, may be NULL).
+ */
+dash_status dash_decode(const dash_decode_params* p, const void* q, const void* kc,
+                        const void* vc, const void* kbar, void* o, float* lse,
+                        int32_t* nsel, float* tau, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* dash_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DASH_H */

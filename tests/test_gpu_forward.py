@@ -1,0 +1,129 @@
+"""GPU forward parity: libdash.so (through the C ABI) against the float64 oracle.
+
+Small cases run the oracle over every row; the full-size workloads (the
+16K and 64K causal prefills) compare sampled rows.  Tolerances are in
+tests/parity.py.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from differentiable_adaptive_block_amd import inputs
+from parity import check_rows, unpack_mask
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _api():
+    from differentiable_adaptive_block_amd import api
+    return api
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _gpu_forward(w, alpha, causal, coarse_scale):
+    api = _api()
+    r = api.forward(w["q"], w["k"], w["v"], alpha=alpha, causal=causal, coarse_scale=coarse_scale, want_mask=True)
+    torch.cuda.synchronize()
+    nb = w["q"].shape[2] // 64
+    sel = r["sel"]
+    return r, dict(o=r["o"].float().cpu().numpy(), lse=r["lse"].cpu().numpy(), tau=sel.tau.cpu().numpy(),
+                   nsel=sel.nsel.cpu().numpy(), mask=unpack_mask(sel.mask, nb))
+
+
+def _np64(t):
+    return t.double().cpu().numpy()
+
+
+SMALL = [
+    # name, B, H, T, D, dtype, causal, alpha, coarse multiple of 1/sqrt(D), planted
+    ("c1", 1, 2, 512, 64, "fp32", False, 1.5, 1.0, None),
+    ("c1s", 1, 2, 512, 64, "fp32", False, 1.5, 16.0, None),
+    ("c1-a1", 1, 2, 512, 64, "fp32", False, 1.0, 1.0, None),
+    ("c1-a125", 1, 2, 512, 64, "fp32", False, 1.25, 16.0, None),
+    ("c1-a2", 1, 2, 512, 64, "fp32", False, 2.0, 16.0, None),
+    ("fp32-causal", 1, 2, 320, 128, "fp32", True, 1.5, 4.0, (1, 3)),
+    ("bf16-causal-ragged", 1, 2, 1088, 128, "bf16", True, 1.5, 4.0, (1, 4)),
+    ("bf16-causal-dense", 2, 1, 576, 128, "bf16", True, 1.5, 1.0, (1, 8)),
+    ("bf16-noncausal-d64", 1, 2, 576, 64, "bf16", False, 1.25, 4.0, (1, 3)),
+    ("bf16-causal-a1", 1, 1, 512, 128, "bf16", True, 1.0, 1.0, (1, 3)),
+    ("bf16-causal-a2", 1, 1, 512, 64, "bf16", True, 2.0, 4.0, (1, 3)),
+    ("bf16-one-block", 1, 2, 64, 128, "bf16", True, 1.5, 1.0, None),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_forward_small_full_oracle(case):
+    name, B, H, T, D, dtype, causal, alpha, csm, planted = case
+    _say(f"[forward] {name} B{B} H{H} T{T} D{D} {dtype} causal={causal} alpha={alpha}")
+    w = inputs.make_prefill(B, H, T, D, dtype, causal, planted, seed=7 + T + D, device="cpu", with_dout=False)
+    w = {k: v.to(DEV) for k, v in w.items()}
+    cs = csm / math.sqrt(D)
+    r, g = _gpu_forward(w, alpha, causal, cs)
+    prm = oracle.Params(alpha=alpha, causal=causal, coarse_scale=cs, storage=dtype)
+    q, k, v = _np64(w["q"]), _np64(w["k"]), _np64(w["v"])
+    # summaries bit-exact
+    kb_o = np.stack([np.stack([oracle.pool_blocks(k[b, h], 64, dtype) for h in range(H)]) for b in range(B)])
+    np.testing.assert_array_equal(r["kbar"].double().cpu().numpy(), kb_o)
+    rows = [(b, h, i) for b in range(B) for h in range(H) for i in range(T)]
+    ora = oracle.forward_rows(q, k, v, prm, rows, kbar=kb_o)
+    st = check_rows(g, ora, rows, w["q"].dtype, alpha, name)
+    _say(f"  ok {st}")
+
+
+def test_forward_deterministic():
+    w = inputs.make_prefill(1, 2, 1024, 128, "bf16", True, (1, 4), seed=3, device="cpu", with_dout=False)
+    w = {k: v.to(DEV) for k, v in w.items()}
+    api = _api()
+    a = api.forward(w["q"], w["k"], w["v"], coarse_scale=3 / math.sqrt(128))
+    b = api.forward(w["q"], w["k"], w["v"], coarse_scale=3 / math.sqrt(128))
+    torch.cuda.synchronize()
+    assert torch.equal(a["o"], b["o"]) and torch.equal(a["lse"], b["lse"])
+    assert torch.equal(a["sel"].mask, b["sel"].mask)
+
+
+def _sampled(name, n_heads=3, n_rows=24, T_sub=None):
+    wl = inputs.CONFIGS[name]
+    sh = wl.shape
+    _say(f"[forward] {name} full size {sh} (sampled rows)")
+    w = inputs.make_prefill(sh["B"], sh["H"], sh["T"], sh["D"], wl.dtype, wl.causal, wl.planted, wl.seed,
+                            device=DEV, with_dout=False)
+    alpha = wl.alpha if not isinstance(wl.alpha, tuple) else wl.alpha[-1]
+    r, g = _gpu_forward(w, alpha, wl.causal, wl.coarse_scale)
+    rng = np.random.default_rng(0)
+    B, H, T = sh["B"], sh["H"], sh["T"]
+    heads = sorted(rng.choice(H, size=n_heads, replace=False).tolist())
+    rows = []
+    for h in heads:
+        pos = rng.choice(T, size=n_rows, replace=False).tolist() + [0, 63, 64, T - 1]
+        rows += [(0, h, i) for i in sorted(set(pos))]
+    prm = oracle.Params(alpha=alpha, causal=wl.causal, coarse_scale=wl.coarse_scale, storage=wl.dtype)
+    ora = []
+    for h in heads:
+        q, k, v = (_np64(w[x][0:1, h:h + 1]) for x in ("q", "k", "v"))
+        kb = oracle.pool_blocks(k[0, 0], 64, wl.dtype)
+        np.testing.assert_array_equal(r["kbar"][0, h].double().cpu().numpy(), kb)
+        hr = [(0, 0, i) for (_, hh, i) in rows if hh == h]
+        ora += oracle.forward_rows(q, k, v, prm, hr, kbar=kb[None, None])
+    st = check_rows(g, ora, rows, torch.bfloat16, alpha, name)
+    density = float(g["nsel"].sum()) / float(sum((i // 64) for i in range(T)) * B * H)
+    _say(f"  ok {st}; selected-pair density {density:.4f}")
+    return density
+
+
+def test_forward_16k_causal_prefill_sampled():
+    _sampled("c2")
+
+
+def test_forward_64k_causal_prefill_sampled():
+    _sampled("c3", n_heads=2, n_rows=12)
