@@ -24,6 +24,8 @@ EXPORTS = [
     "dash_bwd_workspace_bytes",
     "dash_pool",
     "dash_fwd",
+    "dash_fwd_select",
+    "dash_fwd_attend",
     "dash_bwd",
     "dash_decode_workspace_bytes",
     "dash_decode",
@@ -86,6 +88,10 @@ def load() -> ctypes.CDLL:
     L.dash_pool.argtypes = [P(DashParams), vp, vp, vp]
     L.dash_fwd.restype = ctypes.c_int
     L.dash_fwd.argtypes = [P(DashParams), vp, vp, vp, vp, vp, vp, P(DashSel), vp, ctypes.c_size_t, vp]
+    L.dash_fwd_select.restype = ctypes.c_int
+    L.dash_fwd_select.argtypes = [P(DashParams), vp, vp, vp, P(DashSel), vp]
+    L.dash_fwd_attend.restype = ctypes.c_int
+    L.dash_fwd_attend.argtypes = [P(DashParams), vp, vp, vp, vp, P(DashSel), vp, vp, vp]
     L.dash_bwd.restype = ctypes.c_int
     L.dash_bwd.argtypes = [P(DashParams), vp, vp, vp, vp, vp, vp, vp, P(DashSel), vp, vp, vp, vp, vp,
                            ctypes.c_size_t, vp]
@@ -132,6 +138,14 @@ def pool(p: DashParams, k, kbar, stream) -> None:
 
 def fwd(p: DashParams, q, k, v, o, lse, kbar, sel: DashSel, ws, ws_bytes, stream) -> None:
     check(load().dash_fwd(ctypes.byref(p), q, k, v, o, lse, kbar, ctypes.byref(sel), ws, ws_bytes, stream))
+
+
+def fwd_select(p: DashParams, q, k, kbar, sel: DashSel, stream) -> None:
+    check(load().dash_fwd_select(ctypes.byref(p), q, k, kbar, ctypes.byref(sel), stream))
+
+
+def fwd_attend(p: DashParams, q, k, v, kbar, sel: DashSel, o, lse, stream) -> None:
+    check(load().dash_fwd_attend(ctypes.byref(p), q, k, v, kbar, ctypes.byref(sel), o, lse, stream))
 
 
 def bwd(p: DashParams, q, k, v, o, lse, dout, kbar, sel: DashSel, dq, dk, dv, dkbar, ws, ws_bytes, stream) -> None:

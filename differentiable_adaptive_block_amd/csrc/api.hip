@@ -151,19 +151,15 @@ dash_status dash_pool(const dash_params* p, const void* k, void* kbar, void* str
   return e == hipSuccess ? DASH_OK : hip_fail(e, "pool");
 }
 
-dash_status dash_fwd(const dash_params* p, const void* q, const void* k, const void* v, void* o, float* lse,
-                     void* kbar, const dash_sel* sel, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
+dash_status dash_fwd_select(const dash_params* p, const void* q, const void* k, void* kbar, const dash_sel* sel,
+                            void* stream) {
   dash_status s = check_params(p);
   if (s != DASH_OK) return s;
-  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(lse) || !ok_ptr(kbar))
-    return fail(DASH_EINVAL, "q, k, v, o, lse and kbar must be non-null and 16-byte aligned");
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(kbar)) return fail(DASH_EINVAL, "q, k and kbar must be non-null and 16-byte aligned");
   if ((s = check_sel(sel, true)) != DASH_OK) return s;
   hipStream_t st = (hipStream_t)stream;
   const int BH = p->B * p->H;
   const int nb = p->T / DASH_BLOCK;
-  const CoarseArith ca = make_ca(p->alpha, p->coarse_scale);
   hipError_t e;
   if ((e = launch_pool(k, kbar, BH, p->T, p->D, p->dtype, st)) != hipSuccess) return hip_fail(e, "pool");
   if ((e = launch_fill_u32(sel->tile_bits, (size_t)BH * ntile_of(p->T) * nbw_of(nb), 0u, st)) != hipSuccess)
@@ -174,7 +170,7 @@ dash_status dash_fwd(const dash_params* p, const void* q, const void* k, const v
   sa.T = p->T;
   sa.D = p->D;
   sa.causal = p->causal;
-  sa.ca = ca;
+  sa.ca = make_ca(p->alpha, p->coarse_scale);
   sa.tau = sel->tau;
   sa.lognorm = sel->lognorm;
   sa.nsel = sel->nsel;
@@ -183,6 +179,16 @@ dash_status dash_fwd(const dash_params* p, const void* q, const void* k, const v
   if ((e = launch_select(sa, BH, p->dtype, st)) != hipSuccess) return hip_fail(e, "select");
   if ((e = launch_tile_lists(sel->tile_bits, sel->tile_cnt, sel->tile_blk, BH, p->T, p->causal, st)) != hipSuccess)
     return hip_fail(e, "tile lists");
+  return DASH_OK;
+}
+
+dash_status dash_fwd_attend(const dash_params* p, const void* q, const void* k, const void* v, const void* kbar,
+                            const dash_sel* sel, void* o, float* lse, void* stream) {
+  dash_status s = check_params(p);
+  if (s != DASH_OK) return s;
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(lse) || !ok_ptr(kbar))
+    return fail(DASH_EINVAL, "q, k, v, o, lse and kbar must be non-null and 16-byte aligned");
+  if ((s = check_sel(sel, true)) != DASH_OK) return s;
   FwdArgs fa;
   fa.q = q;
   fa.k = k;
@@ -194,14 +200,27 @@ dash_status dash_fwd(const dash_params* p, const void* q, const void* k, const v
   fa.lognorm = sel->lognorm;
   fa.tile_cnt = sel->tile_cnt;
   fa.tile_blk = sel->tile_blk;
-  fa.BH = BH;
+  fa.BH = p->B * p->H;
   fa.T = p->T;
   fa.D = p->D;
   fa.causal = p->causal;
   fa.fine_scale = p->fine_scale;
-  fa.ca = ca;
-  if ((e = launch_fwd(fa, p->dtype, st)) != hipSuccess) return hip_fail(e, "stage 2 forward");
-  return DASH_OK;
+  fa.ca = make_ca(p->alpha, p->coarse_scale);
+  hipError_t e = launch_fwd(fa, p->dtype, (hipStream_t)stream);
+  return e == hipSuccess ? DASH_OK : hip_fail(e, "stage 2 forward");
+}
+
+dash_status dash_fwd(const dash_params* p, const void* q, const void* k, const void* v, void* o, float* lse,
+                     void* kbar, const dash_sel* sel, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  dash_status s = check_params(p);
+  if (s != DASH_OK) return s;
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(lse) || !ok_ptr(kbar))
+    return fail(DASH_EINVAL, "q, k, v, o, lse and kbar must be non-null and 16-byte aligned");
+  if ((s = check_sel(sel, true)) != DASH_OK) return s;
+  if ((s = dash_fwd_select(p, q, k, kbar, sel, stream)) != DASH_OK) return s;
+  return dash_fwd_attend(p, q, k, v, kbar, sel, o, lse, stream);
 }
 
 dash_status dash_bwd(const dash_params* p, const void* q, const void* k, const void* v, const void* o,

@@ -123,6 +123,18 @@ dash_status dash_fwd(const dash_params* p, const void* q, const void* k, const v
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The two halves of dash_fwd, for callers that reuse a selection or time the
+ * stages apart.  dash_fwd_select runs Stages 0 and 1 (kbar and `sel`);
+ * dash_fwd_attend runs Stage 2 from q, k, v, kbar and a selection written by
+ * dash_fwd_select with the same params (o and lse).  Same validation and
+ * error behaviour as dash_fwd.
+ */
+dash_status dash_fwd_select(const dash_params* p, const void* q, const void* k, void* kbar,
+                            const dash_sel* sel, void* stream);
+dash_status dash_fwd_attend(const dash_params* p, const void* q, const void* k, const void* v,
+                            const void* kbar, const dash_sel* sel, void* o, float* lse, void* stream);
+
+/*
  * Backward of the scalar <dout, O>: gradients through Stage 2, log p, the
  * alpha-entmax Jacobian (s = p^(2-alpha), dz = s*(g - <s,g>/sum s), g = dL/dp),
  * the block scores and mean pooling.  Inputs are the forward's q, k, v, o, lse,
