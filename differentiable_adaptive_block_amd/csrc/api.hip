@@ -51,14 +51,14 @@ dash_status check_common(int D, int block, float alpha, float fs, float cs, int 
   return DASH_OK;
 }
 
-dash_status check_params(const dash_params* p) {
+dash_status check_params(const dash_params* p, bool limit_T = true) {
   if (!p) return fail(DASH_EINVAL, "null params");
   if (p->B < 1 || p->H < 1) return fail(DASH_EINVAL, "B and H must be >= 1");
   if (p->T < DASH_BLOCK || p->T % DASH_BLOCK) return fail(DASH_EINVAL, "T must be a positive multiple of 64 (got %d)", p->T);
   if (p->causal != 0 && p->causal != 1) return fail(DASH_EINVAL, "causal must be 0 or 1");
   dash_status s = check_common(p->D, p->block, p->alpha, p->fine_scale, p->coarse_scale, p->dtype);
   if (s != DASH_OK) return s;
-  if (p->T / DASH_BLOCK > DASH_MAX_NB) return fail(DASH_EUNSUPPORTED, "T above %d is not built", DASH_MAX_NB * DASH_BLOCK);
+  if (limit_T && p->T / DASH_BLOCK > DASH_MAX_NB) return fail(DASH_EUNSUPPORTED, "T above %d is not built", DASH_MAX_NB * DASH_BLOCK);
   return DASH_OK;
 }
 
@@ -88,8 +88,8 @@ size_t bwd_ws_layout(const dash_params* p, size_t off[4]) {
 
 size_t decode_ws_layout(const dash_decode_params* p, size_t off[6], int* nsplit, int* chunk) {
   const size_t SH = (size_t)p->S * p->H, nb = p->N / DASH_BLOCK, D = p->D;
-  const int ch = 8;  // blocks per split-KV work item
-  const int ns = (int)((nb + ch - 1) / ch);
+  const int ch = 4;  // waves per split-KV workgroup
+  const int ns = DASH_DEC_SPLIT;
   if (nsplit) *nsplit = ns;
   if (chunk) *chunk = ch;
   size_t o = 0;
@@ -144,7 +144,7 @@ size_t dash_decode_workspace_bytes(const dash_decode_params* p) {
 }
 
 dash_status dash_pool(const dash_params* p, const void* k, void* kbar, void* stream) {
-  dash_status s = check_params(p);
+  dash_status s = check_params(p, false);
   if (s != DASH_OK) return s;
   if (!ok_ptr(k) || !ok_ptr(kbar)) return fail(DASH_EINVAL, "k and kbar must be non-null and 16-byte aligned");
   hipError_t e = launch_pool(k, kbar, p->B * p->H, p->T, p->D, p->dtype, (hipStream_t)stream);
@@ -276,7 +276,8 @@ dash_status dash_decode(const dash_decode_params* p, const void* q, const void* 
   if (p->N < DASH_BLOCK || p->N % DASH_BLOCK) return fail(DASH_EINVAL, "N must be a positive multiple of 64 (got %d)", p->N);
   dash_status s = check_common(p->D, p->block, p->alpha, p->fine_scale, p->coarse_scale, p->dtype);
   if (s != DASH_OK) return s;
-  if (p->N / DASH_BLOCK > 4096) return fail(DASH_EUNSUPPORTED, "cache above 262144 tokens is not built");
+  if (p->N / DASH_BLOCK > 2048) return fail(DASH_EUNSUPPORTED, "cache above 131072 tokens is not built");
+  if (p->dtype != DASH_BF16 || p->D != 128) return fail(DASH_EUNSUPPORTED, "decode is built for bf16, D = 128");
   if (!ok_ptr(q) || !ok_ptr(kc) || !ok_ptr(vc) || !ok_ptr(kbar) || !ok_ptr(o))
     return fail(DASH_EINVAL, "q, kc, vc, kbar and o must be non-null and 16-byte aligned");
   if (!ok_opt(lse) || !ok_opt(nsel) || !ok_opt(tau)) return fail(DASH_EINVAL, "lse/nsel/tau must be 16-byte aligned");

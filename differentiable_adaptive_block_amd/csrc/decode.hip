@@ -1,2 +1,240 @@
+// Decode: one new query per (sequence, head) against a long KV cache
+// (the pages' decoding path; their speed claim is at 96K context with
+// 93.75% block sparsity, "The numbers" on the montana-research page).
+// The new token is the last cached token, so the query's candidates are
+// blocks 0..nb-2 and block nb-1 is attended whole with prior 0.
+//
+// Three kernels, all HBM-bound:
+//   decode_select   one workgroup per row: u = (alpha-1) * coarse_scale * q.kbar_b
+//                   for every candidate (coalesced GEMV over the summaries),
+//                   entmax threshold, compacted ascending list of the selected
+//                   blocks with their log2 prior, then the last block;
+//   decode_attend   split-KV: workgroup (split s, row) and its 4 waves take list
+//                   entries s*4 + w, stepping by 4*nsplit; each wave streams a
+//                   block's 64 keys and values (16 KB each, contiguous) with
+//                   16-byte loads, 1 KB per wave instruction, online softmax;
+//                   the 4 waves merge in LDS and write one partial (m, l, o);
+//   decode_combine  merges the nsplit partials of a row in fixed order.
 #include "kernels.h"
-hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t st) { (void)a; (void)dtype; (void)st; return hipErrorNotSupported; }
+#include "entmax.h"
+
+#define LOG2E_F 1.4426950408889634f
+#define LN2_F 0.6931471805599453f
+
+// 16 lanes share one 256-byte row (D = 128) or two rows (D = 64): lane l
+// holds 8 elements at chunk (l % 16).  Returns the sum over the 16 lanes.
+__device__ __forceinline__ float sum16(float v) {
+  v += __shfl_xor(v, 1, 64);
+  v += __shfl_xor(v, 2, 64);
+  v += __shfl_xor(v, 4, 64);
+  v += __shfl_xor(v, 8, 64);
+  return v;
+}
+
+__device__ __forceinline__ void unpack8(const uint4& r, float (&f)[8]) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[2 * e] = __uint_as_float(w[e] << 16);
+    f[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+  }
+}
+
+// ---------------------------------------------------------------------------- selection
+
+template <int NPL>
+__global__ __launch_bounds__(256) void decode_select_kernel(DecodeArgs a) {
+  constexpr int D = 128;
+  __shared__ float us[NPL * 64];
+  const int row = blockIdx.x;
+  const int nb = a.N / DASH_BLOCK;
+  const int nc = nb - 1;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const bf16_t* q = reinterpret_cast<const bf16_t*>(a.q) + (size_t)row * D;
+  const bf16_t* kb = reinterpret_cast<const bf16_t*>(a.kbar) + (size_t)row * nb * D;
+  const CoarseArith ca = a.ca;
+  float qf[8];
+  unpack8(*reinterpret_cast<const uint4*>(q + (l & 15) * 8), qf);
+  // 4 summaries per wave instruction, 16 lanes each
+  for (int b0 = w * 4; b0 < nc; b0 += 16) {
+    const int b = b0 + (l >> 4);
+    float part = 0.f;
+    if (b < nc) {
+      float kf[8];
+      unpack8(*reinterpret_cast<const uint4*>(kb + (size_t)b * D + (l & 15) * 8), kf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = fmaf(qf[e], kf[e], part);
+    }
+    part = sum16(part);
+    if (b < nc && (l & 15) == 0) us[b] = ca.u_of(part);
+  }
+  __syncthreads();
+  if (w != 0) return;
+  float u[NPL];
+#pragma unroll
+  for (int k = 0; k < NPL; ++k) {
+    const int idx = l + 64 * k;
+    u[k] = idx < nc ? us[idx] : -INFINITY;
+  }
+  EntmaxOut e;
+  if (nc > 0) e = entmax_solve<NPL>(u, ca);
+  else { e.tau = __uint_as_float(0x7fc00000u); e.lognorm = 0.f; e.nsel = 0; }
+  int* list = a.sel_blk + (size_t)row * nb;
+  float* lp = a.sel_lp + (size_t)row * nb;
+  int base = 0;
+#pragma unroll
+  for (int k = 0; k < NPL; ++k) {
+    const int idx = l + 64 * k;
+    const bool s = idx < nc && ca.selected(u[k], e.tau);
+    const unsigned long long bal = __ballot(s);
+    if (s) {
+      const int pos = base + __popcll(bal & ((1ull << l) - 1ull));
+      list[pos] = idx;
+      lp[pos] = ca.logp(u[k], e.tau, e.lognorm) * LOG2E_F;
+    }
+    base += __popcll(bal);
+  }
+  if (l == 0) {
+    list[base] = nb - 1;  // the query's own block, prior 0
+    lp[base] = 0.f;
+    a.sel_cnt[row] = base + 1;
+    a.rowstat[2 * row] = e.tau;
+    a.rowstat[2 * row + 1] = e.lognorm;
+    if (a.nsel) a.nsel[row] = e.nsel;
+    if (a.tau_out) a.tau_out[row] = e.tau;
+  }
+}
+
+// ---------------------------------------------------------------------------- split-KV attention
+
+__global__ __launch_bounds__(256) void decode_attend_kernel(DecodeArgs a) {
+  constexpr int D = 128;
+  __shared__ float red_m[4], red_l[4];
+  __shared__ float red_o[4][D];
+  const int split = blockIdx.x, row = blockIdx.y;
+  const int nb = a.N / DASH_BLOCK;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int g = l >> 4, c = l & 15;  // key group within a 1 KB load, 16-byte chunk
+  const int cnt = a.sel_cnt[row];
+  const int* list = a.sel_blk + (size_t)row * nb;
+  const float* lpl = a.sel_lp + (size_t)row * nb;
+  const bf16_t* K = reinterpret_cast<const bf16_t*>(a.kc) + (size_t)row * a.N * D;
+  const bf16_t* V = reinterpret_cast<const bf16_t*>(a.vc) + (size_t)row * a.N * D;
+  const float sl2 = a.fine_scale * LOG2E_F;
+  float qf[8];
+  unpack8(*reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.q) + (size_t)row * D + c * 8), qf);
+  float m = -INFINITY, lsum = 0.f;
+  float o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
+  const int stride = 4 * a.nsplit;
+  for (int en = split * 4 + w; en < cnt; en += stride) {
+    const int b = list[en];
+    const float pr = lpl[en];
+    const bf16_t* kb = K + (size_t)b * DASH_BLOCK * D;
+    const bf16_t* vb = V + (size_t)b * DASH_BLOCK * D;
+    uint4 kr[16], vr[16];
+#pragma unroll
+    for (int it = 0; it < 16; ++it) kr[it] = *reinterpret_cast<const uint4*>(kb + (size_t)(it * 4 + g) * D + c * 8);
+#pragma unroll
+    for (int it = 0; it < 16; ++it) vr[it] = *reinterpret_cast<const uint4*>(vb + (size_t)(it * 4 + g) * D + c * 8);
+    float s[16];
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      float kf[8];
+      unpack8(kr[it], kf);
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = fmaf(qf[e], kf[e], part);
+      s[it] = sum16(part) * sl2 + pr;  // key it*4 + g, identical in the 16 lanes of group g
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int it = 1; it < 16; ++it) mx = fmaxf(mx, s[it]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mn = fmaxf(m, mx);
+    const float rs = exp2f(m - mn);
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= rs;
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const float p = exp2f(s[it] - mn);
+      ps += p;
+      float vf[8];
+      unpack8(vr[it], vf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = fmaf(p, vf[e], o[e]);
+    }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    lsum = lsum * rs + ps;
+    m = mn;
+  }
+  // merge the 4 key groups of the wave (same m in every lane)
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    o[e] += __shfl_xor(o[e], 16, 64);
+    o[e] += __shfl_xor(o[e], 32, 64);
+  }
+  if (l == 0) { red_m[w] = m; red_l[w] = lsum; }
+  if (g == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red_o[w][c * 8 + e] = o[e];
+  }
+  __syncthreads();
+  if (w == 0) {
+    const float M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+    const float Mr = M == -INFINITY ? 0.f : M;
+    float L = 0.f;
+    float sc[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) { sc[x] = exp2f(red_m[x] - Mr); L += red_l[x] * sc[x]; }
+    float* part = a.part + ((size_t)row * a.nsplit + split) * (D + 2);
+    for (int d = l; d < D; d += 64)
+      part[d] = red_o[0][d] * sc[0] + red_o[1][d] * sc[1] + red_o[2][d] * sc[2] + red_o[3][d] * sc[3];
+    if (l == 0) { part[D] = M; part[D + 1] = L; }
+  }
+}
+
+__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
+  constexpr int D = 128;
+  const int row = blockIdx.x;
+  const int l = threadIdx.x;
+  const float* part = a.part + (size_t)row * a.nsplit * (D + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, part[s * (D + 2) + D]);
+  const float Mr = M == -INFINITY ? 0.f : M;
+  float L = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int s = 0; s < a.nsplit; ++s) {
+    const float* p = part + s * (D + 2);
+    const float sc = exp2f(p[D] - Mr);
+    L += p[D + 1] * sc;
+    o0 += p[l] * sc;
+    o1 += p[l + 64] * sc;
+  }
+  bf16_t* O = reinterpret_cast<bf16_t*>(a.o) + (size_t)row * D;
+  O[l] = f2bf(o0 / L);
+  O[l + 64] = f2bf(o1 / L);
+  if (l == 0 && a.lse) a.lse[row] = (M + __log2f(L)) * LN2_F;
+}
+
+hipError_t launch_decode(const DecodeArgs& a0, int dtype, hipStream_t st) {
+  if (dtype != 1 || a0.D != 128) return hipErrorNotSupported;
+  DecodeArgs a = a0;
+  a.nsplit = DASH_DEC_SPLIT;
+  const int nb = a.N / DASH_BLOCK;
+  if (nb <= 128) decode_select_kernel<2><<<a.SH, 256, 0, st>>>(a);
+  else if (nb <= 256) decode_select_kernel<4><<<a.SH, 256, 0, st>>>(a);
+  else if (nb <= 512) decode_select_kernel<8><<<a.SH, 256, 0, st>>>(a);
+  else if (nb <= 1024) decode_select_kernel<16><<<a.SH, 256, 0, st>>>(a);
+  else if (nb <= 1536) decode_select_kernel<24><<<a.SH, 256, 0, st>>>(a);
+  else decode_select_kernel<32><<<a.SH, 256, 0, st>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  decode_attend_kernel<<<dim3(a.nsplit, a.SH), 256, 0, st>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  decode_combine_kernel<<<a.SH, 64, 0, st>>>(a);
+  return hipGetLastError();
+}

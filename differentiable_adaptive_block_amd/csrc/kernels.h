@@ -3,6 +3,8 @@
 
 #include "common.h"
 
+#define DASH_DEC_SPLIT 16  // split-KV workgroups per decode row
+
 struct SelectArgs {
   const void* q;      // [BH, T, D]
   const void* kbar;   // [BH, nb, D]

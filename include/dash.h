@@ -110,6 +110,7 @@ size_t dash_bwd_workspace_bytes(const dash_params* p);
  * Stage 0 alone: kbar[B,H,T/64,D] = mean of each 64-key block of k[B,H,T,D],
  * accumulated in fp64 and rounded once to dtype.  (Stage 0 of the pages,
  * "What alpha-entmax changes"; used to build the summaries of a decode cache.)
+ * Any T that is a multiple of 64 is accepted here (no 65536 limit).
  */
 dash_status dash_pool(const dash_params* p, const void* k, void* kbar, void* stream);
 
@@ -149,7 +150,7 @@ dash_status dash_bwd(const dash_params* p, const void* q, const void* k, const v
 
 /* Decode shapes: S sequences x H heads, one new query each, cache length N. */
 typedef struct {
-  int32_t S, H, N, D;   /* N multiple of 64, >= 64; D in {64,128} */
+  int32_t S, H, N, D;   /* N multiple of 64, 64 <= N <= 131072; D = 128 (bf16 only) */
   int32_t block;        /* must be 64 */
   float alpha;
   float fine_scale;
