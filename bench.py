@@ -181,6 +181,56 @@ def bench_prefill(name, steps, warmup, device, log_prefix=""):
     return res, (B, H, T, D)
 
 
+def bench_decode(name, steps, warmup, device):
+    """Time dash_decode (select + split-KV attend + combine) on a named decode workload."""
+    from differentiable_adaptive_block_amd import _lib, api, inputs
+
+    wl = inputs.CONFIGS[name]
+    sh = wl.shape
+    t0 = time.time()
+    w = inputs.make_decode(sh["S"], sh["H"], sh["N"], sh["D"], wl.dtype, wl.planted, wl.seed, device=device)
+    q, kc, vc = w["q"], w["k"], w["v"]
+    S, H, N, D = kc.shape
+    kbar = api.pool(kc.view(1, S * H, N, D)).view(S, H, N // 64, D)
+    torch.cuda.synchronize()
+    log(f"inputs {name} generated in {time.time() - t0:.1f}s")
+    p = api.make_decode_params(q, kc, wl.alpha, None, wl.coarse_scale)
+    bufs = api.DecodeBuffers(p, q.dtype, q.device)
+    st = torch.cuda.current_stream().cuda_stream
+
+    def step():
+        _lib.decode(p, q.data_ptr(), kc.data_ptr(), vc.data_ptr(), kbar.data_ptr(), bufs.o.data_ptr(),
+                    bufs.lse.data_ptr(), bufs.nsel.data_ptr(), bufs.tau.data_ptr(), bufs.ws.data_ptr(),
+                    bufs.ws_bytes, st)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [_events(2) for _ in range(steps)]
+    for s in range(steps):
+        evs[s][0].record()
+        step()
+        evs[s][1].record()
+    torch.cuda.synchronize()
+    us = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in evs)
+    us_mean = sum(us) / len(us)
+    nsel = bufs.nsel.to(torch.int64)
+    nb = N // 64
+    sel_bytes = float((nsel + 1).sum()) * 64 * D * 2 * 2  # selected + own block, K and V, bf16
+    summ_bytes = float(S * H * (nb - 1) * D * 2)
+    res = dict(name=name, S=S, H=H, N=N, D=D, coarse_scale=wl.coarse_scale, us_per_step=us_mean,
+               us_min=us[0], block_sparsity=1.0 - float(nsel.double().mean()) / (nb - 1),
+               selected_bytes_gb=sel_bytes / 1e9, summary_bytes_gb=summ_bytes / 1e9,
+               hbm_gbs_selected=sel_bytes / (us_mean * 1e-6) / 1e9,
+               hbm_gbs_all=(sel_bytes + summ_bytes) / (us_mean * 1e-6) / 1e9)
+    res["roofline"] = {"bound": "hbm", "kernel": "dash_decode (3 kernels)", "achieved": res["hbm_gbs_selected"],
+                       "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": res["hbm_gbs_selected"] / PEAK_HBM_GBS,
+                       "work": "selected-block bytes = (selected + own block) x 64 keys x D x 2 (K,V) x 2 B"}
+    del w, q, kc, vc, kbar, bufs
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -190,6 +240,7 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=4096, help="oracle rows per CPU worker")
     ap.add_argument("--cpu-workers", type=int, default=16)
     ap.add_argument("--extra", action="store_true", help="also time the 64K prefill")
+    ap.add_argument("--no-decode", action="store_true", help="skip the 96K decode workloads")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -213,6 +264,14 @@ def main():
         r3, _ = bench_prefill("c3", max(2, args.steps // 3), 1, dev)
         log(f"c3: {r3}")
         extra["prefill_64k"] = r3
+
+    if not args.no_decode:
+        dec = {}
+        for name in ("c4cal", "c4"):
+            d = bench_decode(name, max(5, args.steps), args.warmup, dev)
+            log(f"{name}: {d}")
+            dec[name] = d
+        extra["decode_96k"] = dec
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -41,5 +41,6 @@ from .dash_ref import (  # noqa: F401
     forward,
     forward_rows,
     backward,
+    backward_rows,
     decode,
 )

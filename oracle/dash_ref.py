@@ -244,8 +244,8 @@ def forward(q, k, v, prm: Params):
 # ----------------------------------------------------------------------------- backward
 
 
-def backward(q, k, v, dout, prm: Params):
-    """Gradients of the scalar <dout, O> with respect to q, k, v and the summaries.
+def _backward_row(q, k, v, dout, prm: Params, b, h, i, kb, grads):
+    """Accumulate the gradient contributions of query row (b, h, i) into ``grads``.
 
     Per row (notation of the forward): a = softmax weights over the attended
     tokens, D_i = dout_i . o_i,
@@ -262,52 +262,84 @@ def backward(q, k, v, dout, prm: Params):
 
         dq_i    += coarse_scale * sum_b dz_b kbar_b
         dkbar_b += coarse_scale * dz_b q_i
+    """
+    D = q.shape[-1]
+    blk = prm.block
+    sf, sc = prm.scales(D)
+    dq, dk, dv, dkbar = grads["dq"], grads["dk"], grads["dv"], grads["dkbar"]
+    kh, vh = k[b, h], v[b, h]
+    qi = q[b, h, i]
+    sel = select_row(qi, kb, i, prm, D)
+    oi, _, ctx = attend_row(qi, kh, vh, i, sel, prm, D)
+    idx, a = ctx["idx"], ctx["a"]
+    if idx.size == 0:
+        return
+    gi = dout[b, h, i]
+    Di = gi @ oi
+    dl = a * (vh[idx] @ gi - Di)
+    dv[b, h, idx] += np.outer(a, gi)
+    dq[b, h, i] += sf * (dl @ kh[idx])
+    dk[b, h, idx] += sf * np.outer(dl, qi)
+    chosen = ctx["chosen"]
+    if chosen.size == 0:
+        return
+    # G over the selected candidate blocks (the causal own block carries
+    # prior 0 and no gradient into Stage 1).
+    G = dl[: chosen.size * blk].reshape(chosen.size, blk).sum(axis=1)
+    pc = sel["p"]
+    sup = sel["support"]
+    g = np.zeros_like(pc)
+    g[sup] = G / pc[sup]
+    dz = entmax_jvp(pc, g, prm.alpha)
+    cand = sel["cand"]
+    dq[b, h, i] += sc * (dz @ kb[cand])
+    dkbar[b, h, cand] += sc * np.outer(dz, qi)
 
-    Finally mean pooling sends dkbar_b / block to every key of block b.
+
+def _grad_arrays(q):
+    B, H, T, D = q.shape
+    return dict(dq=np.zeros_like(q), dk=np.zeros_like(q), dv=np.zeros_like(q),
+                dkbar=np.zeros((B, H, T // 64, D)))
+
+
+def backward(q, k, v, dout, prm: Params):
+    """Gradients of the scalar <dout, O> with respect to q, k, v and the summaries.
+
+    Sums the per-row contributions of :func:`_backward_row` over every row,
+    then mean pooling sends dkbar_b / block to every key of block b.
     Returns dict(dq, dk, dv, dkbar) (dk includes the pooling path).
     """
     q, k, v, dout = _as64(q), _as64(k), _as64(v), _as64(dout)
     B, H, T, D = q.shape
-    blk = prm.block
-    nb = T // blk
-    sf, sc = prm.scales(D)
-    dq = np.zeros_like(q)
-    dk = np.zeros_like(k)
-    dv = np.zeros_like(v)
-    dkbar = np.zeros((B, H, nb, D))
+    grads = _grad_arrays(q)
     for b in range(B):
         for h in range(H):
-            kb = pool_blocks(k[b, h], blk, prm.storage)
-            kh, vh = k[b, h], v[b, h]
+            kb = pool_blocks(k[b, h], prm.block, prm.storage)
             for i in range(T):
-                qi = q[b, h, i]
-                sel = select_row(qi, kb, i, prm, D)
-                oi, _, ctx = attend_row(qi, kh, vh, i, sel, prm, D)
-                idx, a = ctx["idx"], ctx["a"]
-                if idx.size == 0:
-                    continue
-                gi = dout[b, h, i]
-                Di = gi @ oi
-                dl = a * (vh[idx] @ gi - Di)
-                dv[b, h, idx] += np.outer(a, gi)
-                dq[b, h, i] += sf * (dl @ kh[idx])
-                dk[b, h, idx] += sf * np.outer(dl, qi)
-                chosen = ctx["chosen"]
-                if chosen.size == 0:
-                    continue
-                # G over the selected candidate blocks (the causal own block
-                # carries prior 0 and no gradient into Stage 1).
-                G = dl[: chosen.size * blk].reshape(chosen.size, blk).sum(axis=1)
-                pc = sel["p"]
-                sup = sel["support"]
-                g = np.zeros_like(pc)
-                g[sup] = G / pc[sup]
-                dz = entmax_jvp(pc, g, prm.alpha)
-                cand = sel["cand"]
-                dq[b, h, i] += sc * (dz @ kb[cand])
-                dkbar[b, h, cand] += sc * np.outer(dz, qi)
-            dk[b, h] += np.repeat(dkbar[b, h], blk, axis=0) / blk
-    return dict(dq=dq, dk=dk, dv=dv, dkbar=dkbar)
+                _backward_row(q, k, v, dout, prm, b, h, i, kb, grads)
+            grads["dk"][b, h] += np.repeat(grads["dkbar"][b, h], prm.block, axis=0) / prm.block
+    return grads
+
+
+def backward_rows(q, k, v, dout, prm: Params, rows):
+    """The contributions of the given query rows (b, h, i) only.
+
+    Returns the same dict as :func:`backward` but summed over ``rows``: dq
+    is complete for those rows; dk, dv and dkbar are complete for any key
+    block attended only by rows in ``rows`` (e.g. the last blocks of a causal
+    head when ``rows`` holds every row from some position on).  dk includes
+    the pooling path of the accumulated dkbar.
+    """
+    q, k, v, dout = _as64(q), _as64(k), _as64(v), _as64(dout)
+    grads = _grad_arrays(q)
+    pooled = {}
+    for (b, h, i) in rows:
+        if (b, h) not in pooled:
+            pooled[(b, h)] = pool_blocks(k[b, h], prm.block, prm.storage)
+        _backward_row(q, k, v, dout, prm, b, h, i, pooled[(b, h)], grads)
+    for (b, h) in pooled:
+        grads["dk"][b, h] += np.repeat(grads["dkbar"][b, h], prm.block, axis=0) / prm.block
+    return grads
 
 
 # ----------------------------------------------------------------------------- decode

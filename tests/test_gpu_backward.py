@@ -1,0 +1,104 @@
+"""GPU backward parity: dash_bwd (through the C ABI) against the float64 oracle.
+
+Gradients must match within 5e-2 relative L2 (tests/parity.py).  Small
+cases compare every gradient; the full-size training workload
+(B2 H16 T16384 D128, alpha in {1.25, 1.5}) compares dQ on sampled rows and
+dK, dV and the summary gradient on the last key blocks of sampled heads,
+which only the rows from those blocks on attend.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from differentiable_adaptive_block_amd import inputs
+from parity import rel_l2
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = 5e-2
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _np64(t):
+    return t.double().cpu().numpy()
+
+
+def _run(w, alpha, causal, cs):
+    from differentiable_adaptive_block_amd import api
+    r = api.forward(w["q"], w["k"], w["v"], alpha=alpha, causal=causal, coarse_scale=cs, want_mask=False)
+    g = api.backward(w["q"], w["k"], w["v"], r["o"], r["lse"], w["dout"], r["kbar"], r["sel"], r["params"])
+    torch.cuda.synchronize()
+    return r, g
+
+
+SMALL = [
+    ("c1", 1, 2, 512, 64, "fp32", False, 1.5, 1.0, None),
+    ("c1s", 1, 2, 512, 64, "fp32", False, 1.5, 16.0, None),
+    ("fp32-causal-a125", 1, 1, 320, 128, "fp32", True, 1.25, 4.0, (1, 3)),
+    ("bf16-causal-ragged", 1, 2, 1088, 128, "bf16", True, 1.5, 4.0, (1, 4)),
+    ("bf16-causal-dense", 1, 1, 1024, 128, "bf16", True, 1.25, 1.0, (1, 8)),
+    ("bf16-causal-d64", 1, 2, 576, 64, "bf16", True, 1.25, 4.0, (1, 3)),
+    ("bf16-noncausal-a2", 1, 2, 512, 128, "bf16", False, 2.0, 4.0, (1, 3)),
+    ("bf16-causal-a1", 1, 1, 512, 128, "bf16", True, 1.0, 1.0, (1, 3)),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_backward_small_full_oracle(case):
+    name, B, H, T, D, dtype, causal, alpha, csm, planted = case
+    _say(f"[backward] {name} B{B} H{H} T{T} D{D} {dtype} causal={causal} alpha={alpha}")
+    w = inputs.make_prefill(B, H, T, D, dtype, causal, planted, seed=17 + T + D, device="cpu", with_dout=True)
+    w = {k: v.to(DEV) for k, v in w.items()}
+    cs = csm / math.sqrt(D)
+    _, g = _run(w, alpha, causal, cs)
+    prm = oracle.Params(alpha=alpha, causal=causal, coarse_scale=cs, storage=dtype)
+    ref = oracle.backward(*(_np64(w[x]) for x in ("q", "k", "v", "dout")), prm)
+    errs = {n: rel_l2(_np64(g[n]), ref[n]) for n in ("dq", "dk", "dv", "dkbar")}
+    _say(f"  rel-L2 {errs}")
+    for n, e in errs.items():
+        assert e <= TOL, (name, n, e)
+
+
+def test_backward_deterministic():
+    w = inputs.make_prefill(1, 2, 1024, 128, "bf16", True, (1, 4), seed=4, device="cpu", with_dout=True)
+    w = {k: v.to(DEV) for k, v in w.items()}
+    _, g1 = _run(w, 1.5, True, 3 / math.sqrt(128))
+    _, g2 = _run(w, 1.5, True, 3 / math.sqrt(128))
+    for n in ("dq", "dk", "dv", "dkbar"):
+        assert torch.equal(g1[n], g2[n]), n
+
+
+@pytest.mark.parametrize("alpha", [1.25, 1.5])
+def test_backward_training_16k_sampled(alpha):
+    wl = inputs.CONFIGS["c5"]
+    sh = wl.shape
+    _say(f"[backward] c5 full size {sh} alpha={alpha} (sampled)")
+    w = inputs.make_prefill(sh["B"], sh["H"], sh["T"], sh["D"], wl.dtype, True, wl.planted, wl.seed, device=DEV,
+                            with_dout=True)
+    _, g = _run(w, alpha, True, wl.coarse_scale)
+    T = sh["T"]
+    nb = T // 64
+    prm = oracle.Params(alpha=alpha, causal=True, coarse_scale=wl.coarse_scale, storage="bf16")
+    rng = np.random.default_rng(2)
+    for (b, h) in [(0, int(rng.integers(sh["H"]))), (1, int(rng.integers(sh["H"])))]:
+        x = {n: _np64(w[n][b:b + 1, h:h + 1]) for n in ("q", "k", "v", "dout")}
+        tail = 4 * 64  # rows attending the last 4 key blocks
+        rows = [(0, 0, i) for i in range(T - tail, T)]
+        rows += [(0, 0, int(i)) for i in rng.choice(T - tail, size=24, replace=False)]
+        ref = oracle.backward_rows(x["q"], x["k"], x["v"], x["dout"], prm, rows)
+        ridx = np.array([i for (_, _, i) in rows])
+        e_dq = rel_l2(_np64(g["dq"][b, h])[ridx], ref["dq"][0, 0][ridx])
+        e_dk = rel_l2(_np64(g["dk"][b, h])[T - tail:], ref["dk"][0, 0][T - tail:])
+        e_dv = rel_l2(_np64(g["dv"][b, h])[T - tail:], ref["dv"][0, 0][T - tail:])
+        e_kb = rel_l2(_np64(g["dkbar"][b, h])[nb - 4:nb - 1], ref["dkbar"][0, 0][nb - 4:nb - 1])
+        _say(f"  (b={b}, h={h}) rel-L2 dq {e_dq:.2e} dk {e_dk:.2e} dv {e_dv:.2e} dkbar {e_kb:.2e}")
+        assert max(e_dq, e_dk, e_dv, e_kb) <= TOL

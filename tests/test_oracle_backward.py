@@ -107,3 +107,16 @@ def test_summary_gradient_matches_finite_differences(alpha):
     # dk contains the pooling path dkbar / 64 on every key of the block
     g_no_pool = g["dk"] - np.repeat(g["dkbar"][0, 0], 64, axis=0)[None, None] / 64
     assert np.abs(g_no_pool).max() > 0
+
+
+def test_backward_rows_matches_full_backward():
+    T, D = 256, 16
+    q, k, v, dout = _inputs(40, T, D, True)
+    prm = Params(causal=True, alpha=1.5, storage="bf16", coarse_scale=4.0 / math.sqrt(D))
+    full = oracle.backward(q, k, v, dout, prm)
+    rows = [(0, 0, i) for i in range(128, T)]  # every row that attends blocks 2 and 3
+    part = oracle.backward_rows(q, k, v, dout, prm, rows)
+    np.testing.assert_allclose(part["dq"][0, 0, 128:], full["dq"][0, 0, 128:], atol=1e-13)
+    for name in ["dk", "dv"]:
+        np.testing.assert_allclose(part[name][0, 0, 128:], full[name][0, 0, 128:], atol=1e-13)
+    np.testing.assert_allclose(part["dkbar"][0, 0, 2:], full["dkbar"][0, 0, 2:], atol=1e-13)
