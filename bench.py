@@ -181,6 +181,54 @@ def bench_prefill(name, steps, warmup, device, log_prefix=""):
     return res, (B, H, T, D)
 
 
+def bench_training(alpha, steps, warmup, device):
+    """Time one training step (dash_fwd + dash_bwd) on the 16K training workload."""
+    from differentiable_adaptive_block_amd import api, inputs
+
+    wl = inputs.CONFIGS["c5"]
+    sh = wl.shape
+    w = inputs.make_prefill(sh["B"], sh["H"], sh["T"], sh["D"], wl.dtype, True, wl.planted, wl.seed, device=device,
+                            with_dout=True)
+    q, k, v, dout = w["q"], w["k"], w["v"], w["dout"]
+    B, H, T, D = q.shape
+    r = api.forward(q, k, v, alpha=alpha, causal=True, coarse_scale=wl.coarse_scale, want_mask=True)
+    torch.cuda.synchronize()
+    sum_sel = int(r["sel"].nsel.to(torch.int64).sum())
+
+    def step(ev=None):
+        f = api.forward(q, k, v, alpha=alpha, causal=True, coarse_scale=wl.coarse_scale, want_mask=False)
+        if ev is not None:
+            ev[0].record()
+        g = api.backward(q, k, v, f["o"], f["lse"], dout, f["kbar"], f["sel"], f["params"])
+        if ev is not None:
+            ev[1].record()
+        return g
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [_events(2) for _ in range(steps)]
+    t0, t1 = _events(2)
+    t0.record()
+    for s_ in range(steps):
+        step(evs[s_])
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    bwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    pairs = 64 * sum_sel + B * H * (T // 64) * (64 * 65 // 2)
+    res = dict(alpha=alpha, B=B, H=H, T=T, D=D, ms_per_step=ms, fwd_ms=ms - bwd_ms, bwd_ms=bwd_ms,
+               tokens_per_s=B * T / (ms / 1e3),
+               pair_density=sum_sel / (B * H * sum(i // 64 for i in range(T))),
+               useful_fwd_tflop=4.0 * D * pairs / 1e12, useful_bwd_tflop=10.0 * D * pairs / 1e12)
+    res["bwd_tflops"] = res["useful_bwd_tflop"] / (bwd_ms / 1e3)
+    res["bwd_mfma_frac"] = res["bwd_tflops"] / PEAK_BF16_TFLOPS
+    res["step_tflops"] = (res["useful_fwd_tflop"] + res["useful_bwd_tflop"]) / (ms / 1e3)
+    del w, q, k, v, dout, r
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_decode(name, steps, warmup, device):
     """Time dash_decode (select + split-KV attend + combine) on a named decode workload."""
     from differentiable_adaptive_block_amd import _lib, api, inputs
@@ -241,6 +289,7 @@ def main():
     ap.add_argument("--cpu-workers", type=int, default=16)
     ap.add_argument("--extra", action="store_true", help="also time the 64K prefill")
     ap.add_argument("--no-decode", action="store_true", help="skip the 96K decode workloads")
+    ap.add_argument("--no-training", action="store_true", help="skip the 16K training step")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -272,6 +321,14 @@ def main():
             log(f"{name}: {d}")
             dec[name] = d
         extra["decode_96k"] = dec
+
+    if not args.no_training:
+        tr = {}
+        for alpha in (1.25, 1.5):
+            t = bench_training(alpha, max(3, args.steps // 2), 1, dev)
+            log(f"training alpha={alpha}: {t}")
+            tr[f"alpha_{alpha}"] = t
+        extra["training_16k"] = tr
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -1,0 +1,145 @@
+"""The C ABI on the host (no GPU needed): exports and argument validation.
+
+Every call here fails validation, which happens before anything is launched,
+so no device work is enqueued.  Fake device pointers are 16-byte aligned
+integers that are never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from differentiable_adaptive_block_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dash.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        from differentiable_adaptive_block_amd import build
+        build.build()
+    return _lib.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dash_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def _params(**kw):
+    p = _lib.DashParams()
+    p.B, p.H, p.T, p.D, p.block = 1, 2, 256, 128, 64
+    p.alpha, p.causal, p.fine_scale, p.coarse_scale, p.dtype = 1.5, 1, 0.088, 0.088, _lib.DASH_BF16
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+FAKE = 0x10000  # aligned, never dereferenced
+
+
+def _sel(**kw):
+    s = _lib.DashSel()
+    for f, _ in s._fields_:
+        setattr(s, f, FAKE)
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+def _fwd(L, p, **ptrs):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, kbar=FAKE)
+    a.update(ptrs)
+    return L.dash_fwd(ctypes.byref(p), a["q"], a["k"], a["v"], a["o"], a["lse"], a["kbar"],
+                      ctypes.byref(_sel()), None, 0, None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("T", 100, _lib.DASH_EINVAL),            # not a multiple of 64
+    ("T", 0, _lib.DASH_EINVAL),
+    ("B", 0, _lib.DASH_EINVAL),
+    ("alpha", 2.5, _lib.DASH_EINVAL),
+    ("alpha", 0.5, _lib.DASH_EINVAL),
+    ("alpha", float("nan"), _lib.DASH_EINVAL),
+    ("fine_scale", 0.0, _lib.DASH_EINVAL),
+    ("coarse_scale", float("inf"), _lib.DASH_EINVAL),
+    ("causal", 2, _lib.DASH_EINVAL),
+    ("dtype", 7, _lib.DASH_EINVAL),
+    ("block", 32, _lib.DASH_EUNSUPPORTED),
+    ("D", 96, _lib.DASH_EUNSUPPORTED),
+    ("T", 65536 + 64, _lib.DASH_EUNSUPPORTED),
+])
+def test_fwd_rejects_bad_params(L, field, value, status):
+    p = _params(**{field: value})
+    assert _fwd(L, p) == status
+    assert L.dash_last_error().decode() != ""
+
+
+def test_fwd_rejects_null_and_misaligned_pointers(L):
+    p = _params()
+    assert _fwd(L, p, q=None) == _lib.DASH_EINVAL
+    assert _fwd(L, p, o=FAKE + 2) == _lib.DASH_EINVAL
+    bad = _sel(tau=None)
+    assert L.dash_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(bad), None, 0,
+                      None) == _lib.DASH_EINVAL
+    assert L.dash_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0,
+                      None) == _lib.DASH_EINVAL
+
+
+def test_bwd_checks_workspace_size(L):
+    p = _params()
+    need = L.dash_bwd_workspace_bytes(ctypes.byref(p))
+    assert need > 0
+    st = L.dash_bwd(ctypes.byref(p), *([FAKE] * 7), ctypes.byref(_sel()), FAKE, FAKE, FAKE, FAKE, FAKE, need - 1,
+                    None)
+    assert st == _lib.DASH_EWORKSPACE
+    assert "workspace" in L.dash_last_error().decode()
+
+
+def test_sel_sizes(L):
+    p = _params(T=1088)
+    sizes = _lib.sel_sizes(p)
+    nb, nbw, nt = 17, 1, 9
+    assert sizes == [2 * 1088, 2 * 1088, 2 * 1088, 2 * 1088 * nbw, 2 * nt, 2 * nt * nb, 2 * nt * nbw]
+    assert _lib.query_tile() == 128
+    with pytest.raises(_lib.DashError) as e:
+        _lib.sel_sizes(_params(D=32))
+    assert e.value.status == _lib.DASH_EUNSUPPORTED
+
+
+def test_decode_validation(L):
+    p = _lib.DashDecodeParams()
+    p.S, p.H, p.N, p.D, p.block = 2, 2, 1024, 128, 64
+    p.alpha, p.fine_scale, p.coarse_scale, p.dtype = 1.5, 0.088, 0.088, _lib.DASH_BF16
+    need = L.dash_decode_workspace_bytes(ctypes.byref(p))
+    assert need > 0
+    args = [FAKE] * 5 + [None, None, None, FAKE]
+    assert L.dash_decode(ctypes.byref(p), *args, need - 1, None) == _lib.DASH_EWORKSPACE
+    p.N = 1000
+    assert L.dash_decode(ctypes.byref(p), *args, need, None) == _lib.DASH_EINVAL
+    p.N, p.dtype = 1024, _lib.DASH_F32
+    assert L.dash_decode(ctypes.byref(p), *args, need, None) == _lib.DASH_EUNSUPPORTED
+    p.dtype, p.D = _lib.DASH_BF16, 64
+    assert L.dash_decode(ctypes.byref(p), *args, need, None) == _lib.DASH_EUNSUPPORTED
+    p.D, p.N = 128, 64 * 4096
+    assert L.dash_decode(ctypes.byref(p), *args, need, None) == _lib.DASH_EUNSUPPORTED
+
+
+def test_pool_accepts_long_sequences_in_validation(L):
+    p = _params(T=98304)
+    # null k is rejected after the shape checks pass (no 65536 limit for pooling)
+    assert L.dash_pool(ctypes.byref(p), None, FAKE, None) == _lib.DASH_EINVAL
+    assert "k and kbar" in L.dash_last_error().decode()
