@@ -58,6 +58,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t vs[64 * KP];
   __shared__ __attribute__((aligned(16))) bf16_t kt[D * VP];
   __shared__ float pri[4][32 * 32];
+  __shared__ int lst[DASH_MAX_NB];
 
   const int nb = a.T / DASH_BLOCK;
   const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
@@ -77,10 +78,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + bh * a.T * D;
   const bf16_t* dO = reinterpret_cast<const bf16_t*>(a.dout) + bh * a.T * D;
   const bf16_t* KB = reinterpret_cast<const bf16_t*>(a.kbar) + bh * nb * D;
-  const int* list = a.tile_blk + (bh * ntile + tile) * nb;
+  const int* glist = a.tile_blk + (bh * ntile + tile) * nb;
   const int cnt = a.tile_cnt[bh * ntile + tile];
   const CoarseArith ca = a.ca;
   const float sl2 = a.fine_scale * LOG2E_F;
+  for (int x = threadIdx.x; x < cnt; x += 256) lst[x] = glist[x];
+  __syncthreads();
+  const int* list = lst;
 
   bf16x8 qb[D / 16], dob[D / 16];
   float tau_i = 0.f, ln_i = 0.f, lse2 = 0.f, dlt = 0.f;
@@ -195,11 +199,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         dp = mfma32(av, dob[st], dp);
       }
       float ds[16];
+      const float off = pr - lse2;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float x = s[r] * sl2 + pr;
-        if (diag && b * DASH_BLOCK + 32 * t + acc_row32(r, l) > i) x = -INFINITY;
-        const float p = exp2f(x - lse2);
+        float sv = s[r];
+        if (diag && b * DASH_BLOCK + 32 * t + acc_row32(r, l) > i) sv = -INFINITY;
+        const float p = __builtin_amdgcn_exp2f(fmaf(sv, sl2, off));
         ds[r] = p * (dp[r] - dlt);
         gsum += ds[r];
       }
@@ -261,8 +266,8 @@ __global__ __launch_bounds__(128) void bwd_entmax_kernel(BwdArgs a) {
     const size_t gi = gidx(bh, ntile, tile, nb, e, rt);
     const float lp2 = a.pbuf[gi];
     if (lp2 == -INFINITY) continue;
-    ss += exp2f(am2 * lp2);
-    ssg += a.gbuf[gi] * exp2f(am1n * lp2);
+    ss += __builtin_amdgcn_exp2f(am2 * lp2);
+    ssg += a.gbuf[gi] * __builtin_amdgcn_exp2f(am1n * lp2);
   }
   const float ratio = ss > 0.f ? ssg / ss : 0.f;
   for (int e = 0; e < cnt; ++e) {
@@ -271,7 +276,8 @@ __global__ __launch_bounds__(128) void bwd_entmax_kernel(BwdArgs a) {
     float dz = 0.f;
     if (!(a.causal && b >= own)) {
       const float lp2 = a.pbuf[gi];
-      if (lp2 != -INFINITY) dz = a.gbuf[gi] * exp2f(am1n * lp2) - exp2f(am2 * lp2) * ratio;
+      if (lp2 != -INFINITY)
+        dz = a.gbuf[gi] * __builtin_amdgcn_exp2f(am1n * lp2) - __builtin_amdgcn_exp2f(am2 * lp2) * ratio;
     }
     a.gbuf[gi] = dz;
   }
@@ -279,38 +285,94 @@ __global__ __launch_bounds__(128) void bwd_entmax_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------- dK, dV, dkbar
 
+// Work item of bwd_dkdv: a 64-query chunk (tile t, half c) that sees at
+// least one of the workgroup's two key blocks; slot[k] = position of block
+// b0 + k in tile t's list, or -1 when the tile does not list it or (causal)
+// the chunk's queries all precede it.
+struct DkdvItem {
+  int t, c, slot0, slot1;
+};
+
+__device__ __forceinline__ int list_slot(const uint32_t* bits, int b) {
+  const uint32_t word = bits[b >> 5];
+  if (!((word >> (b & 31)) & 1u)) return -1;
+  int slot = __popc(word & ((1u << (b & 31)) - 1u));
+  for (int x = 0; x < (b >> 5); ++x) slot += __popc(bits[x]);
+  return slot;
+}
+
+// First item at or after (t, c); t == ntile when there is none.
+__device__ __forceinline__ DkdvItem dkdv_find(const BwdArgs& a, size_t bh, int ntile, int nbw, int b0, int nblk,
+                                              int t, int c) {
+  DkdvItem it;
+  for (; t < ntile; ++t, c = 0) {
+    const uint32_t* bits = a.tile_bits + (bh * ntile + t) * nbw;
+    const int s0 = list_slot(bits, b0);
+    const int s1 = nblk > 1 ? list_slot(bits, b0 + 1) : -1;
+    if (s0 < 0 && s1 < 0) continue;
+    for (; c < DASH_QTILE / 64; ++c) {
+      const int q0 = t * DASH_QTILE + c * 64;
+      if (q0 >= a.T) break;
+      const int ob = q0 / DASH_BLOCK;
+      it.slot0 = (a.causal && ob < b0) ? -1 : s0;
+      it.slot1 = (a.causal && ob < b0 + 1) ? -1 : s1;
+      if (it.slot0 >= 0 || it.slot1 >= 0) {
+        it.t = t;
+        it.c = c;
+        return it;
+      }
+    }
+  }
+  it.t = ntile;
+  it.c = 0;
+  it.slot0 = it.slot1 = -1;
+  return it;
+}
+
+// Key-block-major: a workgroup of 8 waves owns 128 keys (blocks b0, b0+1)
+// and walks the 64-query chunks of the query tiles that list either block.
+// Wave w: block kb = w/4, key half kh = (w/2)&1, query half qh = w&1.  Per
+// chunk and wave (32 queries x 32 keys), with keys as MFMA columns:
+//   S  = Q K^T, dP = dO V^T     (D/16 MFMA each, Q/dO rows as operand A)
+//   dV^T += dO^T P, dK^T += Q^T dS   (dO^T, Q^T staged transposed in LDS)
+// The next item's Q/dO rows are loaded into registers while the current
+// one is computed.  dkbar_b = coarse_scale sum_q dz_qb q_q accumulates from
+// the same staging registers.
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int KP = D + 8;
   constexpr int QP = 64 + 4;
   constexpr int CH = D / 8;
-  constexpr int NL = 64 * CH / 256;  // uint4 per thread for a 64-row tile
-  constexpr int NP = 32 * CH / 256;  // row pairs per thread
-  // one LDS buffer: [ks | vs | qs | qt | os | ot]; after the main loop the
-  // qs..ot part (>= 2 x 2 x (D/32) x 16 x 64 floats) holds the cross-wave sums
-  constexpr int ROWT = 64 * KP;  // bf16 elements of a 64-row tile
-  constexpr int COLT = D * QP;   // bf16 elements of a transposed tile
-  __shared__ __attribute__((aligned(16))) bf16_t smem[4 * ROWT + 2 * COLT];
-  static_assert((2 * ROWT + 2 * COLT) * 2 >= 2 * 2 * (D / 32) * 16 * 64 * 4, "reduction space");
+  constexpr int ROWK = 128 * KP;
+  constexpr int ROWQ = 64 * KP;
+  constexpr int COLQ = D * QP;
+  constexpr int NKL = 128 * CH / 512;  // K (and V) uint4 per thread for the 128 key rows
+  constexpr int NITEM = 32 * CH;       // (row pair, chunk) staging items per query chunk
+  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * ROWK + 2 * ROWQ + 2 * COLQ];
+  static_assert((2 * ROWK + 2 * ROWQ + 2 * COLQ) * 2 >= 4 * 2 * (D / 32) * 16 * 64 * 4, "reduction space");
+  static_assert((2 * ROWK + 2 * ROWQ + 2 * COLQ) * 2 >= 2 * 32 * D * 4, "dkbar reduction space");
   bf16_t* ks = smem;
-  bf16_t* vs = ks + ROWT;
-  bf16_t* qs = vs + ROWT;
-  bf16_t* qt = qs + ROWT;
-  bf16_t* os_ = qt + COLT;
-  bf16_t* ot = os_ + ROWT;
-  __shared__ float prq[64], lsq[64], dlq[64], dzq[64];
-  __shared__ float kbg[D];
+  bf16_t* vs = ks + ROWK;
+  bf16_t* qs = vs + ROWK;
+  bf16_t* os_ = qs + ROWQ;
+  bf16_t* qt = os_ + ROWQ;
+  bf16_t* ot = qt + COLQ;
+  __shared__ float prq[2][64], dzq[2][64], lsq[64], dlq[64];
+  __shared__ float kbg[2][D];
 
   const int nb = a.T / DASH_BLOCK;
   const int nbw = (nb + 31) / 32;
   const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
+  const int ngrp = (nb + 1) / 2;
   const int nwg = gridDim.x, wg = blockIdx.x;
   const int logical = (nwg % 8 == 0) ? (wg % 8) * (nwg / 8) + wg / 8 : wg;
-  const size_t bh = logical / nb;
-  const int b = logical % nb;  // early blocks (most query tiles when causal) first
+  const size_t bh = logical / ngrp;
+  const int b0 = 2 * (logical % ngrp);  // early blocks (most query tiles when causal) first
+  const int nblk = min(2, nb - b0);
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, j = l & 31, h = l >> 5;
-  const int kh = w & 1, qh = w >> 1;
+  const int kb = w >> 2, kh = (w >> 1) & 1, qh = w & 1;
+  const int wb = b0 + kb;  // this wave's key block
 
   const bf16_t* Q = reinterpret_cast<const bf16_t*>(a.q) + bh * a.T * D;
   const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + bh * a.T * D;
@@ -318,16 +380,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const bf16_t* dO = reinterpret_cast<const bf16_t*>(a.dout) + bh * a.T * D;
   const float sl2 = a.fine_scale * LOG2E_F;
 
-  // the key block, row-major
+  // the two key blocks, row-major
   {
-    const bf16_t* kb0 = K + (size_t)b * DASH_BLOCK * D;
-    const bf16_t* vb0 = V + (size_t)b * DASH_BLOCK * D;
+    const bf16_t* kb0 = K + (size_t)b0 * DASH_BLOCK * D;
+    const bf16_t* vb0 = V + (size_t)b0 * DASH_BLOCK * D;
 #pragma unroll
-    for (int x = 0; x < NL; ++x) {
-      const int idx = tid + 256 * x;
+    for (int x = 0; x < NKL; ++x) {
+      const int idx = tid + 512 * x;
       const int row = idx / CH, ch = idx % CH;
-      *reinterpret_cast<uint4*>(&ks[row * KP + ch * 8]) = *reinterpret_cast<const uint4*>(kb0 + (size_t)row * D + ch * 8);
-      *reinterpret_cast<uint4*>(&vs[row * KP + ch * 8]) = *reinterpret_cast<const uint4*>(vb0 + (size_t)row * D + ch * 8);
+      if (row < 64 * nblk) {
+        *reinterpret_cast<uint4*>(&ks[row * KP + ch * 8]) = *reinterpret_cast<const uint4*>(kb0 + (size_t)row * D + ch * 8);
+        *reinterpret_cast<uint4*>(&vs[row * KP + ch * 8]) = *reinterpret_cast<const uint4*>(vb0 + (size_t)row * D + ch * 8);
+      }
     }
   }
   f32x16 dva[D / 32], dka[D / 32];
@@ -335,88 +399,123 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) { dva[dt][r] = 0.f; dka[dt][r] = 0.f; }
-  float kbacc = 0.f;  // dkbar_b[tid] for tid < D
-
-  const int t0 = a.causal ? (b * DASH_BLOCK) / DASH_QTILE : 0;
-  for (int t = t0; t < ntile; ++t) {
-    const uint32_t* bits = a.tile_bits + (bh * ntile + t) * nbw;
-    const uint32_t word = bits[b >> 5];
-    if (!((word >> (b & 31)) & 1u)) continue;
-    int slot = __popc(word & ((1u << (b & 31)) - 1u));
-    for (int x = 0; x < (b >> 5); ++x) slot += __popc(bits[x]);
-    for (int c = 0; c < DASH_QTILE / 64; ++c) {
-      const int q0 = t * DASH_QTILE + c * 64;
-      if (q0 >= a.T) break;
-      if (a.causal && q0 / DASH_BLOCK < b) continue;  // queries before the block never see it
-      const bool diag = a.causal && q0 / DASH_BLOCK == b;
-      __syncthreads();
-      // stage Q and dO rows q0..q0+63 (row-major and transposed) and per-row scalars
+  float kbp[2][8];  // dkbar partial of this thread's staging columns
 #pragma unroll
-      for (int x = 0; x < NP; ++x) {
-        const int idx = tid + 256 * x;
-        const int pr = idx / CH, ch = idx % CH;
-        const size_t r0 = (size_t)(q0 + 2 * pr) * D + ch * 8;
-        const uint4 q0v = *reinterpret_cast<const uint4*>(Q + r0);
-        const uint4 q1v = *reinterpret_cast<const uint4*>(Q + r0 + D);
-        const uint4 o0v = *reinterpret_cast<const uint4*>(dO + r0);
-        const uint4 o1v = *reinterpret_cast<const uint4*>(dO + r0 + D);
-        *reinterpret_cast<uint4*>(&qs[(2 * pr) * KP + ch * 8]) = q0v;
-        *reinterpret_cast<uint4*>(&qs[(2 * pr + 1) * KP + ch * 8]) = q1v;
-        *reinterpret_cast<uint4*>(&os_[(2 * pr) * KP + ch * 8]) = o0v;
-        *reinterpret_cast<uint4*>(&os_[(2 * pr + 1) * KP + ch * 8]) = o1v;
-        const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&q0v);
-        const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&q1v);
-        const uint32_t* b0 = reinterpret_cast<const uint32_t*>(&o0v);
-        const uint32_t* b1 = reinterpret_cast<const uint32_t*>(&o1v);
+  for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kbp[k2][e] = 0.f;
+
+  // staging registers: rows (2pr, 2pr+1), 16-byte chunk ch, of Q and dO
+  const bool stager = tid < NITEM;
+  const int spr = tid / CH, sch = tid % CH;
+  uint4 rq0, rq1, ro0, ro1;
+  float s_pr0 = 0.f, s_pr1 = 0.f, s_dz0 = 0.f, s_dz1 = 0.f, s_ls = 0.f, s_dl = 0.f;
+  auto prefetch = [&](const DkdvItem& it) {
+    const int q0 = it.t * DASH_QTILE + it.c * 64;
+    if (stager) {
+      const size_t r0 = (size_t)(q0 + 2 * spr) * D + sch * 8;
+      rq0 = *reinterpret_cast<const uint4*>(Q + r0);
+      rq1 = *reinterpret_cast<const uint4*>(Q + r0 + D);
+      ro0 = *reinterpret_cast<const uint4*>(dO + r0);
+      ro1 = *reinterpret_cast<const uint4*>(dO + r0 + D);
+    }
+    if (tid < 64) {
+      const int row = it.c * 64 + tid;
+      s_ls = a.lse[bh * a.T + q0 + tid] * LOG2E_F;
+      s_dl = a.delta[bh * a.T + q0 + tid];
+      if (it.slot0 >= 0) {
+        const size_t gi = gidx(bh, ntile, it.t, nb, it.slot0, row);
+        s_pr0 = a.pbuf[gi];
+        s_dz0 = a.gbuf[gi];
+      } else { s_pr0 = -INFINITY; s_dz0 = 0.f; }
+      if (it.slot1 >= 0) {
+        const size_t gi = gidx(bh, ntile, it.t, nb, it.slot1, row);
+        s_pr1 = a.pbuf[gi];
+        s_dz1 = a.gbuf[gi];
+      } else { s_pr1 = -INFINITY; s_dz1 = 0.f; }
+    }
+  };
+
+  DkdvItem it = dkdv_find(a, bh, ntile, nbw, b0, nblk, a.causal ? (b0 * DASH_BLOCK) / DASH_QTILE : 0, 0);
+  if (it.t < ntile) prefetch(it);
+  while (it.t < ntile) {
+    const int q0 = it.t * DASH_QTILE + it.c * 64;
+    __syncthreads();  // the previous item's LDS reads are done
+    if (stager) {
+      *reinterpret_cast<uint4*>(&qs[(2 * spr) * KP + sch * 8]) = rq0;
+      *reinterpret_cast<uint4*>(&qs[(2 * spr + 1) * KP + sch * 8]) = rq1;
+      *reinterpret_cast<uint4*>(&os_[(2 * spr) * KP + sch * 8]) = ro0;
+      *reinterpret_cast<uint4*>(&os_[(2 * spr + 1) * KP + sch * 8]) = ro1;
+      const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&rq0);
+      const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&rq1);
+      const uint32_t* c0 = reinterpret_cast<const uint32_t*>(&ro0);
+      const uint32_t* c1 = reinterpret_cast<const uint32_t*>(&ro1);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = (e & 1) * 16;
+        *reinterpret_cast<uint32_t*>(&qt[(sch * 8 + e) * QP + 2 * spr]) =
+            ((a0[e >> 1] >> sh) & 0xFFFFu) | (((a1[e >> 1] >> sh) & 0xFFFFu) << 16);
+        *reinterpret_cast<uint32_t*>(&ot[(sch * 8 + e) * QP + 2 * spr]) =
+            ((c0[e >> 1] >> sh) & 0xFFFFu) | (((c1[e >> 1] >> sh) & 0xFFFFu) << 16);
+      }
+    }
+    if (tid < 64) {
+      prq[0][tid] = s_pr0 - s_ls;  // -inf stays -inf
+      prq[1][tid] = s_pr1 - s_ls;
+      dzq[0][tid] = s_dz0;
+      dzq[1][tid] = s_dz1;
+      lsq[tid] = s_ls;
+      dlq[tid] = s_dl;
+    }
+    __syncthreads();
+    if (stager) {
+      // dkbar partials from the staged rows
+      const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&rq0);
+      const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&rq1);
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const float z0 = dzq[k2][2 * spr], z1 = dzq[k2][2 * spr + 1];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int sh = (e & 1) * 16;
-          *reinterpret_cast<uint32_t*>(&qt[(ch * 8 + e) * QP + 2 * pr]) =
-              ((a0[e >> 1] >> sh) & 0xFFFFu) | (((a1[e >> 1] >> sh) & 0xFFFFu) << 16);
-          *reinterpret_cast<uint32_t*>(&ot[(ch * 8 + e) * QP + 2 * pr]) =
-              ((b0[e >> 1] >> sh) & 0xFFFFu) | (((b1[e >> 1] >> sh) & 0xFFFFu) << 16);
+          const uint32_t wa = a0[e >> 1], wb2 = a1[e >> 1];
+          const float qa = __uint_as_float((e & 1) ? (wa & 0xFFFF0000u) : (wa << 16));
+          const float qc = __uint_as_float((e & 1) ? (wb2 & 0xFFFF0000u) : (wb2 << 16));
+          kbp[k2][e] = fmaf(z0, qa, fmaf(z1, qc, kbp[k2][e]));
         }
       }
-      if (tid < 64) {
-        const size_t gi = gidx(bh, ntile, t, nb, slot, c * 64 + tid);
-        prq[tid] = a.pbuf[gi];
-        dzq[tid] = a.gbuf[gi];
-        lsq[tid] = a.lse[bh * a.T + q0 + tid] * LOG2E_F;
-        dlq[tid] = a.delta[bh * a.T + q0 + tid];
-      }
-      __syncthreads();
-      // S = Q K^T and dP = dO V^T for this wave's 32 queries x 32 keys
+    }
+    const DkdvItem nx = dkdv_find(a, bh, ntile, nbw, b0, nblk, it.c + 1 < DASH_QTILE / 64 ? it.t : it.t + 1,
+                                  it.c + 1 < DASH_QTILE / 64 ? it.c + 1 : 0);
+    if (nx.t < ntile) prefetch(nx);
+    const int wslot = kb == 0 ? it.slot0 : it.slot1;
+    if (wslot >= 0) {
+      const bool diag = a.causal && q0 / DASH_BLOCK == wb;
       f32x16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
+      const int krow = 64 * kb + 32 * kh + j;
 #pragma unroll
       for (int st = 0; st < D / 16; ++st) {
         const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&qs[(32 * qh + j) * KP + 16 * st + 8 * h]);
         const bf16x8 ao = *reinterpret_cast<const bf16x8*>(&os_[(32 * qh + j) * KP + 16 * st + 8 * h]);
-        const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&ks[(32 * kh + j) * KP + 16 * st + 8 * h]);
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&vs[(32 * kh + j) * KP + 16 * st + 8 * h]);
+        const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&ks[krow * KP + 16 * st + 8 * h]);
+        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&vs[krow * KP + 16 * st + 8 * h]);
         s = mfma32(aq, bk, s);
         dp = mfma32(ao, bv, dp);
       }
-      float pv[16], dsv[16];
-      const int key = b * DASH_BLOCK + 32 * kh + j;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ql = 32 * qh + acc_row32(r, l);
-        float x = s[r] * sl2 + prq[ql];
-        if (diag && key > q0 + ql) x = -INFINITY;
-        const float p = exp2f(x - lsq[ql]);
-        pv[r] = p;
-        dsv[r] = p * (dp[r] - dlq[ql]);
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries (2 k-steps)
+      const int key = wb * DASH_BLOCK + 32 * kh + j;
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         bf16x8 pb, db;
 #pragma unroll
         for (int e8 = 0; e8 < 8; ++e8) {
-          pb[e8] = (__bf16)pv[8 * s2 + e8];
-          db[e8] = (__bf16)dsv[8 * s2 + e8];
+          const int r = 8 * s2 + e8;
+          const int ql = 32 * qh + acc_row32(r, l);
+          float sv = s[r];
+          if (diag && key > q0 + ql) sv = -INFINITY;
+          const float p = __builtin_amdgcn_exp2f(fmaf(sv, sl2, prq[kb][ql]));  // prq holds prior2 - lse2
+          pb[e8] = (__bf16)p;
+          db[e8] = (__bf16)(p * (dp[r] - dlq[ql]));
         }
         const int qk0 = 32 * qh + 16 * s2 + 4 * h;
 #pragma unroll
@@ -431,38 +530,46 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
           dka[dt] = mfma32(__builtin_bit_cast(bf16x8, make_uint4(qlo.x, qlo.y, qhi.x, qhi.y)), db, dka[dt]);
         }
       }
-      // dkbar_b += sum_q dz_qb q_q  (the coarse scale is applied at the end)
-      if (tid < D) {
-        float acc = 0.f;
-        for (int q = 0; q < 64; ++q) acc = fmaf(dzq[q], bf2f(qs[q * KP + tid]), acc);
-        kbacc += acc;
-      }
     }
+    it = nx;
   }
-  // merge the two query halves, add the pooling term, write bf16 rows
+
+  // dkbar: sum the 32 row-pair partials of each column in a fixed order
   __syncthreads();
-  float* red = reinterpret_cast<float*>(qs);  // qs, qt, os_, ot are free now
-  float* red2 = red + 2 * (D / 32) * 16 * 64;
-  if (tid < D) {
-    const float g = kbacc * a.ca.coarse_scale;
-    kbg[tid] = g;
-    a.dkbar[(bh * nb + b) * D + tid] = g;
+  float* red = reinterpret_cast<float*>(smem);
+  if (stager) {
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[(k2 * 32 + spr) * D + sch * 8 + e] = kbp[k2][e];
   }
+  __syncthreads();
+  if (tid < 2 * D) {
+    const int k2 = tid / D, d = tid % D;
+    float g = 0.f;
+    for (int pr = 0; pr < 32; ++pr) g += red[(k2 * 32 + pr) * D + d];
+    g *= a.ca.coarse_scale;
+    kbg[k2][d] = g;
+    if (k2 < nblk) a.dkbar[(bh * nb + b0 + k2) * D + d] = g;
+  }
+  __syncthreads();
+  // merge the two query halves, add the pooling term, write bf16 rows
+  float* red2 = red + 4 * (D / 32) * 16 * 64;
+  const int pairw = w >> 1;  // (kb, kh) index 0..3
   if (qh == 1) {
-    // [kh][dt][r][lane] layout, 2 x (D/32) x 16 x 64 floats = 16 KB per array for D = 128
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        red[((kh * (D / 32) + dt) * 16 + r) * 64 + l] = dva[dt][r];
-        red2[((kh * (D / 32) + dt) * 16 + r) * 64 + l] = dka[dt][r];
+        red[((pairw * (D / 32) + dt) * 16 + r) * 64 + l] = dva[dt][r];
+        red2[((pairw * (D / 32) + dt) * 16 + r) * 64 + l] = dka[dt][r];
       }
   }
   __syncthreads();
-  if (qh == 0) {
+  if (qh == 0 && kb < nblk) {
     bf16_t* dV = reinterpret_cast<bf16_t*>(a.dv) + bh * a.T * D;
     bf16_t* dK = reinterpret_cast<bf16_t*>(a.dk) + bh * a.T * D;
-    const int key = b * DASH_BLOCK + 32 * kh + j;
+    const int key = wb * DASH_BLOCK + 32 * kh + j;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -475,9 +582,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const int r = 4 * r4 + 2 * e2 + e;
-            const size_t ri = ((kh * (D / 32) + dt) * 16 + r) * 64 + l;
+            const size_t ri = ((pairw * (D / 32) + dt) * 16 + r) * 64 + l;
             v0[e] = dva[dt][r] + red[ri];
-            k0[e] = (dka[dt][r] + red2[ri]) * a.fine_scale + kbg[d + 2 * e2 + e] * (1.f / DASH_BLOCK);
+            k0[e] = (dka[dt][r] + red2[ri]) * a.fine_scale + kbg[kb][d + 2 * e2 + e] * (1.f / DASH_BLOCK);
           }
           pv2[e2] = (uint32_t)f2bf(v0[0]) | ((uint32_t)f2bf(v0[1]) << 16);
           pk2[e2] = (uint32_t)f2bf(k0[0]) | ((uint32_t)f2bf(k0[1]) << 16);
@@ -652,8 +759,9 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     bwd_entmax_kernel<<<dim3(ntile, a.BH), 128, 0, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (a.D == 128) bwd_dkdv_kernel<128><<<nb * a.BH, 256, 0, st>>>(a);
-    else bwd_dkdv_kernel<64><<<nb * a.BH, 256, 0, st>>>(a);
+    const int ngrp = (nb + 1) / 2;
+    if (a.D == 128) bwd_dkdv_kernel<128><<<ngrp * a.BH, 512, 0, st>>>(a);
+    else bwd_dkdv_kernel<64><<<ngrp * a.BH, 512, 0, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.D == 128) bwd_dq_final_kernel<128><<<dim3(ntile * 4, a.BH), 256, 0, st>>>(a);
     else bwd_dq_final_kernel<64><<<dim3(ntile * 4, a.BH), 256, 0, st>>>(a);

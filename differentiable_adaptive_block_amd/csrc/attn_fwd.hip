@@ -31,6 +31,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t ks[64 * KP];
   __shared__ __attribute__((aligned(16))) bf16_t vt[D * VP];
   __shared__ float pri[4][32 * 32];
+  __shared__ int lst[DASH_MAX_NB];  // the tile's block list
 
   const int nb = a.T / DASH_BLOCK;
   const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
@@ -54,10 +55,15 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
   const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + bh * a.T * D;
   const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + bh * a.T * D;
   const bf16_t* KB = reinterpret_cast<const bf16_t*>(a.kbar) + bh * nb * D;
-  const int* list = a.tile_blk + (bh * ntile + tile) * nb;
+  const int* glist = a.tile_blk + (bh * ntile + tile) * nb;
   const int cnt = a.tile_cnt[bh * ntile + tile];
   const CoarseArith ca = a.ca;
   const float sl2 = a.fine_scale * LOG2E_F;
+  // Stage the block list in LDS once: every later block index is an LDS
+  // read instead of a dependent global load in front of each K/V fetch.
+  for (int x = threadIdx.x; x < cnt; x += 256) lst[x] = glist[x];
+  __syncthreads();
+  const int* list = lst;
 
   bf16x8 qb[D / 16];
   float tau_i = 0.f, ln_i = 0.f;
@@ -152,38 +158,43 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
       s0 = mfma32(a0, qb[s], s0);
       s1 = mfma32(a1, qb[s], s1);
     }
-    float x[32];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      x[r] = s0[r] * sl2 + pr;
-      x[16 + r] = s1[r] * sl2 + pr;
-    }
+    // The prior is constant over a row's keys in this block, so the block
+    // max is taken on the raw scores and every weight is one FMA + exp2:
+    // p = 2^(s * scale * log2e + prior2 - m).
     if (diag) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = b * DASH_BLOCK + acc_row32(r, l);
-        if (key > i) x[r] = -INFINITY;
-        if (key + 32 > i) x[16 + r] = -INFINITY;
+        if (key > i) s0[r] = -INFINITY;
+        if (key + 32 > i) s1[r] = -INFINITY;
       }
     }
-    float mx = x[0];
+    float mb = fmaxf(s0[0], s1[0]);
 #pragma unroll
-    for (int r = 1; r < 32; ++r) mx = fmaxf(mx, x[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mnew = fmaxf(mrow, mx);
-    const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-    const float resc = exp2f(mrow - mref);
-    mrow = mnew;
-    lrow *= resc;
+    for (int r = 1; r < 16; ++r) mb = fmaxf(mb, fmaxf(s0[r], s1[r]));
+    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+    const float mx = (mb == -INFINITY || pr == -INFINITY) ? -INFINITY : mb * sl2 + pr;
+    // Rows keep a reference max and rescale O only when a block's max
+    // exceeds it by more than 2^8, so weights stay <= 256 and most blocks
+    // skip the rescale (wave-uniform branch).
+    if (__ballot(mx > mrow + 8.f) != 0ull) {
+      const float mnew = fmaxf(mrow, mx);
+      const float resc = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrow - mnew);
+      mrow = mnew;
+      lrow *= resc;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+      for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[dt][r] *= resc;
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= resc;
+    }
+    const float off = (pr == -INFINITY || mrow == -INFINITY) ? -INFINITY : pr - mrow;
+    float x[32];
     float ps = 0.f;
 #pragma unroll
-    for (int r = 0; r < 32; ++r) {
-      x[r] = exp2f(x[r] - mref);
-      ps += x[r];
+    for (int r = 0; r < 16; ++r) {
+      x[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], sl2, off));
+      x[16 + r] = __builtin_amdgcn_exp2f(fmaf(s1[r], sl2, off));
+      ps += x[r] + x[16 + r];
     }
     lrow += ps;
     // O^T += V_b^T P^T, 4 k-steps of 16 keys
@@ -213,7 +224,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) ost[j * D + 32 * dt + acc_row32(r, l)] = f2bf(oacc[dt][r] * inv);
-    if (h == 0) a.lse[bh * a.T + i] = (mrow + __log2f(ltot)) * LN2_F;
+    if (h == 0) a.lse[bh * a.T + i] = (mrow + __builtin_amdgcn_logf(ltot)) * LN2_F;
   }
   __syncthreads();
   if (active) {

@@ -55,18 +55,26 @@ __global__ __launch_bounds__(256) void decode_select_kernel(DecodeArgs a) {
   const CoarseArith ca = a.ca;
   float qf[8];
   unpack8(*reinterpret_cast<const uint4*>(q + (l & 15) * 8), qf);
-  // 4 summaries per wave instruction, 16 lanes each
-  for (int b0 = w * 4; b0 < nc; b0 += 16) {
-    const int b = b0 + (l >> 4);
-    float part = 0.f;
-    if (b < nc) {
+  // 4 summaries per wave instruction, 16 lanes each; 8 loads in flight per lane
+  constexpr int UN = 8;
+  for (int b0 = w * 4; b0 < nc; b0 += 16 * UN) {
+    uint4 kr[UN];
+#pragma unroll
+    for (int x = 0; x < UN; ++x) {
+      const int b = b0 + 16 * x + (l >> 4);
+      kr[x] = b < nc ? *reinterpret_cast<const uint4*>(kb + (size_t)b * D + (l & 15) * 8) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int x = 0; x < UN; ++x) {
+      const int b = b0 + 16 * x + (l >> 4);
       float kf[8];
-      unpack8(*reinterpret_cast<const uint4*>(kb + (size_t)b * D + (l & 15) * 8), kf);
+      unpack8(kr[x], kf);
+      float part = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) part = fmaf(qf[e], kf[e], part);
+      part = sum16(part);
+      if (b < nc && (l & 15) == 0) us[b] = ca.u_of(part);
     }
-    part = sum16(part);
-    if (b < nc && (l & 15) == 0) us[b] = ca.u_of(part);
   }
   __syncthreads();
   if (w != 0) return;
@@ -128,9 +136,19 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(DecodeArgs a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = 0.f;
   const int stride = 4 * a.nsplit;
-  for (int en = split * 4 + w; en < cnt; en += stride) {
-    const int b = list[en];
-    const float pr = lpl[en];
+  const int first = split * 4 + w;
+  // this wave's list entries, one per lane, loaded once (at most 64: the list
+  // holds <= 2048 blocks and the stride is 64)
+  int myb = 0;
+  float mylp = 0.f;
+  {
+    const int en = first + l * stride;
+    if (en < cnt) { myb = list[en]; mylp = lpl[en]; }
+  }
+  const int nmine = cnt > first ? (cnt - first + stride - 1) / stride : 0;
+  for (int k = 0; k < nmine; ++k) {
+    const int b = __shfl(myb, k, 64);
+    const float pr = __shfl(mylp, k, 64);
     const bf16_t* kb = K + (size_t)b * DASH_BLOCK * D;
     const bf16_t* vb = V + (size_t)b * DASH_BLOCK * D;
     uint4 kr[16], vr[16];
@@ -154,13 +172,13 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(DecodeArgs a) {
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float mn = fmaxf(m, mx);
-    const float rs = exp2f(m - mn);
+    const float rs = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - mn);
     float ps = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] *= rs;
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
-      const float p = exp2f(s[it] - mn);
+      const float p = __builtin_amdgcn_exp2f(s[it] - mn);
       ps += p;
       float vf[8];
       unpack8(vr[it], vf);
