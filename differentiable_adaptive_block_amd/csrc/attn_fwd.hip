@@ -30,8 +30,10 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
   constexpr int NVP = 32 * CH / 256;       // V row pairs per thread
   __shared__ __attribute__((aligned(16))) bf16_t ks[64 * KP];
   __shared__ __attribute__((aligned(16))) bf16_t vt[D * VP];
-  __shared__ float pri[4][32 * 32];
+  __shared__ __attribute__((aligned(16))) float pri[4][32 * 32];
   __shared__ int lst[DASH_MAX_NB];  // the tile's block list
+  static_assert(D != 128 || D * VP >= 2 * 32 * KP, "epilogue space in vt");
+  static_assert(D == 128 || 4 * 32 * 32 * 2 >= 2 * 32 * KP, "epilogue space in pri");
 
   const int nb = a.T / DASH_BLOCK;
   const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
@@ -113,7 +115,8 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
       for (int e = 0; e < 8; ++e) {
         const uint32_t lo = (e & 1) ? (v0[e >> 1] >> 16) : (v0[e >> 1] & 0xFFFFu);
         const uint32_t hi = (e & 1) ? (v1[e >> 1] >> 16) : (v1[e >> 1] & 0xFFFFu);
-        *reinterpret_cast<uint32_t*>(&vt[(ch * 8 + e) * VP + 2 * pr]) = lo | (hi << 16);
+        const int d = ch * 8 + e;
+        *reinterpret_cast<uint32_t*>(&vt[d * VP + 2 * tr_pair(d, pr)]) = lo | (hi << 16);
       }
     }
   };
@@ -205,9 +208,10 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
       for (int e8 = 0; e8 < 8; ++e8) pb[e8] = (__bf16)x[16 * (s >> 1) + 8 * (s & 1) + e8];
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const bf16_t* vrow = &vt[(32 * dt + j) * VP + 16 * s + 4 * h];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
+        const int d = 32 * dt + j;
+        const bf16_t* vrow = &vt[d * VP];
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 2 * tr_pair(d, 8 * s + 2 * h));
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 2 * tr_pair(d, 8 * s + 4 + 2 * h));
         const uint4 pk = make_uint4(lo.x, lo.y, hi.x, hi.y);
         oacc[dt] = mfma32(__builtin_bit_cast(bf16x8, pk), pb, oacc[dt]);
       }
@@ -218,12 +222,20 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
   __syncthreads();
   const float ltot = lrow + __shfl_xor(lrow, 32, 64);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-  bf16_t* ost = (w < 2) ? ks + w * 32 * D : vt + (w - 2) * 32 * D;  // 32 x D per wave
+  // 32 rows x D per wave, row pitch KP: waves 0-1 in ks, waves 2-3 in vt
+  // (D = 128) or in the prior buffer (D = 64), all free after the main loop
+  bf16_t* ost = (w < 2) ? ks + w * 32 * KP
+                        : (D == 128 ? vt : reinterpret_cast<bf16_t*>(&pri[0][0])) + (w - 2) * 32 * KP;
   if (active) {
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) ost[j * D + 32 * dt + acc_row32(r, l)] = f2bf(oacc[dt][r] * inv);
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = 32 * dt + 8 * r4 + 4 * h;  // registers 4 r4 .. 4 r4 + 3 hold d .. d + 3
+        const uint32_t w0 = (uint32_t)f2bf(oacc[dt][4 * r4] * inv) | ((uint32_t)f2bf(oacc[dt][4 * r4 + 1] * inv) << 16);
+        const uint32_t w1 = (uint32_t)f2bf(oacc[dt][4 * r4 + 2] * inv) | ((uint32_t)f2bf(oacc[dt][4 * r4 + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(&ost[j * KP + d]) = make_uint2(w0, w1);
+      }
     if (h == 0) a.lse[bh * a.T + i] = (mrow + __builtin_amdgcn_logf(ltot)) * LN2_F;
   }
   __syncthreads();
@@ -234,7 +246,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
       const int idx = it * 64 + l;
       const int row = idx / CH, ch = idx % CH;
       *reinterpret_cast<uint4*>(O + (size_t)(qrow0 + row) * D + ch * 8) =
-          *reinterpret_cast<const uint4*>(ost + row * D + ch * 8);
+          *reinterpret_cast<const uint4*>(ost + row * KP + ch * 8);
     }
   }
 }

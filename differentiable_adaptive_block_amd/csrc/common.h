@@ -94,6 +94,16 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // (the column is l % 32).
 __device__ __forceinline__ int acc_row32(int r, int l) { return 8 * (r >> 2) + 4 * (l >> 5) + (r & 3); }
 
+// ------------------------------------------------------------------ transposed LDS tiles
+//
+// Tiles stored transposed in LDS (row = feature d, 64 keys per row, row
+// pitch 68 bf16) are written as 4-byte pairs of consecutive keys by lanes
+// that hold one 16-byte chunk of a source row each, which would put 32
+// lanes on 4 banks.  XOR-ing the pair index with 2*((d >> 4) & 7) spreads
+// those stores over the banks and keeps the operand reads (8-byte runs of 4
+// keys) 8-byte aligned.
+__device__ __forceinline__ int tr_pair(int d, int pair) { return pair ^ (((d >> 4) & 7) << 1); }
+
 // ------------------------------------------------------------------ Stage-1 score arithmetic
 //
 // One definition of the coarse score used by every kernel, so that the
