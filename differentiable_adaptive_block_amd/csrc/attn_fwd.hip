@@ -1,6 +1,8 @@
 // Stage 2 forward: softmax attention over the selected blocks with log p
 // added to every logit of block b ("Core Mechanism" of the alanhou.org page:
 // fine logits plus log of the coarse scores, softmax, weighted sum of V).
+#include <type_traits>
+
 #include "kernels.h"
 
 #define LOG2E_F 1.4426950408889634f
@@ -113,16 +115,19 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
       const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&vr[2 * x + 1]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t lo = (e & 1) ? (v0[e >> 1] >> 16) : (v0[e >> 1] & 0xFFFFu);
-        const uint32_t hi = (e & 1) ? (v1[e >> 1] >> 16) : (v1[e >> 1] & 0xFFFFu);
+        // element e of key 2 pr (low half) and of key 2 pr + 1 (high half)
+        const uint32_t pk = __builtin_amdgcn_perm(v1[e >> 1], v0[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
         const int d = ch * 8 + e;
-        *reinterpret_cast<uint32_t*>(&vt[d * VP + 2 * tr_pair(d, pr)]) = lo | (hi << 16);
+        *reinterpret_cast<uint32_t*>(&vt[d * VP + 2 * tr_pair(d, pr)]) = pk;
       }
     }
   };
 
-  if (cnt > 0) gload(list[0]);
-  for (int e = 0; e < cnt; ++e) {
+  // One listed block.  OWN: the block may be this wave's own (diagonal)
+  // block or lie after it; only the tile's own blocks, walked last, take
+  // that path, so the off-diagonal loop carries no causal-mask code.
+  auto block_step = [&](int e, auto own_tag) {
+    constexpr bool OWN = decltype(own_tag)::value;
     const int b = list[e];
     __syncthreads();  // every wave is done with the previous block's LDS
     sstore();
@@ -144,11 +149,14 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
     }
     __syncthreads();  // LDS tile and priors visible
     if (e + 1 < cnt) gload(list[e + 1]);
-    if (!active) continue;
-    if (a.causal && b > wblk) continue;
-    const bool diag = a.causal && b == wblk;
+    if (!active) return;
+    bool diag = false;
+    if constexpr (OWN) {
+      if (b > wblk) return;  // after this wave's rows
+      diag = b == wblk;
+    }
     const float pr = diag ? 0.f : pri[w][(e & 31) * 32 + j];
-    if (!diag && __ballot(pr != -INFINITY) == 0ull) continue;
+    if (!diag && __ballot(pr != -INFINITY) == 0ull) return;
 
     // S^T = K_b Q^T
     f32x16 s0, s1;
@@ -161,26 +169,30 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
       s0 = mfma32(a0, qb[s], s0);
       s1 = mfma32(a1, qb[s], s1);
     }
+    if constexpr (OWN) {
+      if (diag) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = b * DASH_BLOCK + acc_row32(r, l);
+          if (key > i) s0[r] = -INFINITY;
+          if (key + 32 > i) s1[r] = -INFINITY;
+        }
+      }
+    }
     // The prior is constant over a row's keys in this block, so the block
     // max is taken on the raw scores and every weight is one FMA + exp2:
     // p = 2^(s * scale * log2e + prior2 - m).
-    if (diag) {
+    float mb = s0[0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = b * DASH_BLOCK + acc_row32(r, l);
-        if (key > i) s0[r] = -INFINITY;
-        if (key + 32 > i) s1[r] = -INFINITY;
-      }
-    }
-    float mb = fmaxf(s0[0], s1[0]);
+    for (int r = 1; r < 16; ++r) mb = fmaxf(mb, s0[r]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mb = fmaxf(mb, fmaxf(s0[r], s1[r]));
+    for (int r = 0; r < 16; ++r) mb = fmaxf(mb, s1[r]);
     mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
     const float mx = (mb == -INFINITY || pr == -INFINITY) ? -INFINITY : mb * sl2 + pr;
     // Rows keep a reference max and rescale O only when a block's max
     // exceeds it by more than 2^8, so weights stay <= 256 and most blocks
     // skip the rescale (wave-uniform branch).
-    if (__ballot(mx > mrow + 8.f) != 0ull) {
+    if (__builtin_expect(__ballot(mx > mrow + 8.f) != 0ull, 0)) {
       const float mnew = fmaxf(mrow, mx);
       const float resc = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrow - mnew);
       mrow = mnew;
@@ -216,7 +228,16 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
         oacc[dt] = mfma32(__builtin_bit_cast(bf16x8, pk), pb, oacc[dt]);
       }
     }
-  }
+  };
+
+  // With a causal mask the list ends with the tile's own blocks (every other
+  // listed block precedes them): walk the rest first without mask code.
+  const int nown = a.causal ? (min(a.T, (tile + 1) * DASH_QTILE) - tile * DASH_QTILE) / DASH_BLOCK : 0;
+  const int nmain = cnt - nown;
+  if (cnt > 0) gload(list[0]);
+  int e = 0;
+  for (; e < nmain; ++e) block_step(e, std::false_type{});
+  for (; e < cnt; ++e) block_step(e, std::true_type{});
 
   // epilogue: O = O^T / l, staged through LDS for 16-byte row stores
   __syncthreads();
@@ -232,9 +253,10 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int d = 32 * dt + 8 * r4 + 4 * h;  // registers 4 r4 .. 4 r4 + 3 hold d .. d + 3
-        const uint32_t w0 = (uint32_t)f2bf(oacc[dt][4 * r4] * inv) | ((uint32_t)f2bf(oacc[dt][4 * r4 + 1] * inv) << 16);
-        const uint32_t w1 = (uint32_t)f2bf(oacc[dt][4 * r4 + 2] * inv) | ((uint32_t)f2bf(oacc[dt][4 * r4 + 3] * inv) << 16);
-        *reinterpret_cast<uint2*>(&ost[j * KP + d]) = make_uint2(w0, w1);
+        bf16x4 o4;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) o4[x] = (__bf16)(oacc[dt][4 * r4 + x] * inv);
+        *reinterpret_cast<bf16x4*>(&ost[j * KP + d]) = o4;
       }
     if (h == 0) a.lse[bh * a.T + i] = (mrow + __builtin_amdgcn_logf(ltot)) * LN2_F;
   }

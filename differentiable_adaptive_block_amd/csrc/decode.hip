@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void decode_select_kernel(DecodeArgs a) {
     u[k] = idx < nc ? us[idx] : -INFINITY;
   }
   EntmaxOut e;
-  if (nc > 0) e = entmax_solve<NPL>(u, ca);
+  if (nc > 0) e = entmax_solve<NPL, 64>(u, nc, ca);
   else { e.tau = __uint_as_float(0x7fc00000u); e.lognorm = 0.f; e.nsel = 0; }
   int* list = a.sel_blk + (size_t)row * nb;
   float* lp = a.sel_lp + (size_t)row * nb;

@@ -7,8 +7,13 @@
 //     f(tau) = sum_b [u_b - tau]_+^m = 1.
 // f is convex and decreasing, so Newton's method started left of the root
 // (at max u - 1, where the largest term alone gives f >= 1) increases
-// monotonically to it, one pair of wave reductions per step.  alpha = 1 is
-// the softmax: tau = log-sum-exp(z).
+// monotonically to it.  alpha = 1 is the softmax: tau = log-sum-exp(z).
+//
+// A row is held by a group of G lanes (G = 16: four rows per wave; G = 64:
+// one row per wave).  Group reductions use DPP within each 16-lane row of
+// the wave (quad swaps, half-row and row mirrors), so every lane of the row
+// ends with the same bits; G = 64 then adds the four row results read back
+// with readlane, in a fixed order.
 #pragma once
 
 #include "common.h"
@@ -19,58 +24,148 @@ struct EntmaxOut {
   int nsel;
 };
 
-// One row per wave.  Lane l holds u[k] = score of candidate l + 64 k for
-// k < NPL, or -INFINITY where there is none.  n = number of candidates (> 0).
-// The result is identical in every lane.
-template <int NPL>
-__device__ __forceinline__ EntmaxOut entmax_solve(const float (&u)[NPL], const CoarseArith& ca) {
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+// DPP controls: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.
+#define DPP_QSWAP1 0xB1
+#define DPP_QSWAP2 0x4E
+#define DPP_HMIRROR 0x141
+#define DPP_MIRROR 0x140
+
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<DPP_QSWAP1>(v);
+  v += dpp_f<DPP_QSWAP2>(v);
+  v += dpp_f<DPP_HMIRROR>(v);
+  v += dpp_f<DPP_MIRROR>(v);
+  return v;
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<DPP_QSWAP1>(v));
+  v = fmaxf(v, dpp_f<DPP_QSWAP2>(v));
+  v = fmaxf(v, dpp_f<DPP_HMIRROR>(v));
+  v = fmaxf(v, dpp_f<DPP_MIRROR>(v));
+  return v;
+}
+__device__ __forceinline__ int row16_sum_i(int v) {
+  v += dpp_i<DPP_QSWAP1>(v);
+  v += dpp_i<DPP_QSWAP2>(v);
+  v += dpp_i<DPP_HMIRROR>(v);
+  v += dpp_i<DPP_MIRROR>(v);
+  return v;
+}
+
+template <int G>
+__device__ __forceinline__ float grp_sum(float v) {
+  v = row16_sum(v);
+  if constexpr (G == 64) {
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    v = (r0 + r1) + (r2 + r3);
+  }
+  return v;
+}
+template <int G>
+__device__ __forceinline__ float grp_max(float v) {
+  v = row16_max(v);
+  if constexpr (G == 64) {
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    v = fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+  }
+  return v;
+}
+template <int G>
+__device__ __forceinline__ int grp_sum_i(int v) {
+  v = row16_sum_i(v);
+  if constexpr (G == 64) {
+    v = (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+        (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+  }
+  return v;
+}
+
+// One row per group of G lanes.  Lane (group-local index g) holds
+// u[k] = score of candidate g + G k for k < NPL, or -INFINITY where there is
+// none; only k with G k < nvalid can hold a candidate (nvalid is the same on
+// every lane of the wave, so the loops below skip the rest with scalar
+// branches); every row has at least one candidate.  All lanes of the wave
+// call this together; the result is identical across each group.
+template <int NPL, int G>
+__device__ __forceinline__ EntmaxOut entmax_solve(const float (&u)[NPL], int nvalid, const CoarseArith& ca) {
   float umax = -INFINITY;
 #pragma unroll
-  for (int k = 0; k < NPL; ++k) umax = fmaxf(umax, u[k]);
-  umax = wave_max(umax);
+  for (int k = 0; k < NPL; ++k)
+    if (k * G < nvalid) umax = fmaxf(umax, u[k]);
+  umax = grp_max<G>(umax);
   EntmaxOut r;
   if (ca.softmax) {
     float s = 0.f;
 #pragma unroll
-    for (int k = 0; k < NPL; ++k) s += (u[k] != -INFINITY) ? __expf(u[k] - umax) : 0.f;
-    s = wave_sum(s);
+    for (int k = 0; k < NPL; ++k)
+      if (k * G < nvalid) s += (u[k] != -INFINITY) ? __expf(u[k] - umax) : 0.f;
+    s = grp_sum<G>(s);
     r.tau = umax + __logf(s);
     float s2 = 0.f;
     int c = 0;
 #pragma unroll
     for (int k = 0; k < NPL; ++k) {
-      if (u[k] != -INFINITY) { s2 += __expf(u[k] - r.tau); ++c; }
+      if (k * G < nvalid && u[k] != -INFINITY) { s2 += __expf(u[k] - r.tau); ++c; }
     }
-    r.lognorm = __logf(wave_sum(s2));
-    r.nsel = wave_sum_i(c);
+    r.lognorm = __logf(grp_sum<G>(s2));
+    r.nsel = grp_sum_i<G>(c);
     return r;
   }
   const float m = ca.m;
+  float v[NPL];
+#pragma unroll
+  for (int k = 0; k < NPL; ++k) v[k] = u[k] - umax;
   float t = -1.f;  // relative to max u: f(-1) >= 1 from the largest term alone
-  // Newton from the left.
+  bool done = false;
+  // Newton from the left; groups that have converged keep their t while the
+  // others iterate (all lanes stay active for the DPP reductions).
   for (int it = 0; it < 64; ++it) {
     float f = 0.f, fp = 0.f;
 #pragma unroll
     for (int k = 0; k < NPL; ++k) {
-      float x = (u[k] - umax) - t;
-      if (x > 0.f) { f += pow_m(x, m); fp += pow_m1(x, m); }
+      if (k * G < nvalid) {
+        const float x = v[k] - t;
+        if (x > 0.f) { f += pow_m(x, m); fp += pow_m1(x, m); }
+      }
     }
-    f = wave_sum(f);
-    fp = wave_sum(fp);
-    float step = (f - 1.f) / (m * fp);
-    if (!(step > 0.f)) break;  // at (or, by rounding, just past) the root
-    t += step;
-    if (step <= 1e-7f) break;
+    f = grp_sum<G>(f);
+    fp = grp_sum<G>(fp);
+    const float step = (f - 1.f) / (m * fp);
+    if (!done) {
+      if (!(step > 0.f)) done = true;  // at (or, by rounding, just past) the root
+      else {
+        t += step;
+        if (step <= 1e-7f) done = true;
+      }
+    }
+    if (__ballot(!done) == 0ull) break;
   }
   r.tau = umax + t;
   float s = 0.f;
   int c = 0;
 #pragma unroll
   for (int k = 0; k < NPL; ++k) {
-    float x = u[k] - r.tau;
-    if (x > 0.f) { s += pow_m(x, m); ++c; }
+    if (k * G < nvalid) {
+      const float x = u[k] - r.tau;
+      if (x > 0.f) { s += pow_m(x, m); ++c; }
+    }
   }
-  r.lognorm = __logf(wave_sum(s));
-  r.nsel = wave_sum_i(c);
+  r.lognorm = __logf(grp_sum<G>(s));
+  r.nsel = grp_sum_i<G>(c);
   return r;
 }

@@ -82,6 +82,45 @@ __device__ __forceinline__ void write_empty_row(const SelectArgs& a, size_t row_
     for (int w = l; w < nbw; w += 64) a.mask[row_g * nbw + w] = 0u;
 }
 
+// Four rows per wave, 16 lanes per row: lane g of the group holds
+// candidates g + 16 k.  Word w of a row's mask takes its low 16 bits from
+// k = 2w and its high 16 bits from k = 2w + 1; lane g writes words g + 16 j
+// and ORs them into the tile's union in LDS.
+template <int NPL>
+__device__ __forceinline__ void write_rows16(const SelectArgs& a, size_t row_g, const float (&u)[NPL], int nc,
+                                             const EntmaxOut& e, const CoarseArith& ca, uint32_t* uni_lds) {
+  const int l = lane_id(), g = l & 15, sh = l & 48;
+  const int nbw = (a.T / DASH_BLOCK + 31) / 32;
+  if (g == 0) {
+    a.tau[row_g] = e.tau;
+    a.lognorm[row_g] = e.lognorm;
+    if (a.nsel) a.nsel[row_g] = e.nsel;
+  }
+  constexpr int NW = (NPL + 1) / 2;
+  constexpr int NJ = (NW + 15) / 16;
+  uint32_t mine[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) mine[j] = 0u;
+#pragma unroll
+  for (int wd = 0; wd < NW; ++wd) {
+    if (32 * wd >= nc) break;  // nc is the same on every lane
+    const int k0 = 2 * wd, k1 = 2 * wd + 1;
+    const unsigned long long b0 = __ballot(g + 16 * k0 < nc && ca.selected(u[k0], e.tau));
+    unsigned long long b1 = 0ull;
+    if (k1 < NPL) b1 = __ballot(g + 16 * k1 < nc && ca.selected(u[k1], e.tau));
+    const uint32_t word = (uint32_t)((b0 >> sh) & 0xFFFFull) | ((uint32_t)((b1 >> sh) & 0xFFFFull) << 16);
+    if (g == (wd & 15)) mine[wd >> 4] = word;
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int idx = g + 16 * j;
+    if (idx < nbw) {
+      if (a.mask) a.mask[row_g * nbw + idx] = mine[j];
+      if (mine[j]) atomicOr(&uni_lds[idx], mine[j]);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------- Stage 1, bf16 MFMA
 
 // One workgroup (4 waves) per 32 query rows.  The block scores of the 32
@@ -90,7 +129,8 @@ __device__ __forceinline__ void write_empty_row(const SelectArgs& a, size_t row_
 //     Z^T[block][query] = kbar[block] . q[query]
 // (operand A = summary rows, B = the queries, fp32 accumulation) and kept in
 // LDS as u = (alpha-1) * coarse_scale * acc; then each wave solves tau for 8
-// rows.  coarse_u_chunk() is the one definition of this arithmetic; the
+// rows, four at a time (16 lanes per row, see entmax_solve).
+// coarse_acc_chunk() is the one definition of the score arithmetic; the
 // Stage-2 and backward kernels call it too, so they see the same bits.
 template <int D, int NPL>
 __global__ __launch_bounds__(256) void select_mfma_kernel(SelectArgs a) {
@@ -123,21 +163,28 @@ __global__ __launch_bounds__(256) void select_mfma_kernel(SelectArgs a) {
     }
   }
   __syncthreads();
-  for (int rr = 0; rr < 8; ++rr) {
-    const int row = 8 * w + rr;
+  const int g = l & 15;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int row = 8 * w + 4 * pass + (l >> 4);
     const size_t row_g = bh * a.T + row0 + row;
     if (nc == 0) {
-      write_empty_row(a, row_g);
+      if (g == 0) {
+        a.tau[row_g] = __uint_as_float(0x7fc00000u);
+        a.lognorm[row_g] = 0.f;
+        if (a.nsel) a.nsel[row_g] = 0;
+      }
+      if (a.mask)
+        for (int x = g; x < nbw; x += 16) a.mask[row_g * nbw + x] = 0u;
       continue;
     }
     float u[NPL];
 #pragma unroll
     for (int k = 0; k < NPL; ++k) {
-      const int idx = l + 64 * k;
+      const int idx = g + 16 * k;
       u[k] = idx < nc ? zs[row * nbp + idx] : -INFINITY;
     }
-    const EntmaxOut e = entmax_solve<NPL>(u, ca);
-    write_row_selection<NPL>(a, row_g, u, nc, e, ca, uni, nullptr);
+    const EntmaxOut e = entmax_solve<NPL, 16>(u, nc, ca);
+    write_rows16<NPL>(a, row_g, u, nc, e, ca, uni);
   }
   __syncthreads();
   const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
@@ -176,7 +223,7 @@ __global__ __launch_bounds__(64) void select_generic_kernel(SelectArgs a) {
     const int b = l + 64 * k;
     u[k] = b < nc ? ca.u_of(dot_row<T>(qs, kb + (size_t)b * D, D)) : -INFINITY;
   }
-  const EntmaxOut e = entmax_solve<NPL>(u, ca);
+  const EntmaxOut e = entmax_solve<NPL, 64>(u, nc, ca);
   const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
   uint32_t* tb = a.tile_bits + (bh * ntile + i / DASH_QTILE) * nbw;
   write_row_selection<NPL>(a, row_g, u, nc, e, ca, nullptr, tb);
@@ -252,11 +299,12 @@ static hipError_t launch_select_mfma_t(const SelectArgs& a, int BH, hipStream_t 
 template <int D>
 static hipError_t launch_select_mfma_d(const SelectArgs& a, int BH, hipStream_t st) {
   const int nb = a.T / DASH_BLOCK;
-  if (nb <= 64) return launch_select_mfma_t<D, 1>(a, BH, st);
-  if (nb <= 128) return launch_select_mfma_t<D, 2>(a, BH, st);
-  if (nb <= 256) return launch_select_mfma_t<D, 4>(a, BH, st);
-  if (nb <= 512) return launch_select_mfma_t<D, 8>(a, BH, st);
-  return launch_select_mfma_t<D, 16>(a, BH, st);
+  // candidates per lane at 16 lanes per row
+  if (nb <= 64) return launch_select_mfma_t<D, 4>(a, BH, st);
+  if (nb <= 128) return launch_select_mfma_t<D, 8>(a, BH, st);
+  if (nb <= 256) return launch_select_mfma_t<D, 16>(a, BH, st);
+  if (nb <= 512) return launch_select_mfma_t<D, 32>(a, BH, st);
+  return launch_select_mfma_t<D, 64>(a, BH, st);
 }
 
 template <typename T>
