@@ -26,10 +26,10 @@
 template <int D>
 __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
   constexpr int KP = D + 8;   // K row pitch in LDS (bf16)
-  constexpr int VP = 64 + 4;  // V^T row pitch in LDS (bf16)
+  constexpr int VP = VT_PITCH;  // V^T row pitch in LDS (bf16)
   constexpr int CH = D / 8;   // 16-byte chunks per key row
   constexpr int NKL = 64 * CH / 256;       // K uint4 per thread
-  constexpr int NVP = 32 * CH / 256;       // V row pairs per thread
+  constexpr int NVP = 32 * CH / 256;       // V key pairs per thread
   __shared__ __attribute__((aligned(16))) bf16_t ks[64 * KP];
   __shared__ __attribute__((aligned(16))) bf16_t vt[D * VP];
   __shared__ __attribute__((aligned(16))) float pri[4][32 * 32];
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
 #pragma unroll
     for (int x = 0; x < NVP; ++x) {
       const int idx = tid + 256 * x;
-      const int pr = idx / CH, ch = idx % CH;
+      const int pr = vt_pos(idx / CH), ch = idx % CH;  // thread item = pair position idx / CH
       vr[2 * x] = *reinterpret_cast<const uint4*>(vb0 + (size_t)(2 * pr) * D + ch * 8);
       vr[2 * x + 1] = *reinterpret_cast<const uint4*>(vb0 + (size_t)(2 * pr + 1) * D + ch * 8);
     }
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
 #pragma unroll
     for (int x = 0; x < NVP; ++x) {
       const int idx = tid + 256 * x;
-      const int pr = idx / CH, ch = idx % CH;
+      const int pos = idx / CH, ch = idx % CH;
       const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&vr[2 * x]);
       const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&vr[2 * x + 1]);
 #pragma unroll
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
         // element e of key 2 pr (low half) and of key 2 pr + 1 (high half)
         const uint32_t pk = __builtin_amdgcn_perm(v1[e >> 1], v0[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
         const int d = ch * 8 + e;
-        *reinterpret_cast<uint32_t*>(&vt[d * VP + 2 * tr_pair(d, pr)]) = pk;
+        *reinterpret_cast<uint32_t*>(&vt[d * VP + 2 * vt_slot(d, pos)]) = pk;
       }
     }
   };
@@ -221,11 +221,8 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
         const int d = 32 * dt + j;
-        const bf16_t* vrow = &vt[d * VP];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 2 * tr_pair(d, 8 * s + 2 * h));
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 2 * tr_pair(d, 8 * s + 4 + 2 * h));
-        const uint4 pk = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        oacc[dt] = mfma32(__builtin_bit_cast(bf16x8, pk), pb, oacc[dt]);
+        const bf16x8 va = load8(&vt[d * VP + 2 * vt_slot(d, 8 * s + 4 * h)]);
+        oacc[dt] = mfma32(va, pb, oacc[dt]);
       }
     }
   };
