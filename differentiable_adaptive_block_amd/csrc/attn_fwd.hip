@@ -1,8 +1,6 @@
 // Stage 2 forward: softmax attention over the selected blocks with log p
 // added to every logit of block b ("Core Mechanism" of the alanhou.org page:
 // fine logits plus log of the coarse scores, softmax, weighted sum of V).
-#include <type_traits>
-
 #include "kernels.h"
 
 #define LOG2E_F 1.4426950408889634f
@@ -12,8 +10,7 @@
 //
 // Workgroup = 4 waves = one query tile of 128 rows; wave w owns rows
 // 32w..32w+31 of the tile.  The workgroup walks the tile's block list
-// (ascending); per block the 64 keys and values are staged once in LDS and
-// shared by the 4 waves.  Per wave and block:
+// (ascending).  Per wave and block:
 //   S^T (64 keys x 32 queries) = K_b Q^T    2 x (D/16) MFMA 32x32x16
 //   online softmax in log2 units, the prior log2 p_ib added per row
 //   O^T (D x 32)  += V_b^T P^T              (D/32) x 4 MFMA 32x32x16
@@ -21,21 +18,59 @@
 // row max / sum need one cross-half exchange, and the result of S^T feeds
 // the B operand of the PV product directly (keys are the contraction index,
 // so the order in which a lane holds them only has to match V's).
+//
+// Staging: the K and V tiles of a block (64 rows of D bf16 each) are copied
+// from global memory straight into LDS by the load unit (16 bytes per
+// lane, 1 KB per wave instruction), double-buffered: while the waves
+// compute block e from one buffer pair, the copy of block e+1 fills the
+// other, and one barrier per block hands the buffers over.  The tiles keep
+// K's and V's row-major layout with the 16-byte chunks of each row
+// permuted (XOR with a function of the row), which makes the K operand
+// reads (16 bytes per lane) and the transposing V operand reads
+// (ds_read_b64_tr_b16, 8 bytes per lane) free of bank conflicts.
+//
 // The per-(row, block) prior is recomputed from the Stage-1 score
-// arithmetic (coarse_acc_chunk) for 32 listed blocks at a time.
+// arithmetic (coarse_acc_chunk) for 32 listed blocks at a time and kept in
+// registers.
+template <int D> struct TileSwz;
+template <> struct TileSwz<128> {  // 16 chunks of 16 B per row
+  static __device__ __forceinline__ int k(int r) { return r & 15; }
+  static __device__ __forceinline__ int v(int r) { return (r & 3) << 2; }
+};
+template <> struct TileSwz<64> {   // 8 chunks of 16 B per row
+  static __device__ __forceinline__ int k(int r) { return (r >> 1) & 7; }
+  static __device__ __forceinline__ int v(int r) { return ((r >> 1) & 1) << 2; }
+};
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// 16 bytes per lane from global memory into LDS: lane L of the wave writes
+// bytes 16 L .. 16 L + 15 after the wave-uniform address lds.
+__device__ __forceinline__ void copy16_to_lds(const bf16_t* g, bf16_t* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+
+// 4 bf16 from 4 consecutive rows (LDS transposing read, see the caller).
+__device__ __forceinline__ bf16x4 ds_read_tr4(const bf16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4*)(__attribute__((address_space(3))) bf16_t*)(p));
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
-  constexpr int KP = D + 8;   // K row pitch in LDS (bf16)
-  constexpr int VP = VT_PITCH;  // V^T row pitch in LDS (bf16)
-  constexpr int CH = D / 8;   // 16-byte chunks per key row
-  constexpr int NKL = 64 * CH / 256;       // K uint4 per thread
-  constexpr int NVP = 32 * CH / 256;       // V key pairs per thread
-  __shared__ __attribute__((aligned(16))) bf16_t ks[64 * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t vt[D * VP];
-  __shared__ __attribute__((aligned(16))) float pri[4][32 * 32];
+  constexpr int CH = D / 8;          // 16-byte chunks per row
+  constexpr int RPI = 1024 / (2 * D);  // rows per 1 KB copy instruction
+  constexpr int NI = 64 / RPI / 4;   // copy instructions per wave and tile
+  constexpr int KS = D / 16;         // k-steps of the S product
+  constexpr int NDT = D / 32;        // 32-row d tiles of O^T
+  // one object per buffer, so that reads of one buffer are not ordered
+  // behind the copy into the other
+  __shared__ __attribute__((aligned(16))) bf16_t kt0[64 * D];
+  __shared__ __attribute__((aligned(16))) bf16_t kt1[64 * D];
+  __shared__ __attribute__((aligned(16))) bf16_t vt0[64 * D];
+  __shared__ __attribute__((aligned(16))) bf16_t vt1[64 * D];
   __shared__ int lst[DASH_MAX_NB];  // the tile's block list
-  static_assert(D != 128 || D * VP >= 2 * 32 * KP, "epilogue space in vt");
-  static_assert(D == 128 || 4 * 32 * 32 * 2 >= 2 * 32 * KP, "epilogue space in pri");
+  static_assert(32 * (D + 8) <= 64 * D, "epilogue staging space");
 
   const int nb = a.T / DASH_BLOCK;
   const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
@@ -63,99 +98,83 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
   const int cnt = a.tile_cnt[bh * ntile + tile];
   const CoarseArith ca = a.ca;
   const float sl2 = a.fine_scale * LOG2E_F;
-  // Stage the block list in LDS once: every later block index is an LDS
-  // read instead of a dependent global load in front of each K/V fetch.
-  for (int x = threadIdx.x; x < cnt; x += 256) lst[x] = glist[x];
+  // The block list is staged in LDS: a global (vector-memory) load inside
+  // the loop would wait for the tile copies in flight, which retire on the
+  // same counter.
+  for (int x = tid; x < cnt; x += 256) lst[x] = glist[x];
   __syncthreads();
   const int* list = lst;
 
-  bf16x8 qb[D / 16];
+  bf16x8 qb[KS];
   float tau_i = 0.f, ln_i = 0.f;
   if (active) {
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) qb[s] = load8(Q + (size_t)i * D + 16 * s + 8 * h);
+    for (int s = 0; s < KS; ++s) qb[s] = load8(Q + (size_t)i * D + 16 * s + 8 * h);
     tau_i = a.tau[bh * a.T + i];
     ln_i = a.lognorm[bh * a.T + i];
   }
-  f32x16 oacc[D / 32];
+  f32x16 oacc[NDT];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
+  for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
   float mrow = -INFINITY, lrow = 0.f;
 
-  uint4 kr[NKL], vr[2 * NVP];
-  auto gload = [&](int b) {
-    const bf16_t* kb0 = K + (size_t)b * DASH_BLOCK * D;
-    const bf16_t* vb0 = V + (size_t)b * DASH_BLOCK * D;
+  // copy block b's K and V tiles into LDS: this wave fills rows
+  // RPI*(NI*w + q) + lane/CH, chunk lane%CH, from source chunk
+  // (lane%CH) ^ swz(row)
+  auto copy_block = [&](int b, bf16_t* kd, bf16_t* vd) {
+    const bf16_t* kg = K + (size_t)b * DASH_BLOCK * D;
+    const bf16_t* vg = V + (size_t)b * DASH_BLOCK * D;
 #pragma unroll
-    for (int x = 0; x < NKL; ++x) {
-      const int idx = tid + 256 * x;
-      kr[x] = *reinterpret_cast<const uint4*>(kb0 + (size_t)(idx / CH) * D + (idx % CH) * 8);
-    }
-#pragma unroll
-    for (int x = 0; x < NVP; ++x) {
-      const int idx = tid + 256 * x;
-      const int pr = vt_pos(idx / CH), ch = idx % CH;  // thread item = pair position idx / CH
-      vr[2 * x] = *reinterpret_cast<const uint4*>(vb0 + (size_t)(2 * pr) * D + ch * 8);
-      vr[2 * x + 1] = *reinterpret_cast<const uint4*>(vb0 + (size_t)(2 * pr + 1) * D + ch * 8);
-    }
-  };
-  auto sstore = [&]() {
-#pragma unroll
-    for (int x = 0; x < NKL; ++x) {
-      const int idx = tid + 256 * x;
-      *reinterpret_cast<uint4*>(&ks[(idx / CH) * KP + (idx % CH) * 8]) = kr[x];
-    }
-#pragma unroll
-    for (int x = 0; x < NVP; ++x) {
-      const int idx = tid + 256 * x;
-      const int pos = idx / CH, ch = idx % CH;
-      const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&vr[2 * x]);
-      const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&vr[2 * x + 1]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        // element e of key 2 pr (low half) and of key 2 pr + 1 (high half)
-        const uint32_t pk = __builtin_amdgcn_perm(v1[e >> 1], v0[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
-        const int d = ch * 8 + e;
-        *reinterpret_cast<uint32_t*>(&vt[d * VP + 2 * vt_slot(d, pos)]) = pk;
-      }
+    for (int q = 0; q < NI; ++q) {
+      const int r0 = RPI * (NI * w + q);
+      const int row = r0 + l / CH, slot = l % CH;
+      copy16_to_lds(kg + (size_t)row * D + 8 * (slot ^ TileSwz<D>::k(row)), kd + r0 * D);
+      copy16_to_lds(vg + (size_t)row * D + 8 * (slot ^ TileSwz<D>::v(row)), vd + r0 * D);
     }
   };
 
-  // One listed block.  OWN: the block may be this wave's own (diagonal)
-  // block or lie after it; only the tile's own blocks, walked last, take
-  // that path, so the off-diagonal loop carries no causal-mask code.
-  auto block_step = [&](int e, auto own_tag) {
-    constexpr bool OWN = decltype(own_tag)::value;
-    const int b = list[e];
-    __syncthreads();  // every wave is done with the previous block's LDS
-    sstore();
-    if ((e & 31) == 0 && active) {
-      // log2 prior for this wave's 32 rows and listed blocks e .. e+31
-      const int ent = e + j;
-      f32x16 acc = coarse_acc_chunk<D>(KB, ent < cnt ? list[ent] : 0, qb);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int slot = acc_row32(r, l);
-        const int en = e + slot;
-        float p2 = -INFINITY;
-        if (en < cnt) {
-          const int bb = list[en];
-          if (!a.causal || bb < wblk) p2 = ca.logp(ca.u_of(acc[r]), tau_i, ln_i) * LOG2E_F;
-        }
-        pri[w][slot * 32 + j] = p2;
-      }
-    }
-    __syncthreads();  // LDS tile and priors visible
-    if (e + 1 < cnt) gload(list[e + 1]);
+  // log2 priors of this wave's 32 rows for listed blocks e0 .. e0+31: lane
+  // (j, h) holds slots 8(r/4) + 4h + r%4 of row j in pacc[r]
+  f32x16 pacc;
+  auto prior_chunk = [&](int e0) {
     if (!active) return;
-    bool diag = false;
-    if constexpr (OWN) {
-      if (b > wblk) return;  // after this wave's rows
-      diag = b == wblk;
+    const int ent = e0 + j;
+    pacc = coarse_acc_chunk<D>(KB, ent < cnt ? list[ent] : 0, qb);
+    // all summary loads in flight before the first MFMA
+    __builtin_amdgcn_sched_group_barrier(0x020, KS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int en = e0 + acc_row32(r, l);
+      float p2 = -INFINITY;
+      if (en < cnt) {
+        const int bb = list[en];
+        if (!a.causal || bb < wblk) p2 = ca.logp(ca.u_of(pacc[r]), tau_i, ln_i) * LOG2E_F;
+      }
+      pacc[r] = p2;
     }
-    const float pr = diag ? 0.f : pri[w][(e & 31) * 32 + j];
+  };
+  // prior of entry e for this lane's row: slot e%32 sits in register
+  // 4(slot/8) + slot%4 of the half (slot/4)%2
+  auto prior_of = [&](int e) -> float {
+    const int slot = e & 31;
+    const int rr = 4 * (slot >> 3) + (slot & 3);
+    float v = pacc[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) v = (r == rr) ? pacc[r] : v;
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    // sw[0]: lanes 0-31 keep their value, lanes 32-63 get lanes 0-31's;
+    // sw[1]: lanes 0-31 get lanes 32-63's, lanes 32-63 keep theirs
+    return __uint_as_float(((slot >> 2) & 1) ? sw[1] : sw[0]);
+  };
+
+  auto block_step = [&](int e, const bf16_t* kt, const bf16_t* vt) {
+    const int b = list[e];
+    const bool diag = a.causal && b == wblk;
+    if (a.causal && b > wblk) return;  // after this wave's rows
+    const float pr = diag ? 0.f : prior_of(e);
     if (!diag && __ballot(pr != -INFINITY) == 0ull) return;
 
     // S^T = K_b Q^T
@@ -163,31 +182,33 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&ks[j * KP + 16 * s + 8 * h]);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&ks[(32 + j) * KP + 16 * s + 8 * h]);
+    for (int s = 0; s < KS; ++s) {
+      const int c = 2 * s + h;
+      const bf16x8 a0 = load8(kt + j * D + 8 * (c ^ TileSwz<D>::k(j)));
+      const bf16x8 a1 = load8(kt + (32 + j) * D + 8 * (c ^ TileSwz<D>::k(32 + j)));
       s0 = mfma32(a0, qb[s], s0);
       s1 = mfma32(a1, qb[s], s1);
     }
-    if constexpr (OWN) {
-      if (diag) {
+    if (diag) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = b * DASH_BLOCK + acc_row32(r, l);
-          if (key > i) s0[r] = -INFINITY;
-          if (key + 32 > i) s1[r] = -INFINITY;
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int key = b * DASH_BLOCK + acc_row32(r, l);
+        if (key > i) s0[r] = -INFINITY;
+        if (key + 32 > i) s1[r] = -INFINITY;
       }
     }
     // The prior is constant over a row's keys in this block, so the block
     // max is taken on the raw scores and every weight is one FMA + exp2:
     // p = 2^(s * scale * log2e + prior2 - m).
-    float mb = s0[0];
+    float mb = fmaxf(s0[0], s0[1]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mb = fmaxf(mb, s0[r]);
+    for (int r = 2; r < 16; ++r) mb = fmaxf(mb, s0[r]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) mb = fmaxf(mb, s1[r]);
-    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mb), __float_as_uint(mb), false, false);
+      mb = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
     const float mx = (mb == -INFINITY || pr == -INFINITY) ? -INFINITY : mb * sl2 + pr;
     // Rows keep a reference max and rescale O only when a block's max
     // exceeds it by more than 2^8, so weights stay <= 256 and most blocks
@@ -198,62 +219,79 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
       mrow = mnew;
       lrow *= resc;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] *= resc;
     }
     const float off = (pr == -INFINITY || mrow == -INFINITY) ? -INFINITY : pr - mrow;
     float x[32];
-    float ps = 0.f;
+    float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       x[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], sl2, off));
       x[16 + r] = __builtin_amdgcn_exp2f(fmaf(s1[r], sl2, off));
-      ps += x[r] + x[16 + r];
+      ps0 += x[r];
+      ps1 += x[16 + r];
     }
-    lrow += ps;
-    // O^T += V_b^T P^T, 4 k-steps of 16 keys
+    lrow += ps0 + ps1;
+    // O^T += V_b^T P^T, 4 k-steps of 16 keys.  At k-step s a lane of half h
+    // needs keys 16s+4h+{0..3} and 16s+8+4h+{0..3} of its column d.  Each
+    // transposing read hands lane 4a+b of a 16-lane group element b of the
+    // 8-byte pieces addressed by lanes a, a+4, a+8, a+12 of the group, so
+    // lane t of the group addresses row key0 + t/4, columns
+    // 32 dt + 16 (group % 2) + 4 (t % 4) .. +3.
+    const int tg = l & 15, grp = l >> 4;
+    const int dof = 16 * (grp & 1) + 4 * (tg & 3);  // column offset within a 32-wide d tile
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bf16x8 pb;
 #pragma unroll
       for (int e8 = 0; e8 < 8; ++e8) pb[e8] = (__bf16)x[16 * (s >> 1) + 8 * (s & 1) + e8];
+      const int r1 = 16 * s + 4 * h + (tg >> 2), r2 = r1 + 8;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const int d = 32 * dt + j;
-        const bf16x8 va = load8(&vt[d * VP + 2 * vt_slot(d, 8 * s + 4 * h)]);
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int col = 32 * dt + dof;
+        const int c = col >> 3, half = (col >> 2) & 1;
+        const bf16x4 lo = ds_read_tr4(vt + r1 * D + 8 * (c ^ TileSwz<D>::v(r1)) + 4 * half);
+        const bf16x4 hi = ds_read_tr4(vt + r2 * D + 8 * (c ^ TileSwz<D>::v(r2)) + 4 * half);
+        const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[dt] = mfma32(va, pb, oacc[dt]);
       }
     }
   };
 
-  // With a causal mask the list ends with the tile's own blocks (every other
-  // listed block precedes them): walk the rest first without mask code.
-  const int nown = a.causal ? (min(a.T, (tile + 1) * DASH_QTILE) - tile * DASH_QTILE) / DASH_BLOCK : 0;
-  const int nmain = cnt - nown;
-  if (cnt > 0) gload(list[0]);
-  int e = 0;
-  for (; e < nmain; ++e) block_step(e, std::false_type{});
-  for (; e < cnt; ++e) block_step(e, std::true_type{});
+  if (cnt > 0) {
+    copy_block(list[0], kt0, vt0);
+    int e = 0;
+    for (; e < cnt; e += 2) {
+      if ((e & 31) == 0) prior_chunk(e);
+      __syncthreads();  // block e in buffers 0; everyone is done with buffers 1
+      if (e + 1 < cnt) copy_block(list[e + 1], kt1, vt1);
+      if (active) block_step(e, kt0, vt0);
+      if (e + 1 >= cnt) break;
+      __syncthreads();  // block e+1 in buffers 1; everyone is done with buffers 0
+      if (e + 2 < cnt) copy_block(list[e + 2], kt0, vt0);
+      if (active) block_step(e + 1, kt1, vt1);
+    }
+  }
 
-  // epilogue: O = O^T / l, staged through LDS for 16-byte row stores
+  // epilogue: O = O^T / l, staged through LDS (32 rows x D per wave, row
+  // pitch D + 8, one tile buffer per wave) for 16-byte row stores
   __syncthreads();
+  constexpr int OP = D + 8;
   const float ltot = lrow + __shfl_xor(lrow, 32, 64);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-  // 32 rows x D per wave, row pitch KP: waves 0-1 in ks, waves 2-3 in vt
-  // (D = 128) or in the prior buffer (D = 64), all free after the main loop
-  bf16_t* ost = (w < 2) ? ks + w * 32 * KP
-                        : (D == 128 ? vt : reinterpret_cast<bf16_t*>(&pri[0][0])) + (w - 2) * 32 * KP;
+  bf16_t* ost = w == 0 ? kt0 : w == 1 ? kt1 : w == 2 ? vt0 : vt1;
   if (active) {
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int d = 32 * dt + 8 * r4 + 4 * h;  // registers 4 r4 .. 4 r4 + 3 hold d .. d + 3
         bf16x4 o4;
 #pragma unroll
         for (int x = 0; x < 4; ++x) o4[x] = (__bf16)(oacc[dt][4 * r4 + x] * inv);
-        *reinterpret_cast<bf16x4*>(&ost[j * KP + d]) = o4;
+        *reinterpret_cast<bf16x4*>(&ost[j * OP + d]) = o4;
       }
     if (h == 0) a.lse[bh * a.T + i] = (mrow + __builtin_amdgcn_logf(ltot)) * LN2_F;
   }
@@ -265,7 +303,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
       const int idx = it * 64 + l;
       const int row = idx / CH, ch = idx % CH;
       *reinterpret_cast<uint4*>(O + (size_t)(qrow0 + row) * D + ch * 8) =
-          *reinterpret_cast<const uint4*>(ost + row * KP + ch * 8);
+          *reinterpret_cast<const uint4*>(ost + row * OP + ch * 8);
     }
   }
 }

@@ -87,11 +87,15 @@ struct DecodeArgs {
 template <int D>
 __device__ __forceinline__ f32x16 coarse_acc_chunk(const bf16_t* kb, int brow, const bf16x8 (&qb)[D / 16]) {
   const int h = lane_id() >> 5;
+  // all operand loads first, so that they are in flight together
+  bf16x8 ka[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) ka[s] = load8(kb + (size_t)brow * D + 16 * s + 8 * h);
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) acc = mfma32(load8(kb + (size_t)brow * D + 16 * s + 8 * h), qb[s], acc);
+  for (int s = 0; s < D / 16; ++s) acc = mfma32(ka[s], qb[s], acc);
   return acc;
 }
 
