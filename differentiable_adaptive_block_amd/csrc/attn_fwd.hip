@@ -189,6 +189,13 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
       s0 = mfma32(a0, qb[s], s0);
       s1 = mfma32(a1, qb[s], s1);
     }
+    // issue order: operand reads run 4 ahead of the MFMAs that use them
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int s = 0; s < 2 * KS; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
     if (diag) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -224,29 +231,27 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
         for (int r = 0; r < 16; ++r) oacc[dt][r] *= resc;
     }
     const float off = (pr == -INFINITY || mrow == -INFINITY) ? -INFINITY : pr - mrow;
-    float x[32];
-    float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      x[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], sl2, off));
-      x[16 + r] = __builtin_amdgcn_exp2f(fmaf(s1[r], sl2, off));
-      ps0 += x[r];
-      ps1 += x[16 + r];
-    }
-    lrow += ps0 + ps1;
     // O^T += V_b^T P^T, 4 k-steps of 16 keys.  At k-step s a lane of half h
-    // needs keys 16s+4h+{0..3} and 16s+8+4h+{0..3} of its column d.  Each
+    // needs keys 16s+4h+{0..3} and 16s+8+4h+{0..3} of its column d; its
+    // weights are registers 8(s%2)..8(s%2)+7 of s0 (s < 2) or s1.  Each
     // transposing read hands lane 4a+b of a 16-lane group element b of the
     // 8-byte pieces addressed by lanes a, a+4, a+8, a+12 of the group, so
     // lane t of the group addresses row key0 + t/4, columns
     // 32 dt + 16 (group % 2) + 4 (t % 4) .. +3.
     const int tg = l & 15, grp = l >> 4;
     const int dof = 16 * (grp & 1) + 4 * (tg & 3);  // column offset within a 32-wide d tile
+    float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bf16x8 pb;
 #pragma unroll
-      for (int e8 = 0; e8 < 8; ++e8) pb[e8] = (__bf16)x[16 * (s >> 1) + 8 * (s & 1) + e8];
+      for (int e8 = 0; e8 < 8; ++e8) {
+        const float sv = (s < 2) ? s0[8 * (s & 1) + e8] : s1[8 * (s & 1) + e8];
+        const float x = __builtin_amdgcn_exp2f(fmaf(sv, sl2, off));
+        if (e8 & 1) ps1 += x;
+        else ps0 += x;
+        pb[e8] = (__bf16)x;
+      }
       const int r1 = 16 * s + 4 * h + (tg >> 2), r2 = r1 + 8;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
@@ -257,6 +262,17 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
         const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[dt] = mfma32(va, pb, oacc[dt]);
       }
+    }
+    lrow += ps0 + ps1;
+    // issue order: the first k-step's weights and operand reads, then each
+    // MFMA followed by two operand reads and a share of the next weights
+    __builtin_amdgcn_sched_group_barrier(0x402, 28, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NDT, 0);
+#pragma unroll
+    for (int s = 0; s < 4 * NDT; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 28 / NDT, 0);
     }
   };
 
