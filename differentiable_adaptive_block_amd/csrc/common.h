@@ -146,17 +146,3 @@ struct CoarseArith {
     return softmax ? true : (u - tau) > 0.f;
   }
 };
-
-// [x]_+^m for the entmax weights, exact for the common m = 1, 2, 4.
-__device__ __forceinline__ float pow_m(float x, float m) {
-  if (m == 2.f) return x * x;
-  if (m == 1.f) return x;
-  if (m == 4.f) { float y = x * x; return y * y; }
-  return exp2f(m * log2f(x));
-}
-__device__ __forceinline__ float pow_m1(float x, float m) {  // x^(m-1)
-  if (m == 2.f) return x;
-  if (m == 1.f) return 1.f;
-  if (m == 4.f) return x * x * x;
-  return exp2f((m - 1.f) * log2f(x));
-}

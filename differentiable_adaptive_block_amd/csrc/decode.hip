@@ -5,8 +5,9 @@
 // blocks 0..nb-2 and block nb-1 is attended whole with prior 0.
 //
 // Three kernels, all HBM-bound:
-//   decode_select   one workgroup per row: u = (alpha-1) * coarse_scale * q.kbar_b
-//                   for every candidate (coalesced GEMV over the summaries),
+//   decode_select   one 8-wave workgroup per row: u = (alpha-1) * coarse_scale
+//                   * q.kbar_b for every candidate (coalesced GEMV over the
+//                   summaries, loads of the next chunk in flight),
 //                   entmax threshold, compacted ascending list of the selected
 //                   blocks with their log2 prior, then the last block;
 //   decode_attend   split-KV: workgroup (split s, row) and its 4 waves take list
@@ -14,22 +15,16 @@
 //                   block's 64 keys and values (16 KB each, contiguous) with
 //                   16-byte loads, 1 KB per wave instruction, online softmax;
 //                   the 4 waves merge in LDS and write one partial (m, l, o);
-//   decode_combine  merges the nsplit partials of a row in fixed order.
+//   decode_combine  merges the nsplit partials of a row (one wave per row).
 #include "kernels.h"
 #include "entmax.h"
 
 #define LOG2E_F 1.4426950408889634f
 #define LN2_F 0.6931471805599453f
 
-// 16 lanes share one 256-byte row (D = 128) or two rows (D = 64): lane l
-// holds 8 elements at chunk (l % 16).  Returns the sum over the 16 lanes.
-__device__ __forceinline__ float sum16(float v) {
-  v += __shfl_xor(v, 1, 64);
-  v += __shfl_xor(v, 2, 64);
-  v += __shfl_xor(v, 4, 64);
-  v += __shfl_xor(v, 8, 64);
-  return v;
-}
+// 16 lanes share one 256-byte row (D = 128): lane l holds 8 elements at
+// chunk (l % 16).  Returns the sum over the 16 lanes (a DPP row).
+__device__ __forceinline__ float sum16(float v) { return row16_sum(v); }
 
 __device__ __forceinline__ void unpack8(const uint4& r, float (&f)[8]) {
   const uint32_t w[4] = {r.x, r.y, r.z, r.w};
@@ -43,8 +38,11 @@ __device__ __forceinline__ void unpack8(const uint4& r, float (&f)[8]) {
 // ---------------------------------------------------------------------------- selection
 
 template <int NPL>
-__global__ __launch_bounds__(256) void decode_select_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(512) void decode_select_kernel(DecodeArgs a) {
   constexpr int D = 128;
+  constexpr int NW = 8;               // waves
+  constexpr int UN = 8;               // 16-byte loads per lane and chunk
+  constexpr int PER = NW * 4 * UN;    // summaries per chunk
   __shared__ float us[NPL * 64];
   const int row = blockIdx.x;
   const int nb = a.N / DASH_BLOCK;
@@ -55,26 +53,38 @@ __global__ __launch_bounds__(256) void decode_select_kernel(DecodeArgs a) {
   const CoarseArith ca = a.ca;
   float qf[8];
   unpack8(*reinterpret_cast<const uint4*>(q + (l & 15) * 8), qf);
-  // 4 summaries per wave instruction, 16 lanes each; 8 loads in flight per lane
-  constexpr int UN = 8;
-  for (int b0 = w * 4; b0 < nc; b0 += 16 * UN) {
-    uint4 kr[UN];
+  // 16 lanes per summary row (8 elements each), 4 rows per wave instruction;
+  // chunk k covers rows PER k .. PER k + PER - 1, and the next chunk's loads
+  // are issued before this chunk's dot products
+  const int nchunk = (nc + PER - 1) / PER;
+  auto issue = [&](int ck, uint4 (&R)[UN]) {
 #pragma unroll
     for (int x = 0; x < UN; ++x) {
-      const int b = b0 + 16 * x + (l >> 4);
-      kr[x] = b < nc ? *reinterpret_cast<const uint4*>(kb + (size_t)b * D + (l & 15) * 8) : make_uint4(0, 0, 0, 0);
+      const int b = ck * PER + (x * NW + w) * 4 + (l >> 4);
+      R[x] = b < nc ? *reinterpret_cast<const uint4*>(kb + (size_t)b * D + (l & 15) * 8) : make_uint4(0, 0, 0, 0);
     }
+  };
+  auto consume = [&](int ck, const uint4 (&R)[UN]) {
 #pragma unroll
     for (int x = 0; x < UN; ++x) {
-      const int b = b0 + 16 * x + (l >> 4);
+      const int b = ck * PER + (x * NW + w) * 4 + (l >> 4);
       float kf[8];
-      unpack8(kr[x], kf);
+      unpack8(R[x], kf);
       float part = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) part = fmaf(qf[e], kf[e], part);
       part = sum16(part);
       if (b < nc && (l & 15) == 0) us[b] = ca.u_of(part);
     }
+  };
+  uint4 ra[UN], rb[UN];
+  if (nchunk > 0) issue(0, ra);
+  for (int ck = 0; ck < nchunk; ck += 2) {
+    if (ck + 1 < nchunk) issue(ck + 1, rb);
+    consume(ck, ra);
+    if (ck + 1 >= nchunk) break;
+    if (ck + 2 < nchunk) issue(ck + 2, ra);
+    consume(ck + 1, rb);
   }
   __syncthreads();
   if (w != 0) return;
@@ -216,25 +226,33 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(DecodeArgs a) {
   }
 }
 
-__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
+// One wave per row, 4 rows per workgroup: lane s < nsplit holds split s's
+// (m, l); the output sums run over the splits with their scales read back
+// lane by lane.
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   constexpr int D = 128;
-  const int row = blockIdx.x;
-  const int l = threadIdx.x;
-  const float* part = a.part + (size_t)row * a.nsplit * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, part[s * (D + 2) + D]);
+  constexpr int NS = DASH_DEC_SPLIT;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.SH) return;
+  const int l = threadIdx.x & 63;
+  const float* part = a.part + (size_t)row * NS * (D + 2);
+  const float ms = l < NS ? part[l * (D + 2) + D] : -INFINITY;
+  const float ls = l < NS ? part[l * (D + 2) + D + 1] : 0.f;
+  const float M = grp_max<64>(ms);
   const float Mr = M == -INFINITY ? 0.f : M;
-  float L = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float* p = part + s * (D + 2);
-    const float sc = exp2f(p[D] - Mr);
-    L += p[D + 1] * sc;
-    o0 += p[l] * sc;
-    o1 += p[l + 64] * sc;
+  const float sc = (l < NS && ms != -INFINITY) ? __builtin_amdgcn_exp2f(ms - Mr) : 0.f;
+  const float L = grp_sum<64>(ls * sc);
+  float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const float scs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), s));
+    o0 = fmaf(part[s * (D + 2) + l], scs, o0);
+    o1 = fmaf(part[s * (D + 2) + l + 64], scs, o1);
   }
   bf16_t* O = reinterpret_cast<bf16_t*>(a.o) + (size_t)row * D;
-  O[l] = f2bf(o0 / L);
-  O[l + 64] = f2bf(o1 / L);
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  O[l] = f2bf(o0 * inv);
+  O[l + 64] = f2bf(o1 * inv);
   if (l == 0 && a.lse) a.lse[row] = (M + __log2f(L)) * LN2_F;
 }
 
@@ -243,16 +261,16 @@ hipError_t launch_decode(const DecodeArgs& a0, int dtype, hipStream_t st) {
   DecodeArgs a = a0;
   a.nsplit = DASH_DEC_SPLIT;
   const int nb = a.N / DASH_BLOCK;
-  if (nb <= 128) decode_select_kernel<2><<<a.SH, 256, 0, st>>>(a);
-  else if (nb <= 256) decode_select_kernel<4><<<a.SH, 256, 0, st>>>(a);
-  else if (nb <= 512) decode_select_kernel<8><<<a.SH, 256, 0, st>>>(a);
-  else if (nb <= 1024) decode_select_kernel<16><<<a.SH, 256, 0, st>>>(a);
-  else if (nb <= 1536) decode_select_kernel<24><<<a.SH, 256, 0, st>>>(a);
-  else decode_select_kernel<32><<<a.SH, 256, 0, st>>>(a);
+  if (nb <= 128) decode_select_kernel<2><<<a.SH, 512, 0, st>>>(a);
+  else if (nb <= 256) decode_select_kernel<4><<<a.SH, 512, 0, st>>>(a);
+  else if (nb <= 512) decode_select_kernel<8><<<a.SH, 512, 0, st>>>(a);
+  else if (nb <= 1024) decode_select_kernel<16><<<a.SH, 512, 0, st>>>(a);
+  else if (nb <= 1536) decode_select_kernel<24><<<a.SH, 512, 0, st>>>(a);
+  else decode_select_kernel<32><<<a.SH, 512, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   decode_attend_kernel<<<dim3(a.nsplit, a.SH), 256, 0, st>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  decode_combine_kernel<<<a.SH, 64, 0, st>>>(a);
+  decode_combine_kernel<<<(a.SH + 3) / 4, 256, 0, st>>>(a);
   return hipGetLastError();
 }

@@ -95,52 +95,48 @@ __device__ __forceinline__ int grp_sum_i(int v) {
   return v;
 }
 
-// One row per group of G lanes.  Lane (group-local index g) holds
-// u[k] = score of candidate g + G k for k < NPL, or -INFINITY where there is
-// none; only k with G k < nvalid can hold a candidate (nvalid is the same on
-// every lane of the wave, so the loops below skip the rest with scalar
-// branches); every row has at least one candidate.  All lanes of the wave
-// call this together; the result is identical across each group.
-template <int NPL, int G>
-__device__ __forceinline__ EntmaxOut entmax_solve(const float (&u)[NPL], int nvalid, const CoarseArith& ca) {
-  float umax = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < NPL; ++k)
-    if (k * G < nvalid) umax = fmaxf(umax, u[k]);
-  umax = grp_max<G>(umax);
-  EntmaxOut r;
-  if (ca.softmax) {
-    float s = 0.f;
-#pragma unroll
-    for (int k = 0; k < NPL; ++k)
-      if (k * G < nvalid) s += (u[k] != -INFINITY) ? __expf(u[k] - umax) : 0.f;
-    s = grp_sum<G>(s);
-    r.tau = umax + __logf(s);
-    float s2 = 0.f;
-    int c = 0;
-#pragma unroll
-    for (int k = 0; k < NPL; ++k) {
-      if (k * G < nvalid && u[k] != -INFINITY) { s2 += __expf(u[k] - r.tau); ++c; }
-    }
-    r.lognorm = __logf(grp_sum<G>(s2));
-    r.nsel = grp_sum_i<G>(c);
-    return r;
+// [x]_+^m and [x]_+^(m-1) for x = v - t, branch-free: PW = 1 (m = 1,
+// alpha = 2), 2 (alpha = 1.5), 4 (alpha = 1.25), 0 (any other m > 1, via
+// the hardware exp2 / log2; x <= 0 gives log2 = -inf and so 0).
+template <int PW>
+__device__ __forceinline__ void entmax_terms(float x, float m, float& fx, float& fpx) {
+  x = fmaxf(x, 0.f);
+  if constexpr (PW == 1) {
+    fx = x;
+    fpx = x > 0.f ? 1.f : 0.f;
+  } else if constexpr (PW == 2) {
+    fx = x * x;
+    fpx = x;
+  } else if constexpr (PW == 4) {
+    const float x2 = x * x;
+    fx = x2 * x2;
+    fpx = x2 * x;
+  } else {
+    const float lx = __builtin_amdgcn_logf(x);
+    fx = __builtin_amdgcn_exp2f(m * lx);
+    fpx = __builtin_amdgcn_exp2f((m - 1.f) * lx);
   }
-  const float m = ca.m;
+}
+
+// alpha > 1: Newton from the left on t = tau - max u (see the header).
+template <int NPL, int G, int PW>
+__device__ __forceinline__ EntmaxOut entmax_newton(const float (&u)[NPL], int nvalid, float umax, float m) {
   float v[NPL];
 #pragma unroll
   for (int k = 0; k < NPL; ++k) v[k] = u[k] - umax;
-  float t = -1.f;  // relative to max u: f(-1) >= 1 from the largest term alone
+  float t = -1.f;  // f(-1) >= 1 from the largest term alone
   bool done = false;
-  // Newton from the left; groups that have converged keep their t while the
-  // others iterate (all lanes stay active for the DPP reductions).
+  // groups that have converged keep their t while the others iterate (all
+  // lanes stay active for the DPP reductions)
   for (int it = 0; it < 64; ++it) {
     float f = 0.f, fp = 0.f;
 #pragma unroll
     for (int k = 0; k < NPL; ++k) {
       if (k * G < nvalid) {
-        const float x = v[k] - t;
-        if (x > 0.f) { f += pow_m(x, m); fp += pow_m1(x, m); }
+        float a, b;
+        entmax_terms<PW>(v[k] - t, m, a, b);
+        f += a;
+        fp += b;
       }
     }
     f = grp_sum<G>(f);
@@ -155,6 +151,7 @@ __device__ __forceinline__ EntmaxOut entmax_solve(const float (&u)[NPL], int nva
     }
     if (__ballot(!done) == 0ull) break;
   }
+  EntmaxOut r;
   r.tau = umax + t;
   float s = 0.f;
   int c = 0;
@@ -162,10 +159,54 @@ __device__ __forceinline__ EntmaxOut entmax_solve(const float (&u)[NPL], int nva
   for (int k = 0; k < NPL; ++k) {
     if (k * G < nvalid) {
       const float x = u[k] - r.tau;
-      if (x > 0.f) { s += pow_m(x, m); ++c; }
+      float a, b;
+      entmax_terms<PW>(x, m, a, b);
+      s += a;
+      c += x > 0.f ? 1 : 0;
     }
   }
   r.lognorm = __logf(grp_sum<G>(s));
   r.nsel = grp_sum_i<G>(c);
   return r;
+}
+
+// One row per group of G lanes.  Lane (group-local index g) holds
+// u[k] = score of candidate g + G k for k < NPL, or -INFINITY where there is
+// none; only k with G k < nvalid can hold a candidate (nvalid is the same on
+// every lane of the wave, so the loops skip the rest with scalar branches);
+// every row has at least one candidate.  All lanes of the wave call this
+// together; the result is identical across each group.
+template <int NPL, int G>
+__device__ __forceinline__ EntmaxOut entmax_solve(const float (&u)[NPL], int nvalid, const CoarseArith& ca) {
+  float umax = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < NPL; ++k)
+    if (k * G < nvalid) umax = fmaxf(umax, u[k]);
+  umax = grp_max<G>(umax);
+  if (ca.softmax) {
+    EntmaxOut r;
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < NPL; ++k)
+      if (k * G < nvalid) s += __expf(u[k] - umax);  // exp(-inf) = 0 for empty slots
+    s = grp_sum<G>(s);
+    r.tau = umax + __logf(s);
+    float s2 = 0.f;
+    int c = 0;
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) {
+      if (k * G < nvalid) {
+        s2 += __expf(u[k] - r.tau);
+        c += u[k] != -INFINITY ? 1 : 0;
+      }
+    }
+    r.lognorm = __logf(grp_sum<G>(s2));
+    r.nsel = grp_sum_i<G>(c);
+    return r;
+  }
+  const float m = ca.m;
+  if (m == 2.f) return entmax_newton<NPL, G, 2>(u, nvalid, umax, m);
+  if (m == 4.f) return entmax_newton<NPL, G, 4>(u, nvalid, umax, m);
+  if (m == 1.f) return entmax_newton<NPL, G, 1>(u, nvalid, umax, m);
+  return entmax_newton<NPL, G, 0>(u, nvalid, umax, m);
 }

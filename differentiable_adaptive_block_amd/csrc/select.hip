@@ -103,13 +103,14 @@ __device__ __forceinline__ void write_rows16(const SelectArgs& a, size_t row_g, 
   for (int j = 0; j < NJ; ++j) mine[j] = 0u;
 #pragma unroll
   for (int wd = 0; wd < NW; ++wd) {
-    if (32 * wd >= nc) break;  // nc is the same on every lane
-    const int k0 = 2 * wd, k1 = 2 * wd + 1;
-    const unsigned long long b0 = __ballot(g + 16 * k0 < nc && ca.selected(u[k0], e.tau));
-    unsigned long long b1 = 0ull;
-    if (k1 < NPL) b1 = __ballot(g + 16 * k1 < nc && ca.selected(u[k1], e.tau));
-    const uint32_t word = (uint32_t)((b0 >> sh) & 0xFFFFull) | ((uint32_t)((b1 >> sh) & 0xFFFFull) << 16);
-    if (g == (wd & 15)) mine[wd >> 4] = word;
+    if (32 * wd < nc) {  // nc is the same on every lane
+      const int k0 = 2 * wd, k1 = 2 * wd + 1;
+      const unsigned long long b0 = __ballot(g + 16 * k0 < nc && ca.selected(u[k0], e.tau));
+      unsigned long long b1 = 0ull;
+      if (k1 < NPL) b1 = __ballot(g + 16 * k1 < nc && ca.selected(u[k1], e.tau));
+      const uint32_t word = (uint32_t)((b0 >> sh) & 0xFFFFull) | ((uint32_t)((b1 >> sh) & 0xFFFFull) << 16);
+      if (g == (wd & 15)) mine[wd >> 4] = word;
+    }
   }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
