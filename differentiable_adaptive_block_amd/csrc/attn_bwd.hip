@@ -17,13 +17,15 @@
 //   bwd_dq        query-tile-major, walks the tile's block list like the forward;
 //                 MFMA for S^T, dP^T and dQ^T; writes G and the log2 prior of
 //                 every (row, listed block) to the workspace
-//   bwd_entmax    per row: dz over its listed candidate blocks (overwrites G)
+//   bwd_coarse    per row: dz over its listed candidate blocks (overwrites G),
+//                 then dQ = fine part + coarse part, to bf16
 //   bwd_dkdv      key-block-major over the query tiles whose list holds the
 //                 block; MFMA for S, dP, dV^T and dK^T; also dkbar and the
 //                 pooling term
-//   bwd_dq_final  dQ = fine part + coarse part, to bf16
 // fp32 path: one wave per query row, dK / dV / dkbar by float atomics.
 #include "kernels.h"
+#include "entmax.h"
+#include "tiles.h"
 
 #define LOG2E_F 1.4426950408889634f
 
@@ -242,57 +244,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------- entmax backward
-
-// One thread per query row: dz over the row's listed candidate blocks,
-// written over G; zero for every other slot.
-__global__ __launch_bounds__(128) void bwd_entmax_kernel(BwdArgs a) {
-  const int nb = a.T / DASH_BLOCK;
-  const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
-  const size_t bh = blockIdx.y;
-  const int tile = blockIdx.x;
-  const int rt = threadIdx.x;
-  const int i = tile * DASH_QTILE + rt;
-  if (i >= a.T) return;
-  const int own = i / DASH_BLOCK;
-  const int* list = a.tile_blk + (bh * ntile + tile) * nb;
-  const int cnt = a.tile_cnt[bh * ntile + tile];
-  const float am2 = 2.f - (a.ca.softmax ? 1.f : 1.f + a.ca.am1);  // 2 - alpha
-  const float am1n = am2 - 1.f;                                    // 1 - alpha
-  float ss = 0.f, ssg = 0.f;
-  for (int e = 0; e < cnt; ++e) {
-    const int b = list[e];
-    if (a.causal && b >= own) continue;
-    const size_t gi = gidx(bh, ntile, tile, nb, e, rt);
-    const float lp2 = a.pbuf[gi];
-    if (lp2 == -INFINITY) continue;
-    ss += __builtin_amdgcn_exp2f(am2 * lp2);
-    ssg += a.gbuf[gi] * __builtin_amdgcn_exp2f(am1n * lp2);
-  }
-  const float ratio = ss > 0.f ? ssg / ss : 0.f;
-  for (int e = 0; e < cnt; ++e) {
-    const int b = list[e];
-    const size_t gi = gidx(bh, ntile, tile, nb, e, rt);
-    float dz = 0.f;
-    if (!(a.causal && b >= own)) {
-      const float lp2 = a.pbuf[gi];
-      if (lp2 != -INFINITY)
-        dz = a.gbuf[gi] * __builtin_amdgcn_exp2f(am1n * lp2) - __builtin_amdgcn_exp2f(am2 * lp2) * ratio;
-    }
-    a.gbuf[gi] = dz;
-  }
-}
-
 // ---------------------------------------------------------------------------- dK, dV, dkbar
 
-// Work item of bwd_dkdv: a 64-query chunk (tile t, half c) that sees at
-// least one of the workgroup's two key blocks; slot[k] = position of block
-// b0 + k in tile t's list, or -1 when the tile does not list it or (causal)
-// the chunk's queries all precede it.
-struct DkdvItem {
-  int t, c, slot0, slot1;
-};
-
+// Position of block b in a tile's ascending list (from the tile's bit set),
+// or -1 when the tile does not list it.
 __device__ __forceinline__ int list_slot(const uint32_t* bits, int b) {
   const uint32_t word = bits[b >> 5];
   if (!((word >> (b & 31)) & 1u)) return -1;
@@ -301,64 +256,37 @@ __device__ __forceinline__ int list_slot(const uint32_t* bits, int b) {
   return slot;
 }
 
-// First item at or after (t, c); t == ntile when there is none.
-__device__ __forceinline__ DkdvItem dkdv_find(const BwdArgs& a, size_t bh, int ntile, int nbw, int b0, int nblk,
-                                              int t, int c) {
-  DkdvItem it;
-  for (; t < ntile; ++t, c = 0) {
-    const uint32_t* bits = a.tile_bits + (bh * ntile + t) * nbw;
-    const int s0 = list_slot(bits, b0);
-    const int s1 = nblk > 1 ? list_slot(bits, b0 + 1) : -1;
-    if (s0 < 0 && s1 < 0) continue;
-    for (; c < DASH_QTILE / 64; ++c) {
-      const int q0 = t * DASH_QTILE + c * 64;
-      if (q0 >= a.T) break;
-      const int ob = q0 / DASH_BLOCK;
-      it.slot0 = (a.causal && ob < b0) ? -1 : s0;
-      it.slot1 = (a.causal && ob < b0 + 1) ? -1 : s1;
-      if (it.slot0 >= 0 || it.slot1 >= 0) {
-        it.t = t;
-        it.c = c;
-        return it;
-      }
-    }
-  }
-  it.t = ntile;
-  it.c = 0;
-  it.slot0 = it.slot1 = -1;
-  return it;
-}
-
 // Key-block-major: a workgroup of 8 waves owns 128 keys (blocks b0, b0+1)
-// and walks the 64-query chunks of the query tiles that list either block.
-// Wave w: block kb = w/4, key half kh = (w/2)&1, query half qh = w&1.  Per
-// chunk and wave (32 queries x 32 keys), with keys as MFMA columns:
-//   S  = Q K^T, dP = dO V^T     (D/16 MFMA each, Q/dO rows as operand A)
-//   dV^T += dO^T P, dK^T += Q^T dS   (dO^T, Q^T staged transposed in LDS)
-// The next item's Q/dO rows are loaded into registers while the current
-// one is computed.  dkbar_b = coarse_scale sum_q dz_qb q_q accumulates from
-// the same staging registers.
+// and walks the items: 64-query chunks (tile t, half c) that see either
+// block, in ascending (t, c); the item list is built once in LDS.  Wave w:
+// block kb = w/4, key half kh = (w/2)&1, query half qh = w&1.  Per item and
+// wave (32 queries x 32 keys), with keys as MFMA columns:
+//   S = Q K^T, dP = dO V^T               D/16 MFMA each
+//   dV^T += dO^T P, dK^T += Q^T dS        (D/32) x 2 MFMA each
+// K and V stay in LDS for the whole walk; each item's Q and dO chunks are
+// copied straight into LDS, double-buffered (one barrier per item), in the
+// permutation that serves both the row reads (S, dP) and the transposing
+// reads (dV, dK).  dkbar_b = coarse_scale sum_q dz_qb q_q accumulates from
+// the same Q chunks.
 template <int D>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int KP = D + 8;
-  constexpr int QP = 64 + 4;
+  constexpr int KS = D / 16;
+  constexpr int NDT = D / 32;
   constexpr int CH = D / 8;
-  constexpr int ROWK = 128 * KP;
-  constexpr int ROWQ = 64 * KP;
-  constexpr int COLQ = D * QP;
-  constexpr int NKL = 128 * CH / 512;  // K (and V) uint4 per thread for the 128 key rows
-  constexpr int NITEM = 32 * CH;       // (row pair, chunk) staging items per query chunk
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * ROWK + 2 * ROWQ + 2 * COLQ];
-  static_assert((2 * ROWK + 2 * ROWQ + 2 * COLQ) * 2 >= 4 * 2 * (D / 32) * 16 * 64 * 4, "reduction space");
-  static_assert((2 * ROWK + 2 * ROWQ + 2 * COLQ) * 2 >= 2 * 32 * D * 4, "dkbar reduction space");
-  bf16_t* ks = smem;
-  bf16_t* vs = ks + ROWK;
-  bf16_t* qs = vs + ROWK;
-  bf16_t* os_ = qs + ROWQ;
-  bf16_t* qt = os_ + ROWQ;
-  bf16_t* ot = qt + COLQ;
-  __shared__ float prq[2][64], dzq[2][64], lsq[64], dlq[64];
+  constexpr int NITEM = 32 * CH;       // (row pair, chunk) dkbar items per query chunk
+  constexpr int MAXIT = 2 * (DASH_MAX_NB / 2);  // 64-query chunks of the longest sequence
+  __shared__ __attribute__((aligned(16))) bf16_t ks[128 * D];
+  __shared__ __attribute__((aligned(16))) bf16_t vs[128 * D];
+  __shared__ __attribute__((aligned(16))) bf16_t qc0[64 * D];
+  __shared__ __attribute__((aligned(16))) bf16_t qc1[64 * D];
+  __shared__ __attribute__((aligned(16))) bf16_t oc0[64 * D];
+  __shared__ __attribute__((aligned(16))) bf16_t oc1[64 * D];
+  __shared__ float prq[2][2][64], dzq[2][2][64], dlq[2][64];  // [buffer][block][row], [buffer][row]
+  __shared__ int itm[MAXIT][3];                                // (t * 2 + c, slot0, slot1)
+  __shared__ int nit_s, wsum[8];
   __shared__ float kbg[2][D];
+  static_assert(2 * 32 * D * 4 <= 128 * D * 2, "dkbar reduction space in the K tile");
+  static_assert(NDT * 16 * 64 * 4 <= 64 * D * 2, "merge space: one partial per 64-row tile buffer");
 
   const int nb = a.T / DASH_BLOCK;
   const int nbw = (nb + 31) / 32;
@@ -380,164 +308,212 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const bf16_t* dO = reinterpret_cast<const bf16_t*>(a.dout) + bh * a.T * D;
   const float sl2 = a.fine_scale * LOG2E_F;
 
-  // the two key blocks, row-major
-  {
-    const bf16_t* kb0 = K + (size_t)b0 * DASH_BLOCK * D;
-    const bf16_t* vb0 = V + (size_t)b0 * DASH_BLOCK * D;
-#pragma unroll
-    for (int x = 0; x < NKL; ++x) {
-      const int idx = tid + 512 * x;
-      const int row = idx / CH, ch = idx % CH;
-      if (row < 64 * nblk) {
-        *reinterpret_cast<uint4*>(&ks[row * KP + ch * 8]) = *reinterpret_cast<const uint4*>(kb0 + (size_t)row * D + ch * 8);
-        *reinterpret_cast<uint4*>(&vs[row * KP + ch * 8]) = *reinterpret_cast<const uint4*>(vb0 + (size_t)row * D + ch * 8);
+  // K and V of the two blocks (waves 0-3 block 0, waves 4-7 block 1)
+  if (w / 4 < nblk) {
+    const size_t r0 = (size_t)(b0 + w / 4) * DASH_BLOCK * D;
+    copy_tile<D, TileSwz<D>::k>(K + r0, ks + (w / 4) * 64 * D, w & 3, l);
+    copy_tile<D, TileSwz<D>::k>(V + r0, vs + (w / 4) * 64 * D, w & 3, l);
+  }
+
+  // item list: thread x looks at tile x (then x + 512, ...), keeps its 0-2
+  // items, and a workgroup prefix sum places them in ascending order
+  if (tid == 0) nit_s = 0;
+  __syncthreads();
+  for (int t0 = 0; t0 < ntile; t0 += 512) {
+    const int t = t0 + tid;
+    int my[2][3];
+    int n = 0;
+    if (t < ntile) {
+      const uint32_t* bits = a.tile_bits + (bh * ntile + t) * nbw;
+      const int s0 = list_slot(bits, b0);
+      const int s1 = nblk > 1 ? list_slot(bits, b0 + 1) : -1;
+      if (s0 >= 0 || s1 >= 0) {
+        for (int c = 0; c < DASH_QTILE / 64; ++c) {
+          const int q0 = t * DASH_QTILE + c * 64;
+          if (q0 >= a.T) break;
+          const int ob = q0 / DASH_BLOCK;
+          const int sl0 = (a.causal && ob < b0) ? -1 : s0;
+          const int sl1 = (a.causal && ob < b0 + 1) ? -1 : s1;
+          if (sl0 >= 0 || sl1 >= 0) {
+            my[n][0] = 2 * t + c;
+            my[n][1] = sl0;
+            my[n][2] = sl1;
+            ++n;
+          }
+        }
       }
     }
-  }
-  f32x16 dva[D / 32], dka[D / 32];
+    // exclusive prefix sum of n over the workgroup
+    int incl = n;
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (l >= o) incl += y;
+    }
+    if (l == 63) wsum[w] = incl;
+    __syncthreads();
+    int base = nit_s;
+    for (int x = 0; x < w; ++x) base += wsum[x];
+    const int pos = base + incl - n;
+    for (int x = 0; x < n; ++x) {
+      itm[pos + x][0] = my[x][0];
+      itm[pos + x][1] = my[x][1];
+      itm[pos + x][2] = my[x][2];
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int tot = 0;
+      for (int x = 0; x < 8; ++x) tot += wsum[x];
+      nit_s += tot;
+    }
+    __syncthreads();
+  }
+  const int nit = nit_s;
+
+  f32x16 dva[NDT], dka[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) { dva[dt][r] = 0.f; dka[dt][r] = 0.f; }
-  float kbp[2][8];  // dkbar partial of this thread's staging columns
+  float kbp[2][8];  // dkbar partials of this thread's (row pair, chunk)
 #pragma unroll
   for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
     for (int e = 0; e < 8; ++e) kbp[k2][e] = 0.f;
-
-  // staging registers: rows (2pr, 2pr+1), 16-byte chunk ch, of Q and dO
-  const bool stager = tid < NITEM;
+  const bool kbthr = tid < NITEM;
   const int spr = tid / CH, sch = tid % CH;
-  uint4 rq0, rq1, ro0, ro1;
-  float s_pr0 = 0.f, s_pr1 = 0.f, s_dz0 = 0.f, s_dz1 = 0.f, s_ls = 0.f, s_dl = 0.f;
-  auto prefetch = [&](const DkdvItem& it) {
-    const int q0 = it.t * DASH_QTILE + it.c * 64;
-    if (stager) {
-      const size_t r0 = (size_t)(q0 + 2 * spr) * D + sch * 8;
-      rq0 = *reinterpret_cast<const uint4*>(Q + r0);
-      rq1 = *reinterpret_cast<const uint4*>(Q + r0 + D);
-      ro0 = *reinterpret_cast<const uint4*>(dO + r0);
-      ro1 = *reinterpret_cast<const uint4*>(dO + r0 + D);
-    }
+
+  // per-row data of an item: threads 0-63 load it into registers, then
+  // store it into LDS buffer `buf`
+  float s_pr0 = 0.f, s_pr1 = 0.f, s_dz0 = 0.f, s_dz1 = 0.f, s_dl = 0.f;
+  auto load_rows = [&](int n) {
     if (tid < 64) {
-      const int row = it.c * 64 + tid;
-      s_ls = a.lse[bh * a.T + q0 + tid] * LOG2E_F;
+      const int t = itm[n][0] >> 1, c = itm[n][0] & 1;
+      const int q0 = t * DASH_QTILE + c * 64;
+      const int row = c * 64 + tid;
+      const float ls = a.lse[bh * a.T + q0 + tid] * LOG2E_F;
       s_dl = a.delta[bh * a.T + q0 + tid];
-      if (it.slot0 >= 0) {
-        const size_t gi = gidx(bh, ntile, it.t, nb, it.slot0, row);
-        s_pr0 = a.pbuf[gi];
+      s_pr0 = -INFINITY; s_dz0 = 0.f;
+      s_pr1 = -INFINITY; s_dz1 = 0.f;
+      if (itm[n][1] >= 0) {
+        const size_t gi = gidx(bh, ntile, t, nb, itm[n][1], row);
+        s_pr0 = a.pbuf[gi] - ls;  // -inf stays -inf
         s_dz0 = a.gbuf[gi];
-      } else { s_pr0 = -INFINITY; s_dz0 = 0.f; }
-      if (it.slot1 >= 0) {
-        const size_t gi = gidx(bh, ntile, it.t, nb, it.slot1, row);
-        s_pr1 = a.pbuf[gi];
+      }
+      if (itm[n][2] >= 0) {
+        const size_t gi = gidx(bh, ntile, t, nb, itm[n][2], row);
+        s_pr1 = a.pbuf[gi] - ls;
         s_dz1 = a.gbuf[gi];
-      } else { s_pr1 = -INFINITY; s_dz1 = 0.f; }
+      }
+    }
+  };
+  auto store_rows = [&](int buf) {
+    if (tid < 64) {
+      prq[buf][0][tid] = s_pr0;
+      prq[buf][1][tid] = s_pr1;
+      dzq[buf][0][tid] = s_dz0;
+      dzq[buf][1][tid] = s_dz1;
+      dlq[buf][tid] = s_dl;
+    }
+  };
+  auto copy_item = [&](int n, bf16_t* qd, bf16_t* od) {
+    const int t = itm[n][0] >> 1, c = itm[n][0] & 1;
+    const size_t r0 = (size_t)(t * DASH_QTILE + c * 64) * D;
+    if (w < 4) copy_tile<D, TileSwz<D>::kv>(Q + r0, qd, w, l);
+    else copy_tile<D, TileSwz<D>::kv>(dO + r0, od, w - 4, l);
+  };
+
+  auto item_step = [&](int n, int buf, const bf16_t* qc, const bf16_t* oc) {
+    const int t = itm[n][0] >> 1, c = itm[n][0] & 1;
+    const int q0 = t * DASH_QTILE + c * 64;
+    // dkbar partials from the chunk's rows 2 spr, 2 spr + 1, chunk sch
+    if (kbthr) {
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const int row = 2 * spr + rr;
+        const uint4 qv = *reinterpret_cast<const uint4*>(qc + row * D + 8 * (sch ^ TileSwz<D>::kv(row)));
+        const uint32_t wv[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const float z = dzq[buf][k2][row];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            kbp[k2][2 * x] = fmaf(z, __uint_as_float(wv[x] << 16), kbp[k2][2 * x]);
+            kbp[k2][2 * x + 1] = fmaf(z, __uint_as_float(wv[x] & 0xFFFF0000u), kbp[k2][2 * x + 1]);
+          }
+        }
+      }
+    }
+    const int wslot = itm[n][1 + kb];
+    if (wslot < 0) return;
+    const bool diag = a.causal && q0 / DASH_BLOCK == wb;
+    // The operand addresses below depend on the lane only; recomputing them
+    // per item (from a lane index the compiler cannot see through) keeps
+    // them out of the registers held across the item loop.
+    int lx = l;
+    asm volatile("" : "+v"(lx));
+    const int jx = lx & 31, hx = lx >> 5;
+    f32x16 sc, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { sc[r] = 0.f; dp[r] = 0.f; }
+    const int krow = 64 * kb + 32 * kh + jx;
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      const bf16x8 bk = tile_row8<D, TileSwz<D>::k>(ks, krow, st, hx);
+      const bf16x8 bv = tile_row8<D, TileSwz<D>::k>(vs, krow, st, hx);
+      sc = mfma32(tile_row8<D, TileSwz<D>::kv>(qc, 32 * qh + jx, st, hx), bk, sc);
+      dp = mfma32(tile_row8<D, TileSwz<D>::kv>(oc, 32 * qh + jx, st, hx), bv, dp);
+    }
+    const int key = wb * DASH_BLOCK + 32 * kh + j;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      bf16x8 pb, db;
+#pragma unroll
+      for (int e8 = 0; e8 < 8; ++e8) {
+        const int r = 8 * s2 + e8;
+        const int ql = 32 * qh + acc_row32(r, l);
+        float sv = sc[r];
+        if (diag && key > q0 + ql) sv = -INFINITY;
+        const float p = __builtin_amdgcn_exp2f(fmaf(sv, sl2, prq[buf][kb][ql]));  // prior2 - lse2
+        pb[e8] = (__bf16)p;
+        db[e8] = (__bf16)(p * (dp[r] - dlq[buf][ql]));
+      }
+      // queries 16 (2 qh + s2) .. +15 of the chunk are this k-step
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        dva[dt] = mfma32(tile_col8<D, TileSwz<D>::kv>(oc, 2 * qh + s2, dt, lx), pb, dva[dt]);
+        dka[dt] = mfma32(tile_col8<D, TileSwz<D>::kv>(qc, 2 * qh + s2, dt, lx), db, dka[dt]);
+      }
     }
   };
 
-  DkdvItem it = dkdv_find(a, bh, ntile, nbw, b0, nblk, a.causal ? (b0 * DASH_BLOCK) / DASH_QTILE : 0, 0);
-  if (it.t < ntile) prefetch(it);
-  while (it.t < ntile) {
-    const int q0 = it.t * DASH_QTILE + it.c * 64;
-    __syncthreads();  // the previous item's LDS reads are done
-    if (stager) {
-      *reinterpret_cast<uint4*>(&qs[(2 * spr) * KP + sch * 8]) = rq0;
-      *reinterpret_cast<uint4*>(&qs[(2 * spr + 1) * KP + sch * 8]) = rq1;
-      *reinterpret_cast<uint4*>(&os_[(2 * spr) * KP + sch * 8]) = ro0;
-      *reinterpret_cast<uint4*>(&os_[(2 * spr + 1) * KP + sch * 8]) = ro1;
-      const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&rq0);
-      const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&rq1);
-      const uint32_t* c0 = reinterpret_cast<const uint32_t*>(&ro0);
-      const uint32_t* c1 = reinterpret_cast<const uint32_t*>(&ro1);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 1) * 16;
-        *reinterpret_cast<uint32_t*>(&qt[(sch * 8 + e) * QP + 2 * spr]) =
-            ((a0[e >> 1] >> sh) & 0xFFFFu) | (((a1[e >> 1] >> sh) & 0xFFFFu) << 16);
-        *reinterpret_cast<uint32_t*>(&ot[(sch * 8 + e) * QP + 2 * spr]) =
-            ((c0[e >> 1] >> sh) & 0xFFFFu) | (((c1[e >> 1] >> sh) & 0xFFFFu) << 16);
+  if (nit > 0) {
+    load_rows(0);
+    copy_item(0, qc0, oc0);
+    store_rows(0);
+    for (int n = 0; n < nit; n += 2) {
+      __syncthreads();  // item n in buffers 0; everyone is done with buffers 1
+      if (n + 1 < nit) {
+        load_rows(n + 1);  // before the copy: waiting on these loads does not wait on it
+        copy_item(n + 1, qc1, oc1);
       }
-    }
-    if (tid < 64) {
-      prq[0][tid] = s_pr0 - s_ls;  // -inf stays -inf
-      prq[1][tid] = s_pr1 - s_ls;
-      dzq[0][tid] = s_dz0;
-      dzq[1][tid] = s_dz1;
-      lsq[tid] = s_ls;
-      dlq[tid] = s_dl;
-    }
-    __syncthreads();
-    if (stager) {
-      // dkbar partials from the staged rows
-      const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&rq0);
-      const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&rq1);
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const float z0 = dzq[k2][2 * spr], z1 = dzq[k2][2 * spr + 1];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t wa = a0[e >> 1], wb2 = a1[e >> 1];
-          const float qa = __uint_as_float((e & 1) ? (wa & 0xFFFF0000u) : (wa << 16));
-          const float qc = __uint_as_float((e & 1) ? (wb2 & 0xFFFF0000u) : (wb2 << 16));
-          kbp[k2][e] = fmaf(z0, qa, fmaf(z1, qc, kbp[k2][e]));
-        }
+      item_step(n, 0, qc0, oc0);
+      if (n + 1 < nit) store_rows(1);
+      if (n + 1 >= nit) break;
+      __syncthreads();  // item n+1 in buffers 1; everyone is done with buffers 0
+      if (n + 2 < nit) {
+        load_rows(n + 2);
+        copy_item(n + 2, qc0, oc0);
       }
+      item_step(n + 1, 1, qc1, oc1);
+      if (n + 2 < nit) store_rows(0);
     }
-    const DkdvItem nx = dkdv_find(a, bh, ntile, nbw, b0, nblk, it.c + 1 < DASH_QTILE / 64 ? it.t : it.t + 1,
-                                  it.c + 1 < DASH_QTILE / 64 ? it.c + 1 : 0);
-    if (nx.t < ntile) prefetch(nx);
-    const int wslot = kb == 0 ? it.slot0 : it.slot1;
-    if (wslot >= 0) {
-      const bool diag = a.causal && q0 / DASH_BLOCK == wb;
-      f32x16 s, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
-      const int krow = 64 * kb + 32 * kh + j;
-#pragma unroll
-      for (int st = 0; st < D / 16; ++st) {
-        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&qs[(32 * qh + j) * KP + 16 * st + 8 * h]);
-        const bf16x8 ao = *reinterpret_cast<const bf16x8*>(&os_[(32 * qh + j) * KP + 16 * st + 8 * h]);
-        const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&ks[krow * KP + 16 * st + 8 * h]);
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&vs[krow * KP + 16 * st + 8 * h]);
-        s = mfma32(aq, bk, s);
-        dp = mfma32(ao, bv, dp);
-      }
-      const int key = wb * DASH_BLOCK + 32 * kh + j;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        bf16x8 pb, db;
-#pragma unroll
-        for (int e8 = 0; e8 < 8; ++e8) {
-          const int r = 8 * s2 + e8;
-          const int ql = 32 * qh + acc_row32(r, l);
-          float sv = s[r];
-          if (diag && key > q0 + ql) sv = -INFINITY;
-          const float p = __builtin_amdgcn_exp2f(fmaf(sv, sl2, prq[kb][ql]));  // prq holds prior2 - lse2
-          pb[e8] = (__bf16)p;
-          db[e8] = (__bf16)(p * (dp[r] - dlq[ql]));
-        }
-        const int qk0 = 32 * qh + 16 * s2 + 4 * h;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const bf16_t* orow = &ot[(32 * dt + j) * QP + qk0];
-          const bf16_t* qrow = &qt[(32 * dt + j) * QP + qk0];
-          const uint2 olo = *reinterpret_cast<const uint2*>(orow);
-          const uint2 ohi = *reinterpret_cast<const uint2*>(orow + 8);
-          const uint2 qlo = *reinterpret_cast<const uint2*>(qrow);
-          const uint2 qhi = *reinterpret_cast<const uint2*>(qrow + 8);
-          dva[dt] = mfma32(__builtin_bit_cast(bf16x8, make_uint4(olo.x, olo.y, ohi.x, ohi.y)), pb, dva[dt]);
-          dka[dt] = mfma32(__builtin_bit_cast(bf16x8, make_uint4(qlo.x, qlo.y, qhi.x, qhi.y)), db, dka[dt]);
-        }
-      }
-    }
-    it = nx;
   }
 
   // dkbar: sum the 32 row-pair partials of each column in a fixed order
   __syncthreads();
-  float* red = reinterpret_cast<float*>(smem);
-  if (stager) {
+  float* red = reinterpret_cast<float*>(ks);
+  if (kbthr) {
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
@@ -553,16 +529,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
     if (k2 < nblk) a.dkbar[(bh * nb + b0 + k2) * D + d] = g;
   }
   __syncthreads();
-  // merge the two query halves, add the pooling term, write bf16 rows
-  float* red2 = red + 4 * (D / 32) * 16 * 64;
+  // merge the two query halves, add the pooling term, write bf16 rows; the
+  // query-half-1 wave of key pair (kb, kh) leaves its dV and dK partials
+  // ([NDT][16][64] floats each) in two of the eight 64-row tile buffers
   const int pairw = w >> 1;  // (kb, kh) index 0..3
+  float* red1 = reinterpret_cast<float*>(pairw < 2 ? ks + pairw * 64 * D : vs + (pairw - 2) * 64 * D);
+  float* red2 = reinterpret_cast<float*>(pairw == 0 ? qc0 : pairw == 1 ? qc1 : pairw == 2 ? oc0 : oc1);
   if (qh == 1) {
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        red[((pairw * (D / 32) + dt) * 16 + r) * 64 + l] = dva[dt][r];
-        red2[((pairw * (D / 32) + dt) * 16 + r) * 64 + l] = dka[dt][r];
+        red1[(dt * 16 + r) * 64 + l] = dva[dt][r];
+        red2[(dt * 16 + r) * 64 + l] = dka[dt][r];
       }
   }
   __syncthreads();
@@ -571,7 +550,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
     bf16_t* dK = reinterpret_cast<bf16_t*>(a.dk) + bh * a.T * D;
     const int key = wb * DASH_BLOCK + 32 * kh + j;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int d = 32 * dt + 8 * r4 + 4 * h;
@@ -582,8 +561,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const int r = 4 * r4 + 2 * e2 + e;
-            const size_t ri = ((pairw * (D / 32) + dt) * 16 + r) * 64 + l;
-            v0[e] = dva[dt][r] + red[ri];
+            const int ri = (dt * 16 + r) * 64 + l;
+            v0[e] = dva[dt][r] + red1[ri];
             k0[e] = (dka[dt][r] + red2[ri]) * a.fine_scale + kbg[kb][d + 2 * e2 + e] * (1.f / DASH_BLOCK);
           }
           pv2[e2] = (uint32_t)f2bf(v0[0]) | ((uint32_t)f2bf(v0[1]) << 16);
@@ -595,35 +574,102 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------- dQ finalize
+// ---------------------------------------------------------------------------- entmax backward + coarse dQ
 
-// dQ_i = fine part (dq_acc) + coarse_scale * sum_slots dz_i,slot kbar_{list[slot]}.
-// grid (ntile * 4, BH), 256 threads = 32 rows x 8 groups of 16 columns (D = 128)
-// or 32 rows x 8 groups of 8 columns (D = 64).
+// Sum over the 8 consecutive lanes of a row group (DPP: quad swaps, then
+// the half-row mirror), identical in the 8 lanes.
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp_f<DPP_QSWAP1>(v);
+  v += dpp_f<DPP_QSWAP2>(v);
+  v += dpp_f<DPP_HMIRROR>(v);
+  return v;
+}
+
+// Per query row i and the tile's listed candidate blocks b (the entmax
+// Jacobian-vector product): s_b = p_b^(2-alpha) on the support,
+// dz_b = s_b g_b - s_b <s, g> / sum s with g_b = G_ib / p_ib, computed as
+// G_ib p^(1-alpha) from the log2 prior; dz overwrites G (the dK kernel
+// reads it for dkbar).  Then dQ_i = dq_acc_i + coarse_scale sum_b dz_b kbar_b.
+// grid (ntile * 4, BH), 256 threads = 32 rows x 8 threads: thread c of a
+// row takes list slots e = c (mod 8) in the first two passes and columns
+// c G .. c G + G - 1 in the last.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_dq_final_kernel(BwdArgs a) {
-  constexpr int G = D / 8;  // columns per thread
+__global__ __launch_bounds__(256) void bwd_coarse_kernel(BwdArgs a) {
+  constexpr int G = D / 8;
   const int nb = a.T / DASH_BLOCK;
   const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
   const size_t bh = blockIdx.y;
   const int tile = blockIdx.x >> 2;
-  const int sub = blockIdx.x & 3;
-  const int rt = sub * 32 + (threadIdx.x >> 3);
+  const int rt = (blockIdx.x & 3) * 32 + (threadIdx.x >> 3);
   const int cg = threadIdx.x & 7;
   const int i = tile * DASH_QTILE + rt;
-  if (i >= a.T) return;
+  const bool valid = i < a.T;
+  const int own = i / DASH_BLOCK;
   const int* list = a.tile_blk + (bh * ntile + tile) * nb;
   const int cnt = a.tile_cnt[bh * ntile + tile];
-  const bf16_t* KB = reinterpret_cast<const bf16_t*>(a.kbar) + bh * nb * D;
+  const float am2 = 2.f - (a.ca.softmax ? 1.f : 1.f + a.ca.am1);  // 2 - alpha
+  const float am1n = am2 - 1.f;                                    // 1 - alpha
+  float ss = 0.f, ssg = 0.f;
+  if (valid) {
+    for (int e = cg; e < cnt; e += 8) {
+      if (a.causal && list[e] >= own) continue;
+      const size_t gi = gidx(bh, ntile, tile, nb, e, rt);
+      const float lp2 = a.pbuf[gi];
+      if (lp2 == -INFINITY) continue;
+      ss += __builtin_amdgcn_exp2f(am2 * lp2);
+      ssg += a.gbuf[gi] * __builtin_amdgcn_exp2f(am1n * lp2);
+    }
+  }
+  ss = sum8(ss);
+  ssg = sum8(ssg);
+  const float ratio = ss > 0.f ? ssg / ss : 0.f;
+  if (valid) {
+    for (int e = cg; e < cnt; e += 8) {
+      const size_t gi = gidx(bh, ntile, tile, nb, e, rt);
+      float dz = 0.f;
+      if (!(a.causal && list[e] >= own)) {
+        const float lp2 = a.pbuf[gi];
+        if (lp2 != -INFINITY)
+          dz = a.gbuf[gi] * __builtin_amdgcn_exp2f(am1n * lp2) - __builtin_amdgcn_exp2f(am2 * lp2) * ratio;
+      }
+      a.gbuf[gi] = dz;
+    }
+  }
+  __syncthreads();  // every dz of the workgroup's rows is written
+  if (!valid) return;
+  const bf16_t* KB = reinterpret_cast<const bf16_t*>(a.kbar) + bh * nb * D + cg * G;
   float acc[G];
 #pragma unroll
   for (int x = 0; x < G; ++x) acc[x] = 0.f;
-  for (int e = 0; e < cnt; ++e) {
-    const float dz = a.gbuf[gidx(bh, ntile, tile, nb, e, rt)];
-    if (dz == 0.f) continue;
-    const bf16_t* kr = KB + (size_t)list[e] * D + cg * G;
+  constexpr int U = 4;  // list entries per step, loads in flight together
+  for (int e0 = 0; e0 < cnt; e0 += U) {
+    float dz[U];
+    uint4 kr[U][G / 8];
 #pragma unroll
-    for (int x = 0; x < G; ++x) acc[x] = fmaf(dz, bf2f(kr[x]), acc[x]);
+    for (int u = 0; u < U; ++u) {
+      const int e = e0 + u;
+      dz[u] = 0.f;
+      if (e < cnt) {
+        dz[u] = a.gbuf[gidx(bh, ntile, tile, nb, e, rt)];
+        const bf16_t* kr0 = KB + (size_t)list[e] * D;
+#pragma unroll
+        for (int c = 0; c < G / 8; ++c) kr[u][c] = *reinterpret_cast<const uint4*>(kr0 + 8 * c);
+      } else {
+#pragma unroll
+        for (int c = 0; c < G / 8; ++c) kr[u][c] = make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int c = 0; c < G / 8; ++c) {
+        const uint32_t wv[4] = {kr[u][c].x, kr[u][c].y, kr[u][c].z, kr[u][c].w};
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          acc[8 * c + 2 * x] = fmaf(dz[u], __uint_as_float(wv[x] << 16), acc[8 * c + 2 * x]);
+          acc[8 * c + 2 * x + 1] = fmaf(dz[u], __uint_as_float(wv[x] & 0xFFFF0000u), acc[8 * c + 2 * x + 1]);
+        }
+      }
   }
   const float* dqa = a.dq_acc + (bh * a.T + i) * D + cg * G;
   bf16_t* dq = reinterpret_cast<bf16_t*>(a.dq) + (bh * a.T + i) * D + cg * G;
@@ -757,14 +803,12 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t st) {
     if (a.D == 128) bwd_dq_kernel<128><<<ntile * a.BH, 256, 0, st>>>(a);
     else bwd_dq_kernel<64><<<ntile * a.BH, 256, 0, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    bwd_entmax_kernel<<<dim3(ntile, a.BH), 128, 0, st>>>(a);
+    if (a.D == 128) bwd_coarse_kernel<128><<<dim3(ntile * 4, a.BH), 256, 0, st>>>(a);
+    else bwd_coarse_kernel<64><<<dim3(ntile * 4, a.BH), 256, 0, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int ngrp = (nb + 1) / 2;
     if (a.D == 128) bwd_dkdv_kernel<128><<<ngrp * a.BH, 512, 0, st>>>(a);
     else bwd_dkdv_kernel<64><<<ngrp * a.BH, 512, 0, st>>>(a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (a.D == 128) bwd_dq_final_kernel<128><<<dim3(ntile * 4, a.BH), 256, 0, st>>>(a);
-    else bwd_dq_final_kernel<64><<<dim3(ntile * 4, a.BH), 256, 0, st>>>(a);
     return hipGetLastError();
   }
   const size_t n = rows * a.D;

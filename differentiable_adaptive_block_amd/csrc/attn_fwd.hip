@@ -2,6 +2,7 @@
 // added to every logit of block b ("Core Mechanism" of the alanhou.org page:
 // fine logits plus log of the coarse scores, softmax, weighted sum of V).
 #include "kernels.h"
+#include "tiles.h"
 
 #define LOG2E_F 1.4426950408889634f
 #define LN2_F 0.6931471805599453f
@@ -32,30 +33,6 @@
 // The per-(row, block) prior is recomputed from the Stage-1 score
 // arithmetic (coarse_acc_chunk) for 32 listed blocks at a time and kept in
 // registers.
-template <int D> struct TileSwz;
-template <> struct TileSwz<128> {  // 16 chunks of 16 B per row
-  static __device__ __forceinline__ int k(int r) { return r & 15; }
-  static __device__ __forceinline__ int v(int r) { return (r & 3) << 2; }
-};
-template <> struct TileSwz<64> {   // 8 chunks of 16 B per row
-  static __device__ __forceinline__ int k(int r) { return (r >> 1) & 7; }
-  static __device__ __forceinline__ int v(int r) { return ((r >> 1) & 1) << 2; }
-};
-
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-
-// 16 bytes per lane from global memory into LDS: lane L of the wave writes
-// bytes 16 L .. 16 L + 15 after the wave-uniform address lds.
-__device__ __forceinline__ void copy16_to_lds(const bf16_t* g, bf16_t* lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
-}
-
-// 4 bf16 from 4 consecutive rows (LDS transposing read, see the caller).
-__device__ __forceinline__ bf16x4 ds_read_tr4(const bf16_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (lds_bf16x4*)(__attribute__((address_space(3))) bf16_t*)(p));
-}
-
 template <int D>
 __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
   constexpr int CH = D / 8;          // 16-byte chunks per row
@@ -135,40 +112,11 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
     }
   };
 
-  // log2 priors of this wave's 32 rows for listed blocks e0 .. e0+31: lane
-  // (j, h) holds slots 8(r/4) + 4h + r%4 of row j in pacc[r]
   f32x16 pacc;
   auto prior_chunk = [&](int e0) {
-    if (!active) return;
-    const int ent = e0 + j;
-    pacc = coarse_acc_chunk<D>(KB, ent < cnt ? list[ent] : 0, qb);
-    // all summary loads in flight before the first MFMA
-    __builtin_amdgcn_sched_group_barrier(0x020, KS, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int en = e0 + acc_row32(r, l);
-      float p2 = -INFINITY;
-      if (en < cnt) {
-        const int bb = list[en];
-        if (!a.causal || bb < wblk) p2 = ca.logp(ca.u_of(pacc[r]), tau_i, ln_i) * LOG2E_F;
-      }
-      pacc[r] = p2;
-    }
+    if (active) pacc = prior_chunk32<D>(KB, list, cnt, e0, qb, ca, tau_i, ln_i, a.causal, wblk);
   };
-  // prior of entry e for this lane's row: slot e%32 sits in register
-  // 4(slot/8) + slot%4 of the half (slot/4)%2
-  auto prior_of = [&](int e) -> float {
-    const int slot = e & 31;
-    const int rr = 4 * (slot >> 3) + (slot & 3);
-    float v = pacc[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) v = (r == rr) ? pacc[r] : v;
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    // sw[0]: lanes 0-31 keep their value, lanes 32-63 get lanes 0-31's;
-    // sw[1]: lanes 0-31 get lanes 32-63's, lanes 32-63 keep theirs
-    return __uint_as_float(((slot >> 2) & 1) ? sw[1] : sw[0]);
-  };
+  auto prior_of = [&](int e) -> float { return prior_pick(pacc, e); };
 
   auto block_step = [&](int e, const bf16_t* kt, const bf16_t* vt) {
     const int b = list[e];

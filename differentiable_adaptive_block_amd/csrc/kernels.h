@@ -99,6 +99,48 @@ __device__ __forceinline__ f32x16 coarse_acc_chunk(const bf16_t* kb, int brow, c
   return acc;
 }
 
+// log2 priors of one wave's 32 query rows (lane column j) for the listed
+// blocks e0 .. e0+31 of a tile list: lane (j, h) gets slots 8(r/4) + 4h +
+// r%4 of row j in register r.  -inf for slots past the list, blocks the
+// row did not select, and (causal) the row's own block and later ones.
+// The summary loads are issued together, ahead of the MFMAs.
+template <int D>
+__device__ __forceinline__ f32x16 prior_chunk32(const bf16_t* KB, const int* list, int cnt, int e0,
+                                                const bf16x8 (&qb)[D / 16], const CoarseArith& ca, float tau_i,
+                                                float ln_i, int causal, int wblk) {
+  const int l = lane_id(), j = l & 31;
+  const int ent = e0 + j;
+  f32x16 pacc = coarse_acc_chunk<D>(KB, ent < cnt ? list[ent] : 0, qb);
+  __builtin_amdgcn_sched_group_barrier(0x020, D / 16, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int en = e0 + acc_row32(r, l);
+    float p2 = -INFINITY;
+    if (en < cnt) {
+      const int bb = list[en];
+      if (!causal || bb < wblk) p2 = ca.logp(ca.u_of(pacc[r]), tau_i, ln_i) * 1.4426950408889634f;
+    }
+    pacc[r] = p2;
+  }
+  return pacc;
+}
+
+// The prior of list entry e for this lane's row from prior_chunk32's
+// registers: slot e%32 sits in register 4(slot/8) + slot%4 of the half
+// (slot/4)%2; the other half's value comes across with permlane32_swap.
+__device__ __forceinline__ float prior_pick(const f32x16& pacc, int e) {
+  const int slot = e & 31;
+  const int rr = 4 * (slot >> 3) + (slot & 3);
+  float v = pacc[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) v = (r == rr) ? pacc[r] : v;
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  // sw[0]: lanes 0-31 keep their value, lanes 32-63 get lanes 0-31's;
+  // sw[1]: lanes 0-31 get lanes 32-63's, lanes 32-63 keep theirs
+  return __uint_as_float(((slot >> 2) & 1) ? sw[1] : sw[0]);
+}
+
 // The generic-path score: sequential fp32 dot product of a query held in
 // LDS (as float) with one summary row.
 template <typename T>

@@ -1,0 +1,82 @@
+// LDS tiles of 64 rows x D bf16 filled by global-to-LDS copies (gfx950).
+//
+// A tile keeps the source's row-major layout with the 16-byte chunks of
+// each row permuted: chunk c of row r sits at slot c ^ swz(r).  The copy
+// instruction writes 16 bytes per lane at consecutive LDS addresses, so a
+// lane that fills slot s of row r reads source chunk s ^ swz(r).  Three
+// permutations, each free of LDS bank conflicts (64 banks of 4 bytes) for
+// the reads it serves:
+//   k   16-byte operand reads of rows j = 0..15 at one chunk (MFMA operand
+//       with the row as the M or N index);
+//   v   transposing reads (ds_read_b64_tr_b16) of 4 consecutive rows at 4
+//       consecutive chunks, two half-chunks each;
+//   kv  both of the above, for a tile read both ways.
+#pragma once
+
+#include "common.h"
+
+template <int D> struct TileSwz;
+template <> struct TileSwz<128> {  // 16 chunks of 16 B per row
+  static __device__ __forceinline__ int k(int r) { return r & 15; }
+  static __device__ __forceinline__ int v(int r) { return (r & 3) << 2; }
+  static __device__ __forceinline__ int kv(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+};
+template <> struct TileSwz<64> {   // 8 chunks of 16 B per row
+  static __device__ __forceinline__ int k(int r) { return (r >> 1) & 7; }
+  static __device__ __forceinline__ int v(int r) { return ((r >> 1) & 1) << 2; }
+  static __device__ __forceinline__ int kv(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+};
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// 16 bytes per lane from global memory into LDS: lane L of the wave writes
+// bytes 16 L .. 16 L + 15 after the wave-uniform address lds.
+__device__ __forceinline__ void copy16_to_lds(const bf16_t* g, bf16_t* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+
+// Transposing read: lane 4a+b of each 16-lane group receives element b of
+// the 8-byte pieces addressed by lanes a, a+4, a+8 and a+12 of the group.
+__device__ __forceinline__ bf16x4 ds_read_tr4(const bf16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4*)(__attribute__((address_space(3))) bf16_t*)(p));
+}
+
+// One wave copies its share of a 64-row tile: rows RPI*(NI*w + q) +
+// lane/CH, q < NI, where RPI rows fill one 1 KB instruction and the 4 waves
+// of a workgroup split the 64 rows.  SWZ is one of TileSwz<D>::{k, v, kv}.
+template <int D, int (*SWZ)(int)>
+__device__ __forceinline__ void copy_tile(const bf16_t* src, bf16_t* dst, int w, int l) {
+  constexpr int CH = D / 8;
+  constexpr int RPI = 1024 / (2 * D);
+  constexpr int NI = 64 / RPI / 4;
+#pragma unroll
+  for (int q = 0; q < NI; ++q) {
+    const int r0 = RPI * (NI * w + q);
+    const int row = r0 + l / CH, slot = l % CH;
+    copy16_to_lds(src + (size_t)row * D + 8 * (slot ^ SWZ(row)), dst + r0 * D);
+  }
+}
+
+// A operand of S^T = K Q^T style products: 8 bf16 of row `row`, elements
+// 16 s + 8 h .. +7 (k-step s, lane half h), from a tile with swizzle SWZ.
+template <int D, int (*SWZ)(int)>
+__device__ __forceinline__ bf16x8 tile_row8(const bf16_t* t, int row, int s, int h) {
+  return load8(t + row * D + 8 * ((2 * s + h) ^ SWZ(row)));
+}
+
+// A operand of O^T += X^T P^T style products (X = V or K, rows = keys):
+// 8 keys 16 s + 4 h + {0..3} and 16 s + 8 + 4 h + {0..3} of column
+// 32 dt + lane % 32, built from two transposing reads.  Lane t of each
+// 16-lane group addresses row key0 + t/4, columns 32 dt + 16 (group % 2)
+// + 4 (t % 4) .. +3.
+template <int D, int (*SWZ)(int)>
+__device__ __forceinline__ bf16x8 tile_col8(const bf16_t* t, int s, int dt, int l) {
+  const int tg = l & 15, h = l >> 5;
+  const int col = 32 * dt + 16 * ((l >> 4) & 1) + 4 * (tg & 3);
+  const int c = col >> 3, half = (col >> 2) & 1;
+  const int r1 = 16 * s + 4 * h + (tg >> 2), r2 = r1 + 8;
+  const bf16x4 lo = ds_read_tr4(t + r1 * D + 8 * (c ^ SWZ(r1)) + 4 * half);
+  const bf16x4 hi = ds_read_tr4(t + r2 * D + 8 * (c ^ SWZ(r2)) + 4 * half);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
