@@ -49,17 +49,22 @@ __device__ __forceinline__ size_t gidx(size_t bh, int ntile, int tile, int nb, i
   return (((bh * ntile + tile) * (size_t)nb + e) * DASH_QTILE) + row_in_tile;
 }
 
+// Query-tile-major like the forward: workgroup = 4 waves = 128 query rows,
+// wave w rows 32w..32w+31; the tile's listed blocks are walked in order with
+// the K and V tiles copied straight into LDS, double-buffered, one barrier
+// per block.  Per wave, block and 32-key half:
+//   S^T = K Q^T, dP^T = V dO^T       D/16 MFMA each (row reads of K, V)
+//   dS^T = P^T (dP^T - delta),  G += sum over the keys of dS
+//   dQ^T += K^T dS^T                 (D/32) x 2 MFMA (transposing reads of K)
+// The K tile uses the permutation that serves both read kinds.
 template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
-  constexpr int KP = D + 8;
-  constexpr int VP = 64 + 4;
-  constexpr int CH = D / 8;
-  constexpr int NVL = 64 * CH / 256;   // V uint4 per thread
-  constexpr int NKP = 32 * CH / 256;   // K row pairs per thread
-  __shared__ __attribute__((aligned(16))) bf16_t ks[64 * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t vs[64 * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t kt[D * VP];
-  __shared__ float pri[4][32 * 32];
+  constexpr int KS = D / 16;
+  constexpr int NDT = D / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t kt0[64 * D];
+  __shared__ __attribute__((aligned(16))) bf16_t kt1[64 * D];
+  __shared__ __attribute__((aligned(16))) bf16_t vt0[64 * D];
+  __shared__ __attribute__((aligned(16))) bf16_t vt1[64 * D];
   __shared__ int lst[DASH_MAX_NB];
 
   const int nb = a.T / DASH_BLOCK;
@@ -84,15 +89,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int cnt = a.tile_cnt[bh * ntile + tile];
   const CoarseArith ca = a.ca;
   const float sl2 = a.fine_scale * LOG2E_F;
-  for (int x = threadIdx.x; x < cnt; x += 256) lst[x] = glist[x];
+  // the list in LDS: no vector-memory load inside the loop, which would
+  // wait for the tile copies in flight
+  for (int x = tid; x < cnt; x += 256) lst[x] = glist[x];
   __syncthreads();
   const int* list = lst;
 
-  bf16x8 qb[D / 16], dob[D / 16];
+  bf16x8 qb[KS], dob[KS];
   float tau_i = 0.f, ln_i = 0.f, lse2 = 0.f, dlt = 0.f;
   if (active) {
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
+    for (int s = 0; s < KS; ++s) {
       qb[s] = load8(Q + (size_t)i * D + 16 * s + 8 * h);
       dob[s] = load8(dO + (size_t)i * D + 16 * s + 8 * h);
     }
@@ -101,51 +108,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     lse2 = a.lse[bh * a.T + i] * LOG2E_F;
     dlt = a.delta[bh * a.T + i];
   }
-  f32x16 dqa[D / 32];
+  f32x16 dqa[NDT];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
+  for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqa[dt][r] = 0.f;
 
-  uint4 kr[2 * NKP], vr[NVL];
-  auto gload = [&](int b) {
-    const bf16_t* kb0 = K + (size_t)b * DASH_BLOCK * D;
-    const bf16_t* vb0 = V + (size_t)b * DASH_BLOCK * D;
-#pragma unroll
-    for (int x = 0; x < NKP; ++x) {
-      const int idx = tid + 256 * x;
-      const int pr = idx / CH, ch = idx % CH;
-      kr[2 * x] = *reinterpret_cast<const uint4*>(kb0 + (size_t)(2 * pr) * D + ch * 8);
-      kr[2 * x + 1] = *reinterpret_cast<const uint4*>(kb0 + (size_t)(2 * pr + 1) * D + ch * 8);
-    }
-#pragma unroll
-    for (int x = 0; x < NVL; ++x) {
-      const int idx = tid + 256 * x;
-      vr[x] = *reinterpret_cast<const uint4*>(vb0 + (size_t)(idx / CH) * D + (idx % CH) * 8);
-    }
+  auto copy_block = [&](int b, bf16_t* kd, bf16_t* vd) {
+    copy_tile<D, TileSwz<D>::kv>(K + (size_t)b * DASH_BLOCK * D, kd, w, l);
+    copy_tile<D, TileSwz<D>::k>(V + (size_t)b * DASH_BLOCK * D, vd, w, l);
   };
-  auto sstore = [&]() {
-#pragma unroll
-    for (int x = 0; x < NKP; ++x) {
-      const int idx = tid + 256 * x;
-      const int pr = idx / CH, ch = idx % CH;
-      *reinterpret_cast<uint4*>(&ks[(2 * pr) * KP + ch * 8]) = kr[2 * x];
-      *reinterpret_cast<uint4*>(&ks[(2 * pr + 1) * KP + ch * 8]) = kr[2 * x + 1];
-      const uint32_t* k0 = reinterpret_cast<const uint32_t*>(&kr[2 * x]);
-      const uint32_t* k1 = reinterpret_cast<const uint32_t*>(&kr[2 * x + 1]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t lo = (e & 1) ? (k0[e >> 1] >> 16) : (k0[e >> 1] & 0xFFFFu);
-        const uint32_t hi = (e & 1) ? (k1[e >> 1] >> 16) : (k1[e >> 1] & 0xFFFFu);
-        *reinterpret_cast<uint32_t*>(&kt[(ch * 8 + e) * VP + 2 * pr]) = lo | (hi << 16);
-      }
-    }
-#pragma unroll
-    for (int x = 0; x < NVL; ++x) {
-      const int idx = tid + 256 * x;
-      *reinterpret_cast<uint4*>(&vs[(idx / CH) * KP + (idx % CH) * 8]) = vr[x];
-    }
-  };
+  f32x16 pacc;
   auto put_g = [&](int e, float g, float p2) {
     if (h == 0) {
       const size_t gi = gidx(bh, ntile, tile, nb, e, w * 32 + j);
@@ -154,86 +127,77 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     }
   };
 
-  if (cnt > 0) gload(list[0]);
-  for (int e = 0; e < cnt; ++e) {
+  auto block_step = [&](int e, const bf16_t* kt, const bf16_t* vt) {
     const int b = list[e];
-    __syncthreads();
-    sstore();
-    if ((e & 31) == 0 && active) {
-      const int ent = e + j;
-      f32x16 acc = coarse_acc_chunk<D>(KB, ent < cnt ? list[ent] : 0, qb);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int slot = acc_row32(r, l);
-        const int en = e + slot;
-        float p2 = -INFINITY;
-        if (en < cnt) {
-          const int bb = list[en];
-          if (!a.causal || bb < wblk) p2 = ca.logp(ca.u_of(acc[r]), tau_i, ln_i) * LOG2E_F;
-        }
-        pri[w][slot * 32 + j] = p2;
-      }
-    }
-    __syncthreads();
-    if (e + 1 < cnt) gload(list[e + 1]);
-    if (!active) continue;
     if (a.causal && b > wblk) {
       put_g(e, 0.f, -INFINITY);
-      continue;
+      return;
     }
     const bool diag = a.causal && b == wblk;
-    const float pr = diag ? 0.f : pri[w][(e & 31) * 32 + j];
+    const float pr = diag ? 0.f : prior_pick(pacc, e);
     if (!diag && __ballot(pr != -INFINITY) == 0ull) {
       put_g(e, 0.f, -INFINITY);
-      continue;
+      return;
     }
+    // operand addresses recomputed per block (see bwd_dkdv_kernel)
+    int lx = l;
+    asm volatile("" : "+v"(lx));
+    const int jx = lx & 31, hx = lx >> 5;
+    const float off = (pr == -INFINITY) ? -INFINITY : pr - lse2;
     float gsum = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      f32x16 s, dp;
+      f32x16 sc, dp;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
+      for (int r = 0; r < 16; ++r) { sc[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
-      for (int st = 0; st < D / 16; ++st) {
-        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&ks[(32 * t + j) * KP + 16 * st + 8 * h]);
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&vs[(32 * t + j) * KP + 16 * st + 8 * h]);
-        s = mfma32(ak, qb[st], s);
-        dp = mfma32(av, dob[st], dp);
+      for (int s = 0; s < KS; ++s) {
+        sc = mfma32(tile_row8<D, TileSwz<D>::kv>(kt, 32 * t + jx, s, hx), qb[s], sc);
+        dp = mfma32(tile_row8<D, TileSwz<D>::k>(vt, 32 * t + jx, s, hx), dob[s], dp);
       }
-      float ds[16];
-      const float off = pr - lse2;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float sv = s[r];
-        if (diag && b * DASH_BLOCK + 32 * t + acc_row32(r, l) > i) sv = -INFINITY;
-        const float p = __builtin_amdgcn_exp2f(fmaf(sv, sl2, off));
-        ds[r] = p * (dp[r] - dlt);
-        gsum += ds[r];
-      }
-      // dQ^T += K^T dS^T over this half's 32 keys (2 k-steps of 16)
+      // dS^T of this half, as the B operand of the dQ product (k-steps of
+      // 16 keys: registers 8 s2 .. 8 s2 + 7)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        bf16x8 pb;
+        bf16x8 db;
 #pragma unroll
-        for (int e8 = 0; e8 < 8; ++e8) pb[e8] = (__bf16)ds[8 * s2 + e8];
-        const int key0 = 32 * t + 16 * s2 + 4 * h;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const bf16_t* krow = &kt[(32 * dt + j) * VP + key0];
-          const uint2 lo = *reinterpret_cast<const uint2*>(krow);
-          const uint2 hi = *reinterpret_cast<const uint2*>(krow + 8);
-          const uint4 pk = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          dqa[dt] = mfma32(__builtin_bit_cast(bf16x8, pk), pb, dqa[dt]);
+        for (int e8 = 0; e8 < 8; ++e8) {
+          const int r = 8 * s2 + e8;
+          float sv = sc[r];
+          if (diag && b * DASH_BLOCK + 32 * t + acc_row32(r, l) > i) sv = -INFINITY;
+          const float p = __builtin_amdgcn_exp2f(fmaf(sv, sl2, off));
+          const float dsv = p * (dp[r] - dlt);
+          gsum += dsv;
+          db[e8] = (__bf16)dsv;
         }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          dqa[dt] = mfma32(tile_col8<D, TileSwz<D>::kv>(kt, 2 * t + s2, dt, lx), db, dqa[dt]);
       }
     }
-    gsum += __shfl_xor(gsum, 32, 64);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(gsum), __float_as_uint(gsum), false, false);
+    gsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     put_g(e, diag ? 0.f : gsum, pr);
+  };
+
+  if (cnt > 0) {
+    copy_block(list[0], kt0, vt0);
+    for (int e = 0; e < cnt; e += 2) {
+      if ((e & 31) == 0 && active)
+        pacc = prior_chunk32<D>(KB, list, cnt, e, qb, ca, tau_i, ln_i, a.causal, wblk);
+      __syncthreads();  // block e in buffers 0; everyone is done with buffers 1
+      if (e + 1 < cnt) copy_block(list[e + 1], kt1, vt1);
+      if (active) block_step(e, kt0, vt0);
+      if (e + 1 >= cnt) break;
+      __syncthreads();  // block e+1 in buffers 1; everyone is done with buffers 0
+      if (e + 2 < cnt) copy_block(list[e + 2], kt0, vt0);
+      if (active) block_step(e + 1, kt1, vt1);
+    }
   }
   if (active) {
     float* dq = a.dq_acc + (bh * a.T + i) * D;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int d = 32 * dt + 8 * r4 + 4 * h;
