@@ -17,11 +17,19 @@ The JSON line also carries:
 * ``selection``: measured sparsity; ``stages_ms``: per-stage times;
 * ``decode`` / ``training`` / ``prefill_64k``: the other workloads, each
   timed the same way (when enabled).
+
+``roofline.traffic`` is the Stage-2 kernel's HBM traffic per launch from the
+committed rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, calibrated
+on a plain 1 GiB copy); it is reported only while the kernel sources still
+hash to the digest recorded there, else null.  ``--traffic-probe`` runs the
+launches that summary is taken from (see the profile file for the
+commands).
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -35,6 +43,34 @@ if ROOT not in sys.path:
 METRIC = "prefill tokens/s @16K/64K, decode µs/step @96K; % of MFMA / HBM roofline"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill16k_stage2_traffic.md")
+STAGE2_SOURCES = ["attn_fwd.hip", "tiles.h", "kernels.h", "common.h"]
+
+
+def stage2_digest():
+    """sha256 (first 16 hex digits) of the Stage-2 kernel sources."""
+    h = hashlib.sha256()
+    for f in STAGE2_SOURCES:
+        with open(os.path.join(ROOT, "differentiable_adaptive_block_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per Stage-2 launch from the committed counter summary, or
+    None when it is missing or was taken on other kernel sources."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if ":" in line and line.split(":", 1)[0].strip() in ("source_digest", "traffic_bytes_per_launch"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("source_digest") != stage2_digest() or "traffic_bytes_per_launch" not in vals:
+        return None
+    return float(vals["traffic_bytes_per_launch"])
 
 
 def log(msg):
@@ -279,6 +315,42 @@ def bench_decode(name, steps, warmup, device):
     return res
 
 
+def traffic_probe(device):
+    """The launches the counter summary is taken from: a plain copy of 1 GiB
+    (calibration: it reads and writes exactly 2^30 bytes), one 16K prefill
+    forward (Stage 0/1 selection, then Stage 2) and one 96K decode."""
+    from differentiable_adaptive_block_amd import api, inputs
+
+    src = torch.empty(1 << 29, dtype=torch.bfloat16, device=device).normal_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    log("copy 1 GiB")
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+    wl = inputs.CONFIGS["c2"]
+    sh = wl.shape
+    w = inputs.make_prefill(sh["B"], sh["H"], sh["T"], sh["D"], wl.dtype, wl.causal, wl.planted, wl.seed,
+                            device=device, with_dout=False)
+    torch.cuda.synchronize()
+    log("prefill forward c2")
+    api.forward(w["q"], w["k"], w["v"], alpha=wl.alpha, causal=wl.causal, coarse_scale=wl.coarse_scale,
+                want_mask=False)
+    torch.cuda.synchronize()
+    del w
+    torch.cuda.empty_cache()
+    wl = inputs.CONFIGS["c4cal"]
+    sh = wl.shape
+    w = inputs.make_decode(sh["S"], sh["H"], sh["N"], sh["D"], wl.dtype, wl.planted, wl.seed, device=device)
+    kbar = api.pool(w["k"].view(1, sh["S"] * sh["H"], sh["N"], sh["D"])).view(sh["S"], sh["H"], -1, sh["D"])
+    torch.cuda.synchronize()
+    log("decode c4cal")
+    api.decode(w["q"], w["k"], w["v"], kbar, alpha=wl.alpha, coarse_scale=wl.coarse_scale)
+    torch.cuda.synchronize()
+    print(json.dumps({"stage2_source_digest": stage2_digest()}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -287,9 +359,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="oracle rows per CPU worker")
     ap.add_argument("--cpu-workers", type=int, default=16)
-    ap.add_argument("--extra", action="store_true", help="also time the 64K prefill")
+    ap.add_argument("--no-64k", action="store_true", help="skip the 64K prefill")
     ap.add_argument("--no-decode", action="store_true", help="skip the 96K decode workloads")
     ap.add_argument("--no-training", action="store_true", help="skip the 16K training step")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only run the launches the HBM-traffic counter summary is taken from")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -305,11 +379,14 @@ def main():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(2)
     dev = "cuda"
+    if args.traffic_probe:
+        traffic_probe(dev)
+        return
     out = {}
     res, shape = bench_prefill("c2", args.steps, args.warmup, dev)
     log(f"c2: {res}")
     extra = {}
-    if args.extra:
+    if not args.no_64k:
         r3, _ = bench_prefill("c3", max(2, args.steps // 3), 1, dev)
         log(f"c3: {r3}")
         extra["prefill_64k"] = r3
@@ -367,7 +444,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": res["stage2_tflops"] / PEAK_BF16_TFLOPS,
-            "traffic": None,
+            "traffic": recorded_traffic(),
             "work": "useful FLOPs = 4*D*(64*sum selected blocks + causal diagonal pairs) per launch",
         },
         "cpu_baseline": cpu,
