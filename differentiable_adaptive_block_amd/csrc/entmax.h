@@ -125,6 +125,42 @@ __device__ __forceinline__ EntmaxOut entmax_newton(const float (&u)[NPL], int nv
 #pragma unroll
   for (int k = 0; k < NPL; ++k) v[k] = u[k] - umax;
   float t = -1.f;  // f(-1) >= 1 from the largest term alone
+  if constexpr (PW == 2) {
+    // alpha = 1.5: sum_{v > t} (v - t)^2 = 1 is a quadratic in t once the
+    // support is fixed.  Its smaller root t_c on the support {v > -1} lies at
+    // or right of the true root (elements of that set that fall below the
+    // root still add to the left-hand side); one Newton step from the right
+    // of a convex decreasing function lands at or left of the root, where the
+    // iteration below starts.  A start that rounding puts anywhere else
+    // falls back to -1.
+    float n = 0.f, sa = 0.f, sb = 0.f;
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) {
+      if (k * G < nvalid) {
+        const bool in = v[k] > -1.f;
+        n += in ? 1.f : 0.f;
+        sa += in ? v[k] : 0.f;
+        sb += in ? v[k] * v[k] : 0.f;
+      }
+    }
+    n = grp_sum<G>(n);
+    sa = grp_sum<G>(sa);
+    sb = grp_sum<G>(sb);
+    const float tc = (sa - __builtin_sqrtf(fmaxf(sa * sa - n * (sb - 1.f), 0.f))) / n;
+    float f = 0.f, fp = 0.f;
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) {
+      if (k * G < nvalid) {
+        const float x = fmaxf(v[k] - tc, 0.f);
+        f += x * x;
+        fp += x;
+      }
+    }
+    f = grp_sum<G>(f);
+    fp = grp_sum<G>(fp);
+    const float t1 = tc + (f - 1.f) / (2.f * fp);
+    if (t1 > -1.f && t1 <= 0.f) t = t1;  // false for NaN too
+  }
   bool done = false;
   // groups that have converged keep their t while the others iterate (all
   // lanes stay active for the DPP reductions)

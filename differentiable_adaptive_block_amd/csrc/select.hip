@@ -124,17 +124,19 @@ __device__ __forceinline__ void write_rows16(const SelectArgs& a, size_t row_g, 
 
 // ---------------------------------------------------------------------------- Stage 1, bf16 MFMA
 
-// One workgroup (4 waves) per 32 query rows.  The block scores of the 32
+// One workgroup (4 or 8 waves) per 32 query rows.  The block scores of the 32
 // rows (all inside one 64-block, so they share their causal candidates) are
 // computed 32 blocks at a time on the 32x32x16 bf16 MFMA as
 //     Z^T[block][query] = kbar[block] . q[query]
 // (operand A = summary rows, B = the queries, fp32 accumulation) and kept in
-// LDS as u = (alpha-1) * coarse_scale * acc; then each wave solves tau for 8
-// rows, four at a time (16 lanes per row, see entmax_solve).
+// LDS as u = (alpha-1) * coarse_scale * acc; then each wave solves tau for
+// its rows (8 with 4 waves, 4 with 8), four at a time (16 lanes per row, see
+// entmax_solve).
 // coarse_acc_chunk() is the one definition of the score arithmetic; the
 // Stage-2 and backward kernels call it too, so they see the same bits.
-template <int D, int NPL>
-__global__ __launch_bounds__(256) void select_mfma_kernel(SelectArgs a) {
+template <int D, int NPL, int NW>
+__global__ __launch_bounds__(64 * NW) void select_mfma_kernel(SelectArgs a) {
+  constexpr int RPW = 32 / NW;   // rows per wave, solved 4 at a time
   extern __shared__ float zs[];  // [32][nb + 1] followed by nbw union words
   const int nb = a.T / DASH_BLOCK;
   const int nbp = nb + 1;
@@ -145,7 +147,7 @@ __global__ __launch_bounds__(256) void select_mfma_kernel(SelectArgs a) {
   const int w = threadIdx.x >> 6, l = lane_id(), j = l & 31, h = l >> 5;
   const int nc = a.causal ? row0 / DASH_BLOCK : nb;
   const CoarseArith ca = a.ca;
-  for (int x = threadIdx.x; x < nbw; x += 256) uni[x] = 0u;
+  for (int x = threadIdx.x; x < nbw; x += 64 * NW) uni[x] = 0u;
 
   const bf16_t* qh = reinterpret_cast<const bf16_t*>(a.q) + bh * a.T * D;
   const bf16_t* kb = reinterpret_cast<const bf16_t*>(a.kbar) + bh * nb * D;
@@ -153,7 +155,7 @@ __global__ __launch_bounds__(256) void select_mfma_kernel(SelectArgs a) {
     bf16x8 qb[D / 16];
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) qb[s] = load8(qh + (size_t)(row0 + j) * D + 16 * s + 8 * h);
-    for (int c = w; c * 32 < nc; c += 4) {
+    for (int c = w; c * 32 < nc; c += NW) {
       const int brow = c * 32 + j;
       f32x16 acc = coarse_acc_chunk<D>(kb, brow < nc ? brow : 0, qb);
 #pragma unroll
@@ -165,8 +167,8 @@ __global__ __launch_bounds__(256) void select_mfma_kernel(SelectArgs a) {
   }
   __syncthreads();
   const int g = l & 15;
-  for (int pass = 0; pass < 2; ++pass) {
-    const int row = 8 * w + 4 * pass + (l >> 4);
+  for (int pass = 0; pass < RPW / 4; ++pass) {
+    const int row = RPW * w + 4 * pass + (l >> 4);
     const size_t row_g = bh * a.T + row0 + row;
     if (nc == 0) {
       if (g == 0) {
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(256) void select_mfma_kernel(SelectArgs a) {
   __syncthreads();
   const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
   uint32_t* tb = a.tile_bits + (bh * ntile + row0 / DASH_QTILE) * nbw;
-  for (int x = threadIdx.x; x < nbw; x += 256)
+  for (int x = threadIdx.x; x < nbw; x += 64 * NW)
     if (uni[x]) atomicOr(&tb[x], uni[x]);
 }
 
@@ -290,10 +292,13 @@ template <int D, int NPL>
 static hipError_t launch_select_mfma_t(const SelectArgs& a, int BH, hipStream_t st) {
   const int nb = a.T / DASH_BLOCK;
   const size_t lds = (size_t)32 * (nb + 1) * sizeof(float) + ((nb + 31) / 32) * sizeof(uint32_t);
-  auto kfn = select_mfma_kernel<D, NPL>;
+  // long sequences: the score tile fills most of the LDS, so one workgroup
+  // per CU; give it 8 waves (4 rows each) instead of 4
+  constexpr int NW = NPL >= 32 ? 8 : 4;
+  auto kfn = select_mfma_kernel<D, NPL, NW>;
   hipError_t e = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  kfn<<<dim3(a.T / 32, BH), 256, lds, st>>>(a);
+  kfn<<<dim3(a.T / 32, BH), 64 * NW, lds, st>>>(a);
   return hipGetLastError();
 }
 
