@@ -121,9 +121,8 @@ __device__ __forceinline__ void entmax_terms(float x, float m, float& fx, float&
 // alpha > 1: Newton from the left on t = tau - max u (see the header).
 template <int NPL, int G, int PW>
 __device__ __forceinline__ EntmaxOut entmax_newton(const float (&u)[NPL], int nvalid, float umax, float m) {
-  float v[NPL];
-#pragma unroll
-  for (int k = 0; k < NPL; ++k) v[k] = u[k] - umax;
+  // v = u - umax, recomputed where used rather than held (NPL registers)
+  auto vof = [&](int k) { return u[k] - umax; };
   float t = -1.f;  // f(-1) >= 1 from the largest term alone
   if constexpr (PW == 2) {
     // alpha = 1.5: sum_{v > t} (v - t)^2 = 1 is a quadratic in t once the
@@ -137,10 +136,11 @@ __device__ __forceinline__ EntmaxOut entmax_newton(const float (&u)[NPL], int nv
 #pragma unroll
     for (int k = 0; k < NPL; ++k) {
       if (k * G < nvalid) {
-        const bool in = v[k] > -1.f;
+        const float vk = vof(k);
+        const bool in = vk > -1.f;
         n += in ? 1.f : 0.f;
-        sa += in ? v[k] : 0.f;
-        sb += in ? v[k] * v[k] : 0.f;
+        sa += in ? vk : 0.f;
+        sb += in ? vk * vk : 0.f;
       }
     }
     n = grp_sum<G>(n);
@@ -151,7 +151,7 @@ __device__ __forceinline__ EntmaxOut entmax_newton(const float (&u)[NPL], int nv
 #pragma unroll
     for (int k = 0; k < NPL; ++k) {
       if (k * G < nvalid) {
-        const float x = fmaxf(v[k] - tc, 0.f);
+        const float x = fmaxf(vof(k) - tc, 0.f);
         f += x * x;
         fp += x;
       }
@@ -170,7 +170,7 @@ __device__ __forceinline__ EntmaxOut entmax_newton(const float (&u)[NPL], int nv
     for (int k = 0; k < NPL; ++k) {
       if (k * G < nvalid) {
         float a, b;
-        entmax_terms<PW>(v[k] - t, m, a, b);
+        entmax_terms<PW>(vof(k) - t, m, a, b);
         f += a;
         fp += b;
       }

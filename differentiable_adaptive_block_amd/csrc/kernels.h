@@ -99,6 +99,23 @@ __device__ __forceinline__ f32x16 coarse_acc_chunk(const bf16_t* kb, int brow, c
   return acc;
 }
 
+// The same accumulation with the query operands read from LDS (q_lds: 32
+// query rows, row pitch `pitch` bf16) instead of registers: identical MFMA
+// sequence and operands, so identical bits.
+template <int D>
+__device__ __forceinline__ f32x16 coarse_acc_chunk_lds(const bf16_t* kb, int brow, const bf16_t* q_lds, int pitch) {
+  const int l = lane_id(), h = l >> 5, j = l & 31;
+  bf16x8 ka[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) ka[s] = load8(kb + (size_t)brow * D + 16 * s + 8 * h);
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) acc = mfma32(ka[s], load8(q_lds + j * pitch + 16 * s + 8 * h), acc);
+  return acc;
+}
+
 // log2 priors of one wave's 32 query rows (lane column j) for the listed
 // blocks e0 .. e0+31 of a tile list: lane (j, h) gets slots 8(r/4) + 4h +
 // r%4 of row j in register r.  -inf for slots past the list, blocks the

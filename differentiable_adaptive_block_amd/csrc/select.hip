@@ -196,6 +196,83 @@ __global__ __launch_bounds__(64 * NW) void select_mfma_kernel(SelectArgs a) {
     if (uni[x]) atomicOr(&tb[x], uni[x]);
 }
 
+// Long sequences (more than 256 blocks): the same computation with the score
+// tile staged 256 blocks at a time (32 rows x 257 floats of LDS), the query
+// operands read from LDS and each wave keeping its 4 rows' scores in
+// registers, so that two 8-wave workgroups fit on a CU.  Lane g of a row's 16 holds candidates g + 16 k,
+// chunk ch filling k = 16 ch .. 16 ch + 15.
+template <int D, int NPL>
+__global__ __launch_bounds__(512, 4) void select_chunked_kernel(SelectArgs a) {
+  constexpr int CB = 256;
+  constexpr int NCH = NPL / 16;
+  constexpr int QP = D + 8;
+  __shared__ float zs[32 * (CB + 1)];
+  __shared__ __attribute__((aligned(16))) bf16_t qs[32 * QP];  // the 32 query rows
+  __shared__ uint32_t uni[DASH_MAX_NB / 32];
+  const int nb = a.T / DASH_BLOCK;
+  const int nbw = (nb + 31) / 32;
+  const size_t bh = blockIdx.y;
+  const int row0 = blockIdx.x * 32;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = lane_id(), j = l & 31, g = l & 15;
+  const int nc = a.causal ? row0 / DASH_BLOCK : nb;
+  const CoarseArith ca = a.ca;
+  for (int x = tid; x < nbw; x += 512) uni[x] = 0u;
+  const int row = 4 * w + (l >> 4);
+  const size_t row_g = bh * a.T + row0 + row;
+
+  const bf16_t* qh = reinterpret_cast<const bf16_t*>(a.q) + bh * a.T * D;
+  const bf16_t* kb = reinterpret_cast<const bf16_t*>(a.kbar) + bh * nb * D;
+  float u[NPL];
+  if (nc > 0) {
+    for (int x = tid; x < 32 * (D / 8); x += 512) {
+      const int r = x / (D / 8), c8 = x % (D / 8);
+      *reinterpret_cast<uint4*>(&qs[r * QP + 8 * c8]) =
+          *reinterpret_cast<const uint4*>(qh + (size_t)(row0 + r) * D + 8 * c8);
+    }
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      const int c0 = ch * CB;
+      if (c0 < nc) {  // the same on every thread
+        __syncthreads();  // the previous chunk's reads are done
+        const int c = c0 / 32 + w;  // 8 sub-chunks of 32 blocks, one per wave
+        if (c * 32 < nc) {
+          const int brow = c * 32 + j;
+          const f32x16 acc = coarse_acc_chunk_lds<D>(kb, brow < nc ? brow : 0, qs, QP);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int b = c * 32 + acc_row32(r, l);
+            if (b < nc) zs[j * (CB + 1) + (b - c0)] = ca.u_of(acc[r]);
+          }
+        }
+        __syncthreads();
+      }
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) {
+        const int idx = c0 + g + 16 * kk;
+        u[16 * ch + kk] = idx < nc ? zs[row * (CB + 1) + g + 16 * kk] : -INFINITY;
+      }
+    }
+  }
+  if (nc == 0) {
+    if (g == 0) {
+      a.tau[row_g] = __uint_as_float(0x7fc00000u);
+      a.lognorm[row_g] = 0.f;
+      if (a.nsel) a.nsel[row_g] = 0;
+    }
+    if (a.mask)
+      for (int x = g; x < nbw; x += 16) a.mask[row_g * nbw + x] = 0u;
+  } else {
+    const EntmaxOut e = entmax_solve<NPL, 16>(u, nc, ca);
+    write_rows16<NPL>(a, row_g, u, nc, e, ca, uni);
+  }
+  __syncthreads();
+  const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
+  uint32_t* tb = a.tile_bits + (bh * ntile + row0 / DASH_QTILE) * nbw;
+  for (int x = tid; x < nbw; x += 512)
+    if (uni[x]) atomicOr(&tb[x], uni[x]);
+}
+
 // ---------------------------------------------------------------------------- Stage 1, generic
 
 // One wave per query row; scores by a sequential fp32 dot product
@@ -309,8 +386,13 @@ static hipError_t launch_select_mfma_d(const SelectArgs& a, int BH, hipStream_t 
   if (nb <= 64) return launch_select_mfma_t<D, 4>(a, BH, st);
   if (nb <= 128) return launch_select_mfma_t<D, 8>(a, BH, st);
   if (nb <= 256) return launch_select_mfma_t<D, 16>(a, BH, st);
-  if (nb <= 512) return launch_select_mfma_t<D, 32>(a, BH, st);
-  return launch_select_mfma_t<D, 64>(a, BH, st);
+  // longer: score tile staged in 256-block chunks
+  if (nb <= 512) {
+    select_chunked_kernel<D, 32><<<dim3(a.T / 32, BH), 512, 0, st>>>(a);
+    return hipGetLastError();
+  }
+  select_chunked_kernel<D, 64><<<dim3(a.T / 32, BH), 512, 0, st>>>(a);
+  return hipGetLastError();
 }
 
 template <typename T>
