@@ -95,32 +95,6 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // (the column is l % 32).
 __device__ __forceinline__ int acc_row32(int r, int l) { return 8 * (r >> 2) + 4 * (l >> 5) + (r & 3); }
 
-// ------------------------------------------------------------------ transposed LDS tiles
-//
-// Tiles stored transposed in LDS (row = feature d, 64 keys per row, row
-// pitch 68 bf16) are written as 4-byte pairs of consecutive keys by lanes
-// that hold one 16-byte chunk of a source row each, which would put 32
-// lanes on 4 banks.  XOR-ing the pair index with 2*((d >> 4) & 7) spreads
-// those stores over the banks and keeps the operand reads (8-byte runs of 4
-// keys) 8-byte aligned.
-__device__ __forceinline__ int tr_pair(int d, int pair) { return pair ^ (((d >> 4) & 7) << 1); }
-
-// The Stage-2 V^T tile (row pitch 72 bf16 = 36 dwords) is laid out for
-// 16-byte operand reads.  At k-step s a lane of half h needs keys
-// 16s+4h+{0..3} and 16s+8+4h+{0..3} (the order in which the S^T
-// accumulator holds them).  Key pair p is placed at pair position
-// vt_pos(p), which swaps pairs 2,3 with 4,5 in every group of 8 pairs (its
-// own inverse), so those 8 keys are the 4 positions 8s+4h..8s+4h+3; and
-// position P of row d is stored at pair slot P ^ 4*((d >> 4) & 7), which
-// keeps 4-pair runs contiguous.  With the 36-dword pitch both the
-// transposing 4-byte stores and the 16-byte reads hit 64 distinct banks.
-#define VT_PITCH 72
-__device__ __forceinline__ int vt_pos(int p) {
-  const int q = p & 6;
-  return (q == 2 || q == 4) ? (p ^ 6) : p;
-}
-__device__ __forceinline__ int vt_slot(int d, int P) { return P ^ (((d >> 4) & 7) << 2); }
-
 // ------------------------------------------------------------------ Stage-1 score arithmetic
 //
 // One definition of the coarse score used by every kernel, so that the
