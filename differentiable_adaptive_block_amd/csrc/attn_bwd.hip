@@ -185,10 +185,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     for (int e = 0; e < cnt; e += 2) {
       if ((e & 31) == 0 && active)
         pacc = prior_chunk32<D>(KB, list, cnt, e, qb, ca, tau_i, ln_i, a.causal, wblk);
+      tile_copies_done();
       __syncthreads();  // block e in buffers 0; everyone is done with buffers 1
       if (e + 1 < cnt) copy_block(list[e + 1], kt1, vt1);
       if (active) block_step(e, kt0, vt0);
       if (e + 1 >= cnt) break;
+      tile_copies_done();
       __syncthreads();  // block e+1 in buffers 1; everyone is done with buffers 0
       if (e + 2 < cnt) copy_block(list[e + 2], kt0, vt0);
       if (active) block_step(e + 1, kt1, vt1);
@@ -456,6 +458,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
     copy_item(0, qc0, oc0);
     store_rows(0);
     for (int n = 0; n < nit; n += 2) {
+      tile_copies_done();
       __syncthreads();  // item n in buffers 0; everyone is done with buffers 1
       if (n + 1 < nit) {
         load_rows(n + 1);  // before the copy: waiting on these loads does not wait on it
@@ -464,6 +467,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
       item_step(n, 0, qc0, oc0);
       if (n + 1 < nit) store_rows(1);
       if (n + 1 >= nit) break;
+      tile_copies_done();
       __syncthreads();  // item n+1 in buffers 1; everyone is done with buffers 0
       if (n + 2 < nit) {
         load_rows(n + 2);

@@ -36,8 +36,6 @@
 template <int D>
 __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
   constexpr int CH = D / 8;          // 16-byte chunks per row
-  constexpr int RPI = 1024 / (2 * D);  // rows per 1 KB copy instruction
-  constexpr int NI = 64 / RPI / 4;   // copy instructions per wave and tile
   constexpr int KS = D / 16;         // k-steps of the S product
   constexpr int NDT = D / 32;        // 32-row d tiles of O^T
   // one object per buffer, so that reads of one buffer are not ordered
@@ -97,19 +95,17 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
   float mrow = -INFINITY, lrow = 0.f;
 
-  // copy block b's K and V tiles into LDS: this wave fills rows
-  // RPI*(NI*w + q) + lane/CH, chunk lane%CH, from source chunk
-  // (lane%CH) ^ swz(row)
+  // copy block b's K and V tiles into LDS: this wave fills a quarter of
+  // the rows of each, chunk slot s of row r from source chunk s ^ swz(r)
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  TileCopy<D, TileSwz<D>::k> kcp;
+  TileCopy<D, TileSwz<D>::v> vcp;
+  kcp.init(wu, l);
+  vcp.init(wu, l);
   auto copy_block = [&](int b, bf16_t* kd, bf16_t* vd) {
-    const bf16_t* kg = K + (size_t)b * DASH_BLOCK * D;
-    const bf16_t* vg = V + (size_t)b * DASH_BLOCK * D;
-#pragma unroll
-    for (int q = 0; q < NI; ++q) {
-      const int r0 = RPI * (NI * w + q);
-      const int row = r0 + l / CH, slot = l % CH;
-      copy16_to_lds(kg + (size_t)row * D + 8 * (slot ^ TileSwz<D>::k(row)), kd + r0 * D);
-      copy16_to_lds(vg + (size_t)row * D + 8 * (slot ^ TileSwz<D>::v(row)), vd + r0 * D);
-    }
+    const size_t o = (size_t)__builtin_amdgcn_readfirstlane(b) * DASH_BLOCK * D;
+    kcp.copy(K + o, kd, wu);
+    vcp.copy(V + o, vd, wu);
   };
 
   f32x16 pacc;
@@ -188,18 +184,24 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
     // 32 dt + 16 (group % 2) + 4 (t % 4) .. +3.
     const int tg = l & 15, grp = l >> 4;
     const int dof = 16 * (grp & 1) + 4 * (tg & 3);  // column offset within a 32-wide d tile
+    // the row sum adds the weights as rounded for the MFMA, two per
+    // instruction (bf16 pair dot (1, 1))
     float ps0 = 0.f, ps1 = 0.f;
+    bf16x2 one2;
+    one2[0] = (__bf16)1.f;
+    one2[1] = (__bf16)1.f;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bf16x8 pb;
 #pragma unroll
       for (int e8 = 0; e8 < 8; ++e8) {
         const float sv = (s < 2) ? s0[8 * (s & 1) + e8] : s1[8 * (s & 1) + e8];
-        const float x = __builtin_amdgcn_exp2f(fmaf(sv, sl2, off));
-        if (e8 & 1) ps1 += x;
-        else ps0 += x;
-        pb[e8] = (__bf16)x;
+        pb[e8] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sv, sl2, off));
       }
+      ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 0, 1), one2, ps0, false);
+      ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 2, 3), one2, ps1, false);
+      ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 4, 5), one2, ps0, false);
+      ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 6, 7), one2, ps1, false);
       const int r1 = 16 * s + 4 * h + (tg >> 2), r2 = r1 + 8;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
@@ -229,10 +231,12 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
     int e = 0;
     for (; e < cnt; e += 2) {
       if ((e & 31) == 0) prior_chunk(e);
+      tile_copies_done();
       __syncthreads();  // block e in buffers 0; everyone is done with buffers 1
       if (e + 1 < cnt) copy_block(list[e + 1], kt1, vt1);
       if (active) block_step(e, kt0, vt0);
       if (e + 1 >= cnt) break;
+      tile_copies_done();
       __syncthreads();  // block e+1 in buffers 1; everyone is done with buffers 0
       if (e + 2 < cnt) copy_block(list[e + 2], kt0, vt0);
       if (active) block_step(e + 1, kt1, vt1);

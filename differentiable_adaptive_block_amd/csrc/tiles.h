@@ -35,6 +35,13 @@ __device__ __forceinline__ void copy16_to_lds(const bf16_t* g, bf16_t* lds) {
   __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
 }
 
+// Wait until this wave's tile copies have landed in LDS (vmcnt(0); the
+// copies count on the vector-memory counter only).  A barrier after the
+// wait then makes every wave's share of a tile visible to all waves.  The
+// immediate is the gfx9 s_waitcnt encoding with vmcnt 0 and the other
+// counters at their maximum (expcnt 7, lgkmcnt 15).
+__device__ __forceinline__ void tile_copies_done() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Transposing read: lane 4a+b of each 16-lane group receives element b of
 // the 8-byte pieces addressed by lanes a, a+4, a+8 and a+12 of the group.
 __device__ __forceinline__ bf16x4 ds_read_tr4(const bf16_t* p) {
@@ -57,6 +64,43 @@ __device__ __forceinline__ void copy_tile(const bf16_t* src, bf16_t* dst, int w,
     copy16_to_lds(src + (size_t)row * D + 8 * (slot ^ SWZ(row)), dst + r0 * D);
   }
 }
+
+// A wave's share of a tile copy (rows RPI*(NI*w + q) + lane/CH, as above,
+// with the tile split over NW waves) with the lane's source byte offsets
+// worked out once.  Given a wave-uniform tile address and wave index, each copy
+// instruction then addresses memory as scalar base + lane offset and writes
+// LDS at a scalar address, so a copy costs no vector arithmetic.
+template <int D, int (*SWZ)(int), int NW = 4>  // NW waves share the tile
+struct TileCopy {
+  static constexpr int CH = D / 8;
+  static constexpr int RPI = 1024 / (2 * D);
+  static constexpr int NI = 64 / RPI / NW;
+  uint32_t off[NI];
+  __device__ __forceinline__ void init(int w, int l) {
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      const int row = RPI * (NI * w + q) + l / CH, slot = l % CH;
+      off[q] = (uint32_t)(row * D + 8 * (slot ^ SWZ(row))) * 2u;
+    }
+  }
+  // src: the tile's first row; w must be wave-uniform
+  __device__ __forceinline__ void copy(const bf16_t* src, bf16_t* dst, int w) const {
+    // the base goes through the scalar unit explicitly, so that it is not
+    // folded with the loop-invariant lane offsets into 64-bit vector addresses
+    const uint64_t a = reinterpret_cast<uint64_t>(src);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const char* base = reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      // a fresh 32-bit copy of the offset here keeps its zero extension
+      // next to the address add, where it folds into the instruction
+      uint32_t o = off[q];
+      asm volatile("" : "+v"(o));
+      copy16_to_lds(reinterpret_cast<const bf16_t*>(base + o), dst + RPI * (NI * w + q) * D);
+    }
+  }
+};
 
 // A operand of S^T = K Q^T style products: 8 bf16 of row `row`, elements
 // 16 s + 8 h .. +7 (k-step s, lane half h), from a tile with swizzle SWZ.

@@ -27,7 +27,10 @@ def tol_out(dtype):
 
 
 def tol_lse(dtype):
-    return 1e-3 if dtype == torch.bfloat16 else 1e-4
+    # bf16: the normaliser is the sum of the weights as rounded to bf16 for
+    # the PV product (relative error <= 2^-8 each), so its log is within
+    # -ln(1 - 2^-8) = 3.91e-3 of the exact one; fp32 keeps 1e-4
+    return 4e-3 if dtype == torch.bfloat16 else 1e-4
 
 
 def unpack_mask(words: torch.Tensor, nb: int) -> np.ndarray:

@@ -81,7 +81,9 @@ def test_decode_equals_last_prefill_row():
     assert torch.equal(pre["kbar"], kbar)
     diff = (dec["o"].float() - pre["o"][:, :, N - 1].float()).abs().max().item()
     assert diff <= 1e-2, diff
-    assert torch.allclose(dec["lse"], pre["lse"][:, :, N - 1], atol=1e-4)
+    # the prefill normaliser sums the weights as rounded to bf16 (each within
+    # 2^-8 relative), decode sums them in fp32: logs within -ln(1 - 2^-8)
+    assert torch.allclose(dec["lse"], pre["lse"][:, :, N - 1], atol=4e-3)
 
 
 @pytest.mark.parametrize("name", ["c4", "c4cal"])
