@@ -200,7 +200,6 @@ dash_status dash_fwd_attend(const dash_params* p, const void* q, const void* k, 
   fa.lognorm = sel->lognorm;
   fa.tile_cnt = sel->tile_cnt;
   fa.tile_blk = sel->tile_blk;
-  fa.tile_bits = sel->tile_bits;
   fa.BH = p->B * p->H;
   fa.T = p->T;
   fa.D = p->D;

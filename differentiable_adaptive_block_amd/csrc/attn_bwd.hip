@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t kt1[64 * D];
   __shared__ __attribute__((aligned(16))) bf16_t vt0[64 * D];
   __shared__ __attribute__((aligned(16))) bf16_t vt1[64 * D];
-  __shared__ int lst[DASH_MAX_NB];
+  __shared__ float prs[4][32][32];  // per wave: log2 prior [list slot % 32][row]
 
   const int nb = a.T / DASH_BLOCK;
   const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
@@ -85,15 +85,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + bh * a.T * D;
   const bf16_t* dO = reinterpret_cast<const bf16_t*>(a.dout) + bh * a.T * D;
   const bf16_t* KB = reinterpret_cast<const bf16_t*>(a.kbar) + bh * nb * D;
-  const int* glist = a.tile_blk + (bh * ntile + tile) * nb;
+  const int* list = a.tile_blk + (bh * ntile + tile) * nb;
   const int cnt = a.tile_cnt[bh * ntile + tile];
   const CoarseArith ca = a.ca;
   const float sl2 = a.fine_scale * LOG2E_F;
-  // the list in LDS: no vector-memory load inside the loop, which would
-  // wait for the tile copies in flight
-  for (int x = tid; x < cnt; x += 256) lst[x] = glist[x];
-  __syncthreads();
-  const int* list = lst;
+  // list entries at a wave-uniform index go through the scalar cache: a
+  // vector-memory load inside the loop would wait for the tile copies in
+  // flight, which retire on the same counter
+  const __attribute__((address_space(4))) int* slist =
+      (const __attribute__((address_space(4))) int*)(uintptr_t)list;
 
   bf16x8 qb[KS], dob[KS];
   float tau_i = 0.f, ln_i = 0.f, lse2 = 0.f, dlt = 0.f;
@@ -114,11 +114,22 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqa[dt][r] = 0.f;
 
-  auto copy_block = [&](int b, bf16_t* kd, bf16_t* vd) {
-    copy_tile<D, TileSwz<D>::kv>(K + (size_t)b * DASH_BLOCK * D, kd, w, l);
-    copy_tile<D, TileSwz<D>::k>(V + (size_t)b * DASH_BLOCK * D, vd, w, l);
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  TileCopy<D, TileSwz<D>::kv> kcp;
+  TileCopy<D, TileSwz<D>::k> vcp;
+  kcp.init(wu, l);
+  vcp.init(wu, l);
+  auto copy_block = [&](int e, bf16_t* kd, bf16_t* vd) {
+    const size_t o = (size_t)slist[e] * DASH_BLOCK * D;
+    kcp.copy(K + o, kd, wu);
+    vcp.copy(V + o, vd, wu);
   };
-  f32x16 pacc;
+  // priors of list entries e0..e0+31 into this wave's LDS table
+  auto prior_chunk = [&](int e0) {
+    const f32x16 pacc = prior_chunk32<D>(KB, list, cnt, e0, qb, ca, tau_i, ln_i, a.causal, wblk);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) prs[w][acc_row32(r, l)][j] = pacc[r];
+  };
   auto put_g = [&](int e, float g, float p2) {
     if (h == 0) {
       const size_t gi = gidx(bh, ntile, tile, nb, e, w * 32 + j);
@@ -128,13 +139,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   };
 
   auto block_step = [&](int e, const bf16_t* kt, const bf16_t* vt) {
-    const int b = list[e];
+    const int b = slist[e];
     if (a.causal && b > wblk) {
       put_g(e, 0.f, -INFINITY);
       return;
     }
     const bool diag = a.causal && b == wblk;
-    const float pr = diag ? 0.f : prior_pick(pacc, e);
+    const float pr = diag ? 0.f : prs[w][e & 31][j];
     if (!diag && __ballot(pr != -INFINITY) == 0ull) {
       put_g(e, 0.f, -INFINITY);
       return;
@@ -155,6 +166,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         sc = mfma32(tile_row8<D, TileSwz<D>::kv>(kt, 32 * t + jx, s, hx), qb[s], sc);
         dp = mfma32(tile_row8<D, TileSwz<D>::k>(vt, 32 * t + jx, s, hx), dob[s], dp);
       }
+      if (diag) {  // the wave's own block: keys after the row are masked (wave-uniform branch)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * t + acc_row32(r, lx) > (qrow0 - b * DASH_BLOCK) + jx) sc[r] = -INFINITY;
+      }
       // dS^T of this half, as the B operand of the dQ product (k-steps of
       // 16 keys: registers 8 s2 .. 8 s2 + 7)
 #pragma unroll
@@ -163,9 +179,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int e8 = 0; e8 < 8; ++e8) {
           const int r = 8 * s2 + e8;
-          float sv = sc[r];
-          if (diag && b * DASH_BLOCK + 32 * t + acc_row32(r, l) > i) sv = -INFINITY;
-          const float p = __builtin_amdgcn_exp2f(fmaf(sv, sl2, off));
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[r], sl2, off));
           const float dsv = p * (dp[r] - dlt);
           gsum += dsv;
           db[e8] = (__bf16)dsv;
@@ -181,18 +195,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   };
 
   if (cnt > 0) {
-    copy_block(list[0], kt0, vt0);
+    copy_block(0, kt0, vt0);
     for (int e = 0; e < cnt; e += 2) {
-      if ((e & 31) == 0 && active)
-        pacc = prior_chunk32<D>(KB, list, cnt, e, qb, ca, tau_i, ln_i, a.causal, wblk);
+      if ((e & 31) == 0 && active) prior_chunk(e);
       tile_copies_done();
       __syncthreads();  // block e in buffers 0; everyone is done with buffers 1
-      if (e + 1 < cnt) copy_block(list[e + 1], kt1, vt1);
+      if (e + 1 < cnt) copy_block(e + 1, kt1, vt1);
       if (active) block_step(e, kt0, vt0);
       if (e + 1 >= cnt) break;
       tile_copies_done();
       __syncthreads();  // block e+1 in buffers 1; everyone is done with buffers 0
-      if (e + 2 < cnt) copy_block(list[e + 2], kt0, vt0);
+      if (e + 2 < cnt) copy_block(e + 2, kt0, vt0);
       if (active) block_step(e + 1, kt1, vt1);
     }
   }
@@ -275,10 +288,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const float sl2 = a.fine_scale * LOG2E_F;
 
   // K and V of the two blocks (waves 0-3 block 0, waves 4-7 block 1)
-  if (w / 4 < nblk) {
-    const size_t r0 = (size_t)(b0 + w / 4) * DASH_BLOCK * D;
-    copy_tile<D, TileSwz<D>::k>(K + r0, ks + (w / 4) * 64 * D, w & 3, l);
-    copy_tile<D, TileSwz<D>::k>(V + r0, vs + (w / 4) * 64 * D, w & 3, l);
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  if (wu / 4 < nblk) {
+    TileCopy<D, TileSwz<D>::k> kvcp;
+    kvcp.init(wu & 3, l);
+    const size_t r0 = (size_t)(b0 + wu / 4) * DASH_BLOCK * D;
+    kvcp.copy(K + r0, ks + (wu / 4) * 64 * D, wu & 3);
+    kvcp.copy(V + r0, vs + (wu / 4) * 64 * D, wu & 3);
   }
 
   // item list: thread x looks at tile x (then x + 512, ...), keeps its 0-2
@@ -382,11 +398,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
       dlq[buf][tid] = s_dl;
     }
   };
+  TileCopy<D, TileSwz<D>::kv> qocp;  // waves 0-3 copy the Q chunk, waves 4-7 the dO chunk
+  qocp.init(wu & 3, l);
   auto copy_item = [&](int n, bf16_t* qd, bf16_t* od) {
     const int t = itm[n][0] >> 1, c = itm[n][0] & 1;
     const size_t r0 = (size_t)(t * DASH_QTILE + c * 64) * D;
-    if (w < 4) copy_tile<D, TileSwz<D>::kv>(Q + r0, qd, w, l);
-    else copy_tile<D, TileSwz<D>::kv>(dO + r0, od, w - 4, l);
+    if (wu < 4) qocp.copy(Q + r0, qd, wu);
+    else qocp.copy(dO + r0, od, wu - 4);
   };
 
   auto item_step = [&](int n, int buf, const bf16_t* qc, const bf16_t* oc) {
@@ -430,7 +448,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
       sc = mfma32(tile_row8<D, TileSwz<D>::kv>(qc, 32 * qh + jx, st, hx), bk, sc);
       dp = mfma32(tile_row8<D, TileSwz<D>::kv>(oc, 32 * qh + jx, st, hx), bv, dp);
     }
-    const int key = wb * DASH_BLOCK + 32 * kh + j;
+    if (diag) {  // the wave's own block: keys after the row are masked (wave-uniform branch)
+      const int kx = wb * DASH_BLOCK + 32 * kh + jx - q0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kx > 32 * qh + acc_row32(r, lx)) sc[r] = -INFINITY;
+    }
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       bf16x8 pb, db;
@@ -438,9 +461,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
       for (int e8 = 0; e8 < 8; ++e8) {
         const int r = 8 * s2 + e8;
         const int ql = 32 * qh + acc_row32(r, l);
-        float sv = sc[r];
-        if (diag && key > q0 + ql) sv = -INFINITY;
-        const float p = __builtin_amdgcn_exp2f(fmaf(sv, sl2, prq[buf][kb][ql]));  // prior2 - lse2
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[r], sl2, prq[buf][kb][ql]));  // prior2 - lse2
         pb[e8] = (__bf16)p;
         db[e8] = (__bf16)(p * (dp[r] - dlq[buf][ql]));
       }

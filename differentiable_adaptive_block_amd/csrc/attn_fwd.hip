@@ -190,6 +190,20 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
     bf16x2 one2;
     one2[0] = (__bf16)1.f;
     one2[1] = (__bf16)1.f;
+    // V operand of k-step s, d tile dt
+    auto vread = [&](int s, int dt) -> bf16x8 {
+      const int r1 = 16 * s + 4 * h + (tg >> 2), r2 = r1 + 8;
+      const int col = 32 * dt + dof;
+      const int c = col >> 3, half = (col >> 2) & 1;
+      const bf16x4 lo = ds_read_tr4(vt + r1 * D + 8 * (c ^ TileSwz<D>::v(r1)) + 4 * half);
+      const bf16x4 hi = ds_read_tr4(vt + r2 * D + 8 * (c ^ TileSwz<D>::v(r2)) + 4 * half);
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    // operands are read one k-step ahead of the MFMAs that use them, in
+    // source order, so each read has NDT MFMAs to land
+    bf16x8 vnext[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) vnext[dt] = vread(0, dt);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bf16x8 pb;
@@ -202,28 +216,14 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
       ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 2, 3), one2, ps1, false);
       ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 4, 5), one2, ps0, false);
       ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 6, 7), one2, ps1, false);
-      const int r1 = 16 * s + 4 * h + (tg >> 2), r2 = r1 + 8;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const int col = 32 * dt + dof;
-        const int c = col >> 3, half = (col >> 2) & 1;
-        const bf16x4 lo = ds_read_tr4(vt + r1 * D + 8 * (c ^ TileSwz<D>::v(r1)) + 4 * half);
-        const bf16x4 hi = ds_read_tr4(vt + r2 * D + 8 * (c ^ TileSwz<D>::v(r2)) + 4 * half);
-        const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 va = vnext[dt];
+        if (s + 1 < 4) vnext[dt] = vread(s + 1, dt);
         oacc[dt] = mfma32(va, pb, oacc[dt]);
       }
     }
     lrow += ps0 + ps1;
-    // issue order: the first k-step's weights and operand reads, then each
-    // MFMA followed by two operand reads and a share of the next weights
-    __builtin_amdgcn_sched_group_barrier(0x402, 28, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NDT, 0);
-#pragma unroll
-    for (int s = 0; s < 4 * NDT; ++s) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, 28 / NDT, 0);
-    }
   };
 
   if (cnt > 0) {

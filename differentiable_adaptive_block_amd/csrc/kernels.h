@@ -28,7 +28,6 @@ struct FwdArgs {
   const float* lognorm;
   const int* tile_cnt;
   const int* tile_blk;
-  const uint32_t* tile_bits;  // [BH, ntile, nbw] block set of each 128-row tile
   int BH, T, D, causal;
   float fine_scale;
   CoarseArith ca;

@@ -29,10 +29,21 @@ template <> struct TileSwz<64> {   // 8 chunks of 16 B per row
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-// 16 bytes per lane from global memory into LDS: lane L of the wave writes
-// bytes 16 L .. 16 L + 15 after the wave-uniform address lds.
-__device__ __forceinline__ void copy16_to_lds(const bf16_t* g, bf16_t* lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+// 16 bytes per lane from global memory into LDS through a buffer resource
+// (MUBUF buffer_load ... lds): lane L of the wave reads 16 bytes at byte
+// offset voff of the buffer and writes them at bytes 16 L .. 16 L + 15
+// after the wave-uniform address lds.  Unlike the global (FLAT-encoded)
+// form, the compiler does not count this copy among the pending
+// LDS-counter events, so the operand reads that follow it keep partial
+// lgkmcnt waits instead of waiting for every read in flight.
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, bf16_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
+// Buffer resource for `bytes` bytes at the wave-uniform address p (gfx9
+// descriptor word 3: 32-bit data format, raw addressing).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
 }
 
 // Wait until this wave's tile copies have landed in LDS (vmcnt(0); the
@@ -49,27 +60,13 @@ __device__ __forceinline__ bf16x4 ds_read_tr4(const bf16_t* p) {
       (lds_bf16x4*)(__attribute__((address_space(3))) bf16_t*)(p));
 }
 
-// One wave copies its share of a 64-row tile: rows RPI*(NI*w + q) +
-// lane/CH, q < NI, where RPI rows fill one 1 KB instruction and the 4 waves
-// of a workgroup split the 64 rows.  SWZ is one of TileSwz<D>::{k, v, kv}.
-template <int D, int (*SWZ)(int)>
-__device__ __forceinline__ void copy_tile(const bf16_t* src, bf16_t* dst, int w, int l) {
-  constexpr int CH = D / 8;
-  constexpr int RPI = 1024 / (2 * D);
-  constexpr int NI = 64 / RPI / 4;
-#pragma unroll
-  for (int q = 0; q < NI; ++q) {
-    const int r0 = RPI * (NI * w + q);
-    const int row = r0 + l / CH, slot = l % CH;
-    copy16_to_lds(src + (size_t)row * D + 8 * (slot ^ SWZ(row)), dst + r0 * D);
-  }
-}
-
-// A wave's share of a tile copy (rows RPI*(NI*w + q) + lane/CH, as above,
-// with the tile split over NW waves) with the lane's source byte offsets
-// worked out once.  Given a wave-uniform tile address and wave index, each copy
-// instruction then addresses memory as scalar base + lane offset and writes
-// LDS at a scalar address, so a copy costs no vector arithmetic.
+// A wave's share of a 64-row tile copy: with RPI rows per 1 KB
+// instruction and the tile split over NW waves, wave w fills rows
+// RPI*(NI*w + q) + lane/CH, q < NI, slot lane%CH of each from source chunk
+// slot ^ swz(row); the lane's source byte offsets are worked out once.
+// Given a wave-uniform tile address and wave index, each copy instruction
+// then addresses memory as scalar descriptor + lane offset and writes LDS
+// at a scalar address, so a copy costs no vector arithmetic.
 template <int D, int (*SWZ)(int), int NW = 4>  // NW waves share the tile
 struct TileCopy {
   static constexpr int CH = D / 8;
@@ -85,20 +82,14 @@ struct TileCopy {
   }
   // src: the tile's first row; w must be wave-uniform
   __device__ __forceinline__ void copy(const bf16_t* src, bf16_t* dst, int w) const {
-    // the base goes through the scalar unit explicitly, so that it is not
-    // folded with the loop-invariant lane offsets into 64-bit vector addresses
+    // the base goes through the scalar unit explicitly (a wave-uniform
+    // buffer descriptor)
     const uint64_t a = reinterpret_cast<uint64_t>(src);
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-    const char* base = reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), 64 * D * 2);
 #pragma unroll
-    for (int q = 0; q < NI; ++q) {
-      // a fresh 32-bit copy of the offset here keeps its zero extension
-      // next to the address add, where it folds into the instruction
-      uint32_t o = off[q];
-      asm volatile("" : "+v"(o));
-      copy16_to_lds(reinterpret_cast<const bf16_t*>(base + o), dst + RPI * (NI * w + q) * D);
-    }
+    for (int q = 0; q < NI; ++q) copy16_to_lds(r, off[q], dst + RPI * (NI * w + q) * D);
   }
 };
 
