@@ -155,6 +155,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     asm volatile("" : "+v"(lx));
     const int jx = lx & 31, hx = lx >> 5;
     const float off = (pr == -INFINITY) ? -INFINITY : pr - lse2;
+    // row reads of keys jx and 32 + jx (same permutation: it depends on row
+    // bits 0-3 only): chunk (2 s + h) ^ swz = 2 s ^ (h ^ swz), so k-step s
+    // XORs 32 s into a per-lane byte offset
+    const char* krb = reinterpret_cast<const char*>(kt + jx * D);
+    const char* vrb = reinterpret_cast<const char*>(vt + jx * D);
+    const uint32_t ky = 16u * (uint32_t)(hx ^ TileSwz<D>::kv(jx));
+    const uint32_t vy = 16u * (uint32_t)(hx ^ TileSwz<D>::k(jx));
+    // transposing reads of K (bytes): A + ((64 dt) ^ B) + 32 D k-step
+    uint32_t A1, B1, A2, B2;
+    col8_parts<D, TileSwz<D>::kv>(lx, A1, B1, A2, B2);
     float gsum = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -163,8 +173,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       for (int r = 0; r < 16; ++r) { sc[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        sc = mfma32(tile_row8<D, TileSwz<D>::kv>(kt, 32 * t + jx, s, hx), qb[s], sc);
-        dp = mfma32(tile_row8<D, TileSwz<D>::k>(vt, 32 * t + jx, s, hx), dob[s], dp);
+        sc = mfma32(load8(reinterpret_cast<const bf16_t*>(krb + 64 * D * t + ((32u * s) ^ ky))), qb[s], sc);
+        dp = mfma32(load8(reinterpret_cast<const bf16_t*>(vrb + 64 * D * t + ((32u * s) ^ vy))), dob[s], dp);
       }
       if (diag) {  // the wave's own block: keys after the row are masked (wave-uniform branch)
 #pragma unroll
@@ -186,7 +196,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
-          dqa[dt] = mfma32(tile_col8<D, TileSwz<D>::kv>(kt, 2 * t + s2, dt, lx), db, dqa[dt]);
+          dqa[dt] = mfma32(tile_col8_b(reinterpret_cast<const char*>(kt) + 32 * D * (2 * t + s2),
+                                       A1 + ((64u * dt) ^ B1), A2 + ((64u * dt) ^ B2)),
+                           db, dqa[dt]);
       }
     }
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(gsum), __float_as_uint(gsum), false, false);
@@ -254,17 +266,23 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int CH = D / 8;
   constexpr int NITEM = 32 * CH;       // (row pair, chunk) dkbar items per query chunk
   constexpr int MAXIT = 2 * (DASH_MAX_NB / 2);  // 64-query chunks of the longest sequence
-  __shared__ __attribute__((aligned(16))) bf16_t ks[128 * D];
-  __shared__ __attribute__((aligned(16))) bf16_t vs[128 * D];
-  __shared__ __attribute__((aligned(16))) bf16_t qc0[64 * D];
-  __shared__ __attribute__((aligned(16))) bf16_t qc1[64 * D];
-  __shared__ __attribute__((aligned(16))) bf16_t oc0[64 * D];
-  __shared__ __attribute__((aligned(16))) bf16_t oc1[64 * D];
+  constexpr int KP = D + 8;  // row pitch of the K and V tiles (padded: conflict-free 16-byte row reads)
+  // per-item tiles, one object per buffer (reads of one are not ordered
+  // behind the copy into the other); the Q tile, then the dO tile 64 D
+  // elements on, so both take one address and an immediate offset
+  __shared__ __attribute__((aligned(16))) bf16_t qo0[2 * 64 * D];
+  __shared__ __attribute__((aligned(16))) bf16_t qo1[2 * 64 * D];
+  bf16_t* const qc0 = qo0;
+  bf16_t* const oc0 = qo0 + 64 * D;
+  bf16_t* const qc1 = qo1;
+  bf16_t* const oc1 = qo1 + 64 * D;
+  __shared__ __attribute__((aligned(16))) bf16_t ks[128 * KP];
+  __shared__ __attribute__((aligned(16))) bf16_t vs[128 * KP];
   __shared__ float prq[2][2][64], dzq[2][2][64], dlq[2][64];  // [buffer][block][row], [buffer][row]
   __shared__ int itm[MAXIT][3];                                // (t * 2 + c, slot0, slot1)
   __shared__ int nit_s, wsum[8];
   __shared__ float kbg[2][D];
-  static_assert(2 * 32 * D * 4 <= 128 * D * 2, "dkbar reduction space in the K tile");
+  static_assert(2 * 32 * D * 4 <= 128 * KP * 2, "dkbar reduction space in the K tile");
   static_assert(NDT * 16 * 64 * 4 <= 64 * D * 2, "merge space: one partial per 64-row tile buffer");
 
   const int nb = a.T / DASH_BLOCK;
@@ -287,14 +305,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const bf16_t* dO = reinterpret_cast<const bf16_t*>(a.dout) + bh * a.T * D;
   const float sl2 = a.fine_scale * LOG2E_F;
 
-  // K and V of the two blocks (waves 0-3 block 0, waves 4-7 block 1)
+  // K and V of the two blocks, rows 0-63 block b0, 64-127 block b0 + 1:
+  // loaded once per workgroup, into row-padded tiles
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  if (wu / 4 < nblk) {
-    TileCopy<D, TileSwz<D>::k> kvcp;
-    kvcp.init(wu & 3, l);
-    const size_t r0 = (size_t)(b0 + wu / 4) * DASH_BLOCK * D;
-    kvcp.copy(K + r0, ks + (wu / 4) * 64 * D, wu & 3);
-    kvcp.copy(V + r0, vs + (wu / 4) * 64 * D, wu & 3);
+  for (int x = tid; x < 64 * nblk * CH; x += 512) {
+    const int row = x / CH, ch = x % CH;
+    const size_t g = ((size_t)b0 * DASH_BLOCK + row) * D + 8 * ch;
+    *reinterpret_cast<uint4*>(ks + row * KP + 8 * ch) = *reinterpret_cast<const uint4*>(K + g);
+    *reinterpret_cast<uint4*>(vs + row * KP + 8 * ch) = *reinterpret_cast<const uint4*>(V + g);
   }
 
   // item list: thread x looks at tile x (then x + 512, ...), keeps its 0-2
@@ -441,13 +459,23 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) { sc[r] = 0.f; dp[r] = 0.f; }
     const int krow = 64 * kb + 32 * kh + jx;
+    // Q / dO row reads: chunk (2 st + h) ^ swz(row) = 2 st ^ (h ^ swz(row)),
+    // so k-step st XORs 32 st into a per-lane byte offset
+    const int qrow = 32 * qh + jx;
+    const char* qrb = reinterpret_cast<const char*>(qc + qrow * D);
+    const uint32_t qy = 16u * (uint32_t)(hx ^ TileSwz<D>::kv(qrow));
 #pragma unroll
     for (int st = 0; st < KS; ++st) {
-      const bf16x8 bk = tile_row8<D, TileSwz<D>::k>(ks, krow, st, hx);
-      const bf16x8 bv = tile_row8<D, TileSwz<D>::k>(vs, krow, st, hx);
-      sc = mfma32(tile_row8<D, TileSwz<D>::kv>(qc, 32 * qh + jx, st, hx), bk, sc);
-      dp = mfma32(tile_row8<D, TileSwz<D>::kv>(oc, 32 * qh + jx, st, hx), bv, dp);
+      const bf16x8 bk = load8(ks + krow * KP + 16 * st + 8 * hx);
+      const bf16x8 bv = load8(vs + krow * KP + 16 * st + 8 * hx);
+      const char* qa = qrb + ((32u * st) ^ qy);
+      sc = mfma32(load8(reinterpret_cast<const bf16_t*>(qa)), bk, sc);
+      dp = mfma32(load8(reinterpret_cast<const bf16_t*>(qa + 2 * 64 * D)), bv, dp);
     }
+    // transposing-read offsets (bytes) of this wave's k-steps 2 qh + s2
+    uint32_t A1, B1, A2, B2;
+    col8_parts<D, TileSwz<D>::kv>(lx, A1, B1, A2, B2);
+    const char* qcb = reinterpret_cast<const char*>(qc) + 64 * D * qh;  // k-step 2 qh
     if (diag) {  // the wave's own block: keys after the row are masked (wave-uniform branch)
       const int kx = wb * DASH_BLOCK + 32 * kh + jx - q0;
 #pragma unroll
@@ -468,8 +496,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
       // queries 16 (2 qh + s2) .. +15 of the chunk are this k-step
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        dva[dt] = mfma32(tile_col8<D, TileSwz<D>::kv>(oc, 2 * qh + s2, dt, lx), pb, dva[dt]);
-        dka[dt] = mfma32(tile_col8<D, TileSwz<D>::kv>(qc, 2 * qh + s2, dt, lx), db, dka[dt]);
+        const uint32_t o1 = A1 + ((64u * dt) ^ B1), o2 = A2 + ((64u * dt) ^ B2);
+        dva[dt] = mfma32(tile_col8_b(qcb + 2 * 64 * D + 32 * D * s2, o1, o2), pb, dva[dt]);
+        dka[dt] = mfma32(tile_col8_b(qcb + 32 * D * s2, o1, o2), db, dka[dt]);
       }
     }
   };

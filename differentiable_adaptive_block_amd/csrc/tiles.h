@@ -115,3 +115,25 @@ __device__ __forceinline__ bf16x8 tile_col8(const bf16_t* t, int s, int dt, int 
   const bf16x4 hi = ds_read_tr4(t + r2 * D + 8 * (c ^ SWZ(r2)) + 4 * half);
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
+
+// Byte offsets of tile_col8's two reads, split so that k-step s and d tile
+// dt cost one XOR-add each: read 1 sits at A1 + ((64 dt) ^ B1) + 32 D s,
+// read 2 at A2 + ((64 dt) ^ B2) + 32 D s.  The permutations above depend
+// on bits 0-3 of the row only (so k-step s, 16 rows on, moves both reads
+// by 32 D bytes), and chunk 4 dt + c0 (c0 < 4) permuted by p is
+// 4 (dt ^ (p >> 2)) + (c0 ^ (p & 3)).
+template <int D, int (*SWZ)(int)>
+__device__ __forceinline__ void col8_parts(int l, uint32_t& A1, uint32_t& B1, uint32_t& A2, uint32_t& B2) {
+  const int tg = l & 15, h = l >> 5;
+  const int c0 = 2 * ((l >> 4) & 1) + ((tg >> 1) & 1), half = tg & 1;
+  const int r1 = 4 * h + (tg >> 2), r2 = r1 + 8;
+  const int p1 = SWZ(r1), p2 = SWZ(r2);
+  A1 = (uint32_t)(2 * r1 * D + 16 * (c0 ^ (p1 & 3)) + 8 * half);
+  A2 = (uint32_t)(2 * r2 * D + 16 * (c0 ^ (p2 & 3)) + 8 * half);
+  B1 = (uint32_t)(16 * (p1 & 12));
+  B2 = (uint32_t)(16 * (p2 & 12));
+}
+__device__ __forceinline__ bf16x8 tile_col8_b(const char* t, uint32_t o1, uint32_t o2) {
+  return __builtin_shufflevector(ds_read_tr4(reinterpret_cast<const bf16_t*>(t + o1)),
+                                 ds_read_tr4(reinterpret_cast<const bf16_t*>(t + o2)), 0, 1, 2, 3, 4, 5, 6, 7);
+}
