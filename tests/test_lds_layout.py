@@ -80,3 +80,48 @@ def test_unpermuted_tile_would_conflict():
     D = 128
     plain = [[(32 * t + l % 32) * 2 * D + 16 * (2 * s + l // 32) for l in range(64)] for t in range(2) for s in range(8)]
     assert max(worst_degree(a, 16) for a in plain) > 1
+
+
+# The XOR-split offsets the backward kernels use in place of the
+# definitions above (restated from csrc/tiles.h col8_parts and the row-read
+# form base + ((32 s) ^ lane bits)); they must give the same byte addresses.
+
+def col8_parts(D, kind, l):
+    tg, h = l % 16, l // 32
+    c0, half = 2 * ((l // 16) % 2) + ((tg >> 1) & 1), tg & 1
+    r1 = 4 * h + tg // 4
+    r2 = r1 + 8
+    p1, p2 = swz(D, kind, r1), swz(D, kind, r2)
+    return (2 * r1 * D + 16 * (c0 ^ (p1 & 3)) + 8 * half, 16 * (p1 & 12),
+            2 * r2 * D + 16 * (c0 ^ (p2 & 3)) + 8 * half, 16 * (p2 & 12))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("kind", ["k", "v", "kv"])
+def test_xor_split_transposing_offsets(D, kind):
+    rb = 2 * D
+    for l in range(64):
+        A1, B1, A2, B2 = col8_parts(D, kind, l)
+        g, tg, h = l // 16, l % 16, l // 32
+        for s in range(4):
+            for dt in range(D // 32):
+                col = 32 * dt + 16 * (g % 2) + 4 * (tg % 4)
+                c, half = col // 8, (col // 4) % 2
+                for hi, (A, B) in ((0, (A1, B1)), (8, (A2, B2))):
+                    row = 16 * s + 4 * h + tg // 4 + hi
+                    want = row * rb + 16 * (c ^ swz(D, kind, row)) + 8 * half
+                    assert A + ((64 * dt) ^ B) + 32 * D * s == want
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("kind", ["k", "kv"])
+def test_xor_split_row_offsets(D, kind):
+    rb = 2 * D
+    for l in range(64):
+        j, h = l % 32, l // 32
+        for t in range(2):
+            row = 32 * t + j
+            y = 16 * (h ^ swz(D, kind, j))  # rows j and 32 + j share the permutation
+            for s in range(D // 16):
+                want = row * rb + 16 * ((2 * s + h) ^ swz(D, kind, row))
+                assert j * rb + 64 * D * t + ((32 * s) ^ y) == want
