@@ -93,32 +93,14 @@ struct TileCopy {
   }
 };
 
-// A operand of S^T = K Q^T style products: 8 bf16 of row `row`, elements
-// 16 s + 8 h .. +7 (k-step s, lane half h), from a tile with swizzle SWZ.
-template <int D, int (*SWZ)(int)>
-__device__ __forceinline__ bf16x8 tile_row8(const bf16_t* t, int row, int s, int h) {
-  return load8(t + row * D + 8 * ((2 * s + h) ^ SWZ(row)));
-}
-
-// A operand of O^T += X^T P^T style products (X = V or K, rows = keys):
-// 8 keys 16 s + 4 h + {0..3} and 16 s + 8 + 4 h + {0..3} of column
-// 32 dt + lane % 32, built from two transposing reads.  Lane t of each
-// 16-lane group addresses row key0 + t/4, columns 32 dt + 16 (group % 2)
-// + 4 (t % 4) .. +3.
-template <int D, int (*SWZ)(int)>
-__device__ __forceinline__ bf16x8 tile_col8(const bf16_t* t, int s, int dt, int l) {
-  const int tg = l & 15, h = l >> 5;
-  const int col = 32 * dt + 16 * ((l >> 4) & 1) + 4 * (tg & 3);
-  const int c = col >> 3, half = (col >> 2) & 1;
-  const int r1 = 16 * s + 4 * h + (tg >> 2), r2 = r1 + 8;
-  const bf16x4 lo = ds_read_tr4(t + r1 * D + 8 * (c ^ SWZ(r1)) + 4 * half);
-  const bf16x4 hi = ds_read_tr4(t + r2 * D + 8 * (c ^ SWZ(r2)) + 4 * half);
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// Byte offsets of tile_col8's two reads, split so that k-step s and d tile
-// dt cost one XOR-add each: read 1 sits at A1 + ((64 dt) ^ B1) + 32 D s,
-// read 2 at A2 + ((64 dt) ^ B2) + 32 D s.  The permutations above depend
+// Operands of O^T += X^T P^T style products (X = V, K, Q or dO; rows of X
+// are the contraction index) from transposing reads: 8 keys 16 s + 4 h +
+// {0..3} and 16 s + 8 + 4 h + {0..3} of column 32 dt + lane % 32, built
+// from two reads in which lane t of each 16-lane group addresses row
+// key0 + t/4, columns 32 dt + 16 (group % 2) + 4 (t % 4) .. +3.  Byte
+// offsets of the two reads, split so that k-step s and d tile dt cost one
+// XOR-add each: read 1 sits at A1 + ((64 dt) ^ B1) + 32 D s, read 2 at
+// A2 + ((64 dt) ^ B2) + 32 D s.  The permutations above depend
 // on bits 0-3 of the row only (so k-step s, 16 rows on, moves both reads
 // by 32 D bytes), and chunk 4 dt + c0 (c0 < 4) permuted by p is
 // 4 (dt ^ (p >> 2)) + (c0 ^ (p & 3)).
