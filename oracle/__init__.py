@@ -43,4 +43,6 @@ from .dash_ref import (  # noqa: F401
     backward,
     backward_rows,
     decode,
+    cache_append,
+    decode_varlen,
 )

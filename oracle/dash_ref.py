@@ -30,6 +30,12 @@ Readings taken where the pages are silent (each is restated in the design doc):
   (round-to-nearest-even) to the storage dtype of K.
 * R7 decode: the new token is the last cached token; the decode output is
   row N-1 of a causal prefill over the cache.
+* R18 decode cache maintenance: appending token n writes it at position n;
+  when that completes a block, the block's summary is its Stage-0 mean.
+* R19 a cache of n tokens (any n >= 1): the query is at position n-1, its
+  candidates are the complete blocks before its own, and its own block is
+  attended over its cached tokens only (row n-1 of a causal prefill over
+  the first n tokens).
 * R9 separate fine scale (logits) and coarse scale (block scores).
 * Backward treats the rounding of the summary to its storage dtype as the
   identity (straight-through).
@@ -370,6 +376,87 @@ def decode(q, kc, vc, prm: Params, kbar=None):
             kb = _as64(kbar[s, h]) if kbar is not None else pool_blocks(kc[s, h], prm.block, prm.storage)
             sel = select_row(q[s, h], kb, N - 1, prm, D)
             oi, li, _ = attend_row(q[s, h], kc[s, h], vc[s, h], N - 1, sel, prm, D)
+            o[s, h], lse[s, h], tau[s, h] = oi, li, sel["tau"]
+            nsel[s, h] = int(sel["support"].sum())
+            mask[s, h, sel["cand"][sel["support"]]] = True
+    return dict(o=o, lse=lse, nsel=nsel, mask=mask, tau=tau)
+
+
+# ----------------------------------------------------------------------------- decode cache maintenance
+
+
+def cache_append(kc, vc, kbar, lens, k_new, v_new, prm: Params):
+    """Append one token per (sequence, head) to a decode cache (R18).
+
+    ``kc, vc``: [S, H, C, D] caches of capacity C (a multiple of the block);
+    ``kbar``: [S, H, C/block, D] their summaries; ``lens``: [S] tokens
+    already cached per sequence (each < C); ``k_new, v_new``: [S, H, D].
+    Sequence s's token goes to position lens[s].  If that position is the
+    last of its block, the block is now complete and its summary becomes the
+    Stage-0 mean of its keys (the decoding path keeps one summary per chunk
+    of the cache: the chunk-summarise stage among the code samples that the
+    codewithpapers.app entry "DashAttention: Differentiable and Adaptive
+    Sparse Hierarchical Attention" lists).  Summaries of incomplete blocks
+    are left as they are.  Returns new arrays (kc, vc, kbar, lens + 1); the inputs are
+    not modified.
+    """
+    kc, vc, kbar = _as64(kc).copy(), _as64(vc).copy(), _as64(kbar).copy()
+    lens = np.asarray(lens, dtype=np.int64)
+    S, H, C, D = kc.shape
+    blk = prm.block
+    if np.any(lens < 0) or np.any(lens >= C):
+        raise ValueError("every length must lie in [0, capacity)")
+    for s in range(S):
+        n = int(lens[s])
+        kc[s, :, n] = _as64(k_new[s])
+        vc[s, :, n] = _as64(v_new[s])
+        if n % blk == blk - 1:
+            b = n // blk
+            for h in range(H):
+                kbar[s, h, b] = pool_blocks(kc[s, h, b * blk:(b + 1) * blk], blk, prm.storage)[0]
+    return kc, vc, kbar, lens + 1
+
+
+def decode_varlen(q, kc, vc, lens, prm: Params, kbar=None):
+    """Decode with a cache length per sequence (R19).
+
+    ``q``: [S, H, D]; ``kc, vc``: [S, H, C, D] with sequence s holding
+    ``lens[s]`` tokens (1 <= lens[s] <= C), the new one last.  Entries beyond
+    a sequence's length are never read.  The output of (s, h) is row
+    lens[s]-1 of a causal prefill over the first lens[s] tokens: candidates
+    are the complete blocks before the query's own block, which is attended
+    over its cached tokens with prior 0.  ``kbar`` ([S, H, C/block, D]) may
+    be given; only the entries of complete blocks before the query's own
+    block are read.  By default they are pooled here.
+    Returns dict(o [S,H,D], lse [S,H], nsel [S,H], mask [S,H,C/block], tau [S,H]).
+    """
+    if not prm.causal:
+        raise ValueError("decode is defined as the last row of a causal prefill")
+    q = _as64(q)
+    S, H, C, D = kc.shape
+    blk = prm.block
+    lens = np.asarray(lens, dtype=np.int64)
+    if np.any(lens < 1) or np.any(lens > C):
+        raise ValueError("every length must lie in [1, capacity]")
+    nbc = C // blk
+    o = np.zeros((S, H, D))
+    lse = np.zeros((S, H))
+    nsel = np.zeros((S, H), dtype=np.int64)
+    mask = np.zeros((S, H, nbc), dtype=bool)
+    tau = np.zeros((S, H))
+    for s in range(S):
+        n = int(lens[s])
+        i = n - 1
+        ncand = i // blk  # complete blocks before the query's own block
+        for h in range(H):
+            k_head = _as64(kc[s, h, :n])
+            v_head = _as64(vc[s, h, :n])
+            if kbar is not None:
+                kb = _as64(kbar[s, h, :ncand])
+            else:
+                kb = pool_blocks(k_head[:ncand * blk], blk, prm.storage)
+            sel = select_row(q[s, h], kb, i, prm, D)
+            oi, li, _ = attend_row(q[s, h], k_head, v_head, i, sel, prm, D)
             o[s, h], lse[s, h], tau[s, h] = oi, li, sel["tau"]
             nsel[s, h] = int(sel["support"].sum())
             mask[s, h, sel["cand"][sel["support"]]] = True
