@@ -29,6 +29,9 @@ EXPORTS = [
     "dash_bwd",
     "dash_decode_workspace_bytes",
     "dash_decode",
+    "dash_cache_append",
+    "dash_decode_varlen",
+    "dash_decode_step",
     "dash_last_error",
 ]
 
@@ -99,6 +102,14 @@ def load() -> ctypes.CDLL:
     L.dash_decode_workspace_bytes.argtypes = [P(DashDecodeParams)]
     L.dash_decode.restype = ctypes.c_int
     L.dash_decode.argtypes = [P(DashDecodeParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.dash_cache_append.restype = ctypes.c_int
+    L.dash_cache_append.argtypes = [P(DashDecodeParams), vp, vp, vp, vp, vp, vp, vp]
+    L.dash_decode_varlen.restype = ctypes.c_int
+    L.dash_decode_varlen.argtypes = [P(DashDecodeParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                     vp]
+    L.dash_decode_step.restype = ctypes.c_int
+    L.dash_decode_step.argtypes = [P(DashDecodeParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                   ctypes.c_size_t, vp]
     L.dash_last_error.restype = ctypes.c_char_p
     L.dash_last_error.argtypes = []
     _lib = L
@@ -155,3 +166,18 @@ def bwd(p: DashParams, q, k, v, o, lse, dout, kbar, sel: DashSel, dq, dk, dv, dk
 
 def decode(p: DashDecodeParams, q, kc, vc, kbar, o, lse, nsel, tau, ws, ws_bytes, stream) -> None:
     check(load().dash_decode(ctypes.byref(p), q, kc, vc, kbar, o, lse, nsel, tau, ws, ws_bytes, stream))
+
+
+def cache_append(p: DashDecodeParams, k_new, v_new, lens, kc, vc, kbar, stream) -> None:
+    check(load().dash_cache_append(ctypes.byref(p), k_new, v_new, lens, kc, vc, kbar, stream))
+
+
+def decode_varlen(p: DashDecodeParams, q, kc, vc, kbar, lens, o, lse, nsel, tau, ws, ws_bytes, stream) -> None:
+    check(load().dash_decode_varlen(ctypes.byref(p), q, kc, vc, kbar, lens, o, lse, nsel, tau, ws, ws_bytes,
+                                    stream))
+
+
+def decode_step(p: DashDecodeParams, q, k_new, v_new, lens, kc, vc, kbar, o, lse, nsel, tau, ws, ws_bytes,
+                stream) -> None:
+    check(load().dash_decode_step(ctypes.byref(p), q, k_new, v_new, lens, kc, vc, kbar, o, lse, nsel, tau, ws,
+                                  ws_bytes, stream))

@@ -172,6 +172,60 @@ def decode(q, kc, vc, kbar, alpha=1.5, fine_scale=None, coarse_scale=None, bufs:
     return dict(o=bufs.o, lse=bufs.lse, nsel=bufs.nsel, tau=bufs.tau)
 
 
+def _require_lens(lens, S, device):
+    if not (isinstance(lens, torch.Tensor) and lens.dtype == torch.int32 and lens.shape == (S,)
+            and lens.device == device and lens.is_contiguous()):
+        raise ValueError(f"lens must be a contiguous int32 tensor of shape ({S},) on {device}")
+
+
+def cache_append(kc, vc, kbar, lens, k_new, v_new):
+    """Write k_new, v_new [S,H,D] at position lens[s] of caches kc, vc [S,H,C,D]
+    and, for blocks the token completes, their summaries in kbar.  lens is not advanced."""
+    S, H, C, D = kc.shape
+    _require(vc, "vc", kc.shape, kc.dtype)
+    _require(kbar, "kbar", (S, H, C // BLOCK, D), kc.dtype)
+    _require(k_new, "k_new", (S, H, D), kc.dtype)
+    _require(v_new, "v_new", (S, H, D), kc.dtype)
+    _require_lens(lens, S, kc.device)
+    p = make_decode_params(k_new, kc, 1.5)
+    _lib.cache_append(p, _ptr(k_new), _ptr(v_new), _ptr(lens), _ptr(kc), _ptr(vc), _ptr(kbar), _stream(kc.device))
+
+
+def decode_varlen(q, kc, vc, kbar, lens, alpha=1.5, fine_scale=None, coarse_scale=None,
+                  bufs: DecodeBuffers | None = None):
+    """Decode with lens[s] tokens cached for sequence s (the new one last) in caches of capacity C."""
+    S, H, C, D = kc.shape
+    _require(q, "q", (S, H, D), kc.dtype)
+    _require(vc, "vc", kc.shape, kc.dtype)
+    _require(kbar, "kbar", (S, H, C // BLOCK, D), kc.dtype)
+    _require_lens(lens, S, q.device)
+    p = make_decode_params(q, kc, alpha, fine_scale, coarse_scale)
+    if bufs is None:
+        bufs = DecodeBuffers(p, q.dtype, q.device)
+    _lib.decode_varlen(p, _ptr(q), _ptr(kc), _ptr(vc), _ptr(kbar), _ptr(lens), _ptr(bufs.o), _ptr(bufs.lse),
+                       _ptr(bufs.nsel), _ptr(bufs.tau), _ptr(bufs.ws), bufs.ws_bytes, _stream(q.device))
+    return dict(o=bufs.o, lse=bufs.lse, nsel=bufs.nsel, tau=bufs.tau)
+
+
+def decode_step(q, k_new, v_new, kc, vc, kbar, lens, alpha=1.5, fine_scale=None, coarse_scale=None,
+                bufs: DecodeBuffers | None = None):
+    """Append (k_new, v_new) at lens[s], then decode over lens[s] + 1 tokens.  lens is not advanced."""
+    S, H, C, D = kc.shape
+    _require(q, "q", (S, H, D), kc.dtype)
+    _require(k_new, "k_new", (S, H, D), kc.dtype)
+    _require(v_new, "v_new", (S, H, D), kc.dtype)
+    _require(vc, "vc", kc.shape, kc.dtype)
+    _require(kbar, "kbar", (S, H, C // BLOCK, D), kc.dtype)
+    _require_lens(lens, S, q.device)
+    p = make_decode_params(q, kc, alpha, fine_scale, coarse_scale)
+    if bufs is None:
+        bufs = DecodeBuffers(p, q.dtype, q.device)
+    _lib.decode_step(p, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(lens), _ptr(kc), _ptr(vc), _ptr(kbar),
+                     _ptr(bufs.o), _ptr(bufs.lse), _ptr(bufs.nsel), _ptr(bufs.tau), _ptr(bufs.ws), bufs.ws_bytes,
+                     _stream(q.device))
+    return dict(o=bufs.o, lse=bufs.lse, nsel=bufs.nsel, tau=bufs.tau)
+
+
 class DashAttentionFn(torch.autograd.Function):
     """DashAttention as an autograd function (forward: Stages 0-2; backward through all of them)."""
 

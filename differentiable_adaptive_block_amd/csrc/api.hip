@@ -268,9 +268,7 @@ dash_status dash_bwd(const dash_params* p, const void* q, const void* k, const v
   return e == hipSuccess ? DASH_OK : hip_fail(e, "backward");
 }
 
-dash_status dash_decode(const dash_decode_params* p, const void* q, const void* kc, const void* vc,
-                        const void* kbar, void* o, float* lse, int32_t* nsel, float* tau, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+static dash_status check_decode_params(const dash_decode_params* p) {
   if (!p) return fail(DASH_EINVAL, "null params");
   if (p->S < 1 || p->H < 1) return fail(DASH_EINVAL, "S and H must be >= 1");
   if (p->N < DASH_BLOCK || p->N % DASH_BLOCK) return fail(DASH_EINVAL, "N must be a positive multiple of 64 (got %d)", p->N);
@@ -278,6 +276,15 @@ dash_status dash_decode(const dash_decode_params* p, const void* q, const void* 
   if (s != DASH_OK) return s;
   if (p->N / DASH_BLOCK > 2048) return fail(DASH_EUNSUPPORTED, "cache above 131072 tokens is not built");
   if (p->dtype != DASH_BF16 || p->D != 128) return fail(DASH_EUNSUPPORTED, "decode is built for bf16, D = 128");
+  return DASH_OK;
+}
+
+// Validation and launch shared by dash_decode, dash_decode_varlen and
+// dash_decode_step: rows hold len[s] + len_add tokens, or N when len is null.
+static dash_status decode_common(const dash_decode_params* p, const void* q, const void* kc, const void* vc,
+                                 const void* kbar, const int32_t* len, int len_add, void* o, float* lse,
+                                 int32_t* nsel, float* tau, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
   if (!ok_ptr(q) || !ok_ptr(kc) || !ok_ptr(vc) || !ok_ptr(kbar) || !ok_ptr(o))
     return fail(DASH_EINVAL, "q, kc, vc, kbar and o must be non-null and 16-byte aligned");
   if (!ok_opt(lse) || !ok_opt(nsel) || !ok_opt(tau)) return fail(DASH_EINVAL, "lse/nsel/tau must be 16-byte aligned");
@@ -302,7 +309,10 @@ dash_status dash_decode(const dash_decode_params* p, const void* q, const void* 
   da.sel_blk = reinterpret_cast<int*>(ws + off[3]);
   da.sel_lp = reinterpret_cast<float*>(ws + off[4]);
   da.part = reinterpret_cast<float*>(ws + off[5]);
+  da.len = len;
+  da.len_add = len_add;
   da.SH = p->S * p->H;
+  da.H = p->H;
   da.N = p->N;
   da.D = p->D;
   da.nsplit = nsplit;
@@ -311,6 +321,69 @@ dash_status dash_decode(const dash_decode_params* p, const void* q, const void* 
   da.ca = make_ca(p->alpha, p->coarse_scale);
   hipError_t e = launch_decode(da, p->dtype, (hipStream_t)stream);
   return e == hipSuccess ? DASH_OK : hip_fail(e, "decode");
+}
+
+static dash_status append_common(const dash_decode_params* p, const void* k_new, const void* v_new,
+                                 const int32_t* len, void* kc, void* vc, void* kbar, void* stream) {
+  if (!ok_ptr(k_new) || !ok_ptr(v_new) || !ok_ptr(kc) || !ok_ptr(vc) || !ok_ptr(kbar))
+    return fail(DASH_EINVAL, "k_new, v_new, kc, vc and kbar must be non-null and 16-byte aligned");
+  if (!len || reinterpret_cast<uintptr_t>(len) % 4) return fail(DASH_EINVAL, "len must be non-null and 4-byte aligned");
+  AppendArgs aa;
+  aa.k_new = k_new;
+  aa.v_new = v_new;
+  aa.len = len;
+  aa.kc = kc;
+  aa.vc = vc;
+  aa.kbar = kbar;
+  aa.SH = p->S * p->H;
+  aa.H = p->H;
+  aa.N = p->N;
+  aa.D = p->D;
+  hipError_t e = launch_append(aa, p->dtype, (hipStream_t)stream);
+  return e == hipSuccess ? DASH_OK : hip_fail(e, "cache append");
+}
+
+dash_status dash_decode(const dash_decode_params* p, const void* q, const void* kc, const void* vc,
+                        const void* kbar, void* o, float* lse, int32_t* nsel, float* tau, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  dash_status s = check_decode_params(p);
+  if (s != DASH_OK) return s;
+  return decode_common(p, q, kc, vc, kbar, nullptr, 0, o, lse, nsel, tau, workspace, workspace_bytes, stream);
+}
+
+dash_status dash_cache_append(const dash_decode_params* p, const void* k_new, const void* v_new,
+                              const int32_t* len, void* kc, void* vc, void* kbar, void* stream) {
+  dash_status s = check_decode_params(p);
+  if (s != DASH_OK) return s;
+  return append_common(p, k_new, v_new, len, kc, vc, kbar, stream);
+}
+
+dash_status dash_decode_varlen(const dash_decode_params* p, const void* q, const void* kc, const void* vc,
+                               const void* kbar, const int32_t* len, void* o, float* lse, int32_t* nsel,
+                               float* tau, void* workspace, size_t workspace_bytes, void* stream) {
+  dash_status s = check_decode_params(p);
+  if (s != DASH_OK) return s;
+  if (!len || reinterpret_cast<uintptr_t>(len) % 4) return fail(DASH_EINVAL, "len must be non-null and 4-byte aligned");
+  return decode_common(p, q, kc, vc, kbar, len, 0, o, lse, nsel, tau, workspace, workspace_bytes, stream);
+}
+
+dash_status dash_decode_step(const dash_decode_params* p, const void* q, const void* k_new, const void* v_new,
+                             const int32_t* len, void* kc, void* vc, void* kbar, void* o, float* lse,
+                             int32_t* nsel, float* tau, void* workspace, size_t workspace_bytes, void* stream) {
+  dash_status s = check_decode_params(p);
+  if (s != DASH_OK) return s;
+  // validate both halves before launching either
+  if (!ok_ptr(q) || !ok_ptr(o)) return fail(DASH_EINVAL, "q and o must be non-null and 16-byte aligned");
+  if (!ok_opt(lse) || !ok_opt(nsel) || !ok_opt(tau)) return fail(DASH_EINVAL, "lse/nsel/tau must be 16-byte aligned");
+  size_t off[6];
+  if (workspace_bytes < decode_ws_layout(p, off, nullptr, nullptr))
+    return fail(DASH_EWORKSPACE, "workspace of %zu bytes needed, %zu given", decode_ws_layout(p, off, nullptr, nullptr),
+                workspace_bytes);
+  if (!ok_ptr(workspace)) return fail(DASH_EINVAL, "workspace must be non-null and 16-byte aligned");
+  if ((s = append_common(p, k_new, v_new, len, kc, vc, kbar, stream)) != DASH_OK) return s;
+  // rows whose length was out of range for the append (len < 0 or >= N)
+  // are out of range here too (len + 1 < 1 or > N): NaN outputs
+  return decode_common(p, q, kc, vc, kbar, len, 1, o, lse, nsel, tau, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

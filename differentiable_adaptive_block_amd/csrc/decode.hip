@@ -1,10 +1,18 @@
 // Decode: one new query per (sequence, head) against a long KV cache
 // (the pages' decoding path; their speed claim is at 96K context with
 // 93.75% block sparsity, "The numbers" on the montana-research page).
-// The new token is the last cached token, so the query's candidates are
-// blocks 0..nb-2 and block nb-1 is attended whole with prior 0.
+// The new token is the last cached token.  A row whose cache holds n tokens
+// (n = the capacity N, or a length per sequence) has its query at n-1: its
+// candidates are the complete blocks 0..own-1, own = (n-1)/64, and its own
+// block is attended over its cached tokens with prior 0.
 //
-// Three kernels, all HBM-bound:
+// Cache maintenance, decode_append: one wave per row writes the new key and
+// value at position len and, when that completes a block, the block's
+// summary (the decoding path keeps one summary per 64-token chunk of the
+// cache; chunk-summarise stage of the code samples listed by the
+// codewithpapers.app entry for the DashAttention paper).
+//
+// Three decode kernels, all HBM-bound:
 //   decode_select   one 8-wave workgroup per row: u = (alpha-1) * coarse_scale
 //                   * q.kbar_b for every candidate (coalesced GEMV over the
 //                   summaries, loads of the next chunk in flight),
@@ -45,11 +53,21 @@ __global__ __launch_bounds__(512) void decode_select_kernel(DecodeArgs a) {
   constexpr int PER = NW * 4 * UN;    // summaries per chunk
   __shared__ float us[NPL * 64];
   const int row = blockIdx.x;
-  const int nb = a.N / DASH_BLOCK;
-  const int nc = nb - 1;
+  const int nbc = a.N / DASH_BLOCK;  // capacity in blocks: row stride of the summaries and the lists
+  const int n = decode_row_len(a, row);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  if (n < 1 || n > a.N) {  // length out of range: empty list; the combine writes NaN
+    if (tid == 0) {
+      a.sel_cnt[row] = 0;
+      if (a.nsel) a.nsel[row] = -1;
+      if (a.tau_out) a.tau_out[row] = __uint_as_float(0x7fc00000u);
+    }
+    return;
+  }
+  const int own = (n - 1) / DASH_BLOCK;  // the query's block
+  const int nc = own;                    // the complete blocks before it are the candidates
   const bf16_t* q = reinterpret_cast<const bf16_t*>(a.q) + (size_t)row * D;
-  const bf16_t* kb = reinterpret_cast<const bf16_t*>(a.kbar) + (size_t)row * nb * D;
+  const bf16_t* kb = reinterpret_cast<const bf16_t*>(a.kbar) + (size_t)row * nbc * D;
   const CoarseArith ca = a.ca;
   float qf[8];
   unpack8(*reinterpret_cast<const uint4*>(q + (l & 15) * 8), qf);
@@ -97,8 +115,8 @@ __global__ __launch_bounds__(512) void decode_select_kernel(DecodeArgs a) {
   EntmaxOut e;
   if (nc > 0) e = entmax_solve<NPL, 64>(u, nc, ca);
   else { e.tau = __uint_as_float(0x7fc00000u); e.lognorm = 0.f; e.nsel = 0; }
-  int* list = a.sel_blk + (size_t)row * nb;
-  float* lp = a.sel_lp + (size_t)row * nb;
+  int* list = a.sel_blk + (size_t)row * nbc;
+  float* lp = a.sel_lp + (size_t)row * nbc;
   int base = 0;
 #pragma unroll
   for (int k = 0; k < NPL; ++k) {
@@ -113,7 +131,7 @@ __global__ __launch_bounds__(512) void decode_select_kernel(DecodeArgs a) {
     base += __popcll(bal);
   }
   if (l == 0) {
-    list[base] = nb - 1;  // the query's own block, prior 0
+    list[base] = own;  // the query's own block, prior 0
     lp[base] = 0.f;
     a.sel_cnt[row] = base + 1;
     a.rowstat[2 * row] = e.tau;
@@ -130,12 +148,13 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(DecodeArgs a) {
   __shared__ float red_m[4], red_l[4];
   __shared__ float red_o[4][D];
   const int split = blockIdx.x, row = blockIdx.y;
-  const int nb = a.N / DASH_BLOCK;
+  const int nbc = a.N / DASH_BLOCK;
+  const int n = decode_row_len(a, row);  // in range whenever the list is not empty
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int g = l >> 4, c = l & 15;  // key group within a 1 KB load, 16-byte chunk
   const int cnt = a.sel_cnt[row];
-  const int* list = a.sel_blk + (size_t)row * nb;
-  const float* lpl = a.sel_lp + (size_t)row * nb;
+  const int* list = a.sel_blk + (size_t)row * nbc;
+  const float* lpl = a.sel_lp + (size_t)row * nbc;
   const bf16_t* K = reinterpret_cast<const bf16_t*>(a.kc) + (size_t)row * a.N * D;
   const bf16_t* V = reinterpret_cast<const bf16_t*>(a.vc) + (size_t)row * a.N * D;
   const float sl2 = a.fine_scale * LOG2E_F;
@@ -175,6 +194,17 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) part = fmaf(qf[e], kf[e], part);
       s[it] = sum16(part) * sl2 + pr;  // key it*4 + g, identical in the 16 lanes of group g
+    }
+    if ((b + 1) * DASH_BLOCK > n) {
+      // the query's own block, partly filled: positions from n on hold no
+      // token (whatever their bits), so they get weight 0 and value 0
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        if (b * DASH_BLOCK + it * 4 + g >= n) {
+          s[it] = -INFINITY;
+          vr[it] = make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
     }
     float mx = s[0];
 #pragma unroll
@@ -235,6 +265,14 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= a.SH) return;
   const int l = threadIdx.x & 63;
+  bf16_t* O = reinterpret_cast<bf16_t*>(a.o) + (size_t)row * D;
+  if (a.sel_cnt[row] <= 0) {  // length out of range (a valid row lists its own block)
+    const bf16_t qnan = 0x7FC0u;
+    O[l] = qnan;
+    O[l + 64] = qnan;
+    if (l == 0 && a.lse) a.lse[row] = __uint_as_float(0x7fc00000u);
+    return;
+  }
   const float* part = a.part + (size_t)row * NS * (D + 2);
   const float ms = l < NS ? part[l * (D + 2) + D] : -INFINITY;
   const float ls = l < NS ? part[l * (D + 2) + D + 1] : 0.f;
@@ -249,11 +287,52 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     o0 = fmaf(part[s * (D + 2) + l], scs, o0);
     o1 = fmaf(part[s * (D + 2) + l + 64], scs, o1);
   }
-  bf16_t* O = reinterpret_cast<bf16_t*>(a.o) + (size_t)row * D;
   const float inv = L > 0.f ? 1.f / L : 0.f;
   O[l] = f2bf(o0 * inv);
   O[l + 64] = f2bf(o1 * inv);
   if (l == 0 && a.lse) a.lse[row] = (M + __log2f(L)) * LN2_F;
+}
+
+// ---------------------------------------------------------------------------- cache maintenance
+
+// One wave per row, 4 rows per workgroup; lane l moves elements 2l and 2l+1
+// (one 4-byte bf16 pair) of the new key and value to position len.  When the
+// token completes its block, the same lane also forms the block's summary
+// for its two elements: the 63 cached keys and the new one summed in fp64
+// in position order, times 1/64, rounded once, which is the arithmetic of
+// the Stage-0 pool kernel.
+__global__ __launch_bounds__(256) void decode_append_kernel(AppendArgs a) {
+  constexpr int D = 128, W = D / 2;  // 32-bit words per row
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.SH) return;
+  const int l = threadIdx.x & 63;
+  const int n = a.len[row / a.H];
+  if (n < 0 || n >= a.N) return;  // full cache or length out of range: nothing written
+  const uint32_t kw = reinterpret_cast<const uint32_t*>(a.k_new)[(size_t)row * W + l];
+  const uint32_t vw = reinterpret_cast<const uint32_t*>(a.v_new)[(size_t)row * W + l];
+  uint32_t* kc = reinterpret_cast<uint32_t*>(a.kc) + (size_t)row * a.N * W;
+  uint32_t* vc = reinterpret_cast<uint32_t*>(a.vc) + (size_t)row * a.N * W;
+  kc[(size_t)n * W + l] = kw;
+  vc[(size_t)n * W + l] = vw;
+  if (n % DASH_BLOCK != DASH_BLOCK - 1) return;
+  const int b = n / DASH_BLOCK;
+  const uint32_t* blk = kc + (size_t)b * DASH_BLOCK * W;
+  double s0 = 0.0, s1 = 0.0;
+  for (int r = 0; r < DASH_BLOCK - 1; ++r) {
+    const uint32_t x = blk[(size_t)r * W + l];
+    s0 += (double)bf2f((bf16_t)(x & 0xFFFFu));
+    s1 += (double)bf2f((bf16_t)(x >> 16));
+  }
+  s0 += (double)bf2f((bf16_t)(kw & 0xFFFFu));
+  s1 += (double)bf2f((bf16_t)(kw >> 16));
+  const uint32_t m0 = d2bf(s0 * (1.0 / DASH_BLOCK)), m1 = d2bf(s1 * (1.0 / DASH_BLOCK));
+  reinterpret_cast<uint32_t*>(a.kbar)[((size_t)row * (a.N / DASH_BLOCK) + b) * W + l] = m0 | (m1 << 16);
+}
+
+hipError_t launch_append(const AppendArgs& a, int dtype, hipStream_t st) {
+  if (dtype != 1 || a.D != 128) return hipErrorNotSupported;
+  decode_append_kernel<<<(a.SH + 3) / 4, 256, 0, st>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a0, int dtype, hipStream_t st) {

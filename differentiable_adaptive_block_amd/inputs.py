@@ -154,14 +154,19 @@ def make_prefill(B, H, T, D, dtype="bf16", causal=True, planted=(1, 8), seed=0, 
     return out
 
 
-def make_decode(S, H, N, D, dtype="bf16", planted=(1, 16), seed=0, device="cpu"):
+def make_decode(S, H, N, D, dtype="bf16", planted=(1, 16), seed=0, device="cpu", lens=None, beyond=None):
     """Decode workload: q [S, H, D] and caches k, v [S, H, N, D].
 
-    The new token is the last cached token (position N-1); planted blocks
-    are drawn among the candidates 0..N/64-2.
+    The new token is the last cached token: position N-1, or lens[s]-1 when
+    a list of per-sequence lengths is given (N is then the capacity).
+    Planted blocks are drawn among the query's candidates, the complete
+    blocks before its own.  ``beyond`` (a float, e.g. NaN) overwrites the
+    cache entries at positions >= lens[s] after everything is drawn.
     """
     if N % BLOCK:
         raise ValueError("N must be a multiple of 64")
+    if lens is not None and (len(lens) != S or min(lens) < 1 or max(lens) > N):
+        raise ValueError("lens must hold S lengths in [1, N]")
     td = torch_dtype(dtype)
     g = _gen(seed, device)
     kc = torch.empty((S, H, N, D), dtype=td, device=device)
@@ -171,8 +176,8 @@ def make_decode(S, H, N, D, dtype="bf16", planted=(1, 16), seed=0, device="cpu")
     for s in range(S):
         vc[s] = _randn((H, N, D), g, td, device, chunk_rows=4)
     q = torch.empty((S, H, D), dtype=td, device=device)
-    pos = torch.tensor([N - 1], device=device)
     for s in range(S):
+        pos = torch.tensor([(N if lens is None else int(lens[s])) - 1], device=device)
         for h in range(H):
             noise = torch.randn((1, D), generator=g, dtype=torch.float32, device=device).double()
             if planted is None:
@@ -180,6 +185,10 @@ def make_decode(S, H, N, D, dtype="bf16", planted=(1, 16), seed=0, device="cpu")
             else:
                 qp = 0.5 * noise + _planted_rows(kc[s, h], pos, True, planted[0], planted[1], g, device)
             q[s, h] = qp[0].float().to(td)
+    if lens is not None and beyond is not None:
+        for s in range(S):
+            kc[s, :, int(lens[s]):] = beyond
+            vc[s, :, int(lens[s]):] = beyond
     return dict(q=q, k=kc, v=vc)
 
 

@@ -173,6 +173,63 @@ dash_status dash_decode(const dash_decode_params* p, const void* q, const void* 
                         int32_t* nsel, float* tau, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/*
+ * Decode cache maintenance and caches of any length (the decoding path keeps
+ * one summary per 64-token chunk of the cache: the chunk-summarise stage
+ * among the code samples that the codewithpapers.app entry "DashAttention:
+ * Differentiable and Adaptive Sparse Hierarchical Attention" lists).
+ *
+ * In the three calls below p->N is the cache CAPACITY C (a multiple of 64,
+ * 64 <= C <= 131072): kc, vc are [S,H,C,D], kbar [S,H,C/64,D], all dtype.
+ * len is a DEVICE array of S int32: the number of tokens sequence s holds.
+ * The library only reads len; the caller advances it.  Values are checked
+ * on the device, not the host: a sequence whose length is out of range gets
+ * the behaviour stated for each call, and no memory outside the caches is
+ * touched.
+ */
+
+/*
+ * Append one token per (sequence, head): kc[s,h,len[s],:] = k_new[s,h,:] and
+ * vc likewise (k_new, v_new [S,H,D]).  When position len[s] is the last of
+ * its block (len[s] % 64 == 63), that block is complete and
+ * kbar[s,h,len[s]/64,:] becomes the mean of its 64 keys, summed in fp64 and
+ * rounded once, bit-identical to dash_pool.  Summaries of incomplete blocks
+ * are not written; for a cache filled by a prefill, dash_pool over the
+ * whole capacity (T = C) gives the complete blocks' summaries, and the
+ * entries of incomplete ones are ignored until an append completes them.
+ * A sequence with len[s] < 0 or len[s] >= C is left unchanged.
+ */
+dash_status dash_cache_append(const dash_decode_params* p, const void* k_new, const void* v_new,
+                              const int32_t* len, void* kc, void* vc, void* kbar, void* stream);
+
+/*
+ * Decode with a length per sequence: sequence s holds n = len[s] tokens, the
+ * new one (whose query is q[s,h]) at position n-1, already appended.  The
+ * result is row n-1 of a causal prefill over the first n tokens: candidates
+ * are the complete blocks 0..(n-1)/64-1, and the query's own block is
+ * attended over its n - 64*((n-1)/64) cached tokens with prior 0.  Cache
+ * entries at positions >= n and summaries of blocks >= (n-1)/64 are never
+ * read.  Outputs as dash_decode; a sequence with len[s] < 1 or len[s] > C
+ * gets o = NaN, lse = NaN, nsel = -1 and tau = NaN.  Workspace: as
+ * dash_decode for the same params.
+ */
+dash_status dash_decode_varlen(const dash_decode_params* p, const void* q, const void* kc,
+                               const void* vc, const void* kbar, const int32_t* len, void* o,
+                               float* lse, int32_t* nsel, float* tau, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
+ * One serving step: dash_cache_append of (k_new, v_new) at len[s], then
+ * dash_decode_varlen over len[s] + 1 tokens, in stream order.  len is not
+ * advanced.  Same outputs and workspace as dash_decode_varlen; a sequence
+ * with len[s] < 0 or len[s] >= C is neither appended nor decoded (NaN
+ * outputs, nsel = -1).
+ */
+dash_status dash_decode_step(const dash_decode_params* p, const void* q, const void* k_new,
+                             const void* v_new, const int32_t* len, void* kc, void* vc, void* kbar,
+                             void* o, float* lse, int32_t* nsel, float* tau, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* Message of the last failing call on this thread ("" if none). */
 const char* dash_last_error(void);
 

@@ -143,3 +143,48 @@ def test_pool_accepts_long_sequences_in_validation(L):
     # null k is rejected after the shape checks pass (no 65536 limit for pooling)
     assert L.dash_pool(ctypes.byref(p), None, FAKE, None) == _lib.DASH_EINVAL
     assert "k and kbar" in L.dash_last_error().decode()
+
+
+def _dparams(**kw):
+    p = _lib.DashDecodeParams()
+    p.S, p.H, p.N, p.D, p.block = 2, 2, 1024, 128, 64
+    p.alpha, p.fine_scale, p.coarse_scale, p.dtype = 1.5, 0.088, 0.088, _lib.DASH_BF16
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_cache_append_validation(L):
+    p = _dparams()
+    # k_new, v_new, len, kc, vc, kbar
+    assert L.dash_cache_append(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == _lib.DASH_EINVAL
+    assert "len" in L.dash_last_error().decode()
+    assert L.dash_cache_append(ctypes.byref(p), FAKE, FAKE, FAKE + 2, FAKE, FAKE, FAKE, None) == _lib.DASH_EINVAL
+    assert L.dash_cache_append(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == _lib.DASH_EINVAL
+    assert L.dash_cache_append(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 8, None) == _lib.DASH_EINVAL
+    assert L.dash_cache_append(ctypes.byref(_dparams(N=1000)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == _lib.DASH_EINVAL
+    assert L.dash_cache_append(ctypes.byref(_dparams(dtype=_lib.DASH_F32)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               None) == _lib.DASH_EUNSUPPORTED
+
+
+def test_decode_varlen_and_step_validation(L):
+    p = _dparams()
+    need = L.dash_decode_workspace_bytes(ctypes.byref(p))
+    # q, kc, vc, kbar, len, o, lse, nsel, tau, ws
+    args = [FAKE] * 6 + [None, None, None, FAKE]
+    assert L.dash_decode_varlen(ctypes.byref(p), *args, need - 1, None) == _lib.DASH_EWORKSPACE
+    bad = list(args)
+    bad[4] = None
+    assert L.dash_decode_varlen(ctypes.byref(p), *bad, need, None) == _lib.DASH_EINVAL
+    assert "len" in L.dash_last_error().decode()
+    assert L.dash_decode_varlen(ctypes.byref(_dparams(N=64 * 4096)), *args, need, None) == _lib.DASH_EUNSUPPORTED
+    # q, k_new, v_new, len, kc, vc, kbar, o, lse, nsel, tau, ws
+    sargs = [FAKE] * 8 + [None, None, None, FAKE]
+    assert L.dash_decode_step(ctypes.byref(p), *sargs, need - 1, None) == _lib.DASH_EWORKSPACE
+    bad = list(sargs)
+    bad[1] = None
+    assert L.dash_decode_step(ctypes.byref(p), *bad, need, None) == _lib.DASH_EINVAL
+    bad = list(sargs)
+    bad[7] = None
+    assert L.dash_decode_step(ctypes.byref(p), *bad, need, None) == _lib.DASH_EINVAL
+    assert L.dash_decode_step(ctypes.byref(_dparams(D=64)), *sargs, need, None) == _lib.DASH_EUNSUPPORTED

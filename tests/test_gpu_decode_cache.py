@@ -1,0 +1,249 @@
+"""GPU parity of decode cache maintenance and per-sequence cache lengths.
+
+dash_cache_append, dash_decode_varlen and dash_decode_step (through the C
+ABI) against the float64 oracle's cache_append and decode_varlen.  Cache
+entries past each sequence's length hold NaN, so any read of them would
+show in the outputs.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from differentiable_adaptive_block_amd import inputs
+from parity import TIE_BAND, tol_lse, tol_out
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+D = 128
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _np64(t):
+    return t.double().cpu().numpy()
+
+
+def _sel_fn(q64, kc64, lens, prm):
+    """Oracle Stage-1 result of row (s, h), for the tie band."""
+    def f(s, h):
+        n = int(lens[s])
+        own = (n - 1) // 64
+        kb = oracle.pool_blocks(kc64[s, h, :64 * own], 64, "bf16")
+        return oracle.select_row(q64[s, h], kb, n - 1, prm, D)
+    return f
+
+
+def _compare(out, ora, rows, prm, what, sel_of):
+    """GPU decode outputs vs oracle decode_varlen results on rows (s, h)."""
+    max_abs, mean_abs = tol_out(torch.bfloat16)
+    errs = []
+    for (s, h) in rows:
+        errs.append(np.abs(_np64(out["o"][s, h]) - ora["o"][s, h]))
+        assert abs(float(out["lse"][s, h]) - ora["lse"][s, h]) <= tol_lse(torch.bfloat16), (what, s, h)
+        ns, nso = int(out["nsel"][s, h]), int(ora["nsel"][s, h])
+        if ns != nso:
+            # selected counts may differ only by candidates within the tie band
+            sel = sel_of(s, h)
+            near = np.abs((prm.alpha - 1.0) * sel["z"] - sel["tau"]) <= TIE_BAND
+            assert abs(ns - nso) <= int(near.sum()), (what, s, h, ns, nso)
+        t, to = float(out["tau"][s, h]), float(ora["tau"][s, h])
+        if math.isnan(to):
+            assert math.isnan(t), (what, s, h, t)
+        else:
+            assert abs(t - to) <= 4e-6 * max(1.0, abs(to)), (what, s, h, t, to)
+    E = np.stack(errs)
+    assert E.max() <= max_abs and E.mean() <= mean_abs, (what, E.max(), E.mean())
+    return float(E.max()), float(E.mean())
+
+
+LENS = [1, 2, 63, 64, 65, 127, 128, 129, 700, 1000, 1023, 1024]
+
+
+def test_decode_varlen_small():
+    from differentiable_adaptive_block_amd import api
+    S, H, C = len(LENS), 3, 1024
+    _say(f"[decode varlen] S{S} H{H} capacity {C} lens {LENS}")
+    w = inputs.make_decode(S, H, C, D, "bf16", (1, 4), seed=31, device="cpu", lens=LENS, beyond=float("nan"))
+    q, kc, vc = (w[x].to(DEV) for x in ("q", "k", "v"))
+    kbar = api.pool(kc.view(1, S * H, C, D)).view(S, H, C // 64, D)  # NaN where a block holds no token
+    lens = torch.tensor(LENS, dtype=torch.int32, device=DEV)
+    cs = 4.0 / math.sqrt(D)
+    out = api.decode_varlen(q, kc, vc, kbar, lens, alpha=1.5, coarse_scale=cs)
+    torch.cuda.synchronize()
+    prm = oracle.Params(alpha=1.5, causal=True, coarse_scale=cs, storage="bf16")
+    ora = oracle.decode_varlen(_np64(q), _np64(kc), _np64(vc), np.array(LENS), prm)
+    assert torch.isfinite(out["o"].float()).all()
+    st = _compare(out, ora, [(s, h) for s in range(S) for h in range(H)], prm, "varlen",
+                  _sel_fn(_np64(q), _np64(kc), LENS, prm))
+    _say(f"  ok max/mean abs {st}")
+
+
+def test_decode_varlen_full_lengths_equal_fixed_decode():
+    from differentiable_adaptive_block_amd import api
+    S, H, C = 2, 4, 2048
+    w = inputs.make_decode(S, H, C, D, "bf16", (1, 4), seed=32, device="cpu")
+    q, kc, vc = (w[x].to(DEV) for x in ("q", "k", "v"))
+    kbar = api.pool(kc.view(1, S * H, C, D)).view(S, H, C // 64, D)
+    cs = 3.0 / math.sqrt(D)
+    a = {k: v.clone() for k, v in api.decode(q, kc, vc, kbar, coarse_scale=cs).items()}
+    b = api.decode_varlen(q, kc, vc, kbar, torch.full((S,), C, dtype=torch.int32, device=DEV), coarse_scale=cs)
+    torch.cuda.synchronize()
+    for key in ("o", "lse", "nsel", "tau"):
+        assert torch.equal(a[key], b[key]), key
+
+
+def test_decode_varlen_out_of_range_lengths():
+    from differentiable_adaptive_block_amd import api
+    S, H, C = 4, 2, 256
+    w = inputs.make_decode(S, H, C, D, "bf16", (1, 4), seed=33, device="cpu")
+    q, kc, vc = (w[x].to(DEV) for x in ("q", "k", "v"))
+    kbar = api.pool(kc.view(1, S * H, C, D)).view(S, H, C // 64, D)
+    lens = torch.tensor([0, 200, C + 1, -7], dtype=torch.int32, device=DEV)
+    out = api.decode_varlen(q, kc, vc, kbar, lens)
+    torch.cuda.synchronize()
+    for s in (0, 2, 3):
+        assert torch.isnan(out["o"][s].float()).all() and torch.isnan(out["lse"][s]).all()
+        assert (out["nsel"][s] == -1).all() and torch.isnan(out["tau"][s]).all()
+    prm = oracle.Params(alpha=1.5, causal=True, storage="bf16")
+    ora = oracle.decode_varlen(_np64(q[1:2]), _np64(kc[1:2]), _np64(vc[1:2]), np.array([200]), prm)
+    got = {k: v[1:2] for k, v in out.items()}
+    _compare(got, ora, [(0, h) for h in range(H)], prm, "in-range row",
+             _sel_fn(_np64(q[1:2]), _np64(kc[1:2]), [200], prm))
+
+
+def test_cache_append_matches_oracle():
+    from differentiable_adaptive_block_amd import api
+    S, H, C = 5, 2, 320
+    lens0 = [0, 37, 63, 64, C - 3]
+    _say(f"[cache append] S{S} H{H} capacity {C} start {lens0}")
+    w = inputs.make_decode(S, H, C, D, "bf16", None, seed=34, device="cpu")
+    kc, vc = w["k"].to(DEV), w["v"].to(DEV)
+    kbar = api.pool(kc.view(1, S * H, C, D)).view(S, H, C // 64, D)
+    kc_o, vc_o, kbar_o = _np64(kc), _np64(vc), _np64(kbar)
+    lens = torch.tensor(lens0, dtype=torch.int32, device=DEV)
+    lens_o = np.array(lens0)
+    g = torch.Generator().manual_seed(35)
+    prm = oracle.Params(storage="bf16")
+    for step in range(140):
+        kn = torch.randn((S, H, D), generator=g).to(torch.bfloat16)
+        vn = torch.randn((S, H, D), generator=g).to(torch.bfloat16)
+        api.cache_append(kc, vc, kbar, lens, kn.to(DEV), vn.to(DEV))
+        live = lens_o < C  # the oracle rejects full caches; the library leaves them unchanged
+        if live.any():
+            idx = np.flatnonzero(live)
+            k2, v2, kb2, l2 = oracle.cache_append(kc_o[idx], vc_o[idx], kbar_o[idx], lens_o[idx],
+                                                  kn.double().numpy()[idx], vn.double().numpy()[idx], prm)
+            kc_o[idx], vc_o[idx], kbar_o[idx], lens_o[idx] = k2, v2, kb2, l2
+        lens += (lens < C).to(torch.int32)
+    torch.cuda.synchronize()
+    assert lens.cpu().tolist() == [min(C, x + 140) for x in lens0] == lens_o.tolist()
+    np.testing.assert_array_equal(_np64(kc), kc_o)
+    np.testing.assert_array_equal(_np64(vc), vc_o)
+    np.testing.assert_array_equal(_np64(kbar), kbar_o)
+    # the blocks completed by appends hold the Stage-0 means of the final cache
+    for s in range(S):
+        for b in range(C // 64):
+            if 64 * b + 63 >= lens0[s] and 64 * b + 64 <= int(lens_o[s]):
+                for h in range(H):
+                    np.testing.assert_array_equal(_np64(kbar[s, h, b]),
+                                                  oracle.pool_blocks(kc_o[s, h, 64 * b:64 * b + 64], 64, "bf16")[0])
+
+
+def test_decode_step_sequence():
+    from differentiable_adaptive_block_amd import api
+    S, H, C = 3, 2, 256
+    lens0 = [0, 60, 120]
+    _say(f"[decode step] S{S} H{H} capacity {C} start {lens0}, 75 steps")
+    w = inputs.make_decode(S, H, C, D, "bf16", None, seed=36, device="cpu", lens=[max(1, x) for x in lens0],
+                           beyond=float("nan"))
+    kc, vc = w["k"].to(DEV), w["v"].to(DEV)
+    kbar = api.pool(kc.view(1, S * H, C, D)).view(S, H, C // 64, D)
+    kc_o, vc_o, kbar_o = _np64(kc), _np64(vc), _np64(kbar)
+    lens = torch.tensor(lens0, dtype=torch.int32, device=DEV)
+    lens_o = np.array(lens0)
+    cs = 6.0 / math.sqrt(D)
+    prm = oracle.Params(alpha=1.5, causal=True, coarse_scale=cs, storage="bf16")
+    g = torch.Generator().manual_seed(37)
+    bufs = None
+    worst = 0.0
+    for step in range(75):
+        kn = torch.randn((S, H, D), generator=g).to(torch.bfloat16)
+        vn = torch.randn((S, H, D), generator=g).to(torch.bfloat16)
+        # queries that lean toward one earlier block of their own cache
+        q = 0.5 * torch.randn((S, H, D), generator=g)
+        for s in range(S):
+            nb_done = int(lens_o[s]) // 64
+            if nb_done:
+                b = int(torch.randint(0, nb_done, (1,), generator=g))
+                kbd = torch.from_numpy(kc_o[s, :, 64 * b:64 * b + 64].mean(axis=1))
+                q[s] += (kbd / kbd.norm(dim=-1, keepdim=True)).float()
+        q = q.to(torch.bfloat16)
+        if bufs is None:
+            bufs = api.DecodeBuffers(api.make_decode_params(q.to(DEV), kc, 1.5, None, cs), torch.bfloat16, DEV)
+        out = api.decode_step(q.to(DEV), kn.to(DEV), vn.to(DEV), kc, vc, kbar, lens, coarse_scale=cs, bufs=bufs)
+        kc_o, vc_o, kbar_o, lens_o = oracle.cache_append(kc_o, vc_o, kbar_o, lens_o, kn.double().numpy(),
+                                                         vn.double().numpy(), prm)
+        ora = oracle.decode_varlen(q.double().numpy(), kc_o, vc_o, lens_o, prm, kbar=kbar_o)
+        torch.cuda.synchronize()
+        st = _compare(out, ora, [(s, h) for s in range(S) for h in range(H)], prm, f"step {step}",
+                      _sel_fn(q.double().numpy(), kc_o, lens_o, prm))
+        worst = max(worst, st[0])
+        lens += 1
+    np.testing.assert_array_equal(_np64(kbar)[np.isfinite(kbar_o)], kbar_o[np.isfinite(kbar_o)])
+    _say(f"  ok worst max-abs {worst:.3g}")
+
+
+@pytest.mark.parametrize("name", ["c4cal"])
+def test_decode_step_96k_ragged_sampled(name):
+    from differentiable_adaptive_block_amd import api
+    wl = inputs.CONFIGS[name]
+    sh = wl.shape
+    S, H, C = sh["S"], sh["H"], sh["N"]
+    rng = np.random.default_rng(38)
+    lens0 = sorted(int(x) for x in rng.integers(C // 2, C, S))
+    lens0[0], lens0[-1] = 64 * 700 - 1, C - 1  # a step that completes a block; the last free slot
+    _say(f"[decode step] {name} capacity {C}, ragged lengths {lens0[:4]}...")
+    w = inputs.make_decode(S, H, C, D, wl.dtype, wl.planted, wl.seed, device=DEV, lens=[x + 1 for x in lens0])
+    q, kc, vc = w["q"], w["k"], w["v"]
+    kbar = api.pool(kc.view(1, S * H, C, D)).view(S, H, C // 64, D)
+    # the new tokens are the ones the generator put at position lens0[s]
+    kn = torch.stack([kc[s, :, lens0[s]] for s in range(S)]).contiguous()
+    vn = torch.stack([vc[s, :, lens0[s]] for s in range(S)]).contiguous()
+    for s in range(S):
+        kc[s, :, lens0[s]:] = float("nan")
+        vc[s, :, lens0[s]:] = float("nan")
+        kbar[s, :, lens0[s] // 64:] = float("nan")  # incomplete blocks: no summary yet
+    lens = torch.tensor(lens0, dtype=torch.int32, device=DEV)
+    out = api.decode_step(q, kn, vn, kc, vc, kbar, lens, alpha=wl.alpha, coarse_scale=wl.coarse_scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out["o"].float()).all()
+    prm = oracle.Params(alpha=wl.alpha, causal=True, coarse_scale=wl.coarse_scale, storage="bf16")
+    rows = [(0, 3), (S - 1, 7)] + [(int(s), int(h)) for s, h in zip(rng.integers(0, S, 4), rng.integers(0, H, 4))]
+    max_abs, mean_abs = tol_out(torch.bfloat16)
+    errs = []
+    for (s, h) in rows:
+        n = lens0[s] + 1
+        k64, v64 = _np64(kc[s, h, :n]), _np64(vc[s, h, :n])
+        ora = oracle.decode_varlen(_np64(q[s, h])[None, None], k64[None, None], v64[None, None], np.array([n]), prm)
+        errs.append(np.abs(_np64(out["o"][s, h]) - ora["o"][0, 0]))
+        assert abs(float(out["lse"][s, h]) - ora["lse"][0, 0]) <= tol_lse(torch.bfloat16)
+        if int(out["nsel"][s, h]) != int(ora["nsel"][0, 0]):
+            sel = _sel_fn(_np64(q[s, h])[None, None], k64[None, None], [n], prm)(0, 0)
+            near = np.abs((prm.alpha - 1.0) * sel["z"] - sel["tau"]) <= TIE_BAND
+            assert abs(int(out["nsel"][s, h]) - int(ora["nsel"][0, 0])) <= int(near.sum())
+    E = np.stack(errs)
+    assert E.max() <= max_abs and E.mean() <= mean_abs, (E.max(), E.mean())
+    # the block completed by this step has its summary
+    b = lens0[0] // 64
+    np.testing.assert_array_equal(_np64(kbar[0, :, b]),
+                                  np.stack([oracle.pool_blocks(_np64(kc[0, h, 64 * b:64 * b + 64]), 64, "bf16")[0]
+                                            for h in range(H)]))
+    _say(f"  ok max/mean abs {E.max():.3g}/{E.mean():.3g}; mean nsel {float(out['nsel'].double().mean()):.1f}")
