@@ -320,6 +320,63 @@ def bench_decode(name, steps, warmup, device):
     return res
 
 
+def bench_decode_step(name, steps, warmup, device):
+    """Time dash_decode_step (append the new token, then decode) on a named decode
+    workload's shape with a different cache length per sequence; lens advances
+    by one after every step, as in a serving loop."""
+    from differentiable_adaptive_block_amd import _lib, api, inputs
+
+    wl = inputs.CONFIGS[name]
+    sh = wl.shape
+    S, H, C, D = sh["S"], sh["H"], sh["N"], sh["D"]
+    g = torch.Generator().manual_seed(wl.seed + 200)
+    # lengths before the first step: uniform in [C/2, C - 64 - steps - warmup]
+    hi = C - 64 - steps - warmup
+    lens0 = torch.randint(C // 2, hi + 1, (S,), generator=g).tolist()
+    t0 = time.time()
+    w = inputs.make_decode(S, H, C, D, wl.dtype, wl.planted, wl.seed, device=device, lens=[x + 1 for x in lens0])
+    q, kc, vc = w["q"], w["k"], w["v"]
+    kbar = api.pool(kc.view(1, S * H, C, D)).view(S, H, C // 64, D)
+    kn = torch.stack([kc[s, :, lens0[s]] for s in range(S)]).contiguous()
+    vn = torch.stack([vc[s, :, lens0[s]] for s in range(S)]).contiguous()
+    lens = torch.tensor(lens0, dtype=torch.int32, device=device)
+    torch.cuda.synchronize()
+    log(f"inputs {name} (ragged lengths) generated in {time.time() - t0:.1f}s")
+    p = api.make_decode_params(q, kc, wl.alpha, None, wl.coarse_scale)
+    bufs = api.DecodeBuffers(p, q.dtype, q.device)
+    st = torch.cuda.current_stream().cuda_stream
+
+    def step():
+        _lib.decode_step(p, q.data_ptr(), kn.data_ptr(), vn.data_ptr(), lens.data_ptr(), kc.data_ptr(),
+                         vc.data_ptr(), kbar.data_ptr(), bufs.o.data_ptr(), bufs.lse.data_ptr(),
+                         bufs.nsel.data_ptr(), bufs.tau.data_ptr(), bufs.ws.data_ptr(), bufs.ws_bytes, st)
+        lens.add_(1)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [_events(2) for _ in range(steps)]
+    for s in range(steps):
+        evs[s][0].record()
+        step()
+        evs[s][1].record()
+    torch.cuda.synchronize()
+    nsel_sum = float(bufs.nsel.to(torch.int64).sum())  # the last step's selection
+    us = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in evs)
+    us_mean = sum(us) / len(us)
+    sel_bytes = (nsel_sum + S * H) * 64 * D * 2 * 2  # selected + own block, K and V, bf16
+    res = dict(name=name, S=S, H=H, capacity=C, D=D, lens_range=[min(lens0), max(lens0) + warmup + steps],
+               coarse_scale=wl.coarse_scale, us_per_step=us_mean, us_min=us[0],
+               mean_selected_blocks=nsel_sum / (S * H), selected_bytes_gb=sel_bytes / 1e9,
+               hbm_gbs_selected=sel_bytes / (us_mean * 1e-6) / 1e9,
+               work="append (K, V at lens[s]; block summary when it fills) + decode over lens[s] + 1 tokens; "
+                    "selected-block bytes of the last step over the mean step time")
+    res["frac_of_hbm_peak"] = res["hbm_gbs_selected"] / PEAK_HBM_GBS
+    del w, q, kc, vc, kbar, bufs
+    torch.cuda.empty_cache()
+    return res
+
+
 def traffic_probe(device):
     """The launches the counter summary is taken from: a plain copy of 1 GiB
     (calibration: it reads and writes exactly 2^30 bytes), one 16K prefill
@@ -408,6 +465,9 @@ def main():
             log(f"{name}: {d}")
             dec[name] = d
         extra["decode_96k"] = dec
+        ds = bench_decode_step("c4cal", max(5, args.steps), args.warmup, dev)
+        log(f"decode step c4cal ragged: {ds}")
+        extra["decode_step_96k_ragged"] = ds
 
     if not args.no_training:
         tr = {}

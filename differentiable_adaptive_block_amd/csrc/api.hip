@@ -8,6 +8,7 @@
 
 #include "dash.h"
 #include "kernels.h"
+#include "decode.h"
 
 namespace {
 

@@ -1,0 +1,44 @@
+// Argument blocks and launchers of the decode kernels (decode.hip).
+#pragma once
+
+#include "common.h"
+
+struct DecodeArgs {
+  const void* q;     // [SH, D]
+  const void* kc;    // [SH, N, D], N the capacity
+  const void* vc;
+  const void* kbar;  // [SH, N / 64, D]
+  void* o;           // [SH, D]
+  float* lse;        // [SH] or null
+  int* nsel;         // [SH] or null
+  float* tau_out;    // [SH] or null
+  // workspace
+  float* zrow;       // [SH, N / 64]   coarse u scores
+  float* rowstat;    // [SH, 2]        tau, lognorm
+  int* sel_cnt;      // [SH]           list length (0: length out of range)
+  int* sel_blk;      // [SH, N / 64]   selected candidate blocks, ascending, then the query's own block
+  float* sel_lp;     // [SH, N / 64]   log2 prior of each listed block
+  float* part;       // [SH, nsplit, D + 2] partial (m, l, o)
+  const int* len;    // [SH / H] tokens per sequence (+ len_add), or null: every row holds N
+  int SH, H, N, D, nsplit, chunk, len_add;  // N: cache capacity (row stride in tokens)
+  float fine_scale;
+  CoarseArith ca;
+};
+
+// Tokens the decode row holds: len[sequence] + len_add, or the capacity.
+__device__ __forceinline__ int decode_row_len(const DecodeArgs& a, int row) {
+  return a.len ? a.len[row / a.H] + a.len_add : a.N;
+}
+
+struct AppendArgs {
+  const void* k_new;  // [SH, D]
+  const void* v_new;
+  const int* len;     // [SH / H] tokens already cached
+  void* kc;           // [SH, N, D]
+  void* vc;
+  void* kbar;         // [SH, N / 64, D]
+  int SH, H, N, D;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t st);
+hipError_t launch_append(const AppendArgs& a, int dtype, hipStream_t st);

@@ -25,6 +25,7 @@
 //                   the 4 waves merge in LDS and write one partial (m, l, o);
 //   decode_combine  merges the nsplit partials of a row (one wave per row).
 #include "kernels.h"
+#include "decode.h"
 #include "entmax.h"
 
 #define LOG2E_F 1.4426950408889634f

@@ -60,43 +60,6 @@ struct BwdArgs {
   CoarseArith ca;
 };
 
-struct DecodeArgs {
-  const void* q;     // [SH, D]
-  const void* kc;    // [SH, N, D]
-  const void* vc;
-  const void* kbar;  // [SH, nb, D]
-  void* o;           // [SH, D]
-  float* lse;        // [SH] or null
-  int* nsel;         // [SH] or null
-  float* tau_out;    // [SH] or null
-  // workspace
-  float* zrow;       // [SH, nb]       coarse u scores
-  float* rowstat;    // [SH, 2]        tau, lognorm
-  int* sel_cnt;      // [SH]
-  int* sel_blk;      // [SH, nb]       selected candidate blocks, ascending, then the last block
-  float* sel_lp;     // [SH, nb]       log2 prior of each listed block
-  float* part;       // [SH, nsplit, D + 2] partial (m, l, o)
-  const int* len;    // [SH / H] tokens per sequence (+ len_add), or null: every row holds N
-  int SH, H, N, D, nsplit, chunk, len_add;  // N: cache capacity (row stride in tokens)
-  float fine_scale;
-  CoarseArith ca;
-};
-
-// Tokens the decode row holds: len[sequence] + len_add, or the capacity.
-__device__ __forceinline__ int decode_row_len(const DecodeArgs& a, int row) {
-  return a.len ? a.len[row / a.H] + a.len_add : a.N;
-}
-
-struct AppendArgs {
-  const void* k_new;  // [SH, D]
-  const void* v_new;
-  const int* len;     // [SH / H] tokens already cached
-  void* kc;           // [SH, N, D]
-  void* vc;
-  void* kbar;         // [SH, N / 64, D]
-  int SH, H, N, D;
-};
-
 // The one Stage-1 score accumulation (see select_mfma_kernel): 32 summaries
 // (operand A, row = lane % 32 is summary `brow`) against the 32 queries in
 // qb (operand B), bf16 MFMA with fp32 accumulation, k-steps in order.
@@ -190,5 +153,3 @@ hipError_t launch_tile_lists(uint32_t* tile_bits, int* tile_cnt, int* tile_blk, 
                              hipStream_t st);
 hipError_t launch_fwd(const FwdArgs& a, int dtype, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t st);
-hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t st);
-hipError_t launch_append(const AppendArgs& a, int dtype, hipStream_t st);
