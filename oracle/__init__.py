@@ -35,6 +35,9 @@ from .dash_ref import (  # noqa: F401
     round_bf16,
     round_storage,
     pool_blocks,
+    pool_attention,
+    pool_attention_vjp,
+    summarise,
     candidate_blocks,
     select_row,
     attend_row,

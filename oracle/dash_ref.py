@@ -32,6 +32,9 @@ Readings taken where the pages are silent (each is restated in the design doc):
   row N-1 of a causal prefill over the cache.
 * R18 decode cache maintenance: appending token n writes it at position n;
   when that completes a block, the block's summary is its Stage-0 mean.
+* R20 the learned summariser: per head a vector w (initialised at zero);
+  a block's summary is sum_j softmax_j(w . k_j) k_j over its keys, which is
+  mean pooling at w = 0.
 * R19 a cache of n tokens (any n >= 1): the query is at position n-1, its
   candidates are the complete blocks before its own, and its own block is
   attended over its cached tokens only (row n-1 of a causal prefill over
@@ -110,6 +113,65 @@ def pool_blocks(k_head, block: int, storage: str):
     return round_storage(mean, storage)
 
 
+def pool_attention(k_head, w, block: int, storage: str):
+    """Stage 0 with the learned summariser (R20): attention pooling per block.
+
+    The montana-research page ("What alpha-entmax changes") has Stage 0
+    summarise each block with a small learned attention head that starts
+    at zero, so training starts from mean pooling.  Here the head is one
+    vector ``w`` [D] per attention head: block b's keys get scores
+    e_j = w . k_j, weights a = softmax(e) over the block, and the summary is
+    sum_j a_j k_j, rounded once to the storage dtype.  At w = 0 every
+    a_j = 1/block exactly, so this is :func:`pool_blocks` bit for bit.
+    """
+    k_head = np.asarray(k_head, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    T, D = k_head.shape
+    if T % block:
+        raise ValueError("T must be a multiple of the block size")
+    kb = k_head.reshape(T // block, block, D)
+    e = kb @ w  # [nb, block]
+    a = np.exp(e - e.max(axis=1, keepdims=True))
+    a = a / a.sum(axis=1, keepdims=True)
+    return round_storage((a[:, :, None] * kb).sum(axis=1), storage)
+
+
+def pool_attention_vjp(k_head, w, dkbar, block: int):
+    """Gradient of sum_b <dkbar_b, summary_b> through :func:`pool_attention`.
+
+    The rounding of the summary is taken as the identity.  With a the block
+    weights, m_b the exact summary and c_j = k_j . dkbar_b - m_b . dkbar_b
+    (the softmax Jacobian applied to the scores' gradient k_j . dkbar_b):
+
+        dk_j = a_j dkbar_b + a_j c_j w,        dw = sum_b sum_j a_j c_j k_j.
+
+    Returns (dk [T, D], dw [D]).  At w = 0 the first term is dkbar_b / block,
+    the mean-pooling gradient.
+    """
+    k_head = np.asarray(k_head, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    dkbar = np.asarray(dkbar, dtype=np.float64)
+    T, D = k_head.shape
+    kb = k_head.reshape(T // block, block, D)
+    e = kb @ w
+    a = np.exp(e - e.max(axis=1, keepdims=True))
+    a = a / a.sum(axis=1, keepdims=True)
+    m = (a[:, :, None] * kb).sum(axis=1)  # [nb, D]
+    c = kb @ dkbar[:, :, None]  # [nb, block, 1]
+    c = c[:, :, 0] - (m * dkbar).sum(axis=1)[:, None]
+    de = a * c  # gradient of the scores
+    dk = a[:, :, None] * dkbar[:, None, :] + de[:, :, None] * w[None, None, :]
+    dw = (de[:, :, None] * kb).sum(axis=(0, 1))
+    return dk.reshape(T, D), dw
+
+
+def summarise(k_head, prm: "Params", w_h=None):
+    """Stage 0 of one head: mean pooling, or the learned summariser when ``w_h`` is given."""
+    if w_h is None:
+        return pool_blocks(k_head, prm.block, prm.storage)
+    return pool_attention(k_head, w_h, prm.block, prm.storage)
+
+
 # ----------------------------------------------------------------------------- Stage 1
 
 
@@ -185,12 +247,13 @@ def _as64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def forward_rows(q, k, v, prm: Params, rows, kbar=None):
+def forward_rows(q, k, v, prm: Params, rows, kbar=None, w=None):
     """Forward for selected rows only.
 
     ``q, k, v``: [B, H, T, D]; ``rows``: iterable of (b, h, i).  Returns a
     list of dicts (o, lse, tau, nsel, mask over all nb blocks, p over all nb
-    blocks).  ``kbar`` may be passed to avoid re-pooling ([B, H, nb, D]).
+    blocks).  ``kbar`` may be passed to avoid re-pooling ([B, H, nb, D]);
+    ``w`` ([H, D]) selects the learned summariser (R20).
     """
     q, k, v = _as64(q), _as64(k), _as64(v)
     D = q.shape[-1]
@@ -202,7 +265,7 @@ def forward_rows(q, k, v, prm: Params, rows, kbar=None):
             kb = _as64(kbar[b, h])
         else:
             if (b, h) not in cache:
-                cache[(b, h)] = pool_blocks(k[b, h], prm.block, prm.storage)
+                cache[(b, h)] = summarise(k[b, h], prm, None if w is None else w[h])
             kb = cache[(b, h)]
         sel = select_row(q[b, h, i], kb, i, prm, D)
         o, lse, _ = attend_row(q[b, h, i], k[b, h], v[b, h], i, sel, prm, D)
@@ -215,8 +278,10 @@ def forward_rows(q, k, v, prm: Params, rows, kbar=None):
     return out
 
 
-def forward(q, k, v, prm: Params):
+def forward(q, k, v, prm: Params, w=None):
     """Full forward over every row: summaries, selection and attention.
+
+    ``w`` ([H, D]) selects the learned summariser (R20); None is mean pooling.
 
     Returns a dict of arrays: kbar [B,H,nb,D], tau [B,H,T], nsel [B,H,T],
     mask [B,H,T,nb] (bool), p [B,H,T,nb], o [B,H,T,D], lse [B,H,T].
@@ -233,7 +298,7 @@ def forward(q, k, v, prm: Params):
     lse = np.zeros((B, H, T))
     for b in range(B):
         for h in range(H):
-            kb = pool_blocks(k[b, h], prm.block, prm.storage)
+            kb = summarise(k[b, h], prm, None if w is None else w[h])
             kbar[b, h] = kb
             for i in range(T):
                 sel = select_row(q[b, h, i], kb, i, prm, D)
@@ -308,43 +373,60 @@ def _grad_arrays(q):
                 dkbar=np.zeros((B, H, T // 64, D)))
 
 
-def backward(q, k, v, dout, prm: Params):
+def _pool_backward(k, prm: Params, w, grads, b, h):
+    """Send dkbar of head (b, h) through Stage 0 into dk (and dw)."""
+    if w is None:
+        grads["dk"][b, h] += np.repeat(grads["dkbar"][b, h], prm.block, axis=0) / prm.block
+        return
+    dk, dw = pool_attention_vjp(k[b, h], w[h], grads["dkbar"][b, h], prm.block)
+    grads["dk"][b, h] += dk
+    grads["dw"][h] += dw
+
+
+def backward(q, k, v, dout, prm: Params, w=None):
     """Gradients of the scalar <dout, O> with respect to q, k, v and the summaries.
 
     Sums the per-row contributions of :func:`_backward_row` over every row,
-    then mean pooling sends dkbar_b / block to every key of block b.
-    Returns dict(dq, dk, dv, dkbar) (dk includes the pooling path).
+    then Stage 0 sends dkbar into dk: dkbar_b / block to every key of block
+    b for mean pooling, :func:`pool_attention_vjp` for the learned
+    summariser ``w`` ([H, D], R20), which also gives dw.
+    Returns dict(dq, dk, dv, dkbar[, dw]) (dk includes the pooling path).
     """
     q, k, v, dout = _as64(q), _as64(k), _as64(v), _as64(dout)
     B, H, T, D = q.shape
     grads = _grad_arrays(q)
+    if w is not None:
+        grads["dw"] = np.zeros((H, D))
     for b in range(B):
         for h in range(H):
-            kb = pool_blocks(k[b, h], prm.block, prm.storage)
+            kb = summarise(k[b, h], prm, None if w is None else w[h])
             for i in range(T):
                 _backward_row(q, k, v, dout, prm, b, h, i, kb, grads)
-            grads["dk"][b, h] += np.repeat(grads["dkbar"][b, h], prm.block, axis=0) / prm.block
+            _pool_backward(k, prm, w, grads, b, h)
     return grads
 
 
-def backward_rows(q, k, v, dout, prm: Params, rows):
+def backward_rows(q, k, v, dout, prm: Params, rows, w=None):
     """The contributions of the given query rows (b, h, i) only.
 
     Returns the same dict as :func:`backward` but summed over ``rows``: dq
     is complete for those rows; dk, dv and dkbar are complete for any key
     block attended only by rows in ``rows`` (e.g. the last blocks of a causal
     head when ``rows`` holds every row from some position on).  dk includes
-    the pooling path of the accumulated dkbar.
+    the pooling path of the accumulated dkbar (and, with the learned
+    summariser ``w``, dw from those rows).
     """
     q, k, v, dout = _as64(q), _as64(k), _as64(v), _as64(dout)
     grads = _grad_arrays(q)
+    if w is not None:
+        grads["dw"] = np.zeros((q.shape[1], q.shape[3]))
     pooled = {}
     for (b, h, i) in rows:
         if (b, h) not in pooled:
-            pooled[(b, h)] = pool_blocks(k[b, h], prm.block, prm.storage)
+            pooled[(b, h)] = summarise(k[b, h], prm, None if w is None else w[h])
         _backward_row(q, k, v, dout, prm, b, h, i, pooled[(b, h)], grads)
     for (b, h) in pooled:
-        grads["dk"][b, h] += np.repeat(grads["dkbar"][b, h], prm.block, axis=0) / prm.block
+        _pool_backward(k, prm, w, grads, b, h)
     return grads
 
 
