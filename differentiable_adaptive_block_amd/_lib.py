@@ -27,6 +27,11 @@ EXPORTS = [
     "dash_fwd_select",
     "dash_fwd_attend",
     "dash_bwd",
+    "dash_pool_attn",
+    "dash_select",
+    "dash_bwd_no_pool",
+    "dash_pool_attn_bwd_workspace_bytes",
+    "dash_pool_attn_bwd",
     "dash_decode_workspace_bytes",
     "dash_decode",
     "dash_cache_append",
@@ -98,6 +103,17 @@ def load() -> ctypes.CDLL:
     L.dash_bwd.restype = ctypes.c_int
     L.dash_bwd.argtypes = [P(DashParams), vp, vp, vp, vp, vp, vp, vp, P(DashSel), vp, vp, vp, vp, vp,
                            ctypes.c_size_t, vp]
+    L.dash_pool_attn.restype = ctypes.c_int
+    L.dash_pool_attn.argtypes = [P(DashParams), vp, vp, vp, vp]
+    L.dash_select.restype = ctypes.c_int
+    L.dash_select.argtypes = [P(DashParams), vp, vp, P(DashSel), vp]
+    L.dash_bwd_no_pool.restype = ctypes.c_int
+    L.dash_bwd_no_pool.argtypes = [P(DashParams), vp, vp, vp, vp, vp, vp, vp, P(DashSel), vp, vp, vp, vp, vp,
+                                   ctypes.c_size_t, vp]
+    L.dash_pool_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.dash_pool_attn_bwd_workspace_bytes.argtypes = [P(DashParams)]
+    L.dash_pool_attn_bwd.restype = ctypes.c_int
+    L.dash_pool_attn_bwd.argtypes = [P(DashParams), vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.dash_decode_workspace_bytes.restype = ctypes.c_size_t
     L.dash_decode_workspace_bytes.argtypes = [P(DashDecodeParams)]
     L.dash_decode.restype = ctypes.c_int
@@ -162,6 +178,28 @@ def fwd_attend(p: DashParams, q, k, v, kbar, sel: DashSel, o, lse, stream) -> No
 def bwd(p: DashParams, q, k, v, o, lse, dout, kbar, sel: DashSel, dq, dk, dv, dkbar, ws, ws_bytes, stream) -> None:
     check(load().dash_bwd(ctypes.byref(p), q, k, v, o, lse, dout, kbar, ctypes.byref(sel), dq, dk, dv, dkbar, ws,
                           ws_bytes, stream))
+
+
+def pool_attn(p: DashParams, k, w, kbar, stream) -> None:
+    check(load().dash_pool_attn(ctypes.byref(p), k, w, kbar, stream))
+
+
+def select(p: DashParams, q, kbar, sel: DashSel, stream) -> None:
+    check(load().dash_select(ctypes.byref(p), q, kbar, ctypes.byref(sel), stream))
+
+
+def bwd_no_pool(p: DashParams, q, k, v, o, lse, dout, kbar, sel: DashSel, dq, dk, dv, dkbar, ws, ws_bytes,
+                stream) -> None:
+    check(load().dash_bwd_no_pool(ctypes.byref(p), q, k, v, o, lse, dout, kbar, ctypes.byref(sel), dq, dk, dv, dkbar,
+                                  ws, ws_bytes, stream))
+
+
+def pool_attn_bwd_workspace_bytes(p: DashParams) -> int:
+    return int(load().dash_pool_attn_bwd_workspace_bytes(ctypes.byref(p)))
+
+
+def pool_attn_bwd(p: DashParams, k, w, dkbar, dk, dw, ws, ws_bytes, stream) -> None:
+    check(load().dash_pool_attn_bwd(ctypes.byref(p), k, w, dkbar, dk, dw, ws, ws_bytes, stream))
 
 
 def decode(p: DashDecodeParams, q, kc, vc, kbar, o, lse, nsel, tau, ws, ws_bytes, stream) -> None:

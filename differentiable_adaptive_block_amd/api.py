@@ -103,11 +103,27 @@ def pool(k: torch.Tensor) -> torch.Tensor:
     return kbar
 
 
-def forward(q, k, v, alpha=1.5, causal=True, fine_scale=None, coarse_scale=None, want_mask=True):
-    """Stages 0-2.  Returns dict(o, lse, kbar, sel, params)."""
+def pool_attn(k: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
+    """Stage 0 with the learned summariser: kbar [B,H,T/64,D] of k [B,H,T,D], head vectors w [H,D] (f32)."""
+    _require(k, "k")
+    p = make_params(k, 1.5, True)
+    _require(w, "w", (p.H, p.D), torch.float32)
+    kbar = torch.empty((p.B, p.H, p.T // BLOCK, p.D), dtype=k.dtype, device=k.device)
+    _lib.pool_attn(p, _ptr(k), _ptr(w), _ptr(kbar), _stream(k.device))
+    return kbar
+
+
+def forward(q, k, v, alpha=1.5, causal=True, fine_scale=None, coarse_scale=None, want_mask=True,
+            summariser_w=None):
+    """Stages 0-2.  Returns dict(o, lse, kbar, sel, params).
+
+    ``summariser_w`` ([H, D] f32) switches Stage 0 to the learned summariser;
+    None is mean pooling."""
     for name, t in (("q", q), ("k", k), ("v", v)):
         _require(t, name, q.shape, q.dtype)
     p = make_params(q, alpha, causal, fine_scale, coarse_scale)
+    if summariser_w is not None:
+        _require(summariser_w, "summariser_w", (p.H, p.D), torch.float32)
     dev = q.device
     o = torch.empty_like(q)
     lse = torch.empty((p.B, p.H, p.T), dtype=torch.float32, device=dev)
@@ -116,12 +132,17 @@ def forward(q, k, v, alpha=1.5, causal=True, fine_scale=None, coarse_scale=None,
     wsb = _lib.fwd_workspace_bytes(p)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     csel = sel.as_c()
-    _lib.fwd(p, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(kbar), csel, _ptr(ws), wsb, _stream(dev))
+    if summariser_w is None:
+        _lib.fwd(p, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(kbar), csel, _ptr(ws), wsb, _stream(dev))
+    else:
+        _lib.pool_attn(p, _ptr(k), _ptr(summariser_w), _ptr(kbar), _stream(dev))
+        _lib.select(p, _ptr(q), _ptr(kbar), csel, _stream(dev))
+        _lib.fwd_attend(p, _ptr(q), _ptr(k), _ptr(v), _ptr(kbar), csel, _ptr(o), _ptr(lse), _stream(dev))
     return dict(o=o, lse=lse, kbar=kbar, sel=sel, params=p)
 
 
-def backward(q, k, v, o, lse, dout, kbar, sel: Selection, p: _lib.DashParams):
-    """Gradients of <dout, O>: dict(dq, dk, dv, dkbar)."""
+def backward(q, k, v, o, lse, dout, kbar, sel: Selection, p: _lib.DashParams, summariser_w=None):
+    """Gradients of <dout, O>: dict(dq, dk, dv, dkbar), plus dw [H,D] with the learned summariser."""
     _require(dout, "dout", q.shape, q.dtype)
     dev = q.device
     dq = torch.empty_like(q)
@@ -130,9 +151,18 @@ def backward(q, k, v, o, lse, dout, kbar, sel: Selection, p: _lib.DashParams):
     dkbar = torch.empty((p.B, p.H, p.T // BLOCK, p.D), dtype=torch.float32, device=dev)
     wsb = _lib.bwd_workspace_bytes(p)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
-    _lib.bwd(p, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(kbar), sel.as_c(), _ptr(dq),
-             _ptr(dk), _ptr(dv), _ptr(dkbar), _ptr(ws), wsb, _stream(dev))
-    return dict(dq=dq, dk=dk, dv=dv, dkbar=dkbar)
+    if summariser_w is None:
+        _lib.bwd(p, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(kbar), sel.as_c(), _ptr(dq),
+                 _ptr(dk), _ptr(dv), _ptr(dkbar), _ptr(ws), wsb, _stream(dev))
+        return dict(dq=dq, dk=dk, dv=dv, dkbar=dkbar)
+    _require(summariser_w, "summariser_w", (p.H, p.D), torch.float32)
+    _lib.bwd_no_pool(p, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(kbar), sel.as_c(), _ptr(dq),
+                     _ptr(dk), _ptr(dv), _ptr(dkbar), _ptr(ws), wsb, _stream(dev))
+    dw = torch.empty((p.H, p.D), dtype=torch.float32, device=dev)
+    wsb2 = _lib.pool_attn_bwd_workspace_bytes(p)
+    ws2 = torch.empty(max(wsb2, 1), dtype=torch.uint8, device=dev)
+    _lib.pool_attn_bwd(p, _ptr(k), _ptr(summariser_w), _ptr(dkbar), _ptr(dk), _ptr(dw), _ptr(ws2), wsb2, _stream(dev))
+    return dict(dq=dq, dk=dk, dv=dv, dkbar=dkbar, dw=dw)
 
 
 def make_decode_params(q, kc, alpha, fine_scale=None, coarse_scale=None):
@@ -230,9 +260,10 @@ class DashAttentionFn(torch.autograd.Function):
     """DashAttention as an autograd function (forward: Stages 0-2; backward through all of them)."""
 
     @staticmethod
-    def forward(ctx, q, k, v, alpha, causal, fine_scale, coarse_scale):
-        r = forward(q, k, v, alpha, causal, fine_scale, coarse_scale, want_mask=False)
+    def forward(ctx, q, k, v, alpha, causal, fine_scale, coarse_scale, summariser_w=None):
+        r = forward(q, k, v, alpha, causal, fine_scale, coarse_scale, want_mask=False, summariser_w=summariser_w)
         ctx.save_for_backward(q, k, v, r["o"], r["lse"], r["kbar"])
+        ctx.w = summariser_w
         ctx.sel = r["sel"]
         ctx.p = r["params"]
         return r["o"]
@@ -240,9 +271,11 @@ class DashAttentionFn(torch.autograd.Function):
     @staticmethod
     def backward(ctx, dout):
         q, k, v, o, lse, kbar = ctx.saved_tensors
-        g = backward(q, k, v, o, lse, dout.contiguous(), kbar, ctx.sel, ctx.p)
-        return g["dq"], g["dk"], g["dv"], None, None, None, None
+        g = backward(q, k, v, o, lse, dout.contiguous(), kbar, ctx.sel, ctx.p, summariser_w=ctx.w)
+        return g["dq"], g["dk"], g["dv"], None, None, None, None, g.get("dw")
 
 
-def dash_attention(q, k, v, alpha=1.5, causal=True, fine_scale=None, coarse_scale=None):
-    return DashAttentionFn.apply(q, k, v, alpha, causal, fine_scale, coarse_scale)
+def dash_attention(q, k, v, alpha=1.5, causal=True, fine_scale=None, coarse_scale=None, summariser_w=None):
+    """DashAttention with autograd; ``summariser_w`` ([H, D] f32, a leaf that may require grad)
+    selects the learned Stage-0 summariser."""
+    return DashAttentionFn.apply(q, k, v, alpha, causal, fine_scale, coarse_scale, summariser_w)

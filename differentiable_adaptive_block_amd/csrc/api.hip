@@ -8,6 +8,8 @@
 
 #include "dash.h"
 #include "kernels.h"
+#include "attn_bwd.h"
+#include "summariser.h"
 #include "decode.h"
 
 namespace {
@@ -152,17 +154,12 @@ dash_status dash_pool(const dash_params* p, const void* k, void* kbar, void* str
   return e == hipSuccess ? DASH_OK : hip_fail(e, "pool");
 }
 
-dash_status dash_fwd_select(const dash_params* p, const void* q, const void* k, void* kbar, const dash_sel* sel,
-                            void* stream) {
-  dash_status s = check_params(p);
-  if (s != DASH_OK) return s;
-  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(kbar)) return fail(DASH_EINVAL, "q, k and kbar must be non-null and 16-byte aligned");
-  if ((s = check_sel(sel, true)) != DASH_OK) return s;
-  hipStream_t st = (hipStream_t)stream;
+// Stage 1 (scores, entmax, masks, tile lists) from summaries already in kbar.
+static dash_status select_from_kbar(const dash_params* p, const void* q, const void* kbar, const dash_sel* sel,
+                                    hipStream_t st) {
   const int BH = p->B * p->H;
   const int nb = p->T / DASH_BLOCK;
   hipError_t e;
-  if ((e = launch_pool(k, kbar, BH, p->T, p->D, p->dtype, st)) != hipSuccess) return hip_fail(e, "pool");
   if ((e = launch_fill_u32(sel->tile_bits, (size_t)BH * ntile_of(p->T) * nbw_of(nb), 0u, st)) != hipSuccess)
     return hip_fail(e, "clear tile bits");
   SelectArgs sa;
@@ -181,6 +178,53 @@ dash_status dash_fwd_select(const dash_params* p, const void* q, const void* k, 
   if ((e = launch_tile_lists(sel->tile_bits, sel->tile_cnt, sel->tile_blk, BH, p->T, p->causal, st)) != hipSuccess)
     return hip_fail(e, "tile lists");
   return DASH_OK;
+}
+
+dash_status dash_fwd_select(const dash_params* p, const void* q, const void* k, void* kbar, const dash_sel* sel,
+                            void* stream) {
+  dash_status s = check_params(p);
+  if (s != DASH_OK) return s;
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(kbar)) return fail(DASH_EINVAL, "q, k and kbar must be non-null and 16-byte aligned");
+  if ((s = check_sel(sel, true)) != DASH_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if ((e = launch_pool(k, kbar, p->B * p->H, p->T, p->D, p->dtype, st)) != hipSuccess) return hip_fail(e, "pool");
+  return select_from_kbar(p, q, kbar, sel, st);
+}
+
+dash_status dash_select(const dash_params* p, const void* q, const void* kbar, const dash_sel* sel, void* stream) {
+  dash_status s = check_params(p);
+  if (s != DASH_OK) return s;
+  if (!ok_ptr(q) || !ok_ptr(kbar)) return fail(DASH_EINVAL, "q and kbar must be non-null and 16-byte aligned");
+  if ((s = check_sel(sel, true)) != DASH_OK) return s;
+  return select_from_kbar(p, q, kbar, sel, (hipStream_t)stream);
+}
+
+dash_status dash_pool_attn(const dash_params* p, const void* k, const float* w, void* kbar, void* stream) {
+  dash_status s = check_params(p, false);
+  if (s != DASH_OK) return s;
+  if (!ok_ptr(k) || !ok_ptr(kbar) || !ok_ptr(w)) return fail(DASH_EINVAL, "k, w and kbar must be non-null and 16-byte aligned");
+  hipError_t e = launch_pool_attn(k, w, kbar, p->B * p->H, p->H, p->T, p->D, p->dtype, (hipStream_t)stream);
+  return e == hipSuccess ? DASH_OK : hip_fail(e, "attention pooling");
+}
+
+size_t dash_pool_attn_bwd_workspace_bytes(const dash_params* p) {
+  if (check_params(p, false) != DASH_OK) return 0;
+  return (size_t)p->B * p->H * (p->T / DASH_BLOCK) * p->D * sizeof(float);
+}
+
+dash_status dash_pool_attn_bwd(const dash_params* p, const void* k, const float* w, const float* dkbar, void* dk,
+                               float* dw, void* workspace, size_t workspace_bytes, void* stream) {
+  dash_status s = check_params(p, false);
+  if (s != DASH_OK) return s;
+  if (!ok_ptr(k) || !ok_ptr(w) || !ok_ptr(dkbar) || !ok_ptr(dk) || !ok_ptr(dw))
+    return fail(DASH_EINVAL, "k, w, dkbar, dk and dw must be non-null and 16-byte aligned");
+  const size_t need = dash_pool_attn_bwd_workspace_bytes(p);
+  if (workspace_bytes < need) return fail(DASH_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (!ok_ptr(workspace)) return fail(DASH_EINVAL, "workspace must be non-null and 16-byte aligned");
+  hipError_t e = launch_pool_attn_bwd(k, w, dkbar, dk, dw, static_cast<float*>(workspace), p->B, p->H, p->T, p->D,
+                                      p->dtype, (hipStream_t)stream);
+  return e == hipSuccess ? DASH_OK : hip_fail(e, "attention pooling backward");
 }
 
 dash_status dash_fwd_attend(const dash_params* p, const void* q, const void* k, const void* v, const void* kbar,
@@ -224,9 +268,10 @@ dash_status dash_fwd(const dash_params* p, const void* q, const void* k, const v
   return dash_fwd_attend(p, q, k, v, kbar, sel, o, lse, stream);
 }
 
-dash_status dash_bwd(const dash_params* p, const void* q, const void* k, const void* v, const void* o,
-                     const float* lse, const void* dout, const void* kbar, const dash_sel* sel, void* dq, void* dk,
-                     void* dv, float* dkbar, void* workspace, size_t workspace_bytes, void* stream) {
+static dash_status bwd_common(const dash_params* p, const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, const void* kbar, const dash_sel* sel, void* dq,
+                              void* dk, void* dv, float* dkbar, void* workspace, size_t workspace_bytes, void* stream,
+                              float pool_scale) {
   dash_status s = check_params(p);
   if (s != DASH_OK) return s;
   if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(lse) || !ok_ptr(dout) || !ok_ptr(kbar) ||
@@ -264,9 +309,23 @@ dash_status dash_bwd(const dash_params* p, const void* q, const void* k, const v
   ba.D = p->D;
   ba.causal = p->causal;
   ba.fine_scale = p->fine_scale;
+  ba.pool_scale = pool_scale;
   ba.ca = make_ca(p->alpha, p->coarse_scale);
   hipError_t e = launch_bwd(ba, p->dtype, (hipStream_t)stream);
   return e == hipSuccess ? DASH_OK : hip_fail(e, "backward");
+}
+
+dash_status dash_bwd(const dash_params* p, const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dout, const void* kbar, const dash_sel* sel, void* dq, void* dk,
+                     void* dv, float* dkbar, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_common(p, q, k, v, o, lse, dout, kbar, sel, dq, dk, dv, dkbar, workspace, workspace_bytes, stream,
+                    1.f / DASH_BLOCK);
+}
+
+dash_status dash_bwd_no_pool(const dash_params* p, const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, const void* kbar, const dash_sel* sel, void* dq,
+                             void* dk, void* dv, float* dkbar, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_common(p, q, k, v, o, lse, dout, kbar, sel, dq, dk, dv, dkbar, workspace, workspace_bytes, stream, 0.f);
 }
 
 static dash_status check_decode_params(const dash_decode_params* p) {

@@ -10,7 +10,8 @@
 //   dV_j  = sum_i a_ij dO_i                 G_ib = sum_{j in b} dS_ij   (= dL/dlog p_ib)
 //   s = p^(2-alpha), s.g = G p^(1-alpha),   dz_ib = s_b g_b - s_b <s,g>/sum s
 //   dQ_i += coarse_scale sum_b dz_ib kbar_b,  dkbar_b = coarse_scale sum_i dz_ib q_i,
-//   dK_j += dkbar_{blk(j)} / 64.
+//   dK_j += dkbar_{blk(j)} / 64 (mean pooling; left out when the summaries come
+//   from another summariser, whose own backward then adds its term).
 //
 // bf16 path (deterministic, no floating-point atomics):
 //   bwd_delta     delta
@@ -24,6 +25,7 @@
 //                 pooling term
 // fp32 path: one wave per query row, dK / dV / dkbar by float atomics.
 #include "kernels.h"
+#include "attn_bwd.h"
 #include "entmax.h"
 #include "tiles.h"
 
@@ -581,7 +583,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
             const int r = 4 * r4 + 2 * e2 + e;
             const int ri = (dt * 16 + r) * 64 + l;
             v0[e] = dva[dt][r] + red1[ri];
-            k0[e] = (dka[dt][r] + red2[ri]) * a.fine_scale + kbg[kb][d + 2 * e2 + e] * (1.f / DASH_BLOCK);
+            k0[e] = (dka[dt][r] + red2[ri]) * a.fine_scale + kbg[kb][d + 2 * e2 + e] * a.pool_scale;
           }
           pv2[e2] = (uint32_t)f2bf(v0[0]) | ((uint32_t)f2bf(v0[1]) << 16);
           pk2[e2] = (uint32_t)f2bf(k0[0]) | ((uint32_t)f2bf(k0[1]) << 16);
@@ -836,6 +838,7 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t st) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   bwd_generic_kernel<float><<<dim3(a.T, a.BH), 64, 0, st>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  bwd_pool_grad_kernel<<<2048, 256, 0, st>>>(reinterpret_cast<float*>(a.dk), a.dkbar, a.T, a.D, n);
+  if (a.pool_scale != 0.f)
+    bwd_pool_grad_kernel<<<2048, 256, 0, st>>>(reinterpret_cast<float*>(a.dk), a.dkbar, a.T, a.D, n);
   return hipGetLastError();
 }

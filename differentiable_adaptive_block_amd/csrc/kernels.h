@@ -33,33 +33,6 @@ struct FwdArgs {
   CoarseArith ca;
 };
 
-struct BwdArgs {
-  const void* q;
-  const void* k;
-  const void* v;
-  const void* o;
-  const float* lse;
-  const void* dout;
-  const void* kbar;
-  const float* tau;
-  const float* lognorm;
-  const int* tile_cnt;
-  const int* tile_blk;
-  const uint32_t* tile_bits;
-  void* dq;
-  void* dk;
-  void* dv;
-  float* dkbar;
-  // workspace
-  float* delta;    // [BH, T]      dout . o
-  float* dq_acc;   // [BH, T, D]   fp32
-  float* gbuf;     // [BH, ntile, nb, QTILE]  G_ib for listed blocks
-  float* pbuf;     // [BH, ntile, nb, QTILE]  log2 prior used for (row, listed block)
-  int BH, T, D, causal;
-  float fine_scale;
-  CoarseArith ca;
-};
-
 // The one Stage-1 score accumulation (see select_mfma_kernel): 32 summaries
 // (operand A, row = lane % 32 is summary `brow`) against the 32 queries in
 // qb (operand B), bf16 MFMA with fp32 accumulation, k-steps in order.
@@ -152,4 +125,3 @@ hipError_t launch_select(const SelectArgs& a, int BH, int dtype, hipStream_t st)
 hipError_t launch_tile_lists(uint32_t* tile_bits, int* tile_cnt, int* tile_blk, int BH, int T, int causal,
                              hipStream_t st);
 hipError_t launch_fwd(const FwdArgs& a, int dtype, hipStream_t st);
-hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t st);

@@ -148,6 +148,50 @@ dash_status dash_bwd(const dash_params* p, const void* q, const void* k, const v
                      const dash_sel* sel, void* dq, void* dk, void* dv, float* dkbar,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The learned Stage-0 summariser (the montana-research page, "What
+ * alpha-entmax changes": each chunk is summarised by a small learned
+ * attention head initialised at zero, so training starts from mean pooling).
+ * The head is one vector per attention head, w [H, D] (f32).  For block b:
+ * e_j = w[h] . k_j over the block's 64 keys, a = softmax(e), kbar_b =
+ * sum_j a_j k_j, in fp64, rounded once to dtype.  At w = 0 this equals
+ * dash_pool bit for bit.  Any T that is a multiple of 64; D <= 128.
+ */
+dash_status dash_pool_attn(const dash_params* p, const void* k, const float* w, void* kbar, void* stream);
+
+/*
+ * Stage 1 alone, from summaries the caller already holds in kbar (for
+ * example dash_pool_attn's): writes the selection `sel` exactly as
+ * dash_fwd_select does after its pooling.  Same validation.
+ */
+dash_status dash_select(const dash_params* p, const void* q, const void* kbar, const dash_sel* sel,
+                        void* stream);
+
+/*
+ * dash_bwd without the Stage-0 term: dk holds the gradient through Stage 2
+ * only (the mean-pooling share dkbar/64 is not added); every other output
+ * is as dash_bwd.  For summaries that did not come from mean pooling: add
+ * their own Stage-0 gradient afterwards (dash_pool_attn_bwd).
+ */
+dash_status dash_bwd_no_pool(const dash_params* p, const void* q, const void* k, const void* v,
+                             const void* o, const float* lse, const void* dout, const void* kbar,
+                             const dash_sel* sel, void* dq, void* dk, void* dv, float* dkbar,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of dash_pool_attn (its rounding taken as the identity): with
+ * g = dkbar[b,h,blk,:] (f32, as dash_bwd writes it) and c_j = k_j.g - kbar.g
+ * (kbar before rounding), adds a_j g + a_j c_j w[h] to dk (dtype, in place:
+ * dk already holds the other gradient terms, e.g. from dash_bwd_no_pool) and
+ * writes dw [H, D] (f32) = the sum over batch and blocks of a_j c_j k_j.
+ * Workspace: dash_pool_attn_bwd_workspace_bytes (per-block partials of dw,
+ * reduced in a fixed order, so the result is deterministic).
+ */
+size_t dash_pool_attn_bwd_workspace_bytes(const dash_params* p);
+dash_status dash_pool_attn_bwd(const dash_params* p, const void* k, const float* w, const float* dkbar,
+                               void* dk, float* dw, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 /* Decode shapes: S sequences x H heads, one new query each, cache length N. */
 typedef struct {
   int32_t S, H, N, D;   /* N multiple of 64, 64 <= N <= 131072; D = 128 (bf16 only) */

@@ -188,3 +188,22 @@ def test_decode_varlen_and_step_validation(L):
     bad[7] = None
     assert L.dash_decode_step(ctypes.byref(p), *bad, need, None) == _lib.DASH_EINVAL
     assert L.dash_decode_step(ctypes.byref(_dparams(D=64)), *sargs, need, None) == _lib.DASH_EUNSUPPORTED
+
+
+def test_summariser_entry_validation(L):
+    p = _params(T=98304)
+    # pooling accepts long sequences (no 65536 limit), rejects null pointers
+    assert L.dash_pool_attn(ctypes.byref(p), FAKE, None, FAKE, None) == _lib.DASH_EINVAL
+    assert L.dash_pool_attn(ctypes.byref(_params(T=100)), FAKE, FAKE, FAKE, None) == _lib.DASH_EINVAL
+    p = _params()
+    assert L.dash_select(ctypes.byref(p), FAKE, None, ctypes.byref(_sel()), None) == _lib.DASH_EINVAL
+    assert L.dash_select(ctypes.byref(p), FAKE, FAKE, ctypes.byref(_sel(tau=None)), None) == _lib.DASH_EINVAL
+    need = L.dash_pool_attn_bwd_workspace_bytes(ctypes.byref(p))
+    assert need == 1 * 2 * (256 // 64) * 128 * 4
+    args = [FAKE] * 5
+    assert L.dash_pool_attn_bwd(ctypes.byref(p), *args, FAKE, need - 1, None) == _lib.DASH_EWORKSPACE
+    assert L.dash_pool_attn_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE, need, None) == _lib.DASH_EINVAL
+    wsb = L.dash_bwd_workspace_bytes(ctypes.byref(p))
+    bargs = [FAKE] * 7 + [ctypes.byref(_sel())] + [FAKE] * 5
+    assert L.dash_bwd_no_pool(ctypes.byref(p), *bargs, wsb - 1, None) == _lib.DASH_EWORKSPACE
+    assert L.dash_bwd_no_pool(ctypes.byref(_params(D=96)), *bargs, wsb, None) != _lib.DASH_OK
