@@ -222,8 +222,15 @@ def bench_prefill(name, steps, warmup, device, log_prefix=""):
     return res, (B, H, T, D)
 
 
-def bench_training(alpha, steps, warmup, device):
-    """Time one training step (dash_fwd + dash_bwd) on the 16K training workload."""
+def _summariser_head(H, D, seed, device):
+    """A non-zero head for the learned summariser (as after some training): 2/sqrt(D) * N(0, 1)."""
+    g = torch.Generator().manual_seed(seed)
+    return (2.0 / math.sqrt(D) * torch.randn((H, D), generator=g)).float().to(device)
+
+
+def bench_training(alpha, steps, warmup, device, learned_summariser=False):
+    """Time one training step (dash_fwd + dash_bwd) on the 16K training workload; with
+    ``learned_summariser`` Stage 0 is the attention-pooling head (forward and its gradient)."""
     from differentiable_adaptive_block_amd import api, inputs
 
     wl = inputs.CONFIGS["c5"]
@@ -232,15 +239,18 @@ def bench_training(alpha, steps, warmup, device):
                             with_dout=True)
     q, k, v, dout = w["q"], w["k"], w["v"], w["dout"]
     B, H, T, D = q.shape
-    r = api.forward(q, k, v, alpha=alpha, causal=True, coarse_scale=wl.coarse_scale, want_mask=True)
+    head = _summariser_head(H, D, wl.seed + 300, device) if learned_summariser else None
+    r = api.forward(q, k, v, alpha=alpha, causal=True, coarse_scale=wl.coarse_scale, want_mask=True,
+                    summariser_w=head)
     torch.cuda.synchronize()
     sum_sel = int(r["sel"].nsel.to(torch.int64).sum())
 
     def step(ev=None):
-        f = api.forward(q, k, v, alpha=alpha, causal=True, coarse_scale=wl.coarse_scale, want_mask=False)
+        f = api.forward(q, k, v, alpha=alpha, causal=True, coarse_scale=wl.coarse_scale, want_mask=False,
+                        summariser_w=head)
         if ev is not None:
             ev[0].record()
-        g = api.backward(q, k, v, f["o"], f["lse"], dout, f["kbar"], f["sel"], f["params"])
+        g = api.backward(q, k, v, f["o"], f["lse"], dout, f["kbar"], f["sel"], f["params"], summariser_w=head)
         if ev is not None:
             ev[1].record()
         return g
@@ -265,9 +275,49 @@ def bench_training(alpha, steps, warmup, device):
     res["bwd_tflops"] = res["useful_bwd_tflop"] / (bwd_ms / 1e3)
     res["bwd_mfma_frac"] = res["bwd_tflops"] / PEAK_BF16_TFLOPS
     res["step_tflops"] = (res["useful_fwd_tflop"] + res["useful_bwd_tflop"]) / (ms / 1e3)
+    if learned_summariser:
+        res["summariser"] = "learned (attention pooling, head 2/sqrt(D) N(0,1))"
+        res.update(_time_summariser(k, head, r["params"], steps))
     del w, q, k, v, dout, r
     torch.cuda.empty_cache()
     return res
+
+
+def _time_summariser(k, head, p, steps):
+    """HIP-event times of the learned summariser's own kernels on the training shape:
+    dash_pool_attn (reads K, writes the summaries) and dash_pool_attn_bwd (reads K
+    and dkbar, reads and writes dK, reduces dw)."""
+    from differentiable_adaptive_block_amd import _lib
+
+    B, H, T, D = k.shape
+    nb = T // 64
+    st = torch.cuda.current_stream().cuda_stream
+    kbar = torch.empty((B, H, nb, D), dtype=k.dtype, device=k.device)
+    dkbar = torch.randn((B, H, nb, D), dtype=torch.float32, device=k.device)
+    dk = torch.zeros_like(k)
+    dw = torch.empty((H, D), dtype=torch.float32, device=k.device)
+    wsb = _lib.pool_attn_bwd_workspace_bytes(p)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=k.device)
+    fwd = lambda: _lib.pool_attn(p, k.data_ptr(), head.data_ptr(), kbar.data_ptr(), st)  # noqa: E731
+    bwd = lambda: _lib.pool_attn_bwd(p, k.data_ptr(), head.data_ptr(), dkbar.data_ptr(), dk.data_ptr(),  # noqa: E731
+                                     dw.data_ptr(), ws.data_ptr(), wsb, st)
+    out = {}
+    esz = k.element_size()
+    moved = {"pool_attn": B * H * T * D * esz + B * H * nb * D * esz,
+             "pool_attn_bwd": 3 * B * H * T * D * esz + B * H * nb * D * 4 * 2}
+    for name, fn in (("pool_attn", fwd), ("pool_attn_bwd", bwd)):
+        fn()
+        torch.cuda.synchronize()
+        evs = [_events(2) for _ in range(steps)]
+        for e in evs:
+            e[0].record()
+            fn()
+            e[1].record()
+        torch.cuda.synchronize()
+        us = sum(e[0].elapsed_time(e[1]) for e in evs) / steps * 1e3
+        out[f"{name}_us"] = us
+        out[f"{name}_gbs"] = moved[name] / (us * 1e-6) / 1e9
+    return out
 
 
 def bench_decode(name, steps, warmup, device):
@@ -475,6 +525,9 @@ def main():
             t = bench_training(alpha, max(3, args.steps // 2), 1, dev)
             log(f"training alpha={alpha}: {t}")
             tr[f"alpha_{alpha}"] = t
+        t = bench_training(1.5, max(3, args.steps // 2), 1, dev, learned_summariser=True)
+        log(f"training alpha=1.5 learned summariser: {t}")
+        tr["alpha_1.5_learned_summariser"] = t
         extra["training_16k"] = tr
 
     cpu = None
