@@ -27,6 +27,9 @@ EXPORTS = [
     "dash_fwd_select",
     "dash_fwd_attend",
     "dash_bwd",
+    "dash_fwd_gqa",
+    "dash_bwd_gqa_workspace_bytes",
+    "dash_bwd_gqa",
     "dash_pool_attn",
     "dash_select",
     "dash_bwd_no_pool",
@@ -103,6 +106,14 @@ def load() -> ctypes.CDLL:
     L.dash_bwd.restype = ctypes.c_int
     L.dash_bwd.argtypes = [P(DashParams), vp, vp, vp, vp, vp, vp, vp, P(DashSel), vp, vp, vp, vp, vp,
                            ctypes.c_size_t, vp]
+    i32 = ctypes.c_int32
+    L.dash_fwd_gqa.restype = ctypes.c_int
+    L.dash_fwd_gqa.argtypes = [P(DashParams), i32, vp, vp, vp, vp, vp, vp, P(DashSel), vp]
+    L.dash_bwd_gqa_workspace_bytes.restype = ctypes.c_size_t
+    L.dash_bwd_gqa_workspace_bytes.argtypes = [P(DashParams), i32]
+    L.dash_bwd_gqa.restype = ctypes.c_int
+    L.dash_bwd_gqa.argtypes = [P(DashParams), i32, vp, vp, vp, vp, vp, vp, vp, P(DashSel), vp, vp, vp, vp, vp,
+                               ctypes.c_size_t, vp]
     L.dash_pool_attn.restype = ctypes.c_int
     L.dash_pool_attn.argtypes = [P(DashParams), vp, vp, vp, vp]
     L.dash_select.restype = ctypes.c_int
@@ -178,6 +189,20 @@ def fwd_attend(p: DashParams, q, k, v, kbar, sel: DashSel, o, lse, stream) -> No
 def bwd(p: DashParams, q, k, v, o, lse, dout, kbar, sel: DashSel, dq, dk, dv, dkbar, ws, ws_bytes, stream) -> None:
     check(load().dash_bwd(ctypes.byref(p), q, k, v, o, lse, dout, kbar, ctypes.byref(sel), dq, dk, dv, dkbar, ws,
                           ws_bytes, stream))
+
+
+def fwd_gqa(p: DashParams, kv_heads: int, q, k, v, o, lse, kbar, sel: DashSel, stream) -> None:
+    check(load().dash_fwd_gqa(ctypes.byref(p), kv_heads, q, k, v, o, lse, kbar, ctypes.byref(sel), stream))
+
+
+def bwd_gqa_workspace_bytes(p: DashParams, kv_heads: int) -> int:
+    return int(load().dash_bwd_gqa_workspace_bytes(ctypes.byref(p), kv_heads))
+
+
+def bwd_gqa(p: DashParams, kv_heads: int, q, k, v, o, lse, dout, kbar, sel: DashSel, dq, dk, dv, dkbar, ws, ws_bytes,
+            stream) -> None:
+    check(load().dash_bwd_gqa(ctypes.byref(p), kv_heads, q, k, v, o, lse, dout, kbar, ctypes.byref(sel), dq, dk, dv,
+                              dkbar, ws, ws_bytes, stream))
 
 
 def pool_attn(p: DashParams, k, w, kbar, stream) -> None:

@@ -118,21 +118,31 @@ def forward(q, k, v, alpha=1.5, causal=True, fine_scale=None, coarse_scale=None,
     """Stages 0-2.  Returns dict(o, lse, kbar, sel, params).
 
     ``summariser_w`` ([H, D] f32) switches Stage 0 to the learned summariser;
-    None is mean pooling."""
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _require(t, name, q.shape, q.dtype)
+    None is mean pooling.  k and v may have fewer heads than q (grouped-query
+    heads with entmax head aggregation, bf16): then kbar has k's heads."""
+    _require(q, "q")
+    B, H, T, D = q.shape
+    Hkv = k.shape[1] if k.dim() == 4 else -1
+    for name, t in (("k", k), ("v", v)):
+        _require(t, name, (B, Hkv, T, D), q.dtype)
+    if Hkv < 1 or H % Hkv:
+        raise ValueError(f"k has {Hkv} heads, which must divide q's {H}")
+    if Hkv != H and summariser_w is not None:
+        raise ValueError("the learned summariser is built for one KV head per query head")
     p = make_params(q, alpha, causal, fine_scale, coarse_scale)
     if summariser_w is not None:
         _require(summariser_w, "summariser_w", (p.H, p.D), torch.float32)
     dev = q.device
     o = torch.empty_like(q)
     lse = torch.empty((p.B, p.H, p.T), dtype=torch.float32, device=dev)
-    kbar = torch.empty((p.B, p.H, p.T // BLOCK, p.D), dtype=q.dtype, device=dev)
+    kbar = torch.empty((p.B, Hkv, p.T // BLOCK, p.D), dtype=q.dtype, device=dev)
     sel = alloc_selection(p, dev, want_mask)
     wsb = _lib.fwd_workspace_bytes(p)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     csel = sel.as_c()
-    if summariser_w is None:
+    if Hkv != H:
+        _lib.fwd_gqa(p, Hkv, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(kbar), csel, _stream(dev))
+    elif summariser_w is None:
         _lib.fwd(p, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(kbar), csel, _ptr(ws), wsb, _stream(dev))
     else:
         _lib.pool_attn(p, _ptr(k), _ptr(summariser_w), _ptr(kbar), _stream(dev))
@@ -142,13 +152,21 @@ def forward(q, k, v, alpha=1.5, causal=True, fine_scale=None, coarse_scale=None,
 
 
 def backward(q, k, v, o, lse, dout, kbar, sel: Selection, p: _lib.DashParams, summariser_w=None):
-    """Gradients of <dout, O>: dict(dq, dk, dv, dkbar), plus dw [H,D] with the learned summariser."""
+    """Gradients of <dout, O>: dict(dq, dk, dv, dkbar), plus dw [H,D] with the learned summariser.
+    With fewer KV heads than query heads, dk, dv and dkbar have k's heads."""
     _require(dout, "dout", q.shape, q.dtype)
     dev = q.device
+    Hkv = k.shape[1]
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    dkbar = torch.empty((p.B, p.H, p.T // BLOCK, p.D), dtype=torch.float32, device=dev)
+    dkbar = torch.empty((p.B, Hkv, p.T // BLOCK, p.D), dtype=torch.float32, device=dev)
+    if Hkv != p.H:
+        wsb = _lib.bwd_gqa_workspace_bytes(p, Hkv)
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+        _lib.bwd_gqa(p, Hkv, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(kbar), sel.as_c(),
+                     _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dkbar), _ptr(ws), wsb, _stream(dev))
+        return dict(dq=dq, dk=dk, dv=dv, dkbar=dkbar)
     wsb = _lib.bwd_workspace_bytes(p)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     if summariser_w is None:

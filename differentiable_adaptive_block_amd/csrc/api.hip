@@ -154,9 +154,10 @@ dash_status dash_pool(const dash_params* p, const void* k, void* kbar, void* str
   return e == hipSuccess ? DASH_OK : hip_fail(e, "pool");
 }
 
-// Stage 1 (scores, entmax, masks, tile lists) from summaries already in kbar.
+// Stage 1 (scores, entmax, masks, tile lists) from summaries already in kbar;
+// grp query heads per key/value head (their tile lists are the group's union).
 static dash_status select_from_kbar(const dash_params* p, const void* q, const void* kbar, const dash_sel* sel,
-                                    hipStream_t st) {
+                                    hipStream_t st, int grp = 1) {
   const int BH = p->B * p->H;
   const int nb = p->T / DASH_BLOCK;
   hipError_t e;
@@ -168,6 +169,7 @@ static dash_status select_from_kbar(const dash_params* p, const void* q, const v
   sa.T = p->T;
   sa.D = p->D;
   sa.causal = p->causal;
+  sa.grp = grp;
   sa.ca = make_ca(p->alpha, p->coarse_scale);
   sa.tau = sel->tau;
   sa.lognorm = sel->lognorm;
@@ -175,6 +177,8 @@ static dash_status select_from_kbar(const dash_params* p, const void* q, const v
   sa.mask = sel->mask;
   sa.tile_bits = sel->tile_bits;
   if ((e = launch_select(sa, BH, p->dtype, st)) != hipSuccess) return hip_fail(e, "select");
+  if ((e = launch_group_union(sel->tile_bits, BH, grp, (size_t)ntile_of(p->T) * nbw_of(nb), st)) != hipSuccess)
+    return hip_fail(e, "group union");
   if ((e = launch_tile_lists(sel->tile_bits, sel->tile_cnt, sel->tile_blk, BH, p->T, p->causal, st)) != hipSuccess)
     return hip_fail(e, "tile lists");
   return DASH_OK;
@@ -227,13 +231,8 @@ dash_status dash_pool_attn_bwd(const dash_params* p, const void* k, const float*
   return e == hipSuccess ? DASH_OK : hip_fail(e, "attention pooling backward");
 }
 
-dash_status dash_fwd_attend(const dash_params* p, const void* q, const void* k, const void* v, const void* kbar,
-                            const dash_sel* sel, void* o, float* lse, void* stream) {
-  dash_status s = check_params(p);
-  if (s != DASH_OK) return s;
-  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(lse) || !ok_ptr(kbar))
-    return fail(DASH_EINVAL, "q, k, v, o, lse and kbar must be non-null and 16-byte aligned");
-  if ((s = check_sel(sel, true)) != DASH_OK) return s;
+static dash_status attend_common(const dash_params* p, const void* q, const void* k, const void* v,
+                                 const void* kbar, const dash_sel* sel, void* o, float* lse, void* stream, int grp) {
   FwdArgs fa;
   fa.q = q;
   fa.k = k;
@@ -249,10 +248,44 @@ dash_status dash_fwd_attend(const dash_params* p, const void* q, const void* k, 
   fa.T = p->T;
   fa.D = p->D;
   fa.causal = p->causal;
+  fa.grp = grp;
   fa.fine_scale = p->fine_scale;
   fa.ca = make_ca(p->alpha, p->coarse_scale);
   hipError_t e = launch_fwd(fa, p->dtype, (hipStream_t)stream);
   return e == hipSuccess ? DASH_OK : hip_fail(e, "stage 2 forward");
+}
+
+dash_status dash_fwd_attend(const dash_params* p, const void* q, const void* k, const void* v, const void* kbar,
+                            const dash_sel* sel, void* o, float* lse, void* stream) {
+  dash_status s = check_params(p);
+  if (s != DASH_OK) return s;
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(lse) || !ok_ptr(kbar))
+    return fail(DASH_EINVAL, "q, k, v, o, lse and kbar must be non-null and 16-byte aligned");
+  if ((s = check_sel(sel, true)) != DASH_OK) return s;
+  return attend_common(p, q, k, v, kbar, sel, o, lse, stream, 1);
+}
+
+static dash_status check_groups(const dash_params* p, int32_t kv_heads) {
+  if (kv_heads < 1 || p->H % kv_heads) return fail(DASH_EINVAL, "kv_heads (%d) must divide H (%d)", kv_heads, p->H);
+  if (kv_heads != p->H && p->dtype != DASH_BF16)
+    return fail(DASH_EUNSUPPORTED, "grouped-query heads are built for bf16 only");
+  return DASH_OK;
+}
+
+dash_status dash_fwd_gqa(const dash_params* p, int32_t kv_heads, const void* q, const void* k, const void* v,
+                         void* o, float* lse, void* kbar, const dash_sel* sel, void* stream) {
+  dash_status s = check_params(p);
+  if (s != DASH_OK) return s;
+  if ((s = check_groups(p, kv_heads)) != DASH_OK) return s;
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(lse) || !ok_ptr(kbar))
+    return fail(DASH_EINVAL, "q, k, v, o, lse and kbar must be non-null and 16-byte aligned");
+  if ((s = check_sel(sel, true)) != DASH_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  const int grp = p->H / kv_heads;
+  hipError_t e;
+  if ((e = launch_pool(k, kbar, p->B * kv_heads, p->T, p->D, p->dtype, st)) != hipSuccess) return hip_fail(e, "pool");
+  if ((s = select_from_kbar(p, q, kbar, sel, st, grp)) != DASH_OK) return s;
+  return attend_common(p, q, k, v, kbar, sel, o, lse, stream, grp);
 }
 
 dash_status dash_fwd(const dash_params* p, const void* q, const void* k, const void* v, void* o, float* lse,
@@ -310,9 +343,84 @@ static dash_status bwd_common(const dash_params* p, const void* q, const void* k
   ba.causal = p->causal;
   ba.fine_scale = p->fine_scale;
   ba.pool_scale = pool_scale;
+  ba.grp = 1;
+  ba.gsum = nullptr;
   ba.ca = make_ca(p->alpha, p->coarse_scale);
   hipError_t e = launch_bwd(ba, p->dtype, (hipStream_t)stream);
   return e == hipSuccess ? DASH_OK : hip_fail(e, "backward");
+}
+
+static size_t bwd_gqa_ws_layout(const dash_params* p, int32_t kv_heads, size_t off[8]) {
+  size_t base = bwd_ws_layout(p, off);
+  const size_t BH = (size_t)p->B * p->H, T = p->T, D = p->D, nb = T / DASH_BLOCK, nt = ntile_of(p->T);
+  const size_t grp = (size_t)p->H / kv_heads;
+  size_t o = base;
+  auto take = [&](size_t bytes) { size_t r = o; o += (bytes + 255) & ~size_t(255); return r; };
+  off[4] = take(BH / grp * nt * nb * DASH_QTILE * sizeof(float));  // G summed over each group
+  off[5] = take(BH * T * D * 2);                                   // dK per query head
+  off[6] = take(BH * T * D * 2);                                   // dV per query head
+  off[7] = take(BH * nb * D * sizeof(float));                      // dkbar per query head
+  return o;
+}
+
+size_t dash_bwd_gqa_workspace_bytes(const dash_params* p, int32_t kv_heads) {
+  if (check_params(p) != DASH_OK || kv_heads < 1 || p->H % kv_heads) return 0;
+  size_t off[8];
+  if (kv_heads == p->H) return bwd_ws_layout(p, off);
+  return bwd_gqa_ws_layout(p, kv_heads, off);
+}
+
+dash_status dash_bwd_gqa(const dash_params* p, int32_t kv_heads, const void* q, const void* k, const void* v,
+                         const void* o, const float* lse, const void* dout, const void* kbar, const dash_sel* sel,
+                         void* dq, void* dk, void* dv, float* dkbar, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  dash_status s = check_params(p);
+  if (s != DASH_OK) return s;
+  if ((s = check_groups(p, kv_heads)) != DASH_OK) return s;
+  if (kv_heads == p->H)
+    return bwd_common(p, q, k, v, o, lse, dout, kbar, sel, dq, dk, dv, dkbar, workspace, workspace_bytes, stream,
+                      1.f / DASH_BLOCK);
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(lse) || !ok_ptr(dout) || !ok_ptr(kbar) ||
+      !ok_ptr(dq) || !ok_ptr(dk) || !ok_ptr(dv) || !ok_ptr(dkbar))
+    return fail(DASH_EINVAL, "tensor pointers must be non-null and 16-byte aligned");
+  if ((s = check_sel(sel, true)) != DASH_OK) return s;
+  size_t off[8];
+  const size_t need = bwd_gqa_ws_layout(p, kv_heads, off);
+  if (workspace_bytes < need) return fail(DASH_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (!ok_ptr(workspace)) return fail(DASH_EINVAL, "workspace must be non-null and 16-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  BwdArgs ba;
+  ba.q = q;
+  ba.k = k;
+  ba.v = v;
+  ba.o = o;
+  ba.lse = lse;
+  ba.dout = dout;
+  ba.kbar = kbar;
+  ba.tau = sel->tau;
+  ba.lognorm = sel->lognorm;
+  ba.tile_cnt = sel->tile_cnt;
+  ba.tile_blk = sel->tile_blk;
+  ba.tile_bits = sel->tile_bits;
+  ba.dq = dq;
+  ba.dk = ws + off[5];
+  ba.dv = ws + off[6];
+  ba.dkbar = reinterpret_cast<float*>(ws + off[7]);
+  ba.delta = reinterpret_cast<float*>(ws + off[0]);
+  ba.dq_acc = reinterpret_cast<float*>(ws + off[1]);
+  ba.gbuf = reinterpret_cast<float*>(ws + off[2]);
+  ba.pbuf = reinterpret_cast<float*>(ws + off[3]);
+  ba.gsum = reinterpret_cast<float*>(ws + off[4]);
+  ba.BH = p->B * p->H;
+  ba.T = p->T;
+  ba.D = p->D;
+  ba.causal = p->causal;
+  ba.grp = p->H / kv_heads;
+  ba.fine_scale = p->fine_scale;
+  ba.pool_scale = 1.f / DASH_BLOCK;
+  ba.ca = make_ca(p->alpha, p->coarse_scale);
+  hipError_t e = launch_bwd_gqa(ba, dk, dv, dkbar, (hipStream_t)stream);
+  return e == hipSuccess ? DASH_OK : hip_fail(e, "grouped-query backward");
 }
 
 dash_status dash_bwd(const dash_params* p, const void* q, const void* k, const void* v, const void* o,

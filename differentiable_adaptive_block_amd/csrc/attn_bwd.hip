@@ -59,7 +59,7 @@ __device__ __forceinline__ size_t gidx(size_t bh, int ntile, int tile, int nb, i
 //   dS^T = P^T (dP^T - delta),  G += sum over the keys of dS
 //   dQ^T += K^T dS^T                 (D/32) x 2 MFMA (transposing reads of K)
 // The K tile uses the permutation that serves both read kinds.
-template <int D>
+template <int D, bool GQA>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   constexpr int KS = D / 16;
   constexpr int NDT = D / 32;
@@ -82,11 +82,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int wblk = qrow0 / DASH_BLOCK;
   const int i = qrow0 + j;
 
+  const size_t bkv = GQA ? bh / a.grp : bh;  // the key/value head
   const bf16_t* Q = reinterpret_cast<const bf16_t*>(a.q) + bh * a.T * D;
-  const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + bh * a.T * D;
-  const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + bh * a.T * D;
+  const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + bkv * a.T * D;
+  const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + bkv * a.T * D;
   const bf16_t* dO = reinterpret_cast<const bf16_t*>(a.dout) + bh * a.T * D;
-  const bf16_t* KB = reinterpret_cast<const bf16_t*>(a.kbar) + bh * nb * D;
+  const bf16_t* KB = reinterpret_cast<const bf16_t*>(a.kbar) + bkv * nb * D;
   const int* list = a.tile_blk + (bh * ntile + tile) * nb;
   const int cnt = a.tile_cnt[bh * ntile + tile];
   const CoarseArith ca = a.ca;
@@ -128,7 +129,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   };
   // priors of list entries e0..e0+31 into this wave's LDS table
   auto prior_chunk = [&](int e0) {
-    const f32x16 pacc = prior_chunk32<D>(KB, list, cnt, e0, qb, ca, tau_i, ln_i, a.causal, wblk);
+    f32x16 pacc;
+    if constexpr (GQA) {
+      const size_t bh0 = bkv * a.grp;  // the group's first query head
+      if (active) {
+        pacc = prior_chunk32_group<D>(KB, list, cnt, e0, reinterpret_cast<const bf16_t*>(a.q) + (bh0 * a.T + i) * D,
+                                      (size_t)a.T * D, a.tau + bh0 * a.T + i, a.lognorm + bh0 * a.T + i, a.T,
+                                      a.grp, ca, a.causal, wblk);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pacc[r] = -INFINITY;
+      }
+    } else {
+      pacc = prior_chunk32<D>(KB, list, cnt, e0, qb, ca, tau_i, ln_i, a.causal, wblk);
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) prs[w][acc_row32(r, l)][j] = pacc[r];
   };
@@ -302,8 +316,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int wb = b0 + kb;  // this wave's key block
 
   const bf16_t* Q = reinterpret_cast<const bf16_t*>(a.q) + bh * a.T * D;
-  const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + bh * a.T * D;
-  const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + bh * a.T * D;
+  const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + (bh / a.grp) * a.T * D;
+  const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + (bh / a.grp) * a.T * D;
   const bf16_t* dO = reinterpret_cast<const bf16_t*>(a.dout) + bh * a.T * D;
   const float sl2 = a.fine_scale * LOG2E_F;
 
@@ -613,7 +627,13 @@ __device__ __forceinline__ float sum8(float v) {
 // grid (ntile * 4, BH), 256 threads = 32 rows x 8 threads: thread c of a
 // row takes list slots e = c (mod 8) in the first two passes and columns
 // c G .. c G + G - 1 in the last.
-template <int D>
+// Grouped-query heads (GQA): the prior in pbuf is the group's log2 pbar and
+// gsum holds G summed over the group; the row's own p (whose Jacobian
+// applies) comes from its own scores, recomputed here by the 8 threads of the
+// row (one partial dot each, summed across them), with g_b = Gsum_b /
+// (grp pbar_b):  s_b g_b = p_b^(2-alpha) Gsum_b pbar_b^-1 / grp.  Pass 1
+// keeps log2 p in the row's own G slots, pass 2 overwrites them with dz.
+template <int D, bool GQA>
 __global__ __launch_bounds__(256) void bwd_coarse_kernel(BwdArgs a) {
   constexpr int G = D / 8;
   const int nb = a.T / DASH_BLOCK;
@@ -629,7 +649,59 @@ __global__ __launch_bounds__(256) void bwd_coarse_kernel(BwdArgs a) {
   const int cnt = a.tile_cnt[bh * ntile + tile];
   const float am2 = 2.f - (a.ca.softmax ? 1.f : 1.f + a.ca.am1);  // 2 - alpha
   const float am1n = am2 - 1.f;                                    // 1 - alpha
+  const size_t bkv = GQA ? bh / a.grp : bh;
   float ss = 0.f, ssg = 0.f;
+  if constexpr (GQA) {
+    // the row's query features cg G .. cg G + G - 1, as float
+    float qf[G];
+    {
+      const bf16_t* qr = reinterpret_cast<const bf16_t*>(a.q) + (bh * a.T + (valid ? i : 0)) * D + cg * G;
+#pragma unroll
+      for (int x = 0; x < G; ++x) qf[x] = valid ? bf2f(qr[x]) : 0.f;
+    }
+    const float tau_i = valid ? a.tau[bh * a.T + i] : 0.f, ln_i = valid ? a.lognorm[bh * a.T + i] : 0.f;
+    const float inv_grp = 1.f / (float)a.grp;
+    const bf16_t* KBc = reinterpret_cast<const bf16_t*>(a.kbar) + bkv * nb * D + cg * G;
+    for (int e = 0; e < cnt; ++e) {  // every thread of the row takes every entry (the dot is shared)
+      const int b = list[e];
+      const bf16_t* kr = KBc + (size_t)b * D;
+      float part = 0.f;
+#pragma unroll
+      for (int x = 0; x < G; ++x) part = fmaf(qf[x], bf2f(kr[x]), part);
+      const float zacc = sum8(part);
+      if ((e & 7) != cg || !valid || (a.causal && b >= own)) continue;
+      const size_t gi = gidx(bh, ntile, tile, nb, e, rt);
+      const float lpb2 = a.pbuf[gi];
+      if (lpb2 == -INFINITY) continue;
+      const float lp2 = a.ca.logp(a.ca.u_of(zacc), tau_i, ln_i) * LOG2E_F;
+      a.gbuf[gi] = lp2;
+      if (lp2 == -INFINITY) continue;
+      const float sv = __builtin_amdgcn_exp2f(am2 * lp2);
+      ss += sv;
+      ssg += sv * a.gsum[gidx(bkv, ntile, tile, nb, e, rt)] * __builtin_amdgcn_exp2f(-lpb2) * inv_grp;
+    }
+    ss = sum8(ss);
+    ssg = sum8(ssg);
+    const float ratio = ss > 0.f ? ssg / ss : 0.f;
+    if (valid) {
+      for (int e = cg; e < cnt; e += 8) {
+        const size_t gi = gidx(bh, ntile, tile, nb, e, rt);
+        float dz = 0.f;
+        if (!(a.causal && list[e] >= own)) {
+          const float lpb2 = a.pbuf[gi];
+          if (lpb2 != -INFINITY) {
+            const float lp2 = a.gbuf[gi];
+            if (lp2 != -INFINITY) {
+              const float sv = __builtin_amdgcn_exp2f(am2 * lp2);
+              const float gv = a.gsum[gidx(bkv, ntile, tile, nb, e, rt)] * __builtin_amdgcn_exp2f(-lpb2) * inv_grp;
+              dz = sv * gv - sv * ratio;
+            }
+          }
+        }
+        a.gbuf[gi] = dz;
+      }
+    }
+  } else {
   if (valid) {
     for (int e = cg; e < cnt; e += 8) {
       if (a.causal && list[e] >= own) continue;
@@ -655,9 +727,10 @@ __global__ __launch_bounds__(256) void bwd_coarse_kernel(BwdArgs a) {
       a.gbuf[gi] = dz;
     }
   }
+  }
   __syncthreads();  // every dz of the workgroup's rows is written
   if (!valid) return;
-  const bf16_t* KB = reinterpret_cast<const bf16_t*>(a.kbar) + bh * nb * D + cg * G;
+  const bf16_t* KB = reinterpret_cast<const bf16_t*>(a.kbar) + bkv * nb * D + cg * G;
   float acc[G];
 #pragma unroll
   for (int x = 0; x < G; ++x) acc[x] = 0.f;
@@ -811,6 +884,93 @@ __global__ void zero_f32_kernel(float* p, size_t n) {
   for (size_t x = (size_t)blockIdx.x * blockDim.x + threadIdx.x; x < n; x += (size_t)gridDim.x * blockDim.x) p[x] = 0.f;
 }
 
+// Grouped-query heads: G of the group's heads summed per (tile, listed
+// block, row) into gsum.  grid (ntile, BH / grp), 256 threads.
+__global__ __launch_bounds__(256) void bwd_gqa_gsum_kernel(BwdArgs a) {
+  const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
+  const int nb = a.T / DASH_BLOCK;
+  const int tile = blockIdx.x;
+  const size_t bkv = blockIdx.y, bh0 = bkv * a.grp;
+  const int cnt = a.tile_cnt[bh0 * ntile + tile];  // the group's heads share the list
+  for (int x = threadIdx.x; x < cnt * DASH_QTILE; x += blockDim.x) {
+    const int e = x / DASH_QTILE, rt = x % DASH_QTILE;
+    float g = 0.f;
+    for (int h = 0; h < a.grp; ++h) g += a.gbuf[gidx(bh0 + h, ntile, tile, nb, e, rt)];
+    a.gsum[gidx(bkv, ntile, tile, nb, e, rt)] = g;
+  }
+}
+
+// dK, dV (bf16, 8 per thread, fp32 sums) and dkbar of each KV head = the sum
+// of its query heads' partials, in head order.
+__global__ void bwd_gqa_reduce_kernel(const bf16_t* __restrict__ dkp, const bf16_t* __restrict__ dvp,
+                                      const float* __restrict__ dkbp, bf16_t* __restrict__ dk,
+                                      bf16_t* __restrict__ dv, float* __restrict__ dkbar, int BHkv, int grp,
+                                      size_t TD, size_t nbD) {
+  const size_t n8 = (size_t)BHkv * TD / 8;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t x = (size_t)blockIdx.x * blockDim.x + threadIdx.x; x < n8; x += stride) {
+    const size_t g = (x * 8) / TD, r = (x * 8) % TD;
+    float sk[8], sv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sk[e] = sv[e] = 0.f;
+    for (int h = 0; h < grp; ++h) {
+      const size_t src = ((size_t)g * grp + h) * TD + r;
+      const uint4 kw = *reinterpret_cast<const uint4*>(dkp + src);
+      const uint4 vw = *reinterpret_cast<const uint4*>(dvp + src);
+      const uint32_t ku[4] = {kw.x, kw.y, kw.z, kw.w}, vu[4] = {vw.x, vw.y, vw.z, vw.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sk[2 * e] += __uint_as_float(ku[e] << 16);
+        sk[2 * e + 1] += __uint_as_float(ku[e] & 0xFFFF0000u);
+        sv[2 * e] += __uint_as_float(vu[e] << 16);
+        sv[2 * e + 1] += __uint_as_float(vu[e] & 0xFFFF0000u);
+      }
+    }
+    uint32_t ko[4], vo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ko[e] = (uint32_t)f2bf(sk[2 * e]) | ((uint32_t)f2bf(sk[2 * e + 1]) << 16);
+      vo[e] = (uint32_t)f2bf(sv[2 * e]) | ((uint32_t)f2bf(sv[2 * e + 1]) << 16);
+    }
+    *reinterpret_cast<uint4*>(dk + x * 8) = make_uint4(ko[0], ko[1], ko[2], ko[3]);
+    *reinterpret_cast<uint4*>(dv + x * 8) = make_uint4(vo[0], vo[1], vo[2], vo[3]);
+  }
+  const size_t nkb = (size_t)BHkv * nbD;
+  for (size_t x = (size_t)blockIdx.x * blockDim.x + threadIdx.x; x < nkb; x += stride) {
+    const size_t g = x / nbD, r = x % nbD;
+    float sum = 0.f;
+    for (int h = 0; h < grp; ++h) sum += dkbp[((size_t)g * grp + h) * nbD + r];
+    dkbar[x] = sum;
+  }
+}
+
+hipError_t launch_bwd_gqa(const BwdArgs& a, void* dk, void* dv, float* dkbar, hipStream_t st) {
+  if (a.grp <= 1 || a.BH % a.grp) return hipErrorInvalidValue;
+  const size_t rows = (size_t)a.BH * a.T;
+  const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
+  const int nb = a.T / DASH_BLOCK;
+  hipError_t e;
+  bwd_delta_kernel<bf16_t><<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(
+      reinterpret_cast<const bf16_t*>(a.o), reinterpret_cast<const bf16_t*>(a.dout), a.delta, rows, a.D);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.D == 128) bwd_dq_kernel<128, true><<<ntile * a.BH, 256, 0, st>>>(a);
+  else bwd_dq_kernel<64, true><<<ntile * a.BH, 256, 0, st>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  bwd_gqa_gsum_kernel<<<dim3(ntile, a.BH / a.grp), 256, 0, st>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.D == 128) bwd_coarse_kernel<128, true><<<dim3(ntile * 4, a.BH), 256, 0, st>>>(a);
+  else bwd_coarse_kernel<64, true><<<dim3(ntile * 4, a.BH), 256, 0, st>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int ngrp = (nb + 1) / 2;
+  if (a.D == 128) bwd_dkdv_kernel<128><<<ngrp * a.BH, 512, 0, st>>>(a);
+  else bwd_dkdv_kernel<64><<<ngrp * a.BH, 512, 0, st>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  bwd_gqa_reduce_kernel<<<2048, 256, 0, st>>>(reinterpret_cast<const bf16_t*>(a.dk), reinterpret_cast<const bf16_t*>(a.dv),
+                                              a.dkbar, reinterpret_cast<bf16_t*>(dk), reinterpret_cast<bf16_t*>(dv), dkbar,
+                                              a.BH / a.grp, a.grp, (size_t)a.T * a.D, (size_t)nb * a.D);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t st) {
   const size_t rows = (size_t)a.BH * a.T;
   const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
@@ -820,11 +980,11 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t st) {
     bwd_delta_kernel<bf16_t><<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(
         reinterpret_cast<const bf16_t*>(a.o), reinterpret_cast<const bf16_t*>(a.dout), a.delta, rows, a.D);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (a.D == 128) bwd_dq_kernel<128><<<ntile * a.BH, 256, 0, st>>>(a);
-    else bwd_dq_kernel<64><<<ntile * a.BH, 256, 0, st>>>(a);
+    if (a.D == 128) bwd_dq_kernel<128, false><<<ntile * a.BH, 256, 0, st>>>(a);
+    else bwd_dq_kernel<64, false><<<ntile * a.BH, 256, 0, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (a.D == 128) bwd_coarse_kernel<128><<<dim3(ntile * 4, a.BH), 256, 0, st>>>(a);
-    else bwd_coarse_kernel<64><<<dim3(ntile * 4, a.BH), 256, 0, st>>>(a);
+    if (a.D == 128) bwd_coarse_kernel<128, false><<<dim3(ntile * 4, a.BH), 256, 0, st>>>(a);
+    else bwd_coarse_kernel<64, false><<<dim3(ntile * 4, a.BH), 256, 0, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int ngrp = (nb + 1) / 2;
     if (a.D == 128) bwd_dkdv_kernel<128><<<ngrp * a.BH, 512, 0, st>>>(a);

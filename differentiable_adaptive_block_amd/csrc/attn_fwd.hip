@@ -33,7 +33,9 @@
 // The per-(row, block) prior is recomputed from the Stage-1 score
 // arithmetic (coarse_acc_chunk) for 32 listed blocks at a time and kept in
 // registers.
-template <int D>
+// GQA: grouped-query heads (a.grp > 1): keys, values and summaries are the
+// KV head's, and the prior is the group's aggregated one (prior_chunk32_group).
+template <int D, bool GQA>
 __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
   constexpr int CH = D / 8;          // 16-byte chunks per row
   constexpr int KS = D / 16;         // k-steps of the S product
@@ -66,9 +68,10 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
   const int i = qrow0 + j;
 
   const bf16_t* Q = reinterpret_cast<const bf16_t*>(a.q) + bh * a.T * D;
-  const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + bh * a.T * D;
-  const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + bh * a.T * D;
-  const bf16_t* KB = reinterpret_cast<const bf16_t*>(a.kbar) + bh * nb * D;
+  const size_t bkv = GQA ? bh / a.grp : bh;  // the key/value head
+  const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + bkv * a.T * D;
+  const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + bkv * a.T * D;
+  const bf16_t* KB = reinterpret_cast<const bf16_t*>(a.kbar) + bkv * nb * D;
   const int* glist = a.tile_blk + (bh * ntile + tile) * nb;
   const int cnt = a.tile_cnt[bh * ntile + tile];
   const CoarseArith ca = a.ca;
@@ -110,7 +113,15 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
 
   f32x16 pacc;
   auto prior_chunk = [&](int e0) {
-    if (active) pacc = prior_chunk32<D>(KB, list, cnt, e0, qb, ca, tau_i, ln_i, a.causal, wblk);
+    if (!active) return;
+    if constexpr (GQA) {
+      const size_t bh0 = bkv * a.grp;  // the group's first query head
+      pacc = prior_chunk32_group<D>(KB, list, cnt, e0, reinterpret_cast<const bf16_t*>(a.q) + (bh0 * a.T + i) * D,
+                                    (size_t)a.T * D, a.tau + bh0 * a.T + i, a.lognorm + bh0 * a.T + i, a.T, a.grp,
+                                    ca, a.causal, wblk);
+    } else {
+      pacc = prior_chunk32<D>(KB, list, cnt, e0, qb, ca, tau_i, ln_i, a.causal, wblk);
+    }
   };
   auto prior_of = [&](int e) -> float { return prior_pick(pacc, e); };
 
@@ -339,9 +350,15 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, hipStream_t st) {
   if (dtype == 1) {
     const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
     dim3 grid(ntile * a.BH);
-    if (a.D == 128) fwd_mfma_kernel<128><<<grid, 256, 0, st>>>(a);
-    else fwd_mfma_kernel<64><<<grid, 256, 0, st>>>(a);
+    if (a.grp > 1) {
+      if (a.D == 128) fwd_mfma_kernel<128, true><<<grid, 256, 0, st>>>(a);
+      else fwd_mfma_kernel<64, true><<<grid, 256, 0, st>>>(a);
+    } else {
+      if (a.D == 128) fwd_mfma_kernel<128, false><<<grid, 256, 0, st>>>(a);
+      else fwd_mfma_kernel<64, false><<<grid, 256, 0, st>>>(a);
+    }
   } else {
+    if (a.grp > 1) return hipErrorNotSupported;
     fwd_generic_kernel<float><<<dim3(a.T, a.BH), 64, 0, st>>>(a);
   }
   return hipGetLastError();

@@ -7,8 +7,9 @@
 
 struct SelectArgs {
   const void* q;      // [BH, T, D]
-  const void* kbar;   // [BH, nb, D]
+  const void* kbar;   // [BH / grp, nb, D]
   int T, D, causal;
+  int grp;            // query heads per key/value head (1: one each)
   CoarseArith ca;
   float* tau;         // [BH, T]
   float* lognorm;     // [BH, T]
@@ -29,6 +30,7 @@ struct FwdArgs {
   const int* tile_cnt;
   const int* tile_blk;
   int BH, T, D, causal;
+  int grp;  // query heads per key/value head: k, v, kbar are indexed by bh / grp
   float fine_scale;
   CoarseArith ca;
 };
@@ -95,6 +97,48 @@ __device__ __forceinline__ f32x16 prior_chunk32(const bf16_t* KB, const int* lis
   return pacc;
 }
 
+// prior_chunk32 for G query heads sharing one key/value head (grouped-query
+// heads with entmax head aggregation): the prior of a listed block for this
+// lane's row is log2 of pbar = (1/G) sum over the group's heads g of p_g,
+// each head's p_g from its own query row at the same position (q0 + g
+// head_stride), its own tau and log-normaliser, and the same summaries;
+// -inf where no head of the group selected the block (and, causal, for the
+// row's own block and later ones).  The list must be the group's union.
+template <int D>
+__device__ __forceinline__ f32x16 prior_chunk32_group(const bf16_t* KB, const int* list, int cnt, int e0,
+                                                      const bf16_t* q0, size_t head_stride, const float* tau0,
+                                                      const float* ln0, size_t stat_stride, int G,
+                                                      const CoarseArith& ca, int causal, int wblk) {
+  const int l = lane_id(), j = l & 31, h = l >> 5;
+  const int ent = e0 + j;
+  const int brow = ent < cnt ? list[ent] : 0;
+  f32x16 psum;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) psum[r] = 0.f;
+  for (int g = 0; g < G; ++g) {
+    bf16x8 qb[D / 16];
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) qb[s] = load8(q0 + g * head_stride + 16 * s + 8 * h);
+    const float tg = tau0[g * stat_stride], lg = ln0[g * stat_stride];
+    const f32x16 z = coarse_acc_chunk<D>(KB, brow, qb);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) psum[r] += __expf(ca.logp(ca.u_of(z[r]), tg, lg));
+  }
+  const float lg2G = __log2f((float)G);
+  f32x16 pacc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int en = e0 + acc_row32(r, l);
+    float p2 = -INFINITY;
+    if (en < cnt && psum[r] > 0.f) {
+      const int bb = list[en];
+      if (!causal || bb < wblk) p2 = __log2f(psum[r]) - lg2G;
+    }
+    pacc[r] = p2;
+  }
+  return pacc;
+}
+
 // The prior of list entry e for this lane's row from prior_chunk32's
 // registers: slot e%32 sits in register 4(slot/8) + slot%4 of the half
 // (slot/4)%2; the other half's value comes across with permlane32_swap.
@@ -122,6 +166,7 @@ __device__ __forceinline__ float dot_row(const float* qs, const T* kr, int D) {
 hipError_t launch_pool(const void* k, void* kbar, int BH, int T, int D, int dtype, hipStream_t st);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t st);
 hipError_t launch_select(const SelectArgs& a, int BH, int dtype, hipStream_t st);
+hipError_t launch_group_union(uint32_t* tile_bits, int BH, int grp, size_t words_per_head, hipStream_t st);
 hipError_t launch_tile_lists(uint32_t* tile_bits, int* tile_cnt, int* tile_blk, int BH, int T, int causal,
                              hipStream_t st);
 hipError_t launch_fwd(const FwdArgs& a, int dtype, hipStream_t st);

@@ -150,7 +150,7 @@ __global__ __launch_bounds__(64 * NW) void select_mfma_kernel(SelectArgs a) {
   for (int x = threadIdx.x; x < nbw; x += 64 * NW) uni[x] = 0u;
 
   const bf16_t* qh = reinterpret_cast<const bf16_t*>(a.q) + bh * a.T * D;
-  const bf16_t* kb = reinterpret_cast<const bf16_t*>(a.kbar) + bh * nb * D;
+  const bf16_t* kb = reinterpret_cast<const bf16_t*>(a.kbar) + (bh / a.grp) * nb * D;
   if (nc > 0) {
     bf16x8 qb[D / 16];
 #pragma unroll
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(512, 4) void select_chunked_kernel(SelectArgs a) {
   const size_t row_g = bh * a.T + row0 + row;
 
   const bf16_t* qh = reinterpret_cast<const bf16_t*>(a.q) + bh * a.T * D;
-  const bf16_t* kb = reinterpret_cast<const bf16_t*>(a.kbar) + bh * nb * D;
+  const bf16_t* kb = reinterpret_cast<const bf16_t*>(a.kbar) + (bh / a.grp) * nb * D;
   float u[NPL];
   if (nc > 0) {
     for (int x = tid; x < 32 * (D / 8); x += 512) {
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(64) void select_generic_kernel(SelectArgs a) {
   const int i = blockIdx.x;
   const int l = lane_id();
   const T* q = reinterpret_cast<const T*>(a.q) + (bh * a.T + i) * D;
-  const T* kb = reinterpret_cast<const T*>(a.kbar) + bh * nb * D;
+  const T* kb = reinterpret_cast<const T*>(a.kbar) + (bh / a.grp) * nb * D;
   for (int d = l; d < D; d += 64) qs[d] = to_f<T>(q[d]);
   __syncthreads();
   const int nc = a.causal ? i / DASH_BLOCK : nb;
@@ -354,6 +354,25 @@ hipError_t launch_pool(const void* k, void* kbar, int BH, int T_, int D, int dty
     pool_kernel<bf16_t><<<grid, 64, 0, st>>>((const bf16_t*)k, (bf16_t*)kbar, T_, D);
   else
     pool_kernel<float><<<grid, 64, 0, st>>>((const float*)k, (float*)kbar, T_, D);
+  return hipGetLastError();
+}
+
+// Grouped-query heads share one block list per tile: OR the tile bit sets
+// of the grp heads of each group and give every head of the group the union.
+__global__ void group_union_kernel(uint32_t* bits, int ngroups, int grp, size_t words) {
+  const size_t n = (size_t)ngroups * words;
+  for (size_t x = (size_t)blockIdx.x * blockDim.x + threadIdx.x; x < n; x += (size_t)gridDim.x * blockDim.x) {
+    const size_t g = x / words, wi = x % words;
+    uint32_t* base = bits + g * grp * words + wi;
+    uint32_t u = 0;
+    for (int h = 0; h < grp; ++h) u |= base[(size_t)h * words];
+    for (int h = 0; h < grp; ++h) base[(size_t)h * words] = u;
+  }
+}
+
+hipError_t launch_group_union(uint32_t* tile_bits, int BH, int grp, size_t words_per_head, hipStream_t st) {
+  if (grp <= 1) return hipSuccess;
+  group_union_kernel<<<1024, 256, 0, st>>>(tile_bits, BH / grp, grp, words_per_head);
   return hipGetLastError();
 }
 

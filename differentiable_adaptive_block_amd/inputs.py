@@ -124,18 +124,24 @@ def _planted_rows(kh, rows_pos, causal, lo, hi, g, device):
 
 
 def make_prefill(B, H, T, D, dtype="bf16", causal=True, planted=(1, 8), seed=0, device="cpu",
-                 with_dout=True):
-    """Q, K, V (and dO) of shape [B, H, T, D].
+                 with_dout=True, kv_heads=None):
+    """Q, K, V (and dO): q and dO [B, H, T, D], k and v [B, kv_heads, T, D]
+    (kv_heads defaults to H; query head h is planted toward the blocks of
+    KV head h // (H / kv_heads)).
 
     ``planted=None`` gives iid N(0,1) queries; otherwise (lo, hi) plants each
     query toward lo..hi earlier blocks as described in the module docstring.
     """
     if T % BLOCK:
         raise ValueError("T must be a multiple of 64")
+    Hkv = H if kv_heads is None else kv_heads
+    if Hkv < 1 or H % Hkv:
+        raise ValueError("kv_heads must divide H")
+    G = H // Hkv
     td = torch_dtype(dtype)
     g = _gen(seed, device)
-    k = _randn((B * H, T, D), g, td, device, chunk_rows=4).view(B, H, T, D)
-    v = _randn((B * H, T, D), g, td, device, chunk_rows=4).view(B, H, T, D)
+    k = _randn((B * Hkv, T, D), g, td, device, chunk_rows=4).view(B, Hkv, T, D)
+    v = _randn((B * Hkv, T, D), g, td, device, chunk_rows=4).view(B, Hkv, T, D)
     if planted is None:
         q = _randn((B * H, T, D), g, td, device, chunk_rows=4).view(B, H, T, D)
     else:
@@ -145,7 +151,7 @@ def make_prefill(B, H, T, D, dtype="bf16", causal=True, planted=(1, 8), seed=0, 
         for b in range(B):
             for h in range(H):
                 noise = torch.randn((T, D), generator=g, dtype=torch.float32, device=device).double()
-                qp = 0.5 * noise + _planted_rows(k[b, h], pos, causal, lo, hi, g, device)
+                qp = 0.5 * noise + _planted_rows(k[b, h // G], pos, causal, lo, hi, g, device)
                 q[b, h] = qp.float().to(td)
     out = dict(q=q, k=k, v=v)
     if with_dout:

@@ -192,6 +192,41 @@ dash_status dash_pool_attn_bwd(const dash_params* p, const void* k, const float*
                                void* dk, float* dw, void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/*
+ * Grouped-query heads with entmax head aggregation.  p->H query heads share
+ * kv_heads key/value heads (kv_heads divides H; query head h uses KV head
+ * h / (H / kv_heads), the expansion of a repeat_kv step, which the
+ * codewithpapers.app entry for the DashAttention paper lists in its prefill
+ * block selection).  The montana-research page ("Non-dispersive attention at
+ * long context") calls entmax head aggregation non-dispersive; here it is:
+ * every query head gets its own alpha-entmax p_h over its KV head's
+ * summaries, the G = H / kv_heads heads of a group share pbar = (1/G) sum_h
+ * p_h, and each attends the blocks of pbar's support (the union of the
+ * heads' supports) with prior log pbar.
+ *
+ * k, v: [B, kv_heads, T, D]; kbar: [B, kv_heads, T/64, D] (written); q, o:
+ * [B, H, T, D]; lse [B, H, T]; `sel` as for H heads: tau, lognorm, nsel and
+ * mask are each head's own entmax, the tile lists the group's union.
+ * kv_heads == H is the per-head method (dash_fwd).  bf16 only when
+ * kv_heads < H.
+ */
+dash_status dash_fwd_gqa(const dash_params* p, int32_t kv_heads, const void* q, const void* k,
+                         const void* v, void* o, float* lse, void* kbar, const dash_sel* sel,
+                         void* stream);
+
+/*
+ * Backward of dash_fwd_gqa: dq [B, H, T, D]; dk, dv [B, kv_heads, T, D] (the
+ * sums over each group's query heads, dk with the mean-pooling path);
+ * dkbar [B, kv_heads, T/64, D] f32.  G_b, the gradient of log pbar_b, sums
+ * the group's heads; each head's p_h then takes its own entmax Jacobian with
+ * dL/dp_h = G / (G_heads pbar).  Workspace: dash_bwd_gqa_workspace_bytes.
+ */
+size_t dash_bwd_gqa_workspace_bytes(const dash_params* p, int32_t kv_heads);
+dash_status dash_bwd_gqa(const dash_params* p, int32_t kv_heads, const void* q, const void* k,
+                         const void* v, const void* o, const float* lse, const void* dout,
+                         const void* kbar, const dash_sel* sel, void* dq, void* dk, void* dv,
+                         float* dkbar, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Decode shapes: S sequences x H heads, one new query each, cache length N. */
 typedef struct {
   int32_t S, H, N, D;   /* N multiple of 64, 64 <= N <= 131072; D = 128 (bf16 only) */

@@ -207,3 +207,20 @@ def test_summariser_entry_validation(L):
     bargs = [FAKE] * 7 + [ctypes.byref(_sel())] + [FAKE] * 5
     assert L.dash_bwd_no_pool(ctypes.byref(p), *bargs, wsb - 1, None) == _lib.DASH_EWORKSPACE
     assert L.dash_bwd_no_pool(ctypes.byref(_params(D=96)), *bargs, wsb, None) != _lib.DASH_OK
+
+
+def test_gqa_entry_validation(L):
+    p = _params(H=4)
+    # q, k, v, o, lse, kbar, sel
+    args = [FAKE] * 6 + [ctypes.byref(_sel())]
+    assert L.dash_fwd_gqa(ctypes.byref(p), 3, *args, None) == _lib.DASH_EINVAL
+    assert "kv_heads" in L.dash_last_error().decode()
+    assert L.dash_fwd_gqa(ctypes.byref(p), 0, *args, None) == _lib.DASH_EINVAL
+    assert L.dash_fwd_gqa(ctypes.byref(_params(H=4, dtype=_lib.DASH_F32, D=64)), 2, *args, None) == _lib.DASH_EUNSUPPORTED
+    assert L.dash_bwd_gqa_workspace_bytes(ctypes.byref(p), 3) == 0
+    need = L.dash_bwd_gqa_workspace_bytes(ctypes.byref(p), 2)
+    assert need > L.dash_bwd_workspace_bytes(ctypes.byref(p)) > 0
+    assert L.dash_bwd_gqa_workspace_bytes(ctypes.byref(p), 4) == L.dash_bwd_workspace_bytes(ctypes.byref(p))
+    bargs = [FAKE] * 7 + [ctypes.byref(_sel())] + [FAKE] * 5
+    assert L.dash_bwd_gqa(ctypes.byref(p), 2, *bargs, need - 1, None) == _lib.DASH_EWORKSPACE
+    assert L.dash_bwd_gqa(ctypes.byref(p), 3, *bargs, need, None) == _lib.DASH_EINVAL

@@ -1,0 +1,146 @@
+"""GPU parity of grouped-query heads with entmax head aggregation.
+
+dash_fwd_gqa and dash_bwd_gqa (through the C ABI) against the float64
+oracle's forward_rows_gqa and backward_gqa: each head's own selection
+(tau, counts, masks) and the outputs to the usual tolerances, the gradients
+to 5e-2 relative L2, the summaries of the KV heads bit for bit; one KV head
+per query head is dash_fwd / dash_bwd bit for bit.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from differentiable_adaptive_block_amd import inputs
+from parity import check_rows, rel_l2, unpack_mask
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _np64(t):
+    return t.double().cpu().numpy()
+
+
+def _gpu(r, nb):
+    sel = r["sel"]
+    return dict(o=r["o"].float().cpu().numpy(), lse=r["lse"].cpu().numpy(), tau=sel.tau.cpu().numpy(),
+                nsel=sel.nsel.cpu().numpy(), mask=unpack_mask(sel.mask, nb))
+
+
+CASES = [
+    # name, B, H, Hkv, T, D, causal, alpha, coarse multiple, planted
+    ("h4-kv2-causal-ragged", 1, 4, 2, 1088, 128, True, 1.5, 4.0, (1, 4)),
+    ("h4-kv1-noncausal-d64", 1, 4, 1, 576, 64, False, 1.25, 4.0, (1, 3)),
+    ("b2-h8-kv2-causal", 2, 8, 2, 512, 128, True, 1.5, 6.0, (1, 3)),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_gqa_forward_and_backward_small(case):
+    from differentiable_adaptive_block_amd import api
+    name, B, H, Hkv, T, D, causal, alpha, csm, planted = case
+    _say(f"[gqa] {name} B{B} H{H} Hkv{Hkv} T{T} D{D} causal={causal} alpha={alpha}")
+    w = inputs.make_prefill(B, H, T, D, "bf16", causal, planted, seed=81 + T, device="cpu", with_dout=True,
+                            kv_heads=Hkv)
+    w = {k: v.to(DEV) for k, v in w.items()}
+    cs = csm / math.sqrt(D)
+    r = api.forward(w["q"], w["k"], w["v"], alpha=alpha, causal=causal, coarse_scale=cs)
+    g = api.backward(w["q"], w["k"], w["v"], r["o"], r["lse"], w["dout"], r["kbar"], r["sel"], r["params"])
+    torch.cuda.synchronize()
+    prm = oracle.Params(alpha=alpha, causal=causal, coarse_scale=cs, storage="bf16")
+    q64, k64, v64, d64 = (_np64(w[x]) for x in ("q", "k", "v", "dout"))
+    for b in range(B):
+        for kv in range(Hkv):
+            np.testing.assert_array_equal(_np64(r["kbar"][b, kv]), oracle.pool_blocks(k64[b, kv], 64, "bf16"))
+    nb = T // 64
+    rows = [(b, h, i) for b in range(B) for h in range(H) for i in range(T)]
+    ora = oracle.forward_rows_gqa(q64, k64, v64, prm, rows)
+    st = check_rows(_gpu(r, nb), ora, rows, torch.bfloat16, alpha, name)
+    ref = oracle.backward_gqa(q64, k64, v64, d64, prm)
+    errs = {n: rel_l2(_np64(g[n]), ref[n]) for n in ("dq", "dk", "dv", "dkbar")}
+    _say(f"  forward {st}; rel-L2 {errs}")
+    for n, e in errs.items():
+        assert e <= 5e-2, (name, n, e)
+    # the group's heads share one block list per tile: the union of their masks
+    ntile = (T + 127) // 128
+    cnt = r["sel"].tile_cnt.view(B, H, ntile).cpu()
+    G = H // Hkv
+    for kv in range(Hkv):
+        for h in range(kv * G + 1, (kv + 1) * G):
+            assert torch.equal(cnt[:, h], cnt[:, kv * G])
+
+
+def test_one_kv_head_per_query_head_is_the_per_head_path():
+    from differentiable_adaptive_block_amd import _lib, api
+    B, H, T, D = 1, 2, 1024, 128
+    w = inputs.make_prefill(B, H, T, D, "bf16", True, (1, 4), seed=85, device="cpu", with_dout=True)
+    w = {k: v.to(DEV) for k, v in w.items()}
+    cs = 4.0 / math.sqrt(D)
+    r = api.forward(w["q"], w["k"], w["v"], alpha=1.5, causal=True, coarse_scale=cs)
+    p = r["params"]
+    o = torch.empty_like(w["q"])
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=DEV)
+    kbar = torch.empty((B, H, T // 64, D), dtype=torch.bfloat16, device=DEV)
+    sel = api.alloc_selection(p, DEV, True)
+    st = torch.cuda.current_stream().cuda_stream
+    _lib.fwd_gqa(p, H, w["q"].data_ptr(), w["k"].data_ptr(), w["v"].data_ptr(), o.data_ptr(), lse.data_ptr(),
+                 kbar.data_ptr(), sel.as_c(), st)
+    g0 = api.backward(w["q"], w["k"], w["v"], r["o"], r["lse"], w["dout"], r["kbar"], r["sel"], p)
+    dq, dk, dv = (torch.empty_like(w[x]) for x in ("q", "k", "v"))
+    dkbar = torch.empty((B, H, T // 64, D), dtype=torch.float32, device=DEV)
+    wsb = _lib.bwd_gqa_workspace_bytes(p, H)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    _lib.bwd_gqa(p, H, w["q"].data_ptr(), w["k"].data_ptr(), w["v"].data_ptr(), r["o"].data_ptr(),
+                 r["lse"].data_ptr(), w["dout"].data_ptr(), r["kbar"].data_ptr(), r["sel"].as_c(), dq.data_ptr(),
+                 dk.data_ptr(), dv.data_ptr(), dkbar.data_ptr(), ws.data_ptr(), wsb, st)
+    torch.cuda.synchronize()
+    assert torch.equal(o, r["o"]) and torch.equal(lse, r["lse"]) and torch.equal(kbar, r["kbar"])
+    for n, t in (("dq", dq), ("dk", dk), ("dv", dv), ("dkbar", dkbar)):
+        assert torch.equal(t, g0[n]), n
+
+
+def test_gqa_deterministic():
+    from differentiable_adaptive_block_amd import api
+    w = inputs.make_prefill(1, 4, 1024, 128, "bf16", True, (1, 4), seed=86, device="cpu", with_dout=True, kv_heads=1)
+    w = {k: v.to(DEV) for k, v in w.items()}
+    outs = []
+    for _ in range(2):
+        r = api.forward(w["q"], w["k"], w["v"], alpha=1.5, causal=True, coarse_scale=4 / math.sqrt(128))
+        g = api.backward(w["q"], w["k"], w["v"], r["o"], r["lse"], w["dout"], r["kbar"], r["sel"], r["params"])
+        outs.append((r["o"], g["dq"], g["dk"], g["dv"], g["dkbar"]))
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_gqa_16k_sampled():
+    from differentiable_adaptive_block_amd import api
+    B, H, Hkv, T, D = 1, 32, 8, 16384, 128
+    _say(f"[gqa] 16K prefill B{B} H{H} Hkv{Hkv} T{T} D{D}")
+    w = inputs.make_prefill(B, H, T, D, "bf16", True, (1, 8), seed=87, device=DEV, with_dout=False, kv_heads=Hkv)
+    cs = 1.0 / math.sqrt(D)
+    r = api.forward(w["q"], w["k"], w["v"], alpha=1.5, causal=True, coarse_scale=cs)
+    torch.cuda.synchronize()
+    prm = oracle.Params(alpha=1.5, causal=True, coarse_scale=cs, storage="bf16")
+    rng = np.random.default_rng(88)
+    rows = [(0, int(h), int(i)) for h, i in zip(rng.integers(0, H, 8), rng.integers(64, T, 8))]
+    rows += [(0, 5, T - 1), (0, 30, 70)]
+    # the oracle reads only the rows' own KV heads and positions up to the row
+    q64 = np.zeros((B, H, T, D))
+    for (_, h, i) in rows:
+        q64[0, (h // 4) * 4:(h // 4) * 4 + 4, i] = _np64(w["q"][0, (h // 4) * 4:(h // 4) * 4 + 4, i])
+    k64, v64 = _np64(w["k"]), _np64(w["v"])
+    ora = oracle.forward_rows_gqa(q64, k64, v64, prm, rows)
+    gpu = _gpu(r, T // 64)
+    st = check_rows({k: v for k, v in gpu.items()}, ora, rows, torch.bfloat16, 1.5, "gqa 16K")
+    _say(f"  ok {st}")
