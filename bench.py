@@ -320,6 +320,86 @@ def _time_summariser(k, head, p, steps):
     return out
 
 
+def _popcount32(x):
+    x = x.to(torch.int64) & 0xFFFFFFFF
+    x = x - ((x >> 1) & 0x55555555)
+    x = (x & 0x33333333) + ((x >> 2) & 0x33333333)
+    x = (x + (x >> 4)) & 0x0F0F0F0F
+    return ((x * 0x01010101) & 0xFFFFFFFF) >> 24
+
+
+def bench_gqa(steps, warmup, device, kv_heads=8):
+    """Grouped-query heads with entmax head aggregation on the 16K causal prefill
+    shape (B1 H32 T16384 D128, coarse scale 1/sqrt(128)) with 8 KV heads (4 query
+    heads per group): dash_fwd_gqa time and useful Stage-2 work over the groups'
+    union supports; then one training step (forward + dash_bwd_gqa)."""
+    from differentiable_adaptive_block_amd import _lib, api, inputs
+
+    wl = inputs.CONFIGS["c2"]
+    sh = wl.shape
+    B, H, T, D = sh["B"], sh["H"], sh["T"], sh["D"]
+    w = inputs.make_prefill(B, H, T, D, wl.dtype, True, wl.planted, wl.seed + 400, device=device, with_dout=True,
+                            kv_heads=kv_heads)
+    q, k, v, dout = w["q"], w["k"], w["v"], w["dout"]
+    r = api.forward(q, k, v, alpha=1.5, causal=True, coarse_scale=wl.coarse_scale, want_mask=True)
+    torch.cuda.synchronize()
+    G = H // kv_heads
+    words = r["sel"].mask.view(B, kv_heads, G, T, -1)
+    union = words[:, :, 0]
+    for g in range(1, G):
+        union = union | words[:, :, g]
+    union_blocks = float(_popcount32(union).sum()) * G  # every head of a group attends the union
+    own_blocks = float(r["sel"].nsel.to(torch.int64).sum())
+    p = r["params"]
+    sel = api.alloc_selection(p, q.device, want_mask=False)
+    csel = sel.as_c()
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    kbar = torch.empty((B, kv_heads, T // 64, D), dtype=q.dtype, device=q.device)
+    st = torch.cuda.current_stream().cuda_stream
+
+    def fwd():
+        _lib.fwd_gqa(p, kv_heads, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                     kbar.data_ptr(), csel, st)
+
+    for _ in range(warmup):
+        fwd()
+    torch.cuda.synchronize()
+    t0, t1 = _events(2)
+    t0.record()
+    for _ in range(steps):
+        fwd()
+    t1.record()
+    torch.cuda.synchronize()
+    fwd_ms = t0.elapsed_time(t1) / steps
+    assert torch.equal(o, r["o"]), "timed forward differs from the validated forward"
+    pairs = 64 * union_blocks + B * H * (T // 64) * (64 * 65 // 2)
+    useful = 4.0 * D * pairs
+    # training step: forward + backward
+    for _ in range(warmup):
+        f = api.forward(q, k, v, alpha=1.5, causal=True, coarse_scale=wl.coarse_scale, want_mask=False)
+        api.backward(q, k, v, f["o"], f["lse"], dout, f["kbar"], f["sel"], f["params"])
+    torch.cuda.synchronize()
+    t0, t1 = _events(2)
+    t0.record()
+    for _ in range(steps):
+        f = api.forward(q, k, v, alpha=1.5, causal=True, coarse_scale=wl.coarse_scale, want_mask=False)
+        api.backward(q, k, v, f["o"], f["lse"], dout, f["kbar"], f["sel"], f["params"])
+    t1.record()
+    torch.cuda.synchronize()
+    train_ms = t0.elapsed_time(t1) / steps
+    res = dict(B=B, H=H, kv_heads=kv_heads, T=T, D=D, coarse_scale=wl.coarse_scale, fwd_ms=fwd_ms,
+               tokens_per_s=B * T / (fwd_ms / 1e3), union_pair_density=union_blocks / (B * H * sum(i // 64 for i in range(T))),
+               own_pair_density=own_blocks / (B * H * sum(i // 64 for i in range(T))),
+               useful_fwd_tflop=useful / 1e12, fwd_tflops=useful / 1e12 / (fwd_ms / 1e3),
+               train_step_ms=train_ms, train_tokens_per_s=B * T / (train_ms / 1e3),
+               work="useful FLOPs = 4*D*(64*sum over heads of the group's union blocks + causal diagonal pairs); "
+                    "fwd_tflops over the whole forward (selection included)")
+    del w, q, k, v, dout, r
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_decode(name, steps, warmup, device):
     """Time dash_decode (select + split-KV attend + combine) on a named decode workload."""
     from differentiable_adaptive_block_amd import _lib, api, inputs
@@ -507,6 +587,10 @@ def main():
         r3c, _ = bench_prefill("c3cal", max(2, args.steps // 3), 1, dev)
         log(f"c3cal: {r3c}")
         extra["prefill_64k_calibrated"] = r3c
+
+    gq = bench_gqa(max(3, args.steps // 2), 1, dev)
+    log(f"gqa 16K: {gq}")
+    extra["prefill_16k_gqa"] = gq
 
     if not args.no_decode:
         dec = {}

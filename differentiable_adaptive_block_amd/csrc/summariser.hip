@@ -123,17 +123,30 @@ __global__ __launch_bounds__(64) void pool_attn_bwd_kernel(const T* __restrict__
   }
 }
 
-// dw[h][c] = sum over (batch, block) of the partials, in a fixed order.
-__global__ void reduce_dw_kernel(const float* __restrict__ dw_part, float* __restrict__ dw, int B, int H, int nb,
-                                 int D) {
+// dw[h][c] = sum over (batch, block) of the partials, in a fixed order:
+// grid (H, ceil(D / 16)), 256 threads = 16 columns x 16 row groups; thread
+// (c, r) sums the partials r, r + 16, ... of its column, then the 16 sums
+// are added in row-group order.
+__global__ __launch_bounds__(256) void reduce_dw_kernel(const float* __restrict__ dw_part, float* __restrict__ dw,
+                                                        int B, int H, int nb, int D) {
+  __shared__ float red[16][17];
   const int h = blockIdx.x;
-  for (int c = threadIdx.x; c < D; c += blockDim.x) {
-    float acc = 0.f;
-    for (int bb = 0; bb < B; ++bb) {
-      const float* src = dw_part + ((size_t)(bb * H + h) * nb) * D + c;
-      for (int b = 0; b < nb; ++b) acc += src[(size_t)b * D];
+  const int cl = threadIdx.x & 15, rg = threadIdx.x >> 4;
+  const int c = blockIdx.y * 16 + cl;
+  float acc = 0.f;
+  if (c < D) {
+    const int n = B * nb;  // partial rows of head h: (batch bb, block b) -> bb * nb + b
+    for (int x = rg; x < n; x += 16) {
+      const int bb = x / nb, b = x % nb;
+      acc += dw_part[((size_t)(bb * H + h) * nb + b) * D + c];
     }
-    dw[(size_t)h * D + c] = acc;
+  }
+  red[rg][cl] = acc;
+  __syncthreads();
+  if (rg == 0 && c < D) {
+    float sum = 0.f;
+    for (int r = 0; r < 16; ++r) sum += red[r][cl];
+    dw[(size_t)h * D + c] = sum;
   }
 }
 
@@ -371,6 +384,6 @@ hipError_t launch_pool_attn_bwd(const void* k, const float* w, const float* dkba
     pool_attn_bwd_kernel<float><<<grid, 64, 0, st>>>((const float*)k, w, dkbar, (float*)dk, dw_part, H, T_, D);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  reduce_dw_kernel<<<H, 128, 0, st>>>(dw_part, dw, B, H, nb, D);
+  reduce_dw_kernel<<<dim3(H, (D + 15) / 16), 256, 0, st>>>(dw_part, dw, B, H, nb, D);
   return hipGetLastError();
 }
