@@ -35,6 +35,10 @@ Readings taken where the pages are silent (each is restated in the design doc):
 * R20 the learned summariser: per head a vector w (initialised at zero);
   a block's summary is sum_j softmax_j(w . k_j) k_j over its keys, which is
   mean pooling at w = 0.
+* R22 a causal prefill of T tokens, T not a multiple of the block: the
+  last block is partial; it is the own block of its queries and never a
+  candidate of any query, so only the complete blocks get summaries.
+  Non-causal attention needs whole blocks (every block is a candidate).
 * R19 a cache of n tokens (any n >= 1): the query is at position n-1, its
   candidates are the complete blocks before its own, and its own block is
   attended over its cached tokens only (row n-1 of a causal prefill over
@@ -166,7 +170,16 @@ def pool_attention_vjp(k_head, w, dkbar, block: int):
 
 
 def summarise(k_head, prm: "Params", w_h=None):
-    """Stage 0 of one head: mean pooling, or the learned summariser when ``w_h`` is given."""
+    """Stage 0 of one head: mean pooling, or the learned summariser when ``w_h`` is given.
+
+    Summaries of the complete blocks only: with a partial last block
+    (causal attention, R22) the partial block gets none.
+    """
+    T = k_head.shape[0]
+    if T % prm.block:
+        if not prm.causal:
+            raise ValueError("non-causal attention needs T to be a multiple of the block size")
+        k_head = k_head[: (T // prm.block) * prm.block]
     if w_h is None:
         return pool_blocks(k_head, prm.block, prm.storage)
     return pool_attention(k_head, w_h, prm.block, prm.storage)
@@ -374,12 +387,14 @@ def _grad_arrays(q):
 
 
 def _pool_backward(k, prm: Params, w, grads, b, h):
-    """Send dkbar of head (b, h) through Stage 0 into dk (and dw)."""
+    """Send dkbar of head (b, h) through Stage 0 into dk (and dw); keys of a
+    partial last block (R22) have no summary and get nothing here."""
+    nk = grads["dkbar"].shape[2] * prm.block
     if w is None:
-        grads["dk"][b, h] += np.repeat(grads["dkbar"][b, h], prm.block, axis=0) / prm.block
+        grads["dk"][b, h, :nk] += np.repeat(grads["dkbar"][b, h], prm.block, axis=0) / prm.block
         return
-    dk, dw = pool_attention_vjp(k[b, h], w[h], grads["dkbar"][b, h], prm.block)
-    grads["dk"][b, h] += dk
+    dk, dw = pool_attention_vjp(k[b, h, :nk], w[h], grads["dkbar"][b, h], prm.block)
+    grads["dk"][b, h, :nk] += dk
     grads["dw"][h] += dw
 
 
