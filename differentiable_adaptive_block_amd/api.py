@@ -77,7 +77,8 @@ class Selection:
 
 def alloc_selection(p: _lib.DashParams, device, want_mask: bool = True) -> Selection:
     n = _lib.sel_sizes(p)
-    B, H, T = p.B, p.H, p.T
+    B, H = p.B, p.H
+    T = -(-p.T // BLOCK) * BLOCK  # rows laid out as whole blocks
     nb = T // BLOCK
     nbw = (nb + 31) // 32
     ntile = n[4] // (B * H)
@@ -135,7 +136,7 @@ def forward(q, k, v, alpha=1.5, causal=True, fine_scale=None, coarse_scale=None,
     dev = q.device
     o = torch.empty_like(q)
     lse = torch.empty((p.B, p.H, p.T), dtype=torch.float32, device=dev)
-    kbar = torch.empty((p.B, Hkv, p.T // BLOCK, p.D), dtype=q.dtype, device=dev)
+    kbar = torch.empty((p.B, Hkv, -(-p.T // BLOCK), p.D), dtype=q.dtype, device=dev)
     sel = alloc_selection(p, dev, want_mask)
     wsb = _lib.fwd_workspace_bytes(p)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
@@ -160,7 +161,7 @@ def backward(q, k, v, o, lse, dout, kbar, sel: Selection, p: _lib.DashParams, su
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    dkbar = torch.empty((p.B, Hkv, p.T // BLOCK, p.D), dtype=torch.float32, device=dev)
+    dkbar = torch.empty((p.B, Hkv, -(-p.T // BLOCK), p.D), dtype=torch.float32, device=dev)
     if Hkv != p.H:
         wsb = _lib.bwd_gqa_workspace_bytes(p, Hkv)
         ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)

@@ -11,6 +11,7 @@
 #include "attn_bwd.h"
 #include "summariser.h"
 #include "decode.h"
+#include "ragged.h"
 
 namespace {
 
@@ -54,16 +55,36 @@ dash_status check_common(int D, int block, float alpha, float fs, float cs, int 
   return DASH_OK;
 }
 
-dash_status check_params(const dash_params* p, bool limit_T = true) {
+// ragged: a T that is not a multiple of 64 is accepted (causal only); the
+// entries that take it (dash_fwd, dash_bwd and their sizes) run on copies
+// padded to whole blocks.
+dash_status check_params(const dash_params* p, bool limit_T = true, bool ragged = false) {
   if (!p) return fail(DASH_EINVAL, "null params");
   if (p->B < 1 || p->H < 1) return fail(DASH_EINVAL, "B and H must be >= 1");
-  if (p->T < DASH_BLOCK || p->T % DASH_BLOCK) return fail(DASH_EINVAL, "T must be a positive multiple of 64 (got %d)", p->T);
+  if (p->T < 1) return fail(DASH_EINVAL, "T must be positive (got %d)", p->T);
+  if (p->T % DASH_BLOCK) {
+    if (!ragged)
+      return fail(DASH_EINVAL, "T must be a multiple of 64 here (got %d); dash_fwd and dash_bwd accept others", p->T);
+    if (p->causal != 1) return fail(DASH_EINVAL, "a partial last block (T = %d) needs causal attention", p->T);
+  }
   if (p->causal != 0 && p->causal != 1) return fail(DASH_EINVAL, "causal must be 0 or 1");
   dash_status s = check_common(p->D, p->block, p->alpha, p->fine_scale, p->coarse_scale, p->dtype);
   if (s != DASH_OK) return s;
-  if (limit_T && p->T / DASH_BLOCK > DASH_MAX_NB) return fail(DASH_EUNSUPPORTED, "T above %d is not built", DASH_MAX_NB * DASH_BLOCK);
+  if (limit_T && (p->T + DASH_BLOCK - 1) / DASH_BLOCK > DASH_MAX_NB)
+    return fail(DASH_EUNSUPPORTED, "T above %d is not built", DASH_MAX_NB * DASH_BLOCK);
   return DASH_OK;
 }
+
+bool is_ragged(const dash_params* p) { return p->T % DASH_BLOCK != 0; }
+
+// The same problem padded to whole blocks.
+dash_params padded(const dash_params* p) {
+  dash_params q = *p;
+  q.T = (p->T + DASH_BLOCK - 1) / DASH_BLOCK * DASH_BLOCK;
+  return q;
+}
+
+size_t elem_bytes(const dash_params* p) { return p->dtype == DASH_BF16 ? 2 : 4; }
 
 int ntile_of(int T) { return (T + DASH_QTILE - 1) / DASH_QTILE; }
 int nbw_of(int nb) { return (nb + 31) / 32; }
@@ -115,10 +136,11 @@ int32_t dash_query_tile(void) { return DASH_QTILE; }
 const char* dash_last_error(void) { return g_err.c_str(); }
 
 dash_status dash_sel_sizes(const dash_params* p, size_t out[7]) {
-  dash_status s = check_params(p);
+  dash_status s = check_params(p, true, true);
   if (s != DASH_OK) return s;
   if (!out) return fail(DASH_EINVAL, "null output array");
-  const size_t BH = (size_t)p->B * p->H, T = p->T, nb = T / DASH_BLOCK, nbw = nbw_of((int)nb), nt = ntile_of(p->T);
+  const dash_params pp = padded(p);  // a partial last block is laid out as a whole one
+  const size_t BH = (size_t)p->B * p->H, T = pp.T, nb = T / DASH_BLOCK, nbw = nbw_of((int)nb), nt = ntile_of(p->T);
   out[0] = BH * T;
   out[1] = BH * T;
   out[2] = BH * T;
@@ -129,14 +151,39 @@ dash_status dash_sel_sizes(const dash_params* p, size_t out[7]) {
   return DASH_OK;
 }
 
+// Padded copies for a ragged T: rows of Tp = whole blocks per head.
+// Forward: q, k, v, o (dtype) and lse.  Backward: q, k, v, o, dout, dq, dk,
+// dv and lse, after the whole-block backward's own workspace.
+size_t ragged_fwd_layout(const dash_params* p, size_t off[5]) {
+  const dash_params pp = padded(p);
+  const size_t BH = (size_t)p->B * p->H, rows = BH * pp.T, mat = rows * p->D * elem_bytes(p);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o += (bytes + 255) & ~size_t(255); return r; };
+  for (int i = 0; i < 4; ++i) off[i] = take(mat);
+  off[4] = take(rows * sizeof(float));
+  return o;
+}
+
+size_t ragged_bwd_layout(const dash_params* p, size_t off[14]) {
+  const dash_params pp = padded(p);
+  size_t o = bwd_ws_layout(&pp, off);  // off[0..3]
+  const size_t BH = (size_t)p->B * p->H, rows = BH * pp.T, mat = rows * p->D * elem_bytes(p);
+  auto take = [&](size_t bytes) { size_t r = o; o += (bytes + 255) & ~size_t(255); return r; };
+  for (int i = 4; i < 12; ++i) off[i] = take(mat);  // q k v o dout dq dk dv
+  off[12] = take(rows * sizeof(float));            // lse
+  return o;
+}
+
 size_t dash_fwd_workspace_bytes(const dash_params* p) {
-  (void)p;
-  return 0;
+  if (!p || check_params(p, true, true) != DASH_OK || !is_ragged(p)) return 0;
+  size_t off[5];
+  return ragged_fwd_layout(p, off);
 }
 
 size_t dash_bwd_workspace_bytes(const dash_params* p) {
-  if (check_params(p) != DASH_OK) return 0;
-  size_t off[4];
+  if (check_params(p, true, true) != DASH_OK) return 0;
+  size_t off[14];
+  if (is_ragged(p)) return ragged_bwd_layout(p, off);
   return bwd_ws_layout(p, off);
 }
 
@@ -290,15 +337,36 @@ dash_status dash_fwd_gqa(const dash_params* p, int32_t kv_heads, const void* q, 
 
 dash_status dash_fwd(const dash_params* p, const void* q, const void* k, const void* v, void* o, float* lse,
                      void* kbar, const dash_sel* sel, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
-  dash_status s = check_params(p);
+  dash_status s = check_params(p, true, true);
   if (s != DASH_OK) return s;
   if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(lse) || !ok_ptr(kbar))
     return fail(DASH_EINVAL, "q, k, v, o, lse and kbar must be non-null and 16-byte aligned");
   if ((s = check_sel(sel, true)) != DASH_OK) return s;
-  if ((s = dash_fwd_select(p, q, k, kbar, sel, stream)) != DASH_OK) return s;
-  return dash_fwd_attend(p, q, k, v, kbar, sel, o, lse, stream);
+  if (!is_ragged(p)) {
+    if ((s = dash_fwd_select(p, q, k, kbar, sel, stream)) != DASH_OK) return s;
+    return dash_fwd_attend(p, q, k, v, kbar, sel, o, lse, stream);
+  }
+  // a partial last block: the whole-block path on padded copies
+  size_t off[5];
+  const size_t need = ragged_fwd_layout(p, off);
+  if (workspace_bytes < need) return fail(DASH_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (!ok_ptr(workspace)) return fail(DASH_EINVAL, "workspace must be non-null and 16-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  const dash_params pp = padded(p);
+  const int BH = p->B * p->H, rb = p->D * (int)elem_bytes(p);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  const void* src[3] = {q, k, v};
+  for (int i = 0; i < 3; ++i)
+    if ((e = launch_pad_rows(src[i], ws + off[i], BH, p->T, pp.T, rb, st)) != hipSuccess) return hip_fail(e, "pad");
+  if ((s = dash_fwd_select(&pp, ws + off[0], ws + off[1], kbar, sel, stream)) != DASH_OK) return s;
+  if ((s = dash_fwd_attend(&pp, ws + off[0], ws + off[1], ws + off[2], kbar, sel, ws + off[3],
+                           reinterpret_cast<float*>(ws + off[4]), stream)) != DASH_OK)
+    return s;
+  if ((e = launch_unpad_rows(ws + off[3], o, BH, p->T, pp.T, rb, st)) != hipSuccess) return hip_fail(e, "unpad");
+  if ((e = launch_unpad_f32(reinterpret_cast<float*>(ws + off[4]), lse, BH, p->T, pp.T, st)) != hipSuccess)
+    return hip_fail(e, "unpad");
+  return DASH_OK;
 }
 
 static dash_status bwd_common(const dash_params* p, const void* q, const void* k, const void* v, const void* o,
@@ -426,8 +494,40 @@ dash_status dash_bwd_gqa(const dash_params* p, int32_t kv_heads, const void* q, 
 dash_status dash_bwd(const dash_params* p, const void* q, const void* k, const void* v, const void* o,
                      const float* lse, const void* dout, const void* kbar, const dash_sel* sel, void* dq, void* dk,
                      void* dv, float* dkbar, void* workspace, size_t workspace_bytes, void* stream) {
-  return bwd_common(p, q, k, v, o, lse, dout, kbar, sel, dq, dk, dv, dkbar, workspace, workspace_bytes, stream,
-                    1.f / DASH_BLOCK);
+  dash_status s = check_params(p, true, true);
+  if (s != DASH_OK) return s;
+  if (!is_ragged(p))
+    return bwd_common(p, q, k, v, o, lse, dout, kbar, sel, dq, dk, dv, dkbar, workspace, workspace_bytes, stream,
+                      1.f / DASH_BLOCK);
+  // a partial last block: the whole-block backward on padded copies; padded
+  // rows get dout = 0 and lse = +inf (weight 0), so they add nothing
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(lse) || !ok_ptr(dout) || !ok_ptr(kbar) ||
+      !ok_ptr(dq) || !ok_ptr(dk) || !ok_ptr(dv) || !ok_ptr(dkbar))
+    return fail(DASH_EINVAL, "tensor pointers must be non-null and 16-byte aligned");
+  if ((s = check_sel(sel, true)) != DASH_OK) return s;
+  size_t off[14];
+  const size_t need = ragged_bwd_layout(p, off);
+  if (workspace_bytes < need) return fail(DASH_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (!ok_ptr(workspace)) return fail(DASH_EINVAL, "workspace must be non-null and 16-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  const dash_params pp = padded(p);
+  const int BH = p->B * p->H, rb = p->D * (int)elem_bytes(p);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  const void* src[5] = {q, k, v, o, dout};
+  for (int i = 0; i < 5; ++i)
+    if ((e = launch_pad_rows(src[i], ws + off[4 + i], BH, p->T, pp.T, rb, st)) != hipSuccess) return hip_fail(e, "pad");
+  float* lsep = reinterpret_cast<float*>(ws + off[12]);
+  if ((e = launch_pad_f32(lse, lsep, BH, p->T, pp.T, INFINITY, st)) != hipSuccess) return hip_fail(e, "pad");
+  size_t boff[4];
+  const size_t bneed = bwd_ws_layout(&pp, boff);
+  if ((s = bwd_common(&pp, ws + off[4], ws + off[5], ws + off[6], ws + off[7], lsep, ws + off[8], kbar, sel,
+                      ws + off[9], ws + off[10], ws + off[11], dkbar, ws, bneed, stream, 1.f / DASH_BLOCK)) != DASH_OK)
+    return s;
+  void* dst[3] = {dq, dk, dv};
+  for (int i = 0; i < 3; ++i)
+    if ((e = launch_unpad_rows(ws + off[9 + i], dst[i], BH, p->T, pp.T, rb, st)) != hipSuccess) return hip_fail(e, "unpad");
+  return DASH_OK;
 }
 
 dash_status dash_bwd_no_pool(const dash_params* p, const void* q, const void* k, const void* v, const void* o,

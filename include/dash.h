@@ -61,7 +61,8 @@ typedef enum { DASH_F32 = 0, DASH_BF16 = 1 } dash_dtype;
 
 /* Prefill / training shapes and hyper-parameters. */
 typedef struct {
-  int32_t B, H, T, D;   /* batch, heads, sequence length (multiple of 64, <= 65536), head dim (64|128) */
+  int32_t B, H, T, D;   /* batch, heads, sequence length (<= 65536; a multiple of 64 except as
+                           below), head dim (64|128) */
   int32_t block;        /* keys per block; must be 64 */
   float alpha;          /* entmax alpha in [1, 2] */
   int32_t causal;       /* 0 or 1 */
@@ -73,7 +74,9 @@ typedef struct {
 /*
  * Stage-1 selection, written by dash_fwd and read by dash_bwd.  All buffers are
  * caller-owned device memory; sizes (in elements) come from dash_sel_sizes().
- * nb = T/64, nbw = ceil(nb/32), ntile = ceil(T/dash_query_tile()).
+ * nb = T/64, nbw = ceil(nb/32), ntile = ceil(T/dash_query_tile()).  With a
+ * partial last block (see dash_fwd) T here means 64 ceil(T/64): rows past
+ * the sequence are padding.
  *   tau      [B,H,T]        f32  entmax threshold (u-units for alpha>1, z-units
  *                                (log-sum-exp) for alpha=1; NaN when the row has
  *                                no candidate block)
@@ -102,7 +105,7 @@ int32_t dash_query_tile(void);
 /* Element counts of the seven dash_sel buffers, in struct order. */
 dash_status dash_sel_sizes(const dash_params* p, size_t out_elems[7]);
 
-/* Bytes of device workspace dash_fwd / dash_bwd need (may be 0). */
+/* Bytes of device workspace dash_fwd / dash_bwd need (dash_fwd: 0 unless T is not a multiple of 64). */
 size_t dash_fwd_workspace_bytes(const dash_params* p);
 size_t dash_bwd_workspace_bytes(const dash_params* p);
 
@@ -118,6 +121,15 @@ dash_status dash_pool(const dash_params* p, const void* k, void* kbar, void* str
  * Forward (Stages 0, 1, 2).  Inputs q, k, v.  Outputs: o [B,H,T,D] (dtype),
  * lse [B,H,T] (f32, log-sum-exp of the Stage-2 logits, for the backward),
  * kbar [B,H,T/64,D] (dtype) and the selection `sel`.
+ *
+ * dash_fwd and dash_bwd also take a causal T that is not a multiple of 64
+ * (the other prefill entry points do not): the last block is partial; it is
+ * the own block of its queries and no query's candidate, so only the
+ * complete blocks have summaries (kbar and dkbar have ceil(T/64) rows; the
+ * last one is not a summary, and dkbar's is 0).  The library then runs the
+ * whole-block kernels on copies padded with zeros in the workspace
+ * (dash_fwd_workspace_bytes) and copies the T rows back; the results are
+ * those of the unpadded problem.  Non-causal attention needs whole blocks.
  */
 dash_status dash_fwd(const dash_params* p, const void* q, const void* k, const void* v,
                      void* o, float* lse, void* kbar, const dash_sel* sel,

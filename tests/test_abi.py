@@ -68,7 +68,6 @@ def _fwd(L, p, **ptrs):
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("T", 100, _lib.DASH_EINVAL),            # not a multiple of 64
     ("T", 0, _lib.DASH_EINVAL),
     ("B", 0, _lib.DASH_EINVAL),
     ("alpha", 2.5, _lib.DASH_EINVAL),
@@ -224,3 +223,21 @@ def test_gqa_entry_validation(L):
     bargs = [FAKE] * 7 + [ctypes.byref(_sel())] + [FAKE] * 5
     assert L.dash_bwd_gqa(ctypes.byref(p), 2, *bargs, need - 1, None) == _lib.DASH_EWORKSPACE
     assert L.dash_bwd_gqa(ctypes.byref(p), 3, *bargs, need, None) == _lib.DASH_EINVAL
+
+
+def test_partial_last_block_validation(L):
+    # a T that is not a multiple of 64: causal only, through dash_fwd / dash_bwd with a workspace
+    assert _fwd(L, _params(T=100, causal=0)) == _lib.DASH_EINVAL
+    assert "causal" in L.dash_last_error().decode()
+    p = _params(T=100)
+    need = L.dash_fwd_workspace_bytes(ctypes.byref(p))
+    assert need > 0 and L.dash_fwd_workspace_bytes(ctypes.byref(_params())) == 0
+    assert _fwd(L, p) == _lib.DASH_EWORKSPACE
+    assert L.dash_bwd_workspace_bytes(ctypes.byref(p)) > L.dash_bwd_workspace_bytes(ctypes.byref(_params(T=128)))
+    sizes = (ctypes.c_size_t * 7)()
+    assert L.dash_sel_sizes(ctypes.byref(p), sizes) == _lib.DASH_OK
+    assert sizes[0] == 1 * 2 * 128  # rows laid out as whole blocks
+    # the stage entry points keep whole blocks
+    assert L.dash_fwd_select(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(_sel()), None) == _lib.DASH_EINVAL
+    assert L.dash_pool(ctypes.byref(p), FAKE, FAKE, None) == _lib.DASH_EINVAL
+    assert L.dash_fwd_gqa(ctypes.byref(p), 2, *([FAKE] * 6), ctypes.byref(_sel()), None) == _lib.DASH_EINVAL
