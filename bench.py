@@ -400,6 +400,52 @@ def bench_gqa(steps, warmup, device, kv_heads=8):
     return res
 
 
+def bench_ragged(steps, warmup, device, cut=37):
+    """The 16K causal prefill shape cut to T = 16384 - cut tokens (a partial last
+    block): dash_fwd on zero-padded workspace copies, whole forward timed."""
+    from differentiable_adaptive_block_amd import _lib, api, inputs
+
+    wl = inputs.CONFIGS["c2"]
+    sh = wl.shape
+    B, H, D = sh["B"], sh["H"], sh["D"]
+    T = sh["T"] - cut
+    w = inputs.make_prefill(B, H, sh["T"], D, wl.dtype, True, wl.planted, wl.seed, device=device, with_dout=False)
+    q, k, v = (w[x][:, :, :T].contiguous() for x in ("q", "k", "v"))
+    del w
+    r = api.forward(q, k, v, alpha=1.5, causal=True, coarse_scale=wl.coarse_scale, want_mask=False)
+    torch.cuda.synchronize()
+    p = r["params"]
+    sel = r["sel"]
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=device)
+    kbar = torch.empty_like(r["kbar"])
+    wsb = _lib.fwd_workspace_bytes(p)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=device)
+    st = torch.cuda.current_stream().cuda_stream
+
+    def fwd():
+        _lib.fwd(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), kbar.data_ptr(),
+                 sel.as_c(), ws.data_ptr(), wsb, st)
+
+    for _ in range(warmup):
+        fwd()
+    torch.cuda.synchronize()
+    t0, t1 = _events(2)
+    t0.record()
+    for _ in range(steps):
+        fwd()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    assert torch.equal(o, r["o"]), "timed forward differs from the validated forward"
+    res = dict(B=B, H=H, T=T, D=D, ms_per_step=ms, tokens_per_s=B * T / (ms / 1e3), workspace_bytes=wsb,
+               work="dash_fwd with a partial last block: pad q, k, v to whole blocks, the whole-block forward, "
+                    "copy o and lse back")
+    del q, k, v, r, o, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_decode(name, steps, warmup, device):
     """Time dash_decode (select + split-KV attend + combine) on a named decode workload."""
     from differentiable_adaptive_block_amd import _lib, api, inputs
@@ -588,6 +634,9 @@ def main():
         log(f"c3cal: {r3c}")
         extra["prefill_64k_calibrated"] = r3c
 
+    rg = bench_ragged(max(3, args.steps // 2), 1, dev)
+    log(f"ragged 16K: {rg}")
+    extra["prefill_16k_ragged"] = rg
     gq = bench_gqa(max(3, args.steps // 2), 1, dev)
     log(f"gqa 16K: {gq}")
     extra["prefill_16k_gqa"] = gq

@@ -413,12 +413,13 @@ static dash_status bwd_common(const dash_params* p, const void* q, const void* k
   ba.pool_scale = pool_scale;
   ba.grp = 1;
   ba.gsum = nullptr;
+  ba.phbuf = nullptr;
   ba.ca = make_ca(p->alpha, p->coarse_scale);
   hipError_t e = launch_bwd(ba, p->dtype, (hipStream_t)stream);
   return e == hipSuccess ? DASH_OK : hip_fail(e, "backward");
 }
 
-static size_t bwd_gqa_ws_layout(const dash_params* p, int32_t kv_heads, size_t off[8]) {
+static size_t bwd_gqa_ws_layout(const dash_params* p, int32_t kv_heads, size_t off[9]) {
   size_t base = bwd_ws_layout(p, off);
   const size_t BH = (size_t)p->B * p->H, T = p->T, D = p->D, nb = T / DASH_BLOCK, nt = ntile_of(p->T);
   const size_t grp = (size_t)p->H / kv_heads;
@@ -428,12 +429,13 @@ static size_t bwd_gqa_ws_layout(const dash_params* p, int32_t kv_heads, size_t o
   off[5] = take(BH * T * D * 2);                                   // dK per query head
   off[6] = take(BH * T * D * 2);                                   // dV per query head
   off[7] = take(BH * nb * D * sizeof(float));                      // dkbar per query head
+  off[8] = take(BH * nt * nb * DASH_QTILE * sizeof(float));         // each row's own log2 p
   return o;
 }
 
 size_t dash_bwd_gqa_workspace_bytes(const dash_params* p, int32_t kv_heads) {
   if (check_params(p) != DASH_OK || kv_heads < 1 || p->H % kv_heads) return 0;
-  size_t off[8];
+  size_t off[9];
   if (kv_heads == p->H) return bwd_ws_layout(p, off);
   return bwd_gqa_ws_layout(p, kv_heads, off);
 }
@@ -452,7 +454,7 @@ dash_status dash_bwd_gqa(const dash_params* p, int32_t kv_heads, const void* q, 
       !ok_ptr(dq) || !ok_ptr(dk) || !ok_ptr(dv) || !ok_ptr(dkbar))
     return fail(DASH_EINVAL, "tensor pointers must be non-null and 16-byte aligned");
   if ((s = check_sel(sel, true)) != DASH_OK) return s;
-  size_t off[8];
+  size_t off[9];
   const size_t need = bwd_gqa_ws_layout(p, kv_heads, off);
   if (workspace_bytes < need) return fail(DASH_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if (!ok_ptr(workspace)) return fail(DASH_EINVAL, "workspace must be non-null and 16-byte aligned");
@@ -479,6 +481,7 @@ dash_status dash_bwd_gqa(const dash_params* p, int32_t kv_heads, const void* q, 
   ba.gbuf = reinterpret_cast<float*>(ws + off[2]);
   ba.pbuf = reinterpret_cast<float*>(ws + off[3]);
   ba.gsum = reinterpret_cast<float*>(ws + off[4]);
+  ba.phbuf = reinterpret_cast<float*>(ws + off[8]);
   ba.BH = p->B * p->H;
   ba.T = p->T;
   ba.D = p->D;

@@ -26,6 +26,7 @@ struct BwdArgs {
   float* gbuf;     // [BH, ntile, nb, QTILE]  G_ib for listed blocks
   float* pbuf;     // [BH, ntile, nb, QTILE]  log2 prior used for (row, listed block)
   float* gsum;     // [BH / grp, ntile, nb, QTILE]  G summed over a group's heads (grp > 1)
+  float* phbuf;    // [BH, ntile, nb, QTILE]  the row's own log2 p (grp > 1)
   int BH, T, D, causal;
   int grp;  // query heads per key/value head: k, v, kbar are indexed by bh / grp
   float fine_scale;

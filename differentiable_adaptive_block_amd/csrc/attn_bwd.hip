@@ -133,6 +133,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     if constexpr (GQA) {
       const size_t bh0 = bkv * a.grp;  // the group's first query head
       if (active) {
+        {
+          // the row's own log2 p (its own entmax, whose Jacobian the coarse
+          // kernel applies), from the same score MFMAs as the forward's
+          const f32x16 own = prior_chunk32<D>(KB, list, cnt, e0, qb, ca, tau_i, ln_i, a.causal, wblk);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int en = e0 + acc_row32(r, l);
+            if (en < cnt) a.phbuf[gidx(bh, ntile, tile, nb, en, w * 32 + j)] = own[r];
+          }
+        }
         pacc = prior_chunk32_group<D>(KB, list, cnt, e0, reinterpret_cast<const bf16_t*>(a.q) + (bh0 * a.T + i) * D,
                                       (size_t)a.T * D, a.tau + bh0 * a.T + i, a.lognorm + bh0 * a.T + i, a.T,
                                       a.grp, ca, a.causal, wblk);
@@ -627,12 +637,10 @@ __device__ __forceinline__ float sum8(float v) {
 // grid (ntile * 4, BH), 256 threads = 32 rows x 8 threads: thread c of a
 // row takes list slots e = c (mod 8) in the first two passes and columns
 // c G .. c G + G - 1 in the last.
-// Grouped-query heads (GQA): the prior in pbuf is the group's log2 pbar and
-// gsum holds G summed over the group; the row's own p (whose Jacobian
-// applies) comes from its own scores, recomputed here by the 8 threads of the
-// row (one partial dot each, summed across them), with g_b = Gsum_b /
-// (grp pbar_b):  s_b g_b = p_b^(2-alpha) Gsum_b pbar_b^-1 / grp.  Pass 1
-// keeps log2 p in the row's own G slots, pass 2 overwrites them with dz.
+// Grouped-query heads (GQA): the prior in pbuf is the group's log2 pbar,
+// gsum holds G summed over the group and phbuf the row's own log2 p (whose
+// Jacobian applies), written by the dQ kernel; with g_b = Gsum_b /
+// (grp pbar_b):  s_b g_b = p_b^(2-alpha) Gsum_b pbar_b^-1 / grp.
 template <int D, bool GQA>
 __global__ __launch_bounds__(256) void bwd_coarse_kernel(BwdArgs a) {
   constexpr int G = D / 8;
@@ -652,33 +660,18 @@ __global__ __launch_bounds__(256) void bwd_coarse_kernel(BwdArgs a) {
   const size_t bkv = GQA ? bh / a.grp : bh;
   float ss = 0.f, ssg = 0.f;
   if constexpr (GQA) {
-    // the row's query features cg G .. cg G + G - 1, as float
-    float qf[G];
-    {
-      const bf16_t* qr = reinterpret_cast<const bf16_t*>(a.q) + (bh * a.T + (valid ? i : 0)) * D + cg * G;
-#pragma unroll
-      for (int x = 0; x < G; ++x) qf[x] = valid ? bf2f(qr[x]) : 0.f;
-    }
-    const float tau_i = valid ? a.tau[bh * a.T + i] : 0.f, ln_i = valid ? a.lognorm[bh * a.T + i] : 0.f;
     const float inv_grp = 1.f / (float)a.grp;
-    const bf16_t* KBc = reinterpret_cast<const bf16_t*>(a.kbar) + bkv * nb * D + cg * G;
-    for (int e = 0; e < cnt; ++e) {  // every thread of the row takes every entry (the dot is shared)
-      const int b = list[e];
-      const bf16_t* kr = KBc + (size_t)b * D;
-      float part = 0.f;
-#pragma unroll
-      for (int x = 0; x < G; ++x) part = fmaf(qf[x], bf2f(kr[x]), part);
-      const float zacc = sum8(part);
-      if ((e & 7) != cg || !valid || (a.causal && b >= own)) continue;
-      const size_t gi = gidx(bh, ntile, tile, nb, e, rt);
-      const float lpb2 = a.pbuf[gi];
-      if (lpb2 == -INFINITY) continue;
-      const float lp2 = a.ca.logp(a.ca.u_of(zacc), tau_i, ln_i) * LOG2E_F;
-      a.gbuf[gi] = lp2;
-      if (lp2 == -INFINITY) continue;
-      const float sv = __builtin_amdgcn_exp2f(am2 * lp2);
-      ss += sv;
-      ssg += sv * a.gsum[gidx(bkv, ntile, tile, nb, e, rt)] * __builtin_amdgcn_exp2f(-lpb2) * inv_grp;
+    if (valid) {
+      for (int e = cg; e < cnt; e += 8) {
+        if (a.causal && list[e] >= own) continue;
+        const size_t gi = gidx(bh, ntile, tile, nb, e, rt);
+        const float lpb2 = a.pbuf[gi];
+        const float lp2 = a.phbuf[gi];
+        if (lpb2 == -INFINITY || lp2 == -INFINITY) continue;
+        const float sv = __builtin_amdgcn_exp2f(am2 * lp2);
+        ss += sv;
+        ssg += sv * a.gsum[gidx(bkv, ntile, tile, nb, e, rt)] * __builtin_amdgcn_exp2f(-lpb2) * inv_grp;
+      }
     }
     ss = sum8(ss);
     ssg = sum8(ssg);
@@ -689,13 +682,11 @@ __global__ __launch_bounds__(256) void bwd_coarse_kernel(BwdArgs a) {
         float dz = 0.f;
         if (!(a.causal && list[e] >= own)) {
           const float lpb2 = a.pbuf[gi];
-          if (lpb2 != -INFINITY) {
-            const float lp2 = a.gbuf[gi];
-            if (lp2 != -INFINITY) {
-              const float sv = __builtin_amdgcn_exp2f(am2 * lp2);
-              const float gv = a.gsum[gidx(bkv, ntile, tile, nb, e, rt)] * __builtin_amdgcn_exp2f(-lpb2) * inv_grp;
-              dz = sv * gv - sv * ratio;
-            }
+          const float lp2 = a.phbuf[gi];
+          if (lpb2 != -INFINITY && lp2 != -INFINITY) {
+            const float sv = __builtin_amdgcn_exp2f(am2 * lp2);
+            const float gv = a.gsum[gidx(bkv, ntile, tile, nb, e, rt)] * __builtin_amdgcn_exp2f(-lpb2) * inv_grp;
+            dz = sv * gv - sv * ratio;
           }
         }
         a.gbuf[gi] = dz;
