@@ -42,6 +42,8 @@ CASES = [
     ("h4-kv2-causal-ragged", 1, 4, 2, 1088, 128, True, 1.5, 4.0, (1, 4)),
     ("h4-kv1-noncausal-d64", 1, 4, 1, 576, 64, False, 1.25, 4.0, (1, 3)),
     ("b2-h8-kv2-causal", 2, 8, 2, 512, 128, True, 1.5, 6.0, (1, 3)),
+    ("h2-kv1-causal-a1", 1, 2, 1, 640, 128, True, 1.0, 2.0, (1, 3)),
+    ("h4-kv2-causal-a2", 1, 4, 2, 576, 128, True, 2.0, 6.0, (1, 3)),
 ]
 
 

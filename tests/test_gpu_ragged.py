@@ -47,6 +47,7 @@ def _gpu(r, T):
 
 CASES = [
     # name, B, H, T, D, dtype, alpha, coarse multiple, planted
+    ("bf16-T10", 1, 2, 10, 128, "bf16", 1.5, 4.0, (1, 3)),
     ("bf16-T65", 1, 2, 65, 128, "bf16", 1.5, 4.0, (1, 3)),
     ("bf16-T100-d64", 1, 2, 100, 64, "bf16", 1.25, 4.0, (1, 3)),
     ("bf16-T1000", 1, 2, 1000, 128, "bf16", 1.5, 4.0, (1, 4)),
