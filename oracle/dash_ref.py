@@ -19,7 +19,7 @@ Method, as the pages state it:
 * Gradients flow from Stage 2 through log p into the entmax and on to the
   summaries (same sections; "What alpha-entmax changes").
 
-Readings taken where the pages are silent (each is restated in the design doc):
+Readings taken where the pages are silent:
 
 * R1 entmax parameterisation u = (alpha-1) z, p = [u - tau]_+^(1/(alpha-1)).
 * R2 one joint softmax over all attended tokens with log p added to the logits.
