@@ -30,7 +30,7 @@ absolute values).
 """
 
 from .entmax import entmax, entmax_threshold, entmax_jvp  # noqa: F401
-from .gqa import select_row_group, forward_rows_gqa, forward_gqa, backward_gqa  # noqa: F401
+from .gqa import select_row_group, forward_rows_gqa, forward_gqa, backward_gqa, decode_gqa  # noqa: F401
 from .dash_ref import (  # noqa: F401
     Params,
     round_bf16,

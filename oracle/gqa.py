@@ -158,3 +158,44 @@ def backward_gqa(q, k, v, dout, prm: Params):
                     dkbar[b, kv, cand] += sc * np.outer(dz, qg[g])
             dk[b, kv] += np.repeat(dkbar[b, kv], blk, axis=0) / blk
     return dict(dq=dq, dk=dk, dv=dv, dkbar=dkbar)
+
+
+def decode_gqa(q, kc, vc, lens, prm: Params):
+    """Decode for grouped-query heads (R21 applied to the decode row, R19 lengths).
+
+    ``q``: [S, H, D]; ``kc, vc``: [S, Hkv, C, D] holding ``lens[s]`` tokens of
+    sequence s (the new one last; lens None: all C).  Each query head attends
+    its KV head's cache with the group's aggregated selection: row lens[s]-1
+    of a grouped-query causal prefill over the first lens[s] tokens.
+    Returns dict(o [S,H,D], lse [S,H], nsel [S,H] (each head's own support),
+    union [S,H,C/block] (the group's), tau [S,H]).
+    """
+    q = _as64(q)
+    S, H, D = q.shape
+    Hkv, C = kc.shape[1], kc.shape[2]
+    G = _group(H, Hkv)
+    blk = prm.block
+    lens = np.full(S, C) if lens is None else np.asarray(lens, dtype=np.int64)
+    if np.any(lens < 1) or np.any(lens > C):
+        raise ValueError("every length must lie in [1, capacity]")
+    o = np.zeros((S, H, D))
+    lse = np.zeros((S, H))
+    nsel = np.zeros((S, H), dtype=np.int64)
+    union = np.zeros((S, H, C // blk), dtype=bool)
+    tau = np.zeros((S, H))
+    for s in range(S):
+        n = int(lens[s])
+        i = n - 1
+        for kv in range(Hkv):
+            kh = _as64(kc[s, kv, :n])
+            vh = _as64(vc[s, kv, :n])
+            kb = pool_blocks(kh[: (i // blk) * blk], blk, prm.storage)
+            grp = select_row_group(q[s, kv * G:(kv + 1) * G], kb, i, prm, D)
+            for g in range(G):
+                h = kv * G + g
+                o[s, h], lse[s, h], _ = attend_row(q[s, h], kh, vh, i, grp, prm, D)
+                own = grp["heads"][g]
+                nsel[s, h] = int(own["support"].sum())
+                tau[s, h] = own["tau"]
+                union[s, h, grp["cand"][grp["support"]]] = True
+    return dict(o=o, lse=lse, nsel=nsel, union=union, tau=tau)

@@ -147,3 +147,37 @@ def test_heads_must_divide():
     k = np.zeros((1, 2, 64, 8))
     with pytest.raises(ValueError):
         oracle.forward_rows_gqa(q, k, k, prm, [(0, 0, 0)])
+
+
+def test_gqa_decode_is_the_last_prefill_row():
+    rng = np.random.default_rng(92)
+    S, H, Hkv, C, D = 3, 4, 2, 256, 16
+    prm = Params(causal=True, alpha=1.5, storage="bf16", coarse_scale=8.0 / math.sqrt(D))
+    lens = np.array([64, 150, 256])
+    kc = rng.normal(size=(S, Hkv, C, D))
+    vc = rng.normal(size=(S, Hkv, C, D))
+    q = rng.normal(size=(S, H, D))
+    for s in range(S):
+        for h in range(H):
+            kb = kc[s, h // 2, :64].mean(axis=0)
+            q[s, h] += 1.5 * kb / np.linalg.norm(kb)
+    dec = oracle.decode_gqa(q, kc, vc, lens, prm)
+    for s, n in enumerate(lens):
+        Tp = 64 * ((n + 63) // 64)
+        qq = np.zeros((1, H, Tp, D))
+        qq[0, :, n - 1] = q[s]
+        kk = np.zeros((1, Hkv, Tp, D))
+        vv = np.zeros((1, Hkv, Tp, D))
+        kk[0, :, :n], vv[0, :, :n] = kc[s, :, :n], vc[s, :, :n]
+        rows = oracle.forward_rows_gqa(qq, kk, vv, prm, [(0, h, n - 1) for h in range(H)])
+        for h, r in enumerate(rows):
+            np.testing.assert_array_equal(dec["o"][s, h], r["o"])
+            assert dec["lse"][s, h] == r["lse"]
+            np.testing.assert_array_equal(dec["union"][s, h, : (n - 1) // 64], r["union"][: (n - 1) // 64])
+    # one KV head per query head: the per-head decode
+    kc1 = np.repeat(kc, 2, axis=1)
+    vc1 = np.repeat(vc, 2, axis=1)
+    a = oracle.decode_gqa(q, kc1, vc1, lens, prm)
+    b = oracle.decode_varlen(q, kc1, vc1, lens, prm)
+    np.testing.assert_array_equal(a["o"], b["o"])
+    np.testing.assert_array_equal(a["nsel"], b["nsel"])
