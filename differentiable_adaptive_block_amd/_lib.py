@@ -40,6 +40,7 @@ EXPORTS = [
     "dash_cache_append",
     "dash_decode_varlen",
     "dash_decode_step",
+    "dash_decode_gqa",
     "dash_last_error",
 ]
 
@@ -137,6 +138,9 @@ def load() -> ctypes.CDLL:
     L.dash_decode_step.restype = ctypes.c_int
     L.dash_decode_step.argtypes = [P(DashDecodeParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                    ctypes.c_size_t, vp]
+    L.dash_decode_gqa.restype = ctypes.c_int
+    L.dash_decode_gqa.argtypes = [P(DashDecodeParams), ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                  ctypes.c_size_t, vp]
     L.dash_last_error.restype = ctypes.c_char_p
     L.dash_last_error.argtypes = []
     _lib = L
@@ -244,3 +248,9 @@ def decode_step(p: DashDecodeParams, q, k_new, v_new, lens, kc, vc, kbar, o, lse
                 stream) -> None:
     check(load().dash_decode_step(ctypes.byref(p), q, k_new, v_new, lens, kc, vc, kbar, o, lse, nsel, tau, ws,
                                   ws_bytes, stream))
+
+
+def decode_gqa(p: DashDecodeParams, kv_heads: int, q, kc, vc, kbar, lens, o, lse, nsel, tau, ws, ws_bytes,
+               stream) -> None:
+    check(load().dash_decode_gqa(ctypes.byref(p), kv_heads, q, kc, vc, kbar, lens, o, lse, nsel, tau, ws, ws_bytes,
+                                 stream))

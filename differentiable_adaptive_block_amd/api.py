@@ -275,6 +275,27 @@ def decode_step(q, k_new, v_new, kc, vc, kbar, lens, alpha=1.5, fine_scale=None,
     return dict(o=bufs.o, lse=bufs.lse, nsel=bufs.nsel, tau=bufs.tau)
 
 
+def decode_gqa(q, kc, vc, kbar, lens=None, alpha=1.5, fine_scale=None, coarse_scale=None,
+               bufs: DecodeBuffers | None = None):
+    """Decode for grouped-query heads: q [S,H,D] over caches kc, vc [S,Hkv,C,D] (Hkv divides H);
+    lens: None (full caches) or int32 [S] device lengths."""
+    S, Hkv, C, D = kc.shape
+    H = q.shape[1]
+    _require(q, "q", (S, H, D), kc.dtype)
+    _require(vc, "vc", kc.shape, kc.dtype)
+    _require(kbar, "kbar", (S, Hkv, C // BLOCK, D), kc.dtype)
+    if lens is not None:
+        _require_lens(lens, S, q.device)
+    p = make_decode_params(q, kc, alpha, fine_scale, coarse_scale)
+    p.H = H
+    if bufs is None:
+        bufs = DecodeBuffers(p, q.dtype, q.device)
+    _lib.decode_gqa(p, Hkv, _ptr(q), _ptr(kc), _ptr(vc), _ptr(kbar), None if lens is None else _ptr(lens),
+                    _ptr(bufs.o), _ptr(bufs.lse), _ptr(bufs.nsel), _ptr(bufs.tau), _ptr(bufs.ws), bufs.ws_bytes,
+                    _stream(q.device))
+    return dict(o=bufs.o, lse=bufs.lse, nsel=bufs.nsel, tau=bufs.tau)
+
+
 class DashAttentionFn(torch.autograd.Function):
     """DashAttention as an autograd function (forward: Stages 0-2; backward through all of them)."""
 

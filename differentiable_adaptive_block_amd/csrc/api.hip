@@ -555,7 +555,7 @@ static dash_status check_decode_params(const dash_decode_params* p) {
 static dash_status decode_common(const dash_decode_params* p, const void* q, const void* kc, const void* vc,
                                  const void* kbar, const int32_t* len, int len_add, void* o, float* lse,
                                  int32_t* nsel, float* tau, void* workspace, size_t workspace_bytes,
-                                 void* stream) {
+                                 void* stream, int grp = 1) {
   if (!ok_ptr(q) || !ok_ptr(kc) || !ok_ptr(vc) || !ok_ptr(kbar) || !ok_ptr(o))
     return fail(DASH_EINVAL, "q, kc, vc, kbar and o must be non-null and 16-byte aligned");
   if (!ok_opt(lse) || !ok_opt(nsel) || !ok_opt(tau)) return fail(DASH_EINVAL, "lse/nsel/tau must be 16-byte aligned");
@@ -582,6 +582,7 @@ static dash_status decode_common(const dash_decode_params* p, const void* q, con
   da.part = reinterpret_cast<float*>(ws + off[5]);
   da.len = len;
   da.len_add = len_add;
+  da.grp = grp;
   da.SH = p->S * p->H;
   da.H = p->H;
   da.N = p->N;
@@ -620,6 +621,18 @@ dash_status dash_decode(const dash_decode_params* p, const void* q, const void* 
   dash_status s = check_decode_params(p);
   if (s != DASH_OK) return s;
   return decode_common(p, q, kc, vc, kbar, nullptr, 0, o, lse, nsel, tau, workspace, workspace_bytes, stream);
+}
+
+dash_status dash_decode_gqa(const dash_decode_params* p, int32_t kv_heads, const void* q, const void* kc,
+                            const void* vc, const void* kbar, const int32_t* len, void* o, float* lse,
+                            int32_t* nsel, float* tau, void* workspace, size_t workspace_bytes, void* stream) {
+  dash_status s = check_decode_params(p);
+  if (s != DASH_OK) return s;
+  if (kv_heads < 1 || p->H % kv_heads) return fail(DASH_EINVAL, "kv_heads (%d) must divide H (%d)", kv_heads, p->H);
+  const int grp = p->H / kv_heads;
+  if (grp > 8) return fail(DASH_EUNSUPPORTED, "more than 8 query heads per KV head is not built (got %d)", grp);
+  if (len && reinterpret_cast<uintptr_t>(len) % 4) return fail(DASH_EINVAL, "len must be 4-byte aligned");
+  return decode_common(p, q, kc, vc, kbar, len, 0, o, lse, nsel, tau, workspace, workspace_bytes, stream, grp);
 }
 
 dash_status dash_cache_append(const dash_decode_params* p, const void* k_new, const void* v_new,

@@ -21,6 +21,7 @@ struct DecodeArgs {
   float* part;       // [SH, nsplit, D + 2] partial (m, l, o)
   const int* len;    // [SH / H] tokens per sequence (+ len_add), or null: every row holds N
   int SH, H, N, D, nsplit, chunk, len_add;  // N: cache capacity (row stride in tokens)
+  int grp;           // query heads per key/value head (1: one each); kc, vc, kbar rows are row / grp
   float fine_scale;
   CoarseArith ca;
 };

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(512) void decode_select_kernel(DecodeArgs a) {
   const int own = (n - 1) / DASH_BLOCK;  // the query's block
   const int nc = own;                    // the complete blocks before it are the candidates
   const bf16_t* q = reinterpret_cast<const bf16_t*>(a.q) + (size_t)row * D;
-  const bf16_t* kb = reinterpret_cast<const bf16_t*>(a.kbar) + (size_t)row * nbc * D;
+  const bf16_t* kb = reinterpret_cast<const bf16_t*>(a.kbar) + (size_t)(row / a.grp) * nbc * D;
   const CoarseArith ca = a.ca;
   float qf[8];
   unpack8(*reinterpret_cast<const uint4*>(q + (l & 15) * 8), qf);
@@ -116,6 +116,22 @@ __global__ __launch_bounds__(512) void decode_select_kernel(DecodeArgs a) {
   EntmaxOut e;
   if (nc > 0) e = entmax_solve<NPL, 64>(u, nc, ca);
   else { e.tau = __uint_as_float(0x7fc00000u); e.lognorm = 0.f; e.nsel = 0; }
+  if (a.grp > 1) {
+    // grouped heads: this head's p over the candidates, for the group's merge
+    float* pr = a.zrow + (size_t)row * nbc;
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) {
+      const int idx = l + 64 * k;
+      if (idx < nc) pr[idx] = ca.selected(u[k], e.tau) ? __expf(ca.logp(u[k], e.tau, e.lognorm)) : 0.f;
+    }
+    if (l == 0) {
+      a.rowstat[2 * row] = e.tau;
+      a.rowstat[2 * row + 1] = e.lognorm;
+      if (a.nsel) a.nsel[row] = e.nsel;
+      if (a.tau_out) a.tau_out[row] = e.tau;
+    }
+    return;
+  }
   int* list = a.sel_blk + (size_t)row * nbc;
   float* lp = a.sel_lp + (size_t)row * nbc;
   int base = 0;
@@ -294,6 +310,154 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   if (l == 0 && a.lse) a.lse[row] = (M + __log2f(L)) * LN2_F;
 }
 
+// ---------------------------------------------------------------------------- grouped heads
+
+// Grouped-query heads (entmax head aggregation): the grp heads of a group
+// share one list, the blocks where pbar = (1/grp) sum_h p_h > 0, with log2
+// pbar as prior, then the own block (prior 0).  One wave per group; the
+// list sits in the group's first row.  A length out of range gives every
+// row of the group an empty list.
+__global__ __launch_bounds__(64) void decode_group_merge_kernel(DecodeArgs a) {
+  const int l = threadIdx.x;
+  const int row0 = blockIdx.x * a.grp;
+  const int nbc = a.N / DASH_BLOCK;
+  const int n = decode_row_len(a, row0);
+  if (n < 1 || n > a.N) {
+    if (l < a.grp) a.sel_cnt[row0 + l] = 0;
+    return;
+  }
+  const int own = (n - 1) / DASH_BLOCK;
+  int* list = a.sel_blk + (size_t)row0 * nbc;
+  float* lp = a.sel_lp + (size_t)row0 * nbc;
+  const float inv = 1.f / (float)a.grp;
+  int base = 0;
+  for (int c0 = 0; c0 < own; c0 += 64) {
+    const int idx = c0 + l;
+    float ps = 0.f;
+    if (idx < own)
+      for (int g = 0; g < a.grp; ++g) ps += a.zrow[(size_t)(row0 + g) * nbc + idx];
+    const bool s = ps > 0.f;
+    const unsigned long long bal = __ballot(s);
+    if (s) {
+      const int pos = base + __popcll(bal & ((1ull << l) - 1ull));
+      list[pos] = idx;
+      lp[pos] = __log2f(ps * inv);
+    }
+    base += __popcll(bal);
+  }
+  if (l == 0) {
+    list[base] = own;
+    lp[base] = 0.f;
+  }
+  if (l < a.grp) a.sel_cnt[row0 + l] = base + 1;
+}
+
+// Split-KV attention for a group: workgroup (split, group), wave w = the
+// group's head w; every wave walks the same list entries (split, split +
+// nsplit, ...), so each block is read from HBM once for the group and its
+// other reads hit the cache.  Each wave writes its row's partial.
+__global__ __launch_bounds__(512) void decode_attend_group_kernel(DecodeArgs a) {
+  constexpr int D = 128;
+  const int split = blockIdx.x, grp_id = blockIdx.y;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int row = grp_id * a.grp + w;
+  const int row0 = grp_id * a.grp;
+  const int nbc = a.N / DASH_BLOCK;
+  const int n = decode_row_len(a, row0);
+  const int g = l >> 4, c = l & 15;
+  const int cnt = a.sel_cnt[row0];
+  const int* list = a.sel_blk + (size_t)row0 * nbc;
+  const float* lpl = a.sel_lp + (size_t)row0 * nbc;
+  const bf16_t* K = reinterpret_cast<const bf16_t*>(a.kc) + (size_t)grp_id * a.N * D;
+  const bf16_t* V = reinterpret_cast<const bf16_t*>(a.vc) + (size_t)grp_id * a.N * D;
+  const float sl2 = a.fine_scale * LOG2E_F;
+  float qf[8];
+  unpack8(*reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.q) + (size_t)row * D + c * 8), qf);
+  float m = -INFINITY, lsum = 0.f;
+  float o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
+  const int stride = a.nsplit;
+  const int nmine = cnt > split ? (cnt - split + stride - 1) / stride : 0;
+  for (int k0 = 0; k0 < nmine; k0 += 64) {
+    // entries split + (k0 + lane) stride, one per lane
+    int myb = 0;
+    float mylp = 0.f;
+    {
+      const int en = split + (k0 + l) * stride;
+      if (k0 + l < nmine) { myb = list[en]; mylp = lpl[en]; }
+    }
+    const int kn = min(64, nmine - k0);
+    for (int k = 0; k < kn; ++k) {
+      const int b = __shfl(myb, k, 64);
+      const float pr = __shfl(mylp, k, 64);
+      const bf16_t* kb = K + (size_t)b * DASH_BLOCK * D;
+      const bf16_t* vb = V + (size_t)b * DASH_BLOCK * D;
+      uint4 kr[16], vr[16];
+#pragma unroll
+      for (int it = 0; it < 16; ++it) kr[it] = *reinterpret_cast<const uint4*>(kb + (size_t)(it * 4 + g) * D + c * 8);
+#pragma unroll
+      for (int it = 0; it < 16; ++it) vr[it] = *reinterpret_cast<const uint4*>(vb + (size_t)(it * 4 + g) * D + c * 8);
+      float s[16];
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        float kf[8];
+        unpack8(kr[it], kf);
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part = fmaf(qf[e], kf[e], part);
+        s[it] = sum16(part) * sl2 + pr;
+      }
+      if ((b + 1) * DASH_BLOCK > n) {  // the own block, partly filled
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+          if (b * DASH_BLOCK + it * 4 + g >= n) {
+            s[it] = -INFINITY;
+            vr[it] = make_uint4(0u, 0u, 0u, 0u);
+          }
+        }
+      }
+      float mx = s[0];
+#pragma unroll
+      for (int it = 1; it < 16; ++it) mx = fmaxf(mx, s[it]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mn = fmaxf(m, mx);
+      const float rs = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - mn);
+      float ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] *= rs;
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const float p = __builtin_amdgcn_exp2f(s[it] - mn);
+        ps += p;
+        float vf[8];
+        unpack8(vr[it], vf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = fmaf(p, vf[e], o[e]);
+      }
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      lsum = lsum * rs + ps;
+      m = mn;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    o[e] += __shfl_xor(o[e], 16, 64);
+    o[e] += __shfl_xor(o[e], 32, 64);
+  }
+  float* part = a.part + ((size_t)row * a.nsplit + split) * (D + 2);
+  if (g == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[c * 8 + e] = o[e];
+  }
+  if (l == 0) {
+    part[D] = m;
+    part[D + 1] = lsum;
+  }
+}
+
 // ---------------------------------------------------------------------------- cache maintenance
 
 // One wave per row, 4 rows per workgroup; lane l moves elements 2l and 2l+1
@@ -349,6 +513,15 @@ hipError_t launch_decode(const DecodeArgs& a0, int dtype, hipStream_t st) {
   else decode_select_kernel<32><<<a.SH, 512, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.grp > 1) {
+    if (a.grp > 8 || a.SH % a.grp) return hipErrorInvalidValue;
+    decode_group_merge_kernel<<<a.SH / a.grp, 64, 0, st>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    decode_attend_group_kernel<<<dim3(a.nsplit, a.SH / a.grp), 64 * a.grp, 0, st>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    decode_combine_kernel<<<(a.SH + 3) / 4, 256, 0, st>>>(a);
+    return hipGetLastError();
+  }
   decode_attend_kernel<<<dim3(a.nsplit, a.SH), 256, 0, st>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   decode_combine_kernel<<<(a.SH + 3) / 4, 256, 0, st>>>(a);

@@ -160,7 +160,8 @@ def make_prefill(B, H, T, D, dtype="bf16", causal=True, planted=(1, 8), seed=0, 
     return out
 
 
-def make_decode(S, H, N, D, dtype="bf16", planted=(1, 16), seed=0, device="cpu", lens=None, beyond=None):
+def make_decode(S, H, N, D, dtype="bf16", planted=(1, 16), seed=0, device="cpu", lens=None, beyond=None,
+                kv_heads=None):
     """Decode workload: q [S, H, D] and caches k, v [S, H, N, D].
 
     The new token is the last cached token: position N-1, or lens[s]-1 when
@@ -168,19 +169,25 @@ def make_decode(S, H, N, D, dtype="bf16", planted=(1, 16), seed=0, device="cpu",
     Planted blocks are drawn among the query's candidates, the complete
     blocks before its own.  ``beyond`` (a float, e.g. NaN) overwrites the
     cache entries at positions >= lens[s] after everything is drawn.
+    ``kv_heads`` (default H) gives caches of that many heads, query head h
+    planted toward KV head h // (H / kv_heads).
     """
     if N % BLOCK:
         raise ValueError("N must be a multiple of 64")
     if lens is not None and (len(lens) != S or min(lens) < 1 or max(lens) > N):
         raise ValueError("lens must hold S lengths in [1, N]")
+    Hkv = H if kv_heads is None else kv_heads
+    if Hkv < 1 or H % Hkv:
+        raise ValueError("kv_heads must divide H")
+    G = H // Hkv
     td = torch_dtype(dtype)
     g = _gen(seed, device)
-    kc = torch.empty((S, H, N, D), dtype=td, device=device)
-    vc = torch.empty((S, H, N, D), dtype=td, device=device)
+    kc = torch.empty((S, Hkv, N, D), dtype=td, device=device)
+    vc = torch.empty((S, Hkv, N, D), dtype=td, device=device)
     for s in range(S):
-        kc[s] = _randn((H, N, D), g, td, device, chunk_rows=4)
+        kc[s] = _randn((Hkv, N, D), g, td, device, chunk_rows=4)
     for s in range(S):
-        vc[s] = _randn((H, N, D), g, td, device, chunk_rows=4)
+        vc[s] = _randn((Hkv, N, D), g, td, device, chunk_rows=4)
     q = torch.empty((S, H, D), dtype=td, device=device)
     for s in range(S):
         pos = torch.tensor([(N if lens is None else int(lens[s])) - 1], device=device)
@@ -189,7 +196,7 @@ def make_decode(S, H, N, D, dtype="bf16", planted=(1, 16), seed=0, device="cpu",
             if planted is None:
                 qp = noise
             else:
-                qp = 0.5 * noise + _planted_rows(kc[s, h], pos, True, planted[0], planted[1], g, device)
+                qp = 0.5 * noise + _planted_rows(kc[s, h // G], pos, True, planted[0], planted[1], g, device)
             q[s, h] = qp[0].float().to(td)
     if lens is not None and beyond is not None:
         for s in range(S):

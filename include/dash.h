@@ -321,6 +321,24 @@ dash_status dash_decode_step(const dash_decode_params* p, const void* q, const v
                              void* o, float* lse, int32_t* nsel, float* tau, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/*
+ * Decode for grouped-query heads (entmax head aggregation, as dash_fwd_gqa):
+ * p->H query heads share kv_heads key/value heads (kv_heads divides H, at
+ * most 8 query heads per KV head).  q [S,H,D]; kc, vc [S,kv_heads,N,D] and
+ * kbar [S,kv_heads,N/64,D] (N the capacity); len: NULL (every cache full,
+ * the new token at N-1) or device lengths as dash_decode_varlen.  Each query
+ * head gets its own alpha-entmax over its KV head's summaries; the group
+ * attends the blocks of pbar = the mean of the heads' p, with prior
+ * log pbar, and its own block (prior 0).  The heads of a group walk the same
+ * blocks together, so a block is read from HBM once per group.  Outputs
+ * o, lse [S,H], nsel and tau (each head's own entmax) as dash_decode;
+ * workspace as dash_decode with the same params.
+ */
+dash_status dash_decode_gqa(const dash_decode_params* p, int32_t kv_heads, const void* q,
+                            const void* kc, const void* vc, const void* kbar, const int32_t* len,
+                            void* o, float* lse, int32_t* nsel, float* tau, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
 /* Message of the last failing call on this thread ("" if none). */
 const char* dash_last_error(void);
 

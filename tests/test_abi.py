@@ -241,3 +241,18 @@ def test_partial_last_block_validation(L):
     assert L.dash_fwd_select(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(_sel()), None) == _lib.DASH_EINVAL
     assert L.dash_pool(ctypes.byref(p), FAKE, FAKE, None) == _lib.DASH_EINVAL
     assert L.dash_fwd_gqa(ctypes.byref(p), 2, *([FAKE] * 6), ctypes.byref(_sel()), None) == _lib.DASH_EINVAL
+
+
+def test_gqa_decode_validation(L):
+    p = _dparams(H=4)
+    need = L.dash_decode_workspace_bytes(ctypes.byref(p))
+    # q, kc, vc, kbar, len, o, lse, nsel, tau, ws
+    args = [FAKE] * 4 + [None, FAKE, None, None, None, FAKE]
+    assert L.dash_decode_gqa(ctypes.byref(p), 3, *args, need, None) == _lib.DASH_EINVAL
+    assert L.dash_decode_gqa(ctypes.byref(p), 2, *args, need - 1, None) == _lib.DASH_EWORKSPACE
+    bad = list(args)
+    bad[4] = FAKE + 2
+    assert L.dash_decode_gqa(ctypes.byref(p), 2, *bad, need, None) == _lib.DASH_EINVAL
+    p16 = _dparams(H=16)
+    need16 = L.dash_decode_workspace_bytes(ctypes.byref(p16))
+    assert L.dash_decode_gqa(ctypes.byref(p16), 1, *args, need16, None) == _lib.DASH_EUNSUPPORTED

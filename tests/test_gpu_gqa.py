@@ -146,3 +146,69 @@ def test_gqa_16k_sampled():
     gpu = _gpu(r, T // 64)
     st = check_rows({k: v for k, v in gpu.items()}, ora, rows, torch.bfloat16, 1.5, "gqa 16K")
     _say(f"  ok {st}")
+
+
+def _decode_check(out, ora, rows, prm, what):
+    from parity import TIE_BAND, tol_lse, tol_out
+    max_abs, mean_abs = tol_out(torch.bfloat16)
+    errs = []
+    for (s, h), (os_, oh) in rows:
+        errs.append(np.abs(_np64(out["o"][s, h]) - ora["o"][os_, oh]))
+        assert abs(float(out["lse"][s, h]) - ora["lse"][os_, oh]) <= tol_lse(torch.bfloat16), (what, s, h)
+        assert int(out["nsel"][s, h]) == int(ora["nsel"][os_, oh]), (what, s, h)
+        t, to = float(out["tau"][s, h]), float(ora["tau"][os_, oh])
+        assert (math.isnan(t) and math.isnan(to)) or abs(t - to) <= 4e-6 * max(1.0, abs(to)), (what, s, h, t, to)
+    E = np.stack(errs)
+    assert E.max() <= max_abs and E.mean() <= mean_abs, (what, E.max(), E.mean())
+    return float(E.max()), float(E.mean())
+
+
+@pytest.mark.parametrize("lens", [None, [1, 65, 700]], ids=["full", "lengths"])
+def test_gqa_decode_small(lens):
+    from differentiable_adaptive_block_amd import api
+    S, H, Hkv, C, D = 3, 4, 2, 1024, 128
+    _say(f"[gqa decode] S{S} H{H} Hkv{Hkv} C{C} lens {lens}")
+    w = inputs.make_decode(S, H, C, D, "bf16", (1, 4), seed=98, device="cpu", lens=lens, kv_heads=Hkv)
+    q, kc, vc = (w[x].to(DEV) for x in ("q", "k", "v"))
+    kbar = api.pool(kc.view(1, S * Hkv, C, D)).view(S, Hkv, C // 64, D)
+    cs = 4.0 / math.sqrt(D)
+    lt = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=DEV)
+    out = api.decode_gqa(q, kc, vc, kbar, lt, coarse_scale=cs)
+    torch.cuda.synchronize()
+    prm = oracle.Params(alpha=1.5, causal=True, coarse_scale=cs, storage="bf16")
+    ora = oracle.decode_gqa(_np64(q), _np64(kc), _np64(vc), lens, prm)
+    st = _decode_check(out, ora, [((s, h), (s, h)) for s in range(S) for h in range(H)], prm, "gqa decode")
+    _say(f"  ok {st}")
+
+
+def test_gqa_decode_one_kv_head_per_query_head_is_dash_decode():
+    from differentiable_adaptive_block_amd import api
+    S, H, C, D = 2, 4, 2048, 128
+    w = inputs.make_decode(S, H, C, D, "bf16", (1, 4), seed=99, device="cpu")
+    q, kc, vc = (w[x].to(DEV) for x in ("q", "k", "v"))
+    kbar = api.pool(kc.view(1, S * H, C, D)).view(S, H, C // 64, D)
+    a = {k: v.clone() for k, v in api.decode(q, kc, vc, kbar, coarse_scale=3 / math.sqrt(D)).items()}
+    b = api.decode_gqa(q, kc, vc, kbar, None, coarse_scale=3 / math.sqrt(D))
+    torch.cuda.synchronize()
+    assert torch.equal(a["nsel"], b["nsel"]) and torch.equal(a["tau"], b["tau"])
+    assert (a["o"].float() - b["o"].float()).abs().max().item() <= 1e-2
+    assert (a["lse"] - b["lse"]).abs().max().item() <= 1e-4
+
+
+def test_gqa_decode_96k_sampled():
+    from differentiable_adaptive_block_amd import api
+    wl = inputs.CONFIGS["c4cal"]
+    S, H, Hkv, C, D = 4, 32, 8, wl.shape["N"], wl.shape["D"]
+    _say(f"[gqa decode] 96K cache S{S} H{H} Hkv{Hkv}")
+    w = inputs.make_decode(S, H, C, D, "bf16", wl.planted, wl.seed, device=DEV, kv_heads=Hkv)
+    q, kc, vc = w["q"], w["k"], w["v"]
+    kbar = api.pool(kc.view(1, S * Hkv, C, D)).view(S, Hkv, C // 64, D)
+    out = api.decode_gqa(q, kc, vc, kbar, None, coarse_scale=wl.coarse_scale)
+    torch.cuda.synchronize()
+    prm = oracle.Params(alpha=1.5, causal=True, coarse_scale=wl.coarse_scale, storage="bf16")
+    G = H // Hkv
+    for (s, kv) in [(0, 0), (3, 5)]:
+        ora = oracle.decode_gqa(_np64(q[s:s + 1, kv * G:(kv + 1) * G]), _np64(kc[s:s + 1, kv:kv + 1]),
+                                _np64(vc[s:s + 1, kv:kv + 1]), None, prm)
+        st = _decode_check(out, ora, [((s, kv * G + g), (0, g)) for g in range(G)], prm, f"gqa decode {s} {kv}")
+        _say(f"  ok group ({s}, {kv}): {st}")
