@@ -553,6 +553,67 @@ def bench_decode_step(name, steps, warmup, device):
     return res
 
 
+def bench_decode_gqa(steps, warmup, device, kv_heads=8):
+    """Grouped-query decode on the calibrated 96K shape: 16 sequences x 32 query heads over
+    8 KV heads (4 per group), full 98304-token caches; each block of a group's union is
+    read once for its 4 heads."""
+    from differentiable_adaptive_block_amd import _lib, api, inputs
+
+    wl = inputs.CONFIGS["c4cal"]
+    sh = wl.shape
+    S, H, C, D = sh["S"], sh["H"], sh["N"], sh["D"]
+    w = inputs.make_decode(S, H, C, D, wl.dtype, wl.planted, wl.seed + 500, device=device, kv_heads=kv_heads)
+    q, kc, vc = w["q"], w["k"], w["v"]
+    kbar = api.pool(kc.view(1, S * kv_heads, C, D)).view(S, kv_heads, C // 64, D)
+    torch.cuda.synchronize()
+    p = api.make_decode_params(q, kc, wl.alpha, None, wl.coarse_scale)
+    p.H = H
+    bufs = api.DecodeBuffers(p, q.dtype, q.device)
+    st = torch.cuda.current_stream().cuda_stream
+
+    def step():
+        _lib.decode_gqa(p, kv_heads, q.data_ptr(), kc.data_ptr(), vc.data_ptr(), kbar.data_ptr(), None,
+                        bufs.o.data_ptr(), bufs.lse.data_ptr(), bufs.nsel.data_ptr(), bufs.tau.data_ptr(),
+                        bufs.ws.data_ptr(), bufs.ws_bytes, st)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [_events(2) for _ in range(steps)]
+    for e in evs:
+        e[0].record()
+        step()
+        e[1].record()
+    torch.cuda.synchronize()
+    us = sum(e[0].elapsed_time(e[1]) for e in evs) / steps * 1e3
+    G = H // kv_heads
+    # the group's list length (union + own block) is what the walk reads; the decode leaves it in its workspace
+    sel_cnt = _decode_list_counts(p, bufs)
+    groups = sel_cnt.view(S * kv_heads, G)[:, 0].to(torch.float64)  # union + own block, per group
+    sel_bytes = float(groups.sum()) * 64 * D * 2 * 2
+    res = dict(S=S, H=H, kv_heads=kv_heads, N=C, D=D, coarse_scale=wl.coarse_scale, us_per_step=us,
+               mean_union_blocks=float(groups.mean()) - 1.0,
+               mean_own_blocks=float(bufs.nsel.double().mean()), selected_bytes_gb=sel_bytes / 1e9,
+               hbm_gbs_selected=sel_bytes / (us * 1e-6) / 1e9,
+               work="bytes = (union of the group's selected blocks + own block) x 64 keys x D x 2 (K,V) x 2 B, "
+                    "once per group")
+    res["frac_of_hbm_peak"] = res["hbm_gbs_selected"] / PEAK_HBM_GBS
+    del w, q, kc, vc, kbar, bufs
+    torch.cuda.empty_cache()
+    return res
+
+
+def _decode_list_counts(p, bufs):
+    """The per-row list lengths the decode left in its workspace: the third region of
+    dash_decode's workspace (after the [S*H, N/64] scores and the [S*H, 2] row statistics,
+    each rounded up to 256 bytes), int32 [S*H]."""
+    SH = p.S * p.H
+    nb = p.N // 64
+    o0 = (SH * nb * 4 + 255) // 256 * 256
+    o1 = o0 + (SH * 2 * 4 + 255) // 256 * 256
+    return bufs.ws[o1:o1 + SH * 4].view(torch.int32).clone()
+
+
 def traffic_probe(device):
     """The launches the counter summary is taken from: a plain copy of 1 GiB
     (calibration: it reads and writes exactly 2^30 bytes), one 16K prefill
@@ -648,6 +709,9 @@ def main():
             log(f"{name}: {d}")
             dec[name] = d
         extra["decode_96k"] = dec
+        dg = bench_decode_gqa(max(5, args.steps), args.warmup, dev)
+        log(f"decode gqa c4cal: {dg}")
+        extra["decode_96k_gqa"] = dg
         ds = bench_decode_step("c4cal", max(5, args.steps), args.warmup, dev)
         log(f"decode step c4cal ragged: {ds}")
         extra["decode_step_96k_ragged"] = ds

@@ -123,7 +123,7 @@ size_t decode_ws_layout(const dash_decode_params* p, size_t off[6], int* nsplit,
   off[2] = take(SH * sizeof(int));                 // list length
   off[3] = take(SH * nb * sizeof(int));            // list
   off[4] = take(SH * nb * sizeof(float));          // log2 priors
-  off[5] = take(SH * ns * (D + 2) * sizeof(float));  // partials
+  off[5] = take(SH * DASH_DEC_SPLIT_GQA * (D + 2) * sizeof(float));  // partials (the larger split count)
   return o;
 }
 
@@ -630,7 +630,8 @@ dash_status dash_decode_gqa(const dash_decode_params* p, int32_t kv_heads, const
   if (s != DASH_OK) return s;
   if (kv_heads < 1 || p->H % kv_heads) return fail(DASH_EINVAL, "kv_heads (%d) must divide H (%d)", kv_heads, p->H);
   const int grp = p->H / kv_heads;
-  if (grp > 8) return fail(DASH_EUNSUPPORTED, "more than 8 query heads per KV head is not built (got %d)", grp);
+  if (grp != 1 && grp != 2 && grp != 4 && grp != 8)
+    return fail(DASH_EUNSUPPORTED, "1, 2, 4 or 8 query heads per KV head are built (got %d)", grp);
   if (len && reinterpret_cast<uintptr_t>(len) % 4) return fail(DASH_EINVAL, "len must be 4-byte aligned");
   return decode_common(p, q, kc, vc, kbar, len, 0, o, lse, nsel, tau, workspace, workspace_bytes, stream, grp);
 }

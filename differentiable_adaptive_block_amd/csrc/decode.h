@@ -3,6 +3,9 @@
 
 #include "common.h"
 
+#define DASH_DEC_SPLIT 16      // split-KV workgroups per decode row
+#define DASH_DEC_SPLIT_GQA 64  // split-KV workgroups per group of grouped-query decode rows
+
 struct DecodeArgs {
   const void* q;     // [SH, D]
   const void* kc;    // [SH, N, D], N the capacity

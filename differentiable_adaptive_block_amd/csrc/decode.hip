@@ -27,6 +27,7 @@
 #include "kernels.h"
 #include "decode.h"
 #include "entmax.h"
+#include "tiles.h"
 
 #define LOG2E_F 1.4426950408889634f
 #define LN2_F 0.6931471805599453f
@@ -276,9 +277,9 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(DecodeArgs a) {
 // One wave per row, 4 rows per workgroup: lane s < nsplit holds split s's
 // (m, l); the output sums run over the splits with their scales read back
 // lane by lane.
+template <int NS>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   constexpr int D = 128;
-  constexpr int NS = DASH_DEC_SPLIT;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= a.SH) return;
   const int l = threadIdx.x & 63;
@@ -314,16 +315,18 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 
 // Grouped-query heads (entmax head aggregation): the grp heads of a group
 // share one list, the blocks where pbar = (1/grp) sum_h p_h > 0, with log2
-// pbar as prior, then the own block (prior 0).  One wave per group; the
-// list sits in the group's first row.  A length out of range gives every
-// row of the group an empty list.
-__global__ __launch_bounds__(64) void decode_group_merge_kernel(DecodeArgs a) {
-  const int l = threadIdx.x;
+// pbar as prior, then the own block (prior 0).  One 4-wave workgroup per
+// group, 256 candidates per step (a ballot per wave, the waves' counts
+// added in LDS); the list sits in the group's first row.  A length out of
+// range gives every row of the group an empty list.
+__global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeArgs a) {
+  __shared__ int wcnt[4];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int row0 = blockIdx.x * a.grp;
   const int nbc = a.N / DASH_BLOCK;
   const int n = decode_row_len(a, row0);
   if (n < 1 || n > a.N) {
-    if (l < a.grp) a.sel_cnt[row0 + l] = 0;
+    if (tid < a.grp) a.sel_cnt[row0 + tid] = 0;
     return;
   }
   const int own = (n - 1) / DASH_BLOCK;
@@ -331,33 +334,54 @@ __global__ __launch_bounds__(64) void decode_group_merge_kernel(DecodeArgs a) {
   float* lp = a.sel_lp + (size_t)row0 * nbc;
   const float inv = 1.f / (float)a.grp;
   int base = 0;
-  for (int c0 = 0; c0 < own; c0 += 64) {
-    const int idx = c0 + l;
+  for (int c0 = 0; c0 < own; c0 += 256) {
+    const int idx = c0 + tid;
     float ps = 0.f;
     if (idx < own)
       for (int g = 0; g < a.grp; ++g) ps += a.zrow[(size_t)(row0 + g) * nbc + idx];
     const bool s = ps > 0.f;
     const unsigned long long bal = __ballot(s);
+    if (l == 0) wcnt[w] = __popcll(bal);
+    __syncthreads();
+    int before = base, total = 0;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      before += x < w ? wcnt[x] : 0;
+      total += wcnt[x];
+    }
     if (s) {
-      const int pos = base + __popcll(bal & ((1ull << l) - 1ull));
+      const int pos = before + __popcll(bal & ((1ull << l) - 1ull));
       list[pos] = idx;
       lp[pos] = __log2f(ps * inv);
     }
-    base += __popcll(bal);
+    base += total;
+    __syncthreads();  // the counts are read before the next step overwrites them
   }
-  if (l == 0) {
+  if (tid == 0) {
     list[base] = own;
     lp[base] = 0.f;
   }
-  if (l < a.grp) a.sel_cnt[row0 + l] = base + 1;
+  if (tid < a.grp) a.sel_cnt[row0 + tid] = base + 1;
 }
 
 // Split-KV attention for a group: workgroup (split, group), wave w = the
-// group's head w; every wave walks the same list entries (split, split +
-// nsplit, ...), so each block is read from HBM once for the group and its
-// other reads hit the cache.  Each wave writes its row's partial.
-__global__ __launch_bounds__(512) void decode_attend_group_kernel(DecodeArgs a) {
+// group's head w; the workgroup walks list entries split, split + nsplit, ...
+// Each block's K and V (32 KB) are read from HBM once: the waves copy a
+// share each straight into LDS (buffer loads to LDS, double-buffered, the
+// next block's copy in flight while this one is used), then every wave
+// computes its head from LDS with the same lane layout as the per-head
+// kernel (16 lanes read one 256-byte row: no bank conflicts, no permutation
+// needed).  Each wave writes its row's partial.  NW = 2, 4 or 8 heads.
+__device__ constexpr int tile_swz_none(int) { return 0; }
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void decode_attend_group_kernel(DecodeArgs a) {
   constexpr int D = 128;
+  constexpr int CH = D / 8;  // 16-byte chunks per row
+  __shared__ __attribute__((aligned(16))) bf16_t kt0[DASH_BLOCK * D];
+  __shared__ __attribute__((aligned(16))) bf16_t kt1[DASH_BLOCK * D];
+  __shared__ __attribute__((aligned(16))) bf16_t vt0[DASH_BLOCK * D];
+  __shared__ __attribute__((aligned(16))) bf16_t vt1[DASH_BLOCK * D];
   const int split = blockIdx.x, grp_id = blockIdx.y;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int row = grp_id * a.grp + w;
@@ -371,76 +395,103 @@ __global__ __launch_bounds__(512) void decode_attend_group_kernel(DecodeArgs a) 
   const bf16_t* K = reinterpret_cast<const bf16_t*>(a.kc) + (size_t)grp_id * a.N * D;
   const bf16_t* V = reinterpret_cast<const bf16_t*>(a.vc) + (size_t)grp_id * a.N * D;
   const float sl2 = a.fine_scale * LOG2E_F;
-  float qf[8];
-  unpack8(*reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.q) + (size_t)row * D + c * 8), qf);
+  // the query's 8 features of this lane as bf16 pairs (scores by v_dot2)
+  const uint4 qraw = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.q) + (size_t)row * D + c * 8);
+  const bf16x2 q0 = __builtin_bit_cast(bf16x2, qraw.x), q1 = __builtin_bit_cast(bf16x2, qraw.y);
+  const bf16x2 q2 = __builtin_bit_cast(bf16x2, qraw.z), q3 = __builtin_bit_cast(bf16x2, qraw.w);
+  const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
   float m = -INFINITY, lsum = 0.f;
   float o[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = 0.f;
   const int stride = a.nsplit;
   const int nmine = cnt > split ? (cnt - split + stride - 1) / stride : 0;
-  for (int k0 = 0; k0 < nmine; k0 += 64) {
-    // entries split + (k0 + lane) stride, one per lane
-    int myb = 0;
-    float mylp = 0.f;
-    {
-      const int en = split + (k0 + l) * stride;
-      if (k0 + l < nmine) { myb = list[en]; mylp = lpl[en]; }
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  TileCopy<D, tile_swz_none, NW> kcp, vcp;
+  kcp.init(wu, l);
+  vcp.init(wu, l);
+  auto copy_block = [&](int b, bf16_t* kd, bf16_t* vd) {
+    const size_t off = (size_t)__builtin_amdgcn_readfirstlane(b) * DASH_BLOCK * D;
+    kcp.copy(K + off, kd, wu);
+    vcp.copy(V + off, vd, wu);
+  };
+  int b = 0;
+  float pr = 0.f;
+  if (nmine > 0) {
+    b = list[split];
+    pr = lpl[split];
+    copy_block(b, kt0, vt0);
+  }
+  for (int k = 0; k < nmine; ++k) {
+    // the next entry's block and prior, loaded before the wait below so that
+    // the wait covers them too
+    int bn = 0;
+    float prn = 0.f;
+    if (k + 1 < nmine) {
+      bn = list[split + (k + 1) * stride];
+      prn = lpl[split + (k + 1) * stride];
     }
-    const int kn = min(64, nmine - k0);
-    for (int k = 0; k < kn; ++k) {
-      const int b = __shfl(myb, k, 64);
-      const float pr = __shfl(mylp, k, 64);
-      const bf16_t* kb = K + (size_t)b * DASH_BLOCK * D;
-      const bf16_t* vb = V + (size_t)b * DASH_BLOCK * D;
-      uint4 kr[16], vr[16];
+    tile_copies_done();
+    __syncthreads();  // block k is in LDS; every wave is done with the other buffers
+    const bf16_t* kt = (k & 1) ? kt1 : kt0;
+    const bf16_t* vt = (k & 1) ? vt1 : vt0;
+    if (k + 1 < nmine) copy_block(bn, (k & 1) ? kt0 : kt1, (k & 1) ? vt0 : vt1);
+    float s[16];
 #pragma unroll
-      for (int it = 0; it < 16; ++it) kr[it] = *reinterpret_cast<const uint4*>(kb + (size_t)(it * 4 + g) * D + c * 8);
-#pragma unroll
-      for (int it = 0; it < 16; ++it) vr[it] = *reinterpret_cast<const uint4*>(vb + (size_t)(it * 4 + g) * D + c * 8);
-      float s[16];
-#pragma unroll
-      for (int it = 0; it < 16; ++it) {
-        float kf[8];
-        unpack8(kr[it], kf);
-        float part = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) part = fmaf(qf[e], kf[e], part);
-        s[it] = sum16(part) * sl2 + pr;
-      }
-      if ((b + 1) * DASH_BLOCK > n) {  // the own block, partly filled
-#pragma unroll
-        for (int it = 0; it < 16; ++it) {
-          if (b * DASH_BLOCK + it * 4 + g >= n) {
-            s[it] = -INFINITY;
-            vr[it] = make_uint4(0u, 0u, 0u, 0u);
-          }
-        }
-      }
-      float mx = s[0];
-#pragma unroll
-      for (int it = 1; it < 16; ++it) mx = fmaxf(mx, s[it]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mn = fmaxf(m, mx);
-      const float rs = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - mn);
-      float ps = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] *= rs;
-#pragma unroll
-      for (int it = 0; it < 16; ++it) {
-        const float p = __builtin_amdgcn_exp2f(s[it] - mn);
-        ps += p;
-        float vf[8];
-        unpack8(vr[it], vf);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = fmaf(p, vf[e], o[e]);
-      }
-      ps += __shfl_xor(ps, 16, 64);
-      ps += __shfl_xor(ps, 32, 64);
-      lsum = lsum * rs + ps;
-      m = mn;
+    for (int it = 0; it < 16; ++it) {
+      const uint4 kr = *reinterpret_cast<const uint4*>(kt + (it * 4 + g) * D + c * 8);
+      float part = __builtin_amdgcn_fdot2_f32_bf16(q0, __builtin_bit_cast(bf16x2, kr.x), 0.f, false);
+      part = __builtin_amdgcn_fdot2_f32_bf16(q1, __builtin_bit_cast(bf16x2, kr.y), part, false);
+      part = __builtin_amdgcn_fdot2_f32_bf16(q2, __builtin_bit_cast(bf16x2, kr.z), part, false);
+      part = __builtin_amdgcn_fdot2_f32_bf16(q3, __builtin_bit_cast(bf16x2, kr.w), part, false);
+      s[it] = sum16(part) * sl2 + pr;
     }
+    const bool partial = (b + 1) * DASH_BLOCK > n;  // the own block, partly filled
+    if (partial) {
+#pragma unroll
+      for (int it = 0; it < 16; ++it)
+        if (b * DASH_BLOCK + it * 4 + g >= n) s[it] = -INFINITY;
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int it = 1; it < 16; ++it) mx = fmaxf(mx, s[it]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mn = fmaxf(m, mx);
+    const float rs = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - mn);
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= rs;
+    // weights rounded to bf16 two keys at a time; each v_dot2 adds both keys'
+    // products for one feature (the two keys' values paired by v_perm), and
+    // the normaliser sums the same rounded weights
+#pragma unroll
+    for (int it = 0; it < 16; it += 2) {
+      uint4 va = *reinterpret_cast<const uint4*>(vt + (it * 4 + g) * D + c * 8);
+      uint4 vb = *reinterpret_cast<const uint4*>(vt + ((it + 1) * 4 + g) * D + c * 8);
+      if (partial) {
+        if (b * DASH_BLOCK + it * 4 + g >= n) va = make_uint4(0u, 0u, 0u, 0u);
+        if (b * DASH_BLOCK + (it + 1) * 4 + g >= n) vb = make_uint4(0u, 0u, 0u, 0u);
+      }
+      bf16x2 pp;
+      pp[0] = (__bf16)__builtin_amdgcn_exp2f(s[it] - mn);
+      pp[1] = (__bf16)__builtin_amdgcn_exp2f(s[it + 1] - mn);
+      ps = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, ps, false);
+      const uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wb[4] = {vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const bf16x2 lo = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(wb[d], wa[d], 0x05040100u));
+        const bf16x2 hi = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(wb[d], wa[d], 0x07060302u));
+        o[2 * d] = __builtin_amdgcn_fdot2_f32_bf16(pp, lo, o[2 * d], false);
+        o[2 * d + 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, hi, o[2 * d + 1], false);
+      }
+    }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    lsum = lsum * rs + ps;
+    m = mn;
+    b = bn;
+    pr = prn;
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -514,16 +565,21 @@ hipError_t launch_decode(const DecodeArgs& a0, int dtype, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.grp > 1) {
-    if (a.grp > 8 || a.SH % a.grp) return hipErrorInvalidValue;
-    decode_group_merge_kernel<<<a.SH / a.grp, 64, 0, st>>>(a);
+    if (a.SH % a.grp) return hipErrorInvalidValue;
+    decode_group_merge_kernel<<<a.SH / a.grp, 256, 0, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    decode_attend_group_kernel<<<dim3(a.nsplit, a.SH / a.grp), 64 * a.grp, 0, st>>>(a);
+    a.nsplit = DASH_DEC_SPLIT_GQA;  // a group walks G times the blocks of a row: more splits
+    const dim3 grid(a.nsplit, a.SH / a.grp);
+    if (a.grp == 2) decode_attend_group_kernel<2><<<grid, 128, 0, st>>>(a);
+    else if (a.grp == 4) decode_attend_group_kernel<4><<<grid, 256, 0, st>>>(a);
+    else if (a.grp == 8) decode_attend_group_kernel<8><<<grid, 512, 0, st>>>(a);
+    else return hipErrorNotSupported;
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    decode_combine_kernel<<<(a.SH + 3) / 4, 256, 0, st>>>(a);
+    decode_combine_kernel<DASH_DEC_SPLIT_GQA><<<(a.SH + 3) / 4, 256, 0, st>>>(a);
     return hipGetLastError();
   }
   decode_attend_kernel<<<dim3(a.nsplit, a.SH), 256, 0, st>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  decode_combine_kernel<<<(a.SH + 3) / 4, 256, 0, st>>>(a);
+  decode_combine_kernel<DASH_DEC_SPLIT><<<(a.SH + 3) / 4, 256, 0, st>>>(a);
   return hipGetLastError();
 }

@@ -3,7 +3,6 @@
 
 #include "common.h"
 
-#define DASH_DEC_SPLIT 16  // split-KV workgroups per decode row
 
 struct SelectArgs {
   const void* q;      // [BH, T, D]

@@ -323,8 +323,8 @@ dash_status dash_decode_step(const dash_decode_params* p, const void* q, const v
 
 /*
  * Decode for grouped-query heads (entmax head aggregation, as dash_fwd_gqa):
- * p->H query heads share kv_heads key/value heads (kv_heads divides H, at
- * most 8 query heads per KV head).  q [S,H,D]; kc, vc [S,kv_heads,N,D] and
+ * p->H query heads share kv_heads key/value heads (H / kv_heads is 1, 2, 4
+ * or 8).  q [S,H,D]; kc, vc [S,kv_heads,N,D] and
  * kbar [S,kv_heads,N/64,D] (N the capacity); len: NULL (every cache full,
  * the new token at N-1) or device lengths as dash_decode_varlen.  Each query
  * head gets its own alpha-entmax over its KV head's summaries; the group
