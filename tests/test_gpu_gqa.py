@@ -212,3 +212,19 @@ def test_gqa_decode_96k_sampled():
                                 _np64(vc[s:s + 1, kv:kv + 1]), None, prm)
         st = _decode_check(out, ora, [((s, kv * G + g), (0, g)) for g in range(G)], prm, f"gqa decode {s} {kv}")
         _say(f"  ok group ({s}, {kv}): {st}")
+
+
+def test_gqa_autograd():
+    from differentiable_adaptive_block_amd import api
+    w = inputs.make_prefill(1, 4, 512, 128, "bf16", True, (1, 3), seed=89, device="cpu", with_dout=True, kv_heads=2)
+    w = {k: v.to(DEV) for k, v in w.items()}
+    q, k, v = (w[x].clone().requires_grad_(True) for x in ("q", "k", "v"))
+    cs = 4 / math.sqrt(128)
+    o = api.dash_attention(q, k, v, 1.5, True, None, cs)
+    (o.float() * w["dout"].float()).sum().backward()
+    r = api.forward(w["q"], w["k"], w["v"], alpha=1.5, causal=True, coarse_scale=cs)
+    g = api.backward(w["q"], w["k"], w["v"], r["o"], r["lse"], w["dout"], r["kbar"], r["sel"], r["params"])
+    torch.cuda.synchronize()
+    assert k.grad.shape == k.shape and v.grad.shape == v.shape
+    for t, n in ((q, "dq"), (k, "dk"), (v, "dv")):
+        assert torch.equal(t.grad, g[n]), n

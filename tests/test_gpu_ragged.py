@@ -129,3 +129,18 @@ def test_ragged_16k_sampled():
     ora = oracle.forward_rows(q64, k64, v64, prm, rows)
     st = check_rows(_gpu(r, T), ora, rows, torch.bfloat16, 1.5, "ragged 16K")
     _say(f"  ok {st}")
+
+
+def test_ragged_autograd():
+    from differentiable_adaptive_block_amd import api
+    w = _make(1, 2, 300, 128, "bf16", (1, 3), 98)
+    q, k, v = (w[x].clone().requires_grad_(True) for x in ("q", "k", "v"))
+    cs = 4 / math.sqrt(128)
+    o = api.dash_attention(q, k, v, 1.5, True, None, cs)
+    (o.float() * w["dout"].float()).sum().backward()
+    r = api.forward(w["q"], w["k"], w["v"], alpha=1.5, causal=True, coarse_scale=cs)
+    g = api.backward(w["q"], w["k"], w["v"], r["o"], r["lse"], w["dout"], r["kbar"], r["sel"], r["params"])
+    torch.cuda.synchronize()
+    assert o.shape == w["q"].shape
+    for t, n in ((q, "dq"), (k, "dk"), (v, "dv")):
+        assert torch.equal(t.grad, g[n]), n
