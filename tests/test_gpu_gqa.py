@@ -44,6 +44,7 @@ CASES = [
     ("b2-h8-kv2-causal", 2, 8, 2, 512, 128, True, 1.5, 6.0, (1, 3)),
     ("h2-kv1-causal-a1", 1, 2, 1, 640, 128, True, 1.0, 2.0, (1, 3)),
     ("h4-kv2-causal-a2", 1, 4, 2, 576, 128, True, 2.0, 6.0, (1, 3)),
+    ("h4-kv1-causal-T2048", 1, 4, 1, 2048, 128, True, 1.5, 6.0, (1, 4)),
 ]
 
 
