@@ -141,3 +141,40 @@ def test_zero_head_gradients_match_mean_pooling_path():
     prm = oracle.Params(alpha=1.5, causal=True, coarse_scale=cs, storage="bf16")
     ref = oracle.backward(*(_np64(w[x]) for x in ("q", "k", "v", "dout")), prm, w=np.zeros((H, D)))
     assert rel_l2(_np64(g1["dw"]), ref["dw"]) <= 5e-2
+
+
+def test_summariser_training_16k_sampled():
+    """The 16K training shape (B2 H16 T16384) with a non-zero summariser head: dQ on sampled
+    rows, dK, dV and the summary gradient of the last key blocks (attended only by the last
+    rows), against the oracle over those rows; dw needs every row and is checked at small sizes."""
+    from differentiable_adaptive_block_amd import api
+    wl = inputs.CONFIGS["c5"]
+    sh = wl.shape
+    _say(f"[summariser] c5 full size {sh} (sampled)")
+    w = inputs.make_prefill(sh["B"], sh["H"], sh["T"], sh["D"], wl.dtype, True, wl.planted, wl.seed, device=DEV,
+                            with_dout=True)
+    head = _head(sh["H"], sh["D"], 2.0, 59).to(DEV)
+    r = api.forward(w["q"], w["k"], w["v"], alpha=1.5, causal=True, coarse_scale=wl.coarse_scale,
+                    summariser_w=head, want_mask=False)
+    g = api.backward(w["q"], w["k"], w["v"], r["o"], r["lse"], w["dout"], r["kbar"], r["sel"], r["params"],
+                     summariser_w=head)
+    torch.cuda.synchronize()
+    T = sh["T"]
+    nb = T // 64
+    prm = oracle.Params(alpha=1.5, causal=True, coarse_scale=wl.coarse_scale, storage="bf16")
+    rng = np.random.default_rng(3)
+    for (b, h) in [(0, int(rng.integers(sh["H"]))), (1, int(rng.integers(sh["H"])))]:
+        x = {n: _np64(w[n][b:b + 1, h:h + 1]) for n in ("q", "k", "v", "dout")}
+        hw = _np64(head[h:h + 1])
+        np.testing.assert_array_equal(_np64(r["kbar"][b, h]), oracle.pool_attention(x["k"][0, 0], hw[0], 64, "bf16"))
+        tail = 4 * 64
+        rows = [(0, 0, i) for i in range(T - tail, T)]
+        rows += [(0, 0, int(i)) for i in rng.choice(T - tail, size=24, replace=False)]
+        ref = oracle.backward_rows(x["q"], x["k"], x["v"], x["dout"], prm, rows, w=hw)
+        ridx = np.array([i for (_, _, i) in rows])
+        e_dq = rel_l2(_np64(g["dq"][b, h])[ridx], ref["dq"][0, 0][ridx])
+        e_dk = rel_l2(_np64(g["dk"][b, h])[T - tail:], ref["dk"][0, 0][T - tail:])
+        e_dv = rel_l2(_np64(g["dv"][b, h])[T - tail:], ref["dv"][0, 0][T - tail:])
+        e_kb = rel_l2(_np64(g["dkbar"][b, h])[nb - 4:nb - 1], ref["dkbar"][0, 0][nb - 4:nb - 1])
+        _say(f"  (b={b}, h={h}) rel-L2 dq {e_dq:.2e} dk {e_dk:.2e} dv {e_dv:.2e} dkbar {e_kb:.2e}")
+        assert max(e_dq, e_dk, e_dv, e_kb) <= 5e-2
