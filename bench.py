@@ -233,7 +233,7 @@ def bench_training(alpha, steps, warmup, device, learned_summariser=False):
     ``learned_summariser`` Stage 0 is the attention-pooling head (forward and its gradient)."""
     from differentiable_adaptive_block_amd import api, inputs
 
-    wl = inputs.CONFIGS["c5"]
+    wl = inputs.CONFIGS["train16k"]
     sh = wl.shape
     w = inputs.make_prefill(sh["B"], sh["H"], sh["T"], sh["D"], wl.dtype, True, wl.planted, wl.seed, device=device,
                             with_dout=True)
@@ -335,7 +335,7 @@ def bench_gqa(steps, warmup, device, kv_heads=8):
     union supports; then one training step (forward + dash_bwd_gqa)."""
     from differentiable_adaptive_block_amd import _lib, api, inputs
 
-    wl = inputs.CONFIGS["c2"]
+    wl = inputs.CONFIGS["prefill16k"]
     sh = wl.shape
     B, H, T, D = sh["B"], sh["H"], sh["T"], sh["D"]
     w = inputs.make_prefill(B, H, T, D, wl.dtype, True, wl.planted, wl.seed + 400, device=device, with_dout=True,
@@ -405,7 +405,7 @@ def bench_ragged(steps, warmup, device, cut=37):
     block): dash_fwd on zero-padded workspace copies, whole forward timed."""
     from differentiable_adaptive_block_amd import _lib, api, inputs
 
-    wl = inputs.CONFIGS["c2"]
+    wl = inputs.CONFIGS["prefill16k"]
     sh = wl.shape
     B, H, D = sh["B"], sh["H"], sh["D"]
     T = sh["T"] - cut
@@ -559,7 +559,7 @@ def bench_decode_gqa(steps, warmup, device, kv_heads=8):
     read once for its 4 heads."""
     from differentiable_adaptive_block_amd import _lib, api, inputs
 
-    wl = inputs.CONFIGS["c4cal"]
+    wl = inputs.CONFIGS["decode96k_sc5"]
     sh = wl.shape
     S, H, C, D = sh["S"], sh["H"], sh["N"], sh["D"]
     w = inputs.make_decode(S, H, C, D, wl.dtype, wl.planted, wl.seed + 500, device=device, kv_heads=kv_heads)
@@ -628,23 +628,23 @@ def traffic_probe(device):
     torch.cuda.synchronize()
     del src, dst
     torch.cuda.empty_cache()
-    wl = inputs.CONFIGS["c2"]
+    wl = inputs.CONFIGS["prefill16k"]
     sh = wl.shape
     w = inputs.make_prefill(sh["B"], sh["H"], sh["T"], sh["D"], wl.dtype, wl.causal, wl.planted, wl.seed,
                             device=device, with_dout=False)
     torch.cuda.synchronize()
-    log("prefill forward c2")
+    log("prefill16k forward")
     api.forward(w["q"], w["k"], w["v"], alpha=wl.alpha, causal=wl.causal, coarse_scale=wl.coarse_scale,
                 want_mask=False)
     torch.cuda.synchronize()
     del w
     torch.cuda.empty_cache()
-    wl = inputs.CONFIGS["c4cal"]
+    wl = inputs.CONFIGS["decode96k_sc5"]
     sh = wl.shape
     w = inputs.make_decode(sh["S"], sh["H"], sh["N"], sh["D"], wl.dtype, wl.planted, wl.seed, device=device)
     kbar = api.pool(w["k"].view(1, sh["S"] * sh["H"], sh["N"], sh["D"])).view(sh["S"], sh["H"], -1, sh["D"])
     torch.cuda.synchronize()
-    log("decode c4cal")
+    log("decode96k_sc5 decode")
     api.decode(w["q"], w["k"], w["v"], kbar, alpha=wl.alpha, coarse_scale=wl.coarse_scale)
     torch.cuda.synchronize()
     print(json.dumps({"stage2_source_digest": stage2_digest()}))
@@ -682,17 +682,17 @@ def main():
         traffic_probe(dev)
         return
     out = {}
-    res, shape = bench_prefill("c2", args.steps, args.warmup, dev)
-    log(f"c2: {res}")
+    res, shape = bench_prefill("prefill16k", args.steps, args.warmup, dev)
+    log(f"prefill16k: {res}")
     extra = {}
     if not args.no_64k:
-        r3, _ = bench_prefill("c3", max(2, args.steps // 3), 1, dev)
-        log(f"c3: {r3}")
+        r3, _ = bench_prefill("prefill64k", max(2, args.steps // 3), 1, dev)
+        log(f"prefill64k: {r3}")
         extra["prefill_64k"] = r3
         # the same 64K prefill at coarse scale 7/sqrt(128): the selected-block
         # fraction the workload text asks for (<= 10%) that 2/sqrt(128) does not give
-        r3c, _ = bench_prefill("c3cal", max(2, args.steps // 3), 1, dev)
-        log(f"c3cal: {r3c}")
+        r3c, _ = bench_prefill("prefill64k_sc7", max(2, args.steps // 3), 1, dev)
+        log(f"prefill64k_sc7: {r3c}")
         extra["prefill_64k_calibrated"] = r3c
 
     rg = bench_ragged(max(3, args.steps // 2), 1, dev)
@@ -704,16 +704,16 @@ def main():
 
     if not args.no_decode:
         dec = {}
-        for name in ("c4cal", "c4"):
+        for name in ("decode96k_sc5", "decode96k"):
             d = bench_decode(name, max(5, args.steps), args.warmup, dev)
             log(f"{name}: {d}")
             dec[name] = d
         extra["decode_96k"] = dec
         dg = bench_decode_gqa(max(5, args.steps), args.warmup, dev)
-        log(f"decode gqa c4cal: {dg}")
+        log(f"decode gqa decode96k_sc5: {dg}")
         extra["decode_96k_gqa"] = dg
-        ds = bench_decode_step("c4cal", max(5, args.steps), args.warmup, dev)
-        log(f"decode step c4cal ragged: {ds}")
+        ds = bench_decode_step("decode96k_sc5", max(5, args.steps), args.warmup, dev)
+        log(f"decode step decode96k_sc5 ragged: {ds}")
         extra["decode_step_96k_ragged"] = ds
 
     if not args.no_training:
@@ -730,7 +730,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         from differentiable_adaptive_block_amd import inputs
-        wl = inputs.CONFIGS["c2"]
+        wl = inputs.CONFIGS["prefill16k"]
         sh = wl.shape
         w = inputs.make_prefill(sh["B"], sh["H"], sh["T"], sh["D"], wl.dtype, wl.causal, wl.planted, wl.seed,
                                 device=dev, with_dout=False)

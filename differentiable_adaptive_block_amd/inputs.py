@@ -52,23 +52,28 @@ def _cfg(name, kind, dtype, alpha, causal, cs_mult, shape, planted, seed, note="
 
 CONFIGS = {
     # tiny non-causal forward + backward, float32
-    "c1": _cfg("c1", "prefill", "fp32", 1.5, False, 1.0, dict(B=1, H=2, T=512, D=64), None, 1001),
+    "tiny512": _cfg("tiny512", "prefill", "fp32", 1.5, False, 1.0, dict(B=1, H=2, T=512, D=64), None,
+                    1001),
     # same inputs with a 16x larger coarse scale, so the masks are exercised
-    "c1s": _cfg("c1s", "prefill", "fp32", 1.5, False, 16.0, dict(B=1, H=2, T=512, D=64), None, 1001),
+    "tiny512_sc16": _cfg("tiny512_sc16", "prefill", "fp32", 1.5, False, 16.0, dict(B=1, H=2, T=512, D=64),
+                         None, 1001),
     # causal prefill at 16K
-    "c2": _cfg("c2", "prefill", "bf16", 1.5, True, 1.0, dict(B=1, H=32, T=16384, D=128), (1, 8), 1002),
+    "prefill16k": _cfg("prefill16k", "prefill", "bf16", 1.5, True, 1.0, dict(B=1, H=32, T=16384, D=128),
+                       (1, 8), 1002),
     # causal prefill at 64K, coarse scale 2/sqrt(128)
-    "c3": _cfg("c3", "prefill", "bf16", 1.5, True, 2.0, dict(B=1, H=32, T=65536, D=128), (1, 8), 1003),
+    "prefill64k": _cfg("prefill64k", "prefill", "bf16", 1.5, True, 2.0, dict(B=1, H=32, T=65536, D=128),
+                       (1, 8), 1003),
     # the same at a coarse scale that gives about 8% selected pairs
-    "c3cal": _cfg("c3cal", "prefill", "bf16", 1.5, True, 7.0, dict(B=1, H=32, T=65536, D=128), (1, 8),
-                  1003, "calibrated coarse scale 7/sqrt(128)"),
+    "prefill64k_sc7": _cfg("prefill64k_sc7", "prefill", "bf16", 1.5, True, 7.0,
+                           dict(B=1, H=32, T=65536, D=128), (1, 8), 1003, "calibrated coarse scale 7/sqrt(128)"),
     # decode: 16 sequences x 32 heads, 98304-token bf16 cache
-    "c4": _cfg("c4", "decode", "bf16", 1.5, True, 1.0, dict(S=16, H=32, N=98304, D=128), (1, 16), 1004),
-    "c4cal": _cfg("c4cal", "decode", "bf16", 1.5, True, 5.0, dict(S=16, H=32, N=98304, D=128), (1, 16),
-                  1004, "calibrated coarse scale 5/sqrt(128)"),
+    "decode96k": _cfg("decode96k", "decode", "bf16", 1.5, True, 1.0, dict(S=16, H=32, N=98304, D=128),
+                      (1, 16), 1004),
+    "decode96k_sc5": _cfg("decode96k_sc5", "decode", "bf16", 1.5, True, 5.0,
+                          dict(S=16, H=32, N=98304, D=128), (1, 16), 1004, "calibrated coarse scale 5/sqrt(128)"),
     # training step (forward + backward), alpha swept over {1.25, 1.5}
-    "c5": _cfg("c5", "prefill", "bf16", (1.25, 1.5), True, 1.0, dict(B=2, H=16, T=16384, D=128), (1, 8),
-               1005),
+    "train16k": _cfg("train16k", "prefill", "bf16", (1.25, 1.5), True, 1.0,
+                     dict(B=2, H=16, T=16384, D=128), (1, 8), 1005),
 }
 
 

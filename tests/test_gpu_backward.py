@@ -41,8 +41,8 @@ def _run(w, alpha, causal, cs):
 
 
 SMALL = [
-    ("c1", 1, 2, 512, 64, "fp32", False, 1.5, 1.0, None),
-    ("c1s", 1, 2, 512, 64, "fp32", False, 1.5, 16.0, None),
+    ("tiny512", 1, 2, 512, 64, "fp32", False, 1.5, 1.0, None),
+    ("tiny512_sc16", 1, 2, 512, 64, "fp32", False, 1.5, 16.0, None),
     ("fp32-causal-a125", 1, 1, 320, 128, "fp32", True, 1.25, 4.0, (1, 3)),
     ("bf16-causal-ragged", 1, 2, 1088, 128, "bf16", True, 1.5, 4.0, (1, 4)),
     ("bf16-causal-dense", 1, 1, 1024, 128, "bf16", True, 1.25, 1.0, (1, 8)),
@@ -79,9 +79,9 @@ def test_backward_deterministic():
 
 @pytest.mark.parametrize("alpha", [1.25, 1.5])
 def test_backward_training_16k_sampled(alpha):
-    wl = inputs.CONFIGS["c5"]
+    wl = inputs.CONFIGS["train16k"]
     sh = wl.shape
-    _say(f"[backward] c5 full size {sh} alpha={alpha} (sampled)")
+    _say(f"[backward] train16k full size {sh} alpha={alpha} (sampled)")
     w = inputs.make_prefill(sh["B"], sh["H"], sh["T"], sh["D"], wl.dtype, True, wl.planted, wl.seed, device=DEV,
                             with_dout=True)
     _, g = _run(w, alpha, True, wl.coarse_scale)

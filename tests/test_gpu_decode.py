@@ -86,7 +86,7 @@ def test_decode_equals_last_prefill_row():
     assert torch.allclose(dec["lse"], pre["lse"][:, :, N - 1], atol=4e-3)
 
 
-@pytest.mark.parametrize("name", ["c4", "c4cal"])
+@pytest.mark.parametrize("name", ["decode96k", "decode96k_sc5"])
 def test_decode_96k_sampled(name):
     from differentiable_adaptive_block_amd import api
     wl = inputs.CONFIGS[name]

@@ -201,7 +201,7 @@ def test_decode_step_sequence():
     _say(f"  ok worst max-abs {worst:.3g}")
 
 
-@pytest.mark.parametrize("name", ["c4cal"])
+@pytest.mark.parametrize("name", ["decode96k_sc5"])
 def test_decode_step_96k_ragged_sampled(name):
     from differentiable_adaptive_block_amd import api
     wl = inputs.CONFIGS[name]

@@ -47,11 +47,11 @@ def _np64(t):
 
 SMALL = [
     # name, B, H, T, D, dtype, causal, alpha, coarse multiple of 1/sqrt(D), planted
-    ("c1", 1, 2, 512, 64, "fp32", False, 1.5, 1.0, None),
-    ("c1s", 1, 2, 512, 64, "fp32", False, 1.5, 16.0, None),
-    ("c1-a1", 1, 2, 512, 64, "fp32", False, 1.0, 1.0, None),
-    ("c1-a125", 1, 2, 512, 64, "fp32", False, 1.25, 16.0, None),
-    ("c1-a2", 1, 2, 512, 64, "fp32", False, 2.0, 16.0, None),
+    ("tiny512", 1, 2, 512, 64, "fp32", False, 1.5, 1.0, None),
+    ("tiny512_sc16", 1, 2, 512, 64, "fp32", False, 1.5, 16.0, None),
+    ("tiny512-a1", 1, 2, 512, 64, "fp32", False, 1.0, 1.0, None),
+    ("tiny512-a125", 1, 2, 512, 64, "fp32", False, 1.25, 16.0, None),
+    ("tiny512-a2", 1, 2, 512, 64, "fp32", False, 2.0, 16.0, None),
     ("fp32-causal", 1, 2, 320, 128, "fp32", True, 1.5, 4.0, (1, 3)),
     ("bf16-causal-ragged", 1, 2, 1088, 128, "bf16", True, 1.5, 4.0, (1, 4)),
     ("bf16-causal-dense", 2, 1, 576, 128, "bf16", True, 1.5, 1.0, (1, 8)),
@@ -122,8 +122,8 @@ def _sampled(name, n_heads=3, n_rows=24, T_sub=None):
 
 
 def test_forward_16k_causal_prefill_sampled():
-    _sampled("c2")
+    _sampled("prefill16k")
 
 
 def test_forward_64k_causal_prefill_sampled():
-    _sampled("c3", n_heads=2, n_rows=12)
+    _sampled("prefill64k", n_heads=2, n_rows=12)

@@ -198,7 +198,7 @@ def test_gqa_decode_one_kv_head_per_query_head_is_dash_decode():
 
 def test_gqa_decode_96k_sampled():
     from differentiable_adaptive_block_amd import api
-    wl = inputs.CONFIGS["c4cal"]
+    wl = inputs.CONFIGS["decode96k_sc5"]
     S, H, Hkv, C, D = 4, 32, 8, wl.shape["N"], wl.shape["D"]
     _say(f"[gqa decode] 96K cache S{S} H{H} Hkv{Hkv}")
     w = inputs.make_decode(S, H, C, D, "bf16", wl.planted, wl.seed, device=DEV, kv_heads=Hkv)

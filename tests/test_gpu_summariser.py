@@ -148,9 +148,9 @@ def test_summariser_training_16k_sampled():
     rows, dK, dV and the summary gradient of the last key blocks (attended only by the last
     rows), against the oracle over those rows; dw needs every row and is checked at small sizes."""
     from differentiable_adaptive_block_amd import api
-    wl = inputs.CONFIGS["c5"]
+    wl = inputs.CONFIGS["train16k"]
     sh = wl.shape
-    _say(f"[summariser] c5 full size {sh} (sampled)")
+    _say(f"[summariser] train16k full size {sh} (sampled)")
     w = inputs.make_prefill(sh["B"], sh["H"], sh["T"], sh["D"], wl.dtype, True, wl.planted, wl.seed, device=DEV,
                             with_dout=True)
     head = _head(sh["H"], sh["D"], 2.0, 59).to(DEV)

@@ -33,5 +33,5 @@ def test_decode_shapes():
 
 
 def test_named_configs_exist():
-    for name in ["c1", "c1s", "c2", "c3", "c3cal", "c4", "c4cal", "c5"]:
+    for name in ["tiny512", "tiny512_sc16", "prefill16k", "prefill64k", "prefill64k_sc7", "decode96k", "decode96k_sc5", "train16k"]:
         assert name in inputs.CONFIGS
