@@ -27,6 +27,52 @@ __global__ __launch_bounds__(64) void pool_kernel(const T* __restrict__ k, T* __
   }
 }
 
+// bf16 keys, D in {64, 128}: the same exact fp64 sums with 16-byte loads.
+// D/8 lanes cover a key row, so one wave load instruction reads 64/(D/8)
+// consecutive rows (1 KB); lane l sums the rows l/(D/8) + (64/(D/8)) x of
+// its 8 columns, then the row groups are added across lanes (xor
+// shuffles).  Every partial sum is exact, so the order does not change the
+// result.  grid (nb, BH), 64 threads.
+template <int D>
+__global__ __launch_bounds__(64) void pool_bf16_kernel(const bf16_t* __restrict__ k, bf16_t* __restrict__ kbar,
+                                                       int T_) {
+  constexpr int CPL = D / 8;            // lanes per key row
+  constexpr int RPI = 64 / CPL;         // rows per load instruction
+  constexpr int NL = DASH_BLOCK / RPI;  // loads per lane
+  const int b = blockIdx.x;
+  const size_t bh = blockIdx.y;
+  const int nb = T_ / DASH_BLOCK;
+  const int l = threadIdx.x;
+  const int c = l % CPL, r0 = l / CPL;
+  const bf16_t* src = k + (bh * T_ + (size_t)b * DASH_BLOCK + r0) * D + 8 * c;
+  uint4 raw[NL];
+#pragma unroll
+  for (int x = 0; x < NL; ++x) raw[x] = *reinterpret_cast<const uint4*>(src + (size_t)RPI * x * D);
+  double acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+#pragma unroll
+  for (int x = 0; x < NL; ++x) {
+    const uint32_t wv[4] = {raw[x].x, raw[x].y, raw[x].z, raw[x].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += (double)__uint_as_float(wv[e] << 16);
+      acc[2 * e + 1] += (double)__uint_as_float(wv[e] & 0xFFFF0000u);
+    }
+  }
+#pragma unroll
+  for (int o = CPL; o < 64; o <<= 1)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
+  if (l < CPL) {
+    uint32_t pk[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      pk[e] = (uint32_t)d2bf(acc[2 * e] * (1.0 / DASH_BLOCK)) | ((uint32_t)d2bf(acc[2 * e + 1] * (1.0 / DASH_BLOCK)) << 16);
+    *reinterpret_cast<uint4*>(kbar + (bh * nb + b) * D + 8 * c) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+  }
+}
+
 __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
 }
@@ -350,7 +396,11 @@ __global__ __launch_bounds__(64) void tile_list_kernel(uint32_t* tile_bits, int*
 
 hipError_t launch_pool(const void* k, void* kbar, int BH, int T_, int D, int dtype, hipStream_t st) {
   dim3 grid(T_ / DASH_BLOCK, BH);
-  if (dtype == 1)
+  if (dtype == 1 && D == 128)
+    pool_bf16_kernel<128><<<grid, 64, 0, st>>>((const bf16_t*)k, (bf16_t*)kbar, T_);
+  else if (dtype == 1 && D == 64)
+    pool_bf16_kernel<64><<<grid, 64, 0, st>>>((const bf16_t*)k, (bf16_t*)kbar, T_);
+  else if (dtype == 1)
     pool_kernel<bf16_t><<<grid, 64, 0, st>>>((const bf16_t*)k, (bf16_t*)kbar, T_, D);
   else
     pool_kernel<float><<<grid, 64, 0, st>>>((const float*)k, (float*)kbar, T_, D);
