@@ -465,7 +465,7 @@ def bench_decode(name, steps, warmup, device):
 
     def step():
         _lib.decode(p, q.data_ptr(), kc.data_ptr(), vc.data_ptr(), kbar.data_ptr(), bufs.o.data_ptr(),
-                    bufs.lse.data_ptr(), bufs.nsel.data_ptr(), bufs.tau.data_ptr(), bufs.ws.data_ptr(),
+                    bufs.lse.data_ptr(), bufs.nsel.data_ptr(), bufs.tau.data_ptr(), None, bufs.ws.data_ptr(),
                     bufs.ws_bytes, st)
 
     for _ in range(warmup):
@@ -525,7 +525,7 @@ def bench_decode_step(name, steps, warmup, device):
     def step():
         _lib.decode_step(p, q.data_ptr(), kn.data_ptr(), vn.data_ptr(), lens.data_ptr(), kc.data_ptr(),
                          vc.data_ptr(), kbar.data_ptr(), bufs.o.data_ptr(), bufs.lse.data_ptr(),
-                         bufs.nsel.data_ptr(), bufs.tau.data_ptr(), bufs.ws.data_ptr(), bufs.ws_bytes, st)
+                         bufs.nsel.data_ptr(), bufs.tau.data_ptr(), None, bufs.ws.data_ptr(), bufs.ws_bytes, st)
         lens.add_(1)
 
     for _ in range(warmup):
@@ -571,10 +571,20 @@ def bench_decode_gqa(steps, warmup, device, kv_heads=8):
     bufs = api.DecodeBuffers(p, q.dtype, q.device)
     st = torch.cuda.current_stream().cuda_stream
 
-    def step():
+    def step(mask=None):
         _lib.decode_gqa(p, kv_heads, q.data_ptr(), kc.data_ptr(), vc.data_ptr(), kbar.data_ptr(), None,
-                        bufs.o.data_ptr(), bufs.lse.data_ptr(), bufs.nsel.data_ptr(), bufs.tau.data_ptr(),
+                        bufs.o.data_ptr(), bufs.lse.data_ptr(), bufs.nsel.data_ptr(), bufs.tau.data_ptr(), mask,
                         bufs.ws.data_ptr(), bufs.ws_bytes, st)
+
+    # one call with the selection masks on: the group walks the OR of its heads' masks plus its own block
+    step(bufs.mask.data_ptr())
+    torch.cuda.synchronize()
+    G = H // kv_heads
+    words = bufs.mask.view(S, kv_heads, G, -1)
+    union = words[:, :, 0]
+    for g in range(1, G):
+        union = union | words[:, :, g]
+    groups = _popcount32(union).sum(-1).to(torch.float64).flatten() + 1.0  # union + own block, per group
 
     for _ in range(warmup):
         step()
@@ -586,10 +596,6 @@ def bench_decode_gqa(steps, warmup, device, kv_heads=8):
         e[1].record()
     torch.cuda.synchronize()
     us = sum(e[0].elapsed_time(e[1]) for e in evs) / steps * 1e3
-    G = H // kv_heads
-    # the group's list length (union + own block) is what the walk reads; the decode leaves it in its workspace
-    sel_cnt = _decode_list_counts(p, bufs)
-    groups = sel_cnt.view(S * kv_heads, G)[:, 0].to(torch.float64)  # union + own block, per group
     sel_bytes = float(groups.sum()) * 64 * D * 2 * 2
     res = dict(S=S, H=H, kv_heads=kv_heads, N=C, D=D, coarse_scale=wl.coarse_scale, us_per_step=us,
                mean_union_blocks=float(groups.mean()) - 1.0,
@@ -601,17 +607,6 @@ def bench_decode_gqa(steps, warmup, device, kv_heads=8):
     del w, q, kc, vc, kbar, bufs
     torch.cuda.empty_cache()
     return res
-
-
-def _decode_list_counts(p, bufs):
-    """The per-row list lengths the decode left in its workspace: the third region of
-    dash_decode's workspace (after the [S*H, N/64] scores and the [S*H, 2] row statistics,
-    each rounded up to 256 bytes), int32 [S*H]."""
-    SH = p.S * p.H
-    nb = p.N // 64
-    o0 = (SH * nb * 4 + 255) // 256 * 256
-    o1 = o0 + (SH * 2 * 4 + 255) // 256 * 256
-    return bufs.ws[o1:o1 + SH * 4].view(torch.int32).clone()
 
 
 def traffic_probe(device):

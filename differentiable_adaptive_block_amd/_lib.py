@@ -129,18 +129,18 @@ def load() -> ctypes.CDLL:
     L.dash_decode_workspace_bytes.restype = ctypes.c_size_t
     L.dash_decode_workspace_bytes.argtypes = [P(DashDecodeParams)]
     L.dash_decode.restype = ctypes.c_int
-    L.dash_decode.argtypes = [P(DashDecodeParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.dash_decode.argtypes = [P(DashDecodeParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.dash_cache_append.restype = ctypes.c_int
     L.dash_cache_append.argtypes = [P(DashDecodeParams), vp, vp, vp, vp, vp, vp, vp]
     L.dash_decode_varlen.restype = ctypes.c_int
-    L.dash_decode_varlen.argtypes = [P(DashDecodeParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
-                                     vp]
+    L.dash_decode_varlen.argtypes = [P(DashDecodeParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                     ctypes.c_size_t, vp]
     L.dash_decode_step.restype = ctypes.c_int
-    L.dash_decode_step.argtypes = [P(DashDecodeParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+    L.dash_decode_step.argtypes = [P(DashDecodeParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                    ctypes.c_size_t, vp]
     L.dash_decode_gqa.restype = ctypes.c_int
     L.dash_decode_gqa.argtypes = [P(DashDecodeParams), ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                  ctypes.c_size_t, vp]
+                                  vp, ctypes.c_size_t, vp]
     L.dash_last_error.restype = ctypes.c_char_p
     L.dash_last_error.argtypes = []
     _lib = L
@@ -231,26 +231,27 @@ def pool_attn_bwd(p: DashParams, k, w, dkbar, dk, dw, ws, ws_bytes, stream) -> N
     check(load().dash_pool_attn_bwd(ctypes.byref(p), k, w, dkbar, dk, dw, ws, ws_bytes, stream))
 
 
-def decode(p: DashDecodeParams, q, kc, vc, kbar, o, lse, nsel, tau, ws, ws_bytes, stream) -> None:
-    check(load().dash_decode(ctypes.byref(p), q, kc, vc, kbar, o, lse, nsel, tau, ws, ws_bytes, stream))
+def decode(p: DashDecodeParams, q, kc, vc, kbar, o, lse, nsel, tau, mask, ws, ws_bytes, stream) -> None:
+    check(load().dash_decode(ctypes.byref(p), q, kc, vc, kbar, o, lse, nsel, tau, mask, ws, ws_bytes, stream))
 
 
 def cache_append(p: DashDecodeParams, k_new, v_new, lens, kc, vc, kbar, stream) -> None:
     check(load().dash_cache_append(ctypes.byref(p), k_new, v_new, lens, kc, vc, kbar, stream))
 
 
-def decode_varlen(p: DashDecodeParams, q, kc, vc, kbar, lens, o, lse, nsel, tau, ws, ws_bytes, stream) -> None:
-    check(load().dash_decode_varlen(ctypes.byref(p), q, kc, vc, kbar, lens, o, lse, nsel, tau, ws, ws_bytes,
+def decode_varlen(p: DashDecodeParams, q, kc, vc, kbar, lens, o, lse, nsel, tau, mask, ws, ws_bytes,
+                  stream) -> None:
+    check(load().dash_decode_varlen(ctypes.byref(p), q, kc, vc, kbar, lens, o, lse, nsel, tau, mask, ws, ws_bytes,
                                     stream))
 
 
-def decode_step(p: DashDecodeParams, q, k_new, v_new, lens, kc, vc, kbar, o, lse, nsel, tau, ws, ws_bytes,
-                stream) -> None:
-    check(load().dash_decode_step(ctypes.byref(p), q, k_new, v_new, lens, kc, vc, kbar, o, lse, nsel, tau, ws,
-                                  ws_bytes, stream))
+def decode_step(p: DashDecodeParams, q, k_new, v_new, lens, kc, vc, kbar, o, lse, nsel, tau, mask, ws,
+                ws_bytes, stream) -> None:
+    check(load().dash_decode_step(ctypes.byref(p), q, k_new, v_new, lens, kc, vc, kbar, o, lse, nsel, tau, mask,
+                                  ws, ws_bytes, stream))
 
 
-def decode_gqa(p: DashDecodeParams, kv_heads: int, q, kc, vc, kbar, lens, o, lse, nsel, tau, ws, ws_bytes,
-               stream) -> None:
-    check(load().dash_decode_gqa(ctypes.byref(p), kv_heads, q, kc, vc, kbar, lens, o, lse, nsel, tau, ws, ws_bytes,
-                                 stream))
+def decode_gqa(p: DashDecodeParams, kv_heads: int, q, kc, vc, kbar, lens, o, lse, nsel, tau, mask, ws,
+               ws_bytes, stream) -> None:
+    check(load().dash_decode_gqa(ctypes.byref(p), kv_heads, q, kc, vc, kbar, lens, o, lse, nsel, tau, mask, ws,
+                                 ws_bytes, stream))

@@ -203,6 +203,8 @@ class DecodeBuffers:
         self.lse = torch.empty((p.S, p.H), dtype=torch.float32, device=device)
         self.nsel = torch.empty((p.S, p.H), dtype=torch.int32, device=device)
         self.tau = torch.empty((p.S, p.H), dtype=torch.float32, device=device)
+        # selected candidate blocks of each row as 32-bit words (int32 storage)
+        self.mask = torch.empty((p.S, p.H, (p.N // BLOCK + 31) // 32), dtype=torch.int32, device=device)
         self.ws_bytes = _lib.decode_workspace_bytes(p)
         self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=device)
 
@@ -217,8 +219,8 @@ def decode(q, kc, vc, kbar, alpha=1.5, fine_scale=None, coarse_scale=None, bufs:
     if bufs is None:
         bufs = DecodeBuffers(p, q.dtype, q.device)
     _lib.decode(p, _ptr(q), _ptr(kc), _ptr(vc), _ptr(kbar), _ptr(bufs.o), _ptr(bufs.lse), _ptr(bufs.nsel),
-                _ptr(bufs.tau), _ptr(bufs.ws), bufs.ws_bytes, _stream(q.device))
-    return dict(o=bufs.o, lse=bufs.lse, nsel=bufs.nsel, tau=bufs.tau)
+                _ptr(bufs.tau), _ptr(bufs.mask), _ptr(bufs.ws), bufs.ws_bytes, _stream(q.device))
+    return dict(o=bufs.o, lse=bufs.lse, nsel=bufs.nsel, tau=bufs.tau, mask=bufs.mask)
 
 
 def _require_lens(lens, S, device):
@@ -252,8 +254,8 @@ def decode_varlen(q, kc, vc, kbar, lens, alpha=1.5, fine_scale=None, coarse_scal
     if bufs is None:
         bufs = DecodeBuffers(p, q.dtype, q.device)
     _lib.decode_varlen(p, _ptr(q), _ptr(kc), _ptr(vc), _ptr(kbar), _ptr(lens), _ptr(bufs.o), _ptr(bufs.lse),
-                       _ptr(bufs.nsel), _ptr(bufs.tau), _ptr(bufs.ws), bufs.ws_bytes, _stream(q.device))
-    return dict(o=bufs.o, lse=bufs.lse, nsel=bufs.nsel, tau=bufs.tau)
+                       _ptr(bufs.nsel), _ptr(bufs.tau), _ptr(bufs.mask), _ptr(bufs.ws), bufs.ws_bytes, _stream(q.device))
+    return dict(o=bufs.o, lse=bufs.lse, nsel=bufs.nsel, tau=bufs.tau, mask=bufs.mask)
 
 
 def decode_step(q, k_new, v_new, kc, vc, kbar, lens, alpha=1.5, fine_scale=None, coarse_scale=None,
@@ -270,9 +272,9 @@ def decode_step(q, k_new, v_new, kc, vc, kbar, lens, alpha=1.5, fine_scale=None,
     if bufs is None:
         bufs = DecodeBuffers(p, q.dtype, q.device)
     _lib.decode_step(p, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(lens), _ptr(kc), _ptr(vc), _ptr(kbar),
-                     _ptr(bufs.o), _ptr(bufs.lse), _ptr(bufs.nsel), _ptr(bufs.tau), _ptr(bufs.ws), bufs.ws_bytes,
-                     _stream(q.device))
-    return dict(o=bufs.o, lse=bufs.lse, nsel=bufs.nsel, tau=bufs.tau)
+                     _ptr(bufs.o), _ptr(bufs.lse), _ptr(bufs.nsel), _ptr(bufs.tau), _ptr(bufs.mask), _ptr(bufs.ws),
+                     bufs.ws_bytes, _stream(q.device))
+    return dict(o=bufs.o, lse=bufs.lse, nsel=bufs.nsel, tau=bufs.tau, mask=bufs.mask)
 
 
 def decode_gqa(q, kc, vc, kbar, lens=None, alpha=1.5, fine_scale=None, coarse_scale=None,
@@ -291,9 +293,9 @@ def decode_gqa(q, kc, vc, kbar, lens=None, alpha=1.5, fine_scale=None, coarse_sc
     if bufs is None:
         bufs = DecodeBuffers(p, q.dtype, q.device)
     _lib.decode_gqa(p, Hkv, _ptr(q), _ptr(kc), _ptr(vc), _ptr(kbar), None if lens is None else _ptr(lens),
-                    _ptr(bufs.o), _ptr(bufs.lse), _ptr(bufs.nsel), _ptr(bufs.tau), _ptr(bufs.ws), bufs.ws_bytes,
-                    _stream(q.device))
-    return dict(o=bufs.o, lse=bufs.lse, nsel=bufs.nsel, tau=bufs.tau)
+                    _ptr(bufs.o), _ptr(bufs.lse), _ptr(bufs.nsel), _ptr(bufs.tau), _ptr(bufs.mask), _ptr(bufs.ws),
+                    bufs.ws_bytes, _stream(q.device))
+    return dict(o=bufs.o, lse=bufs.lse, nsel=bufs.nsel, tau=bufs.tau, mask=bufs.mask)
 
 
 class DashAttentionFn(torch.autograd.Function):

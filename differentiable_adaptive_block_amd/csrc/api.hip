@@ -554,11 +554,12 @@ static dash_status check_decode_params(const dash_decode_params* p) {
 // dash_decode_step: rows hold len[s] + len_add tokens, or N when len is null.
 static dash_status decode_common(const dash_decode_params* p, const void* q, const void* kc, const void* vc,
                                  const void* kbar, const int32_t* len, int len_add, void* o, float* lse,
-                                 int32_t* nsel, float* tau, void* workspace, size_t workspace_bytes,
-                                 void* stream, int grp = 1) {
+                                 int32_t* nsel, float* tau, uint32_t* mask, void* workspace,
+                                 size_t workspace_bytes, void* stream, int grp = 1) {
   if (!ok_ptr(q) || !ok_ptr(kc) || !ok_ptr(vc) || !ok_ptr(kbar) || !ok_ptr(o))
     return fail(DASH_EINVAL, "q, kc, vc, kbar and o must be non-null and 16-byte aligned");
-  if (!ok_opt(lse) || !ok_opt(nsel) || !ok_opt(tau)) return fail(DASH_EINVAL, "lse/nsel/tau must be 16-byte aligned");
+  if (!ok_opt(lse) || !ok_opt(nsel) || !ok_opt(tau) || !ok_opt(mask))
+    return fail(DASH_EINVAL, "lse/nsel/tau/mask must be 16-byte aligned");
   size_t off[6];
   int nsplit = 0, chunk = 0;
   const size_t need = decode_ws_layout(p, off, &nsplit, &chunk);
@@ -574,6 +575,7 @@ static dash_status decode_common(const dash_decode_params* p, const void* q, con
   da.lse = lse;
   da.nsel = nsel;
   da.tau_out = tau;
+  da.mask = mask;
   da.zrow = reinterpret_cast<float*>(ws + off[0]);
   da.rowstat = reinterpret_cast<float*>(ws + off[1]);
   da.sel_cnt = reinterpret_cast<int*>(ws + off[2]);
@@ -616,16 +618,17 @@ static dash_status append_common(const dash_decode_params* p, const void* k_new,
 }
 
 dash_status dash_decode(const dash_decode_params* p, const void* q, const void* kc, const void* vc,
-                        const void* kbar, void* o, float* lse, int32_t* nsel, float* tau, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        const void* kbar, void* o, float* lse, int32_t* nsel, float* tau, uint32_t* mask,
+                        void* workspace, size_t workspace_bytes, void* stream) {
   dash_status s = check_decode_params(p);
   if (s != DASH_OK) return s;
-  return decode_common(p, q, kc, vc, kbar, nullptr, 0, o, lse, nsel, tau, workspace, workspace_bytes, stream);
+  return decode_common(p, q, kc, vc, kbar, nullptr, 0, o, lse, nsel, tau, mask, workspace, workspace_bytes, stream);
 }
 
 dash_status dash_decode_gqa(const dash_decode_params* p, int32_t kv_heads, const void* q, const void* kc,
                             const void* vc, const void* kbar, const int32_t* len, void* o, float* lse,
-                            int32_t* nsel, float* tau, void* workspace, size_t workspace_bytes, void* stream) {
+                            int32_t* nsel, float* tau, uint32_t* mask, void* workspace, size_t workspace_bytes,
+                            void* stream) {
   dash_status s = check_decode_params(p);
   if (s != DASH_OK) return s;
   if (kv_heads < 1 || p->H % kv_heads) return fail(DASH_EINVAL, "kv_heads (%d) must divide H (%d)", kv_heads, p->H);
@@ -633,7 +636,7 @@ dash_status dash_decode_gqa(const dash_decode_params* p, int32_t kv_heads, const
   if (grp != 1 && grp != 2 && grp != 4 && grp != 8)
     return fail(DASH_EUNSUPPORTED, "1, 2, 4 or 8 query heads per KV head are built (got %d)", grp);
   if (len && reinterpret_cast<uintptr_t>(len) % 4) return fail(DASH_EINVAL, "len must be 4-byte aligned");
-  return decode_common(p, q, kc, vc, kbar, len, 0, o, lse, nsel, tau, workspace, workspace_bytes, stream, grp);
+  return decode_common(p, q, kc, vc, kbar, len, 0, o, lse, nsel, tau, mask, workspace, workspace_bytes, stream, grp);
 }
 
 dash_status dash_cache_append(const dash_decode_params* p, const void* k_new, const void* v_new,
@@ -645,21 +648,23 @@ dash_status dash_cache_append(const dash_decode_params* p, const void* k_new, co
 
 dash_status dash_decode_varlen(const dash_decode_params* p, const void* q, const void* kc, const void* vc,
                                const void* kbar, const int32_t* len, void* o, float* lse, int32_t* nsel,
-                               float* tau, void* workspace, size_t workspace_bytes, void* stream) {
+                               float* tau, uint32_t* mask, void* workspace, size_t workspace_bytes, void* stream) {
   dash_status s = check_decode_params(p);
   if (s != DASH_OK) return s;
   if (!len || reinterpret_cast<uintptr_t>(len) % 4) return fail(DASH_EINVAL, "len must be non-null and 4-byte aligned");
-  return decode_common(p, q, kc, vc, kbar, len, 0, o, lse, nsel, tau, workspace, workspace_bytes, stream);
+  return decode_common(p, q, kc, vc, kbar, len, 0, o, lse, nsel, tau, mask, workspace, workspace_bytes, stream);
 }
 
 dash_status dash_decode_step(const dash_decode_params* p, const void* q, const void* k_new, const void* v_new,
                              const int32_t* len, void* kc, void* vc, void* kbar, void* o, float* lse,
-                             int32_t* nsel, float* tau, void* workspace, size_t workspace_bytes, void* stream) {
+                             int32_t* nsel, float* tau, uint32_t* mask, void* workspace, size_t workspace_bytes,
+                             void* stream) {
   dash_status s = check_decode_params(p);
   if (s != DASH_OK) return s;
   // validate both halves before launching either
   if (!ok_ptr(q) || !ok_ptr(o)) return fail(DASH_EINVAL, "q and o must be non-null and 16-byte aligned");
-  if (!ok_opt(lse) || !ok_opt(nsel) || !ok_opt(tau)) return fail(DASH_EINVAL, "lse/nsel/tau must be 16-byte aligned");
+  if (!ok_opt(lse) || !ok_opt(nsel) || !ok_opt(tau) || !ok_opt(mask))
+    return fail(DASH_EINVAL, "lse/nsel/tau/mask must be 16-byte aligned");
   size_t off[6];
   if (workspace_bytes < decode_ws_layout(p, off, nullptr, nullptr))
     return fail(DASH_EWORKSPACE, "workspace of %zu bytes needed, %zu given", decode_ws_layout(p, off, nullptr, nullptr),
@@ -668,7 +673,7 @@ dash_status dash_decode_step(const dash_decode_params* p, const void* q, const v
   if ((s = append_common(p, k_new, v_new, len, kc, vc, kbar, stream)) != DASH_OK) return s;
   // rows whose length was out of range for the append (len < 0 or >= N)
   // are out of range here too (len + 1 < 1 or > N): NaN outputs
-  return decode_common(p, q, kc, vc, kbar, len, 1, o, lse, nsel, tau, workspace, workspace_bytes, stream);
+  return decode_common(p, q, kc, vc, kbar, len, 1, o, lse, nsel, tau, mask, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -23,7 +23,8 @@
 //   bwd_dkdv      key-block-major over the query tiles whose list holds the
 //                 block; MFMA for S, dP, dV^T and dK^T; also dkbar and the
 //                 pooling term
-// fp32 path: one wave per query row, dK / dV / dkbar by float atomics.
+// fp32 path: a row pass (dQ, G, dz), an ordered dkbar reduction and a
+// key-block pass (dK, dV); no atomics either.
 #include "kernels.h"
 #include "attn_bwd.h"
 #include "entmax.h"
@@ -762,12 +763,25 @@ __global__ __launch_bounds__(256) void bwd_coarse_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------- fp32 path
+//
+// Three kernels, each output written by one thread in a fixed order (no
+// atomics, so reruns give the same bits):
+//   bwd_rows_generic   one wave per query row: delta, the row's Stage-2
+//                      gradient terms, G per candidate block, the entmax JVP
+//                      dz and dQ (fine + coarse); stores delta, the log prior
+//                      lp[row][b] of every candidate (-inf when not selected)
+//                      and coarse_scale * dz[row][b] in the workspace
+//   bwd_dkbar_generic  dkbar_b = sum over rows, ascending, of
+//                      coarse_scale dz[row][b] q_row
+//   bwd_keys_generic   one wave per key block, lane = key: walks the rows
+//                      that attend the block (its own rows when causal, then
+//                      the rows whose lp is finite) in ascending order and
+//                      accumulates dK, dV; adds the pooling term.
+// Scores use dot_row, the generic forward's arithmetic, so both passes see
+// the forward's logits bit for bit.
 
-// One wave per query row; dK, dV and dkbar accumulate with float atomics
-// (zeroed first), dQ is owned by the row.  Blocks in ascending order, the
-// prior from the same dot_row score as the generic forward.
 template <typename T>
-__global__ __launch_bounds__(64) void bwd_generic_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64) void bwd_rows_generic_kernel(BwdArgs a) {
   __shared__ float qs[128], gs[128], dsv[64];
   __shared__ float gb[DASH_MAX_NB], lpb[DASH_MAX_NB];
   const int D = a.D;
@@ -781,9 +795,8 @@ __global__ __launch_bounds__(64) void bwd_generic_kernel(BwdArgs a) {
   const T* K = reinterpret_cast<const T*>(a.k) + bh * a.T * D;
   const T* V = reinterpret_cast<const T*>(a.v) + bh * a.T * D;
   const T* KB = reinterpret_cast<const T*>(a.kbar) + bh * nb * D;
-  float* dK = reinterpret_cast<float*>(a.dk) + bh * a.T * D;
-  float* dV = reinterpret_cast<float*>(a.dv) + bh * a.T * D;
-  float* dKB = a.dkbar + bh * nb * D;
+  float* lp_row = a.pbuf + (bh * a.T + i) * (size_t)nb;
+  float* dz_row = a.gbuf + (bh * a.T + i) * (size_t)nb;
   float dl = 0.f;
   for (int d = l; d < D; d += 64) {
     qs[d] = to_f<T>(q[d]);
@@ -791,6 +804,7 @@ __global__ __launch_bounds__(64) void bwd_generic_kernel(BwdArgs a) {
     dl = fmaf(to_f<T>(o[d]), gs[d], dl);
   }
   dl = wave_sum(dl);
+  if (l == 0) a.delta[bh * a.T + i] = dl;
   __syncthreads();
   const CoarseArith ca = a.ca;
   const float tau_i = a.tau[bh * a.T + i], ln_i = a.lognorm[bh * a.T + i];
@@ -798,6 +812,8 @@ __global__ __launch_bounds__(64) void bwd_generic_kernel(BwdArgs a) {
   const int own = i / DASH_BLOCK;
   const int last = a.causal ? own : nb - 1;
   const int nc = a.causal ? own : nb;
+  for (int b = l; b < nb; b += 64) lp_row[b] = -INFINITY;  // overwritten below for candidates
+  __syncthreads();
   float dq0 = 0.f, dq1 = 0.f;
   for (int b = 0; b <= last; ++b) {
     float pr;
@@ -805,7 +821,7 @@ __global__ __launch_bounds__(64) void bwd_generic_kernel(BwdArgs a) {
     if (!cand) pr = 0.f;
     else {
       pr = ca.logp(ca.u_of(dot_row<T>(qs, KB + (size_t)b * D, D)), tau_i, ln_i);
-      if (l == 0) { lpb[b] = pr; gb[b] = 0.f; }
+      if (l == 0) { lpb[b] = pr; gb[b] = 0.f; lp_row[b] = pr; }
       if (pr == -INFINITY) continue;
     }
     const int key = b * DASH_BLOCK + l;
@@ -823,10 +839,6 @@ __global__ __launch_bounds__(64) void bwd_generic_kernel(BwdArgs a) {
       dq0 = fmaf(dsv[kk], to_f<T>(kr[l]), dq0);
       if (l + 64 < D) dq1 = fmaf(dsv[kk], to_f<T>(kr[l + 64]), dq1);
     }
-    for (int d = 0; d < D; ++d) {
-      atomicAdd(&dK[(size_t)key * D + d], a.fine_scale * ds * qs[d]);
-      atomicAdd(&dV[(size_t)key * D + d], p * gs[d]);
-    }
     __syncthreads();
   }
   dq0 *= a.fine_scale;
@@ -836,43 +848,99 @@ __global__ __launch_bounds__(64) void bwd_generic_kernel(BwdArgs a) {
   const float am2 = ca.softmax ? 1.f : 1.f - ca.am1;  // 2 - alpha
   float ss = 0.f, ssg = 0.f;
   for (int b = l; b < nc; b += 64) {
-    const float lp = lpb[b];
-    if (lp == -INFINITY) continue;
-    ss += expf(am2 * lp);
-    ssg += gb[b] * expf((am2 - 1.f) * lp);
+    const float lpv = lpb[b];
+    if (lpv == -INFINITY) continue;
+    ss += expf(am2 * lpv);
+    ssg += gb[b] * expf((am2 - 1.f) * lpv);
   }
   ss = wave_sum(ss);
   ssg = wave_sum(ssg);
   const float ratio = ss > 0.f ? ssg / ss : 0.f;
+  for (int b = l; b < nb; b += 64) dz_row[b] = 0.f;
+  __syncthreads();
   for (int b = 0; b < nc; ++b) {
-    const float lp = lpb[b];
-    if (lp == -INFINITY) continue;
-    const float dz = (gb[b] * expf((am2 - 1.f) * lp) - expf(am2 * lp) * ratio) * ca.coarse_scale;
+    const float lpv = lpb[b];
+    if (lpv == -INFINITY) continue;
+    const float dz = (gb[b] * expf((am2 - 1.f) * lpv) - expf(am2 * lpv) * ratio) * ca.coarse_scale;
     const T* kb = KB + (size_t)b * D;
     dq0 = fmaf(dz, to_f<T>(kb[l]), dq0);
     if (l + 64 < D) dq1 = fmaf(dz, to_f<T>(kb[l + 64]), dq1);
-    atomicAdd(&dKB[(size_t)b * D + l], dz * qs[l]);
-    if (l + 64 < D) atomicAdd(&dKB[(size_t)b * D + l + 64], dz * qs[l + 64]);
+    if (l == 0) dz_row[b] = dz;
   }
   float* dQ = reinterpret_cast<float*>(a.dq) + (bh * a.T + i) * D;
   dQ[l] = dq0;
   if (l + 64 < D) dQ[l + 64] = dq1;
 }
 
-// dk += dkbar / 64 on every key of the block (fp32 path)
-__global__ void bwd_pool_grad_kernel(float* dk, const float* dkbar, int T_, int D, size_t n) {
-  for (size_t x = (size_t)blockIdx.x * blockDim.x + threadIdx.x; x < n; x += (size_t)gridDim.x * blockDim.x) {
-    const size_t d = x % D;
-    const size_t row = x / D;  // bh * T + t
-    const size_t bh = row / T_;
-    const size_t t = row % T_;
-    const int nb = T_ / DASH_BLOCK;
-    dk[x] += dkbar[(bh * nb + t / DASH_BLOCK) * D + d] * (1.f / DASH_BLOCK);
+// dkbar[b][d] = sum over rows r ascending of dz[r][b] q_r[d] (dz carries the
+// coarse scale).  grid (nb, BH), 64 threads over d.
+template <typename T>
+__global__ __launch_bounds__(64) void bwd_dkbar_generic_kernel(BwdArgs a) {
+  const int D = a.D;
+  const int nb = a.T / DASH_BLOCK;
+  const int b = blockIdx.x;
+  const size_t bh = blockIdx.y;
+  const int l = lane_id();
+  const T* Q = reinterpret_cast<const T*>(a.q) + bh * a.T * D;
+  const float* dz = a.gbuf + bh * a.T * (size_t)nb + b;
+  float acc0 = 0.f, acc1 = 0.f;
+  for (int r = a.causal ? (b + 1) * DASH_BLOCK : 0; r < a.T; ++r) {
+    const float z = dz[(size_t)r * nb];
+    if (z == 0.f) continue;
+    acc0 = fmaf(z, to_f<T>(Q[(size_t)r * D + l]), acc0);
+    if (l + 64 < D) acc1 = fmaf(z, to_f<T>(Q[(size_t)r * D + l + 64]), acc1);
   }
+  float* out = a.dkbar + (bh * nb + b) * D;
+  out[l] = acc0;
+  if (l + 64 < D) out[l + 64] = acc1;
 }
 
-__global__ void zero_f32_kernel(float* p, size_t n) {
-  for (size_t x = (size_t)blockIdx.x * blockDim.x + threadIdx.x; x < n; x += (size_t)gridDim.x * blockDim.x) p[x] = 0.f;
+// dK, dV of one key block, lane = key.  DM: the head dim (64 or 128).
+template <typename T, int DM>
+__global__ __launch_bounds__(64) void bwd_keys_generic_kernel(BwdArgs a) {
+  __shared__ float qs[DM], gs[DM];
+  const int nb = a.T / DASH_BLOCK;
+  const int b = blockIdx.x;
+  const size_t bh = blockIdx.y;
+  const int l = lane_id();
+  const int key = b * DASH_BLOCK + l;
+  const T* Q = reinterpret_cast<const T*>(a.q) + bh * a.T * DM;
+  const T* dO = reinterpret_cast<const T*>(a.dout) + bh * a.T * DM;
+  const T* kr = reinterpret_cast<const T*>(a.k) + (bh * a.T + key) * DM;
+  const T* vr = reinterpret_cast<const T*>(a.v) + (bh * a.T + key) * DM;
+  const float* lp = a.pbuf + bh * a.T * (size_t)nb + b;
+  float dk[DM], dv[DM];
+#pragma unroll
+  for (int d = 0; d < DM; ++d) { dk[d] = 0.f; dv[d] = 0.f; }
+  for (int r = a.causal ? b * DASH_BLOCK : 0; r < a.T; ++r) {
+    const bool diag = a.causal && r / DASH_BLOCK == b;
+    const float pr = diag ? 0.f : lp[(size_t)r * nb];  // the same for every lane
+    if (pr == -INFINITY) continue;
+    __syncthreads();  // the previous row's operands are no longer read
+    for (int d = l; d < DM; d += 64) {
+      qs[d] = to_f<T>(Q[(size_t)r * DM + d]);
+      gs[d] = to_f<T>(dO[(size_t)r * DM + d]);
+    }
+    __syncthreads();
+    float s = dot_row<T>(qs, kr, DM) * a.fine_scale + pr;
+    if (diag && key > r) s = -INFINITY;
+    const float p = expf(s - a.lse[bh * a.T + r]);
+    const float dp = dot_row<T>(gs, vr, DM);
+    const float ds = p * (dp - a.delta[bh * a.T + r]);
+#pragma unroll
+    for (int d = 0; d < DM; ++d) {
+      dk[d] = fmaf(ds, qs[d], dk[d]);
+      dv[d] = fmaf(p, gs[d], dv[d]);
+    }
+  }
+  const float* kbg = a.dkbar + (bh * nb + b) * DM;
+  float* dK = reinterpret_cast<float*>(a.dk) + (bh * a.T + key) * DM;
+  float* dV = reinterpret_cast<float*>(a.dv) + (bh * a.T + key) * DM;
+#pragma unroll
+  for (int d = 0; d < DM; ++d) {
+    dK[d] = dk[d] * a.fine_scale + a.pool_scale * kbg[d];
+    dV[d] = dv[d];
+  }
 }
 
 // Grouped-query heads: G of the group's heads summed per (tile, listed
@@ -982,14 +1050,11 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t st) {
     else bwd_dkdv_kernel<64><<<ngrp * a.BH, 512, 0, st>>>(a);
     return hipGetLastError();
   }
-  const size_t n = rows * a.D;
-  zero_f32_kernel<<<2048, 256, 0, st>>>(reinterpret_cast<float*>(a.dk), n);
-  zero_f32_kernel<<<2048, 256, 0, st>>>(reinterpret_cast<float*>(a.dv), n);
-  zero_f32_kernel<<<256, 256, 0, st>>>(a.dkbar, (size_t)a.BH * nb * a.D);
+  bwd_rows_generic_kernel<float><<<dim3(a.T, a.BH), 64, 0, st>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  bwd_generic_kernel<float><<<dim3(a.T, a.BH), 64, 0, st>>>(a);
+  bwd_dkbar_generic_kernel<float><<<dim3(nb, a.BH), 64, 0, st>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (a.pool_scale != 0.f)
-    bwd_pool_grad_kernel<<<2048, 256, 0, st>>>(reinterpret_cast<float*>(a.dk), a.dkbar, a.T, a.D, n);
+  if (a.D == 128) bwd_keys_generic_kernel<float, 128><<<dim3(nb, a.BH), 64, 0, st>>>(a);
+  else bwd_keys_generic_kernel<float, 64><<<dim3(nb, a.BH), 64, 0, st>>>(a);
   return hipGetLastError();
 }

@@ -15,6 +15,7 @@ struct DecodeArgs {
   float* lse;        // [SH] or null
   int* nsel;         // [SH] or null
   float* tau_out;    // [SH] or null
+  uint32_t* mask;    // [SH, ceil(N / 64 / 32)] or null: bit b set iff candidate block b is selected
   // workspace
   float* zrow;       // [SH, N / 64]   coarse u scores
   float* rowstat;    // [SH, 2]        tau, lognorm

@@ -58,12 +58,15 @@ __global__ __launch_bounds__(512) void decode_select_kernel(DecodeArgs a) {
   const int nbc = a.N / DASH_BLOCK;  // capacity in blocks: row stride of the summaries and the lists
   const int n = decode_row_len(a, row);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  if (n < 1 || n > a.N) {  // length out of range: empty list; the combine writes NaN
+  const int nbw = (nbc + 31) / 32;   // mask words per row
+  if (n < 1 || n > a.N) {  // length out of range: empty list and mask; the combine writes NaN
     if (tid == 0) {
       a.sel_cnt[row] = 0;
       if (a.nsel) a.nsel[row] = -1;
       if (a.tau_out) a.tau_out[row] = __uint_as_float(0x7fc00000u);
     }
+    if (a.mask)
+      for (int x = tid; x < nbw; x += 64 * NW) a.mask[(size_t)row * nbw + x] = 0u;
     return;
   }
   const int own = (n - 1) / DASH_BLOCK;  // the query's block
@@ -117,6 +120,17 @@ __global__ __launch_bounds__(512) void decode_select_kernel(DecodeArgs a) {
   EntmaxOut e;
   if (nc > 0) e = entmax_solve<NPL, 64>(u, nc, ca);
   else { e.tau = __uint_as_float(0x7fc00000u); e.lognorm = 0.f; e.nsel = 0; }
+  if (a.mask) {
+    // the row's selected candidates as bits: word 2k + x from ballot k
+    uint32_t* mw = a.mask + (size_t)row * nbw;
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) {
+      const int idx = l + 64 * k;
+      const unsigned long long bal = __ballot(idx < nc && ca.selected(u[k], e.tau));
+      if (l == 0 && 2 * k < nbw) mw[2 * k] = (uint32_t)bal;
+      if (l == 0 && 2 * k + 1 < nbw) mw[2 * k + 1] = (uint32_t)(bal >> 32);
+    }
+  }
   if (a.grp > 1) {
     // grouped heads: this head's p over the candidates, for the group's merge
     float* pr = a.zrow + (size_t)row * nbc;

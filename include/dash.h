@@ -257,11 +257,15 @@ size_t dash_decode_workspace_bytes(const dash_decode_params* p);
  * kbar [S,H,N/64,D] the summaries of the cache (dash_pool).  Candidates are
  * blocks 0..N/64-2; block N/64-1 is attended whole with prior 0.
  * Outputs o [S,H,D] (dtype), lse [S,H] (f32, may be NULL), nsel [S,H] (i32,
- * may be NULL), tau [S,H] (f32, may be NULL).
+ * may be NULL), tau [S,H] (f32, may be NULL) and mask [S,H,nbw] (u32, may be
+ * NULL; nbw = ceil(N/64/32)): the Stage-1 output of the row, its sparse
+ * block weights' support ("Core Mechanism" of the alanhou.org page), bit
+ * b % 32 of word b / 32 set iff candidate block b has p > 0; bits of the
+ * query's own block and of later blocks are 0.
  */
 dash_status dash_decode(const dash_decode_params* p, const void* q, const void* kc,
                         const void* vc, const void* kbar, void* o, float* lse,
-                        int32_t* nsel, float* tau, void* workspace,
+                        int32_t* nsel, float* tau, uint32_t* mask, void* workspace,
                         size_t workspace_bytes, void* stream);
 
 /*
@@ -300,14 +304,15 @@ dash_status dash_cache_append(const dash_decode_params* p, const void* k_new, co
  * are the complete blocks 0..(n-1)/64-1, and the query's own block is
  * attended over its n - 64*((n-1)/64) cached tokens with prior 0.  Cache
  * entries at positions >= n and summaries of blocks >= (n-1)/64 are never
- * read.  Outputs as dash_decode; a sequence with len[s] < 1 or len[s] > C
- * gets o = NaN, lse = NaN, nsel = -1 and tau = NaN.  Workspace: as
+ * read.  Outputs as dash_decode (mask words over the capacity's C/64
+ * blocks); a sequence with len[s] < 1 or len[s] > C gets o = NaN,
+ * lse = NaN, nsel = -1, tau = NaN and an all-zero mask.  Workspace: as
  * dash_decode for the same params.
  */
 dash_status dash_decode_varlen(const dash_decode_params* p, const void* q, const void* kc,
                                const void* vc, const void* kbar, const int32_t* len, void* o,
-                               float* lse, int32_t* nsel, float* tau, void* workspace,
-                               size_t workspace_bytes, void* stream);
+                               float* lse, int32_t* nsel, float* tau, uint32_t* mask,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * One serving step: dash_cache_append of (k_new, v_new) at len[s], then
@@ -318,8 +323,8 @@ dash_status dash_decode_varlen(const dash_decode_params* p, const void* q, const
  */
 dash_status dash_decode_step(const dash_decode_params* p, const void* q, const void* k_new,
                              const void* v_new, const int32_t* len, void* kc, void* vc, void* kbar,
-                             void* o, float* lse, int32_t* nsel, float* tau, void* workspace,
-                             size_t workspace_bytes, void* stream);
+                             void* o, float* lse, int32_t* nsel, float* tau, uint32_t* mask,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Decode for grouped-query heads (entmax head aggregation, as dash_fwd_gqa):
@@ -331,13 +336,14 @@ dash_status dash_decode_step(const dash_decode_params* p, const void* q, const v
  * attends the blocks of pbar = the mean of the heads' p, with prior
  * log pbar, and its own block (prior 0).  The heads of a group walk the same
  * blocks together, so a block is read from HBM once per group.  Outputs
- * o, lse [S,H], nsel and tau (each head's own entmax) as dash_decode;
- * workspace as dash_decode with the same params.
+ * o, lse [S,H], nsel, tau and mask (each head's own entmax support; the
+ * group walks the OR of its heads' masks plus the own block) as
+ * dash_decode; workspace as dash_decode with the same params.
  */
 dash_status dash_decode_gqa(const dash_decode_params* p, int32_t kv_heads, const void* q,
                             const void* kc, const void* vc, const void* kbar, const int32_t* len,
-                            void* o, float* lse, int32_t* nsel, float* tau, void* workspace,
-                            size_t workspace_bytes, void* stream);
+                            void* o, float* lse, int32_t* nsel, float* tau, uint32_t* mask,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* dash_last_error(void);

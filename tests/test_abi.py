@@ -125,8 +125,13 @@ def test_decode_validation(L):
     p.alpha, p.fine_scale, p.coarse_scale, p.dtype = 1.5, 0.088, 0.088, _lib.DASH_BF16
     need = L.dash_decode_workspace_bytes(ctypes.byref(p))
     assert need > 0
-    args = [FAKE] * 5 + [None, None, None, FAKE]
+    # q, kc, vc, kbar, o, lse, nsel, tau, mask, ws
+    args = [FAKE] * 5 + [None, None, None, None, FAKE]
     assert L.dash_decode(ctypes.byref(p), *args, need - 1, None) == _lib.DASH_EWORKSPACE
+    bad = list(args)
+    bad[8] = FAKE + 4  # a mask that is not 16-byte aligned
+    assert L.dash_decode(ctypes.byref(p), *bad, need, None) == _lib.DASH_EINVAL
+    assert "mask" in L.dash_last_error().decode()
     p.N = 1000
     assert L.dash_decode(ctypes.byref(p), *args, need, None) == _lib.DASH_EINVAL
     p.N, p.dtype = 1024, _lib.DASH_F32
@@ -169,16 +174,16 @@ def test_cache_append_validation(L):
 def test_decode_varlen_and_step_validation(L):
     p = _dparams()
     need = L.dash_decode_workspace_bytes(ctypes.byref(p))
-    # q, kc, vc, kbar, len, o, lse, nsel, tau, ws
-    args = [FAKE] * 6 + [None, None, None, FAKE]
+    # q, kc, vc, kbar, len, o, lse, nsel, tau, mask, ws
+    args = [FAKE] * 6 + [None, None, None, None, FAKE]
     assert L.dash_decode_varlen(ctypes.byref(p), *args, need - 1, None) == _lib.DASH_EWORKSPACE
     bad = list(args)
     bad[4] = None
     assert L.dash_decode_varlen(ctypes.byref(p), *bad, need, None) == _lib.DASH_EINVAL
     assert "len" in L.dash_last_error().decode()
     assert L.dash_decode_varlen(ctypes.byref(_dparams(N=64 * 4096)), *args, need, None) == _lib.DASH_EUNSUPPORTED
-    # q, k_new, v_new, len, kc, vc, kbar, o, lse, nsel, tau, ws
-    sargs = [FAKE] * 8 + [None, None, None, FAKE]
+    # q, k_new, v_new, len, kc, vc, kbar, o, lse, nsel, tau, mask, ws
+    sargs = [FAKE] * 8 + [None, None, None, None, FAKE]
     assert L.dash_decode_step(ctypes.byref(p), *sargs, need - 1, None) == _lib.DASH_EWORKSPACE
     bad = list(sargs)
     bad[1] = None
@@ -246,8 +251,8 @@ def test_partial_last_block_validation(L):
 def test_gqa_decode_validation(L):
     p = _dparams(H=4)
     need = L.dash_decode_workspace_bytes(ctypes.byref(p))
-    # q, kc, vc, kbar, len, o, lse, nsel, tau, ws
-    args = [FAKE] * 4 + [None, FAKE, None, None, None, FAKE]
+    # q, kc, vc, kbar, len, o, lse, nsel, tau, mask, ws
+    args = [FAKE] * 4 + [None, FAKE, None, None, None, None, FAKE]
     assert L.dash_decode_gqa(ctypes.byref(p), 3, *args, need, None) == _lib.DASH_EINVAL
     assert L.dash_decode_gqa(ctypes.byref(p), 2, *args, need - 1, None) == _lib.DASH_EWORKSPACE
     bad = list(args)

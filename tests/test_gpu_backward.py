@@ -16,6 +16,7 @@ import torch
 
 import oracle
 from differentiable_adaptive_block_amd import inputs
+import oracle_parallel
 from parity import rel_l2
 
 pytestmark = pytest.mark.gpu
@@ -68,11 +69,16 @@ def test_backward_small_full_oracle(case):
         assert e <= TOL, (name, n, e)
 
 
-def test_backward_deterministic():
-    w = inputs.make_prefill(1, 2, 1024, 128, "bf16", True, (1, 4), seed=4, device="cpu", with_dout=True)
+@pytest.mark.parametrize("dtype,causal", [("bf16", True), ("fp32", False), ("fp32", True)])
+def test_backward_deterministic(dtype, causal):
+    """Bitwise-equal gradients on a rerun (no floating-point atomics on any path)."""
+    D = 128 if dtype == "bf16" else 64
+    w = inputs.make_prefill(1, 2, 1024 if dtype == "bf16" else 512, D, dtype, causal, (1, 4) if causal else None,
+                            seed=4, device="cpu", with_dout=True)
     w = {k: v.to(DEV) for k, v in w.items()}
-    _, g1 = _run(w, 1.5, True, 3 / math.sqrt(128))
-    _, g2 = _run(w, 1.5, True, 3 / math.sqrt(128))
+    _, g1 = _run(w, 1.5, causal, 3 / math.sqrt(D))
+    g1 = {k: v.clone() for k, v in g1.items()}
+    _, g2 = _run(w, 1.5, causal, 3 / math.sqrt(D))
     for n in ("dq", "dk", "dv", "dkbar"):
         assert torch.equal(g1[n], g2[n]), n
 
@@ -102,3 +108,32 @@ def test_backward_training_16k_sampled(alpha):
         e_kb = rel_l2(_np64(g["dkbar"][b, h])[nb - 4:nb - 1], ref["dkbar"][0, 0][nb - 4:nb - 1])
         _say(f"  (b={b}, h={h}) rel-L2 dq {e_dq:.2e} dk {e_dk:.2e} dv {e_dv:.2e} dkbar {e_kb:.2e}")
         assert max(e_dq, e_dk, e_dv, e_kb) <= TOL
+
+
+def test_backward_training_16k_full_head():
+    """One (batch, head) slice of the 16K training workload at alpha 1.5, launched
+    at full size: dQ of every row and dK, dV, dkbar of every key block against
+    oracle.backward over all 16384 rows (run over worker processes)."""
+    wl = inputs.CONFIGS["train16k"]
+    sh = wl.shape
+    _say(f"[backward] train16k full size {sh} alpha=1.5, one head compared whole")
+    w = inputs.make_prefill(sh["B"], sh["H"], sh["T"], sh["D"], wl.dtype, True, wl.planted, wl.seed, device=DEV,
+                            with_dout=True)
+    _, g = _run(w, 1.5, True, wl.coarse_scale)
+    b, h = 1, 5
+    prm = oracle.Params(alpha=1.5, causal=True, coarse_scale=wl.coarse_scale, storage="bf16")
+    ref = oracle_parallel.backward_head(*(w[n][b, h] for n in ("q", "k", "v", "dout")), prm)
+    errs = {n: rel_l2(_np64(g[n][b, h]), ref[n]) for n in ("dq", "dk", "dv", "dkbar")}
+    # the first key blocks collect terms from up to 16K query rows: check them on their own too
+    nb = sh["T"] // 64
+    first = slice(0, 8 * 64)
+    errs["dk_first8"] = rel_l2(_np64(g["dk"][b, h])[first], ref["dk"][first])
+    errs["dv_first8"] = rel_l2(_np64(g["dv"][b, h])[first], ref["dv"][first])
+    errs["dkbar_first8"] = rel_l2(_np64(g["dkbar"][b, h])[:8], ref["dkbar"][:8])
+    # per key block: the worst block's relative error
+    dkb = np.linalg.norm((_np64(g["dk"][b, h]) - ref["dk"]).reshape(nb, -1), axis=1) / np.maximum(
+        np.linalg.norm(ref["dk"].reshape(nb, -1), axis=1), 1e-30)
+    errs["dk_worst_block"] = float(dkb.max())
+    _say(f"  rel-L2 {errs}")
+    for n, e in errs.items():
+        assert e <= TOL, (n, e)

@@ -14,7 +14,8 @@ import torch
 
 import oracle
 from differentiable_adaptive_block_amd import inputs
-from parity import check_rows, unpack_mask
+import oracle_parallel
+from parity import check_out_rows, check_rows, check_stage1_head, unpack_mask
 
 pytestmark = pytest.mark.gpu
 
@@ -92,38 +93,82 @@ def test_forward_deterministic():
     assert torch.equal(a["sel"].mask, b["sel"].mask)
 
 
-def _sampled(name, n_heads=3, n_rows=24, T_sub=None):
+def _prefill_head_checks(w, r, h, prm, dtype, n_rows, rng, what, all_rows_out=False):
+    """One head (batch 0) of a GPU forward against the oracle: the summaries
+    bit for bit, Stage 1 (mask, count, tau) on every row, O and LSE on
+    ``n_rows`` uniformly drawn rows plus the first, block-edge and last rows
+    (every row with ``all_rows_out``).  The oracle runs over worker processes."""
+    T = w["q"].shape[2]
+    qh, kh, vh = (w[x][0, h] for x in ("q", "k", "v"))
+    kb = oracle.pool_blocks(_np64(kh), 64, dtype)
+    np.testing.assert_array_equal(r["kbar"][0, h].double().cpu().numpy(), kb)
+    sel = r["sel"]
+    sels = oracle_parallel.select_rows(qh, r["kbar"][0, h], prm, list(range(T)))
+    flips, tau_w = check_stage1_head(sel.mask[0, h].cpu().numpy(), sel.tau[0, h].cpu().numpy(),
+                                     sel.nsel[0, h].cpu().numpy(), sels, prm.alpha, f"{what} head {h}")
+    if all_rows_out:
+        rows = list(range(T))
+    else:
+        rows = sorted(set(rng.choice(T, size=n_rows, replace=False).tolist() + [0, 63, 64, T - 1]))
+    ora = oracle_parallel.forward_rows(qh, kh, vh, prm, rows, kbar=r["kbar"][0, h])
+    st = check_out_rows(r["o"][0, h].float().cpu().numpy(), r["lse"][0, h].cpu().numpy(), ora, rows,
+                        w["q"].dtype, f"{what} head {h}")
+    st.update(flips=flips, tau_over_bound=tau_w)
+    return st
+
+
+def _sampled(name, n_heads=3, n_rows=512, full_head=False):
+    """A named full-size prefill workload: heads drawn at random get the
+    per-head checks; with ``full_head`` the first of them compares O and LSE
+    on every row."""
     wl = inputs.CONFIGS[name]
     sh = wl.shape
-    _say(f"[forward] {name} full size {sh} (sampled rows)")
+    _say(f"[forward] {name} full size {sh}")
     w = inputs.make_prefill(sh["B"], sh["H"], sh["T"], sh["D"], wl.dtype, wl.causal, wl.planted, wl.seed,
                             device=DEV, with_dout=False)
     alpha = wl.alpha if not isinstance(wl.alpha, tuple) else wl.alpha[-1]
-    r, g = _gpu_forward(w, alpha, wl.causal, wl.coarse_scale)
+    r = _api().forward(w["q"], w["k"], w["v"], alpha=alpha, causal=wl.causal, coarse_scale=wl.coarse_scale,
+                       want_mask=True)
+    torch.cuda.synchronize()
     rng = np.random.default_rng(0)
     B, H, T = sh["B"], sh["H"], sh["T"]
     heads = sorted(rng.choice(H, size=n_heads, replace=False).tolist())
-    rows = []
-    for h in heads:
-        pos = rng.choice(T, size=n_rows, replace=False).tolist() + [0, 63, 64, T - 1]
-        rows += [(0, h, i) for i in sorted(set(pos))]
     prm = oracle.Params(alpha=alpha, causal=wl.causal, coarse_scale=wl.coarse_scale, storage=wl.dtype)
-    ora = []
-    for h in heads:
-        q, k, v = (_np64(w[x][0:1, h:h + 1]) for x in ("q", "k", "v"))
-        kb = oracle.pool_blocks(k[0, 0], 64, wl.dtype)
-        np.testing.assert_array_equal(r["kbar"][0, h].double().cpu().numpy(), kb)
-        hr = [(0, 0, i) for (_, hh, i) in rows if hh == h]
-        ora += oracle.forward_rows(q, k, v, prm, hr, kbar=kb[None, None])
-    st = check_rows(g, ora, rows, torch.bfloat16, alpha, name)
-    density = float(g["nsel"].sum()) / float(sum((i // 64) for i in range(T)) * B * H)
-    _say(f"  ok {st}; selected-pair density {density:.4f}")
+    for n, h in enumerate(heads):
+        st = _prefill_head_checks(w, r, h, prm, wl.dtype, n_rows, rng, name, all_rows_out=full_head and n == 0)
+        _say(f"  head {h}: {st}")
+    density = float(r["sel"].nsel.double().sum()) / float(sum((i // 64) for i in range(T)) * B * H)
+    _say(f"  ok; selected-pair density {density:.4f}")
     return density
 
 
 def test_forward_16k_causal_prefill_sampled():
-    _sampled("prefill16k")
+    _sampled("prefill16k", full_head=True)
 
 
 def test_forward_64k_causal_prefill_sampled():
-    _sampled("prefill64k", n_heads=2, n_rows=12)
+    _sampled("prefill64k", n_heads=2, n_rows=384)
+
+
+def test_forward_64k_calibrated_prefill_sampled():
+    """The 64K prefill at coarse scale 7/sqrt(128) (about 8% of the candidate pairs selected)."""
+    d = _sampled("prefill64k_sc7", n_heads=2, n_rows=384)
+    assert d < 0.12, d
+
+
+@pytest.mark.parametrize("T", [8192, 32768])
+def test_forward_stage1_kernel_sizes(T):
+    """Sequence lengths that take the other Stage-1 kernel shapes: 128 blocks
+    (8 candidates per lane of a 16-lane row group) and 512 blocks (two
+    256-block chunks of the staged score tile)."""
+    B, H, D = 1, 2, 128
+    _say(f"[forward] B{B} H{H} T{T} D{D} bf16 causal, coarse 4/sqrt(D)")
+    w = inputs.make_prefill(B, H, T, D, "bf16", True, (1, 8), seed=50 + T // 1024, device=DEV, with_dout=False)
+    cs = 4.0 / math.sqrt(D)
+    r = _api().forward(w["q"], w["k"], w["v"], alpha=1.5, causal=True, coarse_scale=cs, want_mask=True)
+    torch.cuda.synchronize()
+    prm = oracle.Params(alpha=1.5, causal=True, coarse_scale=cs, storage="bf16")
+    rng = np.random.default_rng(T)
+    for h in range(H):
+        st = _prefill_head_checks(w, r, h, prm, "bf16", 384, rng, f"T{T}")
+        _say(f"  head {h}: {st}")
