@@ -153,13 +153,15 @@ __device__ __forceinline__ float prior_pick(const f32x16& pacc, int e) {
   return __uint_as_float(((slot >> 2) & 1) ? sw[1] : sw[0]);
 }
 
-// The generic-path score: sequential fp32 dot product of a query held in
-// LDS (as float) with one summary row.
+// The generic-path score: dot product of a query held in LDS (as float)
+// with one key or summary row, accumulated in fp64 (fp32 x fp32 products are
+// exact there) and rounded once to fp32, so a score is within half an fp32
+// ulp of the exact dot product whatever D is.
 template <typename T>
 __device__ __forceinline__ float dot_row(const float* qs, const T* kr, int D) {
-  float acc = 0.f;
-  for (int d = 0; d < D; ++d) acc = fmaf(qs[d], to_f<T>(kr[d]), acc);
-  return acc;
+  double acc = 0.0;
+  for (int d = 0; d < D; ++d) acc = fma((double)qs[d], (double)to_f<T>(kr[d]), acc);
+  return (float)acc;
 }
 
 hipError_t launch_pool(const void* k, void* kbar, int BH, int T, int D, int dtype, hipStream_t st);

@@ -57,6 +57,12 @@ def test_cpu_baseline_leg_tiny(monkeypatch):
     wl = inputs.CONFIGS["prefill16k"]
     w = inputs.make_prefill(1, 2, 256, 64, "bf16", True, (1, 2), seed=5, device="cpu", with_dout=False)
     r = bench.cpu_baseline(w, wl, 1.5, rows_per_worker=8, workers=2)
-    assert set(r) == {"value", "unit", "cores", "kind", "sample"}
+    assert set(r) == {"value", "unit", "cores", "kind", "sample", "host_cpu_count", "blas_threads_per_process"}
     assert r["kind"] == "oracle" and r["cores"] == 2 and r["unit"] == "tokens/s"
     assert r["value"] > 0 and "16 query rows" in r["sample"]
+
+
+def test_median_and_columns():
+    assert bench._median([3.0, 1.0, 2.0]) == 2.0
+    assert bench._median([4.0, 1.0, 2.0, 3.0]) == 2.5
+    assert bench._col([[1, 2], [3, 4]], 1) == [2, 4]
