@@ -41,6 +41,8 @@ EXPORTS = [
     "dash_decode_varlen",
     "dash_decode_step",
     "dash_decode_gqa",
+    "dash_decode_static_max_bytes",
+    "dash_decode_static",
     "dash_last_error",
 ]
 
@@ -141,6 +143,10 @@ def load() -> ctypes.CDLL:
     L.dash_decode_gqa.restype = ctypes.c_int
     L.dash_decode_gqa.argtypes = [P(DashDecodeParams), ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                   vp, ctypes.c_size_t, vp]
+    L.dash_decode_static_max_bytes.restype = ctypes.c_size_t
+    L.dash_decode_static_max_bytes.argtypes = []
+    L.dash_decode_static.restype = ctypes.c_int
+    L.dash_decode_static.argtypes = [P(DashDecodeParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.dash_last_error.restype = ctypes.c_char_p
     L.dash_last_error.argtypes = []
     _lib = L
@@ -255,3 +261,11 @@ def decode_gqa(p: DashDecodeParams, kv_heads: int, q, kc, vc, kbar, lens, o, lse
                ws_bytes, stream) -> None:
     check(load().dash_decode_gqa(ctypes.byref(p), kv_heads, q, kc, vc, kbar, lens, o, lse, nsel, tau, mask, ws,
                                  ws_bytes, stream))
+
+
+def decode_static_max_bytes() -> int:
+    return int(load().dash_decode_static_max_bytes())
+
+
+def decode_static(p: DashDecodeParams, q, kc, vc, kbar, o, lse, nsel, tau, mask, stream) -> None:
+    check(load().dash_decode_static(ctypes.byref(p), q, kc, vc, kbar, o, lse, nsel, tau, mask, stream))

@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "dash.h"
@@ -125,6 +126,42 @@ size_t decode_ws_layout(const dash_decode_params* p, size_t off[6], int* nsplit,
   off[4] = take(SH * nb * sizeof(float));          // log2 priors
   off[5] = take(SH * DASH_DEC_SPLIT_GQA * (D + 2) * sizeof(float));  // partials (the larger split count)
   return o;
+}
+
+// Scratch of dash_decode_static: the decode workspace (scores, row
+// statistics, block lists, split partials) of callers that cannot allocate.
+// Each GPU the library runs on holds its own copy until the process ends.
+// In host code `scratch` is the host-side stand-in of the array, not a
+// device address: the device address comes from hipGetSymbolAddress, once
+// per device, with that device current.
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on its first use on
+// that device); nullptr with an error message on failure.
+void* static_scratch(hipError_t* err) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *err = e != hipSuccess ? e : hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *err = hipSuccess;
+  return g_scratch_ptr[dev];
 }
 
 }  // namespace
@@ -623,6 +660,28 @@ dash_status dash_decode(const dash_decode_params* p, const void* q, const void* 
   dash_status s = check_decode_params(p);
   if (s != DASH_OK) return s;
   return decode_common(p, q, kc, vc, kbar, nullptr, 0, o, lse, nsel, tau, mask, workspace, workspace_bytes, stream);
+}
+
+size_t dash_decode_static_max_bytes(void) { return kStaticScratchBytes; }
+
+dash_status dash_decode_static(const dash_decode_params* p, const void* q, const void* kc, const void* vc,
+                               const void* kbar, void* o, float* lse, int32_t* nsel, float* tau, uint32_t* mask,
+                               void* stream) {
+  dash_status s = check_decode_params(p);
+  if (s != DASH_OK) return s;
+  size_t off[6];
+  const size_t need = decode_ws_layout(p, off, nullptr, nullptr);
+  if (need > kStaticScratchBytes)
+    return fail(DASH_EWORKSPACE, "this decode needs %zu bytes of scratch; the static scratch holds %zu "
+                "(use dash_decode with a workspace)", need, kStaticScratchBytes);
+  if (!ok_ptr(q) || !ok_ptr(kc) || !ok_ptr(vc) || !ok_ptr(kbar) || !ok_ptr(o))
+    return fail(DASH_EINVAL, "q, kc, vc, kbar and o must be non-null and 16-byte aligned");
+  if (!ok_opt(lse) || !ok_opt(nsel) || !ok_opt(tau) || !ok_opt(mask))
+    return fail(DASH_EINVAL, "lse/nsel/tau/mask must be 16-byte aligned");
+  hipError_t e;
+  void* ws = static_scratch(&e);
+  if (!ws) return hip_fail(e, "static scratch address");
+  return decode_common(p, q, kc, vc, kbar, nullptr, 0, o, lse, nsel, tau, mask, ws, need, stream);
 }
 
 dash_status dash_decode_gqa(const dash_decode_params* p, int32_t kv_heads, const void* q, const void* kc,

@@ -269,6 +269,26 @@ dash_status dash_decode(const dash_decode_params* p, const void* q, const void* 
                         size_t workspace_bytes, void* stream);
 
 /*
+ * dash_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same decode, its workspace taken from a scratch array of
+ * dash_decode_static_max_bytes() bytes (32 MiB) that the library holds in
+ * device memory, one per GPU, until the process ends.  The call allocates
+ * and frees nothing.  Arguments and outputs as dash_decode, without the
+ * workspace.  Sizes whose dash_decode_workspace_bytes() exceeds the scratch
+ * (e.g. more than 512 rows at a 131072-token cache) return DASH_EWORKSPACE
+ * with nothing launched.  Every call on one GPU uses that GPU's one scratch:
+ * calls that overlap on a GPU (other streams, other host threads) race and
+ * must be serialised by the caller.  Nothing in the scratch needs to start
+ * at zero: each call writes every entry it reads.  The first call on a
+ * device looks up the scratch's address there (with that device current).
+ */
+size_t dash_decode_static_max_bytes(void);
+dash_status dash_decode_static(const dash_decode_params* p, const void* q, const void* kc,
+                               const void* vc, const void* kbar, void* o, float* lse,
+                               int32_t* nsel, float* tau, uint32_t* mask, void* stream);
+
+/*
  * Decode cache maintenance and caches of any length (the decoding path keeps
  * one summary per 64-token chunk of the cache: the chunk-summarise stage
  * among the code samples that the codewithpapers.app entry "DashAttention:

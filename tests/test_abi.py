@@ -261,3 +261,15 @@ def test_gqa_decode_validation(L):
     p16 = _dparams(H=16)
     need16 = L.dash_decode_workspace_bytes(ctypes.byref(p16))
     assert L.dash_decode_gqa(ctypes.byref(p16), 1, *args, need16, None) == _lib.DASH_EUNSUPPORTED
+
+
+def test_decode_static_rejects_sizes_beyond_its_scratch(L):
+    """Validation runs before anything touches the GPU: a decode whose workspace
+    exceeds the static scratch is refused with DASH_EWORKSPACE."""
+    assert L.dash_decode_static_max_bytes() == 32 << 20
+    p = _dparams(S=16, H=64, N=131072)
+    assert L.dash_decode_workspace_bytes(ctypes.byref(p)) > L.dash_decode_static_max_bytes()
+    args = [FAKE] * 5 + [None, None, None, None]
+    assert L.dash_decode_static(ctypes.byref(p), *args, None) == _lib.DASH_EWORKSPACE
+    assert "static scratch" in L.dash_last_error().decode()
+    assert L.dash_decode_static(ctypes.byref(_dparams(N=1000)), *args, None) == _lib.DASH_EINVAL
