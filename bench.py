@@ -601,7 +601,7 @@ def measured_peaks(device):
     del a, b, c
     x = torch.ones(1 << 31, device=device, dtype=torch.bfloat16)
     r = torch.empty((), device=device, dtype=torch.float32)
-    read_ms = _median(_col(run_timed(lambda ev: torch.sum(x, dtype=torch.float32, out=r), 10, 2), 0))
+    read_ms = _median(_col(run_timed(lambda ev: torch.sum(x, dim=0, dtype=torch.float32, out=r), 10, 2), 0))
     del x
     src = torch.ones(1 << 30, device=device, dtype=torch.bfloat16)
     dst = torch.empty_like(src)

@@ -59,7 +59,7 @@ class DashSel(ctypes.Structure):
     _fields_ = [
         ("tau", ctypes.c_void_p), ("lognorm", ctypes.c_void_p), ("nsel", ctypes.c_void_p),
         ("mask", ctypes.c_void_p), ("tile_cnt", ctypes.c_void_p), ("tile_blk", ctypes.c_void_p),
-        ("tile_bits", ctypes.c_void_p),
+        ("tile_bits", ctypes.c_void_p), ("passes", ctypes.c_void_p),
     ]
 
 
@@ -163,7 +163,7 @@ def query_tile() -> int:
 
 
 def sel_sizes(p: DashParams):
-    out = (ctypes.c_size_t * 7)()
+    out = (ctypes.c_size_t * 8)()
     check(load().dash_sel_sizes(ctypes.byref(p), out))
     return list(out)
 

@@ -66,12 +66,14 @@ class Selection:
     tile_cnt: torch.Tensor
     tile_blk: torch.Tensor
     tile_bits: torch.Tensor
+    passes: torch.Tensor | None = None
 
     def as_c(self) -> _lib.DashSel:
         s = _lib.DashSel()
         s.tau, s.lognorm = _ptr(self.tau), _ptr(self.lognorm)
         s.nsel, s.mask = _ptr(self.nsel), _ptr(self.mask)
         s.tile_cnt, s.tile_blk, s.tile_bits = _ptr(self.tile_cnt), _ptr(self.tile_blk), _ptr(self.tile_bits)
+        s.passes = _ptr(self.passes)
         return s
 
 
@@ -92,6 +94,7 @@ def alloc_selection(p: _lib.DashParams, device, want_mask: bool = True) -> Selec
         tile_cnt=e(n[4], torch.int32).view(B, H, ntile),
         tile_blk=e(n[5], torch.int32).view(B, H, ntile, nb),
         tile_bits=e(n[6], torch.int32).view(B, H, ntile, nbw),
+        passes=e(n[7], torch.int32).view(B, H, T) if want_mask else None,
     )
 
 

@@ -95,7 +95,8 @@ dash_status check_sel(const dash_sel* sel, bool need_bits) {
   if (!ok_ptr(sel->tau) || !ok_ptr(sel->lognorm) || !ok_ptr(sel->tile_cnt) || !ok_ptr(sel->tile_blk) ||
       !ok_ptr(sel->tile_bits))
     return fail(DASH_EINVAL, "selection buffers tau/lognorm/tile_cnt/tile_blk/tile_bits must be non-null and 16-byte aligned");
-  if (!ok_opt(sel->nsel) || !ok_opt(sel->mask)) return fail(DASH_EINVAL, "nsel/mask must be 16-byte aligned");
+  if (!ok_opt(sel->nsel) || !ok_opt(sel->mask) || !ok_opt(sel->passes))
+    return fail(DASH_EINVAL, "nsel/mask/passes must be 16-byte aligned");
   (void)need_bits;
   return DASH_OK;
 }
@@ -172,7 +173,7 @@ int32_t dash_query_tile(void) { return DASH_QTILE; }
 
 const char* dash_last_error(void) { return g_err.c_str(); }
 
-dash_status dash_sel_sizes(const dash_params* p, size_t out[7]) {
+dash_status dash_sel_sizes(const dash_params* p, size_t out[8]) {
   dash_status s = check_params(p, true, true);
   if (s != DASH_OK) return s;
   if (!out) return fail(DASH_EINVAL, "null output array");
@@ -185,6 +186,7 @@ dash_status dash_sel_sizes(const dash_params* p, size_t out[7]) {
   out[4] = BH * nt;
   out[5] = BH * nt * nb;
   out[6] = BH * nt * nbw;
+  out[7] = BH * T;
   return DASH_OK;
 }
 
@@ -259,6 +261,7 @@ static dash_status select_from_kbar(const dash_params* p, const void* q, const v
   sa.lognorm = sel->lognorm;
   sa.nsel = sel->nsel;
   sa.mask = sel->mask;
+  sa.passes = sel->passes;
   sa.tile_bits = sel->tile_bits;
   if ((e = launch_select(sa, BH, p->dtype, st)) != hipSuccess) return hip_fail(e, "select");
   if ((e = launch_group_union(sel->tile_bits, BH, grp, (size_t)ntile_of(p->T) * nbw_of(nb), st)) != hipSuccess)

@@ -119,7 +119,7 @@ __global__ __launch_bounds__(512) void decode_select_kernel(DecodeArgs a) {
   }
   EntmaxOut e;
   if (nc > 0) e = entmax_solve<NPL, 64>(u, nc, ca);
-  else { e.tau = __uint_as_float(0x7fc00000u); e.lognorm = 0.f; e.nsel = 0; }
+  else { e.tau = __uint_as_float(0x7fc00000u); e.lognorm = 0.f; e.nsel = 0; e.passes = 0; }
   if (a.mask) {
     // the row's selected candidates as bits: word 2k + x from ballot k
     uint32_t* mw = a.mask + (size_t)row * nbw;

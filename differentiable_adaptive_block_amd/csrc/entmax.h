@@ -5,9 +5,16 @@
 // thelatestinai.com page: the normaliser tau is the costly part of entmax).
 // With u = (alpha-1) z and m = 1/(alpha-1), tau solves
 //     f(tau) = sum_b [u_b - tau]_+^m = 1.
-// f is convex and decreasing, so Newton's method started left of the root
-// (at max u - 1, where the largest term alone gives f >= 1) increases
-// monotonically to it.  alpha = 1 is the softmax: tau = log-sum-exp(z).
+// The iteration is Newton's method on g = f^(1/m) - 1, the m-norm of
+// [u - tau]_+ minus one, rather than on f itself: g is convex and
+// decreasing, so steps taken from the left of the root increase
+// monotonically to it, and g is nearly linear (exactly linear while the
+// support does not change and its scores are equal), so the steps are long
+// for every alpha, where Newton on f crawls at small alpha (each step
+// closes only a fraction 1/m of the gap far from the root).  The start is
+// max u - 1, where the largest term alone gives f >= 1; at alpha = 1.5 a
+// closed-form start is taken first (see entmax_newton).  alpha = 1 is the
+// softmax: tau = log-sum-exp(z).
 //
 // A row is held by a group of G lanes (G = 16: four rows per wave; G = 64:
 // one row per wave).  Group reductions use DPP within each 16-lane row of
@@ -21,7 +28,8 @@
 struct EntmaxOut {
   float tau;
   float lognorm;
-  int nsel;
+  int nsel;    // selected candidates (-1 when not counted)
+  int passes;  // passes over the row's scores the threshold took
 };
 
 template <int CTRL>
@@ -118,20 +126,39 @@ __device__ __forceinline__ void entmax_terms(float x, float m, float& fx, float&
   }
 }
 
-// alpha > 1: Newton from the left on t = tau - max u (see the header).
+// f^((m-1)/m), the factor of the Newton step on f^(1/m).
+template <int PW>
+__device__ __forceinline__ float step_pow(float f, float m) {
+  if constexpr (PW == 1) return 1.f;
+  else if constexpr (PW == 2) return __builtin_sqrtf(f);
+  else if constexpr (PW == 4) {
+    const float r = __builtin_sqrtf(f);
+    return r * __builtin_sqrtf(r);
+  } else {
+    return __builtin_amdgcn_exp2f((m - 1.f) / m * __builtin_amdgcn_logf(f));
+  }
+}
+
+// alpha > 1: Newton on f^(1/m) from the left, on t = tau - max u (see the
+// header).  With x = [v - t]_+ (v = u - max u), S = sum x^m and
+// S1 = sum x^(m-1), the step is (S - S^((m-1)/m)) / S1.  Every pass keeps
+// S, so the pass that finds the step at most 1e-7 is the last: tau =
+// max u + t there and lognorm = log S(t).  `count`: also count the
+// support (one more pass, compares only).
 template <int NPL, int G, int PW>
-__device__ __forceinline__ EntmaxOut entmax_newton(const float (&u)[NPL], int nvalid, float umax, float m) {
+__device__ __forceinline__ EntmaxOut entmax_newton(const float (&u)[NPL], int nvalid, float umax, float m,
+                                                   bool count) {
   // v = u - umax, recomputed where used rather than held (NPL registers)
   auto vof = [&](int k) { return u[k] - umax; };
   float t = -1.f;  // f(-1) >= 1 from the largest term alone
+  int passes = 0;
   if constexpr (PW == 2) {
     // alpha = 1.5: sum_{v > t} (v - t)^2 = 1 is a quadratic in t once the
     // support is fixed.  Its smaller root t_c on the support {v > -1} lies at
     // or right of the true root (elements of that set that fall below the
-    // root still add to the left-hand side); one Newton step from the right
-    // of a convex decreasing function lands at or left of the root, where the
-    // iteration below starts.  A start that rounding puts anywhere else
-    // falls back to -1.
+    // root still add to the left-hand side); g is convex, so one step from
+    // there lands at or left of the root, where the iteration below starts.
+    // A start that rounding puts anywhere else falls back to -1.
     float n = 0.f, sa = 0.f, sb = 0.f;
 #pragma unroll
     for (int k = 0; k < NPL; ++k) {
@@ -147,62 +174,69 @@ __device__ __forceinline__ EntmaxOut entmax_newton(const float (&u)[NPL], int nv
     sa = grp_sum<G>(sa);
     sb = grp_sum<G>(sb);
     const float tc = (sa - __builtin_sqrtf(fmaxf(sa * sa - n * (sb - 1.f), 0.f))) / n;
-    float f = 0.f, fp = 0.f;
+    float f = 0.f, s1 = 0.f;
 #pragma unroll
     for (int k = 0; k < NPL; ++k) {
       if (k * G < nvalid) {
         const float x = fmaxf(vof(k) - tc, 0.f);
         f += x * x;
-        fp += x;
+        s1 += x;
       }
     }
     f = grp_sum<G>(f);
-    fp = grp_sum<G>(fp);
-    const float t1 = tc + (f - 1.f) / (2.f * fp);
+    s1 = grp_sum<G>(s1);
+    const float t1 = tc + (f - __builtin_sqrtf(f)) / s1;
     if (t1 > -1.f && t1 <= 0.f) t = t1;  // false for NaN too
+    passes = 2;
   }
   bool done = false;
-  // groups that have converged keep their t while the others iterate (all
-  // lanes stay active for the DPP reductions)
+  float tfin = t, lnf = 0.f;
+  int npass = passes;
+  // groups that have converged keep their result while the others iterate
+  // (all lanes stay active for the DPP reductions)
   for (int it = 0; it < 64; ++it) {
-    float f = 0.f, fp = 0.f;
+    float f = 0.f, s1 = 0.f;
 #pragma unroll
     for (int k = 0; k < NPL; ++k) {
       if (k * G < nvalid) {
         float a, b;
         entmax_terms<PW>(vof(k) - t, m, a, b);
         f += a;
-        fp += b;
+        s1 += b;
       }
     }
     f = grp_sum<G>(f);
-    fp = grp_sum<G>(fp);
-    const float step = (f - 1.f) / (m * fp);
+    s1 = grp_sum<G>(s1);
+    ++passes;
+    const float step = (f - step_pow<PW>(f, m)) / s1;
     if (!done) {
-      if (!(step > 0.f)) done = true;  // at (or, by rounding, just past) the root
-      else {
+      if (!(step > 1e-7f)) {  // converged (or, by rounding, just past the root; NaN too)
+        done = true;
+        tfin = t;
+        lnf = __logf(f);
+        npass = passes;
+      } else {
         t += step;
-        if (step <= 1e-7f) done = true;
       }
     }
     if (__ballot(!done) == 0ull) break;
   }
-  EntmaxOut r;
-  r.tau = umax + t;
-  float s = 0.f;
-  int c = 0;
-#pragma unroll
-  for (int k = 0; k < NPL; ++k) {
-    if (k * G < nvalid) {
-      const float x = u[k] - r.tau;
-      float a, b;
-      entmax_terms<PW>(x, m, a, b);
-      s += a;
-      c += x > 0.f ? 1 : 0;
-    }
+  if (!done) {  // not reached on finite scores; keep the outputs defined
+    tfin = t;
+    npass = passes;
   }
-  r.lognorm = __logf(grp_sum<G>(s));
-  r.nsel = grp_sum_i<G>(c);
+  EntmaxOut r;
+  r.tau = umax + tfin;
+  r.lognorm = lnf;
+  r.passes = npass;
+  r.nsel = -1;
+  if (count) {
+    int c = 0;
+#pragma unroll
+    for (int k = 0; k < NPL; ++k)
+      if (k * G < nvalid) c += (u[k] - r.tau) > 0.f ? 1 : 0;
+    r.nsel = grp_sum_i<G>(c);
+  }
   return r;
 }
 
@@ -213,7 +247,8 @@ __device__ __forceinline__ EntmaxOut entmax_newton(const float (&u)[NPL], int nv
 // every row has at least one candidate.  All lanes of the wave call this
 // together; the result is identical across each group.
 template <int NPL, int G>
-__device__ __forceinline__ EntmaxOut entmax_solve(const float (&u)[NPL], int nvalid, const CoarseArith& ca) {
+__device__ __forceinline__ EntmaxOut entmax_solve(const float (&u)[NPL], int nvalid, const CoarseArith& ca,
+                                                  bool count = true) {
   float umax = -INFINITY;
 #pragma unroll
   for (int k = 0; k < NPL; ++k)
@@ -238,11 +273,12 @@ __device__ __forceinline__ EntmaxOut entmax_solve(const float (&u)[NPL], int nva
     }
     r.lognorm = __logf(grp_sum<G>(s2));
     r.nsel = grp_sum_i<G>(c);
+    r.passes = 2;
     return r;
   }
   const float m = ca.m;
-  if (m == 2.f) return entmax_newton<NPL, G, 2>(u, nvalid, umax, m);
-  if (m == 4.f) return entmax_newton<NPL, G, 4>(u, nvalid, umax, m);
-  if (m == 1.f) return entmax_newton<NPL, G, 1>(u, nvalid, umax, m);
-  return entmax_newton<NPL, G, 0>(u, nvalid, umax, m);
+  if (m == 2.f) return entmax_newton<NPL, G, 2>(u, nvalid, umax, m, count);
+  if (m == 4.f) return entmax_newton<NPL, G, 4>(u, nvalid, umax, m, count);
+  if (m == 1.f) return entmax_newton<NPL, G, 1>(u, nvalid, umax, m, count);
+  return entmax_newton<NPL, G, 0>(u, nvalid, umax, m, count);
 }

@@ -14,6 +14,7 @@ struct SelectArgs {
   float* lognorm;     // [BH, T]
   int* nsel;          // [BH, T] or null
   uint32_t* mask;     // [BH, T, nbw] or null
+  int* passes;        // [BH, T] or null: passes over the row the threshold solve took
   uint32_t* tile_bits;  // [BH, ntile, nbw], zeroed before the launch
 };
 

@@ -91,6 +91,7 @@ __device__ __forceinline__ void write_row_selection(const SelectArgs& a, size_t 
     a.tau[row_g] = e.tau;
     a.lognorm[row_g] = e.lognorm;
     if (a.nsel) a.nsel[row_g] = e.nsel;
+    if (a.passes) a.passes[row_g] = e.passes;
   }
 #pragma unroll
   for (int k = 0; k < NPL; ++k) {
@@ -123,6 +124,7 @@ __device__ __forceinline__ void write_empty_row(const SelectArgs& a, size_t row_
     a.tau[row_g] = __uint_as_float(0x7fc00000u);
     a.lognorm[row_g] = 0.f;
     if (a.nsel) a.nsel[row_g] = 0;
+    if (a.passes) a.passes[row_g] = 0;
   }
   if (a.mask)
     for (int w = l; w < nbw; w += 64) a.mask[row_g * nbw + w] = 0u;
@@ -141,6 +143,7 @@ __device__ __forceinline__ void write_rows16(const SelectArgs& a, size_t row_g, 
     a.tau[row_g] = e.tau;
     a.lognorm[row_g] = e.lognorm;
     if (a.nsel) a.nsel[row_g] = e.nsel;
+    if (a.passes) a.passes[row_g] = e.passes;
   }
   constexpr int NW = (NPL + 1) / 2;
   constexpr int NJ = (NW + 15) / 16;
@@ -221,6 +224,7 @@ __global__ __launch_bounds__(64 * NW) void select_mfma_kernel(SelectArgs a) {
         a.tau[row_g] = __uint_as_float(0x7fc00000u);
         a.lognorm[row_g] = 0.f;
         if (a.nsel) a.nsel[row_g] = 0;
+        if (a.passes) a.passes[row_g] = 0;
       }
       if (a.mask)
         for (int x = g; x < nbw; x += 16) a.mask[row_g * nbw + x] = 0u;
@@ -232,7 +236,7 @@ __global__ __launch_bounds__(64 * NW) void select_mfma_kernel(SelectArgs a) {
       const int idx = g + 16 * k;
       u[k] = idx < nc ? zs[row * nbp + idx] : -INFINITY;
     }
-    const EntmaxOut e = entmax_solve<NPL, 16>(u, nc, ca);
+    const EntmaxOut e = entmax_solve<NPL, 16>(u, nc, ca, a.nsel != nullptr);
     write_rows16<NPL>(a, row_g, u, nc, e, ca, uni);
   }
   __syncthreads();
@@ -305,11 +309,12 @@ __global__ __launch_bounds__(512, 4) void select_chunked_kernel(SelectArgs a) {
       a.tau[row_g] = __uint_as_float(0x7fc00000u);
       a.lognorm[row_g] = 0.f;
       if (a.nsel) a.nsel[row_g] = 0;
+      if (a.passes) a.passes[row_g] = 0;
     }
     if (a.mask)
       for (int x = g; x < nbw; x += 16) a.mask[row_g * nbw + x] = 0u;
   } else {
-    const EntmaxOut e = entmax_solve<NPL, 16>(u, nc, ca);
+    const EntmaxOut e = entmax_solve<NPL, 16>(u, nc, ca, a.nsel != nullptr);
     write_rows16<NPL>(a, row_g, u, nc, e, ca, uni);
   }
   __syncthreads();
@@ -349,7 +354,7 @@ __global__ __launch_bounds__(64) void select_generic_kernel(SelectArgs a) {
     const int b = l + 64 * k;
     u[k] = b < nc ? ca.u_of(dot_row<T>(qs, kb + (size_t)b * D, D)) : -INFINITY;
   }
-  const EntmaxOut e = entmax_solve<NPL, 64>(u, nc, ca);
+  const EntmaxOut e = entmax_solve<NPL, 64>(u, nc, ca, a.nsel != nullptr);
   const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
   uint32_t* tb = a.tile_bits + (bh * ntile + i / DASH_QTILE) * nbw;
   write_row_selection<NPL>(a, row_g, u, nc, e, ca, nullptr, tb);

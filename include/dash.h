@@ -88,6 +88,8 @@ typedef struct {
  *                                rows' selected blocks plus, when causal, the tile's own
  *                                blocks
  *   tile_bits[B,H,ntile,nbw]u32  the same set as a bit mask
+ *   passes   [B,H,T]        i32  passes over the row's scores the threshold solve took
+ *                                (may be NULL; 0 for rows without candidates)
  */
 typedef struct {
   float* tau;
@@ -97,13 +99,14 @@ typedef struct {
   int32_t* tile_cnt;
   int32_t* tile_blk;
   uint32_t* tile_bits;
+  int32_t* passes;
 } dash_sel;
 
 /* Query rows per Stage-2 tile (the granularity of tile_cnt / tile_blk). */
 int32_t dash_query_tile(void);
 
-/* Element counts of the seven dash_sel buffers, in struct order. */
-dash_status dash_sel_sizes(const dash_params* p, size_t out_elems[7]);
+/* Element counts of the eight dash_sel buffers, in struct order. */
+dash_status dash_sel_sizes(const dash_params* p, size_t out_elems[8]);
 
 /* Bytes of device workspace dash_fwd / dash_bwd need (dash_fwd: 0 unless T is not a multiple of 64). */
 size_t dash_fwd_workspace_bytes(const dash_params* p);

@@ -112,7 +112,7 @@ def test_sel_sizes(L):
     p = _params(T=1088)
     sizes = _lib.sel_sizes(p)
     nb, nbw, nt = 17, 1, 9
-    assert sizes == [2 * 1088, 2 * 1088, 2 * 1088, 2 * 1088 * nbw, 2 * nt, 2 * nt * nb, 2 * nt * nbw]
+    assert sizes == [2 * 1088, 2 * 1088, 2 * 1088, 2 * 1088 * nbw, 2 * nt, 2 * nt * nb, 2 * nt * nbw, 2 * 1088]
     assert _lib.query_tile() == 128
     with pytest.raises(_lib.DashError) as e:
         _lib.sel_sizes(_params(D=32))
@@ -239,7 +239,7 @@ def test_partial_last_block_validation(L):
     assert need > 0 and L.dash_fwd_workspace_bytes(ctypes.byref(_params())) == 0
     assert _fwd(L, p) == _lib.DASH_EWORKSPACE
     assert L.dash_bwd_workspace_bytes(ctypes.byref(p)) > L.dash_bwd_workspace_bytes(ctypes.byref(_params(T=128)))
-    sizes = (ctypes.c_size_t * 7)()
+    sizes = (ctypes.c_size_t * 8)()
     assert L.dash_sel_sizes(ctypes.byref(p), sizes) == _lib.DASH_OK
     assert sizes[0] == 1 * 2 * 128  # rows laid out as whole blocks
     # the stage entry points keep whole blocks
