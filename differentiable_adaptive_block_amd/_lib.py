@@ -35,6 +35,8 @@ EXPORTS = [
     "dash_bwd_no_pool",
     "dash_pool_attn_bwd_workspace_bytes",
     "dash_pool_attn_bwd",
+    "dash_bwd_learned_workspace_bytes",
+    "dash_bwd_learned",
     "dash_decode_workspace_bytes",
     "dash_decode",
     "dash_cache_append",
@@ -128,6 +130,11 @@ def load() -> ctypes.CDLL:
     L.dash_pool_attn_bwd_workspace_bytes.argtypes = [P(DashParams)]
     L.dash_pool_attn_bwd.restype = ctypes.c_int
     L.dash_pool_attn_bwd.argtypes = [P(DashParams), vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.dash_bwd_learned_workspace_bytes.restype = ctypes.c_size_t
+    L.dash_bwd_learned_workspace_bytes.argtypes = [P(DashParams)]
+    L.dash_bwd_learned.restype = ctypes.c_int
+    L.dash_bwd_learned.argtypes = [P(DashParams), vp, vp, vp, vp, vp, vp, vp, P(DashSel), vp, vp, vp, vp, vp, vp, vp,
+                                   ctypes.c_size_t, vp]
     L.dash_decode_workspace_bytes.restype = ctypes.c_size_t
     L.dash_decode_workspace_bytes.argtypes = [P(DashDecodeParams)]
     L.dash_decode.restype = ctypes.c_int
@@ -269,3 +276,13 @@ def decode_static_max_bytes() -> int:
 
 def decode_static(p: DashDecodeParams, q, kc, vc, kbar, o, lse, nsel, tau, mask, stream) -> None:
     check(load().dash_decode_static(ctypes.byref(p), q, kc, vc, kbar, o, lse, nsel, tau, mask, stream))
+
+
+def bwd_learned_workspace_bytes(p: DashParams) -> int:
+    return int(load().dash_bwd_learned_workspace_bytes(ctypes.byref(p)))
+
+
+def bwd_learned(p: DashParams, q, k, v, o, lse, dout, kbar, sel: DashSel, w, dq, dk, dv, dkbar, dw, ws, ws_bytes,
+                stream) -> None:
+    check(load().dash_bwd_learned(ctypes.byref(p), q, k, v, o, lse, dout, kbar, ctypes.byref(sel), w, dq, dk, dv,
+                                  dkbar, dw, ws, ws_bytes, stream))

@@ -171,19 +171,19 @@ def backward(q, k, v, o, lse, dout, kbar, sel: Selection, p: _lib.DashParams, su
         _lib.bwd_gqa(p, Hkv, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(kbar), sel.as_c(),
                      _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dkbar), _ptr(ws), wsb, _stream(dev))
         return dict(dq=dq, dk=dk, dv=dv, dkbar=dkbar)
-    wsb = _lib.bwd_workspace_bytes(p)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     if summariser_w is None:
+        wsb = _lib.bwd_workspace_bytes(p)
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
         _lib.bwd(p, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(kbar), sel.as_c(), _ptr(dq),
                  _ptr(dk), _ptr(dv), _ptr(dkbar), _ptr(ws), wsb, _stream(dev))
         return dict(dq=dq, dk=dk, dv=dv, dkbar=dkbar)
     _require(summariser_w, "summariser_w", (p.H, p.D), torch.float32)
-    _lib.bwd_no_pool(p, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(kbar), sel.as_c(), _ptr(dq),
-                     _ptr(dk), _ptr(dv), _ptr(dkbar), _ptr(ws), wsb, _stream(dev))
     dw = torch.empty((p.H, p.D), dtype=torch.float32, device=dev)
-    wsb2 = _lib.pool_attn_bwd_workspace_bytes(p)
-    ws2 = torch.empty(max(wsb2, 1), dtype=torch.uint8, device=dev)
-    _lib.pool_attn_bwd(p, _ptr(k), _ptr(summariser_w), _ptr(dkbar), _ptr(dk), _ptr(dw), _ptr(ws2), wsb2, _stream(dev))
+    wsb = _lib.bwd_learned_workspace_bytes(p)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    _lib.bwd_learned(p, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(kbar), sel.as_c(),
+                     _ptr(summariser_w), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dkbar), _ptr(dw), _ptr(ws), wsb,
+                     _stream(dev))
     return dict(dq=dq, dk=dk, dv=dv, dkbar=dkbar, dw=dw)
 
 

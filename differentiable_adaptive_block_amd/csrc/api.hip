@@ -107,8 +107,10 @@ size_t bwd_ws_layout(const dash_params* p, size_t off[4]) {
   auto take = [&](size_t bytes) { size_t r = o; o += (bytes + 255) & ~size_t(255); return r; };
   off[0] = take(BH * T * sizeof(float));               // delta
   off[1] = take(BH * T * D * sizeof(float));           // dq accumulator
-  off[2] = take(BH * nt * nb * DASH_QTILE * sizeof(float));  // G
-  off[3] = take(BH * nt * nb * DASH_QTILE * sizeof(float));  // prior
+  // listed-entry room per head; the fp32 path keeps one value per (row, block) instead
+  const size_t per_head = p->dtype == DASH_F32 ? T * nb : bwd_entries_per_head(p->causal, (int)nb, (int)nt) * DASH_QTILE;
+  off[2] = take(BH * per_head * sizeof(float));  // G (fp32 path: coarse-scaled dz)
+  off[3] = take(BH * per_head * sizeof(float));  // prior
   return o;
 }
 
@@ -190,19 +192,9 @@ dash_status dash_sel_sizes(const dash_params* p, size_t out[8]) {
   return DASH_OK;
 }
 
-// Padded copies for a ragged T: rows of Tp = whole blocks per head.
-// Forward: q, k, v, o (dtype) and lse.  Backward: q, k, v, o, dout, dq, dk,
-// dv and lse, after the whole-block backward's own workspace.
-size_t ragged_fwd_layout(const dash_params* p, size_t off[5]) {
-  const dash_params pp = padded(p);
-  const size_t BH = (size_t)p->B * p->H, rows = BH * pp.T, mat = rows * p->D * elem_bytes(p);
-  size_t o = 0;
-  auto take = [&](size_t bytes) { size_t r = o; o += (bytes + 255) & ~size_t(255); return r; };
-  for (int i = 0; i < 4; ++i) off[i] = take(mat);
-  off[4] = take(rows * sizeof(float));
-  return o;
-}
-
+// Padded copies for the backward of a ragged T (rows of Tp = whole blocks
+// per head): q, k, v, o, dout, dq, dk, dv and lse, after the whole-block
+// backward's own workspace.
 size_t ragged_bwd_layout(const dash_params* p, size_t off[14]) {
   const dash_params pp = padded(p);
   size_t o = bwd_ws_layout(&pp, off);  // off[0..3]
@@ -214,9 +206,8 @@ size_t ragged_bwd_layout(const dash_params* p, size_t off[14]) {
 }
 
 size_t dash_fwd_workspace_bytes(const dash_params* p) {
-  if (!p || check_params(p, true, true) != DASH_OK || !is_ragged(p)) return 0;
-  size_t off[5];
-  return ragged_fwd_layout(p, off);
+  (void)p;
+  return 0;  // a partial last block is handled inside the kernels
 }
 
 size_t dash_bwd_workspace_bytes(const dash_params* p) {
@@ -243,7 +234,7 @@ dash_status dash_pool(const dash_params* p, const void* k, void* kbar, void* str
 // Stage 1 (scores, entmax, masks, tile lists) from summaries already in kbar;
 // grp query heads per key/value head (their tile lists are the group's union).
 static dash_status select_from_kbar(const dash_params* p, const void* q, const void* kbar, const dash_sel* sel,
-                                    hipStream_t st, int grp = 1) {
+                                    hipStream_t st, int grp = 1, int Tr = -1) {
   const int BH = p->B * p->H;
   const int nb = p->T / DASH_BLOCK;
   hipError_t e;
@@ -253,6 +244,7 @@ static dash_status select_from_kbar(const dash_params* p, const void* q, const v
   sa.q = q;
   sa.kbar = kbar;
   sa.T = p->T;
+  sa.Tr = Tr < 0 ? p->T : Tr;
   sa.D = p->D;
   sa.causal = p->causal;
   sa.grp = grp;
@@ -319,8 +311,10 @@ dash_status dash_pool_attn_bwd(const dash_params* p, const void* k, const float*
 }
 
 static dash_status attend_common(const dash_params* p, const void* q, const void* k, const void* v,
-                                 const void* kbar, const dash_sel* sel, void* o, float* lse, void* stream, int grp) {
+                                 const void* kbar, const dash_sel* sel, void* o, float* lse, void* stream, int grp,
+                                 int Tr = -1) {
   FwdArgs fa;
+  fa.Tr = Tr < 0 ? p->T : Tr;
   fa.q = q;
   fa.k = k;
   fa.v = v;
@@ -382,37 +376,26 @@ dash_status dash_fwd(const dash_params* p, const void* q, const void* k, const v
   if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(lse) || !ok_ptr(kbar))
     return fail(DASH_EINVAL, "q, k, v, o, lse and kbar must be non-null and 16-byte aligned");
   if ((s = check_sel(sel, true)) != DASH_OK) return s;
+  (void)workspace;  // the forward needs none (see dash_fwd_workspace_bytes)
+  (void)workspace_bytes;
   if (!is_ragged(p)) {
     if ((s = dash_fwd_select(p, q, k, kbar, sel, stream)) != DASH_OK) return s;
     return dash_fwd_attend(p, q, k, v, kbar, sel, o, lse, stream);
   }
-  // a partial last block: the whole-block path on padded copies
-  size_t off[5];
-  const size_t need = ragged_fwd_layout(p, off);
-  if (workspace_bytes < need) return fail(DASH_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
-  if (!ok_ptr(workspace)) return fail(DASH_EINVAL, "workspace must be non-null and 16-byte aligned");
-  char* ws = static_cast<char*>(workspace);
+  // a partial last block: the kernels take the tensors as they are (T rows
+  // per head) and treat the block as whole, its missing rows as zeros
   const dash_params pp = padded(p);
-  const int BH = p->B * p->H, rb = p->D * (int)elem_bytes(p);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
-  const void* src[3] = {q, k, v};
-  for (int i = 0; i < 3; ++i)
-    if ((e = launch_pad_rows(src[i], ws + off[i], BH, p->T, pp.T, rb, st)) != hipSuccess) return hip_fail(e, "pad");
-  if ((s = dash_fwd_select(&pp, ws + off[0], ws + off[1], kbar, sel, stream)) != DASH_OK) return s;
-  if ((s = dash_fwd_attend(&pp, ws + off[0], ws + off[1], ws + off[2], kbar, sel, ws + off[3],
-                           reinterpret_cast<float*>(ws + off[4]), stream)) != DASH_OK)
-    return s;
-  if ((e = launch_unpad_rows(ws + off[3], o, BH, p->T, pp.T, rb, st)) != hipSuccess) return hip_fail(e, "unpad");
-  if ((e = launch_unpad_f32(reinterpret_cast<float*>(ws + off[4]), lse, BH, p->T, pp.T, st)) != hipSuccess)
-    return hip_fail(e, "unpad");
-  return DASH_OK;
+  if ((e = launch_pool(k, kbar, p->B * p->H, pp.T, p->D, p->dtype, st, p->T)) != hipSuccess) return hip_fail(e, "pool");
+  if ((s = select_from_kbar(&pp, q, kbar, sel, st, 1, p->T)) != DASH_OK) return s;
+  return attend_common(&pp, q, k, v, kbar, sel, o, lse, stream, 1, p->T);
 }
 
 static dash_status bwd_common(const dash_params* p, const void* q, const void* k, const void* v, const void* o,
                               const float* lse, const void* dout, const void* kbar, const dash_sel* sel, void* dq,
                               void* dk, void* dv, float* dkbar, void* workspace, size_t workspace_bytes, void* stream,
-                              float pool_scale) {
+                              float pool_scale, int dk_f32 = 0) {
   dash_status s = check_params(p);
   if (s != DASH_OK) return s;
   if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(lse) || !ok_ptr(dout) || !ok_ptr(kbar) ||
@@ -451,6 +434,7 @@ static dash_status bwd_common(const dash_params* p, const void* q, const void* k
   ba.causal = p->causal;
   ba.fine_scale = p->fine_scale;
   ba.pool_scale = pool_scale;
+  ba.dk_f32 = dk_f32;
   ba.grp = 1;
   ba.gsum = nullptr;
   ba.phbuf = nullptr;
@@ -465,11 +449,12 @@ static size_t bwd_gqa_ws_layout(const dash_params* p, int32_t kv_heads, size_t o
   const size_t grp = (size_t)p->H / kv_heads;
   size_t o = base;
   auto take = [&](size_t bytes) { size_t r = o; o += (bytes + 255) & ~size_t(255); return r; };
-  off[4] = take(BH / grp * nt * nb * DASH_QTILE * sizeof(float));  // G summed over each group
+  const size_t ent = bwd_entries_per_head(p->causal, (int)nb, (int)nt);
+  off[4] = take(BH / grp * ent * DASH_QTILE * sizeof(float));  // G summed over each group
   off[5] = take(BH * T * D * 2);                                   // dK per query head
   off[6] = take(BH * T * D * 2);                                   // dV per query head
   off[7] = take(BH * nb * D * sizeof(float));                      // dkbar per query head
-  off[8] = take(BH * nt * nb * DASH_QTILE * sizeof(float));         // each row's own log2 p
+  off[8] = take(BH * ent * DASH_QTILE * sizeof(float));             // each row's own log2 p
   return o;
 }
 
@@ -529,6 +514,7 @@ dash_status dash_bwd_gqa(const dash_params* p, int32_t kv_heads, const void* q, 
   ba.grp = p->H / kv_heads;
   ba.fine_scale = p->fine_scale;
   ba.pool_scale = 1.f / DASH_BLOCK;
+  ba.dk_f32 = 0;
   ba.ca = make_ca(p->alpha, p->coarse_scale);
   hipError_t e = launch_bwd_gqa(ba, dk, dv, dkbar, (hipStream_t)stream);
   return e == hipSuccess ? DASH_OK : hip_fail(e, "grouped-query backward");
@@ -577,6 +563,42 @@ dash_status dash_bwd_no_pool(const dash_params* p, const void* q, const void* k,
                              const float* lse, const void* dout, const void* kbar, const dash_sel* sel, void* dq,
                              void* dk, void* dv, float* dkbar, void* workspace, size_t workspace_bytes, void* stream) {
   return bwd_common(p, q, k, v, o, lse, dout, kbar, sel, dq, dk, dv, dkbar, workspace, workspace_bytes, stream, 0.f);
+}
+
+size_t dash_bwd_learned_workspace_bytes(const dash_params* p) {
+  if (check_params(p) != DASH_OK) return 0;
+  size_t off[4];
+  const size_t bw = (bwd_ws_layout(p, off) + 255) & ~size_t(255);
+  const size_t dkf = ((size_t)p->B * p->H * p->T * p->D * sizeof(float) + 255) & ~size_t(255);
+  return bw + dkf + dash_pool_attn_bwd_workspace_bytes(p);
+}
+
+dash_status dash_bwd_learned(const dash_params* p, const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, const void* kbar, const dash_sel* sel, const float* w,
+                             void* dq, void* dk, void* dv, float* dkbar, float* dw, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  dash_status s = check_params(p);
+  if (s != DASH_OK) return s;
+  if (!ok_ptr(w) || !ok_ptr(dw)) return fail(DASH_EINVAL, "w and dw must be non-null and 16-byte aligned");
+  const size_t need = dash_bwd_learned_workspace_bytes(p);
+  if (workspace_bytes < need) return fail(DASH_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (!ok_ptr(workspace)) return fail(DASH_EINVAL, "workspace must be non-null and 16-byte aligned");
+  size_t off[4];
+  const size_t bw = (bwd_ws_layout(p, off) + 255) & ~size_t(255);
+  const size_t dkf = ((size_t)p->B * p->H * p->T * p->D * sizeof(float) + 255) & ~size_t(255);
+  char* ws = static_cast<char*>(workspace);
+  // bf16: the Stage-2 and Stage-1 terms of dK stay unrounded in the workspace
+  // and the summariser's term is added before the one rounding; fp32: dK
+  // itself holds them
+  const bool f32tmp = p->dtype == DASH_BF16;
+  void* dk_stage = f32tmp ? static_cast<void*>(ws + bw) : dk;
+  if ((s = bwd_common(p, q, k, v, o, lse, dout, kbar, sel, dq, dk_stage, dv, dkbar, ws, bw, stream, 0.f,
+                      f32tmp ? 1 : 0)) != DASH_OK)
+    return s;
+  hipError_t e = launch_pool_attn_bwd(k, w, dkbar, dk, dw, reinterpret_cast<float*>(ws + bw + dkf), p->B, p->H, p->T,
+                                      p->D, p->dtype, (hipStream_t)stream,
+                                      f32tmp ? reinterpret_cast<const float*>(ws + bw) : nullptr);
+  return e == hipSuccess ? DASH_OK : hip_fail(e, "attention pooling backward");
 }
 
 static dash_status check_decode_params(const dash_decode_params* p) {

@@ -48,8 +48,13 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const T* __restrict__ o,
 
 // ---------------------------------------------------------------------------- dQ (fine), G, priors
 
-__device__ __forceinline__ size_t gidx(size_t bh, int ntile, int tile, int nb, int e, int row_in_tile) {
-  return (((bh * ntile + tile) * (size_t)nb + e) * DASH_QTILE) + row_in_tile;
+// Slot of (query tile, listed entry e, row of the tile) in the per-entry
+// buffers (G, prior): each head stores its tiles' entries one after the
+// other, tile t taking room for the most entries its list can hold
+// (bwd_tile_base in attn_bwd.h: the lower triangle when causal).
+__device__ __forceinline__ size_t gidx(size_t bh, int ntile, int tile, int nb, int e, int row_in_tile, int causal) {
+  return ((bh * bwd_entries_per_head(causal, nb, ntile) + bwd_tile_base(causal, nb, tile) + e) * DASH_QTILE) +
+         row_in_tile;
 }
 
 // Query-tile-major like the forward: workgroup = 4 waves = 128 query rows,
@@ -141,7 +146,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int en = e0 + acc_row32(r, l);
-            if (en < cnt) a.phbuf[gidx(bh, ntile, tile, nb, en, w * 32 + j)] = own[r];
+            if (en < cnt) a.phbuf[gidx(bh, ntile, tile, nb, en, w * 32 + j, a.causal)] = own[r];
           }
         }
         pacc = prior_chunk32_group<D>(KB, list, cnt, e0, reinterpret_cast<const bf16_t*>(a.q) + (bh0 * a.T + i) * D,
@@ -159,7 +164,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   };
   auto put_g = [&](int e, float g, float p2) {
     if (h == 0) {
-      const size_t gi = gidx(bh, ntile, tile, nb, e, w * 32 + j);
+      const size_t gi = gidx(bh, ntile, tile, nb, e, w * 32 + j, a.causal);
       a.gbuf[gi] = g;
       a.pbuf[gi] = p2;
     }
@@ -423,12 +428,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
       s_pr0 = -INFINITY; s_dz0 = 0.f;
       s_pr1 = -INFINITY; s_dz1 = 0.f;
       if (itm[n][1] >= 0) {
-        const size_t gi = gidx(bh, ntile, t, nb, itm[n][1], row);
+        const size_t gi = gidx(bh, ntile, t, nb, itm[n][1], row, a.causal);
         s_pr0 = a.pbuf[gi] - ls;  // -inf stays -inf
         s_dz0 = a.gbuf[gi];
       }
       if (itm[n][2] >= 0) {
-        const size_t gi = gidx(bh, ntile, t, nb, itm[n][2], row);
+        const size_t gi = gidx(bh, ntile, t, nb, itm[n][2], row, a.causal);
         s_pr1 = a.pbuf[gi] - ls;
         s_dz1 = a.gbuf[gi];
       }
@@ -600,6 +605,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
       for (int r4 = 0; r4 < 4; ++r4) {
         const int d = 32 * dt + 8 * r4 + 4 * h;
         uint32_t pv2[2], pk2[2];
+        float kf4[4];
 #pragma unroll
         for (int e2 = 0; e2 < 2; ++e2) {
           float v0[2], k0[2];
@@ -608,13 +614,22 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
             const int r = 4 * r4 + 2 * e2 + e;
             const int ri = (dt * 16 + r) * 64 + l;
             v0[e] = dva[dt][r] + red1[ri];
-            k0[e] = (dka[dt][r] + red2[ri]) * a.fine_scale + kbg[kb][d + 2 * e2 + e] * a.pool_scale;
+            // the Stage-2 and Stage-1 terms rounded to fp32 first, then the
+            // pooling share added (exact: a power-of-two multiple of dkbar), so
+            // a later Stage-0 term added to the unrounded fp32 value
+            // (dk_f32) takes the same rounding steps as this one
+            k0[e] = fmaf(kbg[kb][d + 2 * e2 + e], a.pool_scale, __fmul_rn(dka[dt][r] + red2[ri], a.fine_scale));
+            kf4[2 * e2 + e] = k0[e];
           }
           pv2[e2] = (uint32_t)f2bf(v0[0]) | ((uint32_t)f2bf(v0[1]) << 16);
           pk2[e2] = (uint32_t)f2bf(k0[0]) | ((uint32_t)f2bf(k0[1]) << 16);
         }
         *reinterpret_cast<uint2*>(dV + (size_t)key * D + d) = make_uint2(pv2[0], pv2[1]);
-        *reinterpret_cast<uint2*>(dK + (size_t)key * D + d) = make_uint2(pk2[0], pk2[1]);
+        if (a.dk_f32)
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.dk) + (bh * a.T + key) * D + d) =
+              make_float4(kf4[0], kf4[1], kf4[2], kf4[3]);
+        else
+          *reinterpret_cast<uint2*>(dK + (size_t)key * D + d) = make_uint2(pk2[0], pk2[1]);
       }
   }
 }
@@ -665,13 +680,13 @@ __global__ __launch_bounds__(256) void bwd_coarse_kernel(BwdArgs a) {
     if (valid) {
       for (int e = cg; e < cnt; e += 8) {
         if (a.causal && list[e] >= own) continue;
-        const size_t gi = gidx(bh, ntile, tile, nb, e, rt);
+        const size_t gi = gidx(bh, ntile, tile, nb, e, rt, a.causal);
         const float lpb2 = a.pbuf[gi];
         const float lp2 = a.phbuf[gi];
         if (lpb2 == -INFINITY || lp2 == -INFINITY) continue;
         const float sv = __builtin_amdgcn_exp2f(am2 * lp2);
         ss += sv;
-        ssg += sv * a.gsum[gidx(bkv, ntile, tile, nb, e, rt)] * __builtin_amdgcn_exp2f(-lpb2) * inv_grp;
+        ssg += sv * a.gsum[gidx(bkv, ntile, tile, nb, e, rt, a.causal)] * __builtin_amdgcn_exp2f(-lpb2) * inv_grp;
       }
     }
     ss = sum8(ss);
@@ -679,14 +694,14 @@ __global__ __launch_bounds__(256) void bwd_coarse_kernel(BwdArgs a) {
     const float ratio = ss > 0.f ? ssg / ss : 0.f;
     if (valid) {
       for (int e = cg; e < cnt; e += 8) {
-        const size_t gi = gidx(bh, ntile, tile, nb, e, rt);
+        const size_t gi = gidx(bh, ntile, tile, nb, e, rt, a.causal);
         float dz = 0.f;
         if (!(a.causal && list[e] >= own)) {
           const float lpb2 = a.pbuf[gi];
           const float lp2 = a.phbuf[gi];
           if (lpb2 != -INFINITY && lp2 != -INFINITY) {
             const float sv = __builtin_amdgcn_exp2f(am2 * lp2);
-            const float gv = a.gsum[gidx(bkv, ntile, tile, nb, e, rt)] * __builtin_amdgcn_exp2f(-lpb2) * inv_grp;
+            const float gv = a.gsum[gidx(bkv, ntile, tile, nb, e, rt, a.causal)] * __builtin_amdgcn_exp2f(-lpb2) * inv_grp;
             dz = sv * gv - sv * ratio;
           }
         }
@@ -697,7 +712,7 @@ __global__ __launch_bounds__(256) void bwd_coarse_kernel(BwdArgs a) {
   if (valid) {
     for (int e = cg; e < cnt; e += 8) {
       if (a.causal && list[e] >= own) continue;
-      const size_t gi = gidx(bh, ntile, tile, nb, e, rt);
+      const size_t gi = gidx(bh, ntile, tile, nb, e, rt, a.causal);
       const float lp2 = a.pbuf[gi];
       if (lp2 == -INFINITY) continue;
       ss += __builtin_amdgcn_exp2f(am2 * lp2);
@@ -709,7 +724,7 @@ __global__ __launch_bounds__(256) void bwd_coarse_kernel(BwdArgs a) {
   const float ratio = ss > 0.f ? ssg / ss : 0.f;
   if (valid) {
     for (int e = cg; e < cnt; e += 8) {
-      const size_t gi = gidx(bh, ntile, tile, nb, e, rt);
+      const size_t gi = gidx(bh, ntile, tile, nb, e, rt, a.causal);
       float dz = 0.f;
       if (!(a.causal && list[e] >= own)) {
         const float lp2 = a.pbuf[gi];
@@ -735,7 +750,7 @@ __global__ __launch_bounds__(256) void bwd_coarse_kernel(BwdArgs a) {
       const int e = e0 + u;
       dz[u] = 0.f;
       if (e < cnt) {
-        dz[u] = a.gbuf[gidx(bh, ntile, tile, nb, e, rt)];
+        dz[u] = a.gbuf[gidx(bh, ntile, tile, nb, e, rt, a.causal)];
         const bf16_t* kr0 = KB + (size_t)list[e] * D;
 #pragma unroll
         for (int c = 0; c < G / 8; ++c) kr[u][c] = *reinterpret_cast<const uint4*>(kr0 + 8 * c);
@@ -954,8 +969,8 @@ __global__ __launch_bounds__(256) void bwd_gqa_gsum_kernel(BwdArgs a) {
   for (int x = threadIdx.x; x < cnt * DASH_QTILE; x += blockDim.x) {
     const int e = x / DASH_QTILE, rt = x % DASH_QTILE;
     float g = 0.f;
-    for (int h = 0; h < a.grp; ++h) g += a.gbuf[gidx(bh0 + h, ntile, tile, nb, e, rt)];
-    a.gsum[gidx(bkv, ntile, tile, nb, e, rt)] = g;
+    for (int h = 0; h < a.grp; ++h) g += a.gbuf[gidx(bh0 + h, ntile, tile, nb, e, rt, a.causal)];
+    a.gsum[gidx(bkv, ntile, tile, nb, e, rt, a.causal)] = g;
   }
 }
 

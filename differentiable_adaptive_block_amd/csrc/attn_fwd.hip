@@ -10,7 +10,8 @@
 // ---------------------------------------------------------------------------- bf16 MFMA kernel
 //
 // Workgroup = 4 waves = one query tile of 128 rows; wave w owns rows
-// 32w..32w+31 of the tile.  The workgroup walks the tile's block list
+// 32w..32w+31 of the tile (grouped-query heads: 4 x 32 / HG rows of the
+// group's HG heads, see below).  The workgroup walks the tile's block list
 // (ascending).  Per wave and block:
 //   S^T (64 keys x 32 queries) = K_b Q^T    2 x (D/16) MFMA 32x32x16
 //   online softmax in log2 units, the prior log2 p_ib added per row
@@ -33,13 +34,23 @@
 // The per-(row, block) prior is recomputed from the Stage-1 score
 // arithmetic (coarse_acc_chunk) for 32 listed blocks at a time and kept in
 // registers.
-// GQA: grouped-query heads (a.grp > 1): keys, values and summaries are the
-// KV head's, and the prior is the group's aggregated one (prior_chunk32_group).
-template <int D, bool GQA>
+//
+// Grouped-query heads (HG = a.grp > 1 query heads per key/value head): a
+// wave's 32 query columns are the HG heads of the group at 32 / HG
+// consecutive rows (column j: head j / (32 / HG), row j % (32 / HG)), so
+// the group's heads share every K/V tile copy and operand read.  Keys,
+// values and summaries are the KV head's; the prior is the group's
+// aggregated one, log pbar with pbar the mean of the heads' p: each column
+// computes its own head's p from one score MFMA chain (the Stage-1
+// arithmetic) and the columns of a row add theirs across lanes
+// (prior_chunk32_heads).
+template <int D, int HG>
 __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
   constexpr int CH = D / 8;          // 16-byte chunks per row
   constexpr int KS = D / 16;         // k-steps of the S product
   constexpr int NDT = D / 32;        // 32-row d tiles of O^T
+  constexpr int RPW = 32 / HG;       // rows per wave
+  constexpr int RPG = 4 * RPW;       // rows per workgroup
   // one object per buffer, so that reads of one buffer are not ordered
   // behind the copy into the other
   __shared__ __attribute__((aligned(16))) bf16_t kt0[64 * D];
@@ -51,29 +62,36 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
 
   const int nb = a.T / DASH_BLOCK;
   const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
+  const int nrg = (a.T + RPG - 1) / RPG;  // row groups per head group
   const int nwg = gridDim.x;
   const int wg = blockIdx.x;
   // XCD-aware order: consecutive workgroup ids go round-robin over the 8
   // XCDs; give each XCD a contiguous range of heads so their K/V stay in
-  // that XCD's L2, and start every head with its longest (last) tile.
+  // that XCD's L2, and start every head with its longest (last) rows.
   const int logical = (nwg % 8 == 0) ? (wg % 8) * (nwg / 8) + wg / 8 : wg;
-  const size_t bh = logical / ntile;
-  const int tile = ntile - 1 - (logical % ntile);
+  const size_t bkv = logical / nrg;  // the key/value head (the query head when HG = 1)
+  const int rg = nrg - 1 - (logical % nrg);
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, j = l & 31, h = l >> 5;
-  const int qrow0 = tile * DASH_QTILE + w * 32;
+  const int qrow0 = rg * RPG + w * RPW;  // the wave's first row (all its rows lie in one block)
   const bool active = qrow0 < a.T;
   const int wblk = qrow0 / DASH_BLOCK;
-  const int i = qrow0 + j;
+  const int i = qrow0 + j % RPW;                    // this column's row
+  const size_t bh = bkv * HG + j / RPW;             // and query head
+  const int tile = (rg * RPG) / DASH_QTILE;         // the tile whose block list the group walks
 
-  const bf16_t* Q = reinterpret_cast<const bf16_t*>(a.q) + bh * a.T * D;
-  const size_t bkv = GQA ? bh / a.grp : bh;  // the key/value head
-  const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + bkv * a.T * D;
-  const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + bkv * a.T * D;
+  const bf16_t* Q = reinterpret_cast<const bf16_t*>(a.q) + bh * a.Tr * D;
+  const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + bkv * a.Tr * D;
+  const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + bkv * a.Tr * D;
   const bf16_t* KB = reinterpret_cast<const bf16_t*>(a.kbar) + bkv * nb * D;
-  const int* glist = a.tile_blk + (bh * ntile + tile) * nb;
-  const int cnt = a.tile_cnt[bh * ntile + tile];
+  // a partial last block (a.Tr < a.T): its rows past the tensor are zero in
+  // the LDS tiles, zero queries, and never written out
+  const int part_blk = a.Tr < a.T ? nb - 1 : -1;
+  const int part_rows = a.Tr - (nb - 1) * DASH_BLOCK;
+  // the heads of a group share their tile lists (the union of their supports)
+  const int* glist = a.tile_blk + (bkv * HG * ntile + tile) * nb;
+  const int cnt = a.tile_cnt[bkv * HG * ntile + tile];
   const CoarseArith ca = a.ca;
   const float sl2 = a.fine_scale * LOG2E_F;
   // The block list is staged in LDS: a global (vector-memory) load inside
@@ -87,7 +105,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
   float tau_i = 0.f, ln_i = 0.f;
   if (active) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qb[s] = load8(Q + (size_t)i * D + 16 * s + 8 * h);
+    for (int s = 0; s < KS; ++s) qb[s] = i < a.Tr ? load8(Q + (size_t)i * D + 16 * s + 8 * h) : bf16x8{};
     tau_i = a.tau[bh * a.T + i];
     ln_i = a.lognorm[bh * a.T + i];
   }
@@ -106,22 +124,27 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
   kcp.init(wu, l);
   vcp.init(wu, l);
   auto copy_block = [&](int b, bf16_t* kd, bf16_t* vd) {
-    const size_t o = (size_t)__builtin_amdgcn_readfirstlane(b) * DASH_BLOCK * D;
-    kcp.copy(K + o, kd, wu);
-    vcp.copy(V + o, vd, wu);
+    const int bu = __builtin_amdgcn_readfirstlane(b);
+    const size_t o = (size_t)bu * DASH_BLOCK * D;
+    const int rows = bu == part_blk ? part_rows : DASH_BLOCK;
+    kcp.copy(K + o, kd, wu, rows);
+    vcp.copy(V + o, vd, wu, rows);
+  };
+  // After the copy of a partial block has landed (and a barrier): its rows
+  // past the tensor are set to zero (the descriptor kept the copy from
+  // reading them); the caller's next barrier publishes the zeros.
+  auto zero_tail = [&](bf16_t* kd, bf16_t* vd) {
+    for (int x = tid; x < (DASH_BLOCK - part_rows) * CH; x += 256) {
+      *reinterpret_cast<uint4*>(kd + part_rows * D + 8 * x) = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(vd + part_rows * D + 8 * x) = make_uint4(0, 0, 0, 0);
+    }
   };
 
   f32x16 pacc;
   auto prior_chunk = [&](int e0) {
     if (!active) return;
-    if constexpr (GQA) {
-      const size_t bh0 = bkv * a.grp;  // the group's first query head
-      pacc = prior_chunk32_group<D>(KB, list, cnt, e0, reinterpret_cast<const bf16_t*>(a.q) + (bh0 * a.T + i) * D,
-                                    (size_t)a.T * D, a.tau + bh0 * a.T + i, a.lognorm + bh0 * a.T + i, a.T, a.grp,
-                                    ca, a.causal, wblk);
-    } else {
-      pacc = prior_chunk32<D>(KB, list, cnt, e0, qb, ca, tau_i, ln_i, a.causal, wblk);
-    }
+    if constexpr (HG > 1) pacc = prior_chunk32_heads<D, HG>(KB, list, cnt, e0, qb, ca, tau_i, ln_i, a.causal, wblk);
+    else pacc = prior_chunk32<D>(KB, list, cnt, e0, qb, ca, tau_i, ln_i, a.causal, wblk);
   };
   auto prior_of = [&](int e) -> float { return prior_pick(pacc, e); };
 
@@ -244,11 +267,19 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
       if ((e & 31) == 0) prior_chunk(e);
       tile_copies_done();
       __syncthreads();  // block e in buffers 0; everyone is done with buffers 1
+      if (list[e] == part_blk) {  // the partial last block: the last entry of the list
+        zero_tail(kt0, vt0);
+        __syncthreads();
+      }
       if (e + 1 < cnt) copy_block(list[e + 1], kt1, vt1);
       if (active) block_step(e, kt0, vt0);
       if (e + 1 >= cnt) break;
       tile_copies_done();
       __syncthreads();  // block e+1 in buffers 1; everyone is done with buffers 0
+      if (list[e + 1] == part_blk) {
+        zero_tail(kt1, vt1);
+        __syncthreads();
+      }
       if (e + 2 < cnt) copy_block(list[e + 2], kt0, vt0);
       if (active) block_step(e + 1, kt1, vt1);
     }
@@ -272,17 +303,17 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
         for (int x = 0; x < 4; ++x) o4[x] = (__bf16)(oacc[dt][4 * r4 + x] * inv);
         *reinterpret_cast<bf16x4*>(&ost[j * OP + d]) = o4;
       }
-    if (h == 0) a.lse[bh * a.T + i] = (mrow + __builtin_amdgcn_logf(ltot)) * LN2_F;
+    if (h == 0 && i < a.Tr) a.lse[bh * a.Tr + i] = (mrow + __builtin_amdgcn_logf(ltot)) * LN2_F;
   }
   __syncthreads();
   if (active) {
-    bf16_t* O = reinterpret_cast<bf16_t*>(a.o) + bh * a.T * D;
 #pragma unroll
     for (int it = 0; it < 32 * CH / 64; ++it) {
       const int idx = it * 64 + l;
-      const int row = idx / CH, ch = idx % CH;
-      *reinterpret_cast<uint4*>(O + (size_t)(qrow0 + row) * D + ch * 8) =
-          *reinterpret_cast<const uint4*>(ost + row * OP + ch * 8);
+      const int col = idx / CH, ch = idx % CH;  // staged column: head col / RPW, row col % RPW
+      const int row = qrow0 + col % RPW;
+      bf16_t* O = reinterpret_cast<bf16_t*>(a.o) + ((bkv * HG + col / RPW) * a.Tr + row) * D;
+      if (row < a.Tr) *reinterpret_cast<uint4*>(O + ch * 8) = *reinterpret_cast<const uint4*>(ost + col * OP + ch * 8);
     }
   }
 }
@@ -300,10 +331,11 @@ __global__ __launch_bounds__(64) void fwd_generic_kernel(FwdArgs a) {
   const int nb = a.T / DASH_BLOCK;
   const size_t bh = blockIdx.y;
   const int i = blockIdx.x;
+  if (i >= a.Tr) return;  // a row past the tensor (partial last block): nothing to write
   const int l = lane_id();
-  const T* q = reinterpret_cast<const T*>(a.q) + (bh * a.T + i) * D;
-  const T* K = reinterpret_cast<const T*>(a.k) + bh * a.T * D;
-  const T* V = reinterpret_cast<const T*>(a.v) + bh * a.T * D;
+  const T* q = reinterpret_cast<const T*>(a.q) + (bh * a.Tr + i) * D;
+  const T* K = reinterpret_cast<const T*>(a.k) + bh * a.Tr * D;
+  const T* V = reinterpret_cast<const T*>(a.v) + bh * a.Tr * D;
   const T* KB = reinterpret_cast<const T*>(a.kbar) + bh * nb * D;
   for (int d = l; d < D; d += 64) qs[d] = to_f<T>(q[d]);
   __syncthreads();
@@ -321,8 +353,8 @@ __global__ __launch_bounds__(64) void fwd_generic_kernel(FwdArgs a) {
       if (pr == -INFINITY) continue;
     }
     const int key = b * DASH_BLOCK + l;
-    float s = dot_row<T>(qs, K + (size_t)key * D, D) * a.fine_scale + pr;
-    if (a.causal && key > i) s = -INFINITY;
+    // keys after the row (causal) include every key past the tensor
+    float s = (a.causal && key > i) ? -INFINITY : dot_row<T>(qs, K + (size_t)key * D, D) * a.fine_scale + pr;
     const float mx = wave_max(s);
     const float mn = fmaxf(m, mx);
     const float rs = expf(m - mn);
@@ -333,29 +365,37 @@ __global__ __launch_bounds__(64) void fwd_generic_kernel(FwdArgs a) {
     __syncthreads();
     o0 *= rs;
     o1 *= rs;
-    for (int kk = 0; kk < DASH_BLOCK; ++kk) {
+    const int nk = min(DASH_BLOCK, a.Tr - b * DASH_BLOCK);  // keys of the block in the tensor
+    for (int kk = 0; kk < nk; ++kk) {
       const T* vr = V + (size_t)(b * DASH_BLOCK + kk) * D;
       o0 = fmaf(pv[kk], to_f<T>(vr[l]), o0);
       if (l + 64 < D) o1 = fmaf(pv[kk], to_f<T>(vr[l + 64]), o1);
     }
     __syncthreads();
   }
-  T* O = reinterpret_cast<T*>(a.o) + (bh * a.T + i) * D;
+  T* O = reinterpret_cast<T*>(a.o) + (bh * a.Tr + i) * D;
   O[l] = from_f<T>(o0 / lsum);
   if (l + 64 < D) O[l + 64] = from_f<T>(o1 / lsum);
-  if (l == 0) a.lse[bh * a.T + i] = m + logf(lsum);
+  if (l == 0) a.lse[bh * a.Tr + i] = m + logf(lsum);
+}
+
+template <int HG>
+static void launch_fwd_hg(const FwdArgs& a, hipStream_t st) {
+  const int rpg = 4 * (32 / HG);
+  const dim3 grid(((a.T + rpg - 1) / rpg) * (a.BH / HG));
+  if (a.D == 128) fwd_mfma_kernel<128, HG><<<grid, 256, 0, st>>>(a);
+  else fwd_mfma_kernel<64, HG><<<grid, 256, 0, st>>>(a);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype, hipStream_t st) {
   if (dtype == 1) {
-    const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
-    dim3 grid(ntile * a.BH);
-    if (a.grp > 1) {
-      if (a.D == 128) fwd_mfma_kernel<128, true><<<grid, 256, 0, st>>>(a);
-      else fwd_mfma_kernel<64, true><<<grid, 256, 0, st>>>(a);
-    } else {
-      if (a.D == 128) fwd_mfma_kernel<128, false><<<grid, 256, 0, st>>>(a);
-      else fwd_mfma_kernel<64, false><<<grid, 256, 0, st>>>(a);
+    if (a.BH % a.grp) return hipErrorInvalidValue;
+    switch (a.grp) {
+      case 1: launch_fwd_hg<1>(a, st); break;
+      case 2: launch_fwd_hg<2>(a, st); break;
+      case 4: launch_fwd_hg<4>(a, st); break;
+      case 8: launch_fwd_hg<8>(a, st); break;
+      default: return hipErrorNotSupported;
     }
   } else {
     if (a.grp > 1) return hipErrorNotSupported;

@@ -12,16 +12,20 @@
 // cache; chunk-summarise stage of the code samples listed by the
 // codewithpapers.app entry for the DashAttention paper).
 //
-// Three decode kernels, all HBM-bound:
-//   decode_select   one 8-wave workgroup per row: u = (alpha-1) * coarse_scale
-//                   * q.kbar_b for every candidate (coalesced GEMV over the
-//                   summaries, loads of the next chunk in flight),
-//                   entmax threshold, compacted ascending list of the selected
+// Four decode kernels, all HBM-bound except the per-row select:
+//   decode_scores   u = (alpha-1) * coarse_scale * q.kbar_b for every candidate
+//                   of every row: a coalesced GEMV over the summaries spread
+//                   over (row, 256-summary chunk) workgroups, each with all
+//                   its loads in flight before its first dot product;
+//   decode_select   one wave per row: entmax threshold over the row's scores,
+//                   mask words, compacted ascending list of the selected
 //                   blocks with their log2 prior, then the last block;
 //   decode_attend   split-KV: workgroup (split s, row) and its 4 waves take list
 //                   entries s*4 + w, stepping by 4*nsplit; each wave streams a
 //                   block's 64 keys and values (16 KB each, contiguous) with
-//                   16-byte loads, 1 KB per wave instruction, online softmax;
+//                   16-byte loads, 1 KB per wave instruction, online softmax,
+//                   the next entry's K requested once the scores are formed
+//                   and its V once the weighted sum is done;
 //                   the 4 waves merge in LDS and write one partial (m, l, o);
 //   decode_combine  merges the nsplit partials of a row (one wave per row).
 #include "kernels.h"
@@ -47,70 +51,72 @@ __device__ __forceinline__ void unpack8(const uint4& r, float (&f)[8]) {
 
 // ---------------------------------------------------------------------------- selection
 
-template <int NPL>
-__global__ __launch_bounds__(512) void decode_select_kernel(DecodeArgs a) {
+// Block scores of every decode row: u_b = (alpha-1) coarse_scale q . kbar_b
+// for the candidates b < (n-1)/64, written to zrow.  grid (chunks, rows):
+// workgroup (c, row) scores summaries DEC_SPW c .. DEC_SPW (c+1) - 1 with
+// 16 lanes per summary row (8 elements each, 4 rows per wave instruction),
+// every load of the workgroup issued before the first dot product.
+#define DEC_UN 16                    // 16-byte loads per lane
+#define DEC_SPW (4 * 4 * DEC_UN)     // summaries per 4-wave workgroup
+__global__ __launch_bounds__(256) void decode_scores_kernel(DecodeArgs a) {
   constexpr int D = 128;
-  constexpr int NW = 8;               // waves
-  constexpr int UN = 8;               // 16-byte loads per lane and chunk
-  constexpr int PER = NW * 4 * UN;    // summaries per chunk
-  __shared__ float us[NPL * 64];
-  const int row = blockIdx.x;
-  const int nbc = a.N / DASH_BLOCK;  // capacity in blocks: row stride of the summaries and the lists
+  const int row = blockIdx.y;
+  const int nbc = a.N / DASH_BLOCK;
   const int n = decode_row_len(a, row);
+  if (n < 1 || n > a.N) return;  // the select kernel writes this row's outputs
+  const int nc = (n - 1) / DASH_BLOCK;  // candidates: the complete blocks before the query's own
+  const int b0 = blockIdx.x * DEC_SPW;
+  if (b0 >= nc) return;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int nbw = (nbc + 31) / 32;   // mask words per row
-  if (n < 1 || n > a.N) {  // length out of range: empty list and mask; the combine writes NaN
-    if (tid == 0) {
-      a.sel_cnt[row] = 0;
-      if (a.nsel) a.nsel[row] = -1;
-      if (a.tau_out) a.tau_out[row] = __uint_as_float(0x7fc00000u);
-    }
-    if (a.mask)
-      for (int x = tid; x < nbw; x += 64 * NW) a.mask[(size_t)row * nbw + x] = 0u;
-    return;
-  }
-  const int own = (n - 1) / DASH_BLOCK;  // the query's block
-  const int nc = own;                    // the complete blocks before it are the candidates
   const bf16_t* q = reinterpret_cast<const bf16_t*>(a.q) + (size_t)row * D;
   const bf16_t* kb = reinterpret_cast<const bf16_t*>(a.kbar) + (size_t)(row / a.grp) * nbc * D;
   const CoarseArith ca = a.ca;
   float qf[8];
   unpack8(*reinterpret_cast<const uint4*>(q + (l & 15) * 8), qf);
-  // 16 lanes per summary row (8 elements each), 4 rows per wave instruction;
-  // chunk k covers rows PER k .. PER k + PER - 1, and the next chunk's loads
-  // are issued before this chunk's dot products
-  const int nchunk = (nc + PER - 1) / PER;
-  auto issue = [&](int ck, uint4 (&R)[UN]) {
+  uint4 R[DEC_UN];
 #pragma unroll
-    for (int x = 0; x < UN; ++x) {
-      const int b = ck * PER + (x * NW + w) * 4 + (l >> 4);
-      R[x] = b < nc ? *reinterpret_cast<const uint4*>(kb + (size_t)b * D + (l & 15) * 8) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto consume = [&](int ck, const uint4 (&R)[UN]) {
-#pragma unroll
-    for (int x = 0; x < UN; ++x) {
-      const int b = ck * PER + (x * NW + w) * 4 + (l >> 4);
-      float kf[8];
-      unpack8(R[x], kf);
-      float part = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) part = fmaf(qf[e], kf[e], part);
-      part = sum16(part);
-      if (b < nc && (l & 15) == 0) us[b] = ca.u_of(part);
-    }
-  };
-  uint4 ra[UN], rb[UN];
-  if (nchunk > 0) issue(0, ra);
-  for (int ck = 0; ck < nchunk; ck += 2) {
-    if (ck + 1 < nchunk) issue(ck + 1, rb);
-    consume(ck, ra);
-    if (ck + 1 >= nchunk) break;
-    if (ck + 2 < nchunk) issue(ck + 2, ra);
-    consume(ck + 1, rb);
+  for (int x = 0; x < DEC_UN; ++x) {
+    const int b = b0 + (x * 4 + w) * 4 + (l >> 4);
+    R[x] = b < nc ? *reinterpret_cast<const uint4*>(kb + (size_t)b * D + (l & 15) * 8) : make_uint4(0, 0, 0, 0);
   }
-  __syncthreads();
-  if (w != 0) return;
+  float* zr = a.zrow + (size_t)row * nbc;
+#pragma unroll
+  for (int x = 0; x < DEC_UN; ++x) {
+    const int b = b0 + (x * 4 + w) * 4 + (l >> 4);
+    float kf[8];
+    unpack8(R[x], kf);
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part = fmaf(qf[e], kf[e], part);
+    part = sum16(part);
+    if (b < nc && (l & 15) == 0) zr[b] = ca.u_of(part);
+  }
+}
+
+// Per row (one wave): the entmax threshold over the row's scores in zrow,
+// the mask words, and the compacted ascending list of the selected blocks
+// with their log2 priors, then the query's own block (prior 0).
+template <int NPL>
+__global__ __launch_bounds__(64) void decode_select_kernel(DecodeArgs a) {
+  const int row = blockIdx.x;
+  const int nbc = a.N / DASH_BLOCK;  // capacity in blocks: row stride of the summaries and the lists
+  const int n = decode_row_len(a, row);
+  const int l = threadIdx.x;
+  const int nbw = (nbc + 31) / 32;   // mask words per row
+  if (n < 1 || n > a.N) {  // length out of range: empty list and mask; the combine writes NaN
+    if (l == 0) {
+      a.sel_cnt[row] = 0;
+      if (a.nsel) a.nsel[row] = -1;
+      if (a.tau_out) a.tau_out[row] = __uint_as_float(0x7fc00000u);
+    }
+    if (a.mask)
+      for (int x = l; x < nbw; x += 64) a.mask[(size_t)row * nbw + x] = 0u;
+    return;
+  }
+  const int own = (n - 1) / DASH_BLOCK;  // the query's block
+  const int nc = own;                    // the complete blocks before it are the candidates
+  const CoarseArith ca = a.ca;
+  const float* us = a.zrow + (size_t)row * nbc;
   float u[NPL];
 #pragma unroll
   for (int k = 0; k < NPL; ++k) {
@@ -207,16 +213,29 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(DecodeArgs a) {
     if (en < cnt) { myb = list[en]; mylp = lpl[en]; }
   }
   const int nmine = cnt > first ? (cnt - first + stride - 1) / stride : 0;
+  // K and V of the next entry are requested as soon as this entry's
+  // registers are consumed: K(k+1) after the scores of k, V(k+1) after its
+  // weighted sum, so each load overlaps the other half's arithmetic
+  uint4 kr[16], vr[16];
+  auto load_k = [&](int b) {
+    const bf16_t* kb = K + (size_t)b * DASH_BLOCK * D;
+#pragma unroll
+    for (int it = 0; it < 16; ++it) kr[it] = *reinterpret_cast<const uint4*>(kb + (size_t)(it * 4 + g) * D + c * 8);
+  };
+  auto load_v = [&](int b) {
+    const bf16_t* vb = V + (size_t)b * DASH_BLOCK * D;
+#pragma unroll
+    for (int it = 0; it < 16; ++it) vr[it] = *reinterpret_cast<const uint4*>(vb + (size_t)(it * 4 + g) * D + c * 8);
+  };
+  if (nmine > 0) {
+    const int b0 = __shfl(myb, 0, 64);
+    load_k(b0);
+    load_v(b0);
+  }
   for (int k = 0; k < nmine; ++k) {
     const int b = __shfl(myb, k, 64);
     const float pr = __shfl(mylp, k, 64);
-    const bf16_t* kb = K + (size_t)b * DASH_BLOCK * D;
-    const bf16_t* vb = V + (size_t)b * DASH_BLOCK * D;
-    uint4 kr[16], vr[16];
-#pragma unroll
-    for (int it = 0; it < 16; ++it) kr[it] = *reinterpret_cast<const uint4*>(kb + (size_t)(it * 4 + g) * D + c * 8);
-#pragma unroll
-    for (int it = 0; it < 16; ++it) vr[it] = *reinterpret_cast<const uint4*>(vb + (size_t)(it * 4 + g) * D + c * 8);
+    const int bn = __shfl(myb, k + 1 < nmine ? k + 1 : k, 64);
     float s[16];
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
@@ -227,6 +246,7 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(DecodeArgs a) {
       for (int e = 0; e < 8; ++e) part = fmaf(qf[e], kf[e], part);
       s[it] = sum16(part) * sl2 + pr;  // key it*4 + g, identical in the 16 lanes of group g
     }
+    if (k + 1 < nmine) load_k(bn);
     if ((b + 1) * DASH_BLOCK > n) {
       // the query's own block, partly filled: positions from n on hold no
       // token (whatever their bits), so they get weight 0 and value 0
@@ -257,6 +277,7 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = fmaf(p, vf[e], o[e]);
     }
+    if (k + 1 < nmine) load_v(bn);
     ps += __shfl_xor(ps, 16, 64);
     ps += __shfl_xor(ps, 32, 64);
     lsum = lsum * rs + ps;
@@ -570,15 +591,23 @@ hipError_t launch_decode(const DecodeArgs& a0, int dtype, hipStream_t st) {
   DecodeArgs a = a0;
   a.nsplit = DASH_DEC_SPLIT;
   const int nb = a.N / DASH_BLOCK;
-  if (nb <= 128) decode_select_kernel<2><<<a.SH, 512, 0, st>>>(a);
-  else if (nb <= 256) decode_select_kernel<4><<<a.SH, 512, 0, st>>>(a);
-  else if (nb <= 512) decode_select_kernel<8><<<a.SH, 512, 0, st>>>(a);
-  else if (nb <= 1024) decode_select_kernel<16><<<a.SH, 512, 0, st>>>(a);
-  else if (nb <= 1536) decode_select_kernel<24><<<a.SH, 512, 0, st>>>(a);
-  else decode_select_kernel<32><<<a.SH, 512, 0, st>>>(a);
+  decode_scores_kernel<<<dim3((nb + DEC_SPW - 1) / DEC_SPW, a.SH), 256, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.grp > 1) {
+  if (nb <= 128) decode_select_kernel<2><<<a.SH, 64, 0, st>>>(a);
+  else if (nb <= 256) decode_select_kernel<4><<<a.SH, 64, 0, st>>>(a);
+  else if (nb <= 512) decode_select_kernel<8><<<a.SH, 64, 0, st>>>(a);
+  else if (nb <= 1024) decode_select_kernel<16><<<a.SH, 64, 0, st>>>(a);
+  else if (nb <= 1536) decode_select_kernel<24><<<a.SH, 64, 0, st>>>(a);
+  else decode_select_kernel<32><<<a.SH, 64, 0, st>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.grp == 1) {
+    decode_attend_kernel<<<dim3(a.nsplit, a.SH), 256, 0, st>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    decode_combine_kernel<DASH_DEC_SPLIT><<<(a.SH + 3) / 4, 256, 0, st>>>(a);
+    return hipGetLastError();
+  }
+  {
     if (a.SH % a.grp) return hipErrorInvalidValue;
     decode_group_merge_kernel<<<a.SH / a.grp, 256, 0, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -592,8 +621,4 @@ hipError_t launch_decode(const DecodeArgs& a0, int dtype, hipStream_t st) {
     decode_combine_kernel<DASH_DEC_SPLIT_GQA><<<(a.SH + 3) / 4, 256, 0, st>>>(a);
     return hipGetLastError();
   }
-  decode_attend_kernel<<<dim3(a.nsplit, a.SH), 256, 0, st>>>(a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  decode_combine_kernel<DASH_DEC_SPLIT><<<(a.SH + 3) / 4, 256, 0, st>>>(a);
-  return hipGetLastError();
 }

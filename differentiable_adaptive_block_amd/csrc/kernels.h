@@ -5,9 +5,10 @@
 
 
 struct SelectArgs {
-  const void* q;      // [BH, T, D]
+  const void* q;      // [BH, Tr, D]
   const void* kbar;   // [BH / grp, nb, D]
-  int T, D, causal;
+  int T, D, causal;   // T: rows in whole blocks (64 nb); the per-row outputs have T rows
+  int Tr;             // rows of q per head (T, or less with a partial last block: rows past it are zero)
   int grp;            // query heads per key/value head (1: one each)
   CoarseArith ca;
   float* tau;         // [BH, T]
@@ -19,6 +20,10 @@ struct SelectArgs {
 };
 
 struct FwdArgs {
+  // q, k, v, o, lse have Tr rows per head; T = 64 nb counts the partial last
+  // block as whole (tau, lognorm and the tile lists have T rows).  Rows at or
+  // past Tr read as zeros and are not written.
+  int Tr;
   const void* q;
   const void* k;
   const void* v;
@@ -139,6 +144,43 @@ __device__ __forceinline__ f32x16 prior_chunk32_group(const bf16_t* KB, const in
   return pacc;
 }
 
+// prior_chunk32 for a wave whose 32 query columns are HG heads of one
+// grouped-query group at 32 / HG rows (column j: head j / (32 / HG), row
+// j % (32 / HG)); qb, tau_i, ln_i are this column's own.  The prior of a
+// listed block for the column's row is log2 of pbar = (1/HG) sum over the
+// group's heads of p_h: each column computes its own head's p with the one
+// score MFMA chain, and the HG columns of a row add theirs by a butterfly
+// over the lane bits that number the heads (the same sum, in the same
+// order, in each of them).  -inf where no head selected the block (and,
+// causal, for the row's own block and later ones).  The list must be the
+// group's union.
+template <int D, int HG>
+__device__ __forceinline__ f32x16 prior_chunk32_heads(const bf16_t* KB, const int* list, int cnt, int e0,
+                                                      const bf16x8 (&qb)[D / 16], const CoarseArith& ca,
+                                                      float tau_i, float ln_i, int causal, int wblk) {
+  constexpr int RPW = 32 / HG;
+  const int l = lane_id(), j = l & 31;
+  const int ent = e0 + j;
+  f32x16 p = coarse_acc_chunk<D>(KB, ent < cnt ? list[ent] : 0, qb);
+  __builtin_amdgcn_sched_group_barrier(0x020, D / 16, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int en = e0 + acc_row32(r, l);
+    float pv = 0.f;
+    if (en < cnt && (!causal || list[en] < wblk)) pv = __expf(ca.logp(ca.u_of(p[r]), tau_i, ln_i));
+    p[r] = pv;
+  }
+#pragma unroll
+  for (int o = RPW; o < 32; o <<= 1)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r] += __shfl_xor(p[r], o, 64);
+  const float lg2G = __log2f((float)HG);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) p[r] = p[r] > 0.f ? __log2f(p[r]) - lg2G : -INFINITY;
+  return p;
+}
+
 // The prior of list entry e for this lane's row from prior_chunk32's
 // registers: slot e%32 sits in register 4(slot/8) + slot%4 of the half
 // (slot/4)%2; the other half's value comes across with permlane32_swap.
@@ -165,7 +207,7 @@ __device__ __forceinline__ float dot_row(const float* qs, const T* kr, int D) {
   return (float)acc;
 }
 
-hipError_t launch_pool(const void* k, void* kbar, int BH, int T, int D, int dtype, hipStream_t st);
+hipError_t launch_pool(const void* k, void* kbar, int BH, int T, int D, int dtype, hipStream_t st, int Tr = -1);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t st);
 hipError_t launch_select(const SelectArgs& a, int BH, int dtype, hipStream_t st);
 hipError_t launch_group_union(uint32_t* tile_bits, int BH, int grp, size_t words_per_head, hipStream_t st);

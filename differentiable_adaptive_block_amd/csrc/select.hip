@@ -10,17 +10,21 @@
 
 // kbar[bh][b][d] = mean of k[bh][64 b + r][d] over r, summed in fp64 (exact for
 // bf16 keys and for fp32 keys of ordinary magnitude), divided by 64 (exact)
-// and rounded once to the storage type.  grid (nb, BH), 64 threads.
+// and rounded once to the storage type.  grid (nb, BH), 64 threads.  k has
+// Tr rows per head (the row stride); rows at or past Tr (the missing rows
+// of a partial last block) count as zeros.
 template <typename T>
-__global__ __launch_bounds__(64) void pool_kernel(const T* __restrict__ k, T* __restrict__ kbar, int T_, int D) {
+__global__ __launch_bounds__(64) void pool_kernel(const T* __restrict__ k, T* __restrict__ kbar, int T_, int Tr,
+                                                  int D) {
   const int b = blockIdx.x;
   const size_t bh = blockIdx.y;
   const int nb = T_ / DASH_BLOCK;
-  const T* src = k + (bh * T_ + (size_t)b * DASH_BLOCK) * D;
+  const T* src = k + (bh * Tr + (size_t)b * DASH_BLOCK) * D;
+  const int nrow = min(DASH_BLOCK, Tr - b * DASH_BLOCK);
   T* dst = kbar + (bh * nb + b) * D;
   for (int c = threadIdx.x; c < D; c += 64) {
     double acc = 0.0;
-    for (int r = 0; r < DASH_BLOCK; ++r) acc += to_d<T>(src[(size_t)r * D + c]);
+    for (int r = 0; r < nrow; ++r) acc += to_d<T>(src[(size_t)r * D + c]);
     double mean = acc * (1.0 / DASH_BLOCK);
     if constexpr (sizeof(T) == 2) dst[c] = d2bf(mean);
     else dst[c] = __double2float_rn(mean);
@@ -31,11 +35,16 @@ __global__ __launch_bounds__(64) void pool_kernel(const T* __restrict__ k, T* __
 // D/8 lanes cover a key row, so one wave load instruction reads 64/(D/8)
 // consecutive rows (1 KB); lane l sums the rows l/(D/8) + (64/(D/8)) x of
 // its 8 columns, then the row groups are added across lanes (xor
-// shuffles).  Every partial sum is exact, so the order does not change the
-// result.  grid (nb, BH), 64 threads.
+// shuffles).  A bf16 value carries 8 significant bits and 64 of them add at
+// most 6 bits of carry, so every partial sum fits a double's 53 bits exactly
+// while a block's non-zero magnitudes lie within 2^39 of each other (any
+// realistic key block): then the order does not change the result, and it
+// equals the sequential sum.  Beyond that range the lane-split order here and
+// the position order of other summers may round differently.
+// grid (nb, BH), 64 threads.
 template <int D>
 __global__ __launch_bounds__(64) void pool_bf16_kernel(const bf16_t* __restrict__ k, bf16_t* __restrict__ kbar,
-                                                       int T_) {
+                                                       int T_, int Tr) {
   constexpr int CPL = D / 8;            // lanes per key row
   constexpr int RPI = 64 / CPL;         // rows per load instruction
   constexpr int NL = DASH_BLOCK / RPI;  // loads per lane
@@ -44,10 +53,12 @@ __global__ __launch_bounds__(64) void pool_bf16_kernel(const bf16_t* __restrict_
   const int nb = T_ / DASH_BLOCK;
   const int l = threadIdx.x;
   const int c = l % CPL, r0 = l / CPL;
-  const bf16_t* src = k + (bh * T_ + (size_t)b * DASH_BLOCK + r0) * D + 8 * c;
+  const bf16_t* src = k + (bh * Tr + (size_t)b * DASH_BLOCK + r0) * D + 8 * c;
+  const int nrow = Tr - b * DASH_BLOCK;  // rows of the block in the tensor (rows past it count as zeros)
   uint4 raw[NL];
 #pragma unroll
-  for (int x = 0; x < NL; ++x) raw[x] = *reinterpret_cast<const uint4*>(src + (size_t)RPI * x * D);
+  for (int x = 0; x < NL; ++x)
+    raw[x] = r0 + RPI * x < nrow ? *reinterpret_cast<const uint4*>(src + (size_t)RPI * x * D) : make_uint4(0, 0, 0, 0);
   double acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0;
@@ -198,12 +209,14 @@ __global__ __launch_bounds__(64 * NW) void select_mfma_kernel(SelectArgs a) {
   const CoarseArith ca = a.ca;
   for (int x = threadIdx.x; x < nbw; x += 64 * NW) uni[x] = 0u;
 
-  const bf16_t* qh = reinterpret_cast<const bf16_t*>(a.q) + bh * a.T * D;
+  const bf16_t* qh = reinterpret_cast<const bf16_t*>(a.q) + bh * a.Tr * D;
   const bf16_t* kb = reinterpret_cast<const bf16_t*>(a.kbar) + (bh / a.grp) * nb * D;
   if (nc > 0) {
     bf16x8 qb[D / 16];
+    const bool qin = row0 + j < a.Tr;  // rows past the tensor (a partial last block) are zero queries
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) qb[s] = load8(qh + (size_t)(row0 + j) * D + 16 * s + 8 * h);
+    for (int s = 0; s < D / 16; ++s)
+      qb[s] = qin ? load8(qh + (size_t)(row0 + j) * D + 16 * s + 8 * h) : bf16x8{};
     for (int c = w; c * 32 < nc; c += NW) {
       const int brow = c * 32 + j;
       f32x16 acc = coarse_acc_chunk<D>(kb, brow < nc ? brow : 0, qb);
@@ -271,14 +284,14 @@ __global__ __launch_bounds__(512, 4) void select_chunked_kernel(SelectArgs a) {
   const int row = 4 * w + (l >> 4);
   const size_t row_g = bh * a.T + row0 + row;
 
-  const bf16_t* qh = reinterpret_cast<const bf16_t*>(a.q) + bh * a.T * D;
+  const bf16_t* qh = reinterpret_cast<const bf16_t*>(a.q) + bh * a.Tr * D;
   const bf16_t* kb = reinterpret_cast<const bf16_t*>(a.kbar) + (bh / a.grp) * nb * D;
   float u[NPL];
   if (nc > 0) {
     for (int x = tid; x < 32 * (D / 8); x += 512) {
       const int r = x / (D / 8), c8 = x % (D / 8);
       *reinterpret_cast<uint4*>(&qs[r * QP + 8 * c8]) =
-          *reinterpret_cast<const uint4*>(qh + (size_t)(row0 + r) * D + 8 * c8);
+          row0 + r < a.Tr ? *reinterpret_cast<const uint4*>(qh + (size_t)(row0 + r) * D + 8 * c8) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
@@ -337,9 +350,9 @@ __global__ __launch_bounds__(64) void select_generic_kernel(SelectArgs a) {
   const size_t bh = blockIdx.y;
   const int i = blockIdx.x;
   const int l = lane_id();
-  const T* q = reinterpret_cast<const T*>(a.q) + (bh * a.T + i) * D;
+  const T* q = reinterpret_cast<const T*>(a.q) + (bh * a.Tr + i) * D;
   const T* kb = reinterpret_cast<const T*>(a.kbar) + (bh / a.grp) * nb * D;
-  for (int d = l; d < D; d += 64) qs[d] = to_f<T>(q[d]);
+  for (int d = l; d < D; d += 64) qs[d] = i < a.Tr ? to_f<T>(q[d]) : 0.f;
   __syncthreads();
   const int nc = a.causal ? i / DASH_BLOCK : nb;
   const size_t row_g = bh * a.T + i;
@@ -399,16 +412,17 @@ __global__ __launch_bounds__(64) void tile_list_kernel(uint32_t* tile_bits, int*
 
 // ---------------------------------------------------------------------------- launchers
 
-hipError_t launch_pool(const void* k, void* kbar, int BH, int T_, int D, int dtype, hipStream_t st) {
+hipError_t launch_pool(const void* k, void* kbar, int BH, int T_, int D, int dtype, hipStream_t st, int Tr) {
+  if (Tr < 0) Tr = T_;
   dim3 grid(T_ / DASH_BLOCK, BH);
   if (dtype == 1 && D == 128)
-    pool_bf16_kernel<128><<<grid, 64, 0, st>>>((const bf16_t*)k, (bf16_t*)kbar, T_);
+    pool_bf16_kernel<128><<<grid, 64, 0, st>>>((const bf16_t*)k, (bf16_t*)kbar, T_, Tr);
   else if (dtype == 1 && D == 64)
-    pool_bf16_kernel<64><<<grid, 64, 0, st>>>((const bf16_t*)k, (bf16_t*)kbar, T_);
+    pool_bf16_kernel<64><<<grid, 64, 0, st>>>((const bf16_t*)k, (bf16_t*)kbar, T_, Tr);
   else if (dtype == 1)
-    pool_kernel<bf16_t><<<grid, 64, 0, st>>>((const bf16_t*)k, (bf16_t*)kbar, T_, D);
+    pool_kernel<bf16_t><<<grid, 64, 0, st>>>((const bf16_t*)k, (bf16_t*)kbar, T_, Tr, D);
   else
-    pool_kernel<float><<<grid, 64, 0, st>>>((const float*)k, (float*)kbar, T_, D);
+    pool_kernel<float><<<grid, 64, 0, st>>>((const float*)k, (float*)kbar, T_, Tr, D);
   return hipGetLastError();
 }
 

@@ -80,7 +80,8 @@ __global__ __launch_bounds__(64) void pool_attn_kernel(const T* __restrict__ k, 
 template <typename T>
 __global__ __launch_bounds__(64) void pool_attn_bwd_kernel(const T* __restrict__ k, const float* __restrict__ w,
                                                            const float* __restrict__ dkbar, T* __restrict__ dk,
-                                                           float* __restrict__ dw_part, int H, int T_, int D) {
+                                                           const float* __restrict__ dk_in, float* __restrict__ dw_part,
+                                                           int H, int T_, int D) {
   __shared__ float ks[DASH_BLOCK][KP];
   __shared__ float gs[128], ms[128];
   __shared__ float as[DASH_BLOCK], des[DASH_BLOCK];
@@ -109,11 +110,12 @@ __global__ __launch_bounds__(64) void pool_attn_bwd_kernel(const T* __restrict__
   des[l] = a * (kg - mg);  // gradient of key l's score
   __syncthreads();
   T* dkb = dk + row0 * D;
+  const float* dki = dk_in ? dk_in + row0 * D : nullptr;  // unrounded fp32 terms to add to, or dk itself
   for (int r = 0; r < DASH_BLOCK; ++r) {
     for (int c = l; c < D; c += 64) {
       const float add = fmaf(as[r], gs[c], des[r] * wh[c]);
-      if constexpr (sizeof(T) == 2) dkb[(size_t)r * D + c] = f2bf(bf2f(dkb[(size_t)r * D + c]) + add);
-      else dkb[(size_t)r * D + c] += add;
+      const float base = dki ? dki[(size_t)r * D + c] : to_f<T>(dkb[(size_t)r * D + c]);
+      dkb[(size_t)r * D + c] = from_f<T>(base + add);
     }
   }
   for (int c = l; c < D; c += 64) {
@@ -273,10 +275,14 @@ __global__ __launch_bounds__(256) void pool_attn_bf16_kernel(const bf16_t* __res
   }
 }
 
+// F32IN: the other dK terms come unrounded from dk_in (fp32, same layout)
+// and dk is written once; otherwise dk holds them (bf16) and is updated.
+template <bool F32IN>
 __global__ __launch_bounds__(256) void pool_attn_bwd_bf16_kernel(const bf16_t* __restrict__ k,
                                                                 const float* __restrict__ w,
                                                                 const float* __restrict__ dkbar,
                                                                 bf16_t* __restrict__ dk,
+                                                                const float* __restrict__ dk_in,
                                                                 float* __restrict__ dw_part, int H, int T_,
                                                                 int total) {
   const Bf16Block t(H, T_, total);
@@ -284,8 +290,10 @@ __global__ __launch_bounds__(256) void pool_attn_bwd_bf16_kernel(const bf16_t* _
   uint4 kr[16], dr[16];
 #pragma unroll
   for (int it = 0; it < 16; ++it) kr[it] = *reinterpret_cast<const uint4*>(t.row(k, T_, it));
+  if constexpr (!F32IN) {
 #pragma unroll
-  for (int it = 0; it < 16; ++it) dr[it] = *reinterpret_cast<const uint4*>(t.row(dk, T_, it));
+    for (int it = 0; it < 16; ++it) dr[it] = *reinterpret_cast<const uint4*>(t.row(dk, T_, it));
+  }
   float wf[8], gf[8];
   const float* wh = w + (t.bh % H) * 128 + t.c * 8;
   const float* gh = dkbar + (size_t)t.gb * 128 + t.c * 8;
@@ -336,7 +344,16 @@ __global__ __launch_bounds__(256) void pool_attn_bwd_bf16_kernel(const bf16_t* _
     const float de = a[it] * (kg[it] - mg);  // gradient of the key's score
     float kf[8], df[8];
     unpack8(kr[it], kf);
-    unpack8(dr[it], df);
+    if constexpr (F32IN) {
+      // the same element of the fp32 buffer: dk_in has dk's layout
+      const size_t off = t.row(dk, T_, it) - dk;
+      const float4 x0 = *reinterpret_cast<const float4*>(dk_in + off);
+      const float4 x1 = *reinterpret_cast<const float4*>(dk_in + off + 4);
+      df[0] = x0.x; df[1] = x0.y; df[2] = x0.z; df[3] = x0.w;
+      df[4] = x1.x; df[5] = x1.y; df[6] = x1.z; df[7] = x1.w;
+    } else {
+      unpack8(dr[it], df);
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       df[e] += fmaf(a[it], gf[e], de * wf[e]);
@@ -370,18 +387,25 @@ hipError_t launch_pool_attn(const void* k, const float* w, void* kbar, int BH, i
 }
 
 hipError_t launch_pool_attn_bwd(const void* k, const float* w, const float* dkbar, void* dk, float* dw,
-                                float* dw_part, int B, int H, int T_, int D, int dtype, hipStream_t st) {
+                                float* dw_part, int B, int H, int T_, int D, int dtype, hipStream_t st,
+                                const float* dk_in) {
   if (D > 128) return hipErrorNotSupported;
   const int nb = T_ / DASH_BLOCK;
   dim3 grid(nb, B * H);
   const int total = B * H * nb;
-  if (dtype == 1 && D == 128)
-    pool_attn_bwd_bf16_kernel<<<(total + 3) / 4, 256, 0, st>>>((const bf16_t*)k, w, dkbar, (bf16_t*)dk, dw_part, H,
-                                                               T_, total);
-  else if (dtype == 1)
-    pool_attn_bwd_kernel<bf16_t><<<grid, 64, 0, st>>>((const bf16_t*)k, w, dkbar, (bf16_t*)dk, dw_part, H, T_, D);
+  if (dtype == 1 && D == 128) {
+    if (dk_in)
+      pool_attn_bwd_bf16_kernel<true><<<(total + 3) / 4, 256, 0, st>>>((const bf16_t*)k, w, dkbar, (bf16_t*)dk, dk_in,
+                                                                       dw_part, H, T_, total);
+    else
+      pool_attn_bwd_bf16_kernel<false><<<(total + 3) / 4, 256, 0, st>>>((const bf16_t*)k, w, dkbar, (bf16_t*)dk,
+                                                                        nullptr, dw_part, H, T_, total);
+  } else if (dtype == 1)
+    pool_attn_bwd_kernel<bf16_t><<<grid, 64, 0, st>>>((const bf16_t*)k, w, dkbar, (bf16_t*)dk, dk_in, dw_part, H, T_,
+                                                      D);
   else
-    pool_attn_bwd_kernel<float><<<grid, 64, 0, st>>>((const float*)k, w, dkbar, (float*)dk, dw_part, H, T_, D);
+    pool_attn_bwd_kernel<float><<<grid, 64, 0, st>>>((const float*)k, w, dkbar, (float*)dk, dk_in, dw_part, H, T_,
+                                                     D);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   reduce_dw_kernel<<<dim3(H, (D + 15) / 16), 256, 0, st>>>(dw_part, dw, B, H, nb, D);

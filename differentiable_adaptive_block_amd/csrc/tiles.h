@@ -80,14 +80,16 @@ struct TileCopy {
       off[q] = (uint32_t)(row * D + 8 * (slot ^ SWZ(row))) * 2u;
     }
   }
-  // src: the tile's first row; w must be wave-uniform
-  __device__ __forceinline__ void copy(const bf16_t* src, bf16_t* dst, int w) const {
+  // src: the tile's first row; w must be wave-uniform.  rows: the rows of
+  // the tile that exist in the tensor (64 except for a partial last block);
+  // the descriptor covers only those, so no read leaves the tensor.
+  __device__ __forceinline__ void copy(const bf16_t* src, bf16_t* dst, int w, int rows = 64) const {
     // the base goes through the scalar unit explicitly (a wave-uniform
     // buffer descriptor)
     const uint64_t a = reinterpret_cast<uint64_t>(src);
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), 64 * D * 2);
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), rows * D * 2);
 #pragma unroll
     for (int q = 0; q < NI; ++q) copy16_to_lds(r, off[q], dst + RPI * (NI * w + q) * D);
   }

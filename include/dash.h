@@ -108,7 +108,7 @@ int32_t dash_query_tile(void);
 /* Element counts of the eight dash_sel buffers, in struct order. */
 dash_status dash_sel_sizes(const dash_params* p, size_t out_elems[8]);
 
-/* Bytes of device workspace dash_fwd / dash_bwd need (dash_fwd: 0 unless T is not a multiple of 64). */
+/* Bytes of device workspace dash_fwd / dash_bwd need (dash_fwd: always 0). */
 size_t dash_fwd_workspace_bytes(const dash_params* p);
 size_t dash_bwd_workspace_bytes(const dash_params* p);
 
@@ -129,10 +129,13 @@ dash_status dash_pool(const dash_params* p, const void* k, void* kbar, void* str
  * (the other prefill entry points do not): the last block is partial; it is
  * the own block of its queries and no query's candidate, so only the
  * complete blocks have summaries (kbar and dkbar have ceil(T/64) rows; the
- * last one is not a summary, and dkbar's is 0).  The library then runs the
- * whole-block kernels on copies padded with zeros in the workspace
- * (dash_fwd_workspace_bytes) and copies the T rows back; the results are
- * those of the unpadded problem.  Non-causal attention needs whole blocks.
+ * last one is not a summary, and dkbar's is 0).  dash_fwd's kernels take
+ * the T-row tensors as they are and treat the missing rows of the last
+ * block as zeros, never reading or writing past the tensors (its workspace
+ * is 0 bytes; workspace may be NULL); dash_bwd runs the whole-block kernels
+ * on copies padded with zeros in its workspace (dash_bwd_workspace_bytes)
+ * and copies the T rows back.  The results are those of the unpadded
+ * problem.  Non-causal attention needs whole blocks.
  */
 dash_status dash_fwd(const dash_params* p, const void* q, const void* k, const void* v,
                      void* o, float* lse, void* kbar, const dash_sel* sel,
@@ -206,6 +209,22 @@ size_t dash_pool_attn_bwd_workspace_bytes(const dash_params* p);
 dash_status dash_pool_attn_bwd(const dash_params* p, const void* k, const float* w, const float* dkbar,
                                void* dk, float* dw, void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/*
+ * The whole backward with the learned summariser: dash_bwd_no_pool, then
+ * dash_pool_attn_bwd, except that for bf16 the other dK terms stay
+ * unrounded (fp32, in the workspace) until the summariser's term is added,
+ * so dk is rounded once (at w = 0 it equals dash_bwd's dk bit for bit).
+ * Outputs as dash_bwd plus dw [H, D] (f32).  Workspace:
+ * dash_bwd_learned_workspace_bytes (the backward's, B*H*T*D floats, and
+ * dash_pool_attn_bwd's).  Whole blocks only.
+ */
+size_t dash_bwd_learned_workspace_bytes(const dash_params* p);
+dash_status dash_bwd_learned(const dash_params* p, const void* q, const void* k, const void* v,
+                             const void* o, const float* lse, const void* dout, const void* kbar,
+                             const dash_sel* sel, const float* w, void* dq, void* dk, void* dv,
+                             float* dkbar, float* dw, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /*
  * Grouped-query heads with entmax head aggregation.  p->H query heads share

@@ -235,9 +235,10 @@ def test_partial_last_block_validation(L):
     assert _fwd(L, _params(T=100, causal=0)) == _lib.DASH_EINVAL
     assert "causal" in L.dash_last_error().decode()
     p = _params(T=100)
-    need = L.dash_fwd_workspace_bytes(ctypes.byref(p))
-    assert need > 0 and L.dash_fwd_workspace_bytes(ctypes.byref(_params())) == 0
-    assert _fwd(L, p) == _lib.DASH_EWORKSPACE
+    # the forward handles the partial block inside its kernels: no workspace
+    assert L.dash_fwd_workspace_bytes(ctypes.byref(p)) == 0
+    assert L.dash_fwd_workspace_bytes(ctypes.byref(_params())) == 0
+    assert _fwd(L, p, lse=FAKE + 4) == _lib.DASH_EINVAL  # validated before any launch
     assert L.dash_bwd_workspace_bytes(ctypes.byref(p)) > L.dash_bwd_workspace_bytes(ctypes.byref(_params(T=128)))
     sizes = (ctypes.c_size_t * 8)()
     assert L.dash_sel_sizes(ctypes.byref(p), sizes) == _lib.DASH_OK
