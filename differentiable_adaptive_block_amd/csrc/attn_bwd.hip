@@ -650,131 +650,175 @@ __device__ __forceinline__ float sum8(float v) {
 // dz_b = s_b g_b - s_b <s, g> / sum s with g_b = G_ib / p_ib, computed as
 // G_ib p^(1-alpha) from the log2 prior; dz overwrites G (the dK kernel
 // reads it for dkbar).  Then dQ_i = dq_acc_i + coarse_scale sum_b dz_b kbar_b.
-// grid (ntile * 4, BH), 256 threads = 32 rows x 8 threads: thread c of a
-// row takes list slots e = c (mod 8) in the first two passes and columns
-// c G .. c G + G - 1 in the last.
 // Grouped-query heads (GQA): the prior in pbuf is the group's log2 pbar,
 // gsum holds G summed over the group and phbuf the row's own log2 p (whose
 // Jacobian applies), written by the dQ kernel; with g_b = Gsum_b /
 // (grp pbar_b):  s_b g_b = p_b^(2-alpha) Gsum_b pbar_b^-1 / grp.
+//
+// Workgroup = one 128-row query tile, 4 waves of 32 rows; lane (j, h) of
+// wave w holds row 32 w + j.  A first pass over the list gives each row
+// <s, g> / sum s (half h takes the entries of parity h, so a half-wave reads
+// 32 consecutive rows of one entry, 128 bytes); the second pass, 16 entries
+// per k-step, forms the row's dz for the 8 entries its MFMA operand needs,
+// stores them, and adds coarse_scale dz kbar to dQ as a matrix product
+//   dQc^T (D x 32 rows) += Kbar^T (D x 16 entries) dz^T (16 entries x 32 rows)
+// on bf16 MFMA 32x32x16, the summaries of 64 listed entries at a time staged
+// in LDS (rows permuted as the forward's V tiles) and read transposed, as
+// the forward's PV product reads V.
 template <int D, bool GQA>
-__global__ __launch_bounds__(256) void bwd_coarse_kernel(BwdArgs a) {
-  constexpr int G = D / 8;
+__global__ __launch_bounds__(256, 2) void bwd_coarse_kernel(BwdArgs a) {
+  constexpr int NDT = D / 32;
+  constexpr int CH = D / 8;  // 16-byte chunks per summary row
+  __shared__ __attribute__((aligned(16))) bf16_t kbt[64 * D];
+  __shared__ int lst[DASH_MAX_NB];
   const int nb = a.T / DASH_BLOCK;
   const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
   const size_t bh = blockIdx.y;
-  const int tile = blockIdx.x >> 2;
-  const int rt = (blockIdx.x & 3) * 32 + (threadIdx.x >> 3);
-  const int cg = threadIdx.x & 7;
+  const int tile = blockIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, j = l & 31, h = l >> 5;
+  const int rt = 32 * w + j;
   const int i = tile * DASH_QTILE + rt;
   const bool valid = i < a.T;
   const int own = i / DASH_BLOCK;
-  const int* list = a.tile_blk + (bh * ntile + tile) * nb;
+  const int* glist = a.tile_blk + (bh * ntile + tile) * nb;
   const int cnt = a.tile_cnt[bh * ntile + tile];
+  for (int x = tid; x < cnt; x += 256) lst[x] = glist[x];
+  __syncthreads();
   const float am2 = 2.f - (a.ca.softmax ? 1.f : 1.f + a.ca.am1);  // 2 - alpha
   const float am1n = am2 - 1.f;                                    // 1 - alpha
   const size_t bkv = GQA ? bh / a.grp : bh;
-  float ss = 0.f, ssg = 0.f;
-  if constexpr (GQA) {
-    const float inv_grp = 1.f / (float)a.grp;
-    if (valid) {
-      for (int e = cg; e < cnt; e += 8) {
-        if (a.causal && list[e] >= own) continue;
-        const size_t gi = gidx(bh, ntile, tile, nb, e, rt, a.causal);
-        const float lpb2 = a.pbuf[gi];
-        const float lp2 = a.phbuf[gi];
-        if (lpb2 == -INFINITY || lp2 == -INFINITY) continue;
-        const float sv = __builtin_amdgcn_exp2f(am2 * lp2);
-        ss += sv;
-        ssg += sv * a.gsum[gidx(bkv, ntile, tile, nb, e, rt, a.causal)] * __builtin_amdgcn_exp2f(-lpb2) * inv_grp;
-      }
-    }
-    ss = sum8(ss);
-    ssg = sum8(ssg);
-    const float ratio = ss > 0.f ? ssg / ss : 0.f;
-    if (valid) {
-      for (int e = cg; e < cnt; e += 8) {
-        const size_t gi = gidx(bh, ntile, tile, nb, e, rt, a.causal);
-        float dz = 0.f;
-        if (!(a.causal && list[e] >= own)) {
-          const float lpb2 = a.pbuf[gi];
-          const float lp2 = a.phbuf[gi];
-          if (lpb2 != -INFINITY && lp2 != -INFINITY) {
-            const float sv = __builtin_amdgcn_exp2f(am2 * lp2);
-            const float gv = a.gsum[gidx(bkv, ntile, tile, nb, e, rt, a.causal)] * __builtin_amdgcn_exp2f(-lpb2) * inv_grp;
-            dz = sv * gv - sv * ratio;
-          }
-        }
-        a.gbuf[gi] = dz;
-      }
-    }
-  } else {
-  if (valid) {
-    for (int e = cg; e < cnt; e += 8) {
-      if (a.causal && list[e] >= own) continue;
-      const size_t gi = gidx(bh, ntile, tile, nb, e, rt, a.causal);
-      const float lp2 = a.pbuf[gi];
-      if (lp2 == -INFINITY) continue;
-      ss += __builtin_amdgcn_exp2f(am2 * lp2);
-      ssg += a.gbuf[gi] * __builtin_amdgcn_exp2f(am1n * lp2);
-    }
-  }
-  ss = sum8(ss);
-  ssg = sum8(ssg);
-  const float ratio = ss > 0.f ? ssg / ss : 0.f;
-  if (valid) {
-    for (int e = cg; e < cnt; e += 8) {
-      const size_t gi = gidx(bh, ntile, tile, nb, e, rt, a.causal);
-      float dz = 0.f;
-      if (!(a.causal && list[e] >= own)) {
-        const float lp2 = a.pbuf[gi];
-        if (lp2 != -INFINITY)
-          dz = a.gbuf[gi] * __builtin_amdgcn_exp2f(am1n * lp2) - __builtin_amdgcn_exp2f(am2 * lp2) * ratio;
-      }
-      a.gbuf[gi] = dz;
-    }
-  }
-  }
-  __syncthreads();  // every dz of the workgroup's rows is written
-  if (!valid) return;
-  const bf16_t* KB = reinterpret_cast<const bf16_t*>(a.kbar) + bkv * nb * D + cg * G;
-  float acc[G];
-#pragma unroll
-  for (int x = 0; x < G; ++x) acc[x] = 0.f;
-  constexpr int U = 4;  // list entries per step, loads in flight together
-  for (int e0 = 0; e0 < cnt; e0 += U) {
-    float dz[U];
-    uint4 kr[U][G / 8];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int e = e0 + u;
-      dz[u] = 0.f;
-      if (e < cnt) {
-        dz[u] = a.gbuf[gidx(bh, ntile, tile, nb, e, rt, a.causal)];
-        const bf16_t* kr0 = KB + (size_t)list[e] * D;
-#pragma unroll
-        for (int c = 0; c < G / 8; ++c) kr[u][c] = *reinterpret_cast<const uint4*>(kr0 + 8 * c);
+  const float inv_grp = GQA ? 1.f / (float)a.grp : 1.f;
+  const size_t g0 = gidx(bh, ntile, tile, nb, 0, rt, a.causal);   // entry e at g0 + 128 e
+  const size_t s0 = gidx(bkv, ntile, tile, nb, 0, rt, a.causal);  // the group's G sum (GQA)
+  // The per-entry values of 8 entries are loaded together before any of
+  // them is used (loads of one lane in flight at once; entries past the
+  // list read as unselected).  s_b and s_b g_b of (this row, entry e) follow;
+  // an entry the row does not select (at or after its own block, or p = 0)
+  // gives none.
+  struct Ent {
+    float lp2, g, lpb2;  // log2 p (own), G or G summed over the group, log2 pbar (GQA)
+  };
+  auto load_ent = [&](int e) -> Ent {
+    Ent x{-INFINITY, 0.f, -INFINITY};
+    if (e < cnt) {
+      const size_t gi = g0 + (size_t)e * DASH_QTILE;
+      if constexpr (GQA) {
+        x.lpb2 = a.pbuf[gi];
+        x.lp2 = a.phbuf[gi];
+        x.g = a.gsum[s0 + (size_t)e * DASH_QTILE];
       } else {
-#pragma unroll
-        for (int c = 0; c < G / 8; ++c) kr[u][c] = make_uint4(0, 0, 0, 0);
+        x.lp2 = a.pbuf[gi];
+        x.g = a.gbuf[gi];
       }
     }
+    return x;
+  };
+  auto terms = [&](int e, const Ent& x, float& sv, float& sg) -> bool {
+    if (e >= cnt || (a.causal && lst[e] >= own)) return false;
+    if constexpr (GQA) {
+      if (x.lpb2 == -INFINITY || x.lp2 == -INFINITY) return false;
+      sv = __builtin_amdgcn_exp2f(am2 * x.lp2);
+      sg = sv * (x.g * __builtin_amdgcn_exp2f(-x.lpb2) * inv_grp);
+    } else {
+      if (x.lp2 == -INFINITY) return false;
+      sv = __builtin_amdgcn_exp2f(am2 * x.lp2);
+      sg = x.g * __builtin_amdgcn_exp2f(am1n * x.lp2);
+    }
+    return true;
+  };
+  float ss = 0.f, ssg = 0.f;
+  if (valid) {
+    for (int e0 = h; e0 < cnt; e0 += 16) {
+      Ent x[8];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+      for (int u = 0; u < 8; ++u) x[u] = load_ent(e0 + 2 * u);
 #pragma unroll
-      for (int c = 0; c < G / 8; ++c) {
-        const uint32_t wv[4] = {kr[u][c].x, kr[u][c].y, kr[u][c].z, kr[u][c].w};
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          acc[8 * c + 2 * x] = fmaf(dz[u], __uint_as_float(wv[x] << 16), acc[8 * c + 2 * x]);
-          acc[8 * c + 2 * x + 1] = fmaf(dz[u], __uint_as_float(wv[x] & 0xFFFF0000u), acc[8 * c + 2 * x + 1]);
+      for (int u = 0; u < 8; ++u) {
+        float sv, sg;
+        if (terms(e0 + 2 * u, x[u], sv, sg)) {
+          ss += sv;
+          ssg += sg;
         }
       }
+    }
   }
-  const float* dqa = a.dq_acc + (bh * a.T + i) * D + cg * G;
-  bf16_t* dq = reinterpret_cast<bf16_t*>(a.dq) + (bh * a.T + i) * D + cg * G;
+  ss += __shfl_xor(ss, 32, 64);
+  ssg += __shfl_xor(ssg, 32, 64);
+  const float ratio = ss > 0.f ? ssg / ss : 0.f;
+
+  // transposing-read offsets (k-step s, d tile dt): A1 + ((64 dt) ^ B1) + 32 D s
+  uint32_t A1, B1, A2, B2;
+  col8_parts<D, TileSwz<D>::v>(l, A1, B1, A2, B2);
+  const char* kbb = reinterpret_cast<const char*>(kbt);
+  const bf16_t* KB = reinterpret_cast<const bf16_t*>(a.kbar) + bkv * nb * D;
+  f32x16 acc[NDT];
 #pragma unroll
-  for (int x = 0; x < G; ++x) dq[x] = f2bf(dqa[x] + a.ca.coarse_scale * acc[x]);
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+  // k-step ks covers entries 16 ks .. 16 ks + 15; this lane's operand
+  // entries are 16 ks + 4 h + {0..3} and 16 ks + 8 + 4 h + {0..3}, loaded one
+  // k-step ahead
+  auto ent_of = [&](int ks, int x) { return 16 * ks + 4 * h + (x < 4 ? x : x + 4); };
+  const int nks = (cnt + 15) / 16;
+  Ent nx[8];
+#pragma unroll
+  for (int x = 0; x < 8; ++x) nx[x] = (valid && nks > 0) ? load_ent(ent_of(0, x)) : Ent{-INFINITY, 0.f, -INFINITY};
+  for (int ks = 0; ks < nks; ++ks) {
+    if ((ks & 3) == 0) {
+      const int c0 = 16 * ks;
+      __syncthreads();  // the previous chunk's summaries are read
+      for (int x = tid; x < 64 * CH; x += 256) {
+        const int r = x / CH, c = x % CH;
+        const int e = c0 + r;
+        const uint4 v = e < cnt ? *reinterpret_cast<const uint4*>(KB + (size_t)lst[e] * D + 8 * c) : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(kbt + r * D + 8 * (c ^ TileSwz<D>::v(r))) = v;
+      }
+      __syncthreads();
+    }
+    Ent xe[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) xe[x] = nx[x];
+    if (ks + 1 < nks) {
+#pragma unroll
+      for (int x = 0; x < 8; ++x) nx[x] = valid ? load_ent(ent_of(ks + 1, x)) : Ent{-INFINITY, 0.f, -INFINITY};
+    }
+    bf16x8 pb;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const int e = ent_of(ks, x);
+      float dz = 0.f;
+      if (valid && e < cnt) {
+        float sv, sg;
+        if (terms(e, xe[x], sv, sg)) dz = sg - sv * ratio;
+        a.gbuf[g0 + (size_t)e * DASH_QTILE] = dz;
+      }
+      pb[x] = (__bf16)dz;
+    }
+    const uint32_t so = 32u * D * (ks & 3);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const bf16x8 ka = tile_col8_b(kbb, A1 + ((64u * dt) ^ B1) + so, A2 + ((64u * dt) ^ B2) + so);
+      acc[dt] = mfma32(ka, pb, acc[dt]);
+    }
+  }
+  if (!valid) return;
+  const float cs = a.ca.coarse_scale;
+  const float* dqa = a.dq_acc + (bh * a.T + i) * D;
+  bf16_t* dq = reinterpret_cast<bf16_t*>(a.dq) + (bh * a.T + i) * D;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d = 32 * dt + 8 * r4 + 4 * h;  // registers 4 r4 .. 4 r4 + 3 hold d .. d + 3
+      const float4 f = *reinterpret_cast<const float4*>(dqa + d);
+      bf16x4 o4;
+      o4[0] = (__bf16)(f.x + cs * acc[dt][4 * r4 + 0]);
+      o4[1] = (__bf16)(f.y + cs * acc[dt][4 * r4 + 1]);
+      o4[2] = (__bf16)(f.z + cs * acc[dt][4 * r4 + 2]);
+      o4[3] = (__bf16)(f.w + cs * acc[dt][4 * r4 + 3]);
+      *reinterpret_cast<bf16x4*>(dq + d) = o4;
+    }
 }
 
 // ---------------------------------------------------------------------------- fp32 path
@@ -1032,8 +1076,8 @@ hipError_t launch_bwd_gqa(const BwdArgs& a, void* dk, void* dv, float* dkbar, hi
   if ((e = hipGetLastError()) != hipSuccess) return e;
   bwd_gqa_gsum_kernel<<<dim3(ntile, a.BH / a.grp), 256, 0, st>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (a.D == 128) bwd_coarse_kernel<128, true><<<dim3(ntile * 4, a.BH), 256, 0, st>>>(a);
-  else bwd_coarse_kernel<64, true><<<dim3(ntile * 4, a.BH), 256, 0, st>>>(a);
+  if (a.D == 128) bwd_coarse_kernel<128, true><<<dim3(ntile, a.BH), 256, 0, st>>>(a);
+  else bwd_coarse_kernel<64, true><<<dim3(ntile, a.BH), 256, 0, st>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int ngrp = (nb + 1) / 2;
   if (a.D == 128) bwd_dkdv_kernel<128><<<ngrp * a.BH, 512, 0, st>>>(a);
@@ -1057,8 +1101,8 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t st) {
     if (a.D == 128) bwd_dq_kernel<128, false><<<ntile * a.BH, 256, 0, st>>>(a);
     else bwd_dq_kernel<64, false><<<ntile * a.BH, 256, 0, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (a.D == 128) bwd_coarse_kernel<128, false><<<dim3(ntile * 4, a.BH), 256, 0, st>>>(a);
-    else bwd_coarse_kernel<64, false><<<dim3(ntile * 4, a.BH), 256, 0, st>>>(a);
+    if (a.D == 128) bwd_coarse_kernel<128, false><<<dim3(ntile, a.BH), 256, 0, st>>>(a);
+    else bwd_coarse_kernel<64, false><<<dim3(ntile, a.BH), 256, 0, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int ngrp = (nb + 1) / 2;
     if (a.D == 128) bwd_dkdv_kernel<128><<<ngrp * a.BH, 512, 0, st>>>(a);
