@@ -1003,18 +1003,32 @@ __global__ __launch_bounds__(64) void bwd_keys_generic_kernel(BwdArgs a) {
 }
 
 // Grouped-query heads: G of the group's heads summed per (tile, listed
-// block, row) into gsum.  grid (ntile, BH / grp), 256 threads.
+// block, row) into gsum, in head order.  grid (ntile, BH / grp), 256
+// threads; a thread takes 4 consecutive rows of an entry (16-byte loads) and
+// has the grp heads' loads in flight together.
+template <int GRP>
 __global__ __launch_bounds__(256) void bwd_gqa_gsum_kernel(BwdArgs a) {
   const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
   const int nb = a.T / DASH_BLOCK;
   const int tile = blockIdx.x;
-  const size_t bkv = blockIdx.y, bh0 = bkv * a.grp;
+  const size_t bkv = blockIdx.y, bh0 = bkv * GRP;
   const int cnt = a.tile_cnt[bh0 * ntile + tile];  // the group's heads share the list
-  for (int x = threadIdx.x; x < cnt * DASH_QTILE; x += blockDim.x) {
-    const int e = x / DASH_QTILE, rt = x % DASH_QTILE;
-    float g = 0.f;
-    for (int h = 0; h < a.grp; ++h) g += a.gbuf[gidx(bh0 + h, ntile, tile, nb, e, rt, a.causal)];
-    a.gsum[gidx(bkv, ntile, tile, nb, e, rt, a.causal)] = g;
+  const size_t hstride = bwd_entries_per_head(a.causal, nb, ntile) * DASH_QTILE;  // floats per head
+  const float* g0 = a.gbuf + gidx(bh0, ntile, tile, nb, 0, 0, a.causal);
+  float* gs = a.gsum + gidx(bkv, ntile, tile, nb, 0, 0, a.causal);
+  for (int x = threadIdx.x; x < cnt * (DASH_QTILE / 4); x += blockDim.x) {
+    float4 v[GRP];
+#pragma unroll
+    for (int h = 0; h < GRP; ++h) v[h] = *reinterpret_cast<const float4*>(g0 + h * hstride + 4 * (size_t)x);
+    float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int h = 0; h < GRP; ++h) {
+      g.x += v[h].x;
+      g.y += v[h].y;
+      g.z += v[h].z;
+      g.w += v[h].w;
+    }
+    *reinterpret_cast<float4*>(gs + 4 * (size_t)x) = g;
   }
 }
 
@@ -1074,7 +1088,13 @@ hipError_t launch_bwd_gqa(const BwdArgs& a, void* dk, void* dv, float* dkbar, hi
   if (a.D == 128) bwd_dq_kernel<128, true><<<ntile * a.BH, 256, 0, st>>>(a);
   else bwd_dq_kernel<64, true><<<ntile * a.BH, 256, 0, st>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  bwd_gqa_gsum_kernel<<<dim3(ntile, a.BH / a.grp), 256, 0, st>>>(a);
+  {
+    const dim3 grid(ntile, a.BH / a.grp);
+    if (a.grp == 2) bwd_gqa_gsum_kernel<2><<<grid, 256, 0, st>>>(a);
+    else if (a.grp == 4) bwd_gqa_gsum_kernel<4><<<grid, 256, 0, st>>>(a);
+    else if (a.grp == 8) bwd_gqa_gsum_kernel<8><<<grid, 256, 0, st>>>(a);
+    else return hipErrorNotSupported;
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.D == 128) bwd_coarse_kernel<128, true><<<dim3(ntile, a.BH), 256, 0, st>>>(a);
   else bwd_coarse_kernel<64, true><<<dim3(ntile, a.BH), 256, 0, st>>>(a);

@@ -12,14 +12,13 @@
 // cache; chunk-summarise stage of the code samples listed by the
 // codewithpapers.app entry for the DashAttention paper).
 //
-// Four decode kernels, all HBM-bound except the per-row select:
-//   decode_scores   u = (alpha-1) * coarse_scale * q.kbar_b for every candidate
-//                   of every row: a coalesced GEMV over the summaries spread
-//                   over (row, 256-summary chunk) workgroups, each with all
-//                   its loads in flight before its first dot product;
-//   decode_select   one wave per row: entmax threshold over the row's scores,
-//                   mask words, compacted ascending list of the selected
-//                   blocks with their log2 prior, then the last block;
+// Three decode kernels, HBM-bound:
+//   decode_select   one 4-wave workgroup per row: u = (alpha-1) * coarse_scale
+//                   * q.kbar_b for every candidate (a coalesced GEMV over the
+//                   row's summaries, two rounds of loads in flight) into LDS,
+//                   then on one wave the entmax threshold, mask words and the
+//                   compacted ascending list of the selected blocks with their
+//                   log2 prior, then the last block;
 //   decode_attend   split-KV: workgroup (split s, row) and its 4 waves take list
 //                   entries s*4 + w, stepping by 4*nsplit; each wave streams a
 //                   block's 64 keys and values (16 KB each, contiguous) with
@@ -51,59 +50,71 @@ __device__ __forceinline__ void unpack8(const uint4& r, float (&f)[8]) {
 
 // ---------------------------------------------------------------------------- selection
 
-// Block scores of every decode row: u_b = (alpha-1) coarse_scale q . kbar_b
-// for the candidates b < (n-1)/64, written to zrow.  grid (chunks, rows):
-// workgroup (c, row) scores summaries DEC_SPW c .. DEC_SPW (c+1) - 1 with
-// 16 lanes per summary row (8 elements each, 4 rows per wave instruction),
-// every load of the workgroup issued before the first dot product.
-#define DEC_UN 16                    // 16-byte loads per lane
-#define DEC_SPW (4 * 4 * DEC_UN)     // summaries per 4-wave workgroup
-__global__ __launch_bounds__(256) void decode_scores_kernel(DecodeArgs a) {
+// Block scores of one decode row: u_b = (alpha-1) coarse_scale q . kbar_b
+// for the candidates b < nc, into LDS.  The workgroup's 4 waves read 16
+// summary rows per instruction round (16 lanes per 256-byte row, 8
+// elements each); a lane keeps two rounds of DEC_UN 16-byte loads in
+// flight, so one 4-wave workgroup per row streams the row's summaries at
+// full rate.
+#define DEC_UN 8                    // 16-byte loads per lane per round
+#define DEC_SPR (4 * 4 * DEC_UN)    // summary rows per round of the workgroup
+__device__ __forceinline__ void decode_row_scores(const DecodeArgs& a, int row, int nc, float* zs) {
   constexpr int D = 128;
-  const int row = blockIdx.y;
   const int nbc = a.N / DASH_BLOCK;
-  const int n = decode_row_len(a, row);
-  if (n < 1 || n > a.N) return;  // the select kernel writes this row's outputs
-  const int nc = (n - 1) / DASH_BLOCK;  // candidates: the complete blocks before the query's own
-  const int b0 = blockIdx.x * DEC_SPW;
-  if (b0 >= nc) return;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const bf16_t* q = reinterpret_cast<const bf16_t*>(a.q) + (size_t)row * D;
-  const bf16_t* kb = reinterpret_cast<const bf16_t*>(a.kbar) + (size_t)(row / a.grp) * nbc * D;
+  const bf16_t* kb = reinterpret_cast<const bf16_t*>(a.kbar) + (size_t)(row / a.grp) * nbc * D + (l & 15) * 8;
   const CoarseArith ca = a.ca;
   float qf[8];
   unpack8(*reinterpret_cast<const uint4*>(q + (l & 15) * 8), qf);
-  uint4 R[DEC_UN];
+  auto bof = [&](int b0, int x) { return b0 + (x * 4 + w) * 4 + (l >> 4); };
+  uint4 R[2][DEC_UN];
+  auto load = [&](int b0, uint4 (&r)[DEC_UN]) {
 #pragma unroll
-  for (int x = 0; x < DEC_UN; ++x) {
-    const int b = b0 + (x * 4 + w) * 4 + (l >> 4);
-    R[x] = b < nc ? *reinterpret_cast<const uint4*>(kb + (size_t)b * D + (l & 15) * 8) : make_uint4(0, 0, 0, 0);
-  }
-  float* zr = a.zrow + (size_t)row * nbc;
+    for (int x = 0; x < DEC_UN; ++x) {
+      const int b = bof(b0, x);
+      r[x] = b < nc ? *reinterpret_cast<const uint4*>(kb + (size_t)b * D) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto score = [&](int b0, const uint4 (&r)[DEC_UN]) {
 #pragma unroll
-  for (int x = 0; x < DEC_UN; ++x) {
-    const int b = b0 + (x * 4 + w) * 4 + (l >> 4);
-    float kf[8];
-    unpack8(R[x], kf);
-    float part = 0.f;
+    for (int x = 0; x < DEC_UN; ++x) {
+      const int b = bof(b0, x);
+      float kf[8];
+      unpack8(r[x], kf);
+      float part = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) part = fmaf(qf[e], kf[e], part);
-    part = sum16(part);
-    if (b < nc && (l & 15) == 0) zr[b] = ca.u_of(part);
+      for (int e = 0; e < 8; ++e) part = fmaf(qf[e], kf[e], part);
+      part = sum16(part);
+      if (b < nc && (l & 15) == 0) zs[b] = ca.u_of(part);
+    }
+  };
+  // rounds alternate between the two register sets (unrolled by two so
+  // that each set keeps fixed registers)
+  load(0, R[0]);
+  for (int b0 = 0; b0 < nc; b0 += 2 * DEC_SPR) {
+    if (b0 + DEC_SPR < nc) load(b0 + DEC_SPR, R[1]);
+    score(b0, R[0]);
+    if (b0 + DEC_SPR >= nc) break;
+    if (b0 + 2 * DEC_SPR < nc) load(b0 + 2 * DEC_SPR, R[0]);
+    score(b0 + DEC_SPR, R[1]);
   }
 }
 
-// Per row (one wave): the entmax threshold over the row's scores in zrow,
-// the mask words, and the compacted ascending list of the selected blocks
-// with their log2 priors, then the query's own block (prior 0).
+// Per row (one 4-wave workgroup): the row's scores (decode_row_scores, all
+// waves), then on wave 0 the entmax threshold over them, the mask words,
+// and the compacted ascending list of the selected blocks with their log2
+// priors, then the query's own block (prior 0).
 template <int NPL>
-__global__ __launch_bounds__(64) void decode_select_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void decode_select_kernel(DecodeArgs a) {
+  __shared__ float zs[DASH_BLOCK * 32];  // scores of up to 2048 candidates
   const int row = blockIdx.x;
   const int nbc = a.N / DASH_BLOCK;  // capacity in blocks: row stride of the summaries and the lists
   const int n = decode_row_len(a, row);
   const int l = threadIdx.x;
   const int nbw = (nbc + 31) / 32;   // mask words per row
   if (n < 1 || n > a.N) {  // length out of range: empty list and mask; the combine writes NaN
+    if (l >= 64) return;
     if (l == 0) {
       a.sel_cnt[row] = 0;
       if (a.nsel) a.nsel[row] = -1;
@@ -115,8 +126,11 @@ __global__ __launch_bounds__(64) void decode_select_kernel(DecodeArgs a) {
   }
   const int own = (n - 1) / DASH_BLOCK;  // the query's block
   const int nc = own;                    // the complete blocks before it are the candidates
+  decode_row_scores(a, row, nc, zs);
+  __syncthreads();
+  if (l >= 64) return;
   const CoarseArith ca = a.ca;
-  const float* us = a.zrow + (size_t)row * nbc;
+  const float* us = zs;
   float u[NPL];
 #pragma unroll
   for (int k = 0; k < NPL; ++k) {
@@ -591,16 +605,14 @@ hipError_t launch_decode(const DecodeArgs& a0, int dtype, hipStream_t st) {
   DecodeArgs a = a0;
   a.nsplit = DASH_DEC_SPLIT;
   const int nb = a.N / DASH_BLOCK;
-  decode_scores_kernel<<<dim3((nb + DEC_SPW - 1) / DEC_SPW, a.SH), 256, 0, st>>>(a);
+  if (nb <= 128) decode_select_kernel<2><<<a.SH, 256, 0, st>>>(a);
+  else if (nb <= 256) decode_select_kernel<4><<<a.SH, 256, 0, st>>>(a);
+  else if (nb <= 512) decode_select_kernel<8><<<a.SH, 256, 0, st>>>(a);
+  else if (nb <= 1024) decode_select_kernel<16><<<a.SH, 256, 0, st>>>(a);
+  else if (nb <= 1536) decode_select_kernel<24><<<a.SH, 256, 0, st>>>(a);
+  else decode_select_kernel<32><<<a.SH, 256, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (nb <= 128) decode_select_kernel<2><<<a.SH, 64, 0, st>>>(a);
-  else if (nb <= 256) decode_select_kernel<4><<<a.SH, 64, 0, st>>>(a);
-  else if (nb <= 512) decode_select_kernel<8><<<a.SH, 64, 0, st>>>(a);
-  else if (nb <= 1024) decode_select_kernel<16><<<a.SH, 64, 0, st>>>(a);
-  else if (nb <= 1536) decode_select_kernel<24><<<a.SH, 64, 0, st>>>(a);
-  else decode_select_kernel<32><<<a.SH, 64, 0, st>>>(a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.grp == 1) {
     decode_attend_kernel<<<dim3(a.nsplit, a.SH), 256, 0, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
