@@ -44,12 +44,7 @@ struct FwdArgs {
 // (operand A, row = lane % 32 is summary `brow`) against the 32 queries in
 // qb (operand B), bf16 MFMA with fp32 accumulation, k-steps in order.
 template <int D>
-__device__ __forceinline__ f32x16 coarse_acc_chunk(const bf16_t* kb, int brow, const bf16x8 (&qb)[D / 16]) {
-  const int h = lane_id() >> 5;
-  // all operand loads first, so that they are in flight together
-  bf16x8 ka[D / 16];
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) ka[s] = load8(kb + (size_t)brow * D + 16 * s + 8 * h);
+__device__ __forceinline__ f32x16 coarse_acc_q(const bf16x8 (&ka)[D / 16], const bf16x8 (&qb)[D / 16]) {
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
@@ -57,22 +52,42 @@ __device__ __forceinline__ f32x16 coarse_acc_chunk(const bf16_t* kb, int brow, c
   for (int s = 0; s < D / 16; ++s) acc = mfma32(ka[s], qb[s], acc);
   return acc;
 }
-
-// The same accumulation with the query operands read from LDS (q_lds: 32
-// query rows, row pitch `pitch` bf16) instead of registers: identical MFMA
-// sequence and operands, so identical bits.
 template <int D>
-__device__ __forceinline__ f32x16 coarse_acc_chunk_lds(const bf16_t* kb, int brow, const bf16_t* q_lds, int pitch) {
-  const int l = lane_id(), h = l >> 5, j = l & 31;
+__device__ __forceinline__ f32x16 coarse_acc_chunk(const bf16_t* kb, int brow, const bf16x8 (&qb)[D / 16]) {
+  const int h = lane_id() >> 5;
+  // all operand loads first, so that they are in flight together
   bf16x8 ka[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) ka[s] = load8(kb + (size_t)brow * D + 16 * s + 8 * h);
+  return coarse_acc_q<D>(ka, qb);
+}
+
+// The same accumulation with the query operands read from LDS (q_lds: 32
+// query rows, row pitch `pitch` bf16) instead of registers: identical MFMA
+// sequence and operands, so identical bits.  Split into the summary loads
+// and the products, so that a caller can have the loads of its next chunk
+// in flight while it works on this one.
+template <int D>
+__device__ __forceinline__ void coarse_load_kbar(const bf16_t* kb, int brow, bf16x8 (&ka)[D / 16]) {
+  const int h = lane_id() >> 5;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) ka[s] = load8(kb + (size_t)brow * D + 16 * s + 8 * h);
+}
+template <int D>
+__device__ __forceinline__ f32x16 coarse_acc_lds(const bf16x8 (&ka)[D / 16], const bf16_t* q_lds, int pitch) {
+  const int l = lane_id(), h = l >> 5, j = l & 31;
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) acc = mfma32(ka[s], load8(q_lds + j * pitch + 16 * s + 8 * h), acc);
   return acc;
+}
+template <int D>
+__device__ __forceinline__ f32x16 coarse_acc_chunk_lds(const bf16_t* kb, int brow, const bf16_t* q_lds, int pitch) {
+  bf16x8 ka[D / 16];
+  coarse_load_kbar<D>(kb, brow, ka);
+  return coarse_acc_lds<D>(ka, q_lds, pitch);
 }
 
 // log2 priors of one wave's 32 query rows (lane column j) for the listed

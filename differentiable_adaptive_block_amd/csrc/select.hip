@@ -217,9 +217,14 @@ __global__ __launch_bounds__(64 * NW) void select_mfma_kernel(SelectArgs a) {
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
       qb[s] = qin ? load8(qh + (size_t)(row0 + j) * D + 16 * s + 8 * h) : bf16x8{};
+    // the next sub-chunk's summaries are requested once this one's
+    // products have read theirs
+    bf16x8 ka[D / 16];
+    coarse_load_kbar<D>(kb, w * 32 + j < nc ? w * 32 + j : 0, ka);
     for (int c = w; c * 32 < nc; c += NW) {
-      const int brow = c * 32 + j;
-      f32x16 acc = coarse_acc_chunk<D>(kb, brow < nc ? brow : 0, qb);
+      f32x16 acc = coarse_acc_q<D>(ka, qb);
+      const int cn = c + NW;
+      if (cn * 32 < nc) coarse_load_kbar<D>(kb, cn * 32 + j < nc ? cn * 32 + j : 0, ka);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int b = c * 32 + acc_row32(r, l);
@@ -288,6 +293,12 @@ __global__ __launch_bounds__(512, 4) void select_chunked_kernel(SelectArgs a) {
   const bf16_t* kb = reinterpret_cast<const bf16_t*>(a.kbar) + (bh / a.grp) * nb * D;
   float u[NPL];
   if (nc > 0) {
+    // this wave's summaries of chunk ch: sub-chunk 8 ch + w of 32 blocks;
+    // those of the next chunk are requested as soon as this chunk's products
+    // have read theirs, so their latency overlaps the score tile's hand-over
+    auto brow_of = [&](int ch) { const int b = (ch * CB / 32 + w) * 32 + j; return b < nc ? b : 0; };
+    bf16x8 ka[D / 16];
+    coarse_load_kbar<D>(kb, brow_of(0), ka);
     for (int x = tid; x < 32 * (D / 8); x += 512) {
       const int r = x / (D / 8), c8 = x % (D / 8);
       *reinterpret_cast<uint4*>(&qs[r * QP + 8 * c8]) =
@@ -297,16 +308,18 @@ __global__ __launch_bounds__(512, 4) void select_chunked_kernel(SelectArgs a) {
     for (int ch = 0; ch < NCH; ++ch) {
       const int c0 = ch * CB;
       if (c0 < nc) {  // the same on every thread
-        __syncthreads();  // the previous chunk's reads are done
+        __syncthreads();  // the previous chunk's reads are done (first chunk: the queries are staged)
         const int c = c0 / 32 + w;  // 8 sub-chunks of 32 blocks, one per wave
         if (c * 32 < nc) {
-          const int brow = c * 32 + j;
-          const f32x16 acc = coarse_acc_chunk_lds<D>(kb, brow < nc ? brow : 0, qs, QP);
+          const f32x16 acc = coarse_acc_lds<D>(ka, qs, QP);
+          if (ch + 1 < NCH && c0 + CB < nc) coarse_load_kbar<D>(kb, brow_of(ch + 1), ka);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int b = c * 32 + acc_row32(r, l);
             if (b < nc) zs[j * (CB + 1) + (b - c0)] = ca.u_of(acc[r]);
           }
+        } else if (ch + 1 < NCH && c0 + CB < nc) {
+          coarse_load_kbar<D>(kb, brow_of(ch + 1), ka);
         }
         __syncthreads();
       }
