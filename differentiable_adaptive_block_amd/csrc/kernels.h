@@ -201,10 +201,8 @@ __device__ __forceinline__ f32x16 prior_chunk32_heads(const bf16_t* KB, const in
 // (slot/4)%2; the other half's value comes across with permlane32_swap.
 __device__ __forceinline__ float prior_pick(const f32x16& pacc, int e) {
   const int slot = e & 31;
-  const int rr = 4 * (slot >> 3) + (slot & 3);
-  float v = pacc[0];
-#pragma unroll
-  for (int r = 1; r < 16; ++r) v = (r == rr) ? pacc[r] : v;
+  const int rr = __builtin_amdgcn_readfirstlane(4 * (slot >> 3) + (slot & 3));  // the same on every lane
+  const float v = pacc[rr];
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   // sw[0]: lanes 0-31 keep their value, lanes 32-63 get lanes 0-31's;
   // sw[1]: lanes 0-31 get lanes 32-63's, lanes 32-63 keep theirs
