@@ -108,7 +108,15 @@ int32_t dash_query_tile(void);
 /* Element counts of the eight dash_sel buffers, in struct order. */
 dash_status dash_sel_sizes(const dash_params* p, size_t out_elems[8]);
 
-/* Bytes of device workspace dash_fwd / dash_bwd need (dash_fwd: always 0). */
+/*
+ * Bytes of device workspace dash_fwd / dash_bwd need (dash_fwd: always 0).
+ * dash_bwd's grows with T^2: besides O(B H T D) fp32 buffers it keeps, per
+ * (query tile, list slot, row), G and the log2 prior as fp32, with room for
+ * every slot a tile's list can hold: min(T/64, 2t + 2) for causal tile t
+ * (the lower triangle), T/64 when not causal.  Causal, that is about
+ * B H T^2 / 64 floats for each of the two: 541 MB in all at B2 H16 T16384,
+ * 8.6 GB at B1 H32 T65536.
+ */
 size_t dash_fwd_workspace_bytes(const dash_params* p);
 size_t dash_bwd_workspace_bytes(const dash_params* p);
 
@@ -117,6 +125,12 @@ size_t dash_bwd_workspace_bytes(const dash_params* p);
  * accumulated in fp64 and rounded once to dtype.  (Stage 0 of the pages,
  * "What alpha-entmax changes"; used to build the summaries of a decode cache.)
  * Any T that is a multiple of 64 is accepted here (no 65536 limit).
+ * For bf16 keys the fp64 sum of a block is exact, so it does not depend on
+ * the summation order (this kernel, dash_cache_append and a sequential sum
+ * agree bit for bit), as long as the block's non-zero magnitudes lie within
+ * 2^39 of each other (8 significant bits per value, 6 bits of carry for 64
+ * terms, 53 in a double) and the mean is a normal bf16; for keys outside
+ * that range the rounding of the mean may depend on the order.
  */
 dash_status dash_pool(const dash_params* p, const void* k, void* kbar, void* stream);
 
