@@ -558,6 +558,182 @@ __global__ __launch_bounds__(64 * NW) void decode_attend_group_kernel(DecodeArgs
   }
 }
 
+// Split-KV attention for a group of G = 2 or 4 heads, streamed through
+// registers: workgroup (split s, group), its 4 waves take list entries
+// s * 4 + w stepping by 4 * nsplit, as in the per-head kernel; a wave loads
+// a block's 64 keys and values once (16-byte loads, 16 lanes per 256-byte
+// row) and computes every head of the group from those registers, so each
+// block is read from HBM once per group with a whole block in flight per
+// wave.  The waves' per-head partials are merged in LDS and wave h writes
+// head h's partial of this split.
+template <int G>
+__global__ __launch_bounds__(256) void decode_attend_group_reg_kernel(DecodeArgs a) {
+  constexpr int D = 128;
+  __shared__ float red_m[4][G], red_l[4][G];
+  __shared__ float red_o[4][G][D];
+  const int split = blockIdx.x, grp_id = blockIdx.y;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int g = l >> 4, c = l & 15;
+  const int row0 = grp_id * G;
+  const int nbc = a.N / DASH_BLOCK;
+  const int n = decode_row_len(a, row0);  // in range whenever the list is not empty
+  const int cnt = a.sel_cnt[row0];
+  const int* list = a.sel_blk + (size_t)row0 * nbc;
+  const float* lpl = a.sel_lp + (size_t)row0 * nbc;
+  const bf16_t* K = reinterpret_cast<const bf16_t*>(a.kc) + (size_t)grp_id * a.N * D;
+  const bf16_t* V = reinterpret_cast<const bf16_t*>(a.vc) + (size_t)grp_id * a.N * D;
+  const float sl2 = a.fine_scale * LOG2E_F;
+  const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+  // each head's query: this lane's 8 features as bf16 pairs
+  bf16x2 qh[G][4];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const uint4 r = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.q) + (size_t)(row0 + h) * D + c * 8);
+    qh[h][0] = __builtin_bit_cast(bf16x2, r.x);
+    qh[h][1] = __builtin_bit_cast(bf16x2, r.y);
+    qh[h][2] = __builtin_bit_cast(bf16x2, r.z);
+    qh[h][3] = __builtin_bit_cast(bf16x2, r.w);
+  }
+  float m[G], lsum[G], o[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    lsum[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+  }
+  const int stride = 4 * a.nsplit;
+  for (int en = split * 4 + w; en < cnt; en += stride) {
+    const int b = list[en];
+    const float pr = lpl[en];
+    const bool partial = (b + 1) * DASH_BLOCK > n;  // the own block, partly filled
+    // keys first: every head's scores, running max and bf16 weights (so the
+    // key registers are free before the values are loaded into them)
+    uint4 r[16];
+    {
+      const bf16_t* kb = K + (size_t)b * DASH_BLOCK * D;
+#pragma unroll
+      for (int it = 0; it < 16; ++it) r[it] = *reinterpret_cast<const uint4*>(kb + (size_t)(it * 4 + g) * D + c * 8);
+    }
+    bf16x2 pw[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float sc[16];
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        float part = __builtin_amdgcn_fdot2_f32_bf16(qh[h][0], __builtin_bit_cast(bf16x2, r[it].x), 0.f, false);
+        part = __builtin_amdgcn_fdot2_f32_bf16(qh[h][1], __builtin_bit_cast(bf16x2, r[it].y), part, false);
+        part = __builtin_amdgcn_fdot2_f32_bf16(qh[h][2], __builtin_bit_cast(bf16x2, r[it].z), part, false);
+        part = __builtin_amdgcn_fdot2_f32_bf16(qh[h][3], __builtin_bit_cast(bf16x2, r[it].w), part, false);
+        sc[it] = sum16(part) * sl2 + pr;
+      }
+      if (partial) {
+#pragma unroll
+        for (int it = 0; it < 16; ++it)
+          if (b * DASH_BLOCK + it * 4 + g >= n) sc[it] = -INFINITY;
+      }
+      float mx = sc[0];
+#pragma unroll
+      for (int it = 1; it < 16; ++it) mx = fmaxf(mx, sc[it]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mn = fmaxf(m[h], mx);
+      const float rs = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m[h] - mn);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[h][e] *= rs;
+      // weights rounded to bf16 two keys at a time; the normaliser sums the
+      // same rounded weights
+      float ps = 0.f;
+#pragma unroll
+      for (int it = 0; it < 16; it += 2) {
+        bf16x2 pp;
+        pp[0] = (__bf16)__builtin_amdgcn_exp2f(sc[it] - mn);
+        pp[1] = (__bf16)__builtin_amdgcn_exp2f(sc[it + 1] - mn);
+        ps = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, ps, false);
+        pw[h][it >> 1] = pp;
+      }
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      lsum[h] = lsum[h] * rs + ps;
+      m[h] = mn;
+    }
+    // then the values: each v_dot2 adds two keys' products for one feature
+    // (the two keys' values paired by v_perm).  The lane offset passes
+    // through an empty asm that reads the last head's max, so the value
+    // loads are not moved above the scores (which would keep both blocks
+    // in registers at once)
+    {
+      int voff = g * D + c * 8;
+      asm volatile("" : "+v"(voff) : "v"(m[G - 1]));
+      const bf16_t* vb = V + (size_t)b * DASH_BLOCK * D + voff;
+#pragma unroll
+      for (int it = 0; it < 16; ++it) r[it] = *reinterpret_cast<const uint4*>(vb + (size_t)(it * 4) * D);
+    }
+    if (partial) {
+#pragma unroll
+      for (int it = 0; it < 16; ++it)
+        if (b * DASH_BLOCK + it * 4 + g >= n) r[it] = make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int it = 0; it < 16; it += 2) {
+      const uint32_t wa[4] = {r[it].x, r[it].y, r[it].z, r[it].w};
+      const uint32_t wb[4] = {r[it + 1].x, r[it + 1].y, r[it + 1].z, r[it + 1].w};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const bf16x2 lo = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(wb[d], wa[d], 0x05040100u));
+        const bf16x2 hi = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(wb[d], wa[d], 0x07060302u));
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          o[h][2 * d] = __builtin_amdgcn_fdot2_f32_bf16(pw[h][it >> 1], lo, o[h][2 * d], false);
+          o[h][2 * d + 1] = __builtin_amdgcn_fdot2_f32_bf16(pw[h][it >> 1], hi, o[h][2 * d + 1], false);
+        }
+      }
+    }
+  }
+  // merge the 4 waves' partials of each head in LDS
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      o[h][e] += __shfl_xor(o[h][e], 16, 64);
+      o[h][e] += __shfl_xor(o[h][e], 32, 64);
+    }
+    if (g == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red_o[w][h][c * 8 + e] = o[h][e];
+    }
+    if (l == 0) {
+      red_m[w][h] = m[h];
+      red_l[w][h] = lsum[h];
+    }
+  }
+  __syncthreads();
+  if (w >= G) return;
+  const int h = w;
+  float M = -INFINITY;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) M = fmaxf(M, red_m[x][h]);
+  float sc4[4], L = 0.f;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    sc4[x] = (red_m[x][h] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(red_m[x][h] - M);
+    L += red_l[x][h] * sc4[x];
+  }
+  float* part = a.part + ((size_t)(row0 + h) * a.nsplit + split) * (D + 2);
+#pragma unroll
+  for (int d2 = 0; d2 < 2; ++d2) {
+    const int d = l + 64 * d2;
+    float acc = 0.f;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) acc = fmaf(red_o[x][h][d], sc4[x], acc);
+    part[d] = acc;
+  }
+  if (l == 0) {
+    part[D] = M;
+    part[D + 1] = L;
+  }
+}
+
 // ---------------------------------------------------------------------------- cache maintenance
 
 // One wave per row, 4 rows per workgroup; lane l moves elements 2l and 2l+1
@@ -623,11 +799,19 @@ hipError_t launch_decode(const DecodeArgs& a0, int dtype, hipStream_t st) {
     if (a.SH % a.grp) return hipErrorInvalidValue;
     decode_group_merge_kernel<<<a.SH / a.grp, 256, 0, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.grp == 2 || a.grp == 4) {
+      // blocks streamed through registers, all the group's heads per wave
+      a.nsplit = DASH_DEC_SPLIT;
+      const dim3 grid(a.nsplit, a.SH / a.grp);
+      if (a.grp == 2) decode_attend_group_reg_kernel<2><<<grid, 256, 0, st>>>(a);
+      else decode_attend_group_reg_kernel<4><<<grid, 256, 0, st>>>(a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      decode_combine_kernel<DASH_DEC_SPLIT><<<(a.SH + 3) / 4, 256, 0, st>>>(a);
+      return hipGetLastError();
+    }
     a.nsplit = DASH_DEC_SPLIT_GQA;  // a group walks G times the blocks of a row: more splits
     const dim3 grid(a.nsplit, a.SH / a.grp);
-    if (a.grp == 2) decode_attend_group_kernel<2><<<grid, 128, 0, st>>>(a);
-    else if (a.grp == 4) decode_attend_group_kernel<4><<<grid, 256, 0, st>>>(a);
-    else if (a.grp == 8) decode_attend_group_kernel<8><<<grid, 512, 0, st>>>(a);
+    if (a.grp == 8) decode_attend_group_kernel<8><<<grid, 512, 0, st>>>(a);
     else return hipErrorNotSupported;
     if ((e = hipGetLastError()) != hipSuccess) return e;
     decode_combine_kernel<DASH_DEC_SPLIT_GQA><<<(a.SH + 3) / 4, 256, 0, st>>>(a);
