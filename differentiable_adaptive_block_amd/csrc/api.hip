@@ -122,7 +122,7 @@ size_t decode_ws_layout(const dash_decode_params* p, size_t off[6], int* nsplit,
   if (chunk) *chunk = ch;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o += (bytes + 255) & ~size_t(255); return r; };
-  off[0] = take(SH * nb * sizeof(float));          // each head's p (grouped-query merge)
+  off[0] = take(0);                                // (no longer used)
   off[1] = take(SH * 2 * sizeof(float));           // tau, lognorm
   off[2] = take(SH * sizeof(int));                 // list length
   off[3] = take(SH * nb * sizeof(int));            // list
@@ -638,7 +638,6 @@ static dash_status decode_common(const dash_decode_params* p, const void* q, con
   da.nsel = nsel;
   da.tau_out = tau;
   da.mask = mask;
-  da.zrow = reinterpret_cast<float*>(ws + off[0]);
   da.rowstat = reinterpret_cast<float*>(ws + off[1]);
   da.sel_cnt = reinterpret_cast<int*>(ws + off[2]);
   da.sel_blk = reinterpret_cast<int*>(ws + off[3]);

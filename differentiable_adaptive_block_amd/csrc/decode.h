@@ -17,7 +17,6 @@ struct DecodeArgs {
   float* tau_out;    // [SH] or null
   uint32_t* mask;    // [SH, ceil(N / 64 / 32)] or null: bit b set iff candidate block b is selected
   // workspace
-  float* zrow;       // [SH, N / 64]   each head's p over its candidates (grouped-query merge)
   float* rowstat;    // [SH, 2]        tau, lognorm
   int* sel_cnt;      // [SH]           list length (0: length out of range)
   int* sel_blk;      // [SH, N / 64]   selected candidate blocks, ascending, then the query's own block

@@ -101,6 +101,165 @@ __device__ __forceinline__ void decode_row_scores(const DecodeArgs& a, int row, 
   }
 }
 
+// The scores of the G query heads of a group (rows row0 .. row0 + G - 1)
+// over their shared KV head's summaries, into zs[h * zst + b]: one read of
+// the summaries for the G heads, each head's score formed exactly as in
+// decode_row_scores.
+template <int G>
+__device__ __forceinline__ void decode_group_scores(const DecodeArgs& a, int row0, int nc, float* zs, int zst) {
+  constexpr int D = 128;
+  const int nbc = a.N / DASH_BLOCK;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const bf16_t* kb = reinterpret_cast<const bf16_t*>(a.kbar) + (size_t)(row0 / a.grp) * nbc * D + (l & 15) * 8;
+  const CoarseArith ca = a.ca;
+  float qf[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    unpack8(*reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.q) + (size_t)(row0 + h) * D + (l & 15) * 8),
+            qf[h]);
+  auto bof = [&](int b0, int x) { return b0 + (x * 4 + w) * 4 + (l >> 4); };
+  uint4 R[2][DEC_UN];
+  auto load = [&](int b0, uint4 (&r)[DEC_UN]) {
+#pragma unroll
+    for (int x = 0; x < DEC_UN; ++x) {
+      const int b = bof(b0, x);
+      r[x] = b < nc ? *reinterpret_cast<const uint4*>(kb + (size_t)b * D) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto score = [&](int b0, const uint4 (&r)[DEC_UN]) {
+#pragma unroll
+    for (int x = 0; x < DEC_UN; ++x) {
+      const int b = bof(b0, x);
+      float kf[8];
+      unpack8(r[x], kf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part = fmaf(qf[h][e], kf[e], part);
+        part = sum16(part);
+        if (b < nc && (l & 15) == 0) zs[h * zst + b] = ca.u_of(part);
+      }
+    }
+  };
+  load(0, R[0]);
+  for (int b0 = 0; b0 < nc; b0 += 2 * DEC_SPR) {
+    if (b0 + DEC_SPR < nc) load(b0 + DEC_SPR, R[1]);
+    score(b0, R[0]);
+    if (b0 + DEC_SPR >= nc) break;
+    if (b0 + 2 * DEC_SPR < nc) load(b0 + 2 * DEC_SPR, R[0]);
+    score(b0 + DEC_SPR, R[1]);
+  }
+}
+
+// Grouped-query heads (entmax head aggregation): one 4-wave workgroup per
+// group of G query heads sharing a KV head.  Every head's scores from one
+// read of the summaries; each head's own threshold, mask words and count
+// (wave h, and h + 4 when G = 8); then the group's list: the blocks where
+// pbar = (1/G) sum_h p_h > 0, with log2 pbar as prior, then the own block
+// (prior 0), in the group's first row, and the count in every row of the
+// group.  A length out of range gives every row of the group an empty list.
+template <int NPL, int G>
+__global__ __launch_bounds__(256) void decode_select_group_kernel(DecodeArgs a) {
+  constexpr int ZST = DASH_BLOCK * 32;  // up to 2048 candidates per head
+  __shared__ float zs[G * ZST];         // per head: scores, then p
+  __shared__ int wcnt[4];
+  const int row0 = blockIdx.x * G;
+  const int nbc = a.N / DASH_BLOCK;
+  const int n = decode_row_len(a, row0);  // the group's rows are one sequence's heads
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int nbw = (nbc + 31) / 32;
+  if (n < 1 || n > a.N) {
+    for (int h = w; h < G; h += 4) {
+      const int row = row0 + h;
+      if (l == 0) {
+        a.sel_cnt[row] = 0;
+        if (a.nsel) a.nsel[row] = -1;
+        if (a.tau_out) a.tau_out[row] = __uint_as_float(0x7fc00000u);
+      }
+      if (a.mask)
+        for (int x = l; x < nbw; x += 64) a.mask[(size_t)row * nbw + x] = 0u;
+    }
+    return;
+  }
+  const int own = (n - 1) / DASH_BLOCK;
+  const int nc = own;
+  decode_group_scores<G>(a, row0, nc, zs, ZST);
+  __syncthreads();
+  const CoarseArith ca = a.ca;
+  for (int h = w; h < G; h += 4) {
+    const int row = row0 + h;
+    float* zh = zs + h * ZST;
+    float u[NPL];
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) {
+      const int idx = l + 64 * k;
+      u[k] = idx < nc ? zh[idx] : -INFINITY;
+    }
+    EntmaxOut e;
+    if (nc > 0) e = entmax_solve<NPL, 64>(u, nc, ca);
+    else { e.tau = __uint_as_float(0x7fc00000u); e.lognorm = 0.f; e.nsel = 0; e.passes = 0; }
+    if (a.mask) {
+      uint32_t* mw = a.mask + (size_t)row * nbw;
+#pragma unroll
+      for (int k = 0; k < NPL; ++k) {
+        const int idx = l + 64 * k;
+        const unsigned long long bal = __ballot(idx < nc && ca.selected(u[k], e.tau));
+        if (l == 0 && 2 * k < nbw) mw[2 * k] = (uint32_t)bal;
+        if (l == 0 && 2 * k + 1 < nbw) mw[2 * k + 1] = (uint32_t)(bal >> 32);
+      }
+    }
+    // this head's p over the candidates (its own LDS row, this wave only)
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) {
+      const int idx = l + 64 * k;
+      if (idx < nc) zh[idx] = ca.selected(u[k], e.tau) ? __expf(ca.logp(u[k], e.tau, e.lognorm)) : 0.f;
+    }
+    if (l == 0) {
+      a.rowstat[2 * row] = e.tau;
+      a.rowstat[2 * row + 1] = e.lognorm;
+      if (a.nsel) a.nsel[row] = e.nsel;
+      if (a.tau_out) a.tau_out[row] = e.tau;
+    }
+  }
+  __syncthreads();
+  // the group's list, 256 candidates per step (a ballot per wave, the
+  // waves' counts added in LDS)
+  int* list = a.sel_blk + (size_t)row0 * nbc;
+  float* lp = a.sel_lp + (size_t)row0 * nbc;
+  const float inv = 1.f / (float)G;
+  int base = 0;
+  for (int c0 = 0; c0 < own; c0 += 256) {
+    const int idx = c0 + tid;
+    float ps = 0.f;
+    if (idx < own)
+#pragma unroll
+      for (int h = 0; h < G; ++h) ps += zs[h * ZST + idx];
+    const bool sl = ps > 0.f;
+    const unsigned long long bal = __ballot(sl);
+    if (l == 0) wcnt[w] = __popcll(bal);
+    __syncthreads();
+    int before = base, total = 0;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      before += x < w ? wcnt[x] : 0;
+      total += wcnt[x];
+    }
+    if (sl) {
+      const int pos = before + __popcll(bal & ((1ull << l) - 1ull));
+      list[pos] = idx;
+      lp[pos] = __log2f(ps * inv);
+    }
+    base += total;
+    __syncthreads();  // the counts are read before the next step overwrites them
+  }
+  if (tid == 0) {
+    list[base] = own;
+    lp[base] = 0.f;
+  }
+  if (tid < G) a.sel_cnt[row0 + tid] = base + 1;
+}
+
 // Per row (one 4-wave workgroup): the row's scores (decode_row_scores, all
 // waves), then on wave 0 the entmax threshold over them, the mask words,
 // and the compacted ascending list of the selected blocks with their log2
@@ -150,22 +309,6 @@ __global__ __launch_bounds__(256) void decode_select_kernel(DecodeArgs a) {
       if (l == 0 && 2 * k < nbw) mw[2 * k] = (uint32_t)bal;
       if (l == 0 && 2 * k + 1 < nbw) mw[2 * k + 1] = (uint32_t)(bal >> 32);
     }
-  }
-  if (a.grp > 1) {
-    // grouped heads: this head's p over the candidates, for the group's merge
-    float* pr = a.zrow + (size_t)row * nbc;
-#pragma unroll
-    for (int k = 0; k < NPL; ++k) {
-      const int idx = l + 64 * k;
-      if (idx < nc) pr[idx] = ca.selected(u[k], e.tau) ? __expf(ca.logp(u[k], e.tau, e.lognorm)) : 0.f;
-    }
-    if (l == 0) {
-      a.rowstat[2 * row] = e.tau;
-      a.rowstat[2 * row + 1] = e.lognorm;
-      if (a.nsel) a.nsel[row] = e.nsel;
-      if (a.tau_out) a.tau_out[row] = e.tau;
-    }
-    return;
   }
   int* list = a.sel_blk + (size_t)row * nbc;
   float* lp = a.sel_lp + (size_t)row * nbc;
@@ -361,57 +504,6 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------- grouped heads
-
-// Grouped-query heads (entmax head aggregation): the grp heads of a group
-// share one list, the blocks where pbar = (1/grp) sum_h p_h > 0, with log2
-// pbar as prior, then the own block (prior 0).  One 4-wave workgroup per
-// group, 256 candidates per step (a ballot per wave, the waves' counts
-// added in LDS); the list sits in the group's first row.  A length out of
-// range gives every row of the group an empty list.
-__global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeArgs a) {
-  __shared__ int wcnt[4];
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int row0 = blockIdx.x * a.grp;
-  const int nbc = a.N / DASH_BLOCK;
-  const int n = decode_row_len(a, row0);
-  if (n < 1 || n > a.N) {
-    if (tid < a.grp) a.sel_cnt[row0 + tid] = 0;
-    return;
-  }
-  const int own = (n - 1) / DASH_BLOCK;
-  int* list = a.sel_blk + (size_t)row0 * nbc;
-  float* lp = a.sel_lp + (size_t)row0 * nbc;
-  const float inv = 1.f / (float)a.grp;
-  int base = 0;
-  for (int c0 = 0; c0 < own; c0 += 256) {
-    const int idx = c0 + tid;
-    float ps = 0.f;
-    if (idx < own)
-      for (int g = 0; g < a.grp; ++g) ps += a.zrow[(size_t)(row0 + g) * nbc + idx];
-    const bool s = ps > 0.f;
-    const unsigned long long bal = __ballot(s);
-    if (l == 0) wcnt[w] = __popcll(bal);
-    __syncthreads();
-    int before = base, total = 0;
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      before += x < w ? wcnt[x] : 0;
-      total += wcnt[x];
-    }
-    if (s) {
-      const int pos = before + __popcll(bal & ((1ull << l) - 1ull));
-      list[pos] = idx;
-      lp[pos] = __log2f(ps * inv);
-    }
-    base += total;
-    __syncthreads();  // the counts are read before the next step overwrites them
-  }
-  if (tid == 0) {
-    list[base] = own;
-    lp[base] = 0.f;
-  }
-  if (tid < a.grp) a.sel_cnt[row0 + tid] = base + 1;
-}
 
 // Split-KV attention for a group: workgroup (split, group), wave w = the
 // group's head w; the workgroup walks list entries split, split + nsplit, ...
@@ -776,20 +868,32 @@ hipError_t launch_append(const AppendArgs& a, int dtype, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int G>
+static hipError_t launch_select_group(const DecodeArgs& a, int nb, hipStream_t st) {
+  const int ng = a.SH / G;
+  if (nb <= 128) decode_select_group_kernel<2, G><<<ng, 256, 0, st>>>(a);
+  else if (nb <= 256) decode_select_group_kernel<4, G><<<ng, 256, 0, st>>>(a);
+  else if (nb <= 512) decode_select_group_kernel<8, G><<<ng, 256, 0, st>>>(a);
+  else if (nb <= 1024) decode_select_group_kernel<16, G><<<ng, 256, 0, st>>>(a);
+  else if (nb <= 1536) decode_select_group_kernel<24, G><<<ng, 256, 0, st>>>(a);
+  else decode_select_group_kernel<32, G><<<ng, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const DecodeArgs& a0, int dtype, hipStream_t st) {
   if (dtype != 1 || a0.D != 128) return hipErrorNotSupported;
   DecodeArgs a = a0;
   a.nsplit = DASH_DEC_SPLIT;
   const int nb = a.N / DASH_BLOCK;
-  if (nb <= 128) decode_select_kernel<2><<<a.SH, 256, 0, st>>>(a);
-  else if (nb <= 256) decode_select_kernel<4><<<a.SH, 256, 0, st>>>(a);
-  else if (nb <= 512) decode_select_kernel<8><<<a.SH, 256, 0, st>>>(a);
-  else if (nb <= 1024) decode_select_kernel<16><<<a.SH, 256, 0, st>>>(a);
-  else if (nb <= 1536) decode_select_kernel<24><<<a.SH, 256, 0, st>>>(a);
-  else decode_select_kernel<32><<<a.SH, 256, 0, st>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
   if (a.grp == 1) {
+    if (nb <= 128) decode_select_kernel<2><<<a.SH, 256, 0, st>>>(a);
+    else if (nb <= 256) decode_select_kernel<4><<<a.SH, 256, 0, st>>>(a);
+    else if (nb <= 512) decode_select_kernel<8><<<a.SH, 256, 0, st>>>(a);
+    else if (nb <= 1024) decode_select_kernel<16><<<a.SH, 256, 0, st>>>(a);
+    else if (nb <= 1536) decode_select_kernel<24><<<a.SH, 256, 0, st>>>(a);
+    else decode_select_kernel<32><<<a.SH, 256, 0, st>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     decode_attend_kernel<<<dim3(a.nsplit, a.SH), 256, 0, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     decode_combine_kernel<DASH_DEC_SPLIT><<<(a.SH + 3) / 4, 256, 0, st>>>(a);
@@ -797,8 +901,11 @@ hipError_t launch_decode(const DecodeArgs& a0, int dtype, hipStream_t st) {
   }
   {
     if (a.SH % a.grp) return hipErrorInvalidValue;
-    decode_group_merge_kernel<<<a.SH / a.grp, 256, 0, st>>>(a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.grp == 2) e = launch_select_group<2>(a, nb, st);
+    else if (a.grp == 4) e = launch_select_group<4>(a, nb, st);
+    else if (a.grp == 8) e = launch_select_group<8>(a, nb, st);
+    else return hipErrorNotSupported;
+    if (e != hipSuccess) return e;
     if (a.grp == 2 || a.grp == 4) {
       // blocks streamed through registers, all the group's heads per wave
       a.nsplit = DASH_DEC_SPLIT;
