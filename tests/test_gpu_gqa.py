@@ -45,6 +45,9 @@ CASES = [
     ("h2-kv1-causal-a1", 1, 2, 1, 640, 128, True, 1.0, 2.0, (1, 3)),
     ("h4-kv2-causal-a2", 1, 4, 2, 576, 128, True, 2.0, 6.0, (1, 3)),
     ("h4-kv1-causal-T2048", 1, 4, 1, 2048, 128, True, 1.5, 6.0, (1, 4)),
+    # eight query heads per KV head: a wave's 32 columns are 8 heads x 4 rows
+    ("h8-kv1-causal-ragged", 1, 8, 1, 1088, 128, True, 1.5, 4.0, (1, 4)),
+    ("h8-kv1-noncausal-d64", 1, 8, 1, 512, 64, False, 1.25, 4.0, (1, 3)),
 ]
 
 
@@ -184,10 +187,14 @@ def _decode_check(out, ora, rows, prm, what, sel_of):
     return float(E.max()), float(E.mean())
 
 
+@pytest.mark.parametrize("heads", [(4, 2), (8, 2), (8, 1)], ids=["G2", "G4", "G8"])
 @pytest.mark.parametrize("lens", [None, [1, 65, 700]], ids=["full", "lengths"])
-def test_gqa_decode_small(lens):
+def test_gqa_decode_small(lens, heads):
+    """2, 4 and 8 query heads per KV head: the register-streamed walk (2, 4)
+    and the LDS-staged one (8), with each group size's selection kernel."""
     from differentiable_adaptive_block_amd import api
-    S, H, Hkv, C, D = 3, 4, 2, 1024, 128
+    H, Hkv = heads
+    S, C, D = 3, 1024, 128
     _say(f"[gqa decode] S{S} H{H} Hkv{Hkv} C{C} lens {lens}")
     w = inputs.make_decode(S, H, C, D, "bf16", (1, 4), seed=98, device="cpu", lens=lens, kv_heads=Hkv)
     q, kc, vc = (w[x].to(DEV) for x in ("q", "k", "v"))
