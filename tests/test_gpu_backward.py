@@ -137,3 +137,33 @@ def test_backward_training_16k_full_head():
     _say(f"  rel-L2 {errs}")
     for n, e in errs.items():
         assert e <= TOL, (n, e)
+
+
+@pytest.mark.parametrize("csm", [2.0, 7.0], ids=["literal", "calibrated"])
+def test_backward_64k_sampled(csm):
+    """The longest prefill (T 65536: tile lists of up to 1024 blocks, the
+    coarse kernel's summaries in 16 chunks, the dK/dV walk over up to 1024
+    query chunks), two heads at the 64K workload's coarse scales: dQ on
+    sampled rows and dK, dV and dkbar of the last key blocks (which only the
+    last 256 rows attend) against oracle.backward_rows."""
+    B, H, T, D = 1, 2, 65536, 128
+    cs = csm / math.sqrt(D)
+    _say(f"[backward] 64K B{B} H{H} T{T} D{D} coarse {csm}/sqrt(D) (sampled)")
+    w = inputs.make_prefill(B, H, T, D, "bf16", True, (1, 8), seed=1100 + int(csm), device=DEV, with_dout=True)
+    _, g = _run(w, 1.5, True, cs)
+    nb = T // 64
+    prm = oracle.Params(alpha=1.5, causal=True, coarse_scale=cs, storage="bf16")
+    rng = np.random.default_rng(int(csm))
+    for h in range(H):
+        x = {n: _np64(w[n][0:1, h:h + 1]) for n in ("q", "k", "v", "dout")}
+        tail = 4 * 64
+        rows = [(0, 0, i) for i in range(T - tail, T)]
+        rows += [(0, 0, int(i)) for i in rng.choice(T - tail, size=16, replace=False)]
+        ref = oracle.backward_rows(x["q"], x["k"], x["v"], x["dout"], prm, rows)
+        ridx = np.array([i for (_, _, i) in rows])
+        e_dq = rel_l2(_np64(g["dq"][0, h])[ridx], ref["dq"][0, 0][ridx])
+        e_dk = rel_l2(_np64(g["dk"][0, h])[T - tail:], ref["dk"][0, 0][T - tail:])
+        e_dv = rel_l2(_np64(g["dv"][0, h])[T - tail:], ref["dv"][0, 0][T - tail:])
+        e_kb = rel_l2(_np64(g["dkbar"][0, h])[nb - 4:nb - 1], ref["dkbar"][0, 0][nb - 4:nb - 1])
+        _say(f"  h={h} rel-L2 dq {e_dq:.2e} dk {e_dk:.2e} dv {e_dv:.2e} dkbar {e_kb:.2e}")
+        assert max(e_dq, e_dk, e_dv, e_kb) <= TOL
