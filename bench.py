@@ -678,7 +678,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="oracle rows per CPU worker")
     ap.add_argument("--cpu-workers", type=int, default=16)
-    ap.add_argument("--no-64k", action="store_true", help="skip the 64K prefill")
+    ap.add_argument("--no-64k", action="store_true", help="skip the 64K and 96K prefills")
     ap.add_argument("--no-decode", action="store_true", help="skip the 96K decode workloads")
     ap.add_argument("--no-training", action="store_true", help="skip the 16K training step")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -716,6 +716,10 @@ def main():
         r3c, _ = bench_prefill("prefill64k_sc7", max(2, args.steps // 3), 1, dev)
         log(f"prefill64k_sc7: {r3c}")
         extra["prefill_64k_calibrated"] = r3c
+        # the longest prefill the pages quote (96K)
+        r96, _ = bench_prefill("prefill96k", 2, 1, dev)
+        log(f"prefill96k: {r96}")
+        extra["prefill_96k"] = r96
 
     rg = bench_ragged(max(3, args.steps // 2), 1, dev)
     log(f"ragged 16K: {rg}")

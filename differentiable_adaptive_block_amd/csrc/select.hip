@@ -270,7 +270,7 @@ __global__ __launch_bounds__(64 * NW) void select_mfma_kernel(SelectArgs a) {
 // registers, so that two 8-wave workgroups fit on a CU.  Lane g of a row's 16 holds candidates g + 16 k,
 // chunk ch filling k = 16 ch .. 16 ch + 15.
 template <int D, int NPL>
-__global__ __launch_bounds__(512, 4) void select_chunked_kernel(SelectArgs a) {
+__global__ __launch_bounds__(512, NPL > 64 ? 2 : 4) void select_chunked_kernel(SelectArgs a) {
   constexpr int CB = 256;
   constexpr int NCH = NPL / 16;
   constexpr int QP = D + 8;
@@ -492,7 +492,12 @@ static hipError_t launch_select_mfma_d(const SelectArgs& a, int BH, hipStream_t 
     select_chunked_kernel<D, 32><<<dim3(a.T / 32, BH), 512, 0, st>>>(a);
     return hipGetLastError();
   }
-  select_chunked_kernel<D, 64><<<dim3(a.T / 32, BH), 512, 0, st>>>(a);
+  if (nb <= 1024) {
+    select_chunked_kernel<D, 64><<<dim3(a.T / 32, BH), 512, 0, st>>>(a);
+    return hipGetLastError();
+  }
+  // beyond 64K tokens: 96 scores per lane, one 8-wave workgroup per CU
+  select_chunked_kernel<D, 96><<<dim3(a.T / 32, BH), 512, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -504,7 +509,8 @@ static hipError_t launch_select_generic_t(const SelectArgs& a, int BH, hipStream
   else if (nb <= 128) select_generic_kernel<T, 2><<<grid, 64, 0, st>>>(a);
   else if (nb <= 256) select_generic_kernel<T, 4><<<grid, 64, 0, st>>>(a);
   else if (nb <= 512) select_generic_kernel<T, 8><<<grid, 64, 0, st>>>(a);
-  else select_generic_kernel<T, 16><<<grid, 64, 0, st>>>(a);
+  else if (nb <= 1024) select_generic_kernel<T, 16><<<grid, 64, 0, st>>>(a);
+  else select_generic_kernel<T, 24><<<grid, 64, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -66,6 +66,9 @@ CONFIGS = {
     # the same at a coarse scale that gives about 8% selected pairs
     "prefill64k_sc7": _cfg("prefill64k_sc7", "prefill", "bf16", 1.5, True, 7.0,
                            dict(B=1, H=32, T=65536, D=128), (1, 8), 1003, "calibrated coarse scale 7/sqrt(128)"),
+    # causal prefill at 96K (the longest prefill the pages quote), coarse scale 2/sqrt(128)
+    "prefill96k": _cfg("prefill96k", "prefill", "bf16", 1.5, True, 2.0, dict(B=1, H=32, T=98304, D=128),
+                       (1, 8), 1006),
     # decode: 16 sequences x 32 heads, 98304-token bf16 cache
     "decode96k": _cfg("decode96k", "decode", "bf16", 1.5, True, 1.0, dict(S=16, H=32, N=98304, D=128),
                       (1, 16), 1004),

@@ -61,7 +61,7 @@ typedef enum { DASH_F32 = 0, DASH_BF16 = 1 } dash_dtype;
 
 /* Prefill / training shapes and hyper-parameters. */
 typedef struct {
-  int32_t B, H, T, D;   /* batch, heads, sequence length (<= 65536; a multiple of 64 except as
+  int32_t B, H, T, D;   /* batch, heads, sequence length (<= 98304; a multiple of 64 except as
                            below), head dim (64|128) */
   int32_t block;        /* keys per block; must be 64 */
   float alpha;          /* entmax alpha in [1, 2] */

@@ -79,7 +79,7 @@ def _fwd(L, p, **ptrs):
     ("dtype", 7, _lib.DASH_EINVAL),
     ("block", 32, _lib.DASH_EUNSUPPORTED),
     ("D", 96, _lib.DASH_EUNSUPPORTED),
-    ("T", 65536 + 64, _lib.DASH_EUNSUPPORTED),
+    ("T", 98304 + 64, _lib.DASH_EUNSUPPORTED),
 ])
 def test_fwd_rejects_bad_params(L, field, value, status):
     p = _params(**{field: value})

@@ -139,17 +139,18 @@ def test_backward_training_16k_full_head():
         assert e <= TOL, (n, e)
 
 
-@pytest.mark.parametrize("csm", [2.0, 7.0], ids=["literal", "calibrated"])
-def test_backward_64k_sampled(csm):
-    """The longest prefill (T 65536: tile lists of up to 1024 blocks, the
-    coarse kernel's summaries in 16 chunks, the dK/dV walk over up to 1024
-    query chunks), two heads at the 64K workload's coarse scales: dQ on
+@pytest.mark.parametrize("T,csm", [(65536, 2.0), (65536, 7.0), (98304, 2.0)], ids=["64k-literal", "64k-calibrated", "96k"])
+def test_backward_long_sampled(T, csm):
+    """Long prefills (T 65536 and 98304: tile lists of up to 1024 / 1536 blocks,
+    the coarse kernel's summaries in 16 / 24 chunks, the dK/dV walk over up to
+    1024 / 1536 query chunks), at the 64K workload's coarse scales: dQ on
     sampled rows and dK, dV and dkbar of the last key blocks (which only the
     last 256 rows attend) against oracle.backward_rows."""
-    B, H, T, D = 1, 2, 65536, 128
+    B, H, D = 1, 2, 128
     cs = csm / math.sqrt(D)
-    _say(f"[backward] 64K B{B} H{H} T{T} D{D} coarse {csm}/sqrt(D) (sampled)")
-    w = inputs.make_prefill(B, H, T, D, "bf16", True, (1, 8), seed=1100 + int(csm), device=DEV, with_dout=True)
+    _say(f"[backward] B{B} H{H} T{T} D{D} coarse {csm}/sqrt(D) (sampled)")
+    w = inputs.make_prefill(B, H, T, D, "bf16", True, (1, 8), seed=1100 + int(csm) + T // 1024, device=DEV,
+                            with_dout=True)
     _, g = _run(w, 1.5, True, cs)
     nb = T // 64
     prm = oracle.Params(alpha=1.5, causal=True, coarse_scale=cs, storage="bf16")

@@ -156,6 +156,12 @@ def test_forward_64k_calibrated_prefill_sampled():
     assert d < 0.12, d
 
 
+def test_forward_96k_causal_prefill_sampled():
+    """The longest prefill (98304 tokens, 1536 blocks: the Stage-1 shape with 96
+    candidates per lane and six 256-block chunks)."""
+    _sampled("prefill96k", n_heads=1, n_rows=256)
+
+
 @pytest.mark.parametrize("T", [8192, 32768])
 def test_forward_stage1_kernel_sizes(T):
     """Sequence lengths that take the other Stage-1 kernel shapes: 128 blocks
