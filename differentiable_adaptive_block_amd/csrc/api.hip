@@ -114,7 +114,7 @@ size_t bwd_ws_layout(const dash_params* p, size_t off[4]) {
   return o;
 }
 
-size_t decode_ws_layout(const dash_decode_params* p, size_t off[6], int* nsplit, int* chunk) {
+size_t decode_ws_layout(const dash_decode_params* p, size_t off[5], int* nsplit, int* chunk) {
   const size_t SH = (size_t)p->S * p->H, nb = p->N / DASH_BLOCK, D = p->D;
   const int ch = 4;  // waves per split-KV workgroup
   const int ns = DASH_DEC_SPLIT;
@@ -122,17 +122,16 @@ size_t decode_ws_layout(const dash_decode_params* p, size_t off[6], int* nsplit,
   if (chunk) *chunk = ch;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o += (bytes + 255) & ~size_t(255); return r; };
-  off[0] = take(0);                                // (no longer used)
-  off[1] = take(SH * 2 * sizeof(float));           // tau, lognorm
-  off[2] = take(SH * sizeof(int));                 // list length
-  off[3] = take(SH * nb * sizeof(int));            // list
-  off[4] = take(SH * nb * sizeof(float));          // log2 priors
-  off[5] = take(SH * DASH_DEC_SPLIT_GQA * (D + 2) * sizeof(float));  // partials (the larger split count)
+  off[0] = take(SH * 2 * sizeof(float));           // tau, lognorm
+  off[1] = take(SH * sizeof(int));                 // list length
+  off[2] = take(SH * nb * sizeof(int));            // list
+  off[3] = take(SH * nb * sizeof(float));          // log2 priors
+  off[4] = take(SH * DASH_DEC_SPLIT_GQA * (D + 2) * sizeof(float));  // partials (the larger split count)
   return o;
 }
 
-// Scratch of dash_decode_static: the decode workspace (scores, row
-// statistics, block lists, split partials) of callers that cannot allocate.
+// Scratch of dash_decode_static: the decode workspace (row statistics,
+// block lists, split partials) of callers that cannot allocate.
 // Each GPU the library runs on holds its own copy until the process ends.
 // In host code `scratch` is the host-side stand-in of the array, not a
 // device address: the device address comes from hipGetSymbolAddress, once
@@ -219,7 +218,7 @@ size_t dash_bwd_workspace_bytes(const dash_params* p) {
 
 size_t dash_decode_workspace_bytes(const dash_decode_params* p) {
   if (!p || p->S < 1 || p->H < 1 || p->N < DASH_BLOCK || p->N % DASH_BLOCK) return 0;
-  size_t off[6];
+  size_t off[5];
   return decode_ws_layout(p, off, nullptr, nullptr);
 }
 
@@ -622,7 +621,7 @@ static dash_status decode_common(const dash_decode_params* p, const void* q, con
     return fail(DASH_EINVAL, "q, kc, vc, kbar and o must be non-null and 16-byte aligned");
   if (!ok_opt(lse) || !ok_opt(nsel) || !ok_opt(tau) || !ok_opt(mask))
     return fail(DASH_EINVAL, "lse/nsel/tau/mask must be 16-byte aligned");
-  size_t off[6];
+  size_t off[5];
   int nsplit = 0, chunk = 0;
   const size_t need = decode_ws_layout(p, off, &nsplit, &chunk);
   if (workspace_bytes < need) return fail(DASH_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
@@ -638,11 +637,11 @@ static dash_status decode_common(const dash_decode_params* p, const void* q, con
   da.nsel = nsel;
   da.tau_out = tau;
   da.mask = mask;
-  da.rowstat = reinterpret_cast<float*>(ws + off[1]);
-  da.sel_cnt = reinterpret_cast<int*>(ws + off[2]);
-  da.sel_blk = reinterpret_cast<int*>(ws + off[3]);
-  da.sel_lp = reinterpret_cast<float*>(ws + off[4]);
-  da.part = reinterpret_cast<float*>(ws + off[5]);
+  da.rowstat = reinterpret_cast<float*>(ws + off[0]);
+  da.sel_cnt = reinterpret_cast<int*>(ws + off[1]);
+  da.sel_blk = reinterpret_cast<int*>(ws + off[2]);
+  da.sel_lp = reinterpret_cast<float*>(ws + off[3]);
+  da.part = reinterpret_cast<float*>(ws + off[4]);
   da.len = len;
   da.len_add = len_add;
   da.grp = grp;
@@ -693,7 +692,7 @@ dash_status dash_decode_static(const dash_decode_params* p, const void* q, const
                                void* stream) {
   dash_status s = check_decode_params(p);
   if (s != DASH_OK) return s;
-  size_t off[6];
+  size_t off[5];
   const size_t need = decode_ws_layout(p, off, nullptr, nullptr);
   if (need > kStaticScratchBytes)
     return fail(DASH_EWORKSPACE, "this decode needs %zu bytes of scratch; the static scratch holds %zu "
@@ -748,7 +747,7 @@ dash_status dash_decode_step(const dash_decode_params* p, const void* q, const v
   if (!ok_ptr(q) || !ok_ptr(o)) return fail(DASH_EINVAL, "q and o must be non-null and 16-byte aligned");
   if (!ok_opt(lse) || !ok_opt(nsel) || !ok_opt(tau) || !ok_opt(mask))
     return fail(DASH_EINVAL, "lse/nsel/tau/mask must be 16-byte aligned");
-  size_t off[6];
+  size_t off[5];
   if (workspace_bytes < decode_ws_layout(p, off, nullptr, nullptr))
     return fail(DASH_EWORKSPACE, "workspace of %zu bytes needed, %zu given", decode_ws_layout(p, off, nullptr, nullptr),
                 workspace_bytes);

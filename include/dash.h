@@ -312,7 +312,7 @@ dash_status dash_decode(const dash_decode_params* p, const void* q, const void* 
  * device memory, one per GPU, until the process ends.  The call allocates
  * and frees nothing.  Arguments and outputs as dash_decode, without the
  * workspace.  Sizes whose dash_decode_workspace_bytes() exceeds the scratch
- * (e.g. more than 512 rows at a 131072-token cache) return DASH_EWORKSPACE
+ * (more than 736 rows at a 98304-token cache, 675 at 131072) return DASH_EWORKSPACE
  * with nothing launched.  Every call on one GPU uses that GPU's one scratch:
  * calls that overlap on a GPU (other streams, other host threads) race and
  * must be serialised by the caller.  Nothing in the scratch needs to start
