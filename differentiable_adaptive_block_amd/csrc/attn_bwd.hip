@@ -415,34 +415,38 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const bool kbthr = tid < NITEM;
   const int spr = tid / CH, sch = tid % CH;
 
-  // per-row data of an item: threads 0-63 load it into registers, then
-  // store it into LDS buffer `buf`
-  float s_pr0 = 0.f, s_pr1 = 0.f, s_dz0 = 0.f, s_dz1 = 0.f, s_dl = 0.f;
+  // per-row data of an item: threads 0-63 issue the loads into registers
+  // (no arithmetic on the loaded values, so nothing waits for them here and
+  // the wave goes on to its share of the next copy), then, after the item in
+  // flight is computed, combine them and store them into LDS buffer `buf`
+  float s_pr0 = 0.f, s_pr1 = 0.f, s_dz0 = 0.f, s_dz1 = 0.f, s_dl = 0.f, s_ls = 0.f;
   auto load_rows = [&](int n) {
     if (tid < 64) {
       const int t = itm[n][0] >> 1, c = itm[n][0] & 1;
       const int q0 = t * DASH_QTILE + c * 64;
       const int row = c * 64 + tid;
-      const float ls = a.lse[bh * a.T + q0 + tid] * LOG2E_F;
+      s_ls = a.lse[bh * a.T + q0 + tid];
       s_dl = a.delta[bh * a.T + q0 + tid];
       s_pr0 = -INFINITY; s_dz0 = 0.f;
       s_pr1 = -INFINITY; s_dz1 = 0.f;
       if (itm[n][1] >= 0) {
         const size_t gi = gidx(bh, ntile, t, nb, itm[n][1], row, a.causal);
-        s_pr0 = a.pbuf[gi] - ls;  // -inf stays -inf
+        s_pr0 = a.pbuf[gi];
         s_dz0 = a.gbuf[gi];
       }
       if (itm[n][2] >= 0) {
         const size_t gi = gidx(bh, ntile, t, nb, itm[n][2], row, a.causal);
-        s_pr1 = a.pbuf[gi] - ls;
+        s_pr1 = a.pbuf[gi];
         s_dz1 = a.gbuf[gi];
       }
     }
   };
   auto store_rows = [&](int buf) {
+#pragma clang fp contract(off)  // lse * log2e rounded, then subtracted
     if (tid < 64) {
-      prq[buf][0][tid] = s_pr0;
-      prq[buf][1][tid] = s_pr1;
+      const float ls = s_ls * LOG2E_F;
+      prq[buf][0][tid] = s_pr0 - ls;  // -inf stays -inf
+      prq[buf][1][tid] = s_pr1 - ls;
       dzq[buf][0][tid] = s_dz0;
       dzq[buf][1][tid] = s_dz1;
       dlq[buf][tid] = s_dl;
