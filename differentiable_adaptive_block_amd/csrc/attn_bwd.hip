@@ -34,16 +34,38 @@
 
 // ---------------------------------------------------------------------------- delta
 
-template <typename T>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(const T* __restrict__ o, const T* __restrict__ dout,
-                                                        float* __restrict__ delta, size_t rows, int D) {
-  const size_t r = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int l = threadIdx.x & 63;
-  if (r >= rows) return;
+// delta = rowsum(dO o O) of the bf16 rows (the fp32 path forms it in its
+// row kernel), with 16-byte loads: D/8 lanes per row, 64/(D/8) rows per
+// wave.  Each lane adds its 8 products in order, then the lanes of a row add
+// theirs by a butterfly (the same order in every row).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_delta_bf16_kernel(const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
+                                                             float* __restrict__ delta, size_t rows) {
+  constexpr int LPR = D / 8, RPW = 64 / LPR;
+  const int l = threadIdx.x & 63, c = l % LPR;
+  const size_t r = ((size_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + l / LPR;
   float acc = 0.f;
-  for (int d = l; d < D; d += 64) acc = fmaf(to_f<T>(o[r * D + d]), to_f<T>(dout[r * D + d]), acc);
-  acc = wave_sum(acc);
-  if (l == 0) delta[r] = acc;
+  if (r < rows) {
+    const uint4 a = *reinterpret_cast<const uint4*>(o + r * D + 8 * c);
+    const uint4 b = *reinterpret_cast<const uint4*>(dout + r * D + 8 * c);
+    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      acc = fmaf(__uint_as_float(aw[x] << 16), __uint_as_float(bw[x] << 16), acc);
+      acc = fmaf(__uint_as_float(aw[x] & 0xFFFF0000u), __uint_as_float(bw[x] & 0xFFFF0000u), acc);
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
+  if (r < rows && c == 0) delta[r] = acc;
+}
+static hipError_t launch_delta_bf16(const BwdArgs& a, size_t rows, hipStream_t st) {
+  const bf16_t* o = reinterpret_cast<const bf16_t*>(a.o);
+  const bf16_t* g = reinterpret_cast<const bf16_t*>(a.dout);
+  if (a.D == 128) bwd_delta_bf16_kernel<128><<<(unsigned)((rows + 15) / 16), 256, 0, st>>>(o, g, a.delta, rows);
+  else if (a.D == 64) bwd_delta_bf16_kernel<64><<<(unsigned)((rows + 31) / 32), 256, 0, st>>>(o, g, a.delta, rows);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------- dQ (fine), G, priors
@@ -1086,9 +1108,7 @@ hipError_t launch_bwd_gqa(const BwdArgs& a, void* dk, void* dv, float* dkbar, hi
   const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
   const int nb = a.T / DASH_BLOCK;
   hipError_t e;
-  bwd_delta_kernel<bf16_t><<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(
-      reinterpret_cast<const bf16_t*>(a.o), reinterpret_cast<const bf16_t*>(a.dout), a.delta, rows, a.D);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_delta_bf16(a, rows, st)) != hipSuccess) return e;
   if (a.D == 128) bwd_dq_kernel<128, true><<<ntile * a.BH, 256, 0, st>>>(a);
   else bwd_dq_kernel<64, true><<<ntile * a.BH, 256, 0, st>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1119,9 +1139,7 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t st) {
   const int nb = a.T / DASH_BLOCK;
   hipError_t e;
   if (dtype == 1) {
-    bwd_delta_kernel<bf16_t><<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(
-        reinterpret_cast<const bf16_t*>(a.o), reinterpret_cast<const bf16_t*>(a.dout), a.delta, rows, a.D);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_delta_bf16(a, rows, st)) != hipSuccess) return e;
     if (a.D == 128) bwd_dq_kernel<128, false><<<ntile * a.BH, 256, 0, st>>>(a);
     else bwd_dq_kernel<64, false><<<ntile * a.BH, 256, 0, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
