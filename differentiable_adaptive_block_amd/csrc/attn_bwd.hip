@@ -717,8 +717,8 @@ __global__ __launch_bounds__(256, 2) void bwd_coarse_kernel(BwdArgs a) {
   const size_t g0 = gidx(bh, ntile, tile, nb, 0, rt, a.causal);   // entry e at g0 + 128 e
   const size_t s0 = gidx(bkv, ntile, tile, nb, 0, rt, a.causal);  // the group's G sum (GQA)
   // The per-entry values of 8 entries are loaded together before any of
-  // them is used (loads of one lane in flight at once; entries past the
-  // list read as unselected).  s_b and s_b g_b of (this row, entry e) follow;
+  // them is used, the next 8's while they are summed (entries past the list
+  // read as unselected).  s_b and s_b g_b of (this row, entry e) follow;
   // an entry the row does not select (at or after its own block, or p = 0)
   // gives none.
   struct Ent {
@@ -754,10 +754,18 @@ __global__ __launch_bounds__(256, 2) void bwd_coarse_kernel(BwdArgs a) {
   };
   float ss = 0.f, ssg = 0.f;
   if (valid) {
+    // the next 8 entries' loads go out before this 8's terms are summed
+    Ent xn[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) xn[u] = load_ent(h + 2 * u);
     for (int e0 = h; e0 < cnt; e0 += 16) {
       Ent x[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = load_ent(e0 + 2 * u);
+      for (int u = 0; u < 8; ++u) x[u] = xn[u];
+      if (e0 + 16 < cnt) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) xn[u] = load_ent(e0 + 16 + 2 * u);
+      }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         float sv, sg;
