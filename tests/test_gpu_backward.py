@@ -49,6 +49,7 @@ SMALL = [
     ("bf16-causal-dense", 1, 1, 1024, 128, "bf16", True, 1.25, 1.0, (1, 8)),
     ("bf16-causal-d64", 1, 2, 576, 64, "bf16", True, 1.25, 4.0, (1, 3)),
     ("bf16-noncausal-a2", 1, 2, 512, 128, "bf16", False, 2.0, 4.0, (1, 3)),
+    ("bf16-noncausal-d64-tile-tail", 2, 1, 1088, 64, "bf16", False, 1.5, 4.0, (1, 4)),
     ("bf16-causal-a1", 1, 1, 512, 128, "bf16", True, 1.0, 1.0, (1, 3)),
 ]
 

@@ -57,6 +57,7 @@ SMALL = [
     ("bf16-causal-ragged", 1, 2, 1088, 128, "bf16", True, 1.5, 4.0, (1, 4)),
     ("bf16-causal-dense", 2, 1, 576, 128, "bf16", True, 1.5, 1.0, (1, 8)),
     ("bf16-noncausal-d64", 1, 2, 576, 64, "bf16", False, 1.25, 4.0, (1, 3)),
+    ("bf16-noncausal-tile-tail", 2, 2, 1088, 128, "bf16", False, 1.5, 4.0, (1, 4)),
     ("bf16-causal-a1", 1, 1, 512, 128, "bf16", True, 1.0, 1.0, (1, 3)),
     ("bf16-causal-a2", 1, 1, 512, 64, "bf16", True, 2.0, 4.0, (1, 3)),
     ("bf16-one-block", 1, 2, 64, 128, "bf16", True, 1.5, 1.0, None),
