@@ -342,7 +342,10 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(DecodeArgs a) {
   constexpr int D = 128;
   __shared__ float red_m[4], red_l[4];
   __shared__ float red_o[4][D];
-  const int split = blockIdx.x, row = blockIdx.y;
+  // grid (row, split): every row's split 0 is dispatched first, then split 1,
+  // ...; low splits hold the most list entries, so the launch ends on light
+  // workgroups
+  const int row = blockIdx.x, split = blockIdx.y;
   const int nbc = a.N / DASH_BLOCK;
   const int n = decode_row_len(a, row);  // in range whenever the list is not empty
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
@@ -894,7 +897,7 @@ hipError_t launch_decode(const DecodeArgs& a0, int dtype, hipStream_t st) {
     else if (nb <= 1536) decode_select_kernel<24><<<a.SH, 256, 0, st>>>(a);
     else decode_select_kernel<32><<<a.SH, 256, 0, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    decode_attend_kernel<<<dim3(a.nsplit, a.SH), 256, 0, st>>>(a);
+    decode_attend_kernel<<<dim3(a.SH, a.nsplit), 256, 0, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     decode_combine_kernel<DASH_DEC_SPLIT><<<(a.SH + 3) / 4, 256, 0, st>>>(a);
     return hipGetLastError();
