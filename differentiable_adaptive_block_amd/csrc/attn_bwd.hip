@@ -700,7 +700,7 @@ __global__ __launch_bounds__(256, 2) void bwd_coarse_kernel(BwdArgs a) {
   const int nb = a.T / DASH_BLOCK;
   const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
   const size_t bh = blockIdx.y;
-  const int tile = blockIdx.x;
+  const int tile = gridDim.x - 1 - blockIdx.x;  // longest lists (last tiles, causal) first
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, j = l & 31, h = l >> 5;
   const int rt = 32 * w + j;
   const int i = tile * DASH_QTILE + rt;

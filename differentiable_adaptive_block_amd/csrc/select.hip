@@ -203,7 +203,7 @@ __global__ __launch_bounds__(64 * NW) void select_mfma_kernel(SelectArgs a) {
   const int nbw = (nb + 31) / 32;
   uint32_t* uni = reinterpret_cast<uint32_t*>(zs + 32 * nbp);
   const size_t bh = blockIdx.y;
-  const int row0 = blockIdx.x * 32;
+  const int row0 = (gridDim.x - 1 - blockIdx.x) * 32;  // last rows (most causal candidates) first
   const int w = threadIdx.x >> 6, l = lane_id(), j = l & 31, h = l >> 5;
   const int nc = a.causal ? row0 / DASH_BLOCK : nb;
   const CoarseArith ca = a.ca;
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(512, NPL > 64 ? 2 : 4) void select_chunked_kernel(S
   const int nb = a.T / DASH_BLOCK;
   const int nbw = (nb + 31) / 32;
   const size_t bh = blockIdx.y;
-  const int row0 = blockIdx.x * 32;
+  const int row0 = (gridDim.x - 1 - blockIdx.x) * 32;  // last rows (most causal candidates) first
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = lane_id(), j = l & 31, g = l & 15;
   const int nc = a.causal ? row0 / DASH_BLOCK : nb;
