@@ -1044,7 +1044,7 @@ template <int GRP>
 __global__ __launch_bounds__(256) void bwd_gqa_gsum_kernel(BwdArgs a) {
   const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
   const int nb = a.T / DASH_BLOCK;
-  const int tile = blockIdx.x;
+  const int tile = gridDim.x - 1 - blockIdx.x;  // longest lists first
   const size_t bkv = blockIdx.y, bh0 = bkv * GRP;
   const int cnt = a.tile_cnt[bh0 * ntile + tile];  // the group's heads share the list
   const size_t hstride = bwd_entries_per_head(a.causal, nb, ntile) * DASH_QTILE;  // floats per head
