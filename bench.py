@@ -202,8 +202,22 @@ def _col(t, k):
     return [row[k] for row in t]
 
 
-def bench_prefill(name, steps, warmup, device, log_prefix=""):
-    """Time dash_fwd (select + attend) on a named prefill workload."""
+def _column_counts(mask, T):
+    """Rows that selected each candidate block (from the Stage-1 mask words), plus the
+    block's own 64 rows: the column lengths of the low-density schedule, [B*H, nb]."""
+    B, H, _, nbw = mask.shape
+    nb = T // 64
+    words = mask.view(B * H, T, nbw)
+    cols = torch.zeros((B * H, nbw * 32), dtype=torch.int64, device=mask.device)
+    for bit in range(32):
+        cols[:, bit::32] = ((words >> bit) & 1).sum(1)
+    return cols[:, :nb] + 64
+
+
+def bench_prefill(name, steps, warmup, device, log_prefix="", low_density=False):
+    """Time dash_fwd (select + attend) on a named prefill workload; with ``low_density``
+    the attend is dash_fwd_attend_lowdens with a workspace sized beforehand for the
+    qualifying tiles' pairs."""
     from differentiable_adaptive_block_amd import _lib, api, inputs
 
     wl = inputs.CONFIGS[name]
@@ -222,27 +236,51 @@ def bench_prefill(name, steps, warmup, device, log_prefix=""):
     nsel = r["sel"].nsel.to(torch.int64)
     tile_cnt = r["sel"].tile_cnt.to(torch.int64)
     p = r["params"]
-    # timed calls: the selection outputs used only for validation (nsel, mask) are off
-    sel = api.alloc_selection(p, q.device, want_mask=False)
+    # timed calls: the selection outputs used only for validation (nsel, mask) are off,
+    # except the masks, which the low-density schedule builds its lists from
+    sel = api.alloc_selection(p, q.device, want_mask=low_density)
     csel = sel.as_c()
     o = torch.empty_like(q)
     lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
     kbar = torch.empty((B, H, T // 64, D), dtype=q.dtype, device=q.device)
     st = torch.cuda.current_stream().cuda_stream
+    ld = None
+    if low_density:
+        ld_pairs = api.lowdens_pairs(r["sel"], p, api.LOWDENS_RATIO)
+        wsb = _lib.fwd_lowdens_workspace_bytes(p, ld_pairs)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=q.device)
+        cols = _column_counts(r["sel"].mask, T)
+        ld = dict(ratio=api.LOWDENS_RATIO, pairs=ld_pairs, workspace_gb=wsb / 1e9,
+                  pairs_total=int(cols.sum()),
+                  # MFMA columns the partial kernel runs: each work item of <= 128 listed
+                  # rows gives 4 waves of 32 columns, idle waves skipped
+                  walked_pairs=int((((cols + 31) // 32) * 32).sum()))
 
     def step(ev):
         _lib.fwd_select(p, q.data_ptr(), k.data_ptr(), kbar.data_ptr(), csel, st)
         if ev:
             ev[0].record()
-        _lib.fwd_attend(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), kbar.data_ptr(), csel, o.data_ptr(),
-                        lse.data_ptr(), st)
+        if low_density:
+            _lib.fwd_attend_lowdens(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), kbar.data_ptr(), csel,
+                                    api.LOWDENS_RATIO, o.data_ptr(), lse.data_ptr(), ws.data_ptr(), wsb, st)
+        else:
+            _lib.fwd_attend(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), kbar.data_ptr(), csel, o.data_ptr(),
+                            lse.data_ptr(), st)
 
     t = run_timed(step, steps, warmup, marks=1)
     select_ms = _median(_col(t, 0))
     attend_ms = _median(_col(t, 1))
     ms = _median([a + b for a, b in t])
-    # same outputs as the validated path
-    assert torch.equal(o, r["o"]), "timed forward differs from the validated forward"
+    if low_density:
+        # the schedule's rounding differs from the dense walk's: within the output tolerance
+        d = (o.float() - r["o"].float()).abs()
+        ld.update(o_max_abs_vs_dense=float(d.max()), o_mean_abs_vs_dense=float(d.mean()),
+                  lse_max_abs_vs_dense=float((lse - r["lse"]).abs().max()))
+        assert ld["o_max_abs_vs_dense"] <= 2e-2 and ld["o_mean_abs_vs_dense"] <= 2e-3, ld
+        del d
+    else:
+        # same outputs as the validated path
+        assert torch.equal(o, r["o"]), "timed forward differs from the validated forward"
 
     # work accounting
     nb = T // 64
@@ -272,6 +310,11 @@ def bench_prefill(name, steps, warmup, device, log_prefix=""):
         walked_stage2_tflop=4.0 * D * walked_pairs / 1e12,
         stage2_tflops=useful_flops / (attend_ms / 1e3) / 1e12,
     )
+    if ld is not None:
+        ld["walked_over_useful"] = ld["walked_pairs"] / ld["pairs_total"]
+        ld["walked_stage2_tflop"] = 4.0 * D * 64 * ld["walked_pairs"] / 1e12
+        res["walked_stage2_tflop"] = ld["walked_stage2_tflop"]
+        res["low_density"] = ld
     del w, q, k, v, o, r
     torch.cuda.empty_cache()
     return res, (B, H, T, D)
@@ -716,6 +759,10 @@ def main():
         r3c, _ = bench_prefill("prefill64k_sc7", max(2, args.steps // 3), 1, dev)
         log(f"prefill64k_sc7: {r3c}")
         extra["prefill_64k_calibrated"] = r3c
+        # the same workload through the low-density Stage-2 schedule
+        r3l, _ = bench_prefill("prefill64k_sc7", max(3, args.steps // 2), 1, dev, low_density=True)
+        log(f"prefill64k_sc7 low-density: {r3l}")
+        extra["prefill_64k_calibrated_lowdens"] = r3l
         # the longest prefill the pages quote (96K)
         r96, _ = bench_prefill("prefill96k", 2, 1, dev)
         log(f"prefill96k: {r96}")

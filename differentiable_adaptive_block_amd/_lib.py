@@ -26,6 +26,8 @@ EXPORTS = [
     "dash_fwd",
     "dash_fwd_select",
     "dash_fwd_attend",
+    "dash_fwd_lowdens_workspace_bytes",
+    "dash_fwd_attend_lowdens",
     "dash_bwd",
     "dash_fwd_gqa",
     "dash_bwd_gqa_workspace_bytes",
@@ -108,6 +110,11 @@ def load() -> ctypes.CDLL:
     L.dash_fwd_select.argtypes = [P(DashParams), vp, vp, vp, P(DashSel), vp]
     L.dash_fwd_attend.restype = ctypes.c_int
     L.dash_fwd_attend.argtypes = [P(DashParams), vp, vp, vp, vp, P(DashSel), vp, vp, vp]
+    L.dash_fwd_lowdens_workspace_bytes.restype = ctypes.c_size_t
+    L.dash_fwd_lowdens_workspace_bytes.argtypes = [P(DashParams), ctypes.c_int64]
+    L.dash_fwd_attend_lowdens.restype = ctypes.c_int
+    L.dash_fwd_attend_lowdens.argtypes = [P(DashParams), vp, vp, vp, vp, P(DashSel), ctypes.c_float, vp, vp, vp,
+                                          ctypes.c_size_t, vp]
     L.dash_bwd.restype = ctypes.c_int
     L.dash_bwd.argtypes = [P(DashParams), vp, vp, vp, vp, vp, vp, vp, P(DashSel), vp, vp, vp, vp, vp,
                            ctypes.c_size_t, vp]
@@ -201,6 +208,15 @@ def fwd_select(p: DashParams, q, k, kbar, sel: DashSel, stream) -> None:
 
 def fwd_attend(p: DashParams, q, k, v, kbar, sel: DashSel, o, lse, stream) -> None:
     check(load().dash_fwd_attend(ctypes.byref(p), q, k, v, kbar, ctypes.byref(sel), o, lse, stream))
+
+
+def fwd_lowdens_workspace_bytes(p: DashParams, max_pairs: int) -> int:
+    return int(load().dash_fwd_lowdens_workspace_bytes(ctypes.byref(p), int(max_pairs)))
+
+
+def fwd_attend_lowdens(p: DashParams, q, k, v, kbar, sel: DashSel, ratio, o, lse, ws, ws_bytes, stream) -> None:
+    check(load().dash_fwd_attend_lowdens(ctypes.byref(p), q, k, v, kbar, ctypes.byref(sel), float(ratio), o, lse,
+                                         ws, ws_bytes, stream))
 
 
 def bwd(p: DashParams, q, k, v, o, lse, dout, kbar, sel: DashSel, dq, dk, dv, dkbar, ws, ws_bytes, stream) -> None:

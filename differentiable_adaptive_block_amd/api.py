@@ -15,6 +15,7 @@ import torch
 from . import _lib
 
 BLOCK = 64
+QTILE = 128  # query rows per Stage-2 tile (dash_query_tile())
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -117,13 +118,40 @@ def pool_attn(k: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
     return kbar
 
 
+LOWDENS_RATIO = 2.0  # DASH_LOWDENS_RATIO of include/dash.h
+
+
+def lowdens_pairs(sel: Selection, p: _lib.DashParams, ratio: float = LOWDENS_RATIO) -> int:
+    """(row, block) pairs of the query tiles that take the low-density Stage-2 schedule
+    (dash_fwd_attend_lowdens): a tile qualifies when its block-list length x rows exceeds
+    ratio x the sum over its rows of (selected blocks + 1).  Needs sel.nsel; reads one
+    number back from the device."""
+    if sel.nsel is None:
+        raise ValueError("the low-density schedule needs the selection counts (want_mask=True)")
+    B, H, T = sel.nsel.shape
+    ntile = sel.tile_cnt.shape[-1]
+    per_row = sel.nsel.to(torch.int64) + 1
+    per_row = torch.nn.functional.pad(per_row, (0, ntile * QTILE - T))
+    tile_pairs = per_row.view(B, H, ntile, QTILE).sum(-1)
+    rows = torch.clamp(T - QTILE * torch.arange(ntile, device=per_row.device), max=QTILE)
+    walked = sel.tile_cnt.to(torch.int64) * rows
+    take = walked.double() > ratio * tile_pairs.double()
+    return int(tile_pairs[take].sum())
+
+
 def forward(q, k, v, alpha=1.5, causal=True, fine_scale=None, coarse_scale=None, want_mask=True,
-            summariser_w=None):
+            summariser_w=None, low_density=False, ratio=LOWDENS_RATIO):
     """Stages 0-2.  Returns dict(o, lse, kbar, sel, params).
 
     ``summariser_w`` ([H, D] f32) switches Stage 0 to the learned summariser;
     None is mean pooling.  k and v may have fewer heads than q (grouped-query
-    heads with entmax head aggregation, bf16): then kbar has k's heads."""
+    heads with entmax head aggregation, bf16): then kbar has k's heads.
+
+    ``low_density`` lets query tiles whose rows select few blocks take the
+    block-stationary Stage-2 schedule (causal bf16 prefill with whole blocks and
+    one KV head per query head; other cases ignore it): the selection is made
+    first, the pairs of the qualifying tiles are counted (``lowdens_pairs``, one
+    read-back) and the workspace is sized for them."""
     _require(q, "q")
     B, H, T, D = q.shape
     Hkv = k.shape[1] if k.dim() == 4 else -1
@@ -136,6 +164,9 @@ def forward(q, k, v, alpha=1.5, causal=True, fine_scale=None, coarse_scale=None,
     p = make_params(q, alpha, causal, fine_scale, coarse_scale)
     if summariser_w is not None:
         _require(summariser_w, "summariser_w", (p.H, p.D), torch.float32)
+    use_ld = bool(low_density) and q.dtype == torch.bfloat16 and causal and T % BLOCK == 0 and Hkv == H
+    if use_ld:
+        want_mask = True  # the schedule's lists come from the masks
     dev = q.device
     o = torch.empty_like(q)
     lse = torch.empty((p.B, p.H, p.T), dtype=torch.float32, device=dev)
@@ -144,6 +175,18 @@ def forward(q, k, v, alpha=1.5, causal=True, fine_scale=None, coarse_scale=None,
     wsb = _lib.fwd_workspace_bytes(p)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     csel = sel.as_c()
+    if use_ld:
+        if summariser_w is None:
+            _lib.fwd_select(p, _ptr(q), _ptr(k), _ptr(kbar), csel, _stream(dev))
+        else:
+            _lib.pool_attn(p, _ptr(k), _ptr(summariser_w), _ptr(kbar), _stream(dev))
+            _lib.select(p, _ptr(q), _ptr(kbar), csel, _stream(dev))
+        npairs = lowdens_pairs(sel, p, ratio)
+        wsb = _lib.fwd_lowdens_workspace_bytes(p, npairs)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        _lib.fwd_attend_lowdens(p, _ptr(q), _ptr(k), _ptr(v), _ptr(kbar), csel, ratio, _ptr(o), _ptr(lse),
+                                _ptr(ws), wsb, _stream(dev))
+        return dict(o=o, lse=lse, kbar=kbar, sel=sel, params=p, lowdens_pairs=npairs)
     if Hkv != H:
         _lib.fwd_gqa(p, Hkv, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(kbar), csel, _stream(dev))
     elif summariser_w is None:

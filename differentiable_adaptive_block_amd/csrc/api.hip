@@ -311,8 +311,9 @@ dash_status dash_pool_attn_bwd(const dash_params* p, const void* k, const float*
 
 static dash_status attend_common(const dash_params* p, const void* q, const void* k, const void* v,
                                  const void* kbar, const dash_sel* sel, void* o, float* lse, void* stream, int grp,
-                                 int Tr = -1) {
+                                 int Tr = -1, const int* tile_skip = nullptr) {
   FwdArgs fa;
+  fa.tile_skip = tile_skip;
   fa.Tr = Tr < 0 ? p->T : Tr;
   fa.q = q;
   fa.k = k;
@@ -368,6 +369,115 @@ dash_status dash_fwd_gqa(const dash_params* p, int32_t kv_heads, const void* q, 
   return attend_common(p, q, k, v, kbar, sel, o, lse, stream, grp);
 }
 
+// Workspace of the low-density Stage-2 schedule for `cap` (row, block)
+// pairs: offsets of grp_cnt, gpairs, tile_off, row_info, col_cnt,
+// col_base, n_items, items, col_ent, part_ml, part_o, row_pos; returns the
+// total.
+static size_t ld_layout(const dash_params* p, long long cap, size_t off[12]) {
+  const size_t BH = (size_t)p->B * p->H, nb = p->T / DASH_BLOCK, ntile = ntile_of(p->T);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o += (bytes + 255) & ~size_t(255); return r; };
+  off[0] = take(BH * nb * nb * 4);
+  off[1] = take(BH * nb * 4);
+  off[2] = take(BH * ntile * 4);
+  off[3] = take(BH * p->T * 8);
+  off[4] = take(BH * nb * 4);
+  off[5] = take(BH * nb * 4);
+  off[6] = take(16);
+  off[7] = take(((size_t)cap / 128 + BH * nb + 1) * 16);
+  off[8] = take((size_t)cap * 8);
+  off[9] = take((size_t)cap * 8);
+  off[10] = take((size_t)cap * 2 * p->D);
+  off[11] = take((size_t)cap * 4);
+  return o;
+}
+
+static constexpr long long kLdMaxPairs = 0x7FFFFFFFll;  // pair indices are int32
+
+// Pairs a workspace of `bytes` holds (0 when it does not hold the fixed part).
+static long long ld_cap_of(const dash_params* p, size_t bytes) {
+  size_t off[12];
+  const size_t base = ld_layout(p, 0, off);
+  if (bytes < base) return 0;
+  const double per = 20.0 + 2.0 * p->D + 16.0 / 128.0;
+  long long cap = (long long)((double)(bytes - base - 4 * 256) / per);
+  if (cap > kLdMaxPairs) cap = kLdMaxPairs;
+  while (cap > 0 && ld_layout(p, cap, off) > bytes) cap -= 256;
+  return cap < 0 ? 0 : cap;
+}
+
+static bool ld_supported(const dash_params* p, const dash_sel* sel) {
+  return p->dtype == DASH_BF16 && p->causal && p->T % DASH_BLOCK == 0 && sel->mask != nullptr;
+}
+
+size_t dash_fwd_lowdens_workspace_bytes(const dash_params* p, int64_t max_pairs) {
+  if (check_params(p) != DASH_OK || max_pairs < 0 || max_pairs > kLdMaxPairs) return 0;
+  size_t off[12];
+  return ld_layout(p, max_pairs, off);
+}
+
+static dash_status attend_lowdens(const dash_params* p, const void* q, const void* k, const void* v,
+                                  const void* kbar, const dash_sel* sel, float ratio, void* o, float* lse,
+                                  void* workspace, size_t workspace_bytes, hipStream_t st) {
+  LdArgs la;
+  la.q = q;
+  la.k = k;
+  la.v = v;
+  la.kbar = kbar;
+  la.o = o;
+  la.lse = lse;
+  la.tau = sel->tau;
+  la.lognorm = sel->lognorm;
+  la.mask = sel->mask;
+  la.tile_cnt = sel->tile_cnt;
+  la.BH = p->B * p->H;
+  la.T = p->T;
+  la.D = p->D;
+  la.fine_scale = p->fine_scale;
+  la.ca = make_ca(p->alpha, p->coarse_scale);
+  la.ratio = ratio;
+  la.cap = ld_cap_of(p, workspace_bytes);
+  size_t off[12];
+  ld_layout(p, la.cap, off);
+  char* ws = static_cast<char*>(workspace);
+  la.grp_cnt = reinterpret_cast<int*>(ws + off[0]);
+  la.gpairs = reinterpret_cast<int*>(ws + off[1]);
+  la.tile_off = reinterpret_cast<int*>(ws + off[2]);
+  la.row_info = reinterpret_cast<int2*>(ws + off[3]);
+  la.col_cnt = reinterpret_cast<int*>(ws + off[4]);
+  la.col_base = reinterpret_cast<int*>(ws + off[5]);
+  la.n_items = reinterpret_cast<int*>(ws + off[6]);
+  la.items = reinterpret_cast<int4*>(ws + off[7]);
+  la.col_ent = reinterpret_cast<int2*>(ws + off[8]);
+  la.part_ml = reinterpret_cast<float2*>(ws + off[9]);
+  la.part_o = reinterpret_cast<bf16_t*>(ws + off[10]);
+  la.row_pos = reinterpret_cast<int*>(ws + off[11]);
+  hipError_t e;
+  if ((e = launch_lowdens_plan(la, st)) != hipSuccess) return hip_fail(e, "low-density plan");
+  dash_status s = attend_common(p, q, k, v, kbar, sel, o, lse, st, 1, -1, la.tile_off);
+  if (s != DASH_OK) return s;
+  if ((e = launch_lowdens_attend(la, st)) != hipSuccess) return hip_fail(e, "low-density attention");
+  return DASH_OK;
+}
+
+dash_status dash_fwd_attend_lowdens(const dash_params* p, const void* q, const void* k, const void* v,
+                                    const void* kbar, const dash_sel* sel, float ratio, void* o, float* lse,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  dash_status s = check_params(p);
+  if (s != DASH_OK) return s;
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(lse) || !ok_ptr(kbar))
+    return fail(DASH_EINVAL, "q, k, v, o, lse and kbar must be non-null and 16-byte aligned");
+  if ((s = check_sel(sel, true)) != DASH_OK) return s;
+  if (!(ratio >= 0.f) || !std::isfinite(ratio)) return fail(DASH_EINVAL, "ratio must be finite and >= 0 (got %g)", ratio);
+  if (!ld_supported(p, sel))
+    return fail(DASH_EUNSUPPORTED, "the low-density schedule is built for causal bf16 attention and needs sel->mask");
+  size_t off[12];
+  const size_t need = ld_layout(p, 0, off);
+  if (workspace_bytes < need) return fail(DASH_EWORKSPACE, "workspace of at least %zu bytes needed, %zu given", need, workspace_bytes);
+  if (!ok_ptr(workspace)) return fail(DASH_EINVAL, "workspace must be non-null and 16-byte aligned");
+  return attend_lowdens(p, q, k, v, kbar, sel, ratio, o, lse, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
 dash_status dash_fwd(const dash_params* p, const void* q, const void* k, const void* v, void* o, float* lse,
                      void* kbar, const dash_sel* sel, void* workspace, size_t workspace_bytes, void* stream) {
   dash_status s = check_params(p, true, true);
@@ -375,10 +485,12 @@ dash_status dash_fwd(const dash_params* p, const void* q, const void* k, const v
   if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(lse) || !ok_ptr(kbar))
     return fail(DASH_EINVAL, "q, k, v, o, lse and kbar must be non-null and 16-byte aligned");
   if ((s = check_sel(sel, true)) != DASH_OK) return s;
-  (void)workspace;  // the forward needs none (see dash_fwd_workspace_bytes)
-  (void)workspace_bytes;
   if (!is_ragged(p)) {
     if ((s = dash_fwd_select(p, q, k, kbar, sel, stream)) != DASH_OK) return s;
+    // a workspace with room for pairs switches on the low-density schedule
+    if (ld_supported(p, sel) && ok_ptr(workspace) && ld_cap_of(p, workspace_bytes) > 0)
+      return attend_lowdens(p, q, k, v, kbar, sel, DASH_LOWDENS_RATIO, o, lse, workspace, workspace_bytes,
+                            (hipStream_t)stream);
     return dash_fwd_attend(p, q, k, v, kbar, sel, o, lse, stream);
   }
   // a partial last block: the kernels take the tensors as they are (T rows

@@ -92,6 +92,8 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
   // the heads of a group share their tile lists (the union of their supports)
   const int* glist = a.tile_blk + (bkv * HG * ntile + tile) * nb;
   const int cnt = a.tile_cnt[bkv * HG * ntile + tile];
+  if constexpr (HG == 1)
+    if (a.tile_skip != nullptr && a.tile_skip[bkv * ntile + tile] >= 0) return;  // the low-density schedule's
   const CoarseArith ca = a.ca;
   const float sl2 = a.fine_scale * LOG2E_F;
   // The block list is staged in LDS: a global (vector-memory) load inside

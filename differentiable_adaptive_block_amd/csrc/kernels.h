@@ -38,6 +38,43 @@ struct FwdArgs {
   int grp;  // query heads per key/value head: k, v, kbar are indexed by bh / grp
   float fine_scale;
   CoarseArith ca;
+  // [BH, ntile] or null: tiles with an entry >= 0 are left to the
+  // low-density schedule (lowdens.hip) and skipped here
+  const int* tile_skip = nullptr;
+};
+
+// The low-density Stage-2 schedule (lowdens.hip): causal, bf16, one KV head
+// per query head, whole blocks.  Inputs as FwdArgs plus the Stage-1 masks;
+// the rest is the caller's workspace.
+struct LdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* kbar;
+  void* o;
+  float* lse;
+  const float* tau;
+  const float* lognorm;
+  const uint32_t* mask;  // [BH, T, nbw]
+  const int* tile_cnt;   // [BH, ntile]
+  int BH, T, D;
+  float fine_scale;
+  CoarseArith ca;
+  float ratio;       // a tile qualifies when its dense walk exceeds ratio x its pairs
+  long long cap;     // (row, block) pairs the workspace holds
+  // workspace
+  int* grp_cnt;      // [BH, nb, nb] rows of group g that selected block b, then prefixes
+  int* gpairs;       // [BH, nb] pairs of each 64-row group
+  int* tile_off;     // [BH, ntile] first pair of a tile taken here, -1: dense walk
+  int2* row_info;    // [BH, T] (first pair, pairs) of the rows of taken tiles
+  int* col_cnt;      // [BH, nb] listed rows per key block
+  int* col_base;     // [BH, nb] first entry of each column
+  int4* items;       // work items {column, first entry, entries}
+  int* n_items;      // [1]
+  int2* col_ent;     // [cap] (row, partial index) grouped by column
+  int* row_pos;      // [cap] partial indices of each row's pairs, rows at row_info.x
+  float2* part_ml;   // [cap] partial (max + prior, sum) per pair, log2 units
+  bf16_t* part_o;    // [cap, D] partial unnormalised output per pair
 };
 
 // The one Stage-1 score accumulation (see select_mfma_kernel): 32 summaries
@@ -227,3 +264,5 @@ hipError_t launch_group_union(uint32_t* tile_bits, int BH, int grp, size_t words
 hipError_t launch_tile_lists(uint32_t* tile_bits, int* tile_cnt, int* tile_blk, int BH, int T, int causal,
                              hipStream_t st);
 hipError_t launch_fwd(const FwdArgs& a, int dtype, hipStream_t st);
+hipError_t launch_lowdens_plan(const LdArgs& a, hipStream_t st);
+hipError_t launch_lowdens_attend(const LdArgs& a, hipStream_t st);

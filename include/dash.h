@@ -37,7 +37,8 @@
  * last failing call on the calling thread.
  *
  * Determinism: forward, decode and backward results do not depend on
- * scheduling (no floating-point atomics).
+ * scheduling (no floating-point atomics; the integer atomics that build the
+ * low-density schedule's lists order work, not sums).
  */
 #ifndef DASH_H
 #define DASH_H
@@ -109,7 +110,9 @@ int32_t dash_query_tile(void);
 dash_status dash_sel_sizes(const dash_params* p, size_t out_elems[8]);
 
 /*
- * Bytes of device workspace dash_fwd / dash_bwd need (dash_fwd: always 0).
+ * Bytes of device workspace dash_fwd / dash_bwd need (dash_fwd: always 0;
+ * a larger one lets it take the low-density schedule, see
+ * dash_fwd_attend_lowdens).
  * dash_bwd's grows with T^2: besides O(B H T D) fp32 buffers it keeps, per
  * (query tile, list slot, row), G and the log2 prior as fp32, with room for
  * every slot a tile's list can hold: min(T/64, 2t + 2) for causal tile t
@@ -154,6 +157,48 @@ dash_status dash_pool(const dash_params* p, const void* k, void* kbar, void* str
 dash_status dash_fwd(const dash_params* p, const void* q, const void* k, const void* v,
                      void* o, float* lse, void* kbar, const dash_sel* sel,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Stage 2 at low selection density (the AdaSplash-2 abstract on the
+ * thelatestinai.com page: a sparsity-aware implementation that skips the
+ * zero blocks at low cost).  The dense walk runs each 128-row query tile over
+ * the union of its rows' blocks with all 128 rows; when the rows of a tile
+ * select few, different blocks that union holds nearly every candidate and
+ * most of the products are thrown away.  This schedule instead lists, for
+ * every key block, the rows that selected it (plus, causal, its own 64 rows),
+ * computes each (row, block) pair's partial softmax with those rows as the
+ * MFMA columns over one LDS copy of the block's keys and values, and merges
+ * each row's partials in block order.  The result is the same attention
+ * (outputs within bf16 rounding of dash_fwd_attend's; the partials' weighted
+ * values are kept in bf16), and deterministic: integer atomics only order
+ * the lists, not the arithmetic.
+ *
+ * Per call, on the device: a query tile takes this schedule when the dense
+ * walk would visit more than `ratio` times the (row, block) pairs its rows
+ * need (list length x rows > ratio x sum over rows of (selected + 1)), as
+ * long as the pairs of the qualifying tiles up to it, in head-major tile
+ * order, fit in the workspace; every other tile takes the dense walk in the
+ * same call.  ratio 0 sends every tile that fits here.
+ *
+ * Causal, bf16, whole blocks (T a multiple of 64), one KV head per query head;
+ * sel must hold the masks (sel->mask written by dash_fwd_select with the same
+ * params) besides what dash_fwd_attend reads.  Other cases return
+ * DASH_EUNSUPPORTED.  Workspace: dash_fwd_lowdens_workspace_bytes(p, pairs)
+ * for room for `pairs` pairs (B H T of them are the own blocks; the rest is
+ * the sum of the rows' selected counts, sel->nsel); at least the value for
+ * 0 pairs (then every tile takes the dense walk), else DASH_EWORKSPACE.  Per
+ * pair it holds 20 + 2 D bytes; the fixed part is about
+ * B H (8 T + 4 (T/64)^2) bytes (44 MB per head at T = 98304).
+ *
+ * dash_fwd takes the same schedule, with ratio DASH_LOWDENS_RATIO, when its
+ * workspace holds at least one pair beyond that fixed part and the case is
+ * supported (mask non-null); with no workspace it takes the dense walk.
+ */
+#define DASH_LOWDENS_RATIO 2.0f
+size_t dash_fwd_lowdens_workspace_bytes(const dash_params* p, int64_t max_pairs);
+dash_status dash_fwd_attend_lowdens(const dash_params* p, const void* q, const void* k, const void* v,
+                                    const void* kbar, const dash_sel* sel, float ratio, void* o,
+                                    float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The two halves of dash_fwd, for callers that reuse a selection or time the

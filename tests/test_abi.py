@@ -274,3 +274,35 @@ def test_decode_static_rejects_sizes_beyond_its_scratch(L):
     assert L.dash_decode_static(ctypes.byref(p), *args, None) == _lib.DASH_EWORKSPACE
     assert "static scratch" in L.dash_last_error().decode()
     assert L.dash_decode_static(ctypes.byref(_dparams(N=1000)), *args, None) == _lib.DASH_EINVAL
+
+
+def _lowdens(L, p, sel=None, ratio=4.0, ws=FAKE, wsb=1 << 40):
+    return L.dash_fwd_attend_lowdens(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, ctypes.byref(sel or _sel()),
+                                     ratio, FAKE, FAKE, ws, wsb, None)
+
+
+def test_lowdens_workspace_grows_by_pair(L):
+    for D in (64, 128):
+        p = _params(D=D, B=2, H=4, T=4096)
+        base = L.dash_fwd_lowdens_workspace_bytes(ctypes.byref(p), 0)
+        assert base > 8 * 2 * 4 * 4096  # the per-row (first pair, count) table at least
+        n = 1 << 20
+        grow = L.dash_fwd_lowdens_workspace_bytes(ctypes.byref(p), n) - base
+        per = 20 + 2 * D
+        assert per * n <= grow <= per * n + n // 128 * 16 + 8 * 256
+        assert L.dash_fwd_lowdens_workspace_bytes(ctypes.byref(p), -1) == 0
+        assert L.dash_fwd_lowdens_workspace_bytes(ctypes.byref(p), 1 << 31) == 0  # pair indices are int32
+
+
+def test_lowdens_entry_validation(L):
+    p = _params()
+    base = L.dash_fwd_lowdens_workspace_bytes(ctypes.byref(p), 0)
+    assert _lowdens(L, p, ratio=float("nan")) == _lib.DASH_EINVAL
+    assert _lowdens(L, p, ratio=-1.0) == _lib.DASH_EINVAL
+    assert _lowdens(L, _params(dtype=_lib.DASH_F32)) == _lib.DASH_EUNSUPPORTED
+    assert _lowdens(L, _params(causal=0)) == _lib.DASH_EUNSUPPORTED
+    assert _lowdens(L, p, sel=_sel(mask=None)) == _lib.DASH_EUNSUPPORTED
+    assert _lowdens(L, p, wsb=base - 1) == _lib.DASH_EWORKSPACE
+    assert "workspace" in L.dash_last_error().decode()
+    assert _lowdens(L, p, ws=None, wsb=base) == _lib.DASH_EINVAL
+    assert _lowdens(L, _params(T=300)) == _lib.DASH_EINVAL  # whole blocks only
