@@ -311,9 +311,10 @@ dash_status dash_pool_attn_bwd(const dash_params* p, const void* k, const float*
 
 static dash_status attend_common(const dash_params* p, const void* q, const void* k, const void* v,
                                  const void* kbar, const dash_sel* sel, void* o, float* lse, void* stream, int grp,
-                                 int Tr = -1, const int* tile_skip = nullptr) {
+                                 int Tr = -1, const int* dense_list = nullptr, const int* dense_n = nullptr) {
   FwdArgs fa;
-  fa.tile_skip = tile_skip;
+  fa.dense_list = dense_list;
+  fa.dense_n = dense_n;
   fa.Tr = Tr < 0 ? p->T : Tr;
   fa.q = q;
   fa.k = k;
@@ -371,10 +372,11 @@ dash_status dash_fwd_gqa(const dash_params* p, int32_t kv_heads, const void* q, 
 
 // Workspace of the low-density Stage-2 schedule for `cap` (row, block)
 // pairs: offsets of grp_cnt, gpairs, tile_off, row_info, col_cnt,
-// col_base, n_items, items, col_ent, part_ml, part_o, row_pos; returns the
-// total.
-static size_t ld_layout(const dash_params* p, long long cap, size_t off[12]) {
+// col_base, n_items, items, col_ent, part_ml, part_o, row_pos, rng_pref,
+// dense_list, dense_n, head_items; returns the total.
+static size_t ld_layout(const dash_params* p, long long cap, size_t off[16]) {
   const size_t BH = (size_t)p->B * p->H, nb = p->T / DASH_BLOCK, ntile = ntile_of(p->T);
+  const size_t nr = (nb + DASH_LD_RANGE - 1) / DASH_LD_RANGE;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o += (bytes + 255) & ~size_t(255); return r; };
   off[0] = take(BH * nb * nb * 4);
@@ -384,11 +386,15 @@ static size_t ld_layout(const dash_params* p, long long cap, size_t off[12]) {
   off[4] = take(BH * nb * 4);
   off[5] = take(BH * nb * 4);
   off[6] = take(16);
-  off[7] = take(((size_t)cap / 128 + BH * nb + 1) * 16);
+  off[7] = take(((size_t)cap / 128 + BH * nr * nb + 1) * 16);
   off[8] = take((size_t)cap * 8);
   off[9] = take((size_t)cap * 8);
   off[10] = take((size_t)cap * 2 * p->D);
   off[11] = take((size_t)cap * 4);
+  off[12] = take(BH * (nr + 1) * nb * 4);
+  off[13] = take(BH * ntile * 4);
+  off[14] = take(16);
+  off[15] = take(BH * 4);
   return o;
 }
 
@@ -396,14 +402,18 @@ static constexpr long long kLdMaxPairs = 0x7FFFFFFFll;  // pair indices are int3
 
 // Pairs a workspace of `bytes` holds (0 when it does not hold the fixed part).
 static long long ld_cap_of(const dash_params* p, size_t bytes) {
-  size_t off[12];
+  size_t off[16];
   const size_t base = ld_layout(p, 0, off);
   if (bytes < base) return 0;
-  const double per = 20.0 + 2.0 * p->D + 16.0 / 128.0;
-  long long cap = (long long)((double)(bytes - base - 4 * 256) / per);
-  if (cap > kLdMaxPairs) cap = kLdMaxPairs;
-  while (cap > 0 && ld_layout(p, cap, off) > bytes) cap -= 256;
-  return cap < 0 ? 0 : cap;
+  // the largest cap whose layout fits (the layout grows with cap)
+  long long lo = 0, hi = kLdMaxPairs;
+  if (ld_layout(p, hi, off) <= bytes) return hi;
+  while (hi - lo > 1) {
+    const long long mid = lo + (hi - lo) / 2;
+    if (ld_layout(p, mid, off) <= bytes) lo = mid;
+    else hi = mid;
+  }
+  return lo;
 }
 
 static bool ld_supported(const dash_params* p, const dash_sel* sel) {
@@ -412,7 +422,7 @@ static bool ld_supported(const dash_params* p, const dash_sel* sel) {
 
 size_t dash_fwd_lowdens_workspace_bytes(const dash_params* p, int64_t max_pairs) {
   if (check_params(p) != DASH_OK || max_pairs < 0 || max_pairs > kLdMaxPairs) return 0;
-  size_t off[12];
+  size_t off[16];
   return ld_layout(p, max_pairs, off);
 }
 
@@ -437,7 +447,7 @@ static dash_status attend_lowdens(const dash_params* p, const void* q, const voi
   la.ca = make_ca(p->alpha, p->coarse_scale);
   la.ratio = ratio;
   la.cap = ld_cap_of(p, workspace_bytes);
-  size_t off[12];
+  size_t off[16];
   ld_layout(p, la.cap, off);
   char* ws = static_cast<char*>(workspace);
   la.grp_cnt = reinterpret_cast<int*>(ws + off[0]);
@@ -452,9 +462,13 @@ static dash_status attend_lowdens(const dash_params* p, const void* q, const voi
   la.part_ml = reinterpret_cast<float2*>(ws + off[9]);
   la.part_o = reinterpret_cast<bf16_t*>(ws + off[10]);
   la.row_pos = reinterpret_cast<int*>(ws + off[11]);
+  la.rng_pref = reinterpret_cast<int*>(ws + off[12]);
+  la.dense_list = reinterpret_cast<int*>(ws + off[13]);
+  la.dense_n = reinterpret_cast<int*>(ws + off[14]);
+  la.head_items = reinterpret_cast<int*>(ws + off[15]);
   hipError_t e;
   if ((e = launch_lowdens_plan(la, st)) != hipSuccess) return hip_fail(e, "low-density plan");
-  dash_status s = attend_common(p, q, k, v, kbar, sel, o, lse, st, 1, -1, la.tile_off);
+  dash_status s = attend_common(p, q, k, v, kbar, sel, o, lse, st, 1, -1, la.dense_list, la.dense_n);
   if (s != DASH_OK) return s;
   if ((e = launch_lowdens_attend(la, st)) != hipSuccess) return hip_fail(e, "low-density attention");
   return DASH_OK;
@@ -471,7 +485,7 @@ dash_status dash_fwd_attend_lowdens(const dash_params* p, const void* q, const v
   if (!(ratio >= 0.f) || !std::isfinite(ratio)) return fail(DASH_EINVAL, "ratio must be finite and >= 0 (got %g)", ratio);
   if (!ld_supported(p, sel))
     return fail(DASH_EUNSUPPORTED, "the low-density schedule is built for causal bf16 attention and needs sel->mask");
-  size_t off[12];
+  size_t off[16];
   const size_t need = ld_layout(p, 0, off);
   if (workspace_bytes < need) return fail(DASH_EWORKSPACE, "workspace of at least %zu bytes needed, %zu given", need, workspace_bytes);
   if (!ok_ptr(workspace)) return fail(DASH_EINVAL, "workspace must be non-null and 16-byte aligned");

@@ -44,8 +44,10 @@
 // computes its own head's p from one score MFMA chain (the Stage-1
 // arithmetic) and the columns of a row add theirs across lanes
 // (prior_chunk32_heads).
+// One query tile (row group `logical` in the launch's order) of the walk;
+// the body of fwd_mfma_kernel and fwd_mfma_list_kernel.
 template <int D, int HG>
-__global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
+__device__ __forceinline__ void fwd_mfma_tile(const FwdArgs& a, const int logical) {
   constexpr int CH = D / 8;          // 16-byte chunks per row
   constexpr int KS = D / 16;         // k-steps of the S product
   constexpr int NDT = D / 32;        // 32-row d tiles of O^T
@@ -63,12 +65,6 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
   const int nb = a.T / DASH_BLOCK;
   const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
   const int nrg = (a.T + RPG - 1) / RPG;  // row groups per head group
-  const int nwg = gridDim.x;
-  const int wg = blockIdx.x;
-  // XCD-aware order: consecutive workgroup ids go round-robin over the 8
-  // XCDs; give each XCD a contiguous range of heads so their K/V stay in
-  // that XCD's L2, and start every head with its longest (last) rows.
-  const int logical = (nwg % 8 == 0) ? (wg % 8) * (nwg / 8) + wg / 8 : wg;
   const size_t bkv = logical / nrg;  // the key/value head (the query head when HG = 1)
   const int rg = nrg - 1 - (logical % nrg);
 
@@ -92,8 +88,6 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
   // the heads of a group share their tile lists (the union of their supports)
   const int* glist = a.tile_blk + (bkv * HG * ntile + tile) * nb;
   const int cnt = a.tile_cnt[bkv * HG * ntile + tile];
-  if constexpr (HG == 1)
-    if (a.tile_skip != nullptr && a.tile_skip[bkv * ntile + tile] >= 0) return;  // the low-density schedule's
   const CoarseArith ca = a.ca;
   const float sl2 = a.fine_scale * LOG2E_F;
   // The block list is staged in LDS: a global (vector-memory) load inside
@@ -320,6 +314,29 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
   }
 }
 
+template <int D, int HG>
+__global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
+  // XCD-aware order: consecutive workgroup ids go round-robin over the 8
+  // XCDs; give each XCD a contiguous range of heads so their K/V stay in
+  // that XCD's L2, and start every head with its longest (last) rows.
+  const int nwg = gridDim.x;
+  const int wg = blockIdx.x;
+  fwd_mfma_tile<D, HG>(a, (nwg % 8 == 0) ? (wg % 8) * (nwg / 8) + wg / 8 : wg);
+}
+
+// The same walk over a device-side list of row groups (the tiles a
+// low-density call leaves to the dense walk): persistent workgroups take
+// list entries g, g + grid, ...; a call whose tiles all take the other
+// schedule launches only these few workgroups.
+template <int D, int HG>
+__global__ __launch_bounds__(256, 2) void fwd_mfma_list_kernel(FwdArgs a) {
+  const int n = a.dense_n[0];
+  for (int k = blockIdx.x; k < n; k += gridDim.x) {
+    fwd_mfma_tile<D, HG>(a, a.dense_list[k]);
+    __syncthreads();  // the tile's LDS is reused by the next
+  }
+}
+
 // ---------------------------------------------------------------------------- generic kernel
 //
 // One wave per query row, blocks in ascending order, natural-exp online
@@ -384,6 +401,14 @@ __global__ __launch_bounds__(64) void fwd_generic_kernel(FwdArgs a) {
 template <int HG>
 static void launch_fwd_hg(const FwdArgs& a, hipStream_t st) {
   const int rpg = 4 * (32 / HG);
+  if (a.dense_list != nullptr) {
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    const dim3 grid(2 * ncu);  // two workgroups per CU are resident
+    if (a.D == 128) fwd_mfma_list_kernel<128, HG><<<grid, 256, 0, st>>>(a);
+    else fwd_mfma_list_kernel<64, HG><<<grid, 256, 0, st>>>(a);
+    return;
+  }
   const dim3 grid(((a.T + rpg - 1) / rpg) * (a.BH / HG));
   if (a.D == 128) fwd_mfma_kernel<128, HG><<<grid, 256, 0, st>>>(a);
   else fwd_mfma_kernel<64, HG><<<grid, 256, 0, st>>>(a);

@@ -7,6 +7,7 @@
 #define DASH_BLOCK 64       // keys per block (Stage 0 pooling and Stage 2 key tile)
 #define DASH_QTILE 128      // query rows per Stage-2 tile (4 waves x 32 rows)
 #define DASH_MAX_NB 1536    // longest prefill sequence: 1536 blocks = 98304 tokens
+#define DASH_LD_RANGE 128   // low-density schedule: row groups (of 64 rows) per row range of its work items
 
 typedef uint16_t bf16_t;  // raw bfloat16 storage
 

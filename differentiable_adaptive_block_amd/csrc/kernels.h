@@ -38,9 +38,11 @@ struct FwdArgs {
   int grp;  // query heads per key/value head: k, v, kbar are indexed by bh / grp
   float fine_scale;
   CoarseArith ca;
-  // [BH, ntile] or null: tiles with an entry >= 0 are left to the
-  // low-density schedule (lowdens.hip) and skipped here
-  const int* tile_skip = nullptr;
+  // null, or the row groups to walk (in the launch's logical numbering) and
+  // their count, on the device: a low-density call (lowdens.hip) leaves
+  // these tiles to this walk and takes the others itself
+  const int* dense_list = nullptr;
+  const int* dense_n = nullptr;
 };
 
 // The low-density Stage-2 schedule (lowdens.hip): causal, bf16, one KV head
@@ -66,11 +68,15 @@ struct LdArgs {
   int* grp_cnt;      // [BH, nb, nb] rows of group g that selected block b, then prefixes
   int* gpairs;       // [BH, nb] pairs of each 64-row group
   int* tile_off;     // [BH, ntile] first pair of a tile taken here, -1: dense walk
+  int* dense_list;   // [BH * ntile] the dense walk's row groups (FwdArgs::dense_list)
+  int* dense_n;      // [1] their count
   int2* row_info;    // [BH, T] (first pair, pairs) of the rows of taken tiles
   int* col_cnt;      // [BH, nb] listed rows per key block
   int* col_base;     // [BH, nb] first entry of each column
+  int* rng_pref;     // [BH, nrange + 1, nb] entries of column b from rows before each row-range boundary
   int4* items;       // work items {column, first entry, entries}
   int* n_items;      // [1]
+  int* head_items;   // [BH] work items per head
   int2* col_ent;     // [cap] (row, partial index) grouped by column
   int* row_pos;      // [cap] partial indices of each row's pairs, rows at row_info.x
   float2* part_ml;   // [cap] partial (max + prior, sum) per pair, log2 units

@@ -50,6 +50,12 @@ __device__ __forceinline__ uint32_t cand_bits(int rb, int w) {
 }
 
 // ---------------------------------------------------------------------------- plan
+// Work items are cut per (head, row range of DASH_LD_RANGE groups = 8192
+// rows, column): a column's entries are in row order, so the entries of one
+// range are a contiguous run of it, and consecutive items gather their
+// query rows from one 2 MB slice of a head's queries, which stays in the
+// XCD's L2.
+//
 // The lists are built without atomics, from per-(row group, block) counts:
 // row group g is the 64 rows of block g (the own block of all of them).
 //   count:     grp[g][b] = rows of group g that selected candidate b (b < g),
@@ -99,18 +105,26 @@ __global__ __launch_bounds__(256) void ld_count_kernel(LdArgs a) {
 
 // Exclusive scan of n ints in order by one 1024-thread workgroup: value i
 // is load(i); calls emit(i, value, exclusive prefix (64-bit)) for every i.
-// The prefix of a chunk is carried in LDS.
+// Each pass covers 4096 values, 4 consecutive ones per thread; the prefix
+// of the passes so far is carried in LDS.
 template <typename LD, typename F>
 __device__ __forceinline__ void block_scan(int n, LD load, F emit) {
+  constexpr int PER = 4;
   __shared__ long long wsum[16];
   __shared__ long long carry;
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
   if (tid == 0) carry = 0;
   __syncthreads();
-  for (int base = 0; base < n; base += 1024) {
-    const int i = base + tid;
-    const int v = i < n ? load(i) : 0;
-    int x = v;  // inclusive scan in the wave
+  for (int base = 0; base < n; base += 1024 * PER) {
+    const int i0 = base + PER * tid;
+    int v[PER];
+    int tsum = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      v[e] = i0 + e < n ? load(i0 + e) : 0;
+      tsum += v[e];
+    }
+    int x = tsum;  // inclusive scan of the thread sums in the wave
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const int y = __shfl_up(x, o, 64);
@@ -120,7 +134,12 @@ __device__ __forceinline__ void block_scan(int n, LD load, F emit) {
     __syncthreads();
     long long before = carry;
     for (int k = 0; k < w; ++k) before += wsum[k];
-    if (i < n) emit(i, v, before + x - v);
+    long long run = before + x - tsum;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      if (i0 + e < n) emit(i0 + e, v[e], run);
+      run += v[e];
+    }
     __syncthreads();
     if (tid == 1023) carry = before + x;
     __syncthreads();
@@ -145,6 +164,15 @@ __global__ __launch_bounds__(1024) void ld_scan_tiles_kernel(LdArgs a) {
   };
   block_scan(n, pairs_of, [&](int i, int v, long long excl) {
     a.tile_off[i] = (v > 0 && excl + v <= a.cap) ? (int)excl : -1;
+  });
+  __syncthreads();
+  // the tiles left to the dense walk, as its row-group numbers (one KV head
+  // per query head: row group L is tile ntile - 1 - L % ntile of head
+  // L / ntile), in increasing order (each head's longest rows first)
+  auto dense_at = [&](int L) { return a.tile_off[(L / ntile) * ntile + (ntile - 1 - L % ntile)] < 0 ? 1 : 0; };
+  block_scan(n, dense_at, [&](int L, int v, long long excl) {
+    if (v) a.dense_list[excl] = L;
+    if (L == n - 1) a.dense_n[0] = (int)(excl + v);
   });
 }
 
@@ -180,31 +208,70 @@ __global__ __launch_bounds__(1024) void ld_colscan_kernel(LdArgs a) {
     all += v;
   }
   if (b < nb) {
-    for (int g = g0; g < g1; ++g)
+    const int nr = (nb + DASH_LD_RANGE - 1) / DASH_LD_RANGE;
+    int* rp = a.rng_pref + (size_t)bh * (nr + 1) * nb + b;
+    for (int g = g0; g < g1; ++g) {
+      if (g % DASH_LD_RANGE == 0) rp[(size_t)(g / DASH_LD_RANGE) * nb] = before;  // rows before the range
       if (group_taken(a, bh, g)) {
         int* c = grp + (size_t)g * nb + b;
         const int v = *c;
         *c = before;
         before += v;
       }
-    if (k == 0) a.col_cnt[bh * nb + b] = all;
+    }
+    if (k == 0) {
+      // boundaries at or before the column's first group hold none of it
+      for (int r = 0; r * DASH_LD_RANGE <= b; ++r) rp[(size_t)r * nb] = 0;
+      a.col_cnt[bh * nb + b] = all;
+      rp[(size_t)nr * nb] = all;
+    }
   }
 }
 
-// Column bases (exclusive scan of the counts) and the work items: column c
-// with n entries gives ceil(n / 128) items {c, first entry, entries}.
+// Column bases: exclusive scan of the column counts (one workgroup).
 __global__ __launch_bounds__(1024) void ld_scan_cols_kernel(LdArgs a) {
-  const int n = a.BH * (a.T / DASH_BLOCK);
-  block_scan(n, [&](int i) { return a.col_cnt[i]; },
+  block_scan(a.BH * (a.T / DASH_BLOCK), [&](int i) { return a.col_cnt[i]; },
              [&](int i, int v, long long excl) { a.col_base[i] = (int)excl; });
-  __syncthreads();
-  block_scan(n, [&](int i) { return (a.col_cnt[i] + kItemRows - 1) / kItemRows; },
-             [&](int i, int v, long long excl) {
-               const int base = a.col_base[i], cnt = a.col_cnt[i];
-               for (int k = 0; k < v; ++k)
-                 a.items[excl + k] = make_int4(i, base + k * kItemRows, min(kItemRows, cnt - k * kItemRows), 0);
-               if (i == n - 1) a.n_items[0] = (int)(excl + v);
-             });
+}
+
+// Work items, one workgroup per head: the entries of column b from row
+// range r (n of them) give ceil(n / 128) items {column, first entry,
+// entries}, in (head, range, column) order.  With EMIT false the kernel
+// only counts the head's items; with EMIT true it writes them after the
+// items of the heads before it.
+template <bool EMIT>
+__global__ __launch_bounds__(1024) void ld_items_kernel(LdArgs a) {
+  const int nb = a.T / DASH_BLOCK;
+  const int nr = (nb + DASH_LD_RANGE - 1) / DASH_LD_RANGE;
+  const size_t bh = blockIdx.x;
+  // run i = (r, b) of this head: entries rng_pref[r + 1][b] - rng_pref[r][b]
+  auto run = [&](int i, int& first) {
+    const int b = i % nb, r = i / nb;
+    const int* rp = a.rng_pref + (bh * (nr + 1) + r) * nb + b;
+    first = a.col_base[bh * nb + b] + rp[0];
+    return rp[nb] - rp[0];
+  };
+  const int nrun = nr * nb;
+  auto items_of = [&](int i) { int f; return (run(i, f) + kItemRows - 1) / kItemRows; };
+  if constexpr (!EMIT) {
+    __shared__ int total;
+    block_scan(nrun, items_of, [&](int i, int v, long long excl) {
+      if (i == nrun - 1) total = (int)(excl + v);
+    });
+    __syncthreads();
+    if (threadIdx.x == 0) a.head_items[bh] = total;
+  } else {
+    long long hb = 0;  // the items of the heads before this one
+    for (size_t x = 0; x < bh; ++x) hb += a.head_items[x];
+    block_scan(nrun, items_of, [&](int i, int v, long long excl) {
+      int first;
+      const int cnt = run(i, first);
+      const int col = (int)(bh * nb) + i % nb;
+      for (int k = 0; k < v; ++k)
+        a.items[hb + excl + k] = make_int4(col, first + k * kItemRows, min(kItemRows, cnt - k * kItemRows), 0);
+      if (bh == (size_t)a.BH - 1 && i == nrun - 1) a.n_items[0] = (int)(hb + excl + v);
+    });
+  }
 }
 
 // Fill: one wave (one 64-thread workgroup) per row group of a taken tile.
@@ -630,6 +697,8 @@ hipError_t launch_lowdens_plan(const LdArgs& a, hipStream_t st) {
   ld_scan_tiles_kernel<<<1, 1024, 0, st>>>(a);
   ld_colscan_kernel<<<(unsigned)(a.BH * ((nb + 63) / 64)), 1024, 0, st>>>(a);
   ld_scan_cols_kernel<<<1, 1024, 0, st>>>(a);
+  ld_items_kernel<false><<<a.BH, 1024, 0, st>>>(a);
+  ld_items_kernel<true><<<a.BH, 1024, 0, st>>>(a);
   ld_fill_kernel<<<(unsigned)(a.BH * nb), 64, 0, st>>>(a);
   return hipGetLastError();
 }

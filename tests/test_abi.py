@@ -306,3 +306,14 @@ def test_lowdens_entry_validation(L):
     assert "workspace" in L.dash_last_error().decode()
     assert _lowdens(L, p, ws=None, wsb=base) == _lib.DASH_EINVAL
     assert _lowdens(L, _params(T=300)) == _lib.DASH_EINVAL  # whole blocks only
+
+
+def test_lowdens_workspace_sizes_are_monotone(L):
+    """dash_fwd_lowdens_workspace_bytes grows with the pair count (the library derives the
+    capacity of a workspace by searching these sizes; that an exactly sized workspace holds
+    every pair is checked on the GPU, tests/test_gpu_lowdens.py)."""
+    p = _params(T=4096)
+    for n in (1, 127, 128, 100003, 7 << 20):
+        need = L.dash_fwd_lowdens_workspace_bytes(ctypes.byref(p), n)
+        assert L.dash_fwd_lowdens_workspace_bytes(ctypes.byref(p), n - 1) <= need
+        assert L.dash_fwd_lowdens_workspace_bytes(ctypes.byref(p), n + 1024) > need

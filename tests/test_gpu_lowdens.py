@@ -47,9 +47,9 @@ def _np64(t):
     return t.double().cpu().numpy()
 
 
-def _lowdens(w, cs, ratio, pairs=None, alpha=1.5):
+def _lowdens(w, cs, ratio, pairs=None, alpha=1.5, extra_bytes=0):
     """Selection, then Stage 2 through dash_fwd_attend_lowdens with room for
-    ``pairs`` pairs (None: all the qualifying tiles' pairs)."""
+    ``pairs`` pairs (None: all the qualifying tiles' pairs), plus ``extra_bytes``."""
     api, L = _api(), _lib()
     q, k, v = w["q"], w["k"], w["v"]
     B, H, T, D = q.shape
@@ -61,7 +61,7 @@ def _lowdens(w, cs, ratio, pairs=None, alpha=1.5):
     L.fwd_select(p, q.data_ptr(), k.data_ptr(), kbar.data_ptr(), csel, st)
     need = api.lowdens_pairs(sel, p, ratio)
     n = need if pairs is None else pairs
-    wsb = L.fwd_lowdens_workspace_bytes(p, n)
+    wsb = L.fwd_lowdens_workspace_bytes(p, n) + extra_bytes
     ws = torch.empty(wsb, dtype=torch.uint8, device=q.device)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
@@ -125,6 +125,17 @@ def test_lowdens_deterministic_and_close_to_dense():
     assert float(diff.max()) <= mx and float(diff.mean()) <= mn, (float(diff.max()), float(diff.mean()))
     assert float((a["lse"] - d["lse"]).abs().max()) <= 4e-3
     _say(f"[lowdens] vs dense walk: O max {float(diff.max()):.3e} mean {float(diff.mean()):.3e}")
+
+
+def test_lowdens_exact_workspace_takes_every_qualifying_tile():
+    """A workspace sized for exactly the qualifying tiles' pairs holds all of them: the
+    result equals (bit for bit) the one with a much larger workspace, so no tile fell back
+    to the dense walk, whose rounding differs."""
+    w = inputs.make_prefill(1, 2, 4096, 128, "bf16", True, (1, 8), seed=29, device=DEV, with_dout=False)
+    cs = 7.0 / math.sqrt(128)
+    a = _lowdens(w, cs, 0.0)
+    b = _lowdens(w, cs, 0.0, extra_bytes=64 << 20)
+    assert torch.equal(a["o"], b["o"]) and torch.equal(a["lse"], b["lse"])
 
 
 def test_lowdens_api_forward_switch():
