@@ -118,7 +118,7 @@ def pool_attn(k: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
     return kbar
 
 
-LOWDENS_RATIO = 2.0  # DASH_LOWDENS_RATIO of include/dash.h
+LOWDENS_RATIO = 4.0  # DASH_LOWDENS_RATIO of include/dash.h
 
 
 def lowdens_pairs(sel: Selection, p: _lib.DashParams, ratio: float = LOWDENS_RATIO) -> int:

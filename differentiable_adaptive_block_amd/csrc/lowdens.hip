@@ -39,6 +39,10 @@
 
 namespace {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+
 constexpr int kItemRows = 128;  // listed rows per work item (4 waves x 32 columns)
 
 // Candidate mask words of a row in block rb (causal: blocks 0 .. rb-1), and
@@ -586,7 +590,12 @@ __global__ __launch_bounds__(256, 2) void ld_part_kernel(LdArgs a) {
           for (int e = 0; e < 4; ++e) o4[e] = (__bf16)oacc[dt][4 * r4 + e];
           *reinterpret_cast<bf16x4*>(ost + j * D + 8 * (c ^ (j & (CH - 1))) + 4 * h) = o4;
         }
-      if (valid && h == 0) a.part_ml[dest] = make_float2(mcol, ltot);
+      if (valid && h == 0) {
+        f32x2 ml;
+        ml[0] = mcol;
+        ml[1] = ltot;
+        __builtin_nontemporal_store(ml, reinterpret_cast<f32x2*>(a.part_ml + dest));
+      }
     }
     // item i+1's tiles and column data, item i+2's entries, item i+3's
     // descriptor (and the staging above) are complete past this point;
@@ -602,9 +611,12 @@ __global__ __launch_bounds__(256, 2) void ld_part_kernel(LdArgs a) {
         const int idx = q * 64 + l;
         const int cx = idx / CH, ch = idx % CH;
         const int dcx = __shfl(dest, cx, 64);
+        // streaming (nontemporal) stores: the partials are read once, by the
+        // merge, and should not evict the queries and tiles the next items
+        // read from L2
         if (32 * w + cx < nent)
-          *reinterpret_cast<uint4*>(a.part_o + (size_t)dcx * D + 8 * ch) =
-              *reinterpret_cast<const uint4*>(ost + cx * D + 8 * (ch ^ (cx & (CH - 1))));
+          __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(ost + cx * D + 8 * (ch ^ (cx & (CH - 1)))),
+                                      reinterpret_cast<u32x4*>(a.part_o + (size_t)dcx * D + 8 * ch));
       }
     }
     // the staging of this item is read before the barrier at the top of the

@@ -194,7 +194,7 @@ dash_status dash_fwd(const dash_params* p, const void* q, const void* k, const v
  * workspace holds at least one pair beyond that fixed part and the case is
  * supported (mask non-null); with no workspace it takes the dense walk.
  */
-#define DASH_LOWDENS_RATIO 2.0f
+#define DASH_LOWDENS_RATIO 4.0f
 size_t dash_fwd_lowdens_workspace_bytes(const dash_params* p, int64_t max_pairs);
 dash_status dash_fwd_attend_lowdens(const dash_params* p, const void* q, const void* k, const void* v,
                                     const void* kbar, const dash_sel* sel, float ratio, void* o,
