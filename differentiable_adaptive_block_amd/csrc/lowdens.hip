@@ -326,25 +326,46 @@ __global__ __launch_bounds__(64) void ld_fill_kernel(LdArgs a) {
     __builtin_amdgcn_wave_barrier();
     flushed = slot;
   };
-  int goff = gfirst;  // the group's partials of the next block with a selecting row
+  int goff = gfirst;  // the group's first partial of the next word's blocks
+  // per word: block 32 w + b's ballot over the group's rows, its first
+  // column entry and its first partial, for lane b < 32 and, through LDS,
+  // for the rows' own loops over their selected blocks
+  __shared__ unsigned long long sbal[32];
+  __shared__ int sbase[32], sgof[32];
   for (int w = 0; w < cand_words(g); ++w) {
     const uint32_t word = mw[w] & cand_bits(g, w);
-    const int blk = 32 * w + (l & 31);
-    const int base = (l < 32 && blk < g) ? cbase[blk] + grp[blk] : 0;  // lane b: block 32 w + b
+    unsigned long long mybal = 0ull;
+#pragma unroll
     for (int bit = 0; bit < 32; ++bit) {
-      const bool mine = (word >> bit) & 1u;
-      const unsigned long long bal = __ballot(mine);
-      if (bal == 0ull) continue;  // wave-uniform
-      if (__ballot(slot - flushed == kBuf) != 0ull) flush();
-      const int bb = __shfl(base, bit, 64);
-      if (mine) {
-        const int rank = __popcll(bal & below);
-        a.col_ent[bb + rank] = make_int2(r, goff + rank);
-        rbuf[l][slot - flushed] = goff + rank;
-        ++slot;
-      }
-      goff += __popcll(bal);
+      const unsigned long long bal = __ballot((word >> bit) & 1u);
+      if (l == bit) mybal = bal;
     }
+    const int blk = 32 * w + l;
+    const int cntb = l < 32 ? __popcll(mybal) : 0;
+    int xs = cntb;  // inclusive scan of the blocks' counts
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+      const int y = __shfl_up(xs, o, 64);
+      if (l >= o) xs += y;
+    }
+    if (__ballot(slot - flushed + __popc(word) > kBuf) != 0ull) flush();
+    __builtin_amdgcn_wave_barrier();
+    if (l < 32) {
+      sbal[l] = mybal;
+      sbase[l] = blk < g ? cbase[blk] + grp[blk] : 0;
+      sgof[l] = goff + xs - cntb;
+    }
+    __builtin_amdgcn_wave_barrier();
+    // this row's selected blocks of the word, in order
+    for (uint32_t rem = word; rem; rem &= rem - 1u) {
+      const int bit = __builtin_ctz(rem);
+      const int rank = __popcll(sbal[bit] & below);
+      a.col_ent[sbase[bit] + rank] = make_int2(r, sgof[bit] + rank);
+      rbuf[l][slot - flushed] = sgof[bit] + rank;
+      ++slot;
+    }
+    goff += __shfl(xs, 31, 64);
+    __builtin_amdgcn_wave_barrier();
   }
   a.col_ent[cbase[g] + grp[g] + l] = make_int2(r, goff + l);
   if (__ballot(slot - flushed == kBuf) != 0ull) flush();
