@@ -654,13 +654,19 @@ __global__ __launch_bounds__(256, 2) void ld_part_kernel(LdArgs a) {
 
 // ---------------------------------------------------------------------------- merge
 // 16 lanes per row, 4 rows per wave, 16 rows per workgroup (all in one
-// tile).  Lane t of a row holds D/16 consecutive output values.
+// tile).  Lane t of a row holds D/16 consecutive output values.  The
+// workgroups are numbered XCD-aware (consecutive ids go round-robin over
+// the 8 XCDs; each XCD takes a contiguous range of row blocks), so the
+// four workgroups of a 64-row group, whose rows read the group's partials
+// and (max, sum) records in interleaved order, share one L2.
 template <int D>
 __global__ __launch_bounds__(256) void ld_merge_kernel(LdArgs a) {
   constexpr int VPL = D / 16;
   const int ntile = (a.T + DASH_QTILE - 1) / DASH_QTILE;
   const int rows_per_head = a.T;
-  const size_t grow = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int nwg = gridDim.x, wg = blockIdx.x;
+  const int logical = (nwg % 8 == 0) ? (wg % 8) * (nwg / 8) + wg / 8 : wg;
+  const size_t grow = (size_t)logical * 16 + (threadIdx.x >> 4);
   const size_t bh = grow / rows_per_head;
   const int r = (int)(grow % rows_per_head);
   if (bh >= (size_t)a.BH) return;
