@@ -81,7 +81,7 @@ SMALL = [
     # name, B, H, T, D, coarse multiple of 1/sqrt(D), planted, ratio, share of the pairs the workspace holds
     ("all-tiles-d128", 1, 2, 2048, 128, 7.0, (1, 8), 0.0, 1.0),
     ("all-tiles-d64", 2, 1, 1600, 64, 7.0, (1, 4), 0.0, 1.0),
-    ("ratio-mix", 1, 2, 4096, 128, 7.0, (1, 8), 4.0, 1.0),
+    ("ratio-mix", 1, 2, 6144, 128, 16.0, (1, 8), 4.0, 1.0),
     ("half-workspace", 1, 2, 2048, 128, 7.0, (1, 8), 0.0, 0.5),
     ("dense-scale-all-tiles", 1, 1, 1088, 128, 1.0, (1, 8), 0.0, 1.0),
 ]
@@ -99,6 +99,8 @@ def test_lowdens_small_full_oracle(case):
     r = _lowdens(w, cs, ratio, pairs)
     if ratio == 0.0:
         assert r["need"] == full, (r["need"], full)
+    elif share == 1.0:
+        assert 0 < r["need"] < full, (r["need"], full)  # some tiles each way
     _say(f"  pairs: qualifying {r['need']} of {full}, workspace for {pairs if pairs is not None else r['need']}")
     sel = r["sel"]
     g = dict(o=r["o"].float().cpu().numpy(), lse=r["lse"].cpu().numpy(), tau=sel.tau.cpu().numpy(),
@@ -182,3 +184,35 @@ def test_lowdens_64k_calibrated_prefill_sampled():
         st = check_out_rows(r["o"][0, h].float().cpu().numpy(), r["lse"][0, h].cpu().numpy(), ora, rows,
                             torch.bfloat16, f"lowdens 64K head {h}")
         _say(f"  head {h}: {st}")
+
+
+def test_dash_fwd_with_workspace_takes_the_schedule():
+    """dash_fwd given a low-density workspace runs Stages 0-2 with the schedule at
+    DASH_LOWDENS_RATIO: the same bits as dash_fwd_select + dash_fwd_attend_lowdens; with no
+    workspace it runs the dense walk (the same bits as api.forward)."""
+    api, L = _api(), _lib()
+    # a sparse selection (coarse scale 16/sqrt(128): a few blocks per row), so that most
+    # tiles' dense walk exceeds the default ratio times their pairs
+    w = inputs.make_prefill(1, 2, 8192, 128, "bf16", True, (1, 8), seed=31, device=DEV, with_dout=False)
+    cs = 16.0 / math.sqrt(128)
+    ref = _lowdens(w, cs, api.LOWDENS_RATIO)
+    q, k, v = w["q"], w["k"], w["v"]
+    B, H, T, D = q.shape
+    p = api.make_params(q, 1.5, True, None, cs)
+    sel = api.alloc_selection(p, q.device, want_mask=True)
+    kbar = torch.empty((B, H, T // 64, D), dtype=q.dtype, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    wsb = L.fwd_lowdens_workspace_bytes(p, ref["need"])
+    ws = torch.empty(wsb, dtype=torch.uint8, device=q.device)
+    st = torch.cuda.current_stream().cuda_stream
+    L.fwd(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), kbar.data_ptr(), sel.as_c(),
+          ws.data_ptr(), wsb, st)
+    torch.cuda.synchronize()
+    assert ref["need"] > 0
+    assert torch.equal(o, ref["o"]) and torch.equal(lse, ref["lse"])
+    d = _dense(w, cs)
+    L.fwd(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), kbar.data_ptr(), sel.as_c(),
+          0, 0, st)
+    torch.cuda.synchronize()
+    assert torch.equal(o, d["o"]) and torch.equal(lse, d["lse"])
