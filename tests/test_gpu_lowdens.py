@@ -8,7 +8,9 @@ calibrated 64K prefill, where the whole output is also compared with the
 dense walk's.  The cases cover every tile taken (ratio 0), a mix decided by
 the ratio, a workspace too small for every qualifying tile (the rest fall
 back to the dense walk in the same call), head dim 64 and 128, a last tile
-of a single block, and reruns (bit-identical).
+of a single block, the longest prefill (98304 tokens) with every tile
+through the schedule, dash_fwd's own choice with a workspace, and reruns
+(bit-identical).
 """
 
 import math
@@ -216,3 +218,34 @@ def test_dash_fwd_with_workspace_takes_the_schedule():
           0, 0, st)
     torch.cuda.synchronize()
     assert torch.equal(o, d["o"]) and torch.equal(lse, d["lse"])
+
+
+def test_lowdens_96k_every_tile():
+    """The longest prefill (98304 tokens, 1536 blocks: 48 mask words per row, the fill's row
+    buffers flushed more than once, twelve 8192-row ranges) with every tile through the
+    schedule (ratio 0), two heads at coarse scale 7/sqrt(128): every row against the dense
+    walk, sampled rows against the oracle."""
+    B, H, T, D = 1, 2, 98304, 128
+    cs = 7.0 / math.sqrt(D)
+    _say(f"[lowdens] B{B} H{H} T{T} D{D}, every tile, coarse 7/sqrt(D)")
+    w = inputs.make_prefill(B, H, T, D, "bf16", True, (1, 8), seed=97, device=DEV, with_dout=False)
+    r = _lowdens(w, cs, 0.0)
+    total = B * H * T + int(r["sel"].nsel.long().sum())
+    assert r["need"] == total, (r["need"], total)
+    d = _dense(w, cs)
+    assert torch.equal(d["sel"].mask, r["sel"].mask)
+    diff = (r["o"].float() - d["o"].float()).abs()
+    mx, mn = tol_out(torch.bfloat16)
+    _say(f"  pairs {total}; vs dense walk: O max {float(diff.max()):.3e} mean {float(diff.mean()):.3e}")
+    assert float(diff.max()) <= mx and float(diff.mean()) <= mn
+    assert float((r["lse"] - d["lse"]).abs().max()) <= 4e-3
+    del d
+    rng = np.random.default_rng(11)
+    prm = oracle.Params(alpha=1.5, causal=True, coarse_scale=cs, storage="bf16")
+    h = 1
+    rows = sorted(set(rng.choice(T, size=128, replace=False).tolist() + [0, 63, 8191, 8192, T - 1]))
+    qh, kh, vh = (w[x][0, h] for x in ("q", "k", "v"))
+    ora = oracle_parallel.forward_rows(qh, kh, vh, prm, rows, kbar=r["kbar"][0, h])
+    st = check_out_rows(r["o"][0, h].float().cpu().numpy(), r["lse"][0, h].cpu().numpy(), ora, rows,
+                        torch.bfloat16, "lowdens 96K head 1")
+    _say(f"  head {h}: {st}")
