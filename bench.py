@@ -236,9 +236,11 @@ def bench_prefill(name, steps, warmup, device, log_prefix="", low_density=False)
     nsel = r["sel"].nsel.to(torch.int64)
     tile_cnt = r["sel"].tile_cnt.to(torch.int64)
     p = r["params"]
-    # timed calls: the selection outputs used only for validation (nsel, mask) are off,
-    # except the masks, which the low-density schedule builds its lists from
+    # timed calls: the selection outputs used only for validation (nsel, pass counts, mask)
+    # are off, except the masks, which the low-density schedule builds its lists from
     sel = api.alloc_selection(p, q.device, want_mask=low_density)
+    sel.nsel = None
+    sel.passes = None
     csel = sel.as_c()
     o = torch.empty_like(q)
     lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)

@@ -188,7 +188,7 @@ dash_status dash_fwd(const dash_params* p, const void* q, const void* k, const v
  * the sum of the rows' selected counts, sel->nsel); at least the value for
  * 0 pairs (then every tile takes the dense walk), else DASH_EWORKSPACE.  Per
  * pair it holds 20 + 2 D bytes; the fixed part is about
- * B H (8 T + 4 (T/64)^2) bytes (44 MB per head at T = 98304).
+ * B H (8 T + 4 (T/64)^2) bytes (about 10 MB per head at T = 98304).
  *
  * dash_fwd takes the same schedule, with ratio DASH_LOWDENS_RATIO, when its
  * workspace holds at least one pair beyond that fixed part and the case is
