@@ -28,9 +28,10 @@
 // Which tiles take it: a tile whose dense walk would visit more than
 // `ratio` times the pairs its rows need, as long as the pairs of all such
 // tiles so far (in head-major tile order) fit in the caller's workspace;
-// every other tile keeps the dense walk (its kernel skips the tiles taken
-// here).  The lists are built from the masks without atomics (see the plan
-// kernels), so they, too, are the same on every run.
+// every other tile keeps the dense walk, which the same call runs over a
+// device-side list of those tiles (fwd_mfma_list_kernel).  The lists are
+// built from the masks without atomics (see the plan kernels), so they,
+// too, are the same on every run.
 #include "kernels.h"
 #include "tiles.h"
 
@@ -41,7 +42,6 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-
 
 constexpr int kItemRows = 128;  // listed rows per work item (4 waves x 32 columns)
 
@@ -57,8 +57,9 @@ __device__ __forceinline__ uint32_t cand_bits(int rb, int w) {
 // Work items are cut per (head, row range of DASH_LD_RANGE groups = 8192
 // rows, column): a column's entries are in row order, so the entries of one
 // range are a contiguous run of it, and consecutive items gather their
-// query rows from one 2 MB slice of a head's queries, which stays in the
-// XCD's L2.
+// query rows from one 2 MB slice of a head's queries rather than from the
+// whole head (measured a little faster than items in plain column order;
+// narrower ranges re-read each block's keys and values more often).
 //
 // The lists are built without atomics, from per-(row group, block) counts:
 // row group g is the 64 rows of block g (the own block of all of them).
@@ -67,7 +68,8 @@ __device__ __forceinline__ uint32_t cand_bits(int rb, int w) {
 //   tiles:     which tiles take the schedule, their first pair (one workgroup);
 //   columns:   grp[g][b] becomes the exclusive prefix over the taken groups
 //              g' < g of column b, col_cnt[b] the column's length;
-//   bases:     column bases (exclusive scan of col_cnt) and work items;
+//   bases:     column bases (exclusive scan of col_cnt);
+//   items:     work items per head, then after the items of the heads before;
 //   fill:      entry of (row, b) at base[b] + grp[g][b] + the row's rank
 //              among the group's rows that selected b; each row's first pair
 //              and count.
@@ -389,7 +391,8 @@ __device__ __forceinline__ void lds_barrier() {
 
 // ---------------------------------------------------------------------------- partials
 // Persistent: workgroup g takes items g, g + grid, ... (XCD-aware: each XCD
-// a contiguous run of items per round).  Wave w takes the item's entries
+// a contiguous run of items per round).  Its partials go out with streaming
+// (nontemporal) stores: they are read once, by the merge.  Wave w takes the item's entries
 // 32w .. 32w+31 as MFMA columns.  Software-pipelined over items: while
 // item i is computed from one LDS buffer pair, item i+1's K and V tiles are
 // copied into the other (with the block's summary row, the prior's
