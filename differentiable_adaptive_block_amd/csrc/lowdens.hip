@@ -678,51 +678,50 @@ __global__ __launch_bounds__(256) void ld_merge_kernel(LdArgs a) {
   const int2 info = a.row_info[bh * a.T + r];
   const int off = info.x, n = info.y;
   const int* pos = a.row_pos + off;
-  float M = -INFINITY;
-  for (int s = t; s < n; s += 16) M = fmaxf(M, a.part_ml[pos[s]].x);
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-  float L = 0.f;
+  typedef uint16_t u16v __attribute__((ext_vector_type(VPL)));
+  // one pass with a running maximum: a chunk of 16 slots issues its (max,
+  // sum) record and its 16 partial rows together, and the next chunk's
+  // positions are in flight meanwhile, so a row waits on about one load
+  // round trip per chunk; when the maximum rises the sums so far are
+  // rescaled by 2^(old - new)
+  float M = -INFINITY, L = 0.f;
   float acc[VPL];
 #pragma unroll
   for (int e = 0; e < VPL; ++e) acc[e] = 0.f;
+  int ps = t < n ? pos[t] : -1;  // lane t: the chunk's slot t (-1 past the row's end)
   for (int s0 = 0; s0 < n; s0 += 16) {
     const int s = s0 + t;
-    float wgt = 0.f;
-    const int ps = s < n ? pos[s] : 0;  // lane t: the chunk's slot t
-    if (s < n) {
-      const float2 ml = a.part_ml[ps];
-      wgt = __builtin_amdgcn_exp2f(ml.x - M);
-      L = fmaf(wgt, ml.y, L);
+    const int ps_nx = s + 16 < n ? pos[s + 16] : -1;
+    const float2 ml = ps >= 0 ? a.part_ml[ps] : make_float2(-INFINITY, 0.f);
+    u16v ov[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int pk = __shfl(ps, gbase + k, 64);
+      if (pk >= 0) ov[k] = *reinterpret_cast<const u16v*>(a.part_o + (size_t)pk * D + VPL * t);
+      else ov[k] = u16v{};
     }
-    const int kn = min(16, n - s0);
-    // the chunk's partials, loads first
-    if (kn == 16) {
-      typedef uint16_t u16v __attribute__((ext_vector_type(VPL)));
-      u16v ov[16];
+    float cm = ml.x;
 #pragma unroll
-      for (int k = 0; k < 16; ++k)
-        ov[k] = *reinterpret_cast<const u16v*>(a.part_o + (size_t)__shfl(ps, gbase + k, 64) * D + VPL * t);
+    for (int o = 1; o < 16; o <<= 1) cm = fmaxf(cm, __shfl_xor(cm, o, 64));
+    const float Mn = fmaxf(M, cm);  // finite: every chunk holds at least one slot
+    const float c = __builtin_amdgcn_exp2f(M - Mn);
+    M = Mn;
+    const float wgt = ps >= 0 ? __builtin_amdgcn_exp2f(ml.x - M) : 0.f;
+    L = fmaf(L, c, wgt * ml.y);
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const float wk = __shfl(wgt, gbase + k, 64);
+    for (int e = 0; e < VPL; ++e) acc[e] *= c;
 #pragma unroll
-        for (int e = 0; e < VPL; ++e) acc[e] = fmaf(wk, bf2f(ov[k][e]), acc[e]);
-      }
-    } else {
-      for (int k = 0; k < kn; ++k) {
-        const float wk = __shfl(wgt, gbase + k, 64);
-        const bf16_t* po = a.part_o + (size_t)__shfl(ps, gbase + k, 64) * D + VPL * t;
+    for (int k = 0; k < 16; ++k) {
+      const float wk = __shfl(wgt, gbase + k, 64);
 #pragma unroll
-        for (int e = 0; e < VPL; ++e) acc[e] = fmaf(wk, bf2f(po[e]), acc[e]);
-      }
+      for (int e = 0; e < VPL; ++e) acc[e] = fmaf(wk, bf2f(ov[k][e]), acc[e]);
     }
+    ps = ps_nx;
   }
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) L += __shfl_xor(L, o, 64);
   const float inv = 1.f / L;
   bf16_t* O = reinterpret_cast<bf16_t*>(a.o) + (bh * a.T + r) * D + VPL * t;
-  typedef uint16_t u16v __attribute__((ext_vector_type(VPL)));
   u16v ov;
 #pragma unroll
   for (int e = 0; e < VPL; ++e) ov[e] = f2bf(acc[e] * inv);
