@@ -93,16 +93,25 @@ __global__ __launch_bounds__(256) void ld_count_kernel(LdArgs a) {
   const uint32_t* mw = a.mask + (bh * a.T + (size_t)g * DASH_BLOCK + l) * nbw;
   int* grp = a.grp_cnt + ((size_t)bh * nb + g) * nb;
   int sel = 0;
-  for (int w = 0; w < cand_words(g); ++w) {
-    const uint32_t word = mw[w] & cand_bits(g, w);
-    sel += __popc(word);
-    int cnt = 0;  // lane b < 32: rows that selected block 32 w + b
+  const int ncw = cand_words(g);
+  for (int w0 = 0; w0 < ncw; w0 += 4) {
+    uint32_t wd[4];  // four words loaded together: one memory wait per four
 #pragma unroll
-    for (int bit = 0; bit < 32; ++bit) {
-      const int c = __popcll(__ballot((word >> bit) & 1u));
-      if (l == bit) cnt = c;
+    for (int j = 0; j < 4; ++j) wd[j] = w0 + j < ncw ? mw[w0 + j] & cand_bits(g, w0 + j) : 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int w = w0 + j;
+      if (w >= ncw) break;  // the same on every lane
+      const uint32_t word = wd[j];
+      sel += __popc(word);
+      int cnt = 0;  // lane b < 32: rows that selected block 32 w + b
+#pragma unroll
+      for (int bit = 0; bit < 32; ++bit) {
+        const int c = __popcll(__ballot((word >> bit) & 1u));
+        if (l == bit) cnt = c;
+      }
+      if (l < 32 && 32 * w + l < g) grp[32 * w + l] = cnt;
     }
-    if (l < 32 && 32 * w + l < g) grp[32 * w + l] = cnt;
   }
   if (l == 0) grp[g] = DASH_BLOCK;
   const int pairs = (int)wave_sum((float)(sel + 1));  // <= 64 * 1537: exact in fp32
