@@ -343,15 +343,25 @@ __global__ __launch_bounds__(64) void ld_fill_kernel(LdArgs a) {
   // for the rows' own loops over their selected blocks
   __shared__ unsigned long long sbal[32];
   __shared__ int sbase[32], sgof[32];
-  for (int w = 0; w < cand_words(g); ++w) {
-    const uint32_t word = mw[w] & cand_bits(g, w);
+  const int ncw = cand_words(g);
+  // word w + 1's mask word and (lane b < 32) its block's column base are
+  // loaded while word w is handled
+  uint32_t word_nx = ncw > 0 ? mw[0] & cand_bits(g, 0) : 0u;
+  int base_nx = l < 32 && l < g ? cbase[l] + grp[l] : 0;
+  for (int w = 0; w < ncw; ++w) {
+    const uint32_t word = word_nx;
+    const int base = base_nx;
+    if (w + 1 < ncw) {
+      word_nx = mw[w + 1] & cand_bits(g, w + 1);
+      const int bn = 32 * (w + 1) + l;
+      base_nx = l < 32 && bn < g ? cbase[bn] + grp[bn] : 0;
+    }
     unsigned long long mybal = 0ull;
 #pragma unroll
     for (int bit = 0; bit < 32; ++bit) {
       const unsigned long long bal = __ballot((word >> bit) & 1u);
       if (l == bit) mybal = bal;
     }
-    const int blk = 32 * w + l;
     const int cntb = l < 32 ? __popcll(mybal) : 0;
     int xs = cntb;  // inclusive scan of the blocks' counts
 #pragma unroll
@@ -363,7 +373,7 @@ __global__ __launch_bounds__(64) void ld_fill_kernel(LdArgs a) {
     __builtin_amdgcn_wave_barrier();
     if (l < 32) {
       sbal[l] = mybal;
-      sbase[l] = blk < g ? cbase[blk] + grp[blk] : 0;
+      sbase[l] = base;
       sgof[l] = goff + xs - cntb;
     }
     __builtin_amdgcn_wave_barrier();
