@@ -316,7 +316,13 @@ __global__ __launch_bounds__(64) void ld_fill_kernel(LdArgs a) {
   // the group's first pair, then each row's (the rows in order)
   const int gfirst = toff + ((g & 1) ? a.gpairs[bh * nb + g - 1] : 0);
   int cnt = 1;
-  for (int w = 0; w < cand_words(g); ++w) cnt += __popc(mw[w] & cand_bits(g, w));
+  for (int w0 = 0; w0 < cand_words(g); w0 += 4) {  // four words loaded together
+    uint32_t wd[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wd[j] = w0 + j < cand_words(g) ? mw[w0 + j] & cand_bits(g, w0 + j) : 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cnt += __popc(wd[j]);
+  }
   int x = cnt;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
